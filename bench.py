@@ -1,0 +1,204 @@
+"""Benchmark of the multi-LoRA shrink/expand hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: slot metadata
+(lora_prepare_meta), shrink and expand (the two kernels lora_apply runs,
+issued here as lora_shrink + lora_expand so HIP events can bracket each
+kernel).  Inputs are resident in HBM before the timed region starts.  Enough
+copies of the inputs are rotated that consecutive steps never find their data
+in the 256 MB last-level cache (MALL).
+
+Default workload: decode (BGMV form) on a q_proj shape, 4096 -> 4096, rank 16,
+32 slots, 256 one-token requests with 10% of them without an adapter, bf16.
+
+One JSON line on stdout:  value = tokens per second of the whole step (all T
+tokens of the batch, including those without an adapter), plus the roofline
+of the dominant kernel (algorithmic bytes / measured average duration against
+the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LoRA shrink+expand tokens/s; % HBM peak (decode) / % bf16 MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline decode case)")
+    ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
+    ap.add_argument("--rotate-mb", type=float, default=640.0,
+                    help="total size of the rotated input copies (beats the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic(c):
+    """Bytes and flops the method must move/compute for one batch (per kernel).
+
+    A and B slot blocks of every distinct slot used are read once; x rows of
+    tokens with an adapter are read once; the y windows of those tokens are
+    read and written once (add into y).  Metadata and the fp32 rank-r buffer
+    are overheads and are not counted.  r is the padded r_max the kernels read.
+    """
+    import numpy as np
+    ts = c.token_slot
+    lora = ts >= 0
+    U = int(np.unique(ts[lora]).shape[0])
+    TL = int(lora.sum())
+    e = 4 if c.dtype == "f32" else 2
+    sw = sum(c.widths)
+    shrink_bytes = U * c.n_slices * c.d_in * c.r_max * e + TL * c.d_in * e
+    expand_bytes = U * sw * c.r_max * e + TL * sw * e * 2
+    shrink_flops = 2 * TL * c.r_max * c.n_slices * c.d_in
+    expand_flops = 2 * TL * c.r_max * sw
+    return dict(U=U, T_lora=TL, shrink_bytes=shrink_bytes, expand_bytes=expand_bytes,
+                shrink_flops=shrink_flops, expand_flops=expand_flops)
+
+
+def cpu_baseline(c, seconds):
+    """The oracle as it stands (plain C, fp64, one thread) on a bounded sample
+    of the same workload: whole batches, metadata plus every token's delta,
+    repeated until `seconds` have passed (at least one token)."""
+    import numpy as np
+    import oracle
+    T = c.T
+    rows_per_call = max(1, min(T, 64))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.prepare_meta(c.token_slot, c.num_slots)
+        for r0 in range(0, T, rows_per_call):
+            rows = np.arange(r0, min(T, r0 + rows_per_call))
+            oracle.lora_rows(c.x, c.token_slot, c.num_slots, c.A, c.B, c.offsets, c.scale, c.y0,
+                             rows=rows)
+            done += rows.shape[0]
+            if time.perf_counter() - t0 > seconds:
+                break
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} tokens of workload '{c.name}' (metadata + fp64 delta of every "
+                       f"token, whole batches of {T}) in {dt:.1f} s on one host thread")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the path has no multi-GPU stage); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import segmented_gather_rank_amd as L
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = W.config(args.config)
+    alg = algorithmic(c)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    base = dict(ts=torch.from_numpy(c.token_slot).to(dev), x=to_dev(c.x),
+                A=[to_dev(a) for a in c.A], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
+    set_bytes = sum(t.numel() * t.element_size()
+                    for t in [base["ts"], base["x"], base["y"], *base["A"], *base["B"]])
+    nrot = max(1, min(64, int(np.ceil(args.rotate_mb * 2 ** 20 / set_bytes))))
+    sets = [base] + [dict(ts=base["ts"].clone(), x=base["x"].clone(), A=[a.clone() for a in base["A"]],
+                          B=[b.clone() for b in base["B"]], y=base["y"].clone()) for _ in range(nrot - 1)]
+    dtype = base["x"].dtype
+    r = c.r_max
+    sh_need = L.lora_shrink_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, r, dtype, args.mode)
+    for s in sets:
+        s["mws"] = torch.empty(L.lora_meta_workspace_bytes(c.T, c.num_slots), dtype=torch.uint8, device=dev)
+        s["sws"] = torch.empty(max(sh_need, 16), dtype=torch.uint8, device=dev)
+        s["u"] = torch.empty(c.n_slices, c.T, r, dtype=torch.float32, device=dev)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        meta = L.lora_prepare_meta(s["ts"], c.num_slots, workspace=s["mws"])
+        if ev is not None:
+            ev[1].record()
+        L.lora_shrink(meta, s["x"], s["A"], s["u"], scale=c.scale, mode=args.mode, workspace=s["sws"])
+        if ev is not None:
+            ev[2].record()
+        L.lora_expand(meta, s["u"], s["B"], c.offsets, s["y"], add=True, mode=args.mode)
+        if ev is not None:
+            ev[3].record()
+        return meta
+
+    for i in range(args.warmup):
+        step(sets[i % nrot])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % nrot], evs[i])
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    total_ms = evs[0][0].elapsed_time(evs[-1][3])
+    meta_us = 1e3 * np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    shrink_us = 1e3 * np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    expand_us = 1e3 * np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    ms_per_step = total_ms / K
+    value = c.T * K / (total_ms / 1e3)
+
+    kern = {"lora_shrink": (shrink_us, alg["shrink_bytes"], alg["shrink_flops"]),
+            "lora_expand": (expand_us, alg["expand_bytes"], alg["expand_flops"])}
+    dom = max(kern, key=lambda k: kern[k][0])
+    d_us, d_bytes, d_flops = kern[dom]
+    achieved = d_bytes / (d_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "kernel_avg_us": round(d_us, 3), "algorithmic_bytes_per_launch": int(d_bytes)}
+    step_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
+    step_flops = alg["shrink_flops"] + alg["expand_flops"]
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if c.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": c.name, "tokens": c.T, "tokens_with_adapter": alg["T_lora"],
+                   "distinct_slots": alg["U"], "slots": c.num_slots, "d_in": c.d_in,
+                   "slice_widths": c.widths, "r_max": r, "mode": args.mode,
+                   "rotated_input_sets": nrot, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels_us": {"lora_prepare_meta": round(meta_us, 3), "lora_shrink": round(shrink_us, 3),
+                       "lora_expand": round(expand_us, 3)},
+        "step": {"algorithmic_bytes": int(step_bytes), "hbm_frac": round(
+            step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_bf16_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+            "host_wall_s": round(t_host, 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

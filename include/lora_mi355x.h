@@ -1,0 +1,188 @@
+/*
+ * lora_mi355x.h -- C ABI of the multi-LoRA batched low-rank delta on MI355X
+ * (gfx950): slot metadata, shrink, expand, and the fused apply.
+ *
+ * For a batch of T tokens, token t names an adapter slot token_slot[t] in
+ * [0, S), or -1 for "no adapter".  The library adds, for every packed output
+ * slice s (column window [offset[s], offset[s] + width[s]) of y),
+ *
+ *     y[t][offset[s] + n] (+)= sum_j u[s][t][j] * B_s[slot][j][n]
+ *     u[s][t][j]           =  scale * slot_scale[slot] * sum_k x[t][k] * A_s[slot][k][j]
+ *
+ * which is y = xW + s*(xA)B of the LoRA forward with the base product xW
+ * already in y (page "多 LoRA 服务：分段矩阵乘与适配器调度", section
+ * "不合并权重，批量计算"), split into a shrink (x -> rank r, kept in fp32) and
+ * an expand (rank r -> output slice) as in page "vLLM 源码完全拆解(十八):多 LoRA
+ * 服务", sections "调用链" and "两个低秩 GEMM:shrink、expand 与 fp32 中转缓冲".
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device addresses; "host" arrays live in host memory
+ *     and are read before the call returns.
+ *   - The caller owns every buffer, device and host.  The library never
+ *     allocates or frees memory, never synchronises, and keeps no pointer after
+ *     a call returns.  All device work is enqueued on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream), so calls are asynchronous.
+ *   - Errors are return codes; nothing is enqueued when a call returns anything
+ *     but LORA_OK, except LORA_ERR_HIP, which reports a failed launch.
+ *   - Element types: x, A, B and y share one dtype, fp32 or bf16; the rank-r
+ *     buffer u is always fp32; scales are fp32.  Accumulation is fp32.  bf16
+ *     outputs are rounded once, to nearest even, when y is stored.
+ *   - Supported shapes: 1 <= S <= 1023, r_max in {8, 16, 32, 64}, d_in and every
+ *     slice width a multiple of 8, 1 <= n_slices <= 8, every device pointer
+ *     16-byte aligned, ldx and ldy multiples of 8.  Offsets are int64.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_INVALID_ARG = 1,       /* null pointer, bad size, misalignment, overlap */
+    LORA_ERR_UNSUPPORTED = 2,       /* dtype, r_max, slot count or slice count not built */
+    LORA_ERR_WORKSPACE = 3,         /* workspace smaller than the *_workspace_bytes value */
+    LORA_ERR_HIP = 4                /* a HIP launch failed (hipGetLastError) */
+} lora_status;
+
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* How segments are computed.  BGMV: every segment on the vector (matrix-vector)
+ * path; SGMV: every segment on the matrix-core tile path (bf16 only; fp32 falls
+ * back to the vector path); AUTO: per segment, by its token count. */
+typedef enum lora_mode { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode;
+
+/* One packed slice of a stacked factor: slot a's matrix starts at
+ * ptr + a * slot_stride elements.  A_s matrices are [d_in][r_max] (row-major,
+ * row stride r_max); B_s matrices are [r_max][width_s] (row stride width_s). */
+typedef struct lora_weight {
+    const void *ptr;
+    int64_t slot_stride;            /* elements between consecutive slots */
+} lora_weight;
+
+/* Slot metadata of one batch (page "vLLM 源码完全拆解(十八):多 LoRA 服务",
+ * section "LoRAKernelMeta:先按槽位排序").  lora_prepare_meta fills the struct on
+ * the host with device pointers into the caller's workspace and enqueues the
+ * kernel that writes the arrays:
+ *   sorted[T]       token indices grouped by slot: -1 first, then slots in
+ *                   ascending order; original order inside a slot (stable)
+ *   seg_slot[S+1]   slot id of each segment in that order, then -1 padding
+ *   seg_count[S+1]  tokens per segment, then 0 padding
+ *   seg_start[S+2]  0, then running sums of seg_count; T past the last segment
+ *   info[4]         num_segments, no_lora (1 when no token has a valid slot,
+ *                   also for T = 0), num_bad (tokens whose id lies outside
+ *                   [-1, S); they are treated as -1), lora_begin (index in
+ *                   `sorted` of the first token with an adapter)
+ * The struct stays valid until its workspace is reused; rebuild it whenever
+ * token_slot changes.  Pass it by pointer to the compute calls; they only read
+ * it, so any number of them may use one lora_meta at the same time. */
+typedef struct lora_meta {
+    int64_t num_tokens;
+    int32_t num_slots;
+    int32_t reserved;
+    int32_t *sorted;
+    int32_t *seg_slot;
+    int32_t *seg_count;
+    int32_t *seg_start;
+    int32_t *info;
+} lora_meta;
+
+/* Bytes of device workspace lora_prepare_meta needs for T tokens and S slots. */
+lora_status lora_meta_workspace_bytes(int64_t num_tokens, int32_t num_slots,
+                                      size_t *bytes);
+
+/* Build the slot metadata of a batch.
+ *   d_token_slot  device int32 [T], slot per token (-1 = none)
+ *   d_ws          device workspace of at least lora_meta_workspace_bytes bytes,
+ *                 16-byte aligned; owned by the caller, overwritten
+ *   out           host struct, filled with pointers into d_ws
+ * Cites page "vLLM 源码完全拆解(十八):多 LoRA 服务", section
+ * "LoRAKernelMeta:先按槽位排序" (stable sort, unique counts, running sum whose
+ * first entry is 0) and the worked example of section "一个完整的走查:两步
+ * decode 里发生了什么".  T = 0 is valid (no_lora = 1). */
+lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t num_tokens,
+                              int32_t num_slots, void *d_ws, size_t ws_bytes,
+                              lora_meta *out, void *stream);
+
+/* Bytes of device workspace lora_shrink needs (split-K partial sums; 0 when
+ * the shape needs none).  No initialisation is required; calls that run at the
+ * same time need workspaces of their own. */
+lora_status lora_shrink_workspace_bytes(int64_t num_tokens, int32_t num_slots,
+                                        int64_t d_in, int32_t n_slices,
+                                        int32_t r_max, lora_dtype dtype,
+                                        lora_mode mode, size_t *bytes);
+
+/* Shrink: u[s][t][j] = scale * slot_scale[slot(t)] * sum_k x[t][k] * A_s[slot(t)][k][j]
+ * for every token t with an adapter and every slice s; rows of tokens without
+ * an adapter are not written.
+ *   meta          metadata from lora_prepare_meta for this batch
+ *   d_x           device [T][ldx] of dtype; the first d_in columns are read
+ *   A             host array of n_slices descriptors (device pointers)
+ *   scale         fp32 multiplier; d_slot_scale: device fp32 [S] or NULL (= 1)
+ *   d_u           device fp32 [n_slices][T][r_max], contiguous
+ *   d_ws          workspace of lora_shrink_workspace_bytes bytes (may be NULL
+ *                 when that size is 0)
+ * Cites page "vLLM 源码完全拆解(十八):多 LoRA 服务", section "两个低秩 GEMM:
+ * shrink、expand 与 fp32 中转缓冲" (the shrink kernel, its scaling argument and
+ * the fp32 buffer laid out [slice][token][rank]). */
+lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx,
+                        int64_t d_in, lora_dtype dtype, int32_t n_slices,
+                        const lora_weight *A, int32_t r_max, float scale,
+                        const float *d_slot_scale, float *d_u, lora_mode mode,
+                        void *d_ws, size_t ws_bytes, void *stream);
+
+/* Expand: for every token t and slice s, columns [offset[s], offset[s]+width[s])
+ * of row t of y become (add_into_y ? y : 0) + sum_j u[s][t][j] * B_s[slot(t)][j][n];
+ * a token without an adapter contributes 0 (its row is left as is when
+ * add_into_y != 0 and its windows are set to 0 otherwise).  Columns outside
+ * every window are never touched.
+ *   d_u           device fp32 [n_slices][T][r_max] from lora_shrink
+ *   B             host array of n_slices descriptors
+ *   width, offset host int64 arrays [n_slices]; windows must not overlap and
+ *                 must lie inside [0, ldy)
+ *   d_y           device [T][ldy] of dtype, updated in place
+ * Cites page "vLLM 源码完全拆解(十八):多 LoRA 服务", section "两个低秩 GEMM:
+ * shrink、expand 与 fp32 中转缓冲" (the expand kernel: per-slice width and start
+ * column, ADD_INPUTS) and section "双流:让 LoRA 与基座前向并行" (rows without an
+ * adapter and a cleared output). */
+lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slices,
+                        const lora_weight *B, const int64_t *width,
+                        const int64_t *offset, int32_t r_max, void *d_y,
+                        int64_t ldy, lora_dtype dtype, int add_into_y,
+                        lora_mode mode, void *stream);
+
+/* Bytes of device workspace lora_apply needs: the fp32 rank-r buffer plus the
+ * shrink workspace.  No initialisation is required. */
+lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
+                                       int64_t d_in, int32_t n_slices,
+                                       int32_t r_max, lora_dtype dtype,
+                                       lora_mode mode, size_t *bytes);
+
+/* Shrink then expand on one stream: the whole delta of one layer, added into
+ * (or stored to) the slices of y.  Arguments as in lora_shrink and lora_expand;
+ * the rank-r buffer lives in d_ws.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
+ * 服务", section "调用链" (add_lora_linear = shrink into an fp32 buffer, then
+ * expand into the output slices). */
+lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx,
+                       int64_t d_in, lora_dtype dtype, int32_t n_slices,
+                       const lora_weight *A, const lora_weight *B,
+                       const int64_t *width, const int64_t *offset,
+                       int32_t r_max, float scale, const float *d_slot_scale,
+                       void *d_y, int64_t ldy, int add_into_y, lora_mode mode,
+                       void *d_ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *lora_status_string(lora_status status);
+
+/* Library version, for the binding's sanity check. */
+int32_t lora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

@@ -1,0 +1,288 @@
+"""Python binding of the MI355X multi-LoRA shrink/expand library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``liblora_mi355x.so`` (C ABI in ``include/lora_mi355x.h``).  PyTorch provides
+device memory and the current HIP stream.  The functions carry the names of the
+C entry points.
+
+There is no fallback: importing this package fails loudly when the built
+library is missing (build it with ``python segmented_gather_rank_amd/build.py``
+or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python segmented_gather_rank_amd/build.py)")
+
+_cdll = C.CDLL(LIB_PATH)
+
+LORA_OK, LORA_ERR_INVALID_ARG, LORA_ERR_UNSUPPORTED, LORA_ERR_WORKSPACE, LORA_ERR_HIP = range(5)
+LORA_F32, LORA_BF16 = 0, 1
+MODES = {"auto": 0, "bgmv": 1, "sgmv": 2}
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {lora_status_string(status)}")
+        self.status = status
+
+
+class lora_weight(C.Structure):
+    _fields_ = [("ptr", C.c_void_p), ("slot_stride", C.c_int64)]
+
+
+class lora_meta(C.Structure):
+    _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("reserved", C.c_int32),
+                ("sorted", C.c_void_p), ("seg_slot", C.c_void_p), ("seg_count", C.c_void_p),
+                ("seg_start", C.c_void_p), ("info", C.c_void_p)]
+
+
+_p, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_decl = {
+    "lora_abi_version": ([], _i32),
+    "lora_status_string": ([_i32], C.c_char_p),
+    "lora_meta_workspace_bytes": ([_i64, _i32, C.POINTER(_sz)], _i32),
+    "lora_prepare_meta": ([_p, _i64, _i32, _p, _sz, C.POINTER(lora_meta), _p], _i32),
+    "lora_shrink_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
+    "lora_shrink": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight), _i32,
+                     C.c_float, _p, _p, _i32, _p, _sz, _p], _i32),
+    "lora_expand": ([C.POINTER(lora_meta), _p, _i32, C.POINTER(lora_weight), C.POINTER(_i64),
+                     C.POINTER(_i64), _i32, _p, _i64, _i32, C.c_int, _i32, _p], _i32),
+    "lora_apply_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
+    "lora_apply": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight),
+                    C.POINTER(lora_weight), C.POINTER(_i64), C.POINTER(_i64), _i32, C.c_float, _p,
+                    _p, _i64, C.c_int, _i32, _p, _sz, _p], _i32),
+}
+
+
+
+class _Exact:
+    """A C function that takes exactly its declared arguments (ctypes itself
+    would silently pass extra ones)."""
+
+    def __init__(self, f):
+        self.f, self.n = f, len(f.argtypes)
+
+    def __call__(self, *args):
+        if len(args) != self.n:
+            raise TypeError(f"{self.f.__name__} takes {self.n} arguments, got {len(args)}")
+        return self.f(*args)
+
+
+class _Lib:
+    def __init__(self, cdll, decl):
+        for name, (args, res) in decl.items():
+            f = getattr(cdll, name)
+            f.argtypes, f.restype = args, res
+            setattr(self, name, _Exact(f))
+
+
+_lib = _Lib(_cdll, _decl)
+
+if _lib.lora_abi_version() != 1:
+    raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
+
+
+def lora_abi_version() -> int:
+    return int(_lib.lora_abi_version())
+
+
+def lora_status_string(status: int) -> str:
+    return _lib.lora_status_string(int(status)).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != LORA_OK:
+        raise LoraError(fn, st)
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LORA_F32
+    if t.dtype == torch.bfloat16:
+        return LORA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _weights(ws, name: str, inner_shape_ok) -> tuple:
+    """Per-slice stacked factors [S][rows][cols] -> lora_weight array.  The
+    matrices must be contiguous; the slot stride is taken from the tensor."""
+    if isinstance(ws, torch.Tensor):
+        ws = [ws]
+    arr = (lora_weight * len(ws))()
+    for i, w in enumerate(ws):
+        if w.dim() != 3 or w.stride(2) != 1 or w.stride(1) != w.shape[2]:
+            raise ValueError(f"{name}[{i}] must be [S][rows][cols] with contiguous matrices")
+        inner_shape_ok(i, w)
+        arr[i].ptr = _dev(w, f"{name}[{i}]")
+        arr[i].slot_stride = w.stride(0)
+    return arr, list(ws)
+
+
+@dataclass
+class LoraMeta:
+    """Slot metadata of one batch on the device (see ``lora_meta`` in the C header).
+
+    ``workspace`` owns the device arrays; keep this object alive while kernels
+    that use it are in flight."""
+    c: lora_meta
+    workspace: torch.Tensor
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.c.num_tokens)
+
+    @property
+    def num_slots(self) -> int:
+        return int(self.c.num_slots)
+
+    def _view(self, ptr, n):
+        off = ptr - self.workspace.data_ptr()
+        return self.workspace[off:off + 4 * n].view(torch.int32)
+
+    def tensors(self) -> dict:
+        """Device int32 views of the metadata arrays."""
+        T, S = self.num_tokens, self.num_slots
+        return dict(sorted=self._view(self.c.sorted, T), seg_slot=self._view(self.c.seg_slot, S + 1),
+                    seg_count=self._view(self.c.seg_count, S + 1),
+                    seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 4))
+
+
+def lora_meta_workspace_bytes(num_tokens: int, num_slots: int) -> int:
+    b = _sz(0)
+    _check("lora_meta_workspace_bytes", _lib.lora_meta_workspace_bytes(num_tokens, num_slots, C.byref(b)))
+    return int(b.value)
+
+
+def lora_prepare_meta(token_slot: torch.Tensor, num_slots: int, workspace: torch.Tensor | None = None,
+                      stream=None) -> LoraMeta:
+    if token_slot.dtype != torch.int32 or token_slot.dim() != 1 or not token_slot.is_contiguous():
+        raise ValueError("token_slot must be a contiguous int32 vector")
+    T = token_slot.shape[0]
+    need = lora_meta_workspace_bytes(T, num_slots)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=token_slot.device)
+    m = lora_meta()
+    st = _lib.lora_prepare_meta(_dev(token_slot, "token_slot") if T else None, T, num_slots,
+                                _dev(workspace, "workspace"), workspace.numel(), C.byref(m), _stream(stream))
+    _check("lora_prepare_meta", st)
+    return LoraMeta(m, workspace)
+
+
+def lora_shrink_workspace_bytes(num_tokens, num_slots, d_in, n_slices, r_max, dtype, mode="auto") -> int:
+    b = _sz(0)
+    dt = dtype if isinstance(dtype, int) else _dtype(torch.empty(0, dtype=dtype))
+    _check("lora_shrink_workspace_bytes",
+           _lib.lora_shrink_workspace_bytes(num_tokens, num_slots, d_in, n_slices, r_max, dt,
+                                            MODES[mode], C.byref(b)))
+    return int(b.value)
+
+
+def lora_apply_workspace_bytes(num_tokens, num_slots, d_in, n_slices, r_max, dtype, mode="auto") -> int:
+    b = _sz(0)
+    dt = dtype if isinstance(dtype, int) else _dtype(torch.empty(0, dtype=dtype))
+    _check("lora_apply_workspace_bytes",
+           _lib.lora_apply_workspace_bytes(num_tokens, num_slots, d_in, n_slices, r_max, dt,
+                                           MODES[mode], C.byref(b)))
+    return int(b.value)
+
+
+def _x_args(x: torch.Tensor):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [T][ldx] with unit column stride")
+    return _dev(x, "x"), x.stride(0), x.shape[1]
+
+
+def lora_shrink(meta: LoraMeta, x: torch.Tensor, A, u: torch.Tensor, scale: float = 1.0,
+                slot_scale: torch.Tensor | None = None, mode: str = "auto",
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """u[s][t][:] = scale * slot_scale[slot] * x[t] @ A[s][slot]; A: list of [S][d_in][r]."""
+    xp, ldx, d_in = _x_args(x)
+    A_arr, A_list = _weights(A, "A", lambda i, w: None)
+    r = A_list[0].shape[2]
+    n = len(A_list)
+    need = lora_shrink_workspace_bytes(meta.num_tokens, meta.num_slots, d_in, n, r, x.dtype, mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ss = None if slot_scale is None else _dev(slot_scale, "slot_scale")
+    st = _lib.lora_shrink(C.byref(meta.c), xp, ldx, d_in, _dtype(x), n, A_arr, r, float(scale), ss,
+                          _dev(u, "u"), MODES[mode], _dev(workspace, "workspace"), workspace.numel(),
+                          _stream(stream))
+    _check("lora_shrink", st)
+    return u
+
+
+def _slices(B_list, offsets):
+    n = len(B_list)
+    width = (C.c_int64 * n)(*[b.shape[2] for b in B_list])
+    offs = (C.c_int64 * n)(*[int(o) for o in offsets])
+    return width, offs
+
+
+def lora_expand(meta: LoraMeta, u: torch.Tensor, B, offsets, y: torch.Tensor, add: bool = True,
+                mode: str = "auto", stream=None) -> torch.Tensor:
+    """y[t][off_s:off_s+w_s] (+)= u[s][t] @ B[s][slot]; B: list of [S][r][w_s]."""
+    B_arr, B_list = _weights(B, "B", lambda i, w: None)
+    width, offs = _slices(B_list, offsets)
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be [T][ldy] with unit column stride")
+    st = _lib.lora_expand(C.byref(meta.c), _dev(u, "u"), len(B_list), B_arr, width, offs,
+                          B_list[0].shape[1], _dev(y, "y"), y.stride(0), _dtype(y), int(bool(add)),
+                          MODES[mode], _stream(stream))
+    _check("lora_expand", st)
+    return y
+
+
+def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
+               slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto",
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Shrink then expand into the slices of y (the whole delta of one layer)."""
+    xp, ldx, d_in = _x_args(x)
+    A_arr, A_list = _weights(A, "A", lambda i, w: None)
+    B_arr, B_list = _weights(B, "B", lambda i, w: None)
+    width, offs = _slices(B_list, offsets)
+    r = A_list[0].shape[2]
+    n = len(A_list)
+    if len(B_list) != n:
+        raise ValueError("A and B need one entry per slice")
+    need = lora_apply_workspace_bytes(meta.num_tokens, meta.num_slots, d_in, n, r, x.dtype, mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be [T][ldy] with unit column stride")
+    ss = None if slot_scale is None else _dev(slot_scale, "slot_scale")
+    if y.dtype != x.dtype:
+        raise TypeError("x and y must share one dtype")
+    st = _lib.lora_apply(C.byref(meta.c), xp, ldx, d_in, _dtype(x), n, A_arr, B_arr, width, offs, r,
+                         float(scale), ss, _dev(y, "y"), y.stride(0), int(bool(add)),
+                         MODES[mode], _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check("lora_apply", st)
+    return y
+
+
+__all__ = ["lora_abi_version", "lora_status_string", "lora_meta_workspace_bytes", "lora_prepare_meta",
+           "lora_shrink_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_workspace_bytes",
+           "lora_apply", "LoraMeta", "LoraError", "lora_weight", "lora_meta", "LIB_PATH"]

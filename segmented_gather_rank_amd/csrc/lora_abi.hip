@@ -1,0 +1,280 @@
+// lora_abi.hip -- the extern "C" entry points declared in include/lora_mi355x.h:
+// argument checks, workspace layout, dispatch to the kernels.  Every check that
+// can fail runs before the first HIP call, so a rejected call enqueues nothing.
+#include <algorithm>
+#include <cstdlib>
+
+#include "../../include/lora_mi355x.h"
+#include "lora_host.h"
+
+namespace lora {
+
+// Segment length (tokens) from which a bf16 segment takes the matrix-core
+// path in AUTO mode.  Tuning override: LORA_MFMA_MIN_TOKENS_SHRINK / _EXPAND,
+// read once.
+static int env_int(const char *name, int dflt) {
+  const char *v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+int shrink_mma_min_default() {
+  static const int v = env_int("LORA_MFMA_MIN_TOKENS_SHRINK", 16);
+  return v;
+}
+int expand_mma_min_default() {
+  static const int v = env_int("LORA_MFMA_MIN_TOKENS_EXPAND", 16);
+  return v;
+}
+
+}  // namespace lora
+
+using namespace lora;
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool rank_ok(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
+bool dtype_ok(lora_dtype d) { return d == LORA_F32 || d == LORA_BF16; }
+bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV || m == LORA_MODE_SGMV; }
+size_t esize(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
+
+struct MetaLayout {
+  size_t sorted, seg_slot, seg_count, seg_start, info, total;
+};
+MetaLayout meta_layout(int64_t T, int32_t S) {
+  MetaLayout L{};
+  size_t off = 0;
+  L.sorted = off;
+  off += align256(sizeof(int32_t) * (size_t)std::max<int64_t>(T, 1));
+  L.seg_slot = off;
+  off += align256(sizeof(int32_t) * (size_t)(S + 1));
+  L.seg_count = off;
+  off += align256(sizeof(int32_t) * (size_t)(S + 1));
+  L.seg_start = off;
+  off += align256(sizeof(int32_t) * (size_t)(S + 2));
+  L.info = off;
+  off += align256(sizeof(int32_t) * 4);
+  L.total = off;
+  return L;
+}
+
+lora_status check_meta(const lora_meta *m) {
+  if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots)
+    return LORA_ERR_INVALID_ARG;
+  if (!m->sorted || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info)
+    return LORA_ERR_INVALID_ARG;
+  return LORA_OK;
+}
+
+MetaView view_of(const lora_meta *m) {
+  MetaView v;
+  v.sorted = m->sorted;
+  v.seg_slot = m->seg_slot;
+  v.seg_count = m->seg_count;
+  v.seg_start = m->seg_start;
+  v.info = m->info;
+  v.T = m->num_tokens;
+  v.S = m->num_slots;
+  return v;
+}
+
+lora_status check_shrink_args(const lora_meta *meta, const void *x, int64_t ldx, int64_t d_in,
+                              lora_dtype dtype, int32_t n_slices, const lora_weight *A,
+                              int32_t r_max, const float *slot_scale, const float *u,
+                              lora_mode mode) {
+  lora_status st = check_meta(meta);
+  if (st != LORA_OK) return st;
+  if (!dtype_ok(dtype) || !mode_ok(mode)) return LORA_ERR_UNSUPPORTED;
+  if (n_slices < 1 || n_slices > kMaxSlices) return LORA_ERR_UNSUPPORTED;
+  if (!rank_ok(r_max)) return LORA_ERR_UNSUPPORTED;
+  if (d_in < 8 || d_in % 8 || ldx < d_in || ldx % 8) return LORA_ERR_INVALID_ARG;
+  // with no tokens nothing is read or written, so empty buffers may be null
+  const bool empty = meta->num_tokens == 0;
+  if (!A || (!empty && (!x || !u)) || !aligned16(x) || !aligned16(u)) return LORA_ERR_INVALID_ARG;
+  if (slot_scale && (reinterpret_cast<uintptr_t>(slot_scale) & 3u)) return LORA_ERR_INVALID_ARG;
+  for (int s = 0; s < n_slices; ++s) {
+    if (!A[s].ptr || !aligned16(A[s].ptr) || A[s].slot_stride % 8 ||
+        A[s].slot_stride < d_in * r_max)
+      return LORA_ERR_INVALID_ARG;
+  }
+  return LORA_OK;
+}
+
+lora_status check_expand_args(const lora_meta *meta, const float *u, int32_t n_slices,
+                              const lora_weight *B, const int64_t *width, const int64_t *offset,
+                              int32_t r_max, const void *y, int64_t ldy, lora_dtype dtype,
+                              lora_mode mode) {
+  lora_status st = check_meta(meta);
+  if (st != LORA_OK) return st;
+  if (!dtype_ok(dtype) || !mode_ok(mode)) return LORA_ERR_UNSUPPORTED;
+  if (n_slices < 1 || n_slices > kMaxSlices) return LORA_ERR_UNSUPPORTED;
+  if (!rank_ok(r_max)) return LORA_ERR_UNSUPPORTED;
+  const bool empty = meta->num_tokens == 0;
+  if (!B || !width || !offset || (!empty && (!u || !y)) || !aligned16(u) || !aligned16(y))
+    return LORA_ERR_INVALID_ARG;
+  if (ldy < 8 || ldy % 8) return LORA_ERR_INVALID_ARG;
+  for (int s = 0; s < n_slices; ++s) {
+    const int64_t w = width[s], o = offset[s];
+    if (w < 8 || w % 8 || o < 0 || o % 8 || o + w > ldy) return LORA_ERR_INVALID_ARG;
+    if (!B[s].ptr || !aligned16(B[s].ptr) || B[s].slot_stride % 8 || B[s].slot_stride < r_max * w)
+      return LORA_ERR_INVALID_ARG;
+    for (int q = 0; q < s; ++q) {
+      if (o < offset[q] + width[q] && offset[q] < o + w) return LORA_ERR_INVALID_ARG;
+    }
+  }
+  return LORA_OK;
+}
+
+void unpack(const lora_weight *W, int32_t n, const void **ptrs, int64_t *strides) {
+  for (int s = 0; s < n; ++s) {
+    ptrs[s] = W[s].ptr;
+    strides[s] = W[s].slot_stride;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_abi_version(void) { return kAbiVersion; }
+
+const char *lora_status_string(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARG: return "LORA_ERR_INVALID_ARG";
+    case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED";
+    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP";
+  }
+  return "LORA_ERR_UNKNOWN";
+}
+
+lora_status lora_meta_workspace_bytes(int64_t T, int32_t S, size_t *bytes) {
+  if (!bytes || T < 0 || T > INT32_MAX || S < 1) return LORA_ERR_INVALID_ARG;
+  if (S > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+  *bytes = meta_layout(T, S).total;
+  return LORA_OK;
+}
+
+lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S, void *d_ws,
+                              size_t ws_bytes, lora_meta *out, void *stream) {
+  if (!out || T < 0 || T > INT32_MAX || S < 1 || !d_ws || !aligned16(d_ws))
+    return LORA_ERR_INVALID_ARG;
+  if (S > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+  if (T > 0 && !d_token_slot) return LORA_ERR_INVALID_ARG;
+  const MetaLayout L = meta_layout(T, S);
+  if (ws_bytes < L.total) return LORA_ERR_WORKSPACE;
+  char *base = static_cast<char *>(d_ws);
+  out->num_tokens = T;
+  out->num_slots = S;
+  out->reserved = 0;
+  out->sorted = reinterpret_cast<int32_t *>(base + L.sorted);
+  out->seg_slot = reinterpret_cast<int32_t *>(base + L.seg_slot);
+  out->seg_count = reinterpret_cast<int32_t *>(base + L.seg_count);
+  out->seg_start = reinterpret_cast<int32_t *>(base + L.seg_start);
+  out->info = reinterpret_cast<int32_t *>(base + L.info);
+  const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->seg_slot, out->seg_count,
+                                   out->seg_start, out->info, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_shrink_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32_t n_slices,
+                                        int32_t r_max, lora_dtype dtype, lora_mode mode,
+                                        size_t *bytes) {
+  if (!bytes || T < 0 || T > INT32_MAX || S < 1 || d_in < 8 || d_in % 8)
+    return LORA_ERR_INVALID_ARG;
+  if (S > kMaxSlots || n_slices < 1 || n_slices > kMaxSlices || !rank_ok(r_max) ||
+      !dtype_ok(dtype) || !mode_ok(mode))
+    return LORA_ERR_UNSUPPORTED;
+  const ShrinkConfig c = plan_shrink(T, S, d_in, r_max, dtype == LORA_BF16, (int)mode);
+  *bytes = shrink_ws_bytes(c, T, n_slices, r_max);
+  return LORA_OK;
+}
+
+lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in,
+                        lora_dtype dtype, int32_t n_slices, const lora_weight *A, int32_t r_max,
+                        float scale, const float *d_slot_scale, float *d_u, lora_mode mode,
+                        void *d_ws, size_t ws_bytes, void *stream) {
+  lora_status st = check_shrink_args(meta, d_x, ldx, d_in, dtype, n_slices, A, r_max,
+                                     d_slot_scale, d_u, mode);
+  if (st != LORA_OK) return st;
+  size_t need = 0;
+  st = lora_shrink_workspace_bytes(meta->num_tokens, meta->num_slots, d_in, n_slices, r_max,
+                                   dtype, mode, &need);
+  if (st != LORA_OK) return st;
+  if (ws_bytes < need || (need && (!d_ws || !aligned16(d_ws)))) return LORA_ERR_WORKSPACE;
+  const void *ptrs[kMaxSlices];
+  int64_t strides[kMaxSlices];
+  unpack(A, n_slices, ptrs, strides);
+  const hipError_t e =
+      launch_shrink(view_of(meta), d_x, ldx, d_in, dtype == LORA_BF16, n_slices, ptrs, strides,
+                    r_max, scale, d_slot_scale, d_u, (int)mode, d_ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slices,
+                        const lora_weight *B, const int64_t *width, const int64_t *offset,
+                        int32_t r_max, void *d_y, int64_t ldy, lora_dtype dtype, int add_into_y,
+                        lora_mode mode, void *stream) {
+  const lora_status st =
+      check_expand_args(meta, d_u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
+  if (st != LORA_OK) return st;
+  const void *ptrs[kMaxSlices];
+  int64_t strides[kMaxSlices];
+  unpack(B, n_slices, ptrs, strides);
+  const hipError_t e = launch_expand(view_of(meta), d_u, n_slices, ptrs, strides, width, offset,
+                                     r_max, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32_t n_slices,
+                                       int32_t r_max, lora_dtype dtype, lora_mode mode,
+                                       size_t *bytes) {
+  size_t sh = 0;
+  const lora_status st = lora_shrink_workspace_bytes(T, S, d_in, n_slices, r_max, dtype, mode, &sh);
+  if (st != LORA_OK) return st;
+  *bytes = align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max) + sh;
+  return LORA_OK;
+}
+
+lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in,
+                       lora_dtype dtype, int32_t n_slices, const lora_weight *A,
+                       const lora_weight *B, const int64_t *width, const int64_t *offset,
+                       int32_t r_max, float scale, const float *d_slot_scale, void *d_y,
+                       int64_t ldy, int add_into_y, lora_mode mode, void *d_ws, size_t ws_bytes,
+                       void *stream) {
+  if (!meta) return LORA_ERR_INVALID_ARG;
+  size_t need = 0;
+  lora_status st = lora_apply_workspace_bytes(meta->num_tokens, meta->num_slots, d_in, n_slices,
+                                              r_max, dtype, mode, &need);
+  if (st != LORA_OK) return st;
+  if (ws_bytes < need || (need > 0 && (!d_ws || !aligned16(d_ws)))) return LORA_ERR_WORKSPACE;
+  // the rank-r buffer sits at the start of the workspace
+  float *u = static_cast<float *>(d_ws);
+  st = check_shrink_args(meta, d_x, ldx, d_in, dtype, n_slices, A, r_max, d_slot_scale, u, mode);
+  if (st != LORA_OK) return st;
+  st = check_expand_args(meta, u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
+  if (st != LORA_OK) return st;
+  const size_t ubytes = align256(sizeof(float) * (size_t)n_slices * (size_t)meta->num_tokens *
+                                 (size_t)r_max);
+  void *sh_ws = static_cast<char *>(d_ws) + ubytes;
+  const void *aptr[kMaxSlices], *bptr[kMaxSlices];
+  int64_t astr[kMaxSlices], bstr[kMaxSlices];
+  unpack(A, n_slices, aptr, astr);
+  unpack(B, n_slices, bptr, bstr);
+  const MetaView mv = view_of(meta);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
+                               scale, d_slot_scale, u, (int)mode, sh_ws, s);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  e = launch_expand(mv, u, n_slices, bptr, bstr, width, offset, r_max, d_y, ldy,
+                    dtype == LORA_BF16, add_into_y, (int)mode, s);
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// lora_host.h -- host-side launchers shared by the library's translation
+// units.  Internal to the library (not part of the ABI).
+#pragma once
+
+#include "lora_common.h"
+
+namespace lora {
+
+struct ShrinkConfig {
+  int use_mma_mode, mfma_min;
+  int kc, kch;  // k-chunk length and count, shared by both paths
+  int grid;
+};
+
+ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);
+size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32_t R);
+int shrink_mma_min_default();
+int expand_mma_min_default();
+
+hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
+                       int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
+                       int32_t *info, hipStream_t stream);
+
+hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
+                         int32_t n_slices, const void *const *A, const int64_t *a_stride,
+                         int32_t R, float scale, const float *slot_scale, float *u, int mode,
+                         void *ws, hipStream_t stream);
+hipError_t launch_expand(const MetaView &meta, const float *u, int32_t n_slices,
+                         const void *const *B, const int64_t *b_stride, const int64_t *width,
+                         const int64_t *offset, int32_t R, void *y, int64_t ldy, bool bf16,
+                         int add, int mode, hipStream_t stream);
+
+}  // namespace lora

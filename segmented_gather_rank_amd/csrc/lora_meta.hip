@@ -1,0 +1,145 @@
+// lora_meta.hip -- slot metadata of a batch on one workgroup of 16 waves.
+//
+// Page "vLLM 源码完全拆解(十八):多 LoRA 服务", section "LoRAKernelMeta:先按槽位
+// 排序": tokens are stably sorted by slot id (no-adapter id -1 first), the
+// distinct ids are listed in ascending order with their token counts, and the
+// start offsets are the running sum of the counts with a leading 0.
+//
+// Design (gfx950, wave64): keys are slot+1 in [0, S].
+//   1. histogram of keys with LDS integer atomics (order-free, exact);
+//   2. one wave scans the key counts (ballot + popcount for the segment index,
+//      a wave prefix sum for the offsets) and writes the segment arrays;
+//   3. a stable scatter over chunks of 1024 tokens in batch order: inside a
+//      wave, lanes holding the same key find each other with one ballot per
+//      key bit (a wave-wide match), and a lane's rank among equal keys is the
+//      popcount of the matching lanes below it; the per-(wave, key) counts are
+//      prefix-summed across the 16 waves in wave order, so equal keys keep
+//      batch order across waves and across chunks.
+#include "lora_host.h"
+
+namespace lora {
+
+constexpr int kMetaThreads = 1024;
+constexpr int kMetaWaves = kMetaThreads / kWave;
+
+__global__ __launch_bounds__(kMetaThreads) void meta_kernel(
+    const int32_t *__restrict__ token_slot, int64_t T, int32_t S,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ seg_slot,
+    int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
+    int32_t *__restrict__ info) {
+  extern __shared__ int32_t lds[];
+  const int K = S + 1;                      // number of keys
+  int32_t *cnt = lds;                       // [K] tokens per key
+  int32_t *next = lds + K;                  // [K] next free position per key
+  int32_t *wcnt = lds + 2 * K;              // [16][K] per-wave counts, then offsets
+  __shared__ int32_t nbad;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+
+  for (int i = tid; i < K; i += kMetaThreads) cnt[i] = 0;
+  for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) wcnt[i] = 0;
+  if (tid == 0) nbad = 0;
+  __syncthreads();
+
+  // 1. histogram
+  int mybad = 0;
+  for (int64_t t = tid; t < T; t += kMetaThreads) {
+    const int v = token_slot[t];
+    const bool ok = v >= -1 && v < S;
+    mybad += ok ? 0 : 1;
+    atomicAdd(&cnt[ok ? v + 1 : 0], 1);
+  }
+  if (mybad) atomicAdd(&nbad, mybad);
+  __syncthreads();
+
+  // 2. segments: one wave walks the keys in ascending order
+  if (wave == 0) {
+    int seg_base = 0, pos_base = 0;
+    for (int k0 = 0; k0 < K; k0 += kWave) {
+      const int k = k0 + lane;
+      const int c = k < K ? cnt[k] : 0;
+      const uint64_t present = __ballot(c > 0);
+      const int seg = seg_base + __popcll(present & lanemask_lt());
+      const int incl = wave_inclusive_scan(c);
+      const int start = pos_base + incl - c;
+      if (k < K) next[k] = start;
+      if (c > 0) {
+        seg_slot[seg] = k - 1;
+        seg_count[seg] = c;
+        seg_start[seg] = start;
+      }
+      seg_base += __popcll(present);
+      pos_base += __shfl(incl, kWave - 1, kWave);
+    }
+    // padding past the last segment, and the closing offset
+    for (int i = seg_base + lane; i < K; i += kWave) {
+      seg_slot[i] = -1;
+      seg_count[i] = 0;
+    }
+    for (int i = seg_base + lane; i < K + 1; i += kWave) seg_start[i] = (int32_t)T;
+    if (lane == 0) {
+      info[0] = seg_base;
+      info[1] = (T - cnt[0] == 0) ? 1 : 0;
+      info[2] = nbad;
+      info[3] = cnt[0];
+    }
+  }
+  __syncthreads();
+
+  // 3. stable scatter, 1024 tokens per pass in batch order
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  for (int64_t base = 0; base < T; base += kMetaThreads) {
+    const int64_t t = base + tid;
+    const bool valid = t < T;
+    int key = 0;
+    if (valid) {
+      const int v = token_slot[t];
+      key = (v >= -1 && v < S) ? v + 1 : 0;
+    }
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t ones = __ballot(valid && ((key >> b) & 1));
+      same &= ((key >> b) & 1) ? ones : ~ones;
+    }
+    const int rank = __popcll(same & lanemask_lt());
+    const bool leader = valid && rank == 0;
+    if (leader) wcnt[wave * K + key] = __popcll(same);
+    __syncthreads();
+    for (int k = tid; k < K; k += kMetaThreads) {
+      int run = next[k];
+      for (int w = 0; w < kMetaWaves; ++w) {
+        const int c = wcnt[w * K + k];
+        wcnt[w * K + k] = run;
+        run += c;
+      }
+      next[k] = run;
+    }
+    __syncthreads();
+    if (valid) sorted[wcnt[wave * K + key] + rank] = (int32_t)t;
+    __syncthreads();
+    for (int k = tid; k < kMetaWaves * K; k += kMetaThreads) wcnt[k] = 0;
+    __syncthreads();
+  }
+}
+
+size_t meta_lds_bytes(int32_t S) { return sizeof(int32_t) * (size_t)(S + 1) * (2 + kMetaWaves); }
+
+hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
+                       int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
+                       int32_t *info, hipStream_t stream) {
+  const size_t lds = meta_lds_bytes(S);
+  if (lds > 65536) {
+    // large slot counts need more than the default 64 KB of dynamic LDS
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), lds, stream,
+                     token_slot, T, S, sorted, seg_slot, seg_count, seg_start, info);
+  return hipGetLastError();
+}
+
+}  // namespace lora

@@ -1,0 +1,146 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+public header declares, and rejects bad arguments with the documented status
+before any HIP call (so these calls never touch a device)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_mi355x.h")
+
+import segmented_gather_rank_amd as L  # noqa: E402  (fails loudly if the library is not built)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w \t\*]*?\b(lora_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert len(names) >= 9, names
+    lib = C.CDLL(L.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert L.lora_abi_version() == 1
+    assert L.lora_status_string(0) == "LORA_OK"
+    assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
+    assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    assert L.lora_meta_workspace_bytes(256, 32) >= 4 * (256 + 33 + 33 + 34 + 4)
+    assert L.lora_meta_workspace_bytes(0, 1) > 0
+    import torch
+    b_apply = L.lora_apply_workspace_bytes(4096, 128, 14336, 1, 64, torch.bfloat16)
+    assert b_apply >= 4 * 4096 * 64
+    b2 = L.lora_shrink_workspace_bytes(256, 32, 4096, 1, 16, torch.bfloat16)
+    assert b2 > 0 and b2 % 256 == 0
+
+
+_buf = (C.c_uint8 * (1 << 16))()
+_base = (C.addressof(_buf) + 255) // 256 * 256
+
+
+def _ptr(off=0):
+    return C.c_void_p(_base + off)
+
+
+def _call(name, *args):
+    return getattr(L._lib, name)(*args)
+
+
+def test_meta_rejections():
+    m = L.lora_meta()
+    sz = C.c_size_t(0)
+    assert _call("lora_meta_workspace_bytes", -1, 4, C.byref(sz)) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_meta_workspace_bytes", 10, 0, C.byref(sz)) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_meta_workspace_bytes", 10, 1024, C.byref(sz)) == L.LORA_ERR_UNSUPPORTED
+    assert _call("lora_prepare_meta", _ptr(), 10, 4, _ptr(), 16, C.byref(m), None) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_prepare_meta", None, 10, 4, _ptr(), 1 << 15, C.byref(m), None) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_prepare_meta", _ptr(), 10, 4, _ptr(4), 1 << 15, C.byref(m), None) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_prepare_meta", _ptr(), 10, 4, _ptr(), 1 << 15, None, None) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_prepare_meta", _ptr(), 10, 2000, _ptr(), 1 << 15, C.byref(m), None) == L.LORA_ERR_UNSUPPORTED
+
+
+def _meta(T=16, S=4):
+    m = L.lora_meta()
+    m.num_tokens, m.num_slots = T, S
+    for f in ("sorted", "seg_slot", "seg_count", "seg_start", "info"):
+        setattr(m, f, _base)
+    return m
+
+
+def _w(n, stride):
+    arr = (L.lora_weight * n)()
+    for i in range(n):
+        arr[i].ptr, arr[i].slot_stride = _base, stride
+    return arr
+
+
+def _shrink(meta=None, ldx=64, d_in=64, dtype=1, n=1, A=None, r=16, ss=None, u=None, mode=0,
+            ws=None, ws_bytes=1 << 15):
+    meta = meta if meta is not None else _meta()
+    A = A if A is not None else _w(n, d_in * r)
+    return _call("lora_shrink", C.byref(meta), _ptr(), ldx, d_in, dtype, n, A, r, C.c_float(1.0),
+                 ss, u if u is not None else _ptr(), mode, ws if ws is not None else _ptr(), ws_bytes, None)
+
+
+def test_shrink_rejections():
+    assert _shrink(r=12) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(r=128) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(n=0, A=_w(1, 64 * 16)) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(n=9, A=_w(9, 64 * 16)) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(dtype=7) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(mode=5) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(d_in=60, ldx=64, A=_w(1, 64 * 16)) == L.LORA_ERR_INVALID_ARG
+    assert _shrink(ldx=60) == L.LORA_ERR_INVALID_ARG
+    assert _shrink(A=_w(1, 64 * 16 - 8)) == L.LORA_ERR_INVALID_ARG        # slots overlap
+    assert _shrink(u=_ptr(8)) == L.LORA_ERR_INVALID_ARG                    # misaligned
+    bad = _meta()
+    bad.seg_start = None
+    assert _shrink(meta=bad) == L.LORA_ERR_INVALID_ARG
+    assert _shrink(meta=_meta(T=-1)) == L.LORA_ERR_INVALID_ARG
+    # workspace too small: ask for one that needs partial sums
+    need = L.lora_shrink_workspace_bytes(4096, 32, 4096, 1, 16, 1)
+    assert need > 0
+    assert _shrink(meta=_meta(T=4096, S=32), d_in=4096, ldx=4096, A=_w(1, 4096 * 16),
+                   ws_bytes=need - 1) == L.LORA_ERR_WORKSPACE
+
+
+def _expand(n=2, widths=(64, 32), offsets=(0, 64), r=16, ldy=96, B=None, y=None, mode=0):
+    wd = (C.c_int64 * n)(*widths[:n])
+    of = (C.c_int64 * n)(*offsets[:n])
+    B = B if B is not None else (L.lora_weight * n)(*[L.lora_weight(_base, r * w) for w in widths[:n]])
+    return _call("lora_expand", C.byref(_meta()), _ptr(), n, B, wd, of, r,
+                 y if y is not None else _ptr(), ldy, 1, 1, mode, None)
+
+
+def test_expand_rejections():
+    assert _expand(offsets=(0, 32)) == L.LORA_ERR_INVALID_ARG        # windows overlap
+    assert _expand(ldy=90) == L.LORA_ERR_INVALID_ARG                 # ldy not a multiple of 8
+    assert _expand(ldy=88) == L.LORA_ERR_INVALID_ARG                 # window past ldy
+    assert _expand(widths=(64, 30)) == L.LORA_ERR_INVALID_ARG        # width not a multiple of 8
+    assert _expand(offsets=(0, 68)) == L.LORA_ERR_INVALID_ARG        # offset not a multiple of 8
+    assert _expand(r=24) == L.LORA_ERR_UNSUPPORTED
+    assert _expand(y=_ptr(2)) == L.LORA_ERR_INVALID_ARG
+    thin = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64), L.lora_weight(_base, 16 * 32 - 8))
+    assert _expand(B=thin) == L.LORA_ERR_INVALID_ARG
+
+
+def test_apply_rejections():
+    n = 1
+    A, B = _w(1, 64 * 16), _w(1, 16 * 64)
+    wd, of = (C.c_int64 * 1)(64), (C.c_int64 * 1)(0)
+    args = lambda ws, ws_bytes: (C.byref(_meta()), _ptr(), 64, 64, 1, n, A, B, wd, of, 16,
+                                 C.c_float(1.0), None, _ptr(), 64, 1, 0, ws, ws_bytes, None)
+    assert _call("lora_apply", *args(_ptr(), 16)) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_apply", None, *args(_ptr(), 1 << 15)[1:]) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_apply", *args(None, 1 << 15)) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_apply", *args(_ptr(8), 1 << 15)) == L.LORA_ERR_WORKSPACE

@@ -1,0 +1,81 @@
+"""GPU slot metadata against the oracle: bit-exact on every array."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import segmented_gather_rank_amd as lib
+    return lib
+
+
+def _meta_check(L, ts_np, S, label):
+    print(f"[meta] {label} T={ts_np.shape[0]} S={S}", flush=True)
+    ts = torch.from_numpy(np.ascontiguousarray(ts_np, np.int32)).cuda()
+    m = L.lora_prepare_meta(ts, S)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in m.tensors().items()}
+    ref = oracle.prepare_meta(ts_np, S)
+    assert np.array_equal(got["sorted"], ref.sorted), label
+    assert np.array_equal(got["seg_slot"], ref.seg_slot), label
+    assert np.array_equal(got["seg_count"], ref.seg_count), label
+    assert np.array_equal(got["seg_start"], ref.seg_start), label
+    info = got["info"]
+    assert info[0] == ref.num_segments and info[1] == ref.no_lora and info[2] == ref.num_bad, label
+    assert info[3] == int(np.sum((ts_np < -1) | (ts_np >= S) | (ts_np == -1))), label
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_meta_workloads(L, k):
+    c = W.config(k)
+    _meta_check(L, c.token_slot, c.num_slots, c.name)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+PATTERNS = ["uniform", "all_none", "one_slot", "sorted", "reversed", "zipf", "bad_ids"]
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025, 5000, 20000])
+@pytest.mark.parametrize("S", [1, 2, 33, 1023])
+@pytest.mark.parametrize("pattern", PATTERNS)
+def test_meta_random(L, T, S, pattern):
+    rng = _rng(T * 7919 + S * 31 + PATTERNS.index(pattern))
+    if pattern == "uniform":
+        ts = rng.integers(-1, S, T)
+    elif pattern == "all_none":
+        ts = np.full(T, -1)
+    elif pattern == "one_slot":
+        ts = np.full(T, S - 1)
+    elif pattern == "sorted":
+        ts = np.sort(rng.integers(-1, S, T))
+    elif pattern == "reversed":
+        ts = np.sort(rng.integers(-1, S, T))[::-1]
+    elif pattern == "zipf":
+        ts = W.zipf_slots(rng, T, S, 1.1) if T else np.zeros(0, int)
+    else:
+        ts = rng.integers(-3, S + 3, T)
+    _meta_check(L, ts.astype(np.int32), S, f"{pattern}")
+
+
+def test_meta_repeatable_and_workspace_reuse(L):
+    """Same input twice into one workspace: identical arrays (no stale state)."""
+    rng = _rng(5)
+    ts_np = rng.integers(-1, 64, 4000).astype(np.int32)
+    ts = torch.from_numpy(ts_np).cuda()
+    ws = torch.full((L.lora_meta_workspace_bytes(4000, 64),), 0x5A, dtype=torch.uint8, device="cuda")
+    a = {k: v.clone() for k, v in L.lora_prepare_meta(ts, 64, workspace=ws).tensors().items()}
+    other = torch.from_numpy(rng.integers(-1, 64, 4000).astype(np.int32)).cuda()
+    L.lora_prepare_meta(other, 64, workspace=ws)
+    b = L.lora_prepare_meta(ts, 64, workspace=ws).tensors()
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
