@@ -70,6 +70,7 @@ typedef struct lora_weight {
  * kernel that writes the arrays:
  *   sorted[T]       token indices grouped by slot: -1 first, then slots in
  *                   ascending order; original order inside a slot (stable)
+ *   sorted_slot[T]  slot of each entry of `sorted` (-1 for no adapter)
  *   seg_slot[S+1]   slot id of each segment in that order, then -1 padding
  *   seg_count[S+1]  tokens per segment, then 0 padding
  *   seg_start[S+2]  0, then running sums of seg_count; T past the last segment
@@ -85,6 +86,7 @@ typedef struct lora_meta {
     int32_t num_slots;
     int32_t reserved;
     int32_t *sorted;
+    int32_t *sorted_slot;
     int32_t *seg_slot;
     int32_t *seg_count;
     int32_t *seg_start;
@@ -164,7 +166,10 @@ lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
 
 /* Shrink then expand on one stream: the whole delta of one layer, added into
  * (or stored to) the slices of y.  Arguments as in lora_shrink and lora_expand;
- * the rank-r buffer lives in d_ws.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
+ * the rank-r buffer lives in d_ws.  Decode-shaped calls (few tokens per slot,
+ * small per-token factors, mode AUTO or BGMV) run as one fused kernel that keeps
+ * each token's rank-r vector on chip; the others run the shrink and expand
+ * kernels.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
  * 服务", section "调用链" (add_lora_linear = shrink into an fp32 buffer, then
  * expand into the output slices). */
 lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx,

@@ -44,7 +44,8 @@ class lora_weight(C.Structure):
 
 class lora_meta(C.Structure):
     _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("reserved", C.c_int32),
-                ("sorted", C.c_void_p), ("seg_slot", C.c_void_p), ("seg_count", C.c_void_p),
+                ("sorted", C.c_void_p), ("sorted_slot", C.c_void_p), ("seg_slot", C.c_void_p),
+                ("seg_count", C.c_void_p),
                 ("seg_start", C.c_void_p), ("info", C.c_void_p)]
 
 
@@ -166,7 +167,8 @@ class LoraMeta:
     def tensors(self) -> dict:
         """Device int32 views of the metadata arrays."""
         T, S = self.num_tokens, self.num_slots
-        return dict(sorted=self._view(self.c.sorted, T), seg_slot=self._view(self.c.seg_slot, S + 1),
+        return dict(sorted=self._view(self.c.sorted, T), sorted_slot=self._view(self.c.sorted_slot, T),
+                    seg_slot=self._view(self.c.seg_slot, S + 1),
                     seg_count=self._view(self.c.seg_count, S + 1),
                     seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 4))
 

@@ -26,6 +26,12 @@ int expand_mma_min_default() {
   static const int v = env_int("LORA_MFMA_MIN_TOKENS_EXPAND", 16);
   return v;
 }
+// Tuning override: LORA_DISABLE_FUSED_BGMV=1 keeps lora_apply on the
+// shrink + expand kernels even where the fused kernel fits.
+bool fused_disabled() {
+  static const bool v = env_int("LORA_DISABLE_FUSED_BGMV", 0) > 0;
+  return v;
+}
 
 }  // namespace lora
 
@@ -43,12 +49,14 @@ bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV ||
 size_t esize(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
 
 struct MetaLayout {
-  size_t sorted, seg_slot, seg_count, seg_start, info, total;
+  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, total;
 };
 MetaLayout meta_layout(int64_t T, int32_t S) {
   MetaLayout L{};
   size_t off = 0;
   L.sorted = off;
+  off += align256(sizeof(int32_t) * (size_t)std::max<int64_t>(T, 1));
+  L.sorted_slot = off;
   off += align256(sizeof(int32_t) * (size_t)std::max<int64_t>(T, 1));
   L.seg_slot = off;
   off += align256(sizeof(int32_t) * (size_t)(S + 1));
@@ -65,7 +73,7 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
 lora_status check_meta(const lora_meta *m) {
   if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots)
     return LORA_ERR_INVALID_ARG;
-  if (!m->sorted || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info)
+  if (!m->sorted || !m->sorted_slot || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info)
     return LORA_ERR_INVALID_ARG;
   return LORA_OK;
 }
@@ -73,6 +81,7 @@ lora_status check_meta(const lora_meta *m) {
 MetaView view_of(const lora_meta *m) {
   MetaView v;
   v.sorted = m->sorted;
+  v.sorted_slot = m->sorted_slot;
   v.seg_slot = m->seg_slot;
   v.seg_count = m->seg_count;
   v.seg_start = m->seg_start;
@@ -173,11 +182,13 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
   out->num_slots = S;
   out->reserved = 0;
   out->sorted = reinterpret_cast<int32_t *>(base + L.sorted);
+  out->sorted_slot = reinterpret_cast<int32_t *>(base + L.sorted_slot);
   out->seg_slot = reinterpret_cast<int32_t *>(base + L.seg_slot);
   out->seg_count = reinterpret_cast<int32_t *>(base + L.seg_count);
   out->seg_start = reinterpret_cast<int32_t *>(base + L.seg_start);
   out->info = reinterpret_cast<int32_t *>(base + L.info);
-  const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->seg_slot, out->seg_count,
+  const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->sorted_slot, out->seg_slot,
+                                   out->seg_count,
                                    out->seg_start, out->info, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -269,6 +280,13 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   unpack(B, n_slices, bptr, bstr);
   const MetaView mv = view_of(meta);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
+                                     r_max, dtype == LORA_BF16, (int)mode)) {
+    const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
+                                     bptr, bstr, width, offset, r_max, scale, d_slot_scale, d_y,
+                                     ldy, add_into_y, s);
+    return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
   hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
                                scale, d_slot_scale, u, (int)mode, sh_ws, s);
   if (e != hipSuccess) return LORA_ERR_HIP;

@@ -91,6 +91,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 
 struct MetaView {
   const int32_t *sorted;
+  const int32_t *sorted_slot;
   const int32_t *seg_slot;
   const int32_t *seg_count;
   const int32_t *seg_start;

@@ -18,7 +18,7 @@ int shrink_mma_min_default();
 int expand_mma_min_default();
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
-                       int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
+                       int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
                        int32_t *info, hipStream_t stream);
 
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
@@ -29,5 +29,16 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
                          const int64_t *offset, int32_t R, void *y, int64_t ldy, bool bf16,
                          int add, int mode, hipStream_t stream);
+
+// The fused BGMV kernel (one workgroup per token) serves this call?  Decided
+// from host-known sizes only.
+bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64_t *width, int32_t R,
+               bool bf16, int mode);
+hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
+                       int32_t n_slices, const void *const *A, const int64_t *a_stride,
+                       const void *const *B, const int64_t *b_stride, const int64_t *width,
+                       const int64_t *offset, int32_t R, float scale, const float *slot_scale,
+                       void *y, int64_t ldy, int add, hipStream_t stream);
+bool fused_disabled();
 
 }  // namespace lora

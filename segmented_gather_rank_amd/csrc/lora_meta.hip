@@ -24,7 +24,8 @@ constexpr int kMetaWaves = kMetaThreads / kWave;
 
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const int32_t *__restrict__ token_slot, int64_t T, int32_t S,
-    int32_t *__restrict__ sorted, int32_t *__restrict__ seg_slot,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ sorted_slot,
+    int32_t *__restrict__ seg_slot,
     int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
     int32_t *__restrict__ info) {
   extern __shared__ int32_t lds[];
@@ -118,7 +119,11 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       next[k] = run;
     }
     __syncthreads();
-    if (valid) sorted[wcnt[wave * K + key] + rank] = (int32_t)t;
+    if (valid) {
+      const int dst = wcnt[wave * K + key] + rank;
+      sorted[dst] = (int32_t)t;
+      sorted_slot[dst] = key - 1;
+    }
     __syncthreads();
     for (int k = tid; k < kMetaWaves * K; k += kMetaThreads) wcnt[k] = 0;
     __syncthreads();
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
 size_t meta_lds_bytes(int32_t S) { return sizeof(int32_t) * (size_t)(S + 1) * (2 + kMetaWaves); }
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
-                       int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
+                       int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
                        int32_t *info, hipStream_t stream) {
   const size_t lds = meta_lds_bytes(S);
   if (lds > 65536) {
@@ -138,7 +143,7 @@ hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), lds, stream,
-                     token_slot, T, S, sorted, seg_slot, seg_count, seg_start, info);
+                     token_slot, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info);
   return hipGetLastError();
 }
 

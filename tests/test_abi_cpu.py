@@ -72,7 +72,7 @@ def test_meta_rejections():
 def _meta(T=16, S=4):
     m = L.lora_meta()
     m.num_tokens, m.num_slots = T, S
-    for f in ("sorted", "seg_slot", "seg_count", "seg_start", "info"):
+    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info"):
         setattr(m, f, _base)
     return m
 

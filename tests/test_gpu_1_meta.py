@@ -23,6 +23,8 @@ def _meta_check(L, ts_np, S, label):
     got = {k: v.cpu().numpy() for k, v in m.tensors().items()}
     ref = oracle.prepare_meta(ts_np, S)
     assert np.array_equal(got["sorted"], ref.sorted), label
+    eff = np.where((ts_np >= -1) & (ts_np < S), ts_np, -1)
+    assert np.array_equal(got["sorted_slot"], eff[ref.sorted]), label
     assert np.array_equal(got["seg_slot"], ref.seg_slot), label
     assert np.array_equal(got["seg_count"], ref.seg_count), label
     assert np.array_equal(got["seg_start"], ref.seg_start), label
