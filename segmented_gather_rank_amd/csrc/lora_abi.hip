@@ -223,7 +223,8 @@ lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx, int
   unpack(A, n_slices, ptrs, strides);
   const hipError_t e =
       launch_shrink(view_of(meta), d_x, ldx, d_in, dtype == LORA_BF16, n_slices, ptrs, strides,
-                    r_max, scale, d_slot_scale, d_u, (int)mode, d_ws, static_cast<hipStream_t>(stream));
+                    r_max, scale, d_slot_scale, d_u, (int)mode, d_ws, false, nullptr,
+                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -237,9 +238,9 @@ lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slice
   const void *ptrs[kMaxSlices];
   int64_t strides[kMaxSlices];
   unpack(B, n_slices, ptrs, strides);
-  const hipError_t e = launch_expand(view_of(meta), d_u, n_slices, ptrs, strides, width, offset,
-                                     r_max, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode,
-                                     static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_expand(view_of(meta), d_u, 0, 1, n_slices, ptrs, strides, width,
+                                     offset, r_max, d_y, ldy, dtype == LORA_BF16, add_into_y,
+                                     (int)mode, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -287,11 +288,15 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
                                      ldy, add_into_y, s);
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
+  int kch = 1;
   hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
-                               scale, d_slot_scale, u, (int)mode, sh_ws, s);
+                               scale, d_slot_scale, u, (int)mode, sh_ws, true, &kch, s);
   if (e != hipSuccess) return LORA_ERR_HIP;
-  e = launch_expand(mv, u, n_slices, bptr, bstr, width, offset, r_max, d_y, ldy,
-                    dtype == LORA_BF16, add_into_y, (int)mode, s);
+  // the rank-r rows are in sorted order; with a split d_in they are still the
+  // partial sums, which the expand adds
+  const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
+  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, r_max, d_y,
+                    ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

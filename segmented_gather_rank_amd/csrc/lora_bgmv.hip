@@ -58,55 +58,17 @@ struct BgmvParams {
   int32_t add;
 };
 
-template <int CTRL>
-__device__ __forceinline__ float bdpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the lanes of a wave that share (lane mod JO).
-template <int JO>
-__device__ __forceinline__ float lanes_sum(float v) {
-  if constexpr (JO < 2) v += bdpp<0x121>(v);   // row_ror:1
-  if constexpr (JO < 4) v += bdpp<0x122>(v);   // row_ror:2
-  if constexpr (JO < 8) v += bdpp<0x124>(v);   // row_ror:4
-  v += bdpp<0x128>(v);                         // row_ror:8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Sum over aligned groups of `jg` adjacent lanes (jg in 1..16, a power of 2).
 __device__ __forceinline__ float group_sum(float v, int jg) {
-  if (jg >= 2) v += bdpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  if (jg >= 4) v += bdpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  if (jg >= 8) v += bdpp<0x141>(v);   // row_half_mirror
-  if (jg >= 16) v += bdpp<0x140>(v);  // row_mirror
+  if (jg >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (jg >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (jg >= 8) v += dpp_f32<0x141>(v);   // row_half_mirror
+  if (jg >= 16) v += dpp_f32<0x140>(v);  // row_mirror
   return v;
 }
 
-// 8 consecutive elements as raw words (bf16: 4 words, fp32: 8 words)
-template <typename E> struct Raw8;
-template <> struct Raw8<uint16_t> {
-  u32x4 w;
-  __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const u32x4 *>(p); }
-  __device__ __forceinline__ float operator[](int i) const {
-    return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
-  }
-};
-template <> struct Raw8<float> {
-  f32x4 a, b;
-  __device__ __forceinline__ void load(const float *p) {
-    a = *reinterpret_cast<const f32x4 *>(p);
-    b = *reinterpret_cast<const f32x4 *>(p + 4);
-  }
-  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
-};
-
 __device__ __forceinline__ int slice_of_oct(const BgmvParams &p, int o) {
-  int s = 0;
-  while (s + 1 < p.n_slices && p.oct_base[s + 1] <= o) ++s;
-  return s;
+  return last_le(p.oct_base, p.n_slices, o);
 }
 
 template <typename E, int R>
@@ -130,14 +92,14 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   if (pos >= T) return;
   const int64_t t = p.meta.sorted[pos];
   const int slot = p.meta.sorted_slot[pos];
-  const int n_oct = p.oct_base[p.n_slices];
+  const int n_oct = pick(p.oct_base, p.n_slices);
   E *y = reinterpret_cast<E *>(p.y) + t * p.ldy;
 
   if (slot < 0) {  // store mode, no adapter: the windows become 0
     const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int o = tid; o < n_oct; o += kBThreads) {
       const int s = slice_of_oct(p, o);
-      store8(y + p.offset[s] + 8 * (o - p.oct_base[s]), z);
+      store8(y + pick(p.offset, s) + 8 * (o - pick(p.oct_base, s)), z);
     }
     return;
   }
@@ -161,14 +123,14 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   Raw8<E> b[NB];
   if (o0 < n_oct) {
     s0 = slice_of_oct(p, o0);
-    n00 = 8 * (int64_t)(o0 - p.oct_base[s0]);
-    Bb0 = reinterpret_cast<const E *>(p.B[s0]) + (int64_t)slot * p.b_stride[s0] + n00;
+    n00 = 8 * (int64_t)(o0 - pick(p.oct_base, s0));
+    Bb0 = reinterpret_cast<const E *>(pick(p.B, s0)) + (int64_t)slot * pick(p.b_stride, s0) + n00;
 #pragma unroll
     for (int jj = 0; jj < NB; ++jj)
-      if (jj < rj) b[jj].load(Bb0 + (int64_t)(g * rj + jj) * p.width[s0]);
+      if (jj < rj) b[jj].load(Bb0 + (int64_t)(g * rj + jj) * pick(p.width, s0));
   }
   float yv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (o0 < n_oct && g == 0 && p.add) load8(y + p.offset[s0] + n00, yv);
+  if (o0 < n_oct && g == 0 && p.add) load8(y + pick(p.offset, s0) + n00, yv);
   const E *xr = reinterpret_cast<const E *>(p.x) + t * p.ldx;
   for (int o = tid; o < p.d_in / 8; o += kBThreads) {
     Raw8<E> v;
@@ -186,7 +148,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   const int jo = tid % JO;
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   for (int s = 0; s < p.n_slices; ++s) {
-    const E *As = reinterpret_cast<const E *>(p.A[s]) + (int64_t)slot * p.a_stride[s];
+    const E *As = reinterpret_cast<const E *>(pick(p.A, s)) + (int64_t)slot * pick(p.a_stride, s);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int64_t base = 0; base < nel; base += (int64_t)8 * kBThreads * NA) {
       if (s > 0 || base > 0) {
@@ -213,7 +175,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = lanes_sum<JO>(acc[i]);
+    for (int i = 0; i < 8; ++i) acc[i] = wave_sum_mod<JO>(acc[i]);
     if (lane < JO) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) red[wave][8 * jo + i] = acc[i];
@@ -235,11 +197,11 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
     const E *Bb = Bb0;
     if (it > 0) {
       s = slice_of_oct(p, o);
-      n0 = 8 * (int64_t)(o - p.oct_base[s]);
-      Bb = reinterpret_cast<const E *>(p.B[s]) + (int64_t)slot * p.b_stride[s] + n0;
-      if (g == 0 && p.add) load8(y + p.offset[s] + n0, yv);
+      n0 = 8 * (int64_t)(o - pick(p.oct_base, s));
+      Bb = reinterpret_cast<const E *>(pick(p.B, s)) + (int64_t)slot * pick(p.b_stride, s) + n0;
+      if (g == 0 && p.add) load8(y + pick(p.offset, s) + n0, yv);
     }
-    const int64_t w = p.width[s];
+    const int64_t w = pick(p.width, s);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int jb = 0; jb < rj; jb += NB) {
       if (it > 0 || jb > 0) {
@@ -261,7 +223,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
     if (g == 0) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) yv[c] += acc[c];
-      store8(y + p.offset[s] + n0, yv);
+      store8(y + pick(p.offset, s) + n0, yv);
     }
   }
 }

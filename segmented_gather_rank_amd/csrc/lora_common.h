@@ -87,6 +87,29 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// ---------------------------------------------------------------- parameter arrays
+
+// a[i] for a small array held in a kernel's by-value parameter block.  Indexing
+// it with a runtime value would make the compiler copy the whole block to
+// scratch memory; an unrolled select keeps it in the kernarg segment.
+template <typename T, int N>
+__device__ __forceinline__ T pick(const T (&a)[N], int i) {
+  T v = a[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) v = (i == k) ? a[k] : v;
+  return v;
+}
+
+// Index of the last entry of prefix[0..n) (non-decreasing, prefix[0] = 0)
+// that is <= v.
+template <int N>
+__device__ __forceinline__ int last_le(const int32_t (&prefix)[N], int n, int v) {
+  int s = 0;
+#pragma unroll
+  for (int k = 1; k < N; ++k) s = (k < n && prefix[k] <= v) ? k : s;
+  return s;
+}
+
 // ---------------------------------------------------------------- metadata view
 
 struct MetaView {
@@ -103,16 +126,139 @@ struct MetaView {
 // ---------------------------------------------------------------- work lists
 //
 // Both compute kernels walk a list of items derived in-kernel from the segment
-// counts: every segment with an adapter is cut into m-chunks of `mc` tokens
-// (mc depends on the path the segment takes), and every m-chunk into `per_chunk`
-// items (k-chunks for the shrink, slice x n-tile pairs for the expand).  The
-// per-segment item counts are prefix-summed in LDS by one wave, and each item
-// is located by binary search over that prefix.
+// table: every segment is cut into m-chunks (the chunk size depends on the path
+// the segment takes) and every m-chunk into items (k-chunks for the shrink,
+// slice x n-tile pairs for the expand).  The segment table is copied to LDS
+// with one memory round trip (every entry's load is issued before any wait),
+// one wave prefix-sums the item counts, and each item is located by binary
+// search over that prefix.
 
-struct SegPlan {
-  int32_t item_end[kMaxSlots + 2];   // inclusive prefix of items per segment
-  int32_t nseg;
-  int32_t total_items;
+struct SegTable {
+  int32_t *count, *slot, *start;  // LDS copies of seg_count, seg_slot, seg_start
+  int32_t *item_end;              // inclusive prefix of items per used segment
+  int32_t *scal;                  // [0] used segments, [1] first used, [2] items, [3] nseg
+};
+
+// LDS bytes of a segment table for S slots
+__host__ __device__ constexpr size_t seg_table_bytes(int S) {
+  return sizeof(int32_t) * (4 * (size_t)(S + 2) + 4);
+}
+
+__device__ __forceinline__ SegTable seg_table_at(void *lds, int S) {
+  int32_t *b = reinterpret_cast<int32_t *>(lds);
+  const int n = S + 2;
+  return SegTable{b, b + n, b + 2 * n, b + 3 * n, b + 4 * n};
+}
+
+// Fill the table.  Segments from index `first` on are used, where first = 1
+// when skip_none is set and the leading segment is the no-adapter one; used
+// segment i gets items_of(count, slot) items.  Ends with a barrier.
+template <typename F>
+__device__ __forceinline__ void build_items(const MetaView &m, SegTable tb, bool skip_none, F items_of) {
+  const int K = m.S + 1;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    tb.count[i] = m.seg_count[i];
+    tb.slot[i] = m.seg_slot[i];
+    tb.start[i] = m.seg_start[i];
+  }
+  if (threadIdx.x == 0) tb.scal[3] = m.info[0];
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int nseg = tb.scal[3];
+    const int first = (skip_none && nseg > 0 && tb.slot[0] == -1) ? 1 : 0;
+    const int nl = nseg - first;
+    int base = 0;
+    for (int i0 = 0; i0 < nl; i0 += kWave) {
+      const int i = i0 + lane;
+      const int items = i < nl ? items_of(tb.count[first + i], tb.slot[first + i]) : 0;
+      const int incl = wave_inclusive_scan(items);
+      if (i < nl) tb.item_end[i] = base + incl;
+      base += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      tb.scal[0] = nl;
+      tb.scal[1] = first;
+      tb.scal[2] = base;
+    }
+  }
+  __syncthreads();
+}
+
+// Used-segment index of an item (binary search over the item prefix).
+__device__ __forceinline__ int find_item_segment(SegTable tb, int item) {
+  int lo = 0, hi = tb.scal[0] - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (tb.item_end[mid] > item) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- LDS transposing read
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// MFMA 16x16x32 operand from a row-major bf16 tile in LDS: this lane (column
+// n = lane % 16 of a 16-column block starting at `col0`) receives
+// tile[row0 + e][col0 + n] for e = 0..7, where `ld` is the row stride in
+// elements.  Two gfx950 transposing reads: inside each group of 16 lanes,
+// lane 4e + c names 4 consecutive elements (row row0 + e, columns col0 + 4c ..
+// + 3) and lane i receives element i % 4 of the chunks named by lanes 4e + i/4,
+// e = 0..3, i.e. column col0 + i of rows row0 .. row0 + 3.
+__device__ __forceinline__ bf16x8 lds_col8(const uint16_t *tile, int ld, int row0, int col0) {
+  const int l = threadIdx.x % 16;
+  const uint16_t *a = tile + (row0 + l / 4) * ld + col0 + 4 * (l % 4);
+  typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a)));
+  const u32x2 hi =
+      __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a + 4 * ld)));
+  const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------- DPP helpers
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the lanes of a wave that share (lane mod JO), JO in {1,2,4,8}: DPP
+// row rotations inside each 16-lane row, then the gfx950 permlane16 and
+// permlane32 swaps across rows.
+template <int JO>
+__device__ __forceinline__ float wave_sum_mod(float v) {
+  if constexpr (JO < 2) v += dpp_f32<0x121>(v);  // row_ror:1
+  if constexpr (JO < 4) v += dpp_f32<0x122>(v);  // row_ror:2
+  if constexpr (JO < 8) v += dpp_f32<0x124>(v);  // row_ror:4
+  v += dpp_f32<0x128>(v);                        // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 8 consecutive elements held as raw words (bf16: 4 words, fp32: 8 words),
+// widened to fp32 on use.
+template <typename E> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ void zero() { w = u32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ float operator[](int i) const {
+    return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const f32x4 *>(p);
+    b = *reinterpret_cast<const f32x4 *>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
 }  // namespace lora

@@ -21,11 +21,15 @@ hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t 
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
                        int32_t *info, hipStream_t stream);
 
+// for_apply: u is written in sorted-position order, and with a split d_in the
+// partial sums are left in ws for the expand to add (kch_out reports the split)
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
                          int32_t R, float scale, const float *slot_scale, float *u, int mode,
-                         void *ws, hipStream_t stream);
-hipError_t launch_expand(const MetaView &meta, const float *u, int32_t n_slices,
+                         void *ws, bool for_apply, int *kch_out, hipStream_t stream);
+// u_mode 0: u [n_slices][T][R] in token order; 1: the same in sorted-position
+// order; 2: kch partial sums [kch][n_slices][T][R] in sorted-position order
+hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
                          const int64_t *offset, int32_t R, void *y, int64_t ldy, bool bf16,
                          int add, int mode, hipStream_t stream);

@@ -8,7 +8,8 @@
 // matrix-vector product per token) suits decode, SGMV (one small matrix product
 // per segment) suits prefill.
 //
-// One kernel, a grid-stride loop over work items.  Every segment with an adapter
+// One kernel, a grid-stride loop over work items; every item issues the loads
+// that do not depend on each other before it waits for any of them.  Every segment with an adapter
 // is cut into m-chunks (8 tokens on the vector path, 64 on the matrix-core
 // path) and every m-chunk into k-chunks of d_in.  Each item reads its slot's A
 // chunk once and applies it to all tokens of the m-chunk, so a slot's A is read
@@ -22,9 +23,11 @@
 //    fixed-order sum over the 4 waves in LDS.
 //  * matrix-core path (the SGMV form; bf16 segments of at least `mfma_min`
 //    tokens): v_mfma_f32_16x16x32_bf16, 16 token rows per wave; the A tile
-//    (128 k x n_slices*r) is transposed into LDS with an XOR swizzle so both the
-//    transposing writes and the 16-byte operand reads are bank-conflict free;
-//    x fragments go straight from global memory to registers.
+//    (128 k x n_slices*r) is stored row-major in LDS with 16-byte writes and
+//    read back as MFMA operands with the gfx950 transposing LDS read; rows are
+//    padded so the 4 rows of a read group fall in distinct banks; the next
+//    tile's loads are in flight while one tile is multiplied; x fragments go
+//    straight from global memory to registers.
 //
 // With more than one k-chunk, items write scaled fp32 partial sums indexed by
 // sorted position, and a second small kernel adds them in k-chunk order into u:
@@ -38,9 +41,10 @@ constexpr int kShrinkThreads = 256;
 constexpr int kVecRows = 8;        // tokens per vector m-chunk
 constexpr int kVecSub = 1024;      // k per staged x sub-chunk on the vector path
 constexpr int kMmaRows = 64;       // tokens per matrix-core m-chunk (4 waves x 16)
-constexpr int kMmaKT = 128;        // k per staged A tile on the matrix-core path
+constexpr int kMmaKT = 128;        // k per A tile on the matrix-core path
 constexpr int kMmaCols = 128;      // n_slices*r columns per pass (8 MFMA blocks)
-constexpr int kAtStride = kMmaKT + 8;  // bf16 elements per transposed A row
+constexpr int kAlStride = kMmaCols + 16;  // bf16 elements per LDS row of the A tile
+constexpr int kMmaOct = kMmaKT * kMmaCols / 8 / kShrinkThreads;  // A octets per thread per tile
 
 struct ShrinkParams {
   MetaView meta;
@@ -51,23 +55,24 @@ struct ShrinkParams {
   int32_t n_slices;
   float scale;
   const float *slot_scale;
-  // kch == 1: out is u [n_slices][T][R] in token order; otherwise the partial
-  // sums [kch][n_slices][T][R] in sorted-position order
+  // kch == 1: out is u [n_slices][T][R], rows in token order, or in sorted-
+  // position order when u_sorted is set; kch > 1: out holds the partial sums
+  // [kch][n_slices][T][R] in sorted-position order
   float *out;
+  int32_t u_sorted;
   int32_t use_mma_mode;  // 0 = never, 1 = by segment length, 2 = always
   int32_t mfma_min;
   int32_t kc, kch;       // k-chunk length (a multiple of 128) and count
 };
 
 struct ShrinkLds {
-  SegPlan plan;
   union {
     struct {
       float xs[kVecRows][kVecSub];
       float red[4][kVecRows][64];
     } vec;
     struct {
-      uint16_t at[kMmaCols][kAtStride];
+      uint16_t al[kMmaKT * kAlStride];  // A tile, row k, column slice*R + j
     } mma;
   };
 };
@@ -76,51 +81,14 @@ __device__ __forceinline__ bool seg_takes_mma(const ShrinkParams &p, int count) 
   return p.use_mma_mode == 2 || (p.use_mma_mode == 1 && count >= p.mfma_min);
 }
 
-// One wave fills the per-segment item prefix of the adapter segments.
-__device__ void build_plan(const ShrinkParams &p, SegPlan &plan) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    const int nseg = p.meta.info[0];
-    const int first = (nseg > 0 && p.meta.seg_slot[0] == -1) ? 1 : 0;
-    const int nl = nseg - first;
-    int item_base = 0;
-    for (int i0 = 0; i0 < nl; i0 += kWave) {
-      const int i = i0 + lane;
-      int items = 0;
-      if (i < nl) {
-        const int c = p.meta.seg_count[first + i];
-        const int mc = seg_takes_mma(p, c) ? kMmaRows : kVecRows;
-        items = ((c + mc - 1) / mc) * p.kch;
-      }
-      const int ii = wave_inclusive_scan(items);
-      if (i < nl) plan.item_end[i] = item_base + ii;
-      item_base += __shfl(ii, kWave - 1, kWave);
-    }
-    if (lane == 0) {
-      plan.nseg = nl;
-      plan.total_items = item_base;
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ int find_segment(const SegPlan &plan, int item) {
-  int lo = 0, hi = plan.nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (plan.item_end[mid] > item) hi = mid; else lo = mid + 1;
-  }
-  return lo;
-}
-
-// Store one result of row `mm` of an m-chunk: straight into u (token order)
-// when d_in is not split, else into the partial sums (sorted-position order).
+// Store one result: into u (token or sorted order) when d_in is not split,
+// else into the partial sums of k-chunk kc.
 __device__ __forceinline__ void put(const ShrinkParams &p, int R, int s, int64_t pos, int j,
                                    int kc, float v) {
   const int64_t T = p.meta.T;
   if (p.kch == 1) {
-    const int64_t t = p.meta.sorted[pos];
-    p.out[((int64_t)s * T + t) * R + j] = v;
+    const int64_t row = p.u_sorted ? pos : (int64_t)p.meta.sorted[pos];
+    p.out[((int64_t)s * T + row) * R + j] = v;
   } else {
     p.out[(((int64_t)kc * p.n_slices + s) * T + pos) * R + j] = v;
   }
@@ -128,29 +96,11 @@ __device__ __forceinline__ void put(const ShrinkParams &p, int R, int s, int64_t
 
 // ------------------------------------------------------------------ vector path
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the lanes of a wave that share (lane mod JO): DPP row rotations
-// inside each 16-lane row, then the permlane16 / permlane32 swaps across rows.
-template <int JO>
-__device__ __forceinline__ float reduce_lanes(float v) {
-  if constexpr (JO < 2) v += dpp<0x121>(v);   // row_ror:1
-  if constexpr (JO < 4) v += dpp<0x122>(v);   // row_ror:2
-  if constexpr (JO < 8) v += dpp<0x124>(v);   // row_ror:4
-  v += dpp<0x128>(v);                         // row_ror:8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <typename E, int R>
-__device__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_t pos0,
+__device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_t pos0,
                          int rows, int kc, float sc) {
-  constexpr int JO = R / 8;  // rank octets per k row
+  constexpr int JO = R / 8;                       // rank octets per k row
+  constexpr int VA = sizeof(E) == 2 ? 8 : 4;      // A loads in flight per thread
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int64_t k0 = (int64_t)kc * p.kc;
   const int klen = (int)min((int64_t)p.kc, p.d_in - k0);
@@ -167,6 +117,16 @@ __device__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_
 
     for (int sub = 0; sub < klen; sub += kVecSub) {
       const int slen = min(kVecSub, klen - sub);
+      const int nel = slen * R;
+      const E *Ab = reinterpret_cast<const E *>(pick(p.A, s)) + (int64_t)slot * pick(p.a_stride, s) +
+                    (k0 + sub) * R;
+      // the first A batch goes out before the x rows are staged
+      Raw8<E> a[VA];
+#pragma unroll
+      for (int q = 0; q < VA; ++q) {
+        const int e = 8 * (tid + kShrinkThreads * q);
+        if (e < nel) a[q].load(Ab + e);
+      }
       if (staged != sub) {
         __syncthreads();  // earlier readers of xs are done
         const int oct = slen / 8;
@@ -175,31 +135,39 @@ __device__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_
           const int64_t t = p.meta.sorted[pos0 + row];
           float v[8];
           load8(x + t * p.ldx + k0 + sub + 8 * c, v);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) lds.vec.xs[row][8 * c + i] = v[i];
+          *reinterpret_cast<f32x4 *>(&lds.vec.xs[row][8 * c]) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4 *>(&lds.vec.xs[row][8 * c + 4]) = f32x4{v[4], v[5], v[6], v[7]};
         }
         __syncthreads();
         staged = sub;
       }
-      const E *Ab = reinterpret_cast<const E *>(p.A[s]) + (int64_t)slot * p.a_stride[s] +
-                    (k0 + sub) * R;
-      const int nel = slen * R;
-      for (int e = 8 * tid; e < nel; e += 8 * kShrinkThreads) {
-        float a[8];
-        load8(Ab + e, a);
-        const int k = e / R;
+      for (int base = 0; base < nel; base += 8 * kShrinkThreads * VA) {
+        if (base > 0) {
 #pragma unroll
-        for (int m = 0; m < kVecRows; ++m) {
-          const float xv = lds.vec.xs[m][k];   // rows >= `rows` hold stale data, never stored
+          for (int q = 0; q < VA; ++q) {
+            const int e = base + 8 * (tid + kShrinkThreads * q);
+            if (e < nel) a[q].load(Ab + e);
+          }
+        }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[m][i] = fmaf(xv, a[i], acc[m][i]);
+        for (int q = 0; q < VA; ++q) {
+          const int e = base + 8 * (tid + kShrinkThreads * q);
+          if (e < nel) {
+            const int k = e / R;
+#pragma unroll
+            for (int m = 0; m < kVecRows; ++m) {
+              const float xv = lds.vec.xs[m][k];  // rows >= `rows` are stale, never stored
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[m][i] = fmaf(xv, a[q][i], acc[m][i]);
+            }
+          }
         }
       }
     }
 #pragma unroll
     for (int m = 0; m < kVecRows; ++m)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[m][i] = reduce_lanes<JO>(acc[m][i]);
+      for (int i = 0; i < 8; ++i) acc[m][i] = wave_sum_mod<JO>(acc[m][i]);
     if (lane < JO) {
 #pragma unroll
       for (int m = 0; m < kVecRows; ++m)
@@ -219,15 +187,67 @@ __device__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_
 
 // ------------------------------------------------------------- matrix-core path
 
+// One A tile (kMmaKT k rows x ns*R columns) and this lane's x fragments, held
+// in registers between their load and their use.
+struct MmaTile {
+  u32x4 a[kMmaOct];
+  bf16x8 xf[4];
+};
+
 template <int R>
-__device__ void mma_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_t pos0,
+__device__ __forceinline__ void mma_load_tile(const ShrinkParams &p, MmaTile &tl, int slot, int s0,
+                                              int ns, int64_t kt, int klen, int64_t trow, int g) {
+  const int tid = threadIdx.x;
+  const int per_slice = kMmaKT * R / 8;
+#pragma unroll
+  for (int q = 0; q < kMmaOct; ++q) {
+    const int idx = tid + kShrinkThreads * q;
+    const int sl = idx / per_slice;
+    const int e = 8 * (idx - sl * per_slice);
+    const int k = e / R, j0 = e % R;
+    if (sl < ns && k < klen) {
+      tl.a[q] = *reinterpret_cast<const u32x4 *>(
+          reinterpret_cast<const uint16_t *>(pick(p.A, s0 + sl)) + (int64_t)slot * pick(p.a_stride, s0 + sl) +
+          (kt + k) * R + j0);
+    } else {
+      tl.a[q] = u32x4{0, 0, 0, 0};
+    }
+  }
+  const uint16_t *x = reinterpret_cast<const uint16_t *>(p.x);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int kk = 32 * g + 8 * c;
+    if (trow >= 0 && kk < klen) {
+      tl.xf[c] = *reinterpret_cast<const bf16x8 *>(x + trow * p.ldx + kt + kk);
+    } else {
+      tl.xf[c] = bf16x8{};
+    }
+  }
+}
+
+// Row-major store of a tile's A octets (16-byte LDS writes).
+template <int R>
+__device__ __forceinline__ void mma_store_al(ShrinkLds &lds, const MmaTile &tl, int ns) {
+  const int tid = threadIdx.x;
+  const int per_slice = kMmaKT * R / 8;
+#pragma unroll
+  for (int q = 0; q < kMmaOct; ++q) {
+    const int idx = tid + kShrinkThreads * q;
+    const int sl = idx / per_slice;
+    if (sl < ns) {
+      const int e = 8 * (idx - sl * per_slice);
+      *reinterpret_cast<u32x4 *>(&lds.mma.al[(e / R) * kAlStride + sl * R + e % R]) = tl.a[q];
+    }
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void mma_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_t pos0,
                          int rows, int kc, float sc) {
   constexpr int SG = kMmaCols / R;  // slices per pass
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int64_t kbeg = (int64_t)kc * p.kc;
   const int64_t kend = min(p.d_in, kbeg + p.kc);
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(p.x);
-
   const int mrow = lane % 16, g = lane / 16;
   const int row = 16 * wave + mrow;               // this lane's operand row
   const int64_t trow = row < rows ? (int64_t)p.meta.sorted[pos0 + row] : -1;
@@ -239,47 +259,18 @@ __device__ void mma_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_
 #pragma unroll
     for (int b = 0; b < kMmaCols / 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // software pipeline: the next tile's loads are in flight while this one
+    // is multiplied
+    MmaTile tl;
+    mma_load_tile<R>(p, tl, slot, s0, ns, kbeg, (int)min((int64_t)kMmaKT, kend - kbeg), trow, g);
     for (int64_t kt = kbeg; kt < kend; kt += kMmaKT) {
-      const int klen = (int)min((int64_t)kMmaKT, kend - kt);
-      __syncthreads();  // previous tile fully consumed
-      // A tile -> LDS, transposed: at[n][k ^ swz(n)], n = slice*R + j
-      const int per_slice = kMmaKT * R / 8;
-      for (int idx = tid; idx < ns * per_slice; idx += kShrinkThreads) {
-        const int sl = idx / per_slice;
-        const int e = 8 * (idx - sl * per_slice);
-        const int k = e / R, j0 = e % R;
-        const int n0 = sl * R + j0;
-        uint16_t v[8];
-        if (k < klen) {
-          const uint16_t *src = reinterpret_cast<const uint16_t *>(p.A[s0 + sl]) +
-                                (int64_t)slot * p.a_stride[s0 + sl] + (kt + k) * R + j0;
-          u32x4 w = *reinterpret_cast<const u32x4 *>(src);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] = (uint16_t)(w[i] & 0xffffu);
-            v[2 * i + 1] = (uint16_t)(w[i] >> 16);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = 0;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int n = n0 + i;
-          lds.mma.at[n][k ^ (((n >> 3) & 7) << 3)] = v[i];
-        }
-      }
-      // x fragments: lane (mrow, g) holds x[trow][kt + 32g + 8c + e], c = 0..3
+      __syncthreads();  // the previous tile's LDS reads are done
+      mma_store_al<R>(lds, tl, ns);
       bf16x8 xf[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kk = 32 * g + 8 * c;
-        if (trow >= 0 && kk < klen) {
-          xf[c] = *reinterpret_cast<const bf16x8 *>(x + trow * p.ldx + kt + kk);
-        } else {
-          xf[c] = bf16x8{};
-        }
-      }
+      for (int c = 0; c < 4; ++c) xf[c] = tl.xf[c];
+      const int64_t kn = kt + kMmaKT;
+      if (kn < kend) mma_load_tile<R>(p, tl, slot, s0, ns, kn, (int)min((int64_t)kMmaKT, kend - kn), trow, g);
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -287,9 +278,7 @@ __device__ void mma_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_
 #pragma unroll
         for (int b = 0; b < kMmaCols / 16; ++b) {
           if (b < nblk) {
-            const int n = 16 * b + mrow;
-            const bf16x8 bv =
-                *reinterpret_cast<const bf16x8 *>(&lds.mma.at[n][kk ^ (((n >> 3) & 7) << 3)]);
+            const bf16x8 bv = lds_col8(lds.mma.al, kAlStride, kk, 16 * b);
             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[c], bv, acc[b], 0, 0, 0);
           }
         }
@@ -316,25 +305,30 @@ __device__ void mma_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_
 template <typename E, int R>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
   __shared__ ShrinkLds lds;
-  build_plan(p, lds.plan);
-  const int nseg_first = (p.meta.info[0] > 0 && p.meta.seg_slot[0] == -1) ? 1 : 0;
-  for (int item = blockIdx.x; item < lds.plan.total_items; item += gridDim.x) {
+  extern __shared__ __align__(16) unsigned char shrink_dyn[];
+  const SegTable tb = seg_table_at(shrink_dyn, p.meta.S);
+  build_items(p.meta, tb, true, [&](int c, int) {
+    const int mc = seg_takes_mma(p, c) ? kMmaRows : kVecRows;
+    return ((c + mc - 1) / mc) * p.kch;
+  });
+  const int first = tb.scal[1];
+  for (int item = blockIdx.x; item < tb.scal[2]; item += gridDim.x) {
     __syncthreads();  // the previous item's LDS reads are done before this item writes
-    const int si = find_segment(lds.plan, item);
-    const int seg = nseg_first + si;
-    const int count = p.meta.seg_count[seg];
-    const int slot = p.meta.seg_slot[seg];
-    const int local = item - (si > 0 ? lds.plan.item_end[si - 1] : 0);
+    const int si = find_item_segment(tb, item);
+    const int seg = first + si;
+    const int count = tb.count[seg];
+    const int slot = tb.slot[seg];
+    const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
     const int chunk = local / p.kch, kc = local % p.kch;
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
     if constexpr (sizeof(E) == 2 && R >= 16) {
       if (seg_takes_mma(p, count)) {
-        const int64_t pos0 = (int64_t)p.meta.seg_start[seg] + (int64_t)chunk * kMmaRows;
+        const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kMmaRows;
         mma_item<R>(p, lds, slot, pos0, min(kMmaRows, count - chunk * kMmaRows), kc, sc);
         continue;
       }
     }
-    const int64_t pos0 = (int64_t)p.meta.seg_start[seg] + (int64_t)chunk * kVecRows;
+    const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kVecRows;
     vec_item<E, R>(p, lds, slot, pos0, min(kVecRows, count - chunk * kVecRows), kc, sc);
   }
 }
@@ -394,15 +388,17 @@ size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32
 
 template <typename E, int R>
 static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((shrink_kernel<E, R>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
+  hipLaunchKernelGGL((shrink_kernel<E, R>), dim3(grid), dim3(kShrinkThreads),
+                     seg_table_bytes(p.meta.S), stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
                          int32_t R, float scale, const float *slot_scale, float *u, int mode,
-                         void *ws, hipStream_t stream) {
+                         void *ws, bool for_apply, int *kch_out, hipStream_t stream) {
   const ShrinkConfig c = plan_shrink(meta.T, meta.S, d_in, R, bf16, mode);
+  if (kch_out) *kch_out = c.kch;
   ShrinkParams p{};
   p.meta = meta;
   p.x = x;
@@ -416,6 +412,7 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   p.scale = scale;
   p.slot_scale = slot_scale;
   p.out = c.kch == 1 ? u : reinterpret_cast<float *>(ws);
+  p.u_sorted = for_apply ? 1 : 0;
   p.use_mma_mode = c.use_mma_mode;
   p.mfma_min = c.mfma_min;
   p.kc = c.kc;
@@ -428,7 +425,9 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
     case 32: e = bf16 ? launch_t<uint16_t, 32>(p, c.grid, stream) : launch_t<float, 32>(p, c.grid, stream); break;
     case 64: e = bf16 ? launch_t<uint16_t, 64>(p, c.grid, stream) : launch_t<float, 64>(p, c.grid, stream); break;
   }
-  if (e != hipSuccess || c.kch == 1) return e;
+  // lora_apply's expand reads the partial sums itself; lora_shrink must hand
+  // back a finished u
+  if (e != hipSuccess || c.kch == 1 || for_apply) return e;
   const int64_t work = meta.T * n_slices * (R / 4);
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, 1024));
   hipLaunchKernelGGL(shrink_reduce_kernel, dim3(grid), dim3(256), 0, stream, meta,
