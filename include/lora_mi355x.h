@@ -29,7 +29,9 @@
  *     outputs are rounded once, to nearest even, when y is stored.
  *   - Supported shapes: 1 <= S <= 1023, r_max in {8, 16, 32, 64}, d_in and every
  *     slice width a multiple of 8, 1 <= n_slices <= 8, every device pointer
- *     16-byte aligned, ldx and ldy multiples of 8.  Offsets are int64.
+ *     16-byte aligned, ldx and ldy multiples of 8, (r_max + 1) * d_in and
+ *     (r_max + 1) * width below 2^28 (one slot's factor matrix is addressed with
+ *     32-bit byte offsets).  Row offsets into x, u and y are int64.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H

@@ -9,22 +9,11 @@
 
 namespace lora {
 
-// Segment length (tokens) from which a bf16 segment takes the matrix-core
-// path in AUTO mode.  Tuning override: LORA_MFMA_MIN_TOKENS_SHRINK / _EXPAND,
-// read once.
 static int env_int(const char *name, int dflt) {
   const char *v = std::getenv(name);
   if (!v || !*v) return dflt;
   const int x = std::atoi(v);
   return x > 0 ? x : dflt;
-}
-int shrink_mma_min_default() {
-  static const int v = env_int("LORA_MFMA_MIN_TOKENS_SHRINK", 16);
-  return v;
-}
-int expand_mma_min_default() {
-  static const int v = env_int("LORA_MFMA_MIN_TOKENS_EXPAND", 16);
-  return v;
 }
 // Tuning override: LORA_DISABLE_FUSED_BGMV=1 keeps lora_apply on the
 // shrink + expand kernels even where the fused kernel fits.
@@ -38,6 +27,9 @@ bool fused_disabled() {
 using namespace lora;
 
 namespace {
+
+// Kernels address one slot's factor matrix with 32-bit byte offsets.
+constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
 constexpr int32_t kAbiVersion = 1;
 
@@ -101,6 +93,7 @@ lora_status check_shrink_args(const lora_meta *meta, const void *x, int64_t ldx,
   if (n_slices < 1 || n_slices > kMaxSlices) return LORA_ERR_UNSUPPORTED;
   if (!rank_ok(r_max)) return LORA_ERR_UNSUPPORTED;
   if (d_in < 8 || d_in % 8 || ldx < d_in || ldx % 8) return LORA_ERR_INVALID_ARG;
+  if ((int64_t)(r_max + 1) * d_in >= kMaxFactorElems) return LORA_ERR_UNSUPPORTED;  // 32-bit offsets
   // with no tokens nothing is read or written, so empty buffers may be null
   const bool empty = meta->num_tokens == 0;
   if (!A || (!empty && (!x || !u)) || !aligned16(x) || !aligned16(u)) return LORA_ERR_INVALID_ARG;
@@ -129,6 +122,7 @@ lora_status check_expand_args(const lora_meta *meta, const float *u, int32_t n_s
   for (int s = 0; s < n_slices; ++s) {
     const int64_t w = width[s], o = offset[s];
     if (w < 8 || w % 8 || o < 0 || o % 8 || o + w > ldy) return LORA_ERR_INVALID_ARG;
+    if ((int64_t)(r_max + 1) * w >= kMaxFactorElems) return LORA_ERR_UNSUPPORTED;  // 32-bit offsets
     if (!B[s].ptr || !aligned16(B[s].ptr) || B[s].slot_stride % 8 || B[s].slot_stride < r_max * w)
       return LORA_ERR_INVALID_ARG;
     for (int q = 0; q < s; ++q) {
@@ -282,7 +276,7 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   const MetaView mv = view_of(meta);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
-                                     r_max, dtype == LORA_BF16, (int)mode)) {
+                                     r_max, ldy, dtype == LORA_BF16, (int)mode)) {
     const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
                                      bptr, bstr, width, offset, r_max, scale, d_slot_scale, d_y,
                                      ldy, add_into_y, s);

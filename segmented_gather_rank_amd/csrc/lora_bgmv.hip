@@ -17,24 +17,31 @@
 // are handled inside one XCD, whose L2 then serves that slot's A and B to all
 // of them after the first read from HBM.
 //
-//  * shrink: x row staged in LDS; each thread loads 16 contiguous bytes of A
-//    (one rank octet of one k row) per pass, many passes in flight, and
-//    accumulates 8 ranks; the contraction over k finishes in registers (DPP
-//    row rotations, permlane16/32 swaps) and in a fixed-order sum over the 4
-//    waves;
-//  * expand: each thread owns 8-column octets of the output windows; the y
-//    octets are read at the start (they do not depend on the shrink); B rows
-//    are read with 16-byte loads; the delta is summed on its own in fp32 and
-//    added to y once.
+// Loads are issued in the order they are consumed (x row, A, B, y) before the
+// first wait, so the shrink starts while A and B are still arriving.
+//
+//  * shrink: thread (row rr, rank octet jo) loads 16-byte rank octets of A
+//    rows rr, rr + RB, rr + 2 RB, ... (RB = rows covered by one load across the
+//    workgroup), so every load instruction reads contiguous memory.  bf16:
+//    rows k and k + RB are paired, the x row is staged in LDS as matching
+//    (x[k], x[k + RB]) pairs, and one v_dot2_f32_bf16 does two multiply-adds
+//    per rank (a byte permute builds the A pair); fp32 uses plain FMAs.  The
+//    contraction over k finishes with DPP row rotations, permlane16/32 swaps
+//    and a fixed-order sum over the 16 waves.
+//  * expand: jg adjacent lanes own an 8-column octet of an output window and
+//    split its rank rows; bf16 pairs rank rows j, j + 1 the same way, with u
+//    split into bf16 high and low parts (u ~ hi + lo to about 16 bits) so the
+//    rank-r vector keeps fp32-level precision; the delta is summed on its own
+//    in fp32 and added to y once.
 #include "lora_host.h"
 
 namespace lora {
 
 constexpr int kBThreads = 1024;  // 16 waves: enough loads in flight for one token's factors
 constexpr int kBWaves = kBThreads / kWave;
-constexpr int kBMaxLds = 32768;  // bytes of the staged x row
+constexpr int kBMaxX = 32768;    // bytes of one x row
 constexpr int kBMaxOct = 1024;   // output octets (sum of slice widths / 8)
-// loads per thread per batch: 16 bytes each for bf16, 32 for fp32
+// A / B rank octets per thread per batch (16 bytes each for bf16, 32 for fp32)
 template <typename E> constexpr int kBNA = sizeof(E) == 2 ? 8 : 4;
 template <typename E> constexpr int kBNB = sizeof(E) == 2 ? 8 : 4;
 
@@ -51,6 +58,8 @@ struct BgmvParams {
   int32_t oct_base[kMaxSlices + 1];  // prefix of output octets per slice
   int32_t n_slices;
   int32_t jg;                        // threads sharing one output octet (rank split)
+  int32_t n_inst;                    // A load instructions per slice, rounded up to the batch
+  int32_t x_tasks;                   // x staging tasks (<= 2 per thread)
   float scale;
   const float *slot_scale;
   void *y;
@@ -71,27 +80,46 @@ __device__ __forceinline__ int slice_of_oct(const BgmvParams &p, int o) {
   return last_le(p.oct_base, p.n_slices, o);
 }
 
+// One rank octet of A (8 consecutive ranks of one k row) as raw words.
+template <typename E> struct AOct;
+template <> struct AOct<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { w = buf_load16(r, off); }
+};
+template <> struct AOct<float> {
+  u32x4 a, b;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+    a = buf_load16(r, off);
+    b = buf_load16(r, off + 16);
+  }
+  __device__ __forceinline__ float operator[](int i) const {
+    return __uint_as_float(i < 4 ? a[i] : b[i - 4]);
+  }
+};
+
 template <typename E, int R>
 __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
-  constexpr int JO = R / 8;
-  extern __shared__ __align__(16) unsigned char bgmv_lds[];
-  E *xs = reinterpret_cast<E *>(bgmv_lds);
+  constexpr bool kBf16 = sizeof(E) == 2;
+  constexpr int JO = R / 8;             // rank octets per A row
+  constexpr int RB = kBThreads / JO;    // A rows covered by one load across the workgroup
   constexpr int NA = kBNA<E>, NB = kBNB<E>;
+  // x row: bf16 -> (x[k], x[k + RB]) pair words, fp32 -> values; zero-padded
+  extern __shared__ __align__(16) unsigned char bgmv_lds[];
   __shared__ float red[kBWaves][R];
   __shared__ float us[kMaxSlices][R];
+  __shared__ uint32_t uh[kMaxSlices][R / 2], ul[kMaxSlices][R / 2];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int64_t T = p.meta.T;
-  // positions handled: [first, T); the no-adapter tokens lead the sorted
-  // order and only need work when the windows are stored, not added
-  const int64_t first = p.add ? p.meta.info[3] : 0;
-  const int64_t run = (T - first + 7) / 8;
+  const int64_t run = (T + 7) / 8;
   const int64_t local = blockIdx.x / 8;
   if (local >= run) return;
-  const int64_t pos = first + (int64_t)(blockIdx.x % 8) * run + local;
+  const int64_t pos = (int64_t)(blockIdx.x % 8) * run + local;
   if (pos >= T) return;
-  const int64_t t = p.meta.sorted[pos];
-  const int slot = p.meta.sorted_slot[pos];
+  // both metadata loads go out before either is waited for
+  const int slot = __builtin_amdgcn_readfirstlane(p.meta.sorted_slot[pos]);
+  const int64_t t = __builtin_amdgcn_readfirstlane(p.meta.sorted[pos]);
+  if ((slot < 0 && p.add) || t < 0) return;  // no adapter, add mode: nothing to do
   const int n_oct = pick(p.oct_base, p.n_slices);
   E *y = reinterpret_cast<E *>(p.y) + t * p.ldy;
 
@@ -104,73 +132,130 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
     return;
   }
 
-  // ---- issue every independent load first: A (first batch of slice 0), B
-  // (first batch), y, then x; one memory round trip covers them all
-  const int64_t nel = p.d_in * R;  // A elements per slice
-  const E *A0 = reinterpret_cast<const E *>(p.A[0]) + (int64_t)slot * p.a_stride[0];
-  Raw8<E> a[NA];
-#pragma unroll
-  for (int q = 0; q < NA; ++q) {
-    const int64_t e = 8 * ((int64_t)tid + (int64_t)kBThreads * q);
-    if (e < nel) a[q].load(A0 + e);
-  }
+  // ---- addresses first, then every load of the first batch, in the order the
+  // loads are consumed: x, A, B, y.  None of them sits behind a branch, so the
+  // compiler's waits count exactly the loads issued after the one a use needs.
+  const int rr = tid / JO, jo = tid % JO;
+  const uint32_t a_bytes = (uint32_t)(p.d_in * R * sizeof(E));
   // expand mapping: thread -> (octet o = tid / jg + (kBThreads / jg) * i, rank group g)
   const int jg = p.jg, g = tid % jg, rj = R / jg;
+  const int span = rj < NB ? rj : NB;  // rank rows per batch (even)
   const int o0 = tid / jg, ostep = kBThreads / jg;
-  int s0 = 0;
-  int64_t n00 = 0;
-  const E *Bb0 = nullptr;
-  Raw8<E> b[NB];
-  if (o0 < n_oct) {
-    s0 = slice_of_oct(p, o0);
-    n00 = 8 * (int64_t)(o0 - pick(p.oct_base, s0));
-    Bb0 = reinterpret_cast<const E *>(pick(p.B, s0)) + (int64_t)slot * pick(p.b_stride, s0) + n00;
+  // threads without an octet read octet 0's rows and drop them
+  const int oc = o0 < n_oct ? o0 : 0;
+  const int s0 = slice_of_oct(p, oc);
+  const int64_t n00 = 8 * (int64_t)(oc - pick(p.oct_base, s0, p.n_slices));
+  const E *Bb0 = reinterpret_cast<const E *>(pick(p.B, s0, p.n_slices)) +
+                 (int64_t)slot * pick(p.b_stride, s0, p.n_slices) + n00 + (int64_t)g * rj * pick(p.width, s0, p.n_slices);
+  const int64_t w0 = pick(p.width, s0, p.n_slices);
+  const int64_t yoff0 = pick(p.offset, s0, p.n_slices) + n00;
+  const rsrc_t xr = make_rsrc(reinterpret_cast<const E *>(p.x) + t * p.ldx, (uint32_t)(p.d_in * sizeof(E)));
+  const rsrc_t ar0 = make_rsrc(reinterpret_cast<const E *>(p.A[0]) + (int64_t)slot * p.a_stride[0], a_bytes);
+  const rsrc_t yr = make_rsrc(y, (uint32_t)(p.ldy * sizeof(E)));
+  const bool ymine = o0 < n_oct && g == 0 && p.add;
+  const uint32_t yoff_b = ymine ? (uint32_t)(yoff0 * sizeof(E)) : 0x7FFFFFF0u;  // past the row: zeros
+
+  u32x4 xv[2][2];
 #pragma unroll
-    for (int jj = 0; jj < NB; ++jj)
-      if (jj < rj) b[jj].load(Bb0 + (int64_t)(g * rj + jj) * pick(p.width, s0));
+  for (int u = 0; u < 2; ++u) {
+    // tasks past x_tasks read past the row (zeros) and are not stored
+    const int task = tid + kBThreads * u;
+    if constexpr (kBf16) {  // words [pp * RB + i0, + 8): rows 2 pp RB + i0 and that + RB
+      const int pp = task / (RB / 8), i0 = 8 * (task % (RB / 8));
+      const uint32_t k = (uint32_t)(2 * pp * RB + i0);
+      xv[u][0] = buf_load16(xr, 2 * k);
+      xv[u][1] = buf_load16(xr, 2 * (k + RB));
+    } else {                // values [8 task, + 8)
+      xv[u][0] = buf_load16(xr, 32 * task);
+      xv[u][1] = buf_load16(xr, 32 * task + 16);
+    }
   }
-  float yv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (o0 < n_oct && g == 0 && p.add) load8(y + pick(p.offset, s0) + n00, yv);
-  const E *xr = reinterpret_cast<const E *>(p.x) + t * p.ldx;
-  for (int o = tid; o < p.d_in / 8; o += kBThreads) {
-    Raw8<E> v;
-    v.load(xr + 8 * o);
-    if constexpr (sizeof(E) == 2) {
-      *reinterpret_cast<u32x4 *>(xs + 8 * o) = v.w;
-    } else {
-      *reinterpret_cast<f32x4 *>(xs + 8 * o) = v.a;
-      *reinterpret_cast<f32x4 *>(xs + 8 * o + 4) = v.b;
+  // a[q] holds load instruction q of its batch: k row q * RB + rr, rank octet
+  // jo; q pairs (2m, 2m + 1) are the k rows paired by one dot2
+  AOct<E> a[NA];
+#pragma unroll
+  for (int q = 0; q < NA; ++q)
+    a[q].load(ar0, (uint32_t)(((q * RB + rr) * R + 8 * jo) * sizeof(E)));
+  // b[jj] holds rank row jj of the batch (jj < span; later ones repeat the last)
+  Raw8<E> b[NB];
+#pragma unroll
+  for (int jj = 0; jj < NB; ++jj)
+    b[jj].load(Bb0 + (int64_t)(jj < span ? jj : span - 1) * w0);
+  float yv[8];
+  if constexpr (kBf16) {
+    const u32x4 w = buf_load16(yr, yoff_b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      yv[2 * i] = bf16_lo(w[i]);
+      yv[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const u32x4 w = buf_load16(yr, yoff_b), v = buf_load16(yr, yoff_b + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      yv[i] = __uint_as_float(w[i]);
+      yv[4 + i] = __uint_as_float(v[i]);
+    }
+  }
+
+  // ---- x row into LDS
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int task = tid + kBThreads * u;
+    if (task < p.x_tasks) {
+      if constexpr (kBf16) {
+        const int pp = task / (RB / 8), i0 = 8 * (task % (RB / 8));
+        u32x4 w0, w1;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          w0[2 * m] = pair_lo(xv[u][0][m], xv[u][1][m]);
+          w0[2 * m + 1] = pair_hi(xv[u][0][m], xv[u][1][m]);
+          w1[2 * m] = pair_lo(xv[u][0][m + 2], xv[u][1][m + 2]);
+          w1[2 * m + 1] = pair_hi(xv[u][0][m + 2], xv[u][1][m + 2]);
+        }
+        uint32_t *xw = reinterpret_cast<uint32_t *>(bgmv_lds) + pp * RB + i0;
+        *reinterpret_cast<u32x4 *>(xw) = w0;
+        *reinterpret_cast<u32x4 *>(xw + 4) = w1;
+      } else {
+        u32x4 *xf = reinterpret_cast<u32x4 *>(bgmv_lds) + 2 * task;
+        xf[0] = xv[u][0];
+        xf[1] = xv[u][1];
+      }
     }
   }
   __syncthreads();
 
-  // ---- shrink: thread owns rank octet jo of k rows (8 tid + 8192 q) / R
-  const int jo = tid % JO;
+  // ---- shrink
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   for (int s = 0; s < p.n_slices; ++s) {
-    const E *As = reinterpret_cast<const E *>(pick(p.A, s)) + (int64_t)slot * pick(p.a_stride, s);
+    const rsrc_t ar = make_rsrc(reinterpret_cast<const E *>(pick(p.A, s, p.n_slices)) +
+                                    (int64_t)slot * pick(p.a_stride, s, p.n_slices),
+                                a_bytes);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int64_t base = 0; base < nel; base += (int64_t)8 * kBThreads * NA) {
-      if (s > 0 || base > 0) {
+    for (int bb = 0; bb < p.n_inst; bb += NA) {
+      if (s > 0 || bb > 0) {
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+          a[q].load(ar, (uint32_t)((((bb + q) * RB + rr) * R + 8 * jo) * sizeof(E)));
+      }
+      if constexpr (kBf16) {
+        const uint32_t *xw = reinterpret_cast<const uint32_t *>(bgmv_lds) + rr;
+#pragma unroll
+        for (int m = 0; m < NA / 2; ++m) {
+          const uint32_t xp = xw[(bb / 2 + m) * RB];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = dot2_bf16(pair_lo(a[2 * m].w[i], a[2 * m + 1].w[i]), xp, acc[2 * i]);
+            acc[2 * i + 1] = dot2_bf16(pair_hi(a[2 * m].w[i], a[2 * m + 1].w[i]), xp, acc[2 * i + 1]);
+          }
+        }
+      } else {
+        const float *xf = reinterpret_cast<const float *>(bgmv_lds) + rr;
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
-          const int64_t e = base + 8 * ((int64_t)tid + (int64_t)kBThreads * q);
-          if (e < nel) a[q].load(As + e);
-        }
-      }
+          const float xq = xf[(bb + q) * RB];
 #pragma unroll
-      for (int q = 0; q < NA; ++q) {
-        const int64_t e = base + 8 * ((int64_t)tid + (int64_t)kBThreads * q);
-        if (e < nel) {
-          const int k = (int)(e / R);
-          float xv;
-          if constexpr (sizeof(E) == 2) {
-            xv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(xs)[k] << 16);
-          } else {
-            xv = reinterpret_cast<const float *>(xs)[k];
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(xv, a[q][i], acc[i]);
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(xq, a[q][i], acc[i]);
         }
       }
     }
@@ -181,10 +266,25 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
       for (int i = 0; i < 8; ++i) red[wave][8 * jo + i] = acc[i];
     }
     __syncthreads();
-    if (tid < R) {  // fixed-order sum over the waves
-      float v = 0.f;
-      for (int w = 0; w < kBWaves; ++w) v += red[w][tid];
-      us[s][tid] = sc * v;
+    if constexpr (kBf16) {
+      if (tid < R / 2) {  // fixed-order sum over the waves, then the bf16 hi/lo split of u
+        float v0 = 0.f, v1 = 0.f;
+        for (int w = 0; w < kBWaves; ++w) {
+          v0 += red[w][2 * tid];
+          v1 += red[w][2 * tid + 1];
+        }
+        uint32_t h0, l0, h1, l1;
+        split_bf16(sc * v0, h0, l0);
+        split_bf16(sc * v1, h1, l1);
+        uh[s][tid] = h0 | (h1 << 16);
+        ul[s][tid] = l0 | (l1 << 16);
+      }
+    } else {
+      if (tid < R) {  // fixed-order sum over the waves
+        float v = 0.f;
+        for (int w = 0; w < kBWaves; ++w) v += red[w][tid];
+        us[s][tid] = sc * v;
+      }
     }
     __syncthreads();
   }
@@ -193,28 +293,47 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   // rank rows [g * rj, (g + 1) * rj); the group sum lands in lane g == 0
   for (int o = o0, it = 0; o < n_oct; o += ostep, ++it) {
     int s = s0;
-    int64_t n0 = n00;
-    const E *Bb = Bb0;
+    int64_t n0 = n00, w = w0, yoff = yoff0;
+    const E *Bb = Bb0;  // rank row g * rj of this octet's columns
     if (it > 0) {
       s = slice_of_oct(p, o);
-      n0 = 8 * (int64_t)(o - pick(p.oct_base, s));
-      Bb = reinterpret_cast<const E *>(pick(p.B, s)) + (int64_t)slot * pick(p.b_stride, s) + n0;
-      if (g == 0 && p.add) load8(y + pick(p.offset, s) + n0, yv);
+      n0 = 8 * (int64_t)(o - pick(p.oct_base, s, p.n_slices));
+      w = pick(p.width, s, p.n_slices);
+      Bb = reinterpret_cast<const E *>(pick(p.B, s, p.n_slices)) + (int64_t)slot * pick(p.b_stride, s, p.n_slices) +
+           n0 + (int64_t)g * rj * w;
+      yoff = pick(p.offset, s, p.n_slices) + n0;
+      if (g == 0 && p.add) load8(y + yoff, yv);
     }
-    const int64_t w = pick(p.width, s);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int jb = 0; jb < rj; jb += NB) {
       if (it > 0 || jb > 0) {
 #pragma unroll
         for (int jj = 0; jj < NB; ++jj)
-          if (jb + jj < rj) b[jj].load(Bb + (int64_t)(g * rj + jb + jj) * w);
+          b[jj].load(Bb + (int64_t)(jb + (jj < span ? jj : span - 1)) * w);
       }
+      if constexpr (kBf16) {  // rank rows come in pairs (j even, j + 1)
 #pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        if (jb + jj < rj) {
-          const float uv = us[s][g * rj + jb + jj];
+        for (int m = 0; m < NB / 2; ++m) {
+          if (2 * m < span) {
+            const int pj = (g * rj + jb) / 2 + m;
+            const uint32_t hp = uh[s][pj], lp = ul[s][pj];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[c] = fmaf(uv, b[jj][c], acc[c]);
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t e0 = pair_lo(b[2 * m].w[i], b[2 * m + 1].w[i]);
+              const uint32_t e1 = pair_hi(b[2 * m].w[i], b[2 * m + 1].w[i]);
+              acc[2 * i] = dot2_bf16(e0, hp, dot2_bf16(e0, lp, acc[2 * i]));
+              acc[2 * i + 1] = dot2_bf16(e1, hp, dot2_bf16(e1, lp, acc[2 * i + 1]));
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) {
+          if (jj < span) {
+            const float uv = us[s][g * rj + jb + jj];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = fmaf(uv, b[jj][c], acc[c]);
+          }
         }
       }
     }
@@ -223,21 +342,36 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
     if (g == 0) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) yv[c] += acc[c];
-      store8(y + pick(p.offset, s) + n0, yv);
+      store8(y + yoff, yv);
     }
   }
 }
 
 // ------------------------------------------------------------------ host side
 
+// A load instructions per slice (rounded up to whole batches), x staging
+// tasks and LDS bytes of the staged x row.
+static void bgmv_x_plan(int64_t d_in, int32_t R, bool bf16, int32_t &n_inst, int32_t &x_tasks, size_t &lds) {
+  const int64_t rb = (int64_t)kBThreads / (R / 8);
+  const int64_t na = bf16 ? kBNA<uint16_t> : kBNA<float>;
+  n_inst = (int32_t)(((d_in + rb - 1) / rb + na - 1) / na * na);
+  x_tasks = (int32_t)(bf16 ? n_inst * rb / 16 : n_inst * rb / 8);
+  lds = (size_t)n_inst * rb * (bf16 ? 2 : 4);
+}
+
 bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64_t *width, int32_t R,
-               bool bf16, int mode) {
+               int64_t ldy, bool bf16, int mode) {
   if (mode == 2) return false;  // SGMV requested
   const int64_t e = bf16 ? 2 : 4;
   int64_t sw = 0;
   for (int s = 0; s < n_slices; ++s) sw += width[s];
   const int64_t w_tok = ((int64_t)n_slices * d_in + sw) * R * e;  // weight bytes per token
-  if (sw / 8 > kBMaxOct || d_in * e > kBMaxLds || w_tok > (1 << 20)) return false;
+  if (sw / 8 > kBMaxOct || d_in * e > kBMaxX || w_tok > (1 << 20)) return false;
+  if (ldy * e >= (int64_t)1 << 30) return false;  // y rows are addressed with 32-bit buffer offsets
+  int32_t n_inst, x_tasks;
+  size_t lds;
+  bgmv_x_plan(d_in, R, bf16, n_inst, x_tasks, lds);
+  if (x_tasks > 2 * kBThreads || lds > 49152) return false;
   return mode == 1 || T <= 16 * (int64_t)S;  // BGMV requested, or few tokens per slot
 }
 
@@ -270,9 +404,11 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
   p.n_slices = n_slices;
   // split the rank over jg adjacent lanes when there are fewer octets than threads
   const int n_oct = p.oct_base[n_slices];
-  int jg = 1;
-  while (jg < 16 && jg < R && (int64_t)n_oct * jg * 2 <= kBThreads) jg *= 2;
+  int jg = 1;  // at most R / 2, so every lane keeps whole pairs of rank rows
+  while (jg < 16 && jg < R / 2 && (int64_t)n_oct * jg * 2 <= kBThreads) jg *= 2;
   p.jg = jg;
+  size_t lds = 0;
+  bgmv_x_plan(d_in, R, bf16, p.n_inst, p.x_tasks, lds);
   p.scale = scale;
   p.slot_scale = slot_scale;
   p.y = y;
@@ -280,7 +416,6 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
   p.add = add ? 1 : 0;
   if (meta.T == 0) return hipSuccess;
   const int grid = (int)(8 * ((meta.T + 7) / 8));
-  const size_t lds = (size_t)d_in * (bf16 ? 2 : 4);
   switch (R) {
     case 8: return bf16 ? launch_t<uint16_t, 8>(p, grid, lds, stream) : launch_t<float, 8>(p, grid, lds, stream);
     case 16: return bf16 ? launch_t<uint16_t, 16>(p, grid, lds, stream) : launch_t<float, 16>(p, grid, lds, stream);

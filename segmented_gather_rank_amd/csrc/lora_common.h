@@ -34,9 +34,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// Plain loads and stores through the global address space.  A pointer that
+// the compiler cannot trace to a global allocation (one rebuilt from integers,
+// say) would otherwise be accessed with flat instructions, which count against
+// both memory wait counters and so force coarser waits.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) f32x4 g_f32x4;
+__device__ __forceinline__ u32x4 gload16(const void *p) { return *(const g_u32x4 *)p; }
+__device__ __forceinline__ f32x4 gload16f(const void *p) { return *(const g_f32x4 *)p; }
+__device__ __forceinline__ void gstore16(void *p, u32x4 v) { *(g_u32x4 *)p = v; }
+__device__ __forceinline__ void gstore16f(void *p, f32x4 v) { *(g_f32x4 *)p = v; }
+
 // Load 8 consecutive elements (16 B of bf16 or 32 B of fp32) as fp32.
 __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
-  u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+  u32x4 w = gload16(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = bf16_lo(w[i]);
@@ -44,8 +55,8 @@ __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
   }
 }
 __device__ __forceinline__ void load8(const float *p, float v[8]) {
-  f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  f32x4 a = gload16f(p);
+  f32x4 b = gload16f(p + 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[i] = a[i];
@@ -56,7 +67,7 @@ __device__ __forceinline__ void store8(uint16_t *p, const float v[8]) {
   u32x4 w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-  *reinterpret_cast<u32x4 *>(p) = w;
+  gstore16(p, w);
 }
 __device__ __forceinline__ void store8(float *p, const float v[8]) {
   f32x4 a, b;
@@ -65,8 +76,43 @@ __device__ __forceinline__ void store8(float *p, const float v[8]) {
     a[i] = v[i];
     b[i] = v[4 + i];
   }
-  *reinterpret_cast<f32x4 *>(p) = a;
-  *reinterpret_cast<f32x4 *>(p + 4) = b;
+  gstore16f(p, a);
+  gstore16f(p + 4, b);
+}
+
+// ---------------------------------------------------------------- buffer loads
+
+// Raw buffer resource over [base, base + bytes): a load past the end returns
+// zeros instead of touching memory, and offsets are 32-bit, so a kernel walks
+// one slot's matrix from a scalar base with unsigned byte offsets and needs no
+// branch for a ragged tail.  The base must be uniform across the wave.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// ---------------------------------------------------------------- bf16 pairs
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// (low half of a, low half of b) and (high half of a, high half of b)
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+// c + a.lo * b.lo + a.hi * b.hi, bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+// fp32 v split into bf16 hi + lo (v - hi, rounded): about 16 significant bits
+__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16(v);
+  lo = f32_to_bf16(v - __uint_as_float(hi << 16));
 }
 
 // ---------------------------------------------------------------- wave primitives
@@ -89,14 +135,38 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 
 // ---------------------------------------------------------------- parameter arrays
 
-// a[i] for a small array held in a kernel's by-value parameter block.  Indexing
-// it with a runtime value would make the compiler copy the whole block to
-// scratch memory; an unrolled select keeps it in the kernarg segment.
+// A value read from the kernel's parameter block, passed through
+// v_readfirstlane so that it lives in scalar registers and is opaque to the
+// optimiser.  Without it, a chain of selects between such values (below) can be
+// folded back into one indexed per-lane load from the parameter block: a vector
+// memory load, whose wait would also wait for every vector load issued before it.
+template <typename T>
+__device__ __forceinline__ T uniform_value(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values only");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  } else {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 w = __builtin_bit_cast(i32x2, v);
+    w.x = __builtin_amdgcn_readfirstlane(w.x);
+    w.y = __builtin_amdgcn_readfirstlane(w.y);
+    return __builtin_bit_cast(T, w);
+  }
+}
+
+// a[i] for a small array held in a kernel's by-value parameter block, where i
+// may differ between lanes and only the first n entries are in use (n is
+// uniform).  Indexing the array with a runtime value would make the compiler
+// copy the whole block to scratch memory; an unrolled select over scalar
+// copies keeps it in registers.
 template <typename T, int N>
-__device__ __forceinline__ T pick(const T (&a)[N], int i) {
-  T v = a[0];
+__device__ __forceinline__ T pick(const T (&a)[N], int i, int n = N) {
+  T v = uniform_value(a[0]);
 #pragma unroll
-  for (int k = 1; k < N; ++k) v = (i == k) ? a[k] : v;
+  for (int k = 1; k < N; ++k) {
+    if (k >= n) break;
+    v = (i == k) ? uniform_value(a[k]) : v;
+  }
   return v;
 }
 
@@ -106,7 +176,10 @@ template <int N>
 __device__ __forceinline__ int last_le(const int32_t (&prefix)[N], int n, int v) {
   int s = 0;
 #pragma unroll
-  for (int k = 1; k < N; ++k) s = (k < n && prefix[k] <= v) ? k : s;
+  for (int k = 1; k < N; ++k) {
+    if (k >= n) break;
+    s = (uniform_value(prefix[k]) <= v) ? k : s;
+  }
   return s;
 }
 
@@ -245,7 +318,7 @@ __device__ __forceinline__ float wave_sum_mod(float v) {
 template <typename E> struct Raw8;
 template <> struct Raw8<uint16_t> {
   u32x4 w;
-  __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ void load(const uint16_t *p) { w = gload16(p); }
   __device__ __forceinline__ void zero() { w = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ float operator[](int i) const {
     return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
@@ -254,8 +327,8 @@ template <> struct Raw8<uint16_t> {
 template <> struct Raw8<float> {
   f32x4 a, b;
   __device__ __forceinline__ void load(const float *p) {
-    a = *reinterpret_cast<const f32x4 *>(p);
-    b = *reinterpret_cast<const f32x4 *>(p + 4);
+    a = gload16f(p);
+    b = gload16f(p + 4);
   }
   __device__ __forceinline__ void zero() { a = b = f32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }

@@ -33,8 +33,6 @@ namespace lora {
 constexpr int kExpThreads = 256;
 constexpr int kEVecRows = 8;       // tokens per vector m-chunk
 constexpr int kEVecLds = 32768;    // bytes of the shared B tile on the vector path
-constexpr int kEMmaRows = 64;      // tokens per matrix-core m-chunk
-constexpr int kEMmaCols = 128;     // columns per matrix-core n-tile
 
 struct ExpandParams {
   MetaView meta;
@@ -45,29 +43,20 @@ struct ExpandParams {
   int64_t b_stride[kMaxSlices];
   int64_t width[kMaxSlices];
   int64_t offset[kMaxSlices];
-  int32_t ntiles_vec, ntiles_mma;     // n-tiles over all slices, per path
+  int32_t ntiles_vec;                 // vector n-tiles over all slices
   int32_t vec_cols;                   // columns per vector n-tile
+  int32_t cpi, nck;                   // matrix-core path: columns per item, chunks over all slices
+  int32_t chunk_base[kMaxSlices + 1]; // prefix of chunks per slice
   int32_t n_slices;
   void *y;
   int64_t ldy;
   int32_t add;
-  int32_t use_mma_mode, mfma_min;
 };
 
 template <typename E, int R>
 struct ExpandLds {
-  union {
-    struct {
-      E bt[kEVecLds / sizeof(E)];  // B tile [R][vec_cols]
-      float us[kEVecRows][R];
-    } vec;
-    struct {
-      uint16_t bl[(R < 32 ? 32 : R) * (kEMmaCols + 16)];  // B tile, row j, column n
-    } mma;
-    struct {
-      float out[kEMmaRows][kEMmaCols + 4];
-    } epi;
-  };
+  E bt[kEVecLds / sizeof(E)];  // B tile [R][vec_cols]
+  float us[kEVecRows][R];
 };
 
 // Slice and slice-local index of n-tile `tile` when every slice is cut into
@@ -90,9 +79,6 @@ __device__ __forceinline__ void tile_slice(const ExpandParams &p, int nc, int ti
   }
 }
 
-__device__ __forceinline__ bool exp_takes_mma(const ExpandParams &p, int count, int slot) {
-  return slot >= 0 && (p.use_mma_mode == 2 || (p.use_mma_mode == 1 && count >= p.mfma_min));
-}
 
 
 // 8 rank values j..j+7 of slice s for sorted position pos (token t).
@@ -144,10 +130,10 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
       Raw8<E> v;
       if (nbase + 8 * o < w) v.load(Bb + (int64_t)j * w + 8 * o); else v.zero();
       if constexpr (sizeof(E) == 2) {
-        *reinterpret_cast<u32x4 *>(&lds.vec.bt[j * NC + 8 * o]) = v.w;
+        *reinterpret_cast<u32x4 *>(&lds.bt[j * NC + 8 * o]) = v.w;
       } else {
-        *reinterpret_cast<f32x4 *>(&lds.vec.bt[j * NC + 8 * o]) = v.a;
-        *reinterpret_cast<f32x4 *>(&lds.vec.bt[j * NC + 8 * o + 4]) = v.b;
+        *reinterpret_cast<f32x4 *>(&lds.bt[j * NC + 8 * o]) = v.a;
+        *reinterpret_cast<f32x4 *>(&lds.bt[j * NC + 8 * o + 4]) = v.b;
       }
     }
     // rank-r rows
@@ -156,8 +142,8 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
       const int64_t t = p.u_mode == 0 ? (int64_t)p.meta.sorted[pos0 + m] : 0;
       float v[8];
       load_u8(p, R, s, pos0 + m, t, j, v);
-      *reinterpret_cast<f32x4 *>(&lds.vec.us[m][j]) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4 *>(&lds.vec.us[m][j + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+      *reinterpret_cast<f32x4 *>(&lds.us[m][j]) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4 *>(&lds.us[m][j + 4]) = f32x4{v[4], v[5], v[6], v[7]};
     }
   }
 #pragma unroll
@@ -181,12 +167,12 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
       for (int j = 0; j < R; ++j) {
         Raw8<E> b;
         if constexpr (sizeof(E) == 2) {
-          b.w = *reinterpret_cast<const u32x4 *>(&lds.vec.bt[j * NC + 8 * o]);
+          b.w = *reinterpret_cast<const u32x4 *>(&lds.bt[j * NC + 8 * o]);
         } else {
-          b.a = *reinterpret_cast<const f32x4 *>(&lds.vec.bt[j * NC + 8 * o]);
-          b.b = *reinterpret_cast<const f32x4 *>(&lds.vec.bt[j * NC + 8 * o + 4]);
+          b.a = *reinterpret_cast<const f32x4 *>(&lds.bt[j * NC + 8 * o]);
+          b.b = *reinterpret_cast<const f32x4 *>(&lds.bt[j * NC + 8 * o + 4]);
         }
-        const float uv = lds.vec.us[m][j];
+        const float uv = lds.us[m][j];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = fmaf(uv, b[c], acc[c]);
       }
@@ -200,119 +186,233 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
 }
 
 // ------------------------------------------------------------- matrix-core path
+//
+// One item = (segment, tile of up to 64 sorted tokens, chunk of `cpi` columns of
+// one slice), walked in steps of 128 columns.  The product is taken transposed,
+// D'[col][token] = B^T u^T with v_mfma_f32_16x16x16_bf16: the A operand (16
+// columns x 4 ranks per lane) comes from the step's B tile in LDS through the
+// gfx950 transposing read, the B operand (4 ranks of one token per lane) is u
+// split into bf16 hi + lo and held in registers for the whole item.  The B tile
+// is written to LDS with its columns permuted inside every 32-column group so
+// that, for each pair of 16-column blocks, a lane's 8 results are 8 consecutive
+// columns of one token: y is read and written 16 bytes per lane, with no LDS
+// round trip.  The next step's B tile and y octets are loaded while the current
+// step is multiplied (two LDS buffers, one barrier per step).
+//
+// Waves and tokens: a tile has nb = ceil(rows / 16) blocks of 16 tokens; the 4
+// waves are spread over them (4, 2 or 1 waves per block) and the waves that
+// share a block split the step's columns.
 
-template <typename E, int R>
-__device__ __forceinline__ void exp_mma_item(const ExpandParams &p, ExpandLds<E, R> &lds, int slot, int64_t pos0,
-                             int rows, int s, int nt) {
-  constexpr int RP = R < 32 ? 32 : R;  // K padded to whole 32-wide steps
-  constexpr int LDB = kEMmaCols + 16;   // LDS row stride of the B tile
-  constexpr int BOCT = RP * kEMmaCols / 8 / kExpThreads;  // B octets per thread
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int64_t w = pick(p.width, s);
-  const int64_t nbase = (int64_t)nt * kEMmaCols;
-  const uint16_t *Bb = reinterpret_cast<const uint16_t *>(pick(p.B, s)) + (int64_t)slot * pick(p.b_stride, s);
-  uint16_t *y = reinterpret_cast<uint16_t *>(p.y);
+constexpr int kXThreads = 256;
+constexpr int kXStep = 128;          // columns per step
+constexpr int kXLdb = kXStep + 16;   // LDS row stride (elements) of a B step tile
+constexpr int kXRows = 64;           // tokens per tile
 
-  // epilogue ownership: rows tid/16 + 16 i, octet tid % 16; token indices first
-  const int eo = tid % 16;
-  const int64_t en = nbase + 8 * eo;
-  int64_t tok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r_ = tid / 16 + 16 * i;
-    tok[i] = (r_ < rows && en < w) ? (int64_t)p.meta.sorted[pos0 + r_] : -1;
-  }
-  // B tile [R][128] into registers
-  u32x4 bq[BOCT];
-#pragma unroll
-  for (int q = 0; q < BOCT; ++q) {
-    const int idx = tid + kExpThreads * q;
-    const int j = idx / (kEMmaCols / 8), n0 = 8 * (idx % (kEMmaCols / 8));
-    if (j < R && nbase + n0 < w)
-      bq[q] = *reinterpret_cast<const u32x4 *>(Bb + (int64_t)j * w + nbase + n0);
-    else
-      bq[q] = u32x4{0, 0, 0, 0};
-  }
-  // u fragments: lane (mrow, g), step c holds k = 32c + 8g + e, split into bf16 hi + lo
-  const int mrow = lane % 16, g = lane / 16;
-  const int row = 16 * wave + mrow;
-  float uf[RP / 32][8];
-#pragma unroll
-  for (int c = 0; c < RP / 32; ++c) {
-    const int k = 32 * c + 8 * g;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) uf[c][i] = 0.f;
-    if (row < rows && k < R) {
-      const int64_t t = p.u_mode == 0 ? (int64_t)p.meta.sorted[pos0 + row] : 0;
-      load_u8(p, R, s, pos0 + row, t, k, uf[c]);
-    }
-  }
-  // y segments
-  float yv[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) yv[i][c] = 0.f;
-    if (tok[i] >= 0 && p.add) load8(y + tok[i] * p.ldy + pick(p.offset, s) + en, yv[i]);
-  }
-  // B tile -> LDS, row-major (16-byte writes)
-#pragma unroll
-  for (int q = 0; q < BOCT; ++q) {
-    const int idx = tid + kExpThreads * q;
-    const int j = idx / (kEMmaCols / 8), n0 = 8 * (idx % (kEMmaCols / 8));
-    *reinterpret_cast<u32x4 *>(&lds.mma.bl[j * LDB + n0]) = bq[q];
-  }
-  bf16x8 uh[RP / 32], ul[RP / 32];
-#pragma unroll
-  for (int c = 0; c < RP / 32; ++c) {
-    u32x4 hw, lw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t hb[2], lb[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float v = uf[c][2 * i + h];
-        hb[h] = f32_to_bf16(v);
-        lb[h] = f32_to_bf16(v - __uint_as_float(hb[h] << 16));
-      }
-      hw[i] = hb[0] | (hb[1] << 16);
-      lw[i] = lb[0] | (lb[1] << 16);
-    }
-    uh[c] = __builtin_bit_cast(bf16x8, hw);
-    ul[c] = __builtin_bit_cast(bf16x8, lw);
-  }
-  __syncthreads();
-  f32x4 acc[kEMmaCols / 16];
-#pragma unroll
-  for (int b = 0; b < kEMmaCols / 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < RP / 32; ++c) {
-    const int k = 32 * c + 8 * g;
-#pragma unroll
-    for (int b = 0; b < kEMmaCols / 16; ++b) {
-      const bf16x8 bv = lds_col8(lds.mma.bl, LDB, k, 16 * b);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[c], bv, acc[b], 0, 0, 0);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul[c], bv, acc[b], 0, 0, 0);
-    }
-  }
-  __syncthreads();  // the B tile is fully read before the epilogue reuses the LDS
-#pragma unroll
-  for (int b = 0; b < kEMmaCols / 16; ++b)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) lds.epi.out[16 * wave + 4 * g + v][16 * b + mrow] = acc[b][v];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (tok[i] < 0) continue;
-    const int r_ = tid / 16 + 16 * i;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) yv[i][c] += lds.epi.out[r_][8 * eo + c];
-    store8(y + tok[i] * p.ldy + pick(p.offset, s) + en, yv[i]);
-  }
-  __syncthreads();
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A operand of v_mfma_f32_16x16x16_bf16 from a row-major bf16 tile in LDS:
+// lane i of each 16-lane group receives tile[row0 + e][col0 + i], e = 0..3,
+// where row0 is this lane's group's first row.
+__device__ __forceinline__ s16x4 lds_col4(const uint16_t *tile, int ld, int row0, int col0) {
+  const int l = threadIdx.x % 16;
+  const uint16_t *a = tile + (row0 + l / 4) * ld + col0 + 4 * (l % 4);
+  typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+  return __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a)));
 }
 
-// ------------------------------------------------------------------ the kernel
+template <int R>
+struct XLds {
+  static constexpr int RP = R < 16 ? 16 : R;  // ranks padded to whole 16-wide steps
+  uint16_t bl[2][RP * kXLdb];
+};
+
+template <int R>
+__global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p) {
+  constexpr int RP = XLds<R>::RP;
+  constexpr int KS = RP / 16;                     // MFMA k-steps
+  constexpr int BQ = RP * kXStep / 8 / kXThreads;  // B octets per thread per step
+  __shared__ XLds<R> lds;
+  extern __shared__ __align__(16) unsigned char xdyn[];
+  const SegTable tb = seg_table_at(xdyn, p.meta.S);
+  build_items(p.meta, tb, p.add != 0, [&](int c, int) { return ((c + kXRows - 1) / kXRows) * p.nck; });
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = lane % 16, kg = lane / 16;
+  const int64_t T = p.meta.T;
+  const int first = tb.scal[1];
+  // XCD-aware order: XCD x (blockIdx mod 8) takes a contiguous run of items,
+  // so tiles that share a chunk of B meet in one L2
+  const int total = tb.scal[2];
+  const int run = (total + 7) / 8;
+  const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
+  const int lo = xcd * run, hi = min(total, lo + run);
+  uint16_t *y = reinterpret_cast<uint16_t *>(p.y);
+
+  for (int item = lo + (int)blockIdx.x / 8; item < hi; item += per) {
+    const int si = find_item_segment(tb, item);
+    const int seg = first + si;
+    const int count = tb.count[seg];
+    const int slot = tb.slot[seg];
+    const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
+    const int tile = local / p.nck, ck = local % p.nck;
+    const int s = last_le(p.chunk_base, p.n_slices, ck);
+    const int64_t w = pick(p.width, s, p.n_slices);
+    const int64_t col0 = (int64_t)(ck - pick(p.chunk_base, s, p.n_slices)) * p.cpi;
+    const int ncols = (int)min((int64_t)p.cpi, w - col0);
+    const int nsteps = (ncols + kXStep - 1) / kXStep;
+    const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)tile * kXRows;
+    const int rows = min(kXRows, count - tile * kXRows);
+    const int nb = (rows + 15) / 16;
+    const int wpt = nb == 1 ? 4 : (nb == 2 ? 2 : 1);  // waves per token block
+    const int tbw = wave / wpt, wq = wave % wpt;
+    const int cw = kXStep / wpt;                      // columns of this wave per step
+    const int nbp = cw / 32;                          // 16-column block pairs per step
+    const int r = 16 * tbw + n;
+    const bool rv = tbw < nb && r < rows;
+    const int64_t pos = pos0 + (rv ? r : 0);
+    const int64_t t = p.meta.sorted[pos];
+    const int64_t yo = pick(p.offset, s, p.n_slices) + col0;
+    uint16_t *yrow = y + t * p.ldy + yo;
+    // this lane's y octet of block pair pp in step i: columns
+    // i * 128 + wq * cw + 32 pp + 8 kg (clamped to the first one when not ours)
+    auto ycol = [&](int i, int pp) -> int {
+      const int c = i * kXStep + wq * cw + 32 * pp + 8 * kg;
+      return (pp < nbp && c < ncols) ? c : 0;
+    };
+
+    if (slot < 0) {  // store mode, no adapter: the windows become 0
+      for (int i = 0; i < nsteps; ++i)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int c = i * kXStep + wq * cw + 32 * pp + 8 * kg;
+          if (rv && pp < nbp && c < ncols) gstore16(yrow + c, u32x4{0, 0, 0, 0});
+        }
+      continue;
+    }
+
+    // ---- rank-r rows of this lane's token, split into bf16 hi + lo: k-step c
+    // holds ranks 16 c + 4 kg .. + 3
+    s16x4 uh[KS], ul[KS];
+    {
+      const int64_t urow = p.u_mode == 0 ? t : pos;
+      const float *ub = p.u + ((int64_t)s * T + urow) * R;
+      const int64_t plane = (int64_t)p.n_slices * T * R;
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const int j = 16 * c + 4 * kg;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (rv && j < R) {
+          v = gload16f(ub + j);
+          for (int kc = 1; kc < p.kch; ++kc) {  // split-K partial sums, in k-chunk order
+            const f32x4 wv = gload16f(ub + kc * plane + j);
+            v[0] += wv[0];
+            v[1] += wv[1];
+            v[2] += wv[2];
+            v[3] += wv[3];
+          }
+        }
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        uh[c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
+      }
+    }
+
+    // ---- B step tiles: rows j < RP, 128 columns; thread octet q covers row
+    // idx / 16, columns 8 (idx % 16) .. + 7 of the step (idx = tid + 256 q).
+    // Loads past the slot block read zeros (rows >= R); columns past the
+    // window may read anything: their results are never stored.
+    const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick(p.B, s, p.n_slices)) +
+                                    (int64_t)slot * pick(p.b_stride, s, p.n_slices),
+                                (uint32_t)(R * w * 2));
+    u32x4 bq[BQ];
+    auto load_b = [&](int i) {
+#pragma unroll
+      for (int q = 0; q < BQ; ++q) {
+        const int idx = tid + kXThreads * q;
+        const int j = idx / 16, h = idx % 16;
+        const int64_t c = col0 + (int64_t)i * kXStep + 8 * h;
+        bq[q] = buf_load16(br, (uint32_t)(((int64_t)j * w + c) * 2));
+      }
+    };
+    // permuted store: the 8 columns 32 g32 + 8 g4 .. + 7 go to block 2 g32
+    // (rows 4 g4 .. + 3) and block 2 g32 + 1 (same rows)
+    auto store_b = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < BQ; ++q) {
+        const int idx = tid + kXThreads * q;
+        const int j = idx / 16, h = idx % 16;
+        const int col = 32 * (h / 4) + 4 * (h % 4);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2 *>(&lds.bl[buf][j * kXLdb + col]) = u32x2{bq[q][0], bq[q][1]};
+        *reinterpret_cast<u32x2 *>(&lds.bl[buf][j * kXLdb + col + 16]) = u32x2{bq[q][2], bq[q][3]};
+      }
+    };
+    u32x4 ycur[4], ynext[4];
+    auto load_y = [&](int i, u32x4 (&yy)[4]) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) yy[pp] = gload16(yrow + ycol(i, pp));
+    };
+
+    load_b(0);
+    load_y(0, ycur);
+    __syncthreads();  // the previous item's last step has read both buffers
+    store_b(0);
+    __syncthreads();
+    for (int i = 0; i < nsteps; ++i) {
+      // next step's loads (one past the end reads harmless addresses)
+      load_b(i + 1);
+      load_y(i + 1, ynext);
+      const uint16_t *bt = lds.bl[i & 1];
+      f32x4 acc[4][2];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) acc[pp][0] = acc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (tbw < nb) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          if (pp < nbp) {
+            const int blk0 = (wq * cw) / 16 + 2 * pp;
+#pragma unroll
+            for (int c = 0; c < KS; ++c) {
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const s16x4 a = lds_col4(bt, kXLdb, 16 * c + 4 * kg, 16 * (blk0 + hh));
+                acc[pp][hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ul[c], acc[pp][hh], 0, 0, 0);
+                acc[pp][hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, uh[c], acc[pp][hh], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      // epilogue: lane (token n, kg) holds columns 32 pp + 8 kg + 0..7 of the step
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int c = i * kXStep + wq * cw + 32 * pp + 8 * kg;
+        if (rv && pp < nbp && c < ncols) {
+          float v[8];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            v[2 * m] = p.add ? bf16_lo(ycur[pp][m]) : 0.f;
+            v[2 * m + 1] = p.add ? bf16_hi(ycur[pp][m]) : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] += acc[pp][0][e];
+            v[4 + e] += acc[pp][1][e];
+          }
+          store8(yrow + c, v);
+        }
+      }
+      if (i + 1 < nsteps) store_b((i + 1) & 1);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) ycur[pp] = ynext[pp];
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------------ the vector kernel
 
 template <typename E, int R>
 __global__ __launch_bounds__(kExpThreads) void expand_kernel(ExpandParams p) {
@@ -320,10 +420,8 @@ __global__ __launch_bounds__(kExpThreads) void expand_kernel(ExpandParams p) {
   extern __shared__ __align__(16) unsigned char expand_dyn[];
   const SegTable tb = seg_table_at(expand_dyn, p.meta.S);
   // the no-adapter segment (always first) is visited only to store zeros
-  build_items(p.meta, tb, p.add != 0, [&](int c, int slot) {
-    const bool mma = exp_takes_mma(p, c, slot);
-    const int mc = mma ? kEMmaRows : kEVecRows;
-    return ((c + mc - 1) / mc) * (mma ? p.ntiles_mma : p.ntiles_vec);
+  build_items(p.meta, tb, p.add != 0, [&](int c, int) {
+    return ((c + kEVecRows - 1) / kEVecRows) * p.ntiles_vec;
   });
   const int first = tb.scal[1];
   for (int item = blockIdx.x; item < tb.scal[2]; item += gridDim.x) {
@@ -332,16 +430,6 @@ __global__ __launch_bounds__(kExpThreads) void expand_kernel(ExpandParams p) {
     const int count = tb.count[seg];
     const int slot = tb.slot[seg];
     const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
-    if constexpr (sizeof(E) == 2) {
-      if (exp_takes_mma(p, count, slot)) {
-        const int chunk = local / p.ntiles_mma;
-        int s, nt;
-        tile_slice(p, kEMmaCols, local % p.ntiles_mma, s, nt);
-        const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kEMmaRows;
-        exp_mma_item<E, R>(p, lds, slot, pos0, min(kEMmaRows, count - chunk * kEMmaRows), s, nt);
-        continue;
-      }
-    }
     const int chunk = local / p.ntiles_vec;
     int s, nt;
     tile_slice(p, p.vec_cols, local % p.ntiles_vec, s, nt);
@@ -359,6 +447,17 @@ static hipError_t launch_t(const ExpandParams &p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int R>
+static hipError_t launch_mma_t(const ExpandParams &p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), seg_table_bytes(p.meta.S),
+                     stream, p);
+  return hipGetLastError();
+}
+
+// Matrix-core expand: the bf16 path of SGMV and AUTO (tile heights follow the
+// segment lengths); the vector kernel serves fp32 and BGMV.
+bool expand_uses_mma(bool bf16, int mode) { return bf16 && mode != 1; }
+
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
                          const int64_t *offset, int32_t R, void *y, int64_t ldy, bool bf16,
@@ -369,29 +468,51 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   p.u_mode = u_mode;
   p.kch = kch;
   p.n_slices = n_slices;
-  // vector n-tile: up to 512 columns, as many as fit the shared B tile
   const int64_t e = bf16 ? 2 : 4;
-  p.vec_cols = (int)std::min<int64_t>(512, kEVecLds / (R * e));
-  p.ntiles_vec = p.ntiles_mma = 0;
+  const bool mma = expand_uses_mma(bf16, mode);
+  const int64_t T = meta.T, S = meta.S;
+  int64_t sw = 0;
   for (int s = 0; s < n_slices; ++s) {
     p.B[s] = B[s];
     p.b_stride[s] = b_stride[s];
     p.width[s] = width[s];
     p.offset[s] = offset[s];
-    p.ntiles_vec += (int32_t)((width[s] + p.vec_cols - 1) / p.vec_cols);
-    p.ntiles_mma += (int32_t)((width[s] + kEMmaCols - 1) / kEMmaCols);
+    sw += width[s];
   }
   p.y = y;
   p.ldy = ldy;
   p.add = add ? 1 : 0;
-  p.use_mma_mode = !bf16 ? 0 : (mode == 1 ? 0 : (mode == 2 ? 2 : 1));
-  p.mfma_min = expand_mma_min_default();
-  if (meta.T == 0) return hipSuccess;
-  const int64_t T = meta.T, S = meta.S;
+  if (T == 0) return hipSuccess;
+  if (mma) {
+    // columns per item: enough items to fill the chip about 8 times over, at
+    // least one 128-column step, at most 16 steps
+    const int64_t tiles = (T + kXRows - 1) / kXRows + S + 1;
+    const int64_t steps = (sw + kXStep - 1) / kXStep;
+    const int64_t want = 2048;
+    int64_t spi = (tiles * steps + want - 1) / want;
+    spi = std::max<int64_t>(1, std::min<int64_t>(16, spi));
+    p.cpi = (int32_t)(spi * kXStep);
+    p.chunk_base[0] = 0;
+    for (int s = 0; s < n_slices; ++s)
+      p.chunk_base[s + 1] = p.chunk_base[s] + (int32_t)((width[s] + p.cpi - 1) / p.cpi);
+    for (int s = n_slices; s < kMaxSlices; ++s) p.chunk_base[s + 1] = p.chunk_base[s];
+    p.nck = p.chunk_base[n_slices];
+    const int64_t bound = tiles * p.nck;
+    const int grid = (int)(8 * std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, 256)));
+    switch (R) {
+      case 8: return launch_mma_t<8>(p, grid, stream);
+      case 16: return launch_mma_t<16>(p, grid, stream);
+      case 32: return launch_mma_t<32>(p, grid, stream);
+      case 64: return launch_mma_t<64>(p, grid, stream);
+    }
+    return hipErrorInvalidValue;
+  }
+  // vector n-tile: up to 512 columns, as many as fit the shared B tile
+  p.vec_cols = (int)std::min<int64_t>(512, kEVecLds / (R * e));
+  p.ntiles_vec = 0;
+  for (int s = 0; s < n_slices; ++s) p.ntiles_vec += (int32_t)((width[s] + p.vec_cols - 1) / p.vec_cols);
   const int64_t bound_vec = ((T + kEVecRows - 1) / kEVecRows + S + 1) * p.ntiles_vec;
-  const int64_t bound_mma =
-      p.use_mma_mode ? ((T + kEMmaRows - 1) / kEMmaRows + S + 1) * p.ntiles_mma : 0;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound_vec + bound_mma, 4096));
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound_vec, 4096));
   switch (R) {
     case 8: return bf16 ? launch_t<uint16_t, 8>(p, grid, stream) : launch_t<float, 8>(p, grid, stream);
     case 16: return bf16 ? launch_t<uint16_t, 16>(p, grid, stream) : launch_t<float, 16>(p, grid, stream);

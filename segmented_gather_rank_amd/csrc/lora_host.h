@@ -7,15 +7,13 @@
 namespace lora {
 
 struct ShrinkConfig {
-  int use_mma_mode, mfma_min;
-  int kc, kch;  // k-chunk length and count, shared by both paths
+  int use_mma_mode;  // 1: matrix-core kernel, 0: vector kernel
+  int kc, kch;       // k-chunk length and count
   int grid;
 };
 
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);
 size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32_t R);
-int shrink_mma_min_default();
-int expand_mma_min_default();
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
@@ -37,7 +35,7 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
 // The fused BGMV kernel (one workgroup per token) serves this call?  Decided
 // from host-known sizes only.
 bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64_t *width, int32_t R,
-               bool bf16, int mode);
+               int64_t ldy, bool bf16, int mode);
 hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                        int32_t n_slices, const void *const *A, const int64_t *a_stride,
                        const void *const *B, const int64_t *b_stride, const int64_t *width,

@@ -40,11 +40,6 @@ namespace lora {
 constexpr int kShrinkThreads = 256;
 constexpr int kVecRows = 8;        // tokens per vector m-chunk
 constexpr int kVecSub = 1024;      // k per staged x sub-chunk on the vector path
-constexpr int kMmaRows = 64;       // tokens per matrix-core m-chunk (4 waves x 16)
-constexpr int kMmaKT = 128;        // k per A tile on the matrix-core path
-constexpr int kMmaCols = 128;      // n_slices*r columns per pass (8 MFMA blocks)
-constexpr int kAlStride = kMmaCols + 16;  // bf16 elements per LDS row of the A tile
-constexpr int kMmaOct = kMmaKT * kMmaCols / 8 / kShrinkThreads;  // A octets per thread per tile
 
 struct ShrinkParams {
   MetaView meta;
@@ -60,26 +55,13 @@ struct ShrinkParams {
   // [kch][n_slices][T][R] in sorted-position order
   float *out;
   int32_t u_sorted;
-  int32_t use_mma_mode;  // 0 = never, 1 = by segment length, 2 = always
-  int32_t mfma_min;
   int32_t kc, kch;       // k-chunk length (a multiple of 128) and count
 };
 
 struct ShrinkLds {
-  union {
-    struct {
-      float xs[kVecRows][kVecSub];
-      float red[4][kVecRows][64];
-    } vec;
-    struct {
-      uint16_t al[kMmaKT * kAlStride];  // A tile, row k, column slice*R + j
-    } mma;
-  };
+  float xs[kVecRows][kVecSub];
+  float red[4][kVecRows][64];
 };
-
-__device__ __forceinline__ bool seg_takes_mma(const ShrinkParams &p, int count) {
-  return p.use_mma_mode == 2 || (p.use_mma_mode == 1 && count >= p.mfma_min);
-}
 
 // Store one result: into u (token or sorted order) when d_in is not split,
 // else into the partial sums of k-chunk kc.
@@ -92,6 +74,20 @@ __device__ __forceinline__ void put(const ShrinkParams &p, int R, int s, int64_t
   } else {
     p.out[(((int64_t)kc * p.n_slices + s) * T + pos) * R + j] = v;
   }
+}
+
+// Four consecutive ranks j..j+3 of one result row, as one 16-byte store.
+__device__ __forceinline__ void put4(const ShrinkParams &p, int R, int s, int64_t pos, int j, int kc,
+                                    f32x4 v) {
+  const int64_t T = p.meta.T;
+  float *dst;
+  if (p.kch == 1) {
+    const int64_t row = p.u_sorted ? pos : (int64_t)p.meta.sorted[pos];
+    dst = p.out + ((int64_t)s * T + row) * R + j;
+  } else {
+    dst = p.out + (((int64_t)kc * p.n_slices + s) * T + pos) * R + j;
+  }
+  gstore16f(dst, v);
 }
 
 // ------------------------------------------------------------------ vector path
@@ -135,8 +131,8 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
           const int64_t t = p.meta.sorted[pos0 + row];
           float v[8];
           load8(x + t * p.ldx + k0 + sub + 8 * c, v);
-          *reinterpret_cast<f32x4 *>(&lds.vec.xs[row][8 * c]) = f32x4{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4 *>(&lds.vec.xs[row][8 * c + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+          *reinterpret_cast<f32x4 *>(&lds.xs[row][8 * c]) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4 *>(&lds.xs[row][8 * c + 4]) = f32x4{v[4], v[5], v[6], v[7]};
         }
         __syncthreads();
         staged = sub;
@@ -156,7 +152,7 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
             const int k = e / R;
 #pragma unroll
             for (int m = 0; m < kVecRows; ++m) {
-              const float xv = lds.vec.xs[m][k];  // rows >= `rows` are stale, never stored
+              const float xv = lds.xs[m][k];  // rows >= `rows` are stale, never stored
 #pragma unroll
               for (int i = 0; i < 8; ++i) acc[m][i] = fmaf(xv, a[q][i], acc[m][i]);
             }
@@ -172,13 +168,13 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 #pragma unroll
       for (int m = 0; m < kVecRows; ++m)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds.vec.red[wave][m][8 * jo + i] = acc[m][i];
+        for (int i = 0; i < 8; ++i) lds.red[wave][m][8 * jo + i] = acc[m][i];
     }
     __syncthreads();
     for (int idx = tid; idx < rows * R; idx += kShrinkThreads) {
       const int mm = idx / R, j = idx % R;
-      const float v = ((lds.vec.red[0][mm][j] + lds.vec.red[1][mm][j]) + lds.vec.red[2][mm][j]) +
-                      lds.vec.red[3][mm][j];
+      const float v = ((lds.red[0][mm][j] + lds.red[1][mm][j]) + lds.red[2][mm][j]) +
+                      lds.red[3][mm][j];
       put(p, R, s, pos0 + mm, j, kc, v * sc);
     }
     __syncthreads();
@@ -186,115 +182,147 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 }
 
 // ------------------------------------------------------------- matrix-core path
+//
+// One item = (segment, tile of up to 64 sorted tokens, k-chunk of d_in), all
+// slices' ranks as output columns, in passes of CB 16-column blocks.  Wave w
+// owns token block w (16 tokens) of the tile; a tile with fewer blocks leaves
+// waves whose products are never stored, but every wave helps move the A
+// tiles.  v_mfma_f32_16x16x32_bf16: the A operand is 8 consecutive x values of
+// one token (straight from global memory), the B operand 8 k rows of one
+// output column, read from the A tile in LDS with the gfx950 transposing read.
+// A tiles (128 k rows) are double-buffered in LDS: the next tile and the next
+// x fragments are loaded while the current tile is multiplied, with one
+// barrier per tile.  The result goes out through LDS as 16-byte row pieces.
 
-// One A tile (kMmaKT k rows x ns*R columns) and this lane's x fragments, held
-// in registers between their load and their use.
-struct MmaTile {
-  u32x4 a[kMmaOct];
-  bf16x8 xf[4];
-};
+constexpr int kMThreads = 256;
+constexpr int kMRows = 64;   // tokens per tile
+constexpr int kMKT = 128;    // k rows per A tile
 
-template <int R>
-__device__ __forceinline__ void mma_load_tile(const ShrinkParams &p, MmaTile &tl, int slot, int s0,
-                                              int ns, int64_t kt, int klen, int64_t trow, int g) {
-  const int tid = threadIdx.x;
-  const int per_slice = kMmaKT * R / 8;
-#pragma unroll
-  for (int q = 0; q < kMmaOct; ++q) {
-    const int idx = tid + kShrinkThreads * q;
-    const int sl = idx / per_slice;
-    const int e = 8 * (idx - sl * per_slice);
-    const int k = e / R, j0 = e % R;
-    if (sl < ns && k < klen) {
-      tl.a[q] = *reinterpret_cast<const u32x4 *>(
-          reinterpret_cast<const uint16_t *>(pick(p.A, s0 + sl)) + (int64_t)slot * pick(p.a_stride, s0 + sl) +
-          (kt + k) * R + j0);
-    } else {
-      tl.a[q] = u32x4{0, 0, 0, 0};
-    }
-  }
+// LDS row stride (elements) of an A tile with CB column blocks: the 4 rows that
+// one 16-lane transposing read touches fall in distinct banks
+template <int CB> constexpr int kMLda = CB == 1 ? 16 : CB * 16 + 16;
+
+template <int R, int CB>
+__global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p) {
+  constexpr int SG = CB * 16 / R;   // slices per pass
+  constexpr int QS = R / 16;        // octets of one slice per thread per tile
+  constexpr int LDA = kMLda<CB>;
+  static_assert(SG >= 1 && SG * QS == CB, "column blocks hold whole slices");
+  __shared__ uint16_t at[2][kMKT * LDA];
+  extern __shared__ __align__(16) unsigned char mdyn[];
+  const SegTable tb = seg_table_at(mdyn, p.meta.S);
+  build_items(p.meta, tb, true, [&](int c, int) { return ((c + kMRows - 1) / kMRows) * p.kch; });
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int mrow = lane % 16, kg = lane / 16;
+  const int first = tb.scal[1];
+  const int total = tb.scal[2];
+  const int run = (total + 7) / 8;
+  const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
+  const int lo = xcd * run, hi = min(total, lo + run);
   const uint16_t *x = reinterpret_cast<const uint16_t *>(p.x);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int kk = 32 * g + 8 * c;
-    if (trow >= 0 && kk < klen) {
-      tl.xf[c] = *reinterpret_cast<const bf16x8 *>(x + trow * p.ldx + kt + kk);
-    } else {
-      tl.xf[c] = bf16x8{};
-    }
-  }
-}
+  float *red = reinterpret_cast<float *>(&at[0][0]);  // [64 rows][CB * 16] after the k loop
 
-// Row-major store of a tile's A octets (16-byte LDS writes).
-template <int R>
-__device__ __forceinline__ void mma_store_al(ShrinkLds &lds, const MmaTile &tl, int ns) {
-  const int tid = threadIdx.x;
-  const int per_slice = kMmaKT * R / 8;
-#pragma unroll
-  for (int q = 0; q < kMmaOct; ++q) {
-    const int idx = tid + kShrinkThreads * q;
-    const int sl = idx / per_slice;
-    if (sl < ns) {
-      const int e = 8 * (idx - sl * per_slice);
-      *reinterpret_cast<u32x4 *>(&lds.mma.al[(e / R) * kAlStride + sl * R + e % R]) = tl.a[q];
-    }
-  }
-}
+  for (int item = lo + (int)blockIdx.x / 8; item < hi; item += per) {
+    const int si = find_item_segment(tb, item);
+    const int seg = first + si;
+    const int count = tb.count[seg];
+    const int slot = tb.slot[seg];
+    const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
+    const int ntl = (count + kMRows - 1) / kMRows;
+    const int kc = local / ntl, tile = local % ntl;  // tiles sharing an A chunk are adjacent
+    const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)tile * kMRows;
+    const int rows = min(kMRows, count - tile * kMRows);
+    const int r = 16 * wave + mrow;
+    const int64_t trow = p.meta.sorted[pos0 + (r < rows ? r : 0)];
+    const int64_t kbeg = (int64_t)kc * p.kc;
+    const int64_t kend = min(p.d_in, kbeg + p.kc);
+    const int ntiles = (int)((kend - kbeg + kMKT - 1) / kMKT);
+    const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
+    const uint16_t *xrow = x + trow * p.ldx;
 
-template <int R>
-__device__ __forceinline__ void mma_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_t pos0,
-                         int rows, int kc, float sc) {
-  constexpr int SG = kMmaCols / R;  // slices per pass
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int64_t kbeg = (int64_t)kc * p.kc;
-  const int64_t kend = min(p.d_in, kbeg + p.kc);
-  const int mrow = lane % 16, g = lane / 16;
-  const int row = 16 * wave + mrow;               // this lane's operand row
-  const int64_t trow = row < rows ? (int64_t)p.meta.sorted[pos0 + row] : -1;
-
-  for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
-    const int ns = min(SG, p.n_slices - s0);
-    const int nblk = ns * R / 16;
-    f32x4 acc[kMmaCols / 16];
+    for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
+      const int ns = min(SG, p.n_slices - s0);
+      rsrc_t ar[SG];
 #pragma unroll
-    for (int b = 0; b < kMmaCols / 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // software pipeline: the next tile's loads are in flight while this one
-    // is multiplied
-    MmaTile tl;
-    mma_load_tile<R>(p, tl, slot, s0, ns, kbeg, (int)min((int64_t)kMmaKT, kend - kbeg), trow, g);
-    for (int64_t kt = kbeg; kt < kend; kt += kMmaKT) {
-      __syncthreads();  // the previous tile's LDS reads are done
-      mma_store_al<R>(lds, tl, ns);
-      bf16x8 xf[4];
+      for (int g = 0; g < SG; ++g) {
+        const int sidx = s0 + (g < ns ? g : 0);
+        ar[g] = make_rsrc(reinterpret_cast<const uint16_t *>(pick(p.A, sidx, p.n_slices)) +
+                              (int64_t)slot * pick(p.a_stride, sidx, p.n_slices),
+                          (uint32_t)(p.d_in * R * 2));
+      }
+      // A tile octet q = sl * QS + qq of this thread: slice sl, flat element
+      // 8 (tid + 256 qq) of that slice's [128][R] block; rows past the k-chunk
+      // and slices past n_slices read zeros
+      u32x4 aq[CB];
+      auto load_a = [&](int it) {
+        const int64_t k0 = kbeg + (int64_t)it * kMKT;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xf[c] = tl.xf[c];
-      const int64_t kn = kt + kMmaKT;
-      if (kn < kend) mma_load_tile<R>(p, tl, slot, s0, ns, kn, (int)min((int64_t)kMmaKT, kend - kn), trow, g);
+        for (int q = 0; q < CB; ++q) {
+          const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
+          const int k = e / R, j0 = e % R;
+          const bool ok = sl < ns && k0 + k < kend;
+          aq[q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * R + j0) * 2) : 0x7FFFFFF0u);
+        }
+      };
+      auto store_a = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+          const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
+          *reinterpret_cast<u32x4 *>(&at[buf][(e / R) * LDA + sl * R + e % R]) = aq[q];
+        }
+      };
+      // x fragments of tile it: k-step i, lane k offset 32 i + 8 kg.  Past the
+      // chunk a lane reads a valid element of its row instead: those products
+      // meet zero A rows.  Rows that are not ours are never stored.
+      u32x4 xf[4];
+      auto load_x = [&](int it) {
+        const int64_t k0 = kbeg + (int64_t)it * kMKT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t k = k0 + 32 * i + 8 * kg;
+          xf[i] = gload16(xrow + (k < kend ? k : kbeg));
+        }
+      };
+
+      f32x4 acc[CB];
+#pragma unroll
+      for (int b = 0; b < CB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      load_a(0);
+      load_x(0);
+      __syncthreads();  // earlier readers of both buffers are done
+      store_a(0);
       __syncthreads();
+      for (int it = 0; it < ntiles; ++it) {
+        u32x4 xc[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kk = 32 * g + 8 * c;
+        for (int i = 0; i < 4; ++i) xc[i] = xf[i];
+        load_a(it + 1);  // one past the end reads zeros
+        load_x(it + 1);
+        const uint16_t *a_t = at[it & 1];
 #pragma unroll
-        for (int b = 0; b < kMmaCols / 16; ++b) {
-          if (b < nblk) {
-            const bf16x8 bv = lds_col8(lds.mma.al, kAlStride, kk, 16 * b);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[c], bv, acc[b], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 xa = __builtin_bit_cast(bf16x8, xc[i]);
+#pragma unroll
+          for (int b = 0; b < CB; ++b) {
+            const bf16x8 bv = lds_col8(a_t, LDA, 32 * i + 8 * kg, 16 * b);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv, acc[b], 0, 0, 0);
           }
         }
+        if (it + 1 < ntiles) store_a((it + 1) & 1);
+        __syncthreads();
       }
-    }
-    // epilogue: acc[b][v] = C[16*wave + 4*g + v][16*b + mrow]
+      // epilogue through LDS: acc[b][v] = C[16 wave + 4 kg + v][16 b + mrow];
+      // then whole row pieces of 4 ranks are written with 16-byte stores
 #pragma unroll
-    for (int b = 0; b < kMmaCols / 16; ++b) {
-      if (b < nblk) {
-        const int n = 16 * b + mrow;
-        const int s = s0 + n / R, j = n % R;
+      for (int b = 0; b < CB; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r_ = 16 * wave + 4 * g + v;
-          if (r_ < rows) put(p, R, s, pos0 + r_, j, kc, acc[b][v] * sc);
-        }
+        for (int v = 0; v < 4; ++v) red[(16 * wave + 4 * kg + v) * (CB * 16) + 16 * b + mrow] = acc[b][v];
+      __syncthreads();
+      const int C4 = ns * R / 4;
+      for (int idx = tid; idx < rows * C4; idx += kMThreads) {
+        const int r_ = idx / C4, n4 = 4 * (idx - r_ * C4);
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&red[r_ * (CB * 16) + n4]);
+        put4(p, R, s0 + n4 / R, pos0 + r_, n4 % R, kc, f32x4{v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc});
       }
     }
   }
@@ -307,10 +335,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   __shared__ ShrinkLds lds;
   extern __shared__ __align__(16) unsigned char shrink_dyn[];
   const SegTable tb = seg_table_at(shrink_dyn, p.meta.S);
-  build_items(p.meta, tb, true, [&](int c, int) {
-    const int mc = seg_takes_mma(p, c) ? kMmaRows : kVecRows;
-    return ((c + mc - 1) / mc) * p.kch;
-  });
+  build_items(p.meta, tb, true, [&](int c, int) { return ((c + kVecRows - 1) / kVecRows) * p.kch; });
   const int first = tb.scal[1];
   for (int item = blockIdx.x; item < tb.scal[2]; item += gridDim.x) {
     __syncthreads();  // the previous item's LDS reads are done before this item writes
@@ -321,13 +346,6 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
     const int chunk = local / p.kch, kc = local % p.kch;
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
-    if constexpr (sizeof(E) == 2 && R >= 16) {
-      if (seg_takes_mma(p, count)) {
-        const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kMmaRows;
-        mma_item<R>(p, lds, slot, pos0, min(kMmaRows, count - chunk * kMmaRows), kc, sc);
-        continue;
-      }
-    }
     const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kVecRows;
     vec_item<E, R>(p, lds, slot, pos0, min(kVecRows, count - chunk * kVecRows), kc, sc);
   }
@@ -364,20 +382,27 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(MetaView meta, const
 
 // ------------------------------------------------------------------ host side
 
+// Matrix-core shrink: the bf16 path of SGMV and AUTO for r >= 16 (tile heights
+// follow the segment lengths); the vector kernel serves fp32, r = 8 and BGMV.
+static bool shrink_uses_mma(bool bf16, int32_t R, int mode) { return bf16 && R >= 16 && mode != 1; }
+
 // Chunking chosen from host-known sizes only (no device read), so a call
-// never synchronises: split d_in so that there are about 512 items.
+// never synchronises: split d_in so that there are about 1024 items.
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode) {
   ShrinkConfig c{};
-  c.use_mma_mode = (!bf16 || R < 16) ? 0 : (mode == 1 ? 0 : (mode == 2 ? 2 : 1));
-  c.mfma_min = shrink_mma_min_default();
-  const int64_t rows = c.use_mma_mode ? kMmaRows : kVecRows;
+  c.use_mma_mode = shrink_uses_mma(bf16, R, mode) ? 1 : 0;
+  const int64_t rows = c.use_mma_mode ? kMRows : kVecRows;
   const int64_t chunks = (T + rows - 1) / rows + S;
-  const int64_t tiles = (d_in + kMmaKT - 1) / kMmaKT;
-  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(tiles, (512 + chunks - 1) / chunks));
-  c.kc = (int)(((tiles + want - 1) / want) * kMmaKT);
+  const int64_t tiles = (d_in + kMKT - 1) / kMKT;
+  const int64_t target = c.use_mma_mode ? 1024 : 512;
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(tiles, (target + chunks - 1) / chunks));
+  c.kc = (int)(((tiles + want - 1) / want) * kMKT);
   c.kch = (int)((d_in + c.kc - 1) / c.kc);
-  const int64_t bound = ((T + kVecRows - 1) / kVecRows + S) * c.kch;
-  c.grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, 2048));
+  const int64_t bound = chunks * c.kch;
+  if (c.use_mma_mode)
+    c.grid = (int)(8 * std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, 256)));
+  else
+    c.grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, 2048));
   return c;
 }
 
@@ -391,6 +416,21 @@ static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) 
   hipLaunchKernelGGL((shrink_kernel<E, R>), dim3(grid), dim3(kShrinkThreads),
                      seg_table_bytes(p.meta.S), stream, p);
   return hipGetLastError();
+}
+
+template <int R, int CB>
+static hipError_t launch_mma_t(const ShrinkParams &p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), seg_table_bytes(p.meta.S),
+                     stream, p);
+  return hipGetLastError();
+}
+
+// column blocks per pass: the smallest power of two covering every slice's
+// ranks, at most 8 (whole slices per pass)
+static int mma_col_blocks(int32_t n_slices, int32_t R) {
+  int cb = R / 16;
+  while (cb < 8 && cb * 16 < n_slices * R) cb *= 2;
+  return cb;
 }
 
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
@@ -413,17 +453,30 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   p.slot_scale = slot_scale;
   p.out = c.kch == 1 ? u : reinterpret_cast<float *>(ws);
   p.u_sorted = for_apply ? 1 : 0;
-  p.use_mma_mode = c.use_mma_mode;
-  p.mfma_min = c.mfma_min;
   p.kc = c.kc;
   p.kch = c.kch;
   if (meta.T == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
-  switch (R) {
-    case 8: e = bf16 ? launch_t<uint16_t, 8>(p, c.grid, stream) : launch_t<float, 8>(p, c.grid, stream); break;
-    case 16: e = bf16 ? launch_t<uint16_t, 16>(p, c.grid, stream) : launch_t<float, 16>(p, c.grid, stream); break;
-    case 32: e = bf16 ? launch_t<uint16_t, 32>(p, c.grid, stream) : launch_t<float, 32>(p, c.grid, stream); break;
-    case 64: e = bf16 ? launch_t<uint16_t, 64>(p, c.grid, stream) : launch_t<float, 64>(p, c.grid, stream); break;
+  if (c.use_mma_mode) {
+    const int cb = mma_col_blocks(n_slices, R);
+    switch (R * 16 + cb) {
+      case 16 * 16 + 1: e = launch_mma_t<16, 1>(p, c.grid, stream); break;
+      case 16 * 16 + 2: e = launch_mma_t<16, 2>(p, c.grid, stream); break;
+      case 16 * 16 + 4: e = launch_mma_t<16, 4>(p, c.grid, stream); break;
+      case 16 * 16 + 8: e = launch_mma_t<16, 8>(p, c.grid, stream); break;
+      case 32 * 16 + 2: e = launch_mma_t<32, 2>(p, c.grid, stream); break;
+      case 32 * 16 + 4: e = launch_mma_t<32, 4>(p, c.grid, stream); break;
+      case 32 * 16 + 8: e = launch_mma_t<32, 8>(p, c.grid, stream); break;
+      case 64 * 16 + 4: e = launch_mma_t<64, 4>(p, c.grid, stream); break;
+      case 64 * 16 + 8: e = launch_mma_t<64, 8>(p, c.grid, stream); break;
+    }
+  } else {
+    switch (R) {
+      case 8: e = bf16 ? launch_t<uint16_t, 8>(p, c.grid, stream) : launch_t<float, 8>(p, c.grid, stream); break;
+      case 16: e = bf16 ? launch_t<uint16_t, 16>(p, c.grid, stream) : launch_t<float, 16>(p, c.grid, stream); break;
+      case 32: e = bf16 ? launch_t<uint16_t, 32>(p, c.grid, stream) : launch_t<float, 32>(p, c.grid, stream); break;
+      case 64: e = bf16 ? launch_t<uint16_t, 64>(p, c.grid, stream) : launch_t<float, 64>(p, c.grid, stream); break;
+    }
   }
   // lora_apply's expand reads the partial sums itself; lora_shrink must hand
   // back a finished u
