@@ -76,10 +76,18 @@ typedef struct lora_weight {
  *   seg_slot[S+1]   slot id of each segment in that order, then -1 padding
  *   seg_count[S+1]  tokens per segment, then 0 padding
  *   seg_start[S+2]  0, then running sums of seg_count; T past the last segment
- *   info[4]         num_segments, no_lora (1 when no token has a valid slot,
+ *   info[8]         num_segments, no_lora (1 when no token has a valid slot,
  *                   also for T = 0), num_bad (tokens whose id lies outside
  *                   [-1, S); they are treated as -1), lora_begin (index in
- *                   `sorted` of the first token with an adapter)
+ *                   `sorted` of the first token with an adapter), num_tiles,
+ *                   then 3 zeros
+ *   tiles           work tiles: every segment (the -1 one included) cut into
+ *                   runs of at most 64 consecutive entries of `sorted`; tile i
+ *                   is 68 int32 at tiles + 68 i: slot, rows, first position in
+ *                   `sorted`, 0, then the rows token indices (the rest
+ *                   unspecified).  Tiles follow the order of `sorted`; there
+ *                   are num_tiles <= ceil(T / 64) + S + 1 of them.  The compute
+ *                   kernels take their work from this list.
  * The struct stays valid until its workspace is reused; rebuild it whenever
  * token_slot changes.  Pass it by pointer to the compute calls; they only read
  * it, so any number of them may use one lora_meta at the same time. */
@@ -93,6 +101,7 @@ typedef struct lora_meta {
     int32_t *seg_count;
     int32_t *seg_start;
     int32_t *info;
+    int32_t *tiles;
 } lora_meta;
 
 /* Bytes of device workspace lora_prepare_meta needs for T tokens and S slots. */

@@ -46,7 +46,7 @@ class lora_meta(C.Structure):
     _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("reserved", C.c_int32),
                 ("sorted", C.c_void_p), ("sorted_slot", C.c_void_p), ("seg_slot", C.c_void_p),
                 ("seg_count", C.c_void_p),
-                ("seg_start", C.c_void_p), ("info", C.c_void_p)]
+                ("seg_start", C.c_void_p), ("info", C.c_void_p), ("tiles", C.c_void_p)]
 
 
 _p, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
@@ -91,7 +91,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 1:
+if _lib.lora_abi_version() != 2:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -143,6 +143,15 @@ def _weights(ws, name: str, inner_shape_ok) -> tuple:
     return arr, list(ws)
 
 
+TILE_ROWS = 64          # sorted positions per work tile of the metadata
+TILE_INTS = 4 + TILE_ROWS
+
+
+def max_tiles(num_tokens: int, num_slots: int) -> int:
+    """Capacity of the metadata's work-tile list."""
+    return (num_tokens + TILE_ROWS - 1) // TILE_ROWS + num_slots + 1
+
+
 @dataclass
 class LoraMeta:
     """Slot metadata of one batch on the device (see ``lora_meta`` in the C header).
@@ -170,7 +179,8 @@ class LoraMeta:
         return dict(sorted=self._view(self.c.sorted, T), sorted_slot=self._view(self.c.sorted_slot, T),
                     seg_slot=self._view(self.c.seg_slot, S + 1),
                     seg_count=self._view(self.c.seg_count, S + 1),
-                    seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 4))
+                    seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 8),
+                    tiles=self._view(self.c.tiles, TILE_INTS * max_tiles(T, S)).view(-1, TILE_INTS))
 
 
 def lora_meta_workspace_bytes(num_tokens: int, num_slots: int) -> int:

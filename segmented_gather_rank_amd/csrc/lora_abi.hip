@@ -31,7 +31,7 @@ namespace {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -41,7 +41,7 @@ bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV ||
 size_t esize(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
 
 struct MetaLayout {
-  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, total;
+  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, total;
 };
 MetaLayout meta_layout(int64_t T, int32_t S) {
   MetaLayout L{};
@@ -57,7 +57,9 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
   L.seg_start = off;
   off += align256(sizeof(int32_t) * (size_t)(S + 2));
   L.info = off;
-  off += align256(sizeof(int32_t) * 4);
+  off += align256(sizeof(int32_t) * 8);
+  L.tiles = off;
+  off += align256(sizeof(int32_t) * kTileInts * (size_t)max_tiles(T, S));
   L.total = off;
   return L;
 }
@@ -65,7 +67,8 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
 lora_status check_meta(const lora_meta *m) {
   if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots)
     return LORA_ERR_INVALID_ARG;
-  if (!m->sorted || !m->sorted_slot || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info)
+  if (!m->sorted || !m->sorted_slot || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info ||
+      !m->tiles)
     return LORA_ERR_INVALID_ARG;
   return LORA_OK;
 }
@@ -78,6 +81,7 @@ MetaView view_of(const lora_meta *m) {
   v.seg_count = m->seg_count;
   v.seg_start = m->seg_start;
   v.info = m->info;
+  v.tiles = m->tiles;
   v.T = m->num_tokens;
   v.S = m->num_slots;
   return v;
@@ -181,9 +185,10 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
   out->seg_count = reinterpret_cast<int32_t *>(base + L.seg_count);
   out->seg_start = reinterpret_cast<int32_t *>(base + L.seg_start);
   out->info = reinterpret_cast<int32_t *>(base + L.info);
+  out->tiles = reinterpret_cast<int32_t *>(base + L.tiles);
   const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->sorted_slot, out->seg_slot,
-                                   out->seg_count,
-                                   out->seg_start, out->info, static_cast<hipStream_t>(stream));
+                                   out->seg_count, out->seg_start, out->info, out->tiles,
+                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

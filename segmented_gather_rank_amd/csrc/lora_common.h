@@ -45,6 +45,29 @@ __device__ __forceinline__ f32x4 gload16f(const void *p) { return *(const g_f32x
 __device__ __forceinline__ void gstore16(void *p, u32x4 v) { *(g_u32x4 *)p = v; }
 __device__ __forceinline__ void gstore16f(void *p, f32x4 v) { *(g_f32x4 *)p = v; }
 
+// Sum of kch split-K partial rows of 4 floats at p, p + plane, ..., added in
+// k-chunk order.  The loads go out 8 at a time before any of them is waited
+// for (a loop that waits for each partial would pay one memory round trip per
+// chunk); past the end the last partial is read again and not added.
+__device__ __forceinline__ f32x4 sum_partials4(const float *p, int64_t plane, int kch) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < kch; k0 += 8) {
+    f32x4 w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = gload16f(p + (int64_t)min(k0 + q, kch - 1) * plane);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (k0 + q < kch) {
+        v[0] += w[q][0];
+        v[1] += w[q][1];
+        v[2] += w[q][2];
+        v[3] += w[q][3];
+      }
+    }
+  }
+  return v;
+}
+
 // Load 8 consecutive elements (16 B of bf16 or 32 B of fp32) as fp32.
 __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
   u32x4 w = gload16(p);
@@ -191,10 +214,19 @@ struct MetaView {
   const int32_t *seg_slot;
   const int32_t *seg_count;
   const int32_t *seg_start;
-  const int32_t *info;  // num_segments, no_lora, num_bad, lora_begin
+  const int32_t *info;   // num_segments, no_lora, num_bad, lora_begin, num_tiles
+  const int32_t *tiles;  // kTileInts int32 per tile: slot, rows, pos0, 0, tokens[kTileRows]
   int64_t T;
   int32_t S;
 };
+
+// Work tiles of the metadata: every segment cut into runs of at most
+// kTileRows sorted positions.
+constexpr int kTileRows = 64;
+constexpr int kTileInts = 4 + kTileRows;
+__host__ __device__ constexpr int64_t max_tiles(int64_t T, int32_t S) {
+  return (T + kTileRows - 1) / kTileRows + S + 1;
+}
 
 // ---------------------------------------------------------------- work lists
 //

@@ -86,15 +86,14 @@ __device__ __forceinline__ void load_u8(const ExpandParams &p, int R, int s, int
                                         int64_t t, int j, float v[8]) {
   const int64_t T = p.meta.T;
   const int64_t row = p.u_mode == 0 ? t : pos;
-  load8(p.u + ((int64_t)s * T + row) * R + j, v);
-  if (p.u_mode == 2) {
-    const int64_t plane = (int64_t)p.n_slices * T * R;
-    for (int kc = 1; kc < p.kch; ++kc) {
-      float w[8];
-      load8(p.u + kc * plane + ((int64_t)s * T + pos) * R + j, w);
+  const float *src = p.u + ((int64_t)s * T + row) * R + j;
+  const int64_t plane = (int64_t)p.n_slices * T * R;
+  const int kch = p.u_mode == 2 ? p.kch : 1;
+  const f32x4 a = sum_partials4(src, plane, kch), b = sum_partials4(src + 4, plane, kch);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += w[i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
   }
 }
 
@@ -206,7 +205,6 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
 constexpr int kXThreads = 256;
 constexpr int kXStep = 128;          // columns per step
 constexpr int kXLdb = kXStep + 16;   // LDS row stride (elements) of a B step tile
-constexpr int kXRows = 64;           // tokens per tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -232,35 +230,35 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
   constexpr int KS = RP / 16;                     // MFMA k-steps
   constexpr int BQ = RP * kXStep / 8 / kXThreads;  // B octets per thread per step
   __shared__ XLds<R> lds;
-  extern __shared__ __align__(16) unsigned char xdyn[];
-  const SegTable tb = seg_table_at(xdyn, p.meta.S);
-  build_items(p.meta, tb, p.add != 0, [&](int c, int) { return ((c + kXRows - 1) / kXRows) * p.nck; });
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n = lane % 16, kg = lane / 16;
   const int64_t T = p.meta.T;
-  const int first = tb.scal[1];
-  // XCD-aware order: XCD x (blockIdx mod 8) takes a contiguous run of items,
-  // so tiles that share a chunk of B meet in one L2
-  const int total = tb.scal[2];
+  // items (column chunk, tile) over the metadata's tile list, padded to its
+  // host-known capacity: item = ck * tmax + tile, so tiles that share a chunk
+  // of B are neighbours; XCD x (blockIdx mod 8) takes a contiguous run of items
+  const int tmax = (int)max_tiles(T, p.meta.S);
+  const int total = tmax * p.nck;
   const int run = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
   const int lo = xcd * run, hi = min(total, lo + run);
   uint16_t *y = reinterpret_cast<uint16_t *>(p.y);
 
   for (int item = lo + (int)blockIdx.x / 8; item < hi; item += per) {
-    const int si = find_item_segment(tb, item);
-    const int seg = first + si;
-    const int count = tb.count[seg];
-    const int slot = tb.slot[seg];
-    const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
-    const int tile = local / p.nck, ck = local % p.nck;
+    const int ck = item / tmax, tile = item % tmax;
+    const int32_t *tl = p.meta.tiles + (int64_t)tile * kTileInts;
+    const int ntl = p.meta.info[4];
+    const int slot = tl[0], rows = tl[1];
+    const int64_t pos0 = tl[2];
+    // this lane's token for each possible spread of waves over token blocks
+    // (which one applies depends on rows, loaded in the same round trip)
+    const int32_t tk1 = tl[4 + 16 * wave + n], tk2 = tl[4 + 16 * (wave / 2) + n], tk4 = tl[4 + n];
+    // past the list; tokens without an adapter only need work when storing
+    if (tile >= ntl || (slot < 0 && p.add)) continue;
     const int s = last_le(p.chunk_base, p.n_slices, ck);
     const int64_t w = pick(p.width, s, p.n_slices);
     const int64_t col0 = (int64_t)(ck - pick(p.chunk_base, s, p.n_slices)) * p.cpi;
     const int ncols = (int)min((int64_t)p.cpi, w - col0);
     const int nsteps = (ncols + kXStep - 1) / kXStep;
-    const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)tile * kXRows;
-    const int rows = min(kXRows, count - tile * kXRows);
     const int nb = (rows + 15) / 16;
     const int wpt = nb == 1 ? 4 : (nb == 2 ? 2 : 1);  // waves per token block
     const int tbw = wave / wpt, wq = wave % wpt;
@@ -269,7 +267,7 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
     const int r = 16 * tbw + n;
     const bool rv = tbw < nb && r < rows;
     const int64_t pos = pos0 + (rv ? r : 0);
-    const int64_t t = p.meta.sorted[pos];
+    const int64_t t = rv ? (int64_t)(wpt == 4 ? tk4 : (wpt == 2 ? tk2 : tk1)) : (int64_t)tl[4];
     const int64_t yo = pick(p.offset, s, p.n_slices) + col0;
     uint16_t *yrow = y + t * p.ldy + yo;
     // this lane's y octet of block pair pp in step i: columns
@@ -300,16 +298,7 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
       for (int c = 0; c < KS; ++c) {
         const int j = 16 * c + 4 * kg;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (rv && j < R) {
-          v = gload16f(ub + j);
-          for (int kc = 1; kc < p.kch; ++kc) {  // split-K partial sums, in k-chunk order
-            const f32x4 wv = gload16f(ub + kc * plane + j);
-            v[0] += wv[0];
-            v[1] += wv[1];
-            v[2] += wv[2];
-            v[3] += wv[3];
-          }
-        }
+        if (rv && j < R) v = sum_partials4(ub + j, plane, p.kch);  // split-K sums, in k-chunk order
         uint32_t h[4], l[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
@@ -449,8 +438,7 @@ static hipError_t launch_t(const ExpandParams &p, int grid, hipStream_t stream) 
 
 template <int R>
 static hipError_t launch_mma_t(const ExpandParams &p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), seg_table_bytes(p.meta.S),
-                     stream, p);
+  hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -484,9 +472,9 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   p.add = add ? 1 : 0;
   if (T == 0) return hipSuccess;
   if (mma) {
-    // columns per item: enough items to fill the chip about 8 times over, at
-    // least one 128-column step, at most 16 steps
-    const int64_t tiles = (T + kXRows - 1) / kXRows + S + 1;
+    // columns per item: about 2048 items, at least one 128-column step, at
+    // most 16
+    const int64_t tiles = max_tiles(T, (int32_t)S);
     const int64_t steps = (sw + kXStep - 1) / kXStep;
     const int64_t want = 2048;
     int64_t spi = (tiles * steps + want - 1) / want;
@@ -497,8 +485,12 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
       p.chunk_base[s + 1] = p.chunk_base[s] + (int32_t)((width[s] + p.cpi - 1) / p.cpi);
     for (int s = n_slices; s < kMaxSlices; ++s) p.chunk_base[s + 1] = p.chunk_base[s];
     p.nck = p.chunk_base[n_slices];
+    // no more workgroups than stay resident together (3 or 4 per CU by the
+    // kernel's registers): the rest of the items are taken by the same
+    // workgroups instead of waiting for a slot to be dispatched
     const int64_t bound = tiles * p.nck;
-    const int grid = (int)(8 * std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, 256)));
+    const int64_t resident = 32 * (R <= 16 ? 4 : 3);
+    const int grid = (int)(8 * std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, resident)));
     switch (R) {
       case 8: return launch_mma_t<8>(p, grid, stream);
       case 16: return launch_mma_t<16>(p, grid, stream);

@@ -17,7 +17,7 @@ size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
-                       int32_t *info, hipStream_t stream);
+                       int32_t *info, int32_t *tiles, hipStream_t stream);
 
 // for_apply: u is written in sorted-position order, and with a split d_in the
 // partial sums are left in ws for the expand to add (kch_out reports the split)

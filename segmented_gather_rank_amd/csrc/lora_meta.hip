@@ -14,7 +14,10 @@
 //      key bit (a wave-wide match), and a lane's rank among equal keys is the
 //      popcount of the matching lanes below it; the per-(wave, key) counts are
 //      prefix-summed across the 16 waves in wave order, so equal keys keep
-//      batch order across waves and across chunks.
+//      batch order across waves and across chunks;
+//   4. while scattering, every token also lands in its work tile (its
+//      segment's sorted range cut into runs of 64), and the token that opens a
+//      tile writes the tile's header.
 #include "lora_host.h"
 
 namespace lora {
@@ -27,12 +30,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     int32_t *__restrict__ sorted, int32_t *__restrict__ sorted_slot,
     int32_t *__restrict__ seg_slot,
     int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
-    int32_t *__restrict__ info) {
+    int32_t *__restrict__ info, int32_t *__restrict__ tiles) {
   extern __shared__ int32_t lds[];
   const int K = S + 1;                      // number of keys
   int32_t *cnt = lds;                       // [K] tokens per key
   int32_t *next = lds + K;                  // [K] next free position per key
-  int32_t *wcnt = lds + 2 * K;              // [16][K] per-wave counts, then offsets
+  int32_t *kstart = lds + 2 * K;            // [K] first sorted position per key
+  int32_t *tbase = lds + 3 * K;             // [K] first work tile per key
+  int32_t *wcnt = lds + 4 * K;              // [16][K] per-wave counts, then offsets
   __shared__ int32_t nbad;
 
   const int tid = threadIdx.x;
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
 
   // 2. segments: one wave walks the keys in ascending order
   if (wave == 0) {
-    int seg_base = 0, pos_base = 0;
+    int seg_base = 0, pos_base = 0, tile_base = 0;
     for (int k0 = 0; k0 < K; k0 += kWave) {
       const int k = k0 + lane;
       const int c = k < K ? cnt[k] : 0;
@@ -65,7 +70,13 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       const int seg = seg_base + __popcll(present & lanemask_lt());
       const int incl = wave_inclusive_scan(c);
       const int start = pos_base + incl - c;
-      if (k < K) next[k] = start;
+      const int nt = (c + kTileRows - 1) / kTileRows;
+      const int tincl = wave_inclusive_scan(nt);
+      if (k < K) {
+        next[k] = start;
+        kstart[k] = start;
+        tbase[k] = tile_base + tincl - nt;
+      }
       if (c > 0) {
         seg_slot[seg] = k - 1;
         seg_count[seg] = c;
@@ -73,6 +84,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       }
       seg_base += __popcll(present);
       pos_base += __shfl(incl, kWave - 1, kWave);
+      tile_base += __shfl(tincl, kWave - 1, kWave);
     }
     // padding past the last segment, and the closing offset
     for (int i = seg_base + lane; i < K; i += kWave) {
@@ -85,6 +97,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       info[1] = (T - cnt[0] == 0) ? 1 : 0;
       info[2] = nbad;
       info[3] = cnt[0];
+      info[4] = tile_base;
+      info[5] = info[6] = info[7] = 0;
     }
   }
   __syncthreads();
@@ -123,6 +137,15 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       const int dst = wcnt[wave * K + key] + rank;
       sorted[dst] = (int32_t)t;
       sorted_slot[dst] = key - 1;
+      const int off = dst - kstart[key];
+      int32_t *tl = tiles + (int64_t)(tbase[key] + off / kTileRows) * kTileInts;
+      tl[4 + off % kTileRows] = (int32_t)t;
+      if (off % kTileRows == 0) {
+        tl[0] = key - 1;
+        tl[1] = min(kTileRows, cnt[key] - off);
+        tl[2] = dst;
+        tl[3] = 0;
+      }
     }
     __syncthreads();
     for (int k = tid; k < kMetaWaves * K; k += kMetaThreads) wcnt[k] = 0;
@@ -130,11 +153,11 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   }
 }
 
-size_t meta_lds_bytes(int32_t S) { return sizeof(int32_t) * (size_t)(S + 1) * (2 + kMetaWaves); }
+size_t meta_lds_bytes(int32_t S) { return sizeof(int32_t) * (size_t)(S + 1) * (4 + kMetaWaves); }
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
-                       int32_t *info, hipStream_t stream) {
+                       int32_t *info, int32_t *tiles, hipStream_t stream) {
   const size_t lds = meta_lds_bytes(S);
   if (lds > 65536) {
     // large slot counts need more than the default 64 KB of dynamic LDS
@@ -143,7 +166,7 @@ hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), lds, stream,
-                     token_slot, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info);
+                     token_slot, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles);
   return hipGetLastError();
 }
 

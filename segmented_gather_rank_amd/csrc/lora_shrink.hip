@@ -195,7 +195,6 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 // barrier per tile.  The result goes out through LDS as 16-byte row pieces.
 
 constexpr int kMThreads = 256;
-constexpr int kMRows = 64;   // tokens per tile
 constexpr int kMKT = 128;    // k rows per A tile
 
 // LDS row stride (elements) of an A tile with CB column blocks: the 4 rows that
@@ -209,13 +208,14 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
   constexpr int LDA = kMLda<CB>;
   static_assert(SG >= 1 && SG * QS == CB, "column blocks hold whole slices");
   __shared__ uint16_t at[2][kMKT * LDA];
-  extern __shared__ __align__(16) unsigned char mdyn[];
-  const SegTable tb = seg_table_at(mdyn, p.meta.S);
-  build_items(p.meta, tb, true, [&](int c, int) { return ((c + kMRows - 1) / kMRows) * p.kch; });
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int mrow = lane % 16, kg = lane / 16;
-  const int first = tb.scal[1];
-  const int total = tb.scal[2];
+  // items (k-chunk, tile) over the metadata's tile list, padded to its
+  // host-known capacity: item = kc * tmax + tile, so the tiles of one segment
+  // that share an A chunk are neighbours; XCD x (blockIdx mod 8) takes a
+  // contiguous run of items, and those tiles meet in one L2
+  const int tmax = (int)max_tiles(p.meta.T, p.meta.S);
+  const int total = tmax * p.kch;
   const int run = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
   const int lo = xcd * run, hi = min(total, lo + run);
@@ -223,22 +223,21 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
   float *red = reinterpret_cast<float *>(&at[0][0]);  // [64 rows][CB * 16] after the k loop
 
   for (int item = lo + (int)blockIdx.x / 8; item < hi; item += per) {
-    const int si = find_item_segment(tb, item);
-    const int seg = first + si;
-    const int count = tb.count[seg];
-    const int slot = tb.slot[seg];
-    const int local = item - (si > 0 ? tb.item_end[si - 1] : 0);
-    const int ntl = (count + kMRows - 1) / kMRows;
-    const int kc = local / ntl, tile = local % ntl;  // tiles sharing an A chunk are adjacent
-    const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)tile * kMRows;
-    const int rows = min(kMRows, count - tile * kMRows);
+    const int kc = item / tmax, tile = item % tmax;
+    // the tile's header and this lane's token come in one round trip, with
+    // the tile count
+    const int32_t *tl = p.meta.tiles + (int64_t)tile * kTileInts;
+    const int ntl = p.meta.info[4];
+    const int slot = tl[0], rows = tl[1];
+    const int64_t pos0 = tl[2];
     const int r = 16 * wave + mrow;
-    const int64_t trow = p.meta.sorted[pos0 + (r < rows ? r : 0)];
+    const int64_t trow = tl[4 + r];
+    if (tile >= ntl || slot < 0) continue;  // past the list, or tokens without an adapter
     const int64_t kbeg = (int64_t)kc * p.kc;
     const int64_t kend = min(p.d_in, kbeg + p.kc);
     const int ntiles = (int)((kend - kbeg + kMKT - 1) / kMKT);
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
-    const uint16_t *xrow = x + trow * p.ldx;
+    const uint16_t *xrow = x + (r < rows ? trow : (int64_t)tl[4]) * p.ldx;
 
     for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
       const int ns = min(SG, p.n_slices - s0);
@@ -367,14 +366,7 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(MetaView meta, const
     const int64_t pos = begin + rest % (T - begin);
     const int64_t s = rest / (T - begin);
     const float *src = partial + (s * T + pos) * R + 4 * q;
-    f32x4 v = *reinterpret_cast<const f32x4 *>(src);
-    for (int kc = 1; kc < kch; ++kc) {
-      const f32x4 w = *reinterpret_cast<const f32x4 *>(src + kc * plane);
-      v[0] += w[0];
-      v[1] += w[1];
-      v[2] += w[2];
-      v[3] += w[3];
-    }
+    const f32x4 v = sum_partials4(src, plane, kch);
     const int64_t t = meta.sorted[pos];
     *reinterpret_cast<f32x4 *>(u + (s * T + t) * R + 4 * q) = v;
   }
@@ -391,11 +383,13 @@ static bool shrink_uses_mma(bool bf16, int32_t R, int mode) { return bf16 && R >
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode) {
   ShrinkConfig c{};
   c.use_mma_mode = shrink_uses_mma(bf16, R, mode) ? 1 : 0;
-  const int64_t rows = c.use_mma_mode ? kMRows : kVecRows;
-  const int64_t chunks = (T + rows - 1) / rows + S;
+  const int64_t chunks = c.use_mma_mode ? max_tiles(T, S) : (T + kVecRows - 1) / kVecRows + S;
   const int64_t tiles = (d_in + kMKT - 1) / kMKT;
+  // about 1024 items on the matrix-core path, but at most 8 k-chunks: the
+  // expand adds the partial sums with one batch of loads
   const int64_t target = c.use_mma_mode ? 1024 : 512;
-  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(tiles, (target + chunks - 1) / chunks));
+  const int64_t cap = c.use_mma_mode ? 8 : tiles;
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(std::min(tiles, cap), (target + chunks - 1) / chunks));
   c.kc = (int)(((tiles + want - 1) / want) * kMKT);
   c.kch = (int)((d_in + c.kc - 1) / c.kc);
   const int64_t bound = chunks * c.kch;
@@ -420,8 +414,7 @@ static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) 
 
 template <int R, int CB>
 static hipError_t launch_mma_t(const ShrinkParams &p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), seg_table_bytes(p.meta.S),
-                     stream, p);
+  hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -28,14 +28,14 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 1
+    assert L.lora_abi_version() == 2
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
 
 
 def test_workspace_sizes():
-    assert L.lora_meta_workspace_bytes(256, 32) >= 4 * (256 + 33 + 33 + 34 + 4)
+    assert L.lora_meta_workspace_bytes(256, 32) >= 4 * (2 * 256 + 33 + 33 + 34 + 8 + 68 * (4 + 33))
     assert L.lora_meta_workspace_bytes(0, 1) > 0
     import torch
     b_apply = L.lora_apply_workspace_bytes(4096, 128, 14336, 1, 64, torch.bfloat16)
@@ -72,7 +72,7 @@ def test_meta_rejections():
 def _meta(T=16, S=4):
     m = L.lora_meta()
     m.num_tokens, m.num_slots = T, S
-    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info"):
+    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info", "tiles"):
         setattr(m, f, _base)
     return m
 
@@ -105,6 +105,9 @@ def test_shrink_rejections():
     assert _shrink(u=_ptr(8)) == L.LORA_ERR_INVALID_ARG                    # misaligned
     bad = _meta()
     bad.seg_start = None
+    assert _shrink(meta=bad) == L.LORA_ERR_INVALID_ARG
+    bad = _meta()
+    bad.tiles = None
     assert _shrink(meta=bad) == L.LORA_ERR_INVALID_ARG
     assert _shrink(meta=_meta(T=-1)) == L.LORA_ERR_INVALID_ARG
     # workspace too small: ask for one that needs partial sums

@@ -31,6 +31,19 @@ def _meta_check(L, ts_np, S, label):
     info = got["info"]
     assert info[0] == ref.num_segments and info[1] == ref.no_lora and info[2] == ref.num_bad, label
     assert info[3] == int(np.sum((ts_np < -1) | (ts_np >= S) | (ts_np == -1))), label
+    # work tiles: every segment of the oracle's metadata cut into runs of 64
+    # sorted positions, in order (the library's own tile format)
+    tiles = got["tiles"]
+    k = 0
+    for g in range(ref.num_segments):
+        slot, c, st = int(ref.seg_slot[g]), int(ref.seg_count[g]), int(ref.seg_start[g])
+        for i in range((c + 63) // 64):
+            rows, pos0 = min(64, c - 64 * i), st + 64 * i
+            assert list(tiles[k, :4]) == [slot, rows, pos0, 0], (label, k)
+            assert np.array_equal(tiles[k, 4:4 + rows], ref.sorted[pos0:pos0 + rows]), (label, k)
+            k += 1
+    assert info[4] == k and list(info[5:8]) == [0, 0, 0], label
+    assert k <= L.max_tiles(ts_np.shape[0], S), label
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
@@ -80,4 +93,10 @@ def test_meta_repeatable_and_workspace_reuse(L):
     b = L.lora_prepare_meta(ts, 64, workspace=ws).tensors()
     torch.cuda.synchronize()
     for k in a:
-        assert torch.equal(a[k], b[k]), k
+        if k != "tiles":
+            assert torch.equal(a[k], b[k]), k
+    # tiles: the defined part (headers and the rows token indices of each tile)
+    ta, tb = a["tiles"].cpu().numpy(), b["tiles"].cpu().numpy()
+    for i in range(int(a["info"][4])):
+        rows = int(ta[i, 1])
+        assert np.array_equal(ta[i, :4 + rows], tb[i, :4 + rows]), i
