@@ -46,7 +46,118 @@ def parse():
                     help="total size of the rotated input copies (beats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run under rocprofv3 --pmc: a plain copy of known size, then --steps eager steps")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of --pmc-pass (FETCH_SIZE, WRITE_SIZE) into the "
+                         "traffic summary under profiles/")
     return ap.parse_args()
+
+
+PMC_COPY_ELEMS = 64 << 20   # bf16 elements of the calibration copy (128 MiB read, 128 MiB written)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest():
+    """Hash of the kernel sources: a traffic figure is only reported while the
+    kernels it was measured on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in ("segmented_gather_rank_amd/csrc", "include"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            h.update(f.encode())
+            h.update(open(os.path.join(ROOT, d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def dominant_kernel(c, mode):
+    """Name (substring) of the kernel that lora_apply runs on this workload."""
+    sw = sum(c.widths)
+    e = 4 if c.dtype == "f32" else 2
+    w_tok = (c.n_slices * c.d_in + sw) * c.r_max * e
+    fused = (os.environ.get("LORA_DISABLE_FUSED_BGMV", "0") in ("", "0") and mode != "sgmv" and sw // 8 <= 1024 and c.d_in * e <= 32768 and w_tok <= (1 << 20)
+             and (mode == "bgmv" or c.T <= 16 * c.num_slots))
+    if fused:
+        return "bgmv_fused_kernel"
+    return "expand_mma_kernel" if c.dtype == "bf16" and mode != "bgmv" else "expand_kernel"
+
+
+def traffic_file(c):
+    return os.path.join(PROFILES, f"traffic_{c.name}.md")
+
+
+def read_traffic(c):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel sources."""
+    try:
+        text = open(traffic_file(c)).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith("- ") and ": " in line)
+    if fields.get("- kernel sources") != source_digest():
+        return None
+    return int(fields["- traffic bytes per launch"])
+
+
+def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
+    """FETCH_SIZE / WRITE_SIZE per dispatch (KiB) of the dominant kernel, scaled
+    by what the same counters read for the calibration copy."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert f, f"no counter_collection.csv under {d}"
+        vals = {}
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copy = [v for k, v in vals.items() if "neg" in k.lower()]
+        kern = [v for k, v in vals.items() if kernel_key in k]
+        assert copy and kern, (counter, list(vals))
+        copy_kib = sum(copy[0]) / len(copy[0])
+        kern_kib = sum(kern[0]) / len(kern[0])
+        out[counter] = (kern_kib, copy_kib, len(kern[0]))
+    nbytes = PMC_COPY_ELEMS * 2
+    f_r = nbytes / (out["FETCH_SIZE"][1] * 1024)
+    f_w = nbytes / (out["WRITE_SIZE"][1] * 1024)
+    traffic = out["FETCH_SIZE"][0] * 1024 * f_r + out["WRITE_SIZE"][0] * 1024 * f_w
+    alg = algorithmic(c)
+    alg_b = alg["shrink_bytes"] + alg["expand_bytes"]
+    lines = [
+        f"# HBM traffic of `{kernel_key}` on workload {c.name}",
+        "",
+        "Two rocprofv3 counter runs of `bench.py --pmc-pass` (a bf16 negation of "
+        f"{PMC_COPY_ELEMS} elements as the plain copy of known size, then the workload's steps):",
+        "",
+        "```",
+        "export TMPDIR=/tmp",
+        f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200",
+        f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200",
+        f"python bench.py --config {k} --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "```",
+        "",
+        f"| Counter | `{kernel_key}` KiB/dispatch | copy KiB/dispatch | copy bytes | scale |",
+        "|---|---|---|---|---|",
+        f"| FETCH_SIZE | {out['FETCH_SIZE'][0]:.1f} (n={out['FETCH_SIZE'][2]}) | {out['FETCH_SIZE'][1]:.1f} | {nbytes} | {f_r:.4f} |",
+        f"| WRITE_SIZE | {out['WRITE_SIZE'][0]:.1f} (n={out['WRITE_SIZE'][2]}) | {out['WRITE_SIZE'][1]:.1f} | {nbytes} | {f_w:.4f} |",
+        "",
+        f"Scaled traffic {traffic / 1e6:.3f} MB per launch against {alg_b / 1e6:.3f} MB algorithmic "
+        f"({traffic / alg_b:.3f}x).",
+        "",
+        f"- kernel sources: {source_digest()}",
+        f"- traffic bytes per launch: {int(round(traffic))}",
+        "",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    open(traffic_file(c), "w").write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def algorithmic(c):
@@ -107,15 +218,20 @@ def main():
         sys.exit(2)
 
     import numpy as np
+    import workloads as W
+
+    c = W.config(args.config)
+    alg = algorithmic(c)
+    if args.summarize_pmc:
+        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode))
+        return
+
     import torch
 
     import segmented_gather_rank_amd as L
-    import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = W.config(args.config)
-    alg = algorithmic(c)
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -153,6 +269,18 @@ def main():
         apply_call(i)
 
     K = args.steps
+    if args.pmc_pass:
+        # the calibration copy (reads and writes PMC_COPY_ELEMS bf16 values),
+        # then K eager steps; rocprofv3 --pmc collects the counters per dispatch
+        src = torch.ones(PMC_COPY_ELEMS, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        for i in range(max(K, nrot)):
+            step(i)
+        torch.cuda.synchronize()
+        print(f"pmc pass done: {K} steps of {c.name}", flush=True)
+        return
     # eager warm-up (also builds every set's metadata once)
     for i in range(max(args.warmup, nrot)):
         step(i)
@@ -207,7 +335,8 @@ def main():
     d_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
     achieved = d_bytes / (d_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "lora_apply",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(c),
+                "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + dominant_kernel(c, args.mode) + ")",
                 "kernel_avg_us": round(d_us, 3), "algorithmic_bytes_per_launch": int(d_bytes)}
     step_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
     step_flops = alg["shrink_flops"] + alg["expand_flops"]
