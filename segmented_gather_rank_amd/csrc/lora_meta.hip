@@ -13,8 +13,9 @@
 //      wave, lanes holding the same key find each other with one ballot per
 //      key bit (a wave-wide match), and a lane's rank among equal keys is the
 //      popcount of the matching lanes below it; the per-(wave, key) counts are
-//      prefix-summed across the 16 waves in wave order, so equal keys keep
-//      batch order across waves and across chunks;
+//      prefix-summed across the 16 waves in wave order (one 16-lane DPP row
+//      scan per key), so equal keys keep batch order across waves and across
+//      chunks;
 //   4. while scattering, every token also lands in its work tile (its
 //      segment's sorted range cut into runs of 64), and the token that opens a
 //      tile writes the tile's header.
@@ -24,6 +25,16 @@ namespace lora {
 
 constexpr int kMetaThreads = 1024;
 constexpr int kMetaWaves = kMetaThreads / kWave;
+
+// Inclusive prefix sum inside each row of 16 lanes (DPP row shifts; lanes
+// shifted in from outside the row contribute 0).
+__device__ __forceinline__ int row16_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return v;
+}
 
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const int32_t *__restrict__ token_slot, int64_t T, int32_t S,
@@ -49,10 +60,12 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   if (tid == 0) nbad = 0;
   __syncthreads();
 
-  // 1. histogram
+  // 1. histogram (the first 1024 slot ids stay in registers for the scatter)
   int mybad = 0;
+  int first_v = -1;
   for (int64_t t = tid; t < T; t += kMetaThreads) {
     const int v = token_slot[t];
+    if (t < kMetaThreads) first_v = v;
     const bool ok = v >= -1 && v < S;
     mybad += ok ? 0 : 1;
     atomicAdd(&cnt[ok ? v + 1 : 0], 1);
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const bool valid = t < T;
     int key = 0;
     if (valid) {
-      const int v = token_slot[t];
+      const int v = base == 0 ? first_v : token_slot[t];
       key = (v >= -1 && v < S) ? v + 1 : 0;
     }
     uint64_t same = __ballot(valid);
@@ -123,14 +136,16 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const bool leader = valid && rank == 0;
     if (leader) wcnt[wave * K + key] = __popcll(same);
     __syncthreads();
-    for (int k = tid; k < K; k += kMetaThreads) {
-      int run = next[k];
-      for (int w = 0; w < kMetaWaves; ++w) {
-        const int c = wcnt[w * K + k];
-        wcnt[w * K + k] = run;
-        run += c;
-      }
-      next[k] = run;
+    // per key, prefix of the 16 waves' counts in wave order: the 16 counts of
+    // one key sit in one 16-lane row (thread = 16 key + wave) and are scanned
+    // with DPP row shifts; the row's last lane advances the key's next position
+    for (int k0 = 0; k0 < K; k0 += kMetaThreads / kMetaWaves) {
+      const int k = k0 + tid / kMetaWaves, w = tid % kMetaWaves;
+      const int c = k < K ? wcnt[w * K + k] : 0;
+      const int incl = row16_inclusive_scan(c);
+      const int at = k < K ? next[k] : 0;
+      if (k < K) wcnt[w * K + k] = at + incl - c;
+      if (k < K && w == kMetaWaves - 1) next[k] = at + incl;
     }
     __syncthreads();
     if (valid) {
@@ -147,9 +162,11 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
         tl[3] = 0;
       }
     }
-    __syncthreads();
-    for (int k = tid; k < kMetaWaves * K; k += kMetaThreads) wcnt[k] = 0;
-    __syncthreads();
+    if (base + kMetaThreads < T) {  // the count table starts the next pass at zero
+      __syncthreads();
+      for (int k = tid; k < kMetaWaves * K; k += kMetaThreads) wcnt[k] = 0;
+      __syncthreads();
+    }
   }
 }
 
