@@ -121,6 +121,19 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t num_tokens,
                               int32_t num_slots, void *d_ws, size_t ws_bytes,
                               lora_meta *out, void *stream);
 
+/* Per-slot ranks (argument d_slot_rank of lora_shrink, lora_expand and
+ * lora_apply): NULL, or device int32 [S] giving the rank r_a <= r_max that slot
+ * a's adapter really has.  The stacked buffers are sized for r_max, and an
+ * adapter of smaller rank occupies only its first r_a columns of A and rows of
+ * B, the rest being zero (page "vLLM 源码完全拆解(十八):多 LoRA 服务", section
+ * "两个 LRU 缓存": a slot's buffers are written only in the adapter's valid
+ * range).  With d_slot_rank the kernels read only those ranks, rounded up to a
+ * multiple of 8, so a batch that mixes ranks no longer moves every adapter at
+ * r_max (page "多 LoRA 服务：分段矩阵乘与适配器调度", section "练习": mixed ranks
+ * padded to the largest waste memory traffic).  The result equals the padded
+ * one whenever the padding holds zeros; u[s][t][j] is written as 0 for
+ * j >= r_a.  Values are clamped to [0, r_max]. */
+
 /* Bytes of device workspace lora_shrink needs (split-K partial sums; 0 when
  * the shape needs none).  No initialisation is required; calls that run at the
  * same time need workspaces of their own. */
@@ -136,6 +149,7 @@ lora_status lora_shrink_workspace_bytes(int64_t num_tokens, int32_t num_slots,
  *   d_x           device [T][ldx] of dtype; the first d_in columns are read
  *   A             host array of n_slices descriptors (device pointers)
  *   scale         fp32 multiplier; d_slot_scale: device fp32 [S] or NULL (= 1)
+ *   d_slot_rank   device int32 [S] or NULL (= r_max for every slot), see above
  *   d_u           device fp32 [n_slices][T][r_max], contiguous
  *   d_ws          workspace of lora_shrink_workspace_bytes bytes (may be NULL
  *                 when that size is 0)
@@ -145,8 +159,9 @@ lora_status lora_shrink_workspace_bytes(int64_t num_tokens, int32_t num_slots,
 lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx,
                         int64_t d_in, lora_dtype dtype, int32_t n_slices,
                         const lora_weight *A, int32_t r_max, float scale,
-                        const float *d_slot_scale, float *d_u, lora_mode mode,
-                        void *d_ws, size_t ws_bytes, void *stream);
+                        const float *d_slot_scale, const int32_t *d_slot_rank,
+                        float *d_u, lora_mode mode, void *d_ws, size_t ws_bytes,
+                        void *stream);
 
 /* Expand: for every token t and slice s, columns [offset[s], offset[s]+width[s])
  * of row t of y become (add_into_y ? y : 0) + sum_j u[s][t][j] * B_s[slot(t)][j][n];
@@ -157,6 +172,7 @@ lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx,
  *   B             host array of n_slices descriptors
  *   width, offset host int64 arrays [n_slices]; windows must not overlap and
  *                 must lie inside [0, ldy)
+ *   d_slot_rank   device int32 [S] or NULL; ranks j >= r_a of u and B are not read
  *   d_y           device [T][ldy] of dtype, updated in place
  * Cites page "vLLM 源码完全拆解(十八):多 LoRA 服务", section "两个低秩 GEMM:
  * shrink、expand 与 fp32 中转缓冲" (the expand kernel: per-slice width and start
@@ -164,9 +180,10 @@ lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx,
  * adapter and a cleared output). */
 lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slices,
                         const lora_weight *B, const int64_t *width,
-                        const int64_t *offset, int32_t r_max, void *d_y,
-                        int64_t ldy, lora_dtype dtype, int add_into_y,
-                        lora_mode mode, void *stream);
+                        const int64_t *offset, int32_t r_max,
+                        const int32_t *d_slot_rank, void *d_y, int64_t ldy,
+                        lora_dtype dtype, int add_into_y, lora_mode mode,
+                        void *stream);
 
 /* Bytes of device workspace lora_apply needs: the fp32 rank-r buffer plus the
  * shrink workspace.  No initialisation is required. */
@@ -188,8 +205,9 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx,
                        const lora_weight *A, const lora_weight *B,
                        const int64_t *width, const int64_t *offset,
                        int32_t r_max, float scale, const float *d_slot_scale,
-                       void *d_y, int64_t ldy, int add_into_y, lora_mode mode,
-                       void *d_ws, size_t ws_bytes, void *stream);
+                       const int32_t *d_slot_rank, void *d_y, int64_t ldy,
+                       int add_into_y, lora_mode mode, void *d_ws,
+                       size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *lora_status_string(lora_status status);

@@ -57,13 +57,13 @@ _decl = {
     "lora_prepare_meta": ([_p, _i64, _i32, _p, _sz, C.POINTER(lora_meta), _p], _i32),
     "lora_shrink_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "lora_shrink": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight), _i32,
-                     C.c_float, _p, _p, _i32, _p, _sz, _p], _i32),
+                     C.c_float, _p, _p, _p, _i32, _p, _sz, _p], _i32),
     "lora_expand": ([C.POINTER(lora_meta), _p, _i32, C.POINTER(lora_weight), C.POINTER(_i64),
-                     C.POINTER(_i64), _i32, _p, _i64, _i32, C.c_int, _i32, _p], _i32),
+                     C.POINTER(_i64), _i32, _p, _p, _i64, _i32, C.c_int, _i32, _p], _i32),
     "lora_apply_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "lora_apply": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight),
                     C.POINTER(lora_weight), C.POINTER(_i64), C.POINTER(_i64), _i32, C.c_float, _p,
-                    _p, _i64, C.c_int, _i32, _p, _sz, _p], _i32),
+                    _p, _p, _i64, C.c_int, _i32, _p, _sz, _p], _i32),
 }
 
 
@@ -91,7 +91,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 2:
+if _lib.lora_abi_version() != 3:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -228,10 +228,20 @@ def _x_args(x: torch.Tensor):
     return _dev(x, "x"), x.stride(0), x.shape[1]
 
 
+def _ranks(slot_rank):
+    if slot_rank is None:
+        return None
+    if slot_rank.dtype != torch.int32:
+        raise TypeError("slot_rank must be int32")
+    return _dev(slot_rank, "slot_rank")
+
+
 def lora_shrink(meta: LoraMeta, x: torch.Tensor, A, u: torch.Tensor, scale: float = 1.0,
                 slot_scale: torch.Tensor | None = None, mode: str = "auto",
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """u[s][t][:] = scale * slot_scale[slot] * x[t] @ A[s][slot]; A: list of [S][d_in][r]."""
+                workspace: torch.Tensor | None = None, stream=None,
+                slot_rank: torch.Tensor | None = None) -> torch.Tensor:
+    """u[s][t][:] = scale * slot_scale[slot] * x[t] @ A[s][slot]; A: list of [S][d_in][r].
+    slot_rank: optional int32 [S], ranks each slot's adapter really has."""
     xp, ldx, d_in = _x_args(x)
     A_arr, A_list = _weights(A, "A", lambda i, w: None)
     r = A_list[0].shape[2]
@@ -241,8 +251,8 @@ def lora_shrink(meta: LoraMeta, x: torch.Tensor, A, u: torch.Tensor, scale: floa
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     ss = None if slot_scale is None else _dev(slot_scale, "slot_scale")
     st = _lib.lora_shrink(C.byref(meta.c), xp, ldx, d_in, _dtype(x), n, A_arr, r, float(scale), ss,
-                          _dev(u, "u"), MODES[mode], _dev(workspace, "workspace"), workspace.numel(),
-                          _stream(stream))
+                          _ranks(slot_rank), _dev(u, "u"), MODES[mode], _dev(workspace, "workspace"),
+                          workspace.numel(), _stream(stream))
     _check("lora_shrink", st)
     return u
 
@@ -255,22 +265,23 @@ def _slices(B_list, offsets):
 
 
 def lora_expand(meta: LoraMeta, u: torch.Tensor, B, offsets, y: torch.Tensor, add: bool = True,
-                mode: str = "auto", stream=None) -> torch.Tensor:
+                mode: str = "auto", stream=None, slot_rank: torch.Tensor | None = None) -> torch.Tensor:
     """y[t][off_s:off_s+w_s] (+)= u[s][t] @ B[s][slot]; B: list of [S][r][w_s]."""
     B_arr, B_list = _weights(B, "B", lambda i, w: None)
     width, offs = _slices(B_list, offsets)
     if y.dim() != 2 or y.stride(1) != 1:
         raise ValueError("y must be [T][ldy] with unit column stride")
     st = _lib.lora_expand(C.byref(meta.c), _dev(u, "u"), len(B_list), B_arr, width, offs,
-                          B_list[0].shape[1], _dev(y, "y"), y.stride(0), _dtype(y), int(bool(add)),
-                          MODES[mode], _stream(stream))
+                          B_list[0].shape[1], _ranks(slot_rank), _dev(y, "y"), y.stride(0), _dtype(y),
+                          int(bool(add)), MODES[mode], _stream(stream))
     _check("lora_expand", st)
     return y
 
 
 def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
                slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto",
-               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+               workspace: torch.Tensor | None = None, stream=None,
+               slot_rank: torch.Tensor | None = None) -> torch.Tensor:
     """Shrink then expand into the slices of y (the whole delta of one layer)."""
     xp, ldx, d_in = _x_args(x)
     A_arr, A_list = _weights(A, "A", lambda i, w: None)
@@ -289,7 +300,7 @@ def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, 
     if y.dtype != x.dtype:
         raise TypeError("x and y must share one dtype")
     st = _lib.lora_apply(C.byref(meta.c), xp, ldx, d_in, _dtype(x), n, A_arr, B_arr, width, offs, r,
-                         float(scale), ss, _dev(y, "y"), y.stride(0), int(bool(add)),
+                         float(scale), ss, _ranks(slot_rank), _dev(y, "y"), y.stride(0), int(bool(add)),
                          MODES[mode], _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check("lora_apply", st)
     return y

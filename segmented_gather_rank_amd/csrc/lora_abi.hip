@@ -31,12 +31,13 @@ namespace {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool rank_ok(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
 bool dtype_ok(lora_dtype d) { return d == LORA_F32 || d == LORA_BF16; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV || m == LORA_MODE_SGMV; }
 size_t esize(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
 
@@ -207,11 +208,12 @@ lora_status lora_shrink_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int3
 
 lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in,
                         lora_dtype dtype, int32_t n_slices, const lora_weight *A, int32_t r_max,
-                        float scale, const float *d_slot_scale, float *d_u, lora_mode mode,
-                        void *d_ws, size_t ws_bytes, void *stream) {
+                        float scale, const float *d_slot_scale, const int32_t *d_slot_rank,
+                        float *d_u, lora_mode mode, void *d_ws, size_t ws_bytes, void *stream) {
   lora_status st = check_shrink_args(meta, d_x, ldx, d_in, dtype, n_slices, A, r_max,
                                      d_slot_scale, d_u, mode);
   if (st != LORA_OK) return st;
+  if (!aligned4(d_slot_rank)) return LORA_ERR_INVALID_ARG;
   size_t need = 0;
   st = lora_shrink_workspace_bytes(meta->num_tokens, meta->num_slots, d_in, n_slices, r_max,
                                    dtype, mode, &need);
@@ -222,24 +224,25 @@ lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx, int
   unpack(A, n_slices, ptrs, strides);
   const hipError_t e =
       launch_shrink(view_of(meta), d_x, ldx, d_in, dtype == LORA_BF16, n_slices, ptrs, strides,
-                    r_max, scale, d_slot_scale, d_u, (int)mode, d_ws, false, nullptr,
+                    r_max, scale, d_slot_scale, d_slot_rank, d_u, (int)mode, d_ws, false, nullptr,
                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slices,
                         const lora_weight *B, const int64_t *width, const int64_t *offset,
-                        int32_t r_max, void *d_y, int64_t ldy, lora_dtype dtype, int add_into_y,
-                        lora_mode mode, void *stream) {
+                        int32_t r_max, const int32_t *d_slot_rank, void *d_y, int64_t ldy,
+                        lora_dtype dtype, int add_into_y, lora_mode mode, void *stream) {
   const lora_status st =
       check_expand_args(meta, d_u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
   if (st != LORA_OK) return st;
+  if (!aligned4(d_slot_rank)) return LORA_ERR_INVALID_ARG;
   const void *ptrs[kMaxSlices];
   int64_t strides[kMaxSlices];
   unpack(B, n_slices, ptrs, strides);
   const hipError_t e = launch_expand(view_of(meta), d_u, 0, 1, n_slices, ptrs, strides, width,
-                                     offset, r_max, d_y, ldy, dtype == LORA_BF16, add_into_y,
-                                     (int)mode, static_cast<hipStream_t>(stream));
+                                     offset, r_max, d_slot_rank, d_y, ldy, dtype == LORA_BF16,
+                                     add_into_y, (int)mode, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -256,9 +259,9 @@ lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32
 lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in,
                        lora_dtype dtype, int32_t n_slices, const lora_weight *A,
                        const lora_weight *B, const int64_t *width, const int64_t *offset,
-                       int32_t r_max, float scale, const float *d_slot_scale, void *d_y,
-                       int64_t ldy, int add_into_y, lora_mode mode, void *d_ws, size_t ws_bytes,
-                       void *stream) {
+                       int32_t r_max, float scale, const float *d_slot_scale,
+                       const int32_t *d_slot_rank, void *d_y, int64_t ldy, int add_into_y,
+                       lora_mode mode, void *d_ws, size_t ws_bytes, void *stream) {
   if (!meta) return LORA_ERR_INVALID_ARG;
   size_t need = 0;
   lora_status st = lora_apply_workspace_bytes(meta->num_tokens, meta->num_slots, d_in, n_slices,
@@ -271,6 +274,7 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   if (st != LORA_OK) return st;
   st = check_expand_args(meta, u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
   if (st != LORA_OK) return st;
+  if (!aligned4(d_slot_rank)) return LORA_ERR_INVALID_ARG;
   const size_t ubytes = align256(sizeof(float) * (size_t)n_slices * (size_t)meta->num_tokens *
                                  (size_t)r_max);
   void *sh_ws = static_cast<char *>(d_ws) + ubytes;
@@ -283,19 +287,19 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
                                      r_max, ldy, dtype == LORA_BF16, (int)mode)) {
     const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
-                                     bptr, bstr, width, offset, r_max, scale, d_slot_scale, d_y,
-                                     ldy, add_into_y, s);
+                                     bptr, bstr, width, offset, r_max, scale, d_slot_scale,
+                                     d_slot_rank, d_y, ldy, add_into_y, s);
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   int kch = 1;
   hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
-                               scale, d_slot_scale, u, (int)mode, sh_ws, true, &kch, s);
+                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s);
   if (e != hipSuccess) return LORA_ERR_HIP;
   // the rank-r rows are in sorted order; with a split d_in they are still the
   // partial sums, which the expand adds
   const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
-  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, r_max, d_y,
-                    ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
+  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, r_max,
+                    d_slot_rank, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

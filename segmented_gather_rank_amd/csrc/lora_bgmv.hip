@@ -62,6 +62,7 @@ struct BgmvParams {
   int32_t x_tasks;                   // x staging tasks (<= 2 per thread)
   float scale;
   const float *slot_scale;
+  const int32_t *slot_rank;  // per-slot ranks, or null (every slot uses R)
   void *y;
   int64_t ldy;
   int32_t add;
@@ -97,7 +98,9 @@ template <> struct AOct<float> {
   }
 };
 
-template <typename E, int R>
+// RK: per-slot ranks are given (a separate instantiation, so that the common
+// case carries none of the extra registers)
+template <typename E, int R, bool RK>
 __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   constexpr bool kBf16 = sizeof(E) == 2;
   constexpr int JO = R / 8;             // rank octets per A row
@@ -119,11 +122,13 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   // both metadata loads go out before either is waited for
   const int slot = __builtin_amdgcn_readfirstlane(p.meta.sorted_slot[pos]);
   const int64_t t = __builtin_amdgcn_readfirstlane(p.meta.sorted[pos]);
-  if ((slot < 0 && p.add) || t < 0) return;  // no adapter, add mode: nothing to do
+  // ranks this slot's adapter really has (rank 0: nothing to add)
+  const int rk = slot < 0 ? 0 : (RK ? slot_rank_of(p.slot_rank, slot, R) : R);
+  if ((rk == 0 && p.add) || t < 0) return;  // no adapter, add mode: nothing to do
   const int n_oct = pick(p.oct_base, p.n_slices);
   E *y = reinterpret_cast<E *>(p.y) + t * p.ldy;
 
-  if (slot < 0) {  // store mode, no adapter: the windows become 0
+  if (rk == 0) {  // store mode, no adapter: the windows become 0
     const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int o = tid; o < n_oct; o += kBThreads) {
       const int s = slice_of_oct(p, o);
@@ -146,12 +151,13 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   const int s0 = slice_of_oct(p, oc);
   const int64_t n00 = 8 * (int64_t)(oc - pick(p.oct_base, s0, p.n_slices));
   const E *Bb0 = reinterpret_cast<const E *>(pick(p.B, s0, p.n_slices)) +
-                 (int64_t)slot * pick(p.b_stride, s0, p.n_slices) + n00 + (int64_t)g * rj * pick(p.width, s0, p.n_slices);
+                 (int64_t)slot * pick(p.b_stride, s0, p.n_slices) + n00;  // rank row 0 of the octet
   const int64_t w0 = pick(p.width, s0, p.n_slices);
   const int64_t yoff0 = pick(p.offset, s0, p.n_slices) + n00;
   const rsrc_t xr = make_rsrc(reinterpret_cast<const E *>(p.x) + t * p.ldx, (uint32_t)(p.d_in * sizeof(E)));
   const rsrc_t ar0 = make_rsrc(reinterpret_cast<const E *>(p.A[0]) + (int64_t)slot * p.a_stride[0], a_bytes);
   const rsrc_t yr = make_rsrc(y, (uint32_t)(p.ldy * sizeof(E)));
+  const bool a_live = !RK || 8 * jo < rk;  // this lane's A rank octet is within the slot's rank
   const bool ymine = o0 < n_oct && g == 0 && p.add;
   const uint32_t yoff_b = ymine ? (uint32_t)(yoff0 * sizeof(E)) : 0x7FFFFFF0u;  // past the row: zeros
 
@@ -175,12 +181,22 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   AOct<E> a[NA];
 #pragma unroll
   for (int q = 0; q < NA; ++q)
-    a[q].load(ar0, (uint32_t)(((q * RB + rr) * R + 8 * jo) * sizeof(E)));
+    a[q].load(ar0, a_live ? (uint32_t)(((q * RB + rr) * R + 8 * jo) * sizeof(E)) : 0x7FFFFFF0u);
   // b[jj] holds rank row jj of the batch (jj < span; later ones repeat the last)
   Raw8<E> b[NB];
+  // rank row g * rj + jj; rows at or past the slot's rank are not read: row 0
+  // (live, and read by other lanes anyway) stands in, and meets u = 0 there
+  // (the shrink read no A column past the rank)
+  {
+    const E *Bg = Bb0 + (int64_t)g * rj * w0;
 #pragma unroll
-  for (int jj = 0; jj < NB; ++jj)
-    b[jj].load(Bb0 + (int64_t)(jj < span ? jj : span - 1) * w0);
+    for (int jj = 0; jj < NB; ++jj) {
+      const int jc = jj < span ? jj : span - 1;
+      const E *ptr = Bg + (int64_t)jc * w0;
+      if constexpr (RK) ptr = g * rj + jc < rk ? ptr : Bb0;
+      b[jj].load(ptr);
+    }
+  }
   float yv[8];
   if constexpr (kBf16) {
     const u32x4 w = buf_load16(yr, yoff_b);
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
       if (s > 0 || bb > 0) {
 #pragma unroll
         for (int q = 0; q < NA; ++q)
-          a[q].load(ar, (uint32_t)((((bb + q) * RB + rr) * R + 8 * jo) * sizeof(E)));
+          a[q].load(ar, a_live ? (uint32_t)((((bb + q) * RB + rr) * R + 8 * jo) * sizeof(E)) : 0x7FFFFFF0u);
       }
       if constexpr (kBf16) {
         const uint32_t *xw = reinterpret_cast<const uint32_t *>(bgmv_lds) + rr;
@@ -294,13 +310,13 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   for (int o = o0, it = 0; o < n_oct; o += ostep, ++it) {
     int s = s0;
     int64_t n0 = n00, w = w0, yoff = yoff0;
-    const E *Bb = Bb0;  // rank row g * rj of this octet's columns
+    const E *Bb = Bb0;  // rank row 0 of this octet's columns
     if (it > 0) {
       s = slice_of_oct(p, o);
       n0 = 8 * (int64_t)(o - pick(p.oct_base, s, p.n_slices));
       w = pick(p.width, s, p.n_slices);
       Bb = reinterpret_cast<const E *>(pick(p.B, s, p.n_slices)) + (int64_t)slot * pick(p.b_stride, s, p.n_slices) +
-           n0 + (int64_t)g * rj * w;
+           n0;
       yoff = pick(p.offset, s, p.n_slices) + n0;
       if (g == 0 && p.add) load8(y + yoff, yv);
     }
@@ -308,8 +324,12 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
     for (int jb = 0; jb < rj; jb += NB) {
       if (it > 0 || jb > 0) {
 #pragma unroll
-        for (int jj = 0; jj < NB; ++jj)
-          b[jj].load(Bb + (int64_t)(jb + (jj < span ? jj : span - 1)) * w);
+        for (int jj = 0; jj < NB; ++jj) {
+          const int jc = jb + (jj < span ? jj : span - 1);
+          const E *ptr = Bb + ((int64_t)g * rj + jc) * w;
+          if constexpr (RK) ptr = g * rj + jc < rk ? ptr : Bb;
+          b[jj].load(ptr);
+        }
       }
       if constexpr (kBf16) {  // rank rows come in pairs (j even, j + 1)
 #pragma unroll
@@ -377,7 +397,10 @@ bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64
 
 template <typename E, int R>
 static hipError_t launch_t(const BgmvParams &p, int grid, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((bgmv_fused_kernel<E, R>), dim3(grid), dim3(kBThreads), lds, stream, p);
+  if (p.slot_rank)
+    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true>), dim3(grid), dim3(kBThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false>), dim3(grid), dim3(kBThreads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -385,7 +408,7 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
                        int32_t n_slices, const void *const *A, const int64_t *a_stride,
                        const void *const *B, const int64_t *b_stride, const int64_t *width,
                        const int64_t *offset, int32_t R, float scale, const float *slot_scale,
-                       void *y, int64_t ldy, int add, hipStream_t stream) {
+                       const int32_t *slot_rank, void *y, int64_t ldy, int add, hipStream_t stream) {
   BgmvParams p{};
   p.meta = meta;
   p.x = x;
@@ -411,6 +434,7 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
   bgmv_x_plan(d_in, R, bf16, p.n_inst, p.x_tasks, lds);
   p.scale = scale;
   p.slot_scale = slot_scale;
+  p.slot_rank = slot_rank;
   p.y = y;
   p.ldy = ldy;
   p.add = add ? 1 : 0;

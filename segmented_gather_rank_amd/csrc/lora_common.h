@@ -206,6 +206,17 @@ __device__ __forceinline__ int last_le(const int32_t (&prefix)[N], int n, int v)
   return s;
 }
 
+// ---------------------------------------------------------------- slot ranks
+
+// Ranks a kernel reads for a slot: its own rank rounded up to whole octets of
+// 8, clamped to [0, R]; R when no per-slot ranks are given.  (The rank is
+// uniform across a workgroup.)
+__device__ __forceinline__ int slot_rank_of(const int32_t *slot_rank, int slot, int R) {
+  if (!slot_rank) return R;
+  const int r = __builtin_amdgcn_readfirstlane(slot_rank[slot]);
+  return r <= 0 ? 0 : (r >= R ? R : (r + 7) & ~7);
+}
+
 // ---------------------------------------------------------------- metadata view
 
 struct MetaView {

@@ -51,6 +51,7 @@ struct ExpandParams {
   void *y;
   int64_t ldy;
   int32_t add;
+  const int32_t *slot_rank;  // per-slot ranks, or null (every slot uses R)
 };
 
 template <typename E, int R>
@@ -102,6 +103,7 @@ __device__ __forceinline__ void load_u8(const ExpandParams &p, int R, int s, int
 template <typename E, int R>
 __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E, R> &lds, int slot, int64_t pos0,
                              int rows, int s, int nt) {
+  const int rk = slot >= 0 ? slot_rank_of(p.slot_rank, slot, R) : 0;  // ranks past rk are not read
   const int tid = threadIdx.x;
   const int NC = p.vec_cols;           // columns of this tile (a multiple of 8)
   const int OCT = NC / 8;
@@ -127,7 +129,7 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
     for (int idx = tid; idx < R * OCT; idx += kExpThreads) {
       const int j = idx / OCT, o = idx % OCT;
       Raw8<E> v;
-      if (nbase + 8 * o < w) v.load(Bb + (int64_t)j * w + 8 * o); else v.zero();
+      if (nbase + 8 * o < w && j < rk) v.load(Bb + (int64_t)j * w + 8 * o); else v.zero();
       if constexpr (sizeof(E) == 2) {
         *reinterpret_cast<u32x4 *>(&lds.bt[j * NC + 8 * o]) = v.w;
       } else {
@@ -139,8 +141,8 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
     for (int idx = tid; idx < rows * (R / 8); idx += kExpThreads) {
       const int m = idx / (R / 8), j = 8 * (idx % (R / 8));
       const int64_t t = p.u_mode == 0 ? (int64_t)p.meta.sorted[pos0 + m] : 0;
-      float v[8];
-      load_u8(p, R, s, pos0 + m, t, j, v);
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j < rk) load_u8(p, R, s, pos0 + m, t, j, v);
       *reinterpret_cast<f32x4 *>(&lds.us[m][j]) = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4 *>(&lds.us[m][j + 4]) = f32x4{v[4], v[5], v[6], v[7]};
     }
@@ -287,6 +289,7 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
       continue;
     }
 
+    const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
     // ---- rank-r rows of this lane's token, split into bf16 hi + lo: k-step c
     // holds ranks 16 c + 4 kg .. + 3
     s16x4 uh[KS], ul[KS];
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
       for (int c = 0; c < KS; ++c) {
         const int j = 16 * c + 4 * kg;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (rv && j < R) v = sum_partials4(ub + j, plane, p.kch);  // split-K sums, in k-chunk order
+        if (rv && j < rk) v = sum_partials4(ub + j, plane, p.kch);  // split-K sums, in k-chunk order
         uint32_t h[4], l[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
         const int idx = tid + kXThreads * q;
         const int j = idx / 16, h = idx % 16;
         const int64_t c = col0 + (int64_t)i * kXStep + 8 * h;
-        bq[q] = buf_load16(br, (uint32_t)(((int64_t)j * w + c) * 2));
+        bq[q] = buf_load16(br, j < rk ? (uint32_t)(((int64_t)j * w + c) * 2) : 0x7FFFFFF0u);
       }
     };
     // permuted store: the 8 columns 32 g32 + 8 g4 .. + 7 go to block 2 g32
@@ -448,8 +451,8 @@ bool expand_uses_mma(bool bf16, int mode) { return bf16 && mode != 1; }
 
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
-                         const int64_t *offset, int32_t R, void *y, int64_t ldy, bool bf16,
-                         int add, int mode, hipStream_t stream) {
+                         const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y,
+                         int64_t ldy, bool bf16, int add, int mode, hipStream_t stream) {
   ExpandParams p{};
   p.meta = meta;
   p.u = u;
@@ -470,6 +473,7 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   p.y = y;
   p.ldy = ldy;
   p.add = add ? 1 : 0;
+  p.slot_rank = slot_rank;
   if (T == 0) return hipSuccess;
   if (mma) {
     // columns per item: about 2048 items, at least one 128-column step, at

@@ -23,14 +23,14 @@ hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t 
 // partial sums are left in ws for the expand to add (kch_out reports the split)
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
-                         int32_t R, float scale, const float *slot_scale, float *u, int mode,
-                         void *ws, bool for_apply, int *kch_out, hipStream_t stream);
+                         int32_t R, float scale, const float *slot_scale, const int32_t *slot_rank,
+                         float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream);
 // u_mode 0: u [n_slices][T][R] in token order; 1: the same in sorted-position
 // order; 2: kch partial sums [kch][n_slices][T][R] in sorted-position order
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
-                         const int64_t *offset, int32_t R, void *y, int64_t ldy, bool bf16,
-                         int add, int mode, hipStream_t stream);
+                         const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y,
+                         int64_t ldy, bool bf16, int add, int mode, hipStream_t stream);
 
 // The fused BGMV kernel (one workgroup per token) serves this call?  Decided
 // from host-known sizes only.
@@ -40,7 +40,7 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
                        int32_t n_slices, const void *const *A, const int64_t *a_stride,
                        const void *const *B, const int64_t *b_stride, const int64_t *width,
                        const int64_t *offset, int32_t R, float scale, const float *slot_scale,
-                       void *y, int64_t ldy, int add, hipStream_t stream);
+                       const int32_t *slot_rank, void *y, int64_t ldy, int add, hipStream_t stream);
 bool fused_disabled();
 
 }  // namespace lora

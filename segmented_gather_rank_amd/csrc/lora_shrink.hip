@@ -50,6 +50,7 @@ struct ShrinkParams {
   int32_t n_slices;
   float scale;
   const float *slot_scale;
+  const int32_t *slot_rank;  // per-slot ranks, or null (every slot uses R)
   // kch == 1: out is u [n_slices][T][R], rows in token order, or in sorted-
   // position order when u_sorted is set; kch > 1: out holds the partial sums
   // [kch][n_slices][T][R] in sorted-position order
@@ -94,7 +95,7 @@ __device__ __forceinline__ void put4(const ShrinkParams &p, int R, int s, int64_
 
 template <typename E, int R>
 __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, int slot, int64_t pos0,
-                         int rows, int kc, float sc) {
+                         int rows, int kc, float sc, int rk) {
   constexpr int JO = R / 8;                       // rank octets per k row
   constexpr int VA = sizeof(E) == 2 ? 8 : 4;      // A loads in flight per thread
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -121,7 +122,7 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 #pragma unroll
       for (int q = 0; q < VA; ++q) {
         const int e = 8 * (tid + kShrinkThreads * q);
-        if (e < nel) a[q].load(Ab + e);
+        if (e < nel && e % R < rk) a[q].load(Ab + e); else a[q].zero();
       }
       if (staged != sub) {
         __syncthreads();  // earlier readers of xs are done
@@ -142,7 +143,7 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 #pragma unroll
           for (int q = 0; q < VA; ++q) {
             const int e = base + 8 * (tid + kShrinkThreads * q);
-            if (e < nel) a[q].load(Ab + e);
+            if (e < nel && e % R < rk) a[q].load(Ab + e); else a[q].zero();
           }
         }
 #pragma unroll
@@ -237,6 +238,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
     const int64_t kend = min(p.d_in, kbeg + p.kc);
     const int ntiles = (int)((kend - kbeg + kMKT - 1) / kMKT);
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
+    const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
     const uint16_t *xrow = x + (r < rows ? trow : (int64_t)tl[4]) * p.ldx;
 
     for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
         for (int q = 0; q < CB; ++q) {
           const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
           const int k = e / R, j0 = e % R;
-          const bool ok = sl < ns && k0 + k < kend;
+          const bool ok = sl < ns && k0 + k < kend && j0 < rk;
           aq[q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * R + j0) * 2) : 0x7FFFFFF0u);
         }
       };
@@ -346,7 +348,8 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     const int chunk = local / p.kch, kc = local % p.kch;
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
     const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kVecRows;
-    vec_item<E, R>(p, lds, slot, pos0, min(kVecRows, count - chunk * kVecRows), kc, sc);
+    vec_item<E, R>(p, lds, slot, pos0, min(kVecRows, count - chunk * kVecRows), kc, sc,
+                   slot_rank_of(p.slot_rank, slot, R));
   }
 }
 
@@ -428,8 +431,8 @@ static int mma_col_blocks(int32_t n_slices, int32_t R) {
 
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
-                         int32_t R, float scale, const float *slot_scale, float *u, int mode,
-                         void *ws, bool for_apply, int *kch_out, hipStream_t stream) {
+                         int32_t R, float scale, const float *slot_scale, const int32_t *slot_rank,
+                         float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream) {
   const ShrinkConfig c = plan_shrink(meta.T, meta.S, d_in, R, bf16, mode);
   if (kch_out) *kch_out = c.kch;
   ShrinkParams p{};
@@ -444,6 +447,7 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   p.n_slices = n_slices;
   p.scale = scale;
   p.slot_scale = slot_scale;
+  p.slot_rank = slot_rank;
   p.out = c.kch == 1 ? u : reinterpret_cast<float *>(ws);
   p.u_sorted = for_apply ? 1 : 0;
   p.kc = c.kc;

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 2
+    assert L.lora_abi_version() == 3
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -89,7 +89,8 @@ def _shrink(meta=None, ldx=64, d_in=64, dtype=1, n=1, A=None, r=16, ss=None, u=N
     meta = meta if meta is not None else _meta()
     A = A if A is not None else _w(n, d_in * r)
     return _call("lora_shrink", C.byref(meta), _ptr(), ldx, d_in, dtype, n, A, r, C.c_float(1.0),
-                 ss, u if u is not None else _ptr(), mode, ws if ws is not None else _ptr(), ws_bytes, None)
+                 ss, None, u if u is not None else _ptr(), mode, ws if ws is not None else _ptr(), ws_bytes,
+                 None)
 
 
 def test_shrink_rejections():
@@ -121,7 +122,7 @@ def _expand(n=2, widths=(64, 32), offsets=(0, 64), r=16, ldy=96, B=None, y=None,
     wd = (C.c_int64 * n)(*widths[:n])
     of = (C.c_int64 * n)(*offsets[:n])
     B = B if B is not None else (L.lora_weight * n)(*[L.lora_weight(_base, r * w) for w in widths[:n]])
-    return _call("lora_expand", C.byref(_meta()), _ptr(), n, B, wd, of, r,
+    return _call("lora_expand", C.byref(_meta()), _ptr(), n, B, wd, of, r, None,
                  y if y is not None else _ptr(), ldy, 1, 1, mode, None)
 
 
@@ -142,7 +143,7 @@ def test_apply_rejections():
     A, B = _w(1, 64 * 16), _w(1, 16 * 64)
     wd, of = (C.c_int64 * 1)(64), (C.c_int64 * 1)(0)
     args = lambda ws, ws_bytes: (C.byref(_meta()), _ptr(), 64, 64, 1, n, A, B, wd, of, 16,
-                                 C.c_float(1.0), None, _ptr(), 64, 1, 0, ws, ws_bytes, None)
+                                 C.c_float(1.0), None, None, _ptr(), 64, 1, 0, ws, ws_bytes, None)
     assert _call("lora_apply", *args(_ptr(), 16)) == L.LORA_ERR_WORKSPACE
     assert _call("lora_apply", None, *args(_ptr(), 1 << 15)[1:]) == L.LORA_ERR_INVALID_ARG
     assert _call("lora_apply", *args(None, 1 << 15)) == L.LORA_ERR_WORKSPACE

@@ -119,3 +119,39 @@ def test_modes_agree(L):
     ref = oracle_rows(c, np.arange(c.T))
     for m, v in outs.items():
         assert np.all(np.abs(v - ref) <= 2e-2 * (1 + np.abs(ref))), m
+
+
+def many_slices_case(seed, dtype, r, n_slices=8):
+    """Eight packed slices of uneven widths with gaps between windows: the
+    matrix-core shrink covers the slices' ranks in one or two passes of output
+    columns, and the expand walks many (slice, column chunk) pairs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.array([1] * 10 + [40, 2, 90, 17, 1, 66], np.int64)
+    S = 5
+    req = rng.integers(-1, S, lengths.shape[0]).astype(np.int32)
+    widths = [24, 136, 8, 64, 200, 40, 16, 128][:n_slices]
+    offsets, o = [], 0
+    for w in widths:
+        offsets.append(o)
+        o += w + 8
+    c = W.make_case(name=f"slices{n_slices}_{dtype}_r{r}", seed=seed, rng=rng, dtype=dtype,
+                    lengths=lengths, req_slot=req, num_slots=S, d_in=392, r_max=r, widths=widths,
+                    offsets=offsets, ldy=o, scale=1.25, weight_sd=0.05)
+    return c
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("r", [8, 16, 32, 64])
+@pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
+def test_apply_many_slices(L, dtype, r, mode):
+    c = many_slices_case(300 + r, dtype, r)
+    print(f"[slices] {c.name} T={c.T} mode={mode}", flush=True)
+    d = DevCase(c)
+    for add in (True, False):
+        y, _ = d.apply(L, mode=mode, add=add)
+        got = from_dev(y)
+        check_rows(c, got, oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
+        outside = np.ones(c.ldy, bool)
+        for w, o in zip(c.widths, c.offsets):
+            outside[o:o + w] = False
+        assert _bits_equal(got[:, outside], c.y0[:, outside])

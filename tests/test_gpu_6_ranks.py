@@ -1,0 +1,123 @@
+"""Per-slot ranks (d_slot_rank): the kernels read only the ranks each slot's
+adapter really has (rounded up to 8), so padding past them is never touched.
+The tests fill that padding with NaN: a kernel that reads it turns its output
+into NaN.  The oracle runs on the zero-padded factors, whose result is the
+defined one (a slot's buffers hold zeros past its rank)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import DELTA_L2, DevCase, as_f64, check_rows, from_dev, oracle_rows, to_dev
+from test_gpu_2_apply import small_case
+from test_gpu_4_edges import integer_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import segmented_gather_rank_amd as lib
+    return lib
+
+
+def nan_padded(c):
+    """Copies of A and B whose entries past each slot's rank rounded up to 8
+    are NaN (between the rank and that bound they stay zero)."""
+    nan = W.bf16_round(np.array([np.nan], np.float32))[0] if c.dtype == "bf16" else np.float32(np.nan)
+    A, B = [], []
+    for a, b in zip(c.A, c.B):
+        a, b = a.copy(), b.copy()
+        for slot in range(c.num_slots):
+            r8 = min(c.r_max, (int(c.ranks[slot]) + 7) // 8 * 8)
+            a[slot, :, r8:] = nan
+            b[slot, r8:, :] = nan
+        A.append(a)
+        B.append(b)
+    return A, B
+
+
+class RankedDev(DevCase):
+    def __init__(self, c):
+        super().__init__(c)
+        A, B = nan_padded(c)
+        self.A = [to_dev(a, c.dtype) for a in A]
+        self.B = [to_dev(b, c.dtype) for b in B]
+        self.ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).cuda()
+
+    def apply_ranked(self, L, mode="auto", add=True):
+        meta = L.lora_prepare_meta(self.token_slot, self.c.num_slots)
+        y = self.y0.clone()
+        L.lora_apply(meta, self.x, self.A, self.B, self.c.offsets, y, scale=self.c.scale,
+                     slot_scale=self.slot_scale, add=add, mode=mode, slot_rank=self.ranks)
+        return y, meta
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("r", [8, 16, 32, 64])
+@pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
+def test_ranked_apply_small(L, dtype, r, mode):
+    c = small_case(500 + r, dtype, r)
+    print(f"[ranks] {c.name} ranks={sorted(set(c.ranks.tolist()))} mode={mode}", flush=True)
+    d = RankedDev(c)
+    for add in (True, False):
+        y, _ = d.apply_ranked(L, mode=mode, add=add)
+        got = from_dev(y)
+        check_rows(c, got, oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["auto", "sgmv"])
+def test_ranked_shrink_and_expand_alone(L, dtype, mode):
+    c = small_case(600, dtype, 64)
+    d = RankedDev(c)
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    u = torch.full((c.n_slices, c.T, c.r_max), float("nan"), dtype=torch.float32, device="cuda")
+    L.lora_shrink(meta, d.x, d.A, u, scale=c.scale, slot_scale=d.slot_scale, mode=mode, slot_rank=d.ranks)
+    torch.cuda.synchronize()
+    _, uref = oracle_rows(c, np.arange(c.T), return_u=True)
+    got = u.cpu().numpy()
+    has = c.token_slot >= 0
+    for s in range(c.n_slices):
+        g = got[s][has].astype(np.float64)
+        ref = uref[has, s, :]
+        tol = 1e-4 if dtype == "f32" else 2e-2
+        assert np.all(np.abs(g - ref) <= tol * (1 + np.abs(ref))), s
+        # ranks past each token's slot rank are written as exact zeros
+        r8 = np.minimum(c.r_max, (c.ranks[c.token_slot[has]] + 7) // 8 * 8)
+        for i in range(g.shape[0]):
+            assert np.all(g[i, r8[i]:] == 0.0)
+    # the expand alone, from the oracle's u (zeros past the ranks)
+    y = d.y0.clone()
+    uu = torch.from_numpy(np.ascontiguousarray(np.transpose(uref, (1, 0, 2))).astype(np.float32)).cuda()
+    uu[:, ~torch.from_numpy(has).cuda(), :] = 0
+    L.lora_expand(meta, uu, d.B, c.offsets, y, add=True, mode=mode, slot_rank=d.ranks)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), "expand alone")
+
+
+@pytest.mark.parametrize("k", [4, 5])
+@pytest.mark.parametrize("mode", ["auto", "bgmv"])
+def test_ranked_workloads(L, k, mode):
+    """The mixed-rank workloads at full size, sampled rows."""
+    c = W.config(k)
+    print(f"[ranks] workload {c.name} mode={mode}", flush=True)
+    d = RankedDev(c)
+    y, _ = d.apply_ranked(L, mode=mode)
+    rng = np.random.Generator(np.random.PCG64(k))
+    rows = np.sort(rng.choice(c.T, 96, replace=False))
+    check_rows(c, from_dev(y)[rows], oracle_rows(c, rows), c.name)
+
+
+@pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
+def test_ranked_integer_bit_exact(L, mode):
+    c = integer_case(21, [1] * 200 + [300, 77], 16, 2048, [1024, 512], 64, 2.0)
+    c.ranks = np.random.Generator(np.random.PCG64(3)).choice(np.array([8, 16, 32, 64], np.int32), 16)
+    for a, b in zip(c.A, c.B):   # zero the factors past each slot's rank (the defined padding)
+        for slot in range(16):
+            a[slot, :, c.ranks[slot]:] = 0
+            b[slot, c.ranks[slot]:, :] = 0
+    ref = oracle_rows(c, np.arange(c.T))
+    assert np.all(ref == np.round(ref)) and np.max(np.abs(ref)) <= 256
+    d = RankedDev(c)
+    y, _ = d.apply_ranked(L, mode=mode)
+    assert np.array_equal(as_f64(from_dev(y)), ref)
