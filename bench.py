@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline decode case)")
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
+    ap.add_argument("--slot-ranks", action="store_true",
+                    help="pass each slot's own rank (the kernels then skip the zero-padded ranks)")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the rotated input copies (beats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -160,25 +162,33 @@ def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
     print("\n".join(lines))
 
 
-def algorithmic(c):
+def algorithmic(c, ranked=False):
     """Bytes and flops the method must move/compute for one batch (per kernel).
 
     A and B slot blocks of every distinct slot used are read once; x rows of
     tokens with an adapter are read once; the y windows of those tokens are
     read and written once (add into y).  Metadata and the fp32 rank-r buffer
-    are overheads and are not counted.  r is the padded r_max the kernels read.
+    are overheads and are not counted.  r is the padded r_max the kernels read,
+    or, with per-slot ranks, each slot's own rank rounded up to 8.
     """
     import numpy as np
     ts = c.token_slot
     lora = ts >= 0
-    U = int(np.unique(ts[lora]).shape[0])
+    used = np.unique(ts[lora])
+    U = int(used.shape[0])
     TL = int(lora.sum())
     e = 4 if c.dtype == "f32" else 2
     sw = sum(c.widths)
-    shrink_bytes = U * c.n_slices * c.d_in * c.r_max * e + TL * c.d_in * e
-    expand_bytes = U * sw * c.r_max * e + TL * sw * e * 2
-    shrink_flops = 2 * TL * c.r_max * c.n_slices * c.d_in
-    expand_flops = 2 * TL * c.r_max * sw
+    if ranked:
+        r_slot = np.minimum(c.r_max, (np.asarray(c.ranks, np.int64) + 7) // 8 * 8)
+        r_sum = int(r_slot[used].sum())                 # ranks over the distinct slots
+        r_tok = int(r_slot[ts[lora]].sum())             # ranks over the LoRA tokens
+    else:
+        r_sum, r_tok = U * c.r_max, TL * c.r_max
+    shrink_bytes = r_sum * c.n_slices * c.d_in * e + TL * c.d_in * e
+    expand_bytes = r_sum * sw * e + TL * sw * e * 2
+    shrink_flops = 2 * r_tok * c.n_slices * c.d_in
+    expand_flops = 2 * r_tok * sw
     return dict(U=U, T_lora=TL, shrink_bytes=shrink_bytes, expand_bytes=expand_bytes,
                 shrink_flops=shrink_flops, expand_flops=expand_flops)
 
@@ -221,7 +231,7 @@ def main():
     import workloads as W
 
     c = W.config(args.config)
-    alg = algorithmic(c)
+    alg = algorithmic(c, args.slot_ranks)
     if args.summarize_pmc:
         summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode))
         return
@@ -254,6 +264,7 @@ def main():
         s["aws"] = torch.empty(max(ap_need, 16), dtype=torch.uint8, device=dev)
 
     metas = [None] * nrot
+    ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).to(dev) if args.slot_ranks else None
 
     def meta_call(i):
         metas[i % nrot] = L.lora_prepare_meta(sets[i % nrot]["ts"], c.num_slots,
@@ -262,7 +273,7 @@ def main():
     def apply_call(i):
         s = sets[i % nrot]
         L.lora_apply(metas[i % nrot], s["x"], s["A"], s["B"], c.offsets, s["y"], scale=c.scale,
-                     add=True, mode=args.mode, workspace=s["aws"])
+                     add=True, mode=args.mode, workspace=s["aws"], slot_rank=ranks)
 
     def step(i):
         meta_call(i)
@@ -335,7 +346,8 @@ def main():
     d_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
     achieved = d_bytes / (d_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(c),
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if args.slot_ranks else read_traffic(c),
                 "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + dominant_kernel(c, args.mode) + ")",
                 "kernel_avg_us": round(d_us, 3), "algorithmic_bytes_per_launch": int(d_bytes)}
     step_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
@@ -348,6 +360,7 @@ def main():
         "config": {"workload": c.name, "tokens": c.T, "tokens_with_adapter": alg["T_lora"],
                    "distinct_slots": alg["U"], "slots": c.num_slots, "d_in": c.d_in,
                    "slice_widths": c.widths, "r_max": r, "mode": args.mode,
+                   "slot_ranks": bool(args.slot_ranks),
                    "rotated_input_sets": nrot, "parallelism": "single GPU"},
         "roofline": roofline,
         "calls_us": {"lora_prepare_meta": round(meta_us, 3), "lora_apply": round(apply_us, 3)},

@@ -1,4 +1,4 @@
-"""The five standard workloads at full size, in the launch configuration the
+"""The standard workloads at full size, in the launch configuration the
 benchmark times (AUTO mode, add into y): sampled rows against the oracle, plus
 the invariants that hold at any size."""
 import numpy as np
@@ -17,7 +17,7 @@ def L():
     return lib
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6])
 def test_workload_parity(L, k):
     c = W.config(k)
     print(f"[workload] {c.name} T={c.T}", flush=True)
@@ -38,7 +38,8 @@ def test_workload_parity(L, k):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("k,mode", [(2, "bgmv"), (2, "sgmv"), (3, "bgmv"), (4, "sgmv"), (5, "bgmv"), (5, "sgmv")])
+@pytest.mark.parametrize("k,mode", [(2, "bgmv"), (2, "sgmv"), (3, "bgmv"), (4, "sgmv"), (5, "bgmv"), (5, "sgmv"),
+                                    (6, "bgmv"), (6, "sgmv")])
 def test_workload_modes(L, k, mode):
     c = W.config(k)
     print(f"[workload-mode] {c.name} mode={mode}", flush=True)
@@ -66,3 +67,22 @@ def test_toy_full_forward(L):
         c.x.astype(np.float64) @ c.notes["W"].astype(np.float64)
     got = y.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= 1e-4 * (1 + np.abs(ref)))
+
+
+def test_logits_rows_through_the_sampler_mapping(L):
+    """The vocabulary-projection LoRA on sampled rows: gather the sampler's rows
+    of a full step's hidden states, build the metadata from the sampler-side
+    slot list, and compare every sampled row with the oracle."""
+    c = W.config(6)
+    step_lengths = c.notes["step_lengths"]
+    rows = c.notes["sampled_token_rows"]
+    # a full step of hidden states whose sampled rows are the workload's x
+    T_step = int(step_lengths.sum())
+    full = torch.zeros((T_step, c.d_in), dtype=torch.bfloat16, device="cuda")
+    d = DevCase(c)
+    full[torch.from_numpy(rows).cuda()] = d.x
+    xs = full.index_select(0, torch.from_numpy(rows).cuda())
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    y = d.y0.clone()
+    L.lora_apply(meta, xs, d.A, d.B, c.offsets, y, scale=c.scale)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), "logits, all sampled rows")

@@ -26,6 +26,15 @@ Workloads (shapes and distributions of the five standard cases):
   5 many-adapter    -- down_proj 14336 -> 4096, r_max=64 with slot ranks
                        U{8,16,32,64}, 128 slots, 4096 one-token requests,
                        slots Zipf(0.8), 5% without adapter, scale 1.0.
+  6 logits          -- the LoRA of the vocabulary projection on the rows the
+                       sampler reads ("vLLM 源码完全拆解(十八):多 LoRA 服务",
+                       section "lm_head / logits"): a step of 192 decode
+                       requests and 8 prefill requests of length U{64..1024}
+                       samples one row per request (the last one); those 200
+                       rows, with the slots of their requests, are the batch.
+                       4096 -> vocabulary 76 800 (the vocabulary size of that
+                       page's embedding example), r=16, 8 slots, 10 requests
+                       without adapter, scale 2.
 """
 from __future__ import annotations
 
@@ -188,7 +197,14 @@ CONFIG_NAMES = {
     3: "prefill_sgmv_bf16_gateup4096x2x14336_r64_s8",
     4: "mixed_qkv_gqa_bf16_r32_s64_t4608",
     5: "many_adapter_decode_bf16_down14336x4096_r64_s128_t4096",
+    6: "logits_sampled_rows_bf16_d4096_v76800_r16_s8_t200",
 }
+
+
+def sampler_rows(lengths) -> np.ndarray:
+    """Index, in the step's token batch, of the row the sampler reads for each
+    request: its last row (one row for a decode request)."""
+    return np.cumsum(np.asarray(lengths, np.int64)) - 1
 
 
 def _toy() -> Case:
@@ -255,4 +271,15 @@ def config(k: int) -> Case:
                          lengths=np.ones(4096, np.int64), req_slot=req_slot,
                          num_slots=S, d_in=14336, r_max=64, widths=[4096],
                          scale=1.0, ranks=ranks, no_lora_frac=0.05)
+    if k == 6:
+        S = 8
+        step_lengths = np.concatenate([np.ones(192, np.int64), rng.integers(64, 1025, 8)])
+        req_slot = rng.integers(0, S, step_lengths.shape[0]).astype(np.int32)
+        req_slot[rng.permutation(step_lengths.shape[0])[:10]] = -1
+        c = make_case(name=CONFIG_NAMES[6], seed=seed, rng=rng, dtype="bf16",
+                      lengths=np.ones(step_lengths.shape[0], np.int64), req_slot=req_slot,
+                      num_slots=S, d_in=4096, r_max=16, widths=[76800], scale=2.0)
+        c.notes["step_lengths"] = step_lengths
+        c.notes["sampled_token_rows"] = sampler_rows(step_lengths)
+        return c
     raise ValueError(f"no workload {k}")
