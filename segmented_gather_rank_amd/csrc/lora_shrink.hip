@@ -388,9 +388,13 @@ ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf1
   c.use_mma_mode = shrink_uses_mma(bf16, R, mode) ? 1 : 0;
   const int64_t chunks = c.use_mma_mode ? max_tiles(T, S) : (T + kVecRows - 1) / kVecRows + S;
   const int64_t tiles = (d_in + kMKT - 1) / kMKT;
-  // about 1024 items on the matrix-core path, but at most 8 k-chunks: the
-  // expand adds the partial sums with one batch of loads
-  const int64_t target = c.use_mma_mode ? 1024 : 512;
+  // matrix-core path: about 1024 items, or 2048 when the tiles are short
+  // (fewer than 32 tokens on average: an item's time is then mostly its A
+  // chunk, and smaller items even out the workgroups' finishing times); at
+  // most 8 k-chunks, so that the expand adds the partial sums with one batch
+  // of loads
+  const bool short_tiles = T < 32 * chunks;
+  const int64_t target = c.use_mma_mode ? (short_tiles ? 2048 : 1024) : 512;
   const int64_t cap = c.use_mma_mode ? 8 : tiles;
   const int64_t want = std::max<int64_t>(1, std::min<int64_t>(std::min(tiles, cap), (target + chunks - 1) / chunks));
   c.kc = (int)(((tiles + want - 1) / want) * kMKT);
