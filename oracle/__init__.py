@@ -53,6 +53,8 @@ def _declare(lib: C.CDLL) -> None:
     lib.oracle_expand_rows.argtypes = [C.c_int, p, i64, p, i32, i32, i32, p, p,
                                        p, p, p, i64, C.c_int, p, i64, p]
     lib.oracle_expand_rows.restype = C.c_int
+    lib.oracle_moe_keys.argtypes = [p, i64, i32, p, i32, i32, i32, p, p]
+    lib.oracle_moe_keys.restype = C.c_int
 
 
 def _ptr(a: np.ndarray | None):
@@ -163,3 +165,38 @@ def expand_rows(u, token_slot, num_slots, B, offsets, y0, add=True, rows=None, l
     if rc != 0:
         raise ValueError("oracle_expand_rows rejected its arguments")
     return y_out
+
+
+def moe_keys(topk_ids, token_slot, num_slots, num_experts, num_local_experts, expert_map=None,
+             lib=None) -> np.ndarray:
+    """Key of every (token, choice) pair (oracle_moe_keys): int32 [T * topk]."""
+    lib = lib or load()
+    topk_ids = np.ascontiguousarray(topk_ids, np.int32)
+    token_slot = np.ascontiguousarray(token_slot, np.int32)
+    T, K = topk_ids.shape
+    em = None if expert_map is None else np.ascontiguousarray(expert_map, np.int32)
+    keys = np.empty(T * K, np.int32)
+    rc = lib.oracle_moe_keys(_ptr(topk_ids), T, K, _ptr(token_slot), num_slots, num_experts,
+                             num_local_experts, _ptr(em), _ptr(keys))
+    assert rc == 0, rc
+    return keys
+
+
+def moe_rows(x, topk_ids, token_slot, num_slots, num_experts, num_local_experts, A, B, offsets,
+             scale, y0, expert_map=None, x_per_pair=False, add=True, rows=None, slot_scale=None,
+             lib=None):
+    """The experts' LoRA of one MoE layer step ([V] section "融合计算:add_lora_w13
+    与 add_lora_w2"): output row p = t * topk + j gets the delta of token t's
+    adapter on its j-th expert, with the factors of (slot, local expert).  A_s
+    and B_s are stacked [S][E_local][...]; the input row of pair p is x[t] (the
+    token's hidden state, gate/up LoRA) or x[p] when x_per_pair (down LoRA).
+    Evaluated as the rows of lora_rows with the pair keys as slots."""
+    lib = lib or load()
+    keys = moe_keys(topk_ids, token_slot, num_slots, num_experts, num_local_experts, expert_map, lib)
+    K = np.asarray(topk_ids).shape[1]
+    xp = x if x_per_pair else np.repeat(x, K, axis=0)
+    SE = num_slots * num_local_experts
+    Af = [np.ascontiguousarray(a).reshape((SE,) + a.shape[2:]) for a in A]
+    Bf = [np.ascontiguousarray(b).reshape((SE,) + b.shape[2:]) for b in B]
+    ss = None if slot_scale is None else np.repeat(np.asarray(slot_scale, np.float32), num_local_experts)
+    return lora_rows(xp, keys, SE, Af, Bf, offsets, scale, y0, add=add, rows=rows, slot_scale=ss, lib=lib)

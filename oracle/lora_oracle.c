@@ -28,6 +28,11 @@
  *                            expand 与 fp32 中转缓冲"; the per-slice output window
  *                            [offset, offset+width) follows the expand kernel
  *                            description there.
+ *   oracle_moe_keys       -- [V] sections "融合计算:add_lora_w13 与 add_lora_w2"
+ *                            and "EP 下只装载本地专家的权重": the (slot, local
+ *                            expert) key of every (token, choice) pair of a
+ *                            top-k routing step; the experts' LoRA is then the
+ *                            rows above with these keys as slots.
  *   oracle_expand_rows    -- the expand step alone, from a given fp32 rank-r
  *                            buffer laid out [slice][token][rank] ([V] section
  *                            "调用链").
@@ -258,6 +263,53 @@ int oracle_expand_rows(int dtype, const float *u, int64_t ldu,
                 const double base = add ? yrow[off + n] : 0.0;
                 yrow[off + n] = base + acc;
             }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * oracle_moe_keys -- key of every (token, choice) pair of a top-k MoE routing
+ * step, for the experts' LoRA ([V] section "融合计算:add_lora_w13 与
+ * add_lora_w2": the LoRA works on the tokens regrouped by adapter and expert;
+ * section "缓冲布局": factors stacked per slot and local expert; section
+ * "EP 下只装载本地专家的权重": a rank holds its local experts only).
+ *   pair p = t * topk + j is token t's j-th chosen expert e = topk_ids[p];
+ *   its local id is expert_map[e] when a map is given (-1: held by another
+ *   rank), e itself otherwise;
+ *   key = slot(t) * E_local + local id, or -1 when the token has no adapter
+ *   or the expert is not local, or -2 when an id is out of range (a slot
+ *   outside [-1, S), an expert outside [0, E_global), a local id outside
+ *   [-1, E_local), or without a map an expert >= E_local).
+ */
+int oracle_moe_keys(const int32_t *topk_ids, int64_t T, int32_t topk,
+                    const int32_t *token_slot, int32_t S, int32_t E_global,
+                    int32_t E_local, const int32_t *expert_map,
+                    int32_t *keys)
+{
+    if (T < 0 || topk < 1 || S < 1 || E_global < 1 || E_local < 1)
+        return ORACLE_BAD_ARG;
+    for (int64_t t = 0; t < T; ++t) {
+        const int32_t slot = token_slot[t];
+        for (int32_t j = 0; j < topk; ++j) {
+            const int32_t e = topk_ids[t * topk + j];
+            int32_t key;
+            if (slot < -1 || slot >= S || e < 0 || e >= E_global) {
+                key = -2;
+            } else {
+                int32_t local;
+                if (expert_map)
+                    local = expert_map[e];
+                else
+                    local = e < E_local ? e : -2;
+                if (local < -1 || local >= E_local)
+                    key = -2;
+                else if (slot == -1 || local == -1)
+                    key = -1;
+                else
+                    key = slot * E_local + local;
+            }
+            keys[t * topk + j] = key;
         }
     }
     return ORACLE_OK;

@@ -349,4 +349,106 @@ def pin_bf16_inputs_exact(lib):
     assert np.array_equal(yf, ref)
 
 
+# --------------------------------------------------------------------------- MoE experts' LoRA
+
+def _moe_case(seed, T=11, K=3, S=3, E_global=8, E_local=4, d_in=24, widths=(16, 8), r=8):
+    """Tiny MoE step: top-K distinct experts per token, slots with -1, stacked
+    per-(slot, local expert) factors [S][E_local][...]."""
+    rng = _rng(seed)
+    topk = np.stack([rng.permutation(E_global)[:K] for _ in range(T)]).astype(np.int32)
+    ts = rng.integers(-1, S, T).astype(np.int32)
+    x = rng.standard_normal((T, d_in)).astype(np.float32)
+    A = [rng.standard_normal((S, E_local, d_in, r)).astype(np.float32) for _ in widths]
+    B = [rng.standard_normal((S, E_local, r, w)).astype(np.float32) for w in widths]
+    offsets = list(np.cumsum((0,) + tuple(widths))[:-1] + 4 * np.arange(len(widths)))
+    ldy = int(offsets[-1] + widths[-1] + 4)
+    y0 = rng.standard_normal((T * K, ldy)).astype(np.float32)
+    return dict(x=x, topk=topk, ts=ts, S=S, E=E_global, EL=E_local, A=A, B=B, offsets=offsets, y0=y0)
+
+
+def _moe(m, lib, expert_map=None, add=True, **kw):
+    q = dict(m, **kw)
+    return oracle.moe_rows(q["x"], q["topk"], q["ts"], q["S"], q["E"], q["EL"], q["A"], q["B"],
+                           q["offsets"], 1.5, q["y0"], expert_map=expert_map, add=add, lib=lib)
+
+
+def pin_moe_keys_by_hand(lib):
+    """Keys worked out by hand from the definition: tokens on slots 1, -1, 0;
+    experts 0..3 local (map to 0..3), 4..7 on another rank."""
+    topk = np.array([[2, 5], [0, 1], [7, 3]], np.int32)
+    emap = np.array([0, 1, 2, 3, -1, -1, -1, -1], np.int32)
+    k = oracle.moe_keys(topk, np.array([1, -1, 0], np.int32), 2, 8, 4, emap, lib=lib)
+    # t0: slot 1, expert 2 -> 1*4+2 = 6; expert 5 remote -> -1.  t1: no adapter.
+    # t2: slot 0, expert 7 remote -> -1; expert 3 -> 0*4+3 = 3
+    assert list(k) == [6, -1, -1, -1, -1, 3]
+    # out of range: slot 5 >= S, expert 9 >= E, map entry 4 >= E_local; no map: expert 6 >= E_local
+    k = oracle.moe_keys(np.array([[1], [9], [4]], np.int32), np.array([5, 0, 1], np.int32), 2, 8, 4,
+                        np.array([0, 1, 2, 3, 4, -1, -1, -1], np.int32), lib=lib)
+    assert list(k) == [-2, -2, -2]
+    k = oracle.moe_keys(np.array([[6, 1]], np.int32), np.array([1], np.int32), 2, 8, 4, None, lib=lib)
+    assert list(k) == [-2, 5]
+
+
+def pin_moe_reduces_to_dense(lib):
+    """One expert and top-1: the experts' LoRA is the dense LoRA of the tokens."""
+    m = _moe_case(41, K=1, E_global=1, E_local=1)
+    y = _moe(m, lib)
+    yd = oracle.lora_rows(m["x"], m["ts"], m["S"], [a[:, 0] for a in m["A"]], [b[:, 0] for b in m["B"]],
+                          m["offsets"], 1.5, m["y0"], lib=lib)
+    assert np.array_equal(y, yd)
+
+
+def pin_moe_pairs_closed_form(lib):
+    """Every output row against numpy: row t*K + j adds 1.5 * x[t] @ A[a][e] @ B[a][e]
+    on each slice window (or nothing), with e the local expert of the choice."""
+    m = _moe_case(43)
+    emap = np.array([3, -1, 0, 2, -1, 1, -1, -1], np.int32)
+    y = _moe(m, lib, expert_map=emap)
+    K = m["topk"].shape[1]
+    ref = m["y0"].astype(np.float64).copy()
+    for t in range(m["x"].shape[0]):
+        a = int(m["ts"][t])
+        for j in range(K):
+            e = int(emap[m["topk"][t, j]])
+            if a < 0 or e < 0:
+                continue
+            for s, o in enumerate(m["offsets"]):
+                d = 1.5 * (m["x"][t].astype(np.float64) @ m["A"][s][a, e].astype(np.float64)) \
+                    @ m["B"][s][a, e].astype(np.float64)
+                ref[t * K + j, o:o + d.shape[0]] += d
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_moe_expert_relabel(lib):
+    """Renumbering the local experts together with their factor blocks and the
+    expert map leaves every row unchanged."""
+    m = _moe_case(47)
+    emap = np.array([0, 1, 2, 3, -1, -1, -1, -1], np.int32)
+    y = _moe(m, lib, expert_map=emap)
+    sigma = np.array([2, 0, 3, 1])                     # old local id e -> new id sigma[e]
+    inv = np.argsort(sigma)
+    emap2 = np.where(emap >= 0, sigma[np.maximum(emap, 0)], -1).astype(np.int32)
+    y2 = _moe(m, lib, expert_map=emap2, A=[a[:, inv] for a in m["A"]], B=[b[:, inv] for b in m["B"]])
+    assert np.array_equal(y, y2)
+
+
+def pin_moe_expert_parallel_partition(lib):
+    """Two ranks holding experts 0..3 and 4..7: their deltas (stored, not
+    added) sum to the delta of one rank holding all eight experts."""
+    m = _moe_case(53, E_local=8)
+    full = _moe(m, lib, add=False)
+    parts = 0
+    for rank in range(2):
+        emap = np.array([e - 4 * rank if 4 * rank <= e < 4 * rank + 4 else -1 for e in range(8)], np.int32)
+        sub = dict(m, EL=4, A=[a[:, 4 * rank:4 * rank + 4] for a in m["A"]],
+                   B=[b[:, 4 * rank:4 * rank + 4] for b in m["B"]])
+        parts = parts + oracle.moe_rows(sub["x"], sub["topk"], sub["ts"], sub["S"], sub["E"], 4, sub["A"],
+                                        sub["B"], sub["offsets"], 1.5, sub["y0"], expert_map=emap, add=False,
+                                        lib=lib)
+    windows = np.zeros(full.shape[1], bool)
+    for o, w in zip(m["offsets"], (16, 8)):
+        windows[o:o + w] = True
+    assert np.array_equal(parts[:, windows], full[:, windows])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,6 +39,10 @@ MUTANTS = [
      "const double base = yrow[off + n];\n                yrow[off + n] = base + acc;\n            }\n        }\n    }\n    return ORACLE_OK;"),
     ("expand alone reads the wrong token", "const float *ut = u + ((int64_t)s * ldu + t) * r_max;",
      "const float *ut = u + ((int64_t)s * ldu + (t > 0 ? t - 1 : t)) * r_max;"),
+    ("moe key strides slots by all experts", "key = slot * E_local + local;", "key = slot * E_global + local;"),
+    ("moe expert map ignored", "local = expert_map[e];", "local = e < E_local ? e : -2;"),
+    ("moe remote experts kept", "else if (slot == -1 || local == -1)", "else if (slot == -1)"),
+    ("moe reads the wrong choice", "const int32_t e = topk_ids[t * topk + j];", "const int32_t e = topk_ids[t * topk];"),
 ]
 
 
