@@ -92,9 +92,10 @@ typedef struct lora_weight {
  * token_slot changes.  Pass it by pointer to the compute calls; they only read
  * it, so any number of them may use one lora_meta at the same time. */
 typedef struct lora_meta {
-    int64_t num_tokens;
-    int32_t num_slots;
-    int32_t reserved;
+    int64_t num_tokens;             /* rows of the batch */
+    int32_t num_slots;              /* keys: slots, or (slot, local expert) pairs */
+    int32_t x_row_div;              /* row i of the batch reads row i / x_row_div of x
+                                       (1, or top-k for the MoE gate/up LoRA) */
     int32_t *sorted;
     int32_t *sorted_slot;
     int32_t *seg_slot;
@@ -116,7 +117,7 @@ lora_status lora_meta_workspace_bytes(int64_t num_tokens, int32_t num_slots,
  * Cites page "vLLM 源码完全拆解(十八):多 LoRA 服务", section
  * "LoRAKernelMeta:先按槽位排序" (stable sort, unique counts, running sum whose
  * first entry is 0) and the worked example of section "一个完整的走查:两步
- * decode 里发生了什么".  T = 0 is valid (no_lora = 1). */
+ * decode 里发生了什么".  T = 0 is valid (no_lora = 1).  Sets x_row_div = 1. */
 lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t num_tokens,
                               int32_t num_slots, void *d_ws, size_t ws_bytes,
                               lora_meta *out, void *stream);
@@ -133,6 +134,41 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t num_tokens,
  * padded to the largest waste memory traffic).  The result equals the padded
  * one whenever the padding holds zeros; u[s][t][j] is written as 0 for
  * j >= r_a.  Values are clamped to [0, r_max]. */
+
+/* MoE LoRA: metadata over the (token, choice) pairs of a top-k routing step,
+ * keyed by (slot, local expert).  Page "vLLM 源码完全拆解(十八):多 LoRA 服务",
+ * section "融合计算:add_lora_w13 与 add_lora_w2": the experts' LoRA is applied
+ * after the gate/up projection (before the activation) and after the down
+ * projection (before the top-k weighted sum), on the tokens regrouped by
+ * (adapter, expert); section "缓冲布局": the factors are stacked per slot and
+ * local expert; section "EP 下只装载本地专家的权重": a rank holds only its
+ * local experts.
+ * Row p = t * topk + j is token t's j-th choice.  Its key is
+ *     slot(t) * E_local + local(topk_ids[t][j])
+ * where local(e) = d_expert_map[e] when a map is given (-1: the expert lives
+ * on another rank) and e otherwise; the key is -1 when the token has no
+ * adapter or the expert is not local.  Ids out of range (a slot outside
+ * [-1, S), an expert outside [0, E_global), a mapped id outside [-1, E_local),
+ * or without a map an expert >= E_local) count as bad (info[2]) and as -1.
+ * The result is an ordinary lora_meta over T * topk rows and S * E_local keys
+ * (S * E_local <= 1023), with x_row_div = topk: lora_shrink and lora_apply
+ * then read x row t for pair p, the token's hidden state (gate/up LoRA).  For
+ * the down-projection LoRA, whose input has one row per pair, use a copy of
+ * the struct with x_row_div = 1.  Factor slot index = slot * E_local + expert:
+ * for stacks [S][E_local][...] pass slot_stride = one expert's matrix.
+ *   d_topk_ids    device int32 [T][topk]
+ *   d_token_slot  device int32 [T]
+ *   d_expert_map  device int32 [E_global] or NULL */
+lora_status lora_moe_meta_workspace_bytes(int64_t num_tokens, int32_t topk,
+                                          int32_t num_slots,
+                                          int32_t num_local_experts,
+                                          size_t *bytes);
+lora_status lora_prepare_moe_meta(const int32_t *d_topk_ids, int64_t num_tokens,
+                                  int32_t topk, const int32_t *d_token_slot,
+                                  int32_t num_slots, int32_t num_experts,
+                                  int32_t num_local_experts,
+                                  const int32_t *d_expert_map, void *d_ws,
+                                  size_t ws_bytes, lora_meta *out, void *stream);
 
 /* Bytes of device workspace lora_shrink needs (split-K partial sums; 0 when
  * the shape needs none).  No initialisation is required; calls that run at the

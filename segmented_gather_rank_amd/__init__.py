@@ -43,7 +43,7 @@ class lora_weight(C.Structure):
 
 
 class lora_meta(C.Structure):
-    _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("reserved", C.c_int32),
+    _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("x_row_div", C.c_int32),
                 ("sorted", C.c_void_p), ("sorted_slot", C.c_void_p), ("seg_slot", C.c_void_p),
                 ("seg_count", C.c_void_p),
                 ("seg_start", C.c_void_p), ("info", C.c_void_p), ("tiles", C.c_void_p)]
@@ -55,6 +55,9 @@ _decl = {
     "lora_status_string": ([_i32], C.c_char_p),
     "lora_meta_workspace_bytes": ([_i64, _i32, C.POINTER(_sz)], _i32),
     "lora_prepare_meta": ([_p, _i64, _i32, _p, _sz, C.POINTER(lora_meta), _p], _i32),
+    "lora_moe_meta_workspace_bytes": ([_i64, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
+    "lora_prepare_moe_meta": ([_p, _i64, _i32, _p, _i32, _i32, _i32, _p, _p, _sz, C.POINTER(lora_meta), _p],
+                              _i32),
     "lora_shrink_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "lora_shrink": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight), _i32,
                      C.c_float, _p, _p, _p, _i32, _p, _sz, _p], _i32),
@@ -91,7 +94,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 3:
+if _lib.lora_abi_version() != 4:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -173,6 +176,14 @@ class LoraMeta:
         off = ptr - self.workspace.data_ptr()
         return self.workspace[off:off + 4 * n].view(torch.int32)
 
+    def with_x_row_div(self, div: int) -> "LoraMeta":
+        """The same metadata with another x row divisor (MoE: 1 for the
+        down-projection LoRA, whose input has one row per pair)."""
+        c = lora_meta()
+        C.pointer(c)[0] = self.c
+        c.x_row_div = int(div)
+        return LoraMeta(c, self.workspace)
+
     def tensors(self) -> dict:
         """Device int32 views of the metadata arrays."""
         T, S = self.num_tokens, self.num_slots
@@ -201,6 +212,42 @@ def lora_prepare_meta(token_slot: torch.Tensor, num_slots: int, workspace: torch
     st = _lib.lora_prepare_meta(_dev(token_slot, "token_slot") if T else None, T, num_slots,
                                 _dev(workspace, "workspace"), workspace.numel(), C.byref(m), _stream(stream))
     _check("lora_prepare_meta", st)
+    return LoraMeta(m, workspace)
+
+
+def lora_moe_meta_workspace_bytes(num_tokens: int, topk: int, num_slots: int, num_local_experts: int) -> int:
+    b = _sz(0)
+    _check("lora_moe_meta_workspace_bytes",
+           _lib.lora_moe_meta_workspace_bytes(num_tokens, topk, num_slots, num_local_experts, C.byref(b)))
+    return int(b.value)
+
+
+def lora_prepare_moe_meta(topk_ids: torch.Tensor, token_slot: torch.Tensor, num_slots: int, num_experts: int,
+                          num_local_experts: int, expert_map: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, stream=None) -> LoraMeta:
+    """Metadata over the (token, choice) pairs of a top-k routing step, keyed by
+    (slot, local expert); topk_ids int32 [T][topk], token_slot int32 [T],
+    expert_map int32 [num_experts] or None."""
+    for name, t in (("topk_ids", topk_ids), ("token_slot", token_slot)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous int32")
+    if topk_ids.dim() != 2 or token_slot.dim() != 1 or topk_ids.shape[0] != token_slot.shape[0]:
+        raise ValueError("topk_ids must be [T][topk] and token_slot [T]")
+    T, K = topk_ids.shape
+    need = lora_moe_meta_workspace_bytes(T, K, num_slots, num_local_experts)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=topk_ids.device)
+    em = None
+    if expert_map is not None:
+        if expert_map.dtype != torch.int32 or expert_map.numel() != num_experts:
+            raise ValueError("expert_map must be int32 [num_experts]")
+        em = _dev(expert_map, "expert_map")
+    m = lora_meta()
+    st = _lib.lora_prepare_moe_meta(_dev(topk_ids, "topk_ids") if T else None, T, K,
+                                    _dev(token_slot, "token_slot") if T else None, num_slots, num_experts,
+                                    num_local_experts, em, _dev(workspace, "workspace"), workspace.numel(),
+                                    C.byref(m), _stream(stream))
+    _check("lora_prepare_moe_meta", st)
     return LoraMeta(m, workspace)
 
 
@@ -307,5 +354,6 @@ def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, 
 
 
 __all__ = ["lora_abi_version", "lora_status_string", "lora_meta_workspace_bytes", "lora_prepare_meta",
+           "lora_moe_meta_workspace_bytes", "lora_prepare_moe_meta",
            "lora_shrink_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_workspace_bytes",
            "lora_apply", "LoraMeta", "LoraError", "lora_weight", "lora_meta", "LIB_PATH"]

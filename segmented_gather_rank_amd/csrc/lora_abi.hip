@@ -31,7 +31,7 @@ namespace {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -66,7 +66,7 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
 }
 
 lora_status check_meta(const lora_meta *m) {
-  if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots)
+  if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots || m->x_row_div < 1)
     return LORA_ERR_INVALID_ARG;
   if (!m->sorted || !m->sorted_slot || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info ||
       !m->tiles)
@@ -85,6 +85,7 @@ MetaView view_of(const lora_meta *m) {
   v.tiles = m->tiles;
   v.T = m->num_tokens;
   v.S = m->num_slots;
+  v.x_row_div = m->x_row_div;
   return v;
 }
 
@@ -179,7 +180,7 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
   char *base = static_cast<char *>(d_ws);
   out->num_tokens = T;
   out->num_slots = S;
-  out->reserved = 0;
+  out->x_row_div = 1;
   out->sorted = reinterpret_cast<int32_t *>(base + L.sorted);
   out->sorted_slot = reinterpret_cast<int32_t *>(base + L.sorted_slot);
   out->seg_slot = reinterpret_cast<int32_t *>(base + L.seg_slot);
@@ -191,6 +192,44 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
                                    out->seg_count, out->seg_start, out->info, out->tiles,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_moe_meta_workspace_bytes(int64_t T, int32_t topk, int32_t S, int32_t E_local,
+                                          size_t *bytes) {
+  if (!bytes || T < 0 || topk < 1 || S < 1 || E_local < 1) return LORA_ERR_INVALID_ARG;
+  if (T * topk > INT32_MAX) return LORA_ERR_INVALID_ARG;
+  if ((int64_t)S * E_local > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+  const int64_t n = T * topk;
+  *bytes = align256(sizeof(int32_t) * (size_t)std::max<int64_t>(n, 1)) + meta_layout(n, S * E_local).total;
+  return LORA_OK;
+}
+
+lora_status lora_prepare_moe_meta(const int32_t *d_topk_ids, int64_t T, int32_t topk,
+                                  const int32_t *d_token_slot, int32_t S, int32_t E_global,
+                                  int32_t E_local, const int32_t *d_expert_map, void *d_ws,
+                                  size_t ws_bytes, lora_meta *out, void *stream) {
+  if (!out || T < 0 || topk < 1 || S < 1 || E_global < 1 || E_local < 1 || !d_ws || !aligned16(d_ws))
+    return LORA_ERR_INVALID_ARG;
+  if (T * topk > INT32_MAX) return LORA_ERR_INVALID_ARG;
+  if ((int64_t)S * E_local > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+  if (T > 0 && (!d_topk_ids || !d_token_slot)) return LORA_ERR_INVALID_ARG;
+  if (!aligned4(d_topk_ids) || !aligned4(d_token_slot) || !aligned4(d_expert_map)) return LORA_ERR_INVALID_ARG;
+  size_t need = 0;
+  lora_status st = lora_moe_meta_workspace_bytes(T, topk, S, E_local, &need);
+  if (st != LORA_OK) return st;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  const int64_t n = T * topk;
+  int32_t *keys = static_cast<int32_t *>(d_ws);
+  char *rest = static_cast<char *>(d_ws) + align256(sizeof(int32_t) * (size_t)std::max<int64_t>(n, 1));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_moe_keys(d_topk_ids, T, topk, d_token_slot, S, E_global, E_local, d_expert_map, keys, s) !=
+      hipSuccess)
+    return LORA_ERR_HIP;
+  st = lora_prepare_meta(keys, n, S * E_local, rest, ws_bytes - (rest - static_cast<char *>(d_ws)), out,
+                         stream);
+  if (st != LORA_OK) return st;
+  out->x_row_div = topk;
+  return LORA_OK;
 }
 
 lora_status lora_shrink_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32_t n_slices,

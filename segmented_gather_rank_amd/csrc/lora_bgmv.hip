@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
                  (int64_t)slot * pick(p.b_stride, s0, p.n_slices) + n00;  // rank row 0 of the octet
   const int64_t w0 = pick(p.width, s0, p.n_slices);
   const int64_t yoff0 = pick(p.offset, s0, p.n_slices) + n00;
-  const rsrc_t xr = make_rsrc(reinterpret_cast<const E *>(p.x) + t * p.ldx, (uint32_t)(p.d_in * sizeof(E)));
+  const rsrc_t xr = make_rsrc(reinterpret_cast<const E *>(p.x) + x_row_of(p.meta, t) * p.ldx,
+                              (uint32_t)(p.d_in * sizeof(E)));
   const rsrc_t ar0 = make_rsrc(reinterpret_cast<const E *>(p.A[0]) + (int64_t)slot * p.a_stride[0], a_bytes);
   const rsrc_t yr = make_rsrc(y, (uint32_t)(p.ldy * sizeof(E)));
   const bool a_live = !RK || 8 * jo < rk;  // this lane's A rank octet is within the slot's rank

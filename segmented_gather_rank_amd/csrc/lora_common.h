@@ -229,7 +229,13 @@ struct MetaView {
   const int32_t *tiles;  // kTileInts int32 per tile: slot, rows, pos0, 0, tokens[kTileRows]
   int64_t T;
   int32_t S;
+  int32_t x_row_div;     // batch row i reads x row i / x_row_div
 };
+
+// x row read by batch row i.
+__device__ __forceinline__ int64_t x_row_of(const MetaView &m, int64_t i) {
+  return m.x_row_div == 1 ? i : i / m.x_row_div;
+}
 
 // Work tiles of the metadata: every segment cut into runs of at most
 // kTileRows sorted positions.

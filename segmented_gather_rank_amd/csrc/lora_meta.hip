@@ -19,6 +19,8 @@
 //   4. while scattering, every token also lands in its work tile (its
 //      segment's sorted range cut into runs of 64), and the token that opens a
 //      tile writes the tile's header.
+#include <algorithm>
+
 #include "lora_host.h"
 
 namespace lora {
@@ -168,6 +170,40 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       __syncthreads();
     }
   }
+}
+
+// Key of pair p = t * topk + j: slot * E_local + local expert, -1 for no
+// adapter or a remote expert, -2 (counted as bad by the metadata kernel) for
+// ids out of range.
+__global__ __launch_bounds__(256) void moe_keys_kernel(const int32_t *__restrict__ topk_ids, int64_t n,
+                                                       int32_t topk, const int32_t *__restrict__ token_slot,
+                                                       int32_t S, int32_t E_global, int32_t E_local,
+                                                       const int32_t *__restrict__ expert_map,
+                                                       int32_t *__restrict__ keys) {
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < n; p += (int64_t)gridDim.x * 256) {
+    const int slot = token_slot[p / topk];
+    const int e = topk_ids[p];
+    int key;
+    if (slot < -1 || slot >= S || e < 0 || e >= E_global) {
+      key = -2;
+    } else {
+      const int le = expert_map ? expert_map[e] : (e < E_local ? e : -2);
+      if (le < -1 || le >= E_local) key = -2;
+      else key = (slot < 0 || le < 0) ? -1 : slot * E_local + le;
+    }
+    keys[p] = key;
+  }
+}
+
+hipError_t launch_moe_keys(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
+                           int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
+                           int32_t *keys, hipStream_t stream) {
+  const int64_t n = T * topk;
+  if (n == 0) return hipSuccess;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(moe_keys_kernel, dim3(grid), dim3(256), 0, stream, topk_ids, n, topk, token_slot, S,
+                     E_global, E_local, expert_map, keys);
+  return hipGetLastError();
 }
 
 size_t meta_lds_bytes(int32_t S) { return sizeof(int32_t) * (size_t)(S + 1) * (4 + kMetaWaves); }

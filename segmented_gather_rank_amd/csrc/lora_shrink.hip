@@ -131,7 +131,7 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
           const int row = idx / oct, c = idx - row * oct;
           const int64_t t = p.meta.sorted[pos0 + row];
           float v[8];
-          load8(x + t * p.ldx + k0 + sub + 8 * c, v);
+          load8(x + x_row_of(p.meta, t) * p.ldx + k0 + sub + 8 * c, v);
           *reinterpret_cast<f32x4 *>(&lds.xs[row][8 * c]) = f32x4{v[0], v[1], v[2], v[3]};
           *reinterpret_cast<f32x4 *>(&lds.xs[row][8 * c + 4]) = f32x4{v[4], v[5], v[6], v[7]};
         }
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
     const int ntiles = (int)((kend - kbeg + kMKT - 1) / kMKT);
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
     const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
-    const uint16_t *xrow = x + (r < rows ? trow : (int64_t)tl[4]) * p.ldx;
+    const uint16_t *xrow = x + x_row_of(p.meta, r < rows ? trow : (int64_t)tl[4]) * p.ldx;
 
     for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
       const int ns = min(SG, p.n_slices - s0);

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 3
+    assert L.lora_abi_version() == 4
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -71,7 +71,7 @@ def test_meta_rejections():
 
 def _meta(T=16, S=4):
     m = L.lora_meta()
-    m.num_tokens, m.num_slots = T, S
+    m.num_tokens, m.num_slots, m.x_row_div = T, S, 1
     for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info", "tiles"):
         setattr(m, f, _base)
     return m
@@ -148,3 +148,20 @@ def test_apply_rejections():
     assert _call("lora_apply", None, *args(_ptr(), 1 << 15)[1:]) == L.LORA_ERR_INVALID_ARG
     assert _call("lora_apply", *args(None, 1 << 15)) == L.LORA_ERR_WORKSPACE
     assert _call("lora_apply", *args(_ptr(8), 1 << 15)) == L.LORA_ERR_WORKSPACE
+
+
+def test_moe_meta_rejections():
+    m = L.lora_meta()
+    sz = C.c_size_t(0)
+    assert _call("lora_moe_meta_workspace_bytes", 16, 8, 4, 32, C.byref(sz)) == L.LORA_OK
+    assert sz.value >= 4 * 16 * 8
+    assert _call("lora_moe_meta_workspace_bytes", 16, 0, 4, 32, C.byref(sz)) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_moe_meta_workspace_bytes", 16, 8, 64, 32, C.byref(sz)) == L.LORA_ERR_UNSUPPORTED
+    args = lambda ws_bytes, em=None, topk=8: (_ptr(), 16, topk, _ptr(), 4, 256, 32, em, _ptr(), ws_bytes,
+                                             C.byref(m), None)
+    assert _call("lora_prepare_moe_meta", *args(16)) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_prepare_moe_meta", *args(1 << 15, em=_ptr(2))) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_prepare_moe_meta", *args(1 << 15, topk=0)) == L.LORA_ERR_INVALID_ARG
+    bad = _meta()
+    bad.x_row_div = 0
+    assert _shrink(meta=bad) == L.LORA_ERR_INVALID_ARG

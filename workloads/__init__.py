@@ -35,6 +35,18 @@ Workloads (shapes and distributions of the five standard cases):
                        4096 -> vocabulary 76 800 (the vocabulary size of that
                        page's embedding example), r=16, 8 slots, 10 requests
                        without adapter, scale 2.
+  7 MoE gate/up     -- the experts' LoRA of a top-8 MoE layer in a decode step
+                       ("vLLM 源码完全拆解(十八)", section "缓冲布局": hidden
+                       7168, expert intermediate 2048, 256 experts, 8-way
+                       expert parallelism so 32 local experts, rank 64, 4
+                       slots): 256 tokens, 8 distinct experts each, uniform;
+                       the rank-0 shard holds experts 0..31.  Gate and up
+                       slices (2048 each) of the 2048 (token, choice) rows;
+                       x is the tokens' hidden state.  Scale 1 (the page gives
+                       no alpha).
+  8 MoE down        -- the same step's down-projection LoRA: x has one row
+                       per (token, choice) pair (the activated intermediate,
+                       2048 wide), output 7168.
 """
 from __future__ import annotations
 
@@ -198,7 +210,79 @@ CONFIG_NAMES = {
     4: "mixed_qkv_gqa_bf16_r32_s64_t4608",
     5: "many_adapter_decode_bf16_down14336x4096_r64_s128_t4096",
     6: "logits_sampled_rows_bf16_d4096_v76800_r16_s8_t200",
+    7: "moe_w13_bf16_h7168_i2048_e256ep8_top8_r64_s4_t256",
+    8: "moe_w2_bf16_i2048_h7168_e256ep8_top8_r64_s4_t256",
 }
+
+
+@dataclass
+class MoeCase:
+    """One MoE layer step: token slots, top-k expert choices, the expert map of
+    this rank, and factors stacked per (slot, local expert).  Output rows are
+    the (token, choice) pairs, row t * topk + j."""
+    name: str
+    dtype: str
+    token_slot: np.ndarray          # int32 [T] (per token)
+    topk_ids: np.ndarray            # int32 [T][topk]
+    expert_map: np.ndarray | None   # int32 [E_global] or None
+    num_slots: int
+    num_experts: int
+    num_local_experts: int
+    d_in: int
+    r_max: int
+    ranks: np.ndarray               # int32 [S]
+    widths: list
+    offsets: list
+    ldy: int
+    scale: float
+    x: np.ndarray                   # [T][d_in] (x_per_pair False) or [T*topk][d_in]
+    x_per_pair: bool
+    A: list                         # per slice [S][E_local][d_in][r_max]
+    B: list                         # per slice [S][E_local][r_max][w_s]
+    y0: np.ndarray                  # [T*topk][ldy]
+    slot_scale: np.ndarray | None = None
+    seed: int = 0
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:             # tokens
+        return int(self.token_slot.shape[0])
+
+    @property
+    def topk(self) -> int:
+        return int(self.topk_ids.shape[1])
+
+    @property
+    def rows(self) -> int:          # (token, choice) pairs
+        return self.T * self.topk
+
+    @property
+    def n_slices(self) -> int:
+        return len(self.A)
+
+
+def _moe_case(k: int) -> MoeCase:
+    seed = 1000 + k
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, K, S, E, EL, r = 256, 8, 4, 256, 32, 64
+    hidden, inter = 7168, 2048
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    ts = rng.integers(0, S, T).astype(np.int32)
+    ts[rng.permutation(T)[:26]] = -1
+    emap = np.where(np.arange(E) < EL, np.arange(E), -1).astype(np.int32)
+    if k == 7:
+        d_in, widths, offsets, ldy, per_pair = hidden, [inter, inter], [0, inter], 2 * inter, False
+    else:
+        d_in, widths, offsets, ldy, per_pair = inter, [hidden], [0], hidden, True
+    xr = T * K if per_pair else T
+    x = _draw(rng, (xr, d_in), 1.0, "bf16")
+    A = [_draw(rng, (S, EL, d_in, r), 0.02, "bf16") for _ in widths]
+    B = [_draw(rng, (S, EL, r, w), 0.02, "bf16") for w in widths]
+    y0 = _draw(rng, (T * K, ldy), 1.0, "bf16")
+    return MoeCase(name=CONFIG_NAMES[k], dtype="bf16", token_slot=ts, topk_ids=topk, expert_map=emap,
+                   num_slots=S, num_experts=E, num_local_experts=EL, d_in=d_in, r_max=r,
+                   ranks=np.full(S, r, np.int32), widths=widths, offsets=offsets, ldy=ldy, scale=1.0,
+                   x=x, x_per_pair=per_pair, A=A, B=B, y0=y0, seed=seed)
 
 
 def sampler_rows(lengths) -> np.ndarray:
@@ -282,4 +366,6 @@ def config(k: int) -> Case:
         c.notes["step_lengths"] = step_lengths
         c.notes["sampled_token_rows"] = sampler_rows(step_lengths)
         return c
+    if k in (7, 8):
+        return _moe_case(k)
     raise ValueError(f"no workload {k}")
