@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline decode case)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1..8 (2 = the headline decode case; 7, 8 = MoE experts' LoRA)")
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--slot-ranks", action="store_true",
                     help="pass each slot's own rank (the kernels then skip the zero-padded ranks)")
@@ -60,16 +61,49 @@ PMC_COPY_ELEMS = 64 << 20   # bf16 elements of the calibration copy (128 MiB rea
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def source_digest():
-    """Hash of the kernel sources: a traffic figure is only reported while the
-    kernels it was measured on are unchanged."""
+KERNEL_SOURCES = {   # the sources each measured kernel is built from
+    "bgmv_fused_kernel": ["lora_bgmv.hip"],
+    "shrink+expand": ["lora_shrink.hip", "lora_expand.hip"],
+}
+
+
+def source_digest(kernel_key):
+    """Hash of the sources of one kernel (its file, the shared device headers,
+    the C header): a traffic figure is only reported while the kernel it was
+    measured on is unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for d in ("segmented_gather_rank_amd/csrc", "include"):
-        for f in sorted(os.listdir(os.path.join(ROOT, d))):
-            h.update(f.encode())
-            h.update(open(os.path.join(ROOT, d, f), "rb").read())
+    csrc = os.path.join(ROOT, "segmented_gather_rank_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in KERNEL_SOURCES[kernel_key] + ["lora_common.h", "lora_host.h"]]
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+class MoeFlat:
+    """An MoE step seen as the plain batch the kernels run: one row per
+    (token, choice) pair whose slot is its (slot, local expert) key, factors
+    stacked [S * E_local][...].  Used for the byte accounting and kernel
+    choice; the keys themselves are computed on the device by the library."""
+
+    def __init__(self, c):
+        import numpy as np
+        self.moe = c
+        e = c.topk_ids.reshape(-1).astype(np.int64)
+        tok = np.repeat(np.arange(c.T), c.topk)
+        slot = c.token_slot[tok]
+        le = c.expert_map[e] if c.expert_map is not None else e
+        self.token_slot = np.where((slot >= 0) & (le >= 0), slot * c.num_local_experts + le, -1).astype(np.int32)
+        self.T = c.rows
+        self.num_slots = c.num_slots * c.num_local_experts
+        self.n_slices, self.d_in, self.r_max, self.widths = c.n_slices, c.d_in, c.r_max, c.widths
+        self.dtype, self.name, self.scale, self.offsets = c.dtype, c.name, c.scale, c.offsets
+        self.ranks = np.repeat(np.asarray(c.ranks, np.int32), c.num_local_experts)
+        # x rows the step must read: tokens with a keyed pair (gate/up), or keyed pairs (down)
+        keyed = self.token_slot >= 0
+        self.x_rows = int(keyed.sum()) if c.x_per_pair else int(np.unique(tok[keyed]).shape[0])
 
 
 def dominant_kernel(c, mode):
@@ -81,14 +115,19 @@ def dominant_kernel(c, mode):
              and (mode == "bgmv" or c.T <= 16 * c.num_slots))
     if fused:
         return "bgmv_fused_kernel"
-    return "expand_mma_kernel" if c.dtype == "bf16" and mode != "bgmv" else "expand_kernel"
+    return "shrink+expand"
+
+
+def kernel_keys(kernel_key):
+    """Substrings of the kernel names that make up one lora_apply launch."""
+    return kernel_key.split("+")
 
 
 def traffic_file(c):
     return os.path.join(PROFILES, f"traffic_{c.name}.md")
 
 
-def read_traffic(c):
+def read_traffic(c, kernel_key):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel sources."""
     try:
@@ -96,7 +135,7 @@ def read_traffic(c):
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith("- ") and ": " in line)
-    if fields.get("- kernel sources") != source_digest():
+    if fields.get("- kernel sources") != source_digest(kernel_key):
         return None
     return int(fields["- traffic bytes per launch"])
 
@@ -121,11 +160,12 @@ def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
         copy = [v for k, v in vals.items() if "neg" in k.lower()]
-        kern = [v for k, v in vals.items() if kernel_key in k]
+        kern = [v for k, v in vals.items() if any(key in k for key in kernel_keys(kernel_key))]
         assert copy and kern, (counter, list(vals))
         copy_kib = sum(copy[0]) / len(copy[0])
-        kern_kib = sum(kern[0]) / len(kern[0])
-        out[counter] = (kern_kib, copy_kib, len(kern[0]))
+        # one apply = one dispatch of each of its kernels: sum their per-dispatch means
+        kern_kib = sum(sum(v) / len(v) for v in kern)
+        out[counter] = (kern_kib, copy_kib, min(len(v) for v in kern))
     nbytes = PMC_COPY_ELEMS * 2
     f_r = nbytes / (out["FETCH_SIZE"][1] * 1024)
     f_w = nbytes / (out["WRITE_SIZE"][1] * 1024)
@@ -153,7 +193,7 @@ def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
         f"Scaled traffic {traffic / 1e6:.3f} MB per launch against {alg_b / 1e6:.3f} MB algorithmic "
         f"({traffic / alg_b:.3f}x).",
         "",
-        f"- kernel sources: {source_digest()}",
+        f"- kernel sources: {source_digest(kernel_key)}",
         f"- traffic bytes per launch: {int(round(traffic))}",
         "",
     ]
@@ -166,7 +206,8 @@ def algorithmic(c, ranked=False):
     """Bytes and flops the method must move/compute for one batch (per kernel).
 
     A and B slot blocks of every distinct slot used are read once; x rows of
-    tokens with an adapter are read once; the y windows of those tokens are
+    tokens with an adapter are read once (for an MoE step, the distinct x rows
+    its keyed pairs use); the y windows of those tokens are
     read and written once (add into y).  Metadata and the fp32 rank-r buffer
     are overheads and are not counted.  r is the padded r_max the kernels read,
     or, with per-slot ranks, each slot's own rank rounded up to 8.
@@ -185,7 +226,8 @@ def algorithmic(c, ranked=False):
         r_tok = int(r_slot[ts[lora]].sum())             # ranks over the LoRA tokens
     else:
         r_sum, r_tok = U * c.r_max, TL * c.r_max
-    shrink_bytes = r_sum * c.n_slices * c.d_in * e + TL * c.d_in * e
+    x_rows = getattr(c, "x_rows", TL)
+    shrink_bytes = r_sum * c.n_slices * c.d_in * e + x_rows * c.d_in * e
     expand_bytes = r_sum * sw * e + TL * sw * e * 2
     shrink_flops = 2 * r_tok * c.n_slices * c.d_in
     expand_flops = 2 * r_tok * sw
@@ -196,19 +238,31 @@ def algorithmic(c, ranked=False):
 def cpu_baseline(c, seconds):
     """The oracle as it stands (plain C, fp64, one thread) on a bounded sample
     of the same workload: whole batches, metadata plus every token's delta,
-    repeated until `seconds` have passed (at least one token)."""
+    repeated until `seconds` have passed (at least one token).  An MoE step is
+    counted in tokens: a token is done when all its top-k pairs are."""
     import numpy as np
     import oracle
-    T = c.T
-    rows_per_call = max(1, min(T, 64))
+    moe = getattr(c, "moe", None)
+    T = c.T if moe is None else moe.T
+    rows_per_call = max(1, min(T, 64 if moe is None else 8))
     done = 0
     t0 = time.perf_counter()
     while True:
-        oracle.prepare_meta(c.token_slot, c.num_slots)
+        if moe is None:
+            oracle.prepare_meta(c.token_slot, c.num_slots)
+        else:
+            oracle.prepare_meta(oracle.moe_keys(moe.topk_ids, moe.token_slot, moe.num_slots, moe.num_experts,
+                                                moe.num_local_experts, moe.expert_map), c.num_slots)
         for r0 in range(0, T, rows_per_call):
             rows = np.arange(r0, min(T, r0 + rows_per_call))
-            oracle.lora_rows(c.x, c.token_slot, c.num_slots, c.A, c.B, c.offsets, c.scale, c.y0,
-                             rows=rows)
+            if moe is None:
+                oracle.lora_rows(c.x, c.token_slot, c.num_slots, c.A, c.B, c.offsets, c.scale, c.y0,
+                                 rows=rows)
+            else:
+                pairs = (rows[:, None] * moe.topk + np.arange(moe.topk)).reshape(-1)
+                oracle.moe_rows(moe.x, moe.topk_ids, moe.token_slot, moe.num_slots, moe.num_experts,
+                                moe.num_local_experts, moe.A, moe.B, moe.offsets, moe.scale, moe.y0,
+                                expert_map=moe.expert_map, x_per_pair=moe.x_per_pair, rows=pairs)
             done += rows.shape[0]
             if time.perf_counter() - t0 > seconds:
                 break
@@ -231,6 +285,9 @@ def main():
     import workloads as W
 
     c = W.config(args.config)
+    moe = None
+    if isinstance(c, W.MoeCase):
+        moe, c = c, MoeFlat(c)
     alg = algorithmic(c, args.slot_ranks)
     if args.summarize_pmc:
         summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode))
@@ -249,26 +306,41 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    base = dict(ts=torch.from_numpy(c.token_slot).to(dev), x=to_dev(c.x),
-                A=[to_dev(a) for a in c.A], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
+    if moe is None:
+        base = dict(ts=torch.from_numpy(c.token_slot).to(dev), x=to_dev(c.x),
+                    A=[to_dev(a) for a in c.A], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
+    else:
+        SE = c.num_slots
+        base = dict(ts=torch.from_numpy(moe.token_slot).to(dev), x=to_dev(moe.x),
+                    A=[to_dev(a).view(SE, *a.shape[2:]) for a in moe.A],
+                    B=[to_dev(b).view(SE, *b.shape[2:]) for b in moe.B], y=to_dev(moe.y0),
+                    topk=torch.from_numpy(moe.topk_ids).to(dev),
+                    emap=None if moe.expert_map is None else torch.from_numpy(moe.expert_map).to(dev))
     set_bytes = sum(t.numel() * t.element_size()
                     for t in [base["ts"], base["x"], base["y"], *base["A"], *base["B"]])
     nrot = max(1, min(64, int(np.ceil(args.rotate_mb * 2 ** 20 / set_bytes))))
-    sets = [base] + [dict(ts=base["ts"].clone(), x=base["x"].clone(), A=[a.clone() for a in base["A"]],
-                          B=[b.clone() for b in base["B"]], y=base["y"].clone()) for _ in range(nrot - 1)]
+    sets = [base] + [{k: (None if v is None else [a.clone() for a in v] if isinstance(v, list) else v.clone())
+                      for k, v in base.items()} for _ in range(nrot - 1)]
     dtype = base["x"].dtype
     r = c.r_max
     ap_need = L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, r, dtype, args.mode)
+    mws_bytes = (L.lora_meta_workspace_bytes(c.T, c.num_slots) if moe is None else
+                 L.lora_moe_meta_workspace_bytes(moe.T, moe.topk, moe.num_slots, moe.num_local_experts))
     for s in sets:
-        s["mws"] = torch.empty(L.lora_meta_workspace_bytes(c.T, c.num_slots), dtype=torch.uint8, device=dev)
+        s["mws"] = torch.empty(mws_bytes, dtype=torch.uint8, device=dev)
         s["aws"] = torch.empty(max(ap_need, 16), dtype=torch.uint8, device=dev)
 
     metas = [None] * nrot
     ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).to(dev) if args.slot_ranks else None
 
     def meta_call(i):
-        metas[i % nrot] = L.lora_prepare_meta(sets[i % nrot]["ts"], c.num_slots,
-                                              workspace=sets[i % nrot]["mws"])
+        s = sets[i % nrot]
+        if moe is None:
+            metas[i % nrot] = L.lora_prepare_meta(s["ts"], c.num_slots, workspace=s["mws"])
+        else:
+            m = L.lora_prepare_moe_meta(s["topk"], s["ts"], moe.num_slots, moe.num_experts,
+                                        moe.num_local_experts, s["emap"], workspace=s["mws"])
+            metas[i % nrot] = m.with_x_row_div(1) if moe.x_per_pair else m
 
     def apply_call(i):
         s = sets[i % nrot]
@@ -340,14 +412,15 @@ def main():
     eager_ms_per_step = e0.elapsed_time(e1) / K
 
     ms_per_step = total_ms / K
-    value = c.T * K / (total_ms / 1e3)
+    tokens = c.T if moe is None else moe.T       # an MoE step's tokens (each with top-k pairs)
+    value = tokens * K / (total_ms / 1e3)
 
     d_us = apply_us
     d_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
     achieved = d_bytes / (d_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if args.slot_ranks else read_traffic(c),
+                "traffic": None if args.slot_ranks else read_traffic(c, dominant_kernel(c, args.mode)),
                 "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + dominant_kernel(c, args.mode) + ")",
                 "kernel_avg_us": round(d_us, 3), "algorithmic_bytes_per_launch": int(d_bytes)}
     step_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
@@ -357,8 +430,13 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if c.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": c.name, "tokens": c.T, "tokens_with_adapter": alg["T_lora"],
-                   "distinct_slots": alg["U"], "slots": c.num_slots, "d_in": c.d_in,
+        "config": {"workload": c.name, "tokens": tokens,
+                   **({} if moe is None else {"topk": moe.topk, "pairs": c.T, "experts": moe.num_experts,
+                                              "local_experts": moe.num_local_experts,
+                                              "adapter_slots": moe.num_slots}),
+                   "tokens_with_adapter" if moe is None else "keyed_pairs": alg["T_lora"],
+                   "distinct_slots" if moe is None else "distinct_keys": alg["U"],
+                   "slots": c.num_slots, "d_in": c.d_in,
                    "slice_widths": c.widths, "r_max": r, "mode": args.mode,
                    "slot_ranks": bool(args.slot_ranks),
                    "rotated_input_sets": nrot, "parallelism": "single GPU"},

@@ -140,7 +140,8 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t num_tokens,
  * section "融合计算:add_lora_w13 与 add_lora_w2": the experts' LoRA is applied
  * after the gate/up projection (before the activation) and after the down
  * projection (before the top-k weighted sum), on the tokens regrouped by
- * (adapter, expert); section "缓冲布局": the factors are stacked per slot and
+ * (adapter, expert); section "MoE 的 LoRA:按专家挂载、融合 kernel 与 EP 切片",
+ * its buffer list: the factors are stacked per slot and
  * local expert; section "EP 下只装载本地专家的权重": a rank holds only its
  * local experts.
  * Row p = t * topk + j is token t's j-th choice.  Its key is

@@ -272,7 +272,8 @@ int oracle_expand_rows(int dtype, const float *u, int64_t ldu,
  * oracle_moe_keys -- key of every (token, choice) pair of a top-k MoE routing
  * step, for the experts' LoRA ([V] section "融合计算:add_lora_w13 与
  * add_lora_w2": the LoRA works on the tokens regrouped by adapter and expert;
- * section "缓冲布局": factors stacked per slot and local expert; section
+ * section "MoE 的 LoRA:按专家挂载、融合 kernel 与 EP 切片", its buffer list:
+ * factors stacked per slot and local expert; section
  * "EP 下只装载本地专家的权重": a rank holds its local experts only).
  *   pair p = t * topk + j is token t's j-th chosen expert e = topk_ids[p];
  *   its local id is expert_map[e] when a map is given (-1: held by another

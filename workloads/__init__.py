@@ -36,7 +36,8 @@ Workloads (shapes and distributions of the five standard cases):
                        page's embedding example), r=16, 8 slots, 10 requests
                        without adapter, scale 2.
   7 MoE gate/up     -- the experts' LoRA of a top-8 MoE layer in a decode step
-                       ("vLLM 源码完全拆解(十八)", section "缓冲布局": hidden
+                       ("vLLM 源码完全拆解(十八)", section "MoE 的 LoRA:按专家
+                       挂载、融合 kernel 与 EP 切片", its buffer list: hidden
                        7168, expert intermediate 2048, 256 experts, 8-way
                        expert parallelism so 32 local experts, rank 64, 4
                        slots): 256 tokens, 8 distinct experts each, uniform;
