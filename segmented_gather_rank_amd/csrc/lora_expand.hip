@@ -45,8 +45,8 @@ struct ExpandParams {
   int64_t offset[kMaxSlices];
   int32_t ntiles_vec;                 // vector n-tiles over all slices
   int32_t vec_cols;                   // columns per vector n-tile
-  int32_t cpi, nck;                   // matrix-core path: columns per item, chunks over all slices
-  int32_t chunk_base[kMaxSlices + 1]; // prefix of chunks per slice
+  int32_t steps[kMaxSlices];          // matrix-core path: 128-column steps per slice
+  int32_t steps_total;                // and over all slices
   int32_t n_slices;
   void *y;
   int64_t ldy;
@@ -227,7 +227,7 @@ struct XLds {
 };
 
 template <int R>
-__global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p) {
+__global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(ExpandParams p) {
   constexpr int RP = XLds<R>::RP;
   constexpr int KS = RP / 16;                     // MFMA k-steps
   constexpr int BQ = RP * kXStep / 8 / kXThreads;  // B octets per thread per step
@@ -235,31 +235,64 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n = lane % 16, kg = lane / 16;
   const int64_t T = p.meta.T;
-  // items (column chunk, tile) over the metadata's tile list, padded to its
-  // host-known capacity: item = ck * tmax + tile, so tiles that share a chunk
-  // of B are neighbours; XCD x (blockIdx mod 8) takes a contiguous run of items
-  const int tmax = (int)max_tiles(T, p.meta.S);
-  const int total = tmax * p.nck;
+  // live tiles: the tile list is in key order, so the tiles of tokens without
+  // an adapter come first, and adding into y they need no work
+  const int ntl = uniform_value(p.meta.info[4]);
+  const int t0 = p.add ? (uniform_value(p.meta.info[3]) + kTileRows - 1) / kTileRows : 0;
+  const int live = ntl - t0;
+  if (live <= 0) return;
+  // steps per item: the live tiles' steps spread evenly over the grid, at most
+  // 16; an item is (column chunk of one slice, tile), chunk-major, so tiles
+  // that share a chunk of B are neighbours, and XCD x (blockIdx mod 8) takes a
+  // contiguous run of items
+  const int spi = min(16, max(1, (int)(((int64_t)live * p.steps_total + gridDim.x - 1) / gridDim.x)));
+  const int cpi = spi * kXStep;
+  int nck = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxSlices; ++k) {
+    if (k >= p.n_slices) break;
+    nck += (uniform_value(p.steps[k]) + spi - 1) / spi;
+  }
+  const int total = live * nck;
   const int run = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
-  const int lo = xcd * run, hi = min(total, lo + run);
+  const int hi = min(total, xcd * run + run);
+  int item = xcd * run + (int)blockIdx.x / 8;
+  if (item >= hi) return;
   uint16_t *y = reinterpret_cast<uint16_t *>(p.y);
 
-  for (int item = lo + (int)blockIdx.x / 8; item < hi; item += per) {
-    const int ck = item / tmax, tile = item % tmax;
-    const int32_t *tl = p.meta.tiles + (int64_t)tile * kTileInts;
-    const int ntl = p.meta.info[4];
-    const int slot = tl[0], rows = tl[1];
-    const int64_t pos0 = tl[2];
-    // this lane's token for each possible spread of waves over token blocks
-    // (which one applies depends on rows, loaded in the same round trip)
-    const int32_t tk1 = tl[4 + 16 * wave + n], tk2 = tl[4 + 16 * (wave / 2) + n], tk4 = tl[4 + n];
-    // past the list; tokens without an adapter only need work when storing
-    if (tile >= ntl || (slot < 0 && p.add)) continue;
-    const int s = last_le(p.chunk_base, p.n_slices, ck);
+  // tile header, and this lane's token for each possible spread of waves over
+  // token blocks (which one applies depends on rows); the next item's header
+  // is loaded while the current item runs
+  struct Header {
+    int slot, rows, pos0, tk1, tk2, tk4, tfirst;
+  };
+  auto read_header = [&](int it) {
+    const int32_t *tl = p.meta.tiles + (int64_t)(t0 + it % live) * kTileInts;
+    return Header{tl[0], tl[1], tl[2], tl[4 + 16 * wave + n], tl[4 + 16 * (wave / 2) + n], tl[4 + n], tl[4]};
+  };
+  Header hnext = read_header(item);
+
+  for (; item < hi; item += per) {
+    const int ck = item / live;
+    const Header hd = hnext;
+    if (item + per < hi) hnext = read_header(item + per);
+    const int slot = uniform_value(hd.slot), rows = uniform_value(hd.rows);
+    const int64_t pos0 = uniform_value(hd.pos0);
+    // chunk ck -> slice s and the chunk's first column in it
+    int s = 0, cbase = 0, acc = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxSlices; ++k) {
+      if (k >= p.n_slices) break;
+      if (ck >= acc) {
+        s = k;
+        cbase = acc;
+      }
+      acc += (uniform_value(p.steps[k]) + spi - 1) / spi;
+    }
     const int64_t w = pick(p.width, s, p.n_slices);
-    const int64_t col0 = (int64_t)(ck - pick(p.chunk_base, s, p.n_slices)) * p.cpi;
-    const int ncols = (int)min((int64_t)p.cpi, w - col0);
+    const int64_t col0 = (int64_t)(ck - cbase) * cpi;
+    const int ncols = (int)min((int64_t)cpi, w - col0);
     const int nsteps = (ncols + kXStep - 1) / kXStep;
     const int nb = (rows + 15) / 16;
     const int wpt = nb == 1 ? 4 : (nb == 2 ? 2 : 1);  // waves per token block
@@ -269,7 +302,7 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
     const int r = 16 * tbw + n;
     const bool rv = tbw < nb && r < rows;
     const int64_t pos = pos0 + (rv ? r : 0);
-    const int64_t t = rv ? (int64_t)(wpt == 4 ? tk4 : (wpt == 2 ? tk2 : tk1)) : (int64_t)tl[4];
+    const int64_t t = rv ? (int64_t)(wpt == 4 ? hd.tk4 : (wpt == 2 ? hd.tk2 : hd.tk1)) : (int64_t)hd.tfirst;
     const int64_t yo = pick(p.offset, s, p.n_slices) + col0;
     uint16_t *yrow = y + t * p.ldy + yo;
     // this lane's y octet of block pair pp in step i: columns
@@ -289,32 +322,11 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
       continue;
     }
 
-    const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
-    // ---- rank-r rows of this lane's token, split into bf16 hi + lo: k-step c
-    // holds ranks 16 c + 4 kg .. + 3
-    s16x4 uh[KS], ul[KS];
-    {
-      const int64_t urow = p.u_mode == 0 ? t : pos;
-      const float *ub = p.u + ((int64_t)s * T + urow) * R;
-      const int64_t plane = (int64_t)p.n_slices * T * R;
-#pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        const int j = 16 * c + 4 * kg;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (rv && j < rk) v = sum_partials4(ub + j, plane, p.kch);  // split-K sums, in k-chunk order
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        uh[c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-        ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
-      }
-    }
-
     // ---- B step tiles: rows j < RP, 128 columns; thread octet q covers row
     // idx / 16, columns 8 (idx % 16) .. + 7 of the step (idx = tid + 256 q).
     // Loads past the slot block read zeros (rows >= R); columns past the
     // window may read anything: their results are never stored.
+    const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
     const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick(p.B, s, p.n_slices)) +
                                     (int64_t)slot * pick(p.b_stride, s, p.n_slices),
                                 (uint32_t)(R * w * 2));
@@ -349,13 +361,37 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
 
     load_b(0);
     load_y(0, ycur);
+    // ---- rank-r rows of this lane's token, split into bf16 hi + lo: k-step c
+    // holds ranks 16 c + 4 kg .. + 3
+    s16x4 uh[KS], ul[KS];
+    {
+      const int64_t urow = p.u_mode == 0 ? t : pos;
+      const float *ub = p.u + ((int64_t)s * T + urow) * R;
+      const int64_t plane = (int64_t)p.n_slices * T * R;
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const int j = 16 * c + 4 * kg;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (rv && j < rk) v = sum_partials4(ub + j, plane, p.kch);  // split-K sums, in k-chunk order
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        uh[c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
+      }
+    }
+
     __syncthreads();  // the previous item's last step has read both buffers
     store_b(0);
     __syncthreads();
     for (int i = 0; i < nsteps; ++i) {
-      // next step's loads (one past the end reads harmless addresses)
-      load_b(i + 1);
-      load_y(i + 1, ynext);
+      // next step's loads
+      const bool more = i + 1 < nsteps;
+      if (more) {
+        load_b(i + 1);
+        load_y(i + 1, ynext);
+      }
       const uint16_t *bt = lds.bl[i & 1];
       f32x4 acc[4][2];
 #pragma unroll
@@ -396,9 +432,11 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_mma_kernel(ExpandParams p
           store8(yrow + c, v);
         }
       }
-      if (i + 1 < nsteps) store_b((i + 1) & 1);
+      if (more) {
+        store_b((i + 1) & 1);
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) ycur[pp] = ynext[pp];
+        for (int pp = 0; pp < 4; ++pp) ycur[pp] = ynext[pp];
+      }
       __syncthreads();
     }
   }
@@ -440,7 +478,10 @@ static hipError_t launch_t(const ExpandParams &p, int grid, hipStream_t stream) 
 }
 
 template <int R>
-static hipError_t launch_mma_t(const ExpandParams &p, int grid, hipStream_t stream) {
+static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, hipStream_t stream) {
+  static std::atomic<int> resident[kMaxDevices];
+  const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R>),
+                                                   kXThreads, 0));
   hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -462,13 +503,11 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   const int64_t e = bf16 ? 2 : 4;
   const bool mma = expand_uses_mma(bf16, mode);
   const int64_t T = meta.T, S = meta.S;
-  int64_t sw = 0;
   for (int s = 0; s < n_slices; ++s) {
     p.B[s] = B[s];
     p.b_stride[s] = b_stride[s];
     p.width[s] = width[s];
     p.offset[s] = offset[s];
-    sw += width[s];
   }
   p.y = y;
   p.ldy = ldy;
@@ -476,30 +515,20 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   p.slot_rank = slot_rank;
   if (T == 0) return hipSuccess;
   if (mma) {
-    // columns per item: about 2048 items, at least one 128-column step, at
-    // most 16
-    const int64_t tiles = max_tiles(T, (int32_t)S);
-    const int64_t steps = (sw + kXStep - 1) / kXStep;
-    const int64_t want = 2048;
-    int64_t spi = (tiles * steps + want - 1) / want;
-    spi = std::max<int64_t>(1, std::min<int64_t>(16, spi));
-    p.cpi = (int32_t)(spi * kXStep);
-    p.chunk_base[0] = 0;
-    for (int s = 0; s < n_slices; ++s)
-      p.chunk_base[s + 1] = p.chunk_base[s] + (int32_t)((width[s] + p.cpi - 1) / p.cpi);
-    for (int s = n_slices; s < kMaxSlices; ++s) p.chunk_base[s + 1] = p.chunk_base[s];
-    p.nck = p.chunk_base[n_slices];
-    // no more workgroups than stay resident together (3 or 4 per CU by the
-    // kernel's registers): the rest of the items are taken by the same
-    // workgroups instead of waiting for a slot to be dispatched
-    const int64_t bound = tiles * p.nck;
-    const int64_t resident = 32 * (R <= 16 ? 4 : 3);
-    const int grid = (int)(8 * std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, resident)));
+    // the kernel sizes its items from the live tile count; the grid is at most
+    // the workgroups that stay resident together, and no more than the items
+    // could ever number
+    p.steps_total = 0;
+    for (int s = 0; s < kMaxSlices; ++s) {
+      p.steps[s] = s < n_slices ? (int32_t)((width[s] + kXStep - 1) / kXStep) : 0;
+      p.steps_total += p.steps[s];
+    }
+    const int64_t bound = max_tiles(T, (int32_t)S) * p.steps_total;
     switch (R) {
-      case 8: return launch_mma_t<8>(p, grid, stream);
-      case 16: return launch_mma_t<16>(p, grid, stream);
-      case 32: return launch_mma_t<32>(p, grid, stream);
-      case 64: return launch_mma_t<64>(p, grid, stream);
+      case 8: return launch_mma_t<8>(p, bound, stream);
+      case 16: return launch_mma_t<16>(p, bound, stream);
+      case 32: return launch_mma_t<32>(p, bound, stream);
+      case 64: return launch_mma_t<64>(p, bound, stream);
     }
     return hipErrorInvalidValue;
   }

@@ -2,14 +2,52 @@
 // units.  Internal to the library (not part of the ABI).
 #pragma once
 
+#include <algorithm>
+#include <atomic>
+
 #include "lora_common.h"
 
 namespace lora {
 
+constexpr int kMaxDevices = 64;
+
+// Workgroups of one kernel that fit on the current device at once: its
+// occupancy per CU (registers, LDS) times the CU count.  `cache` is the
+// caller's table for that kernel, filled on first use per device.
+inline int resident_groups(std::atomic<int> (&cache)[kMaxDevices], const void *kernel, int threads,
+                           size_t lds_bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds_bytes) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 8;
+  (void)hipGetLastError();  // a failed query must not be reported by the next launch
+  const int v = per_cu * cus;
+  if (cached) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Grid of a work-list kernel: a multiple of 8 (one share per XCD), no more
+// than `resident` workgroups and no more than `bound` items need.
+inline int xcd_grid(int64_t bound, int resident) {
+  const int64_t per_xcd = std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, resident / 8));
+  return (int)(8 * per_xcd);
+}
+
 struct ShrinkConfig {
   int use_mma_mode;  // 1: matrix-core kernel, 0: vector kernel
   int kc, kch;       // k-chunk length and count
-  int grid;
+  int64_t bound;     // items at most
+  int grid;          // vector kernel's grid
 };
 
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);

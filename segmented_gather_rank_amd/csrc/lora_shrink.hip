@@ -185,15 +185,20 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 // ------------------------------------------------------------- matrix-core path
 //
 // One item = (segment, tile of up to 64 sorted tokens, k-chunk of d_in), all
-// slices' ranks as output columns, in passes of CB 16-column blocks.  Wave w
-// owns token block w (16 tokens) of the tile; a tile with fewer blocks leaves
-// waves whose products are never stored, but every wave helps move the A
-// tiles.  v_mfma_f32_16x16x32_bf16: the A operand is 8 consecutive x values of
-// one token (straight from global memory), the B operand 8 k rows of one
-// output column, read from the A tile in LDS with the gfx950 transposing read.
-// A tiles (128 k rows) are double-buffered in LDS: the next tile and the next
-// x fragments are loaded while the current tile is multiplied, with one
-// barrier per tile.  The result goes out through LDS as 16-byte row pieces.
+// slices' ranks as output columns, in passes of CB 16-column blocks.
+// v_mfma_f32_16x16x32_bf16: the A operand is 8 consecutive x values of one
+// token (straight from global memory), the B operand 8 k rows of one output
+// column, read from the A tile in LDS with the gfx950 transposing read.
+//
+// Waves and tokens: a tile has nb = ceil(rows / 16) blocks of 16 tokens.  The
+// 4 waves are spread over them, 4, 2 or 1 waves per block (wpt); the waves that
+// share a block split the k-steps of every A tile between them, and their
+// partial products are added in a fixed order in the epilogue.  So a tile of
+// few tokens still has each wave load only its share of x, and an A batch can
+// hold more tiles: A tiles (128 k rows) move in batches of up to NTB tiles
+// (at most wpt), double-buffered in LDS: the next batch and its x fragments
+// are loaded while the current one is multiplied, with one barrier per batch.
+// The result goes out through LDS as 16-byte row pieces.
 
 constexpr int kMThreads = 256;
 constexpr int kMKT = 128;    // k rows per A tile
@@ -201,45 +206,72 @@ constexpr int kMKT = 128;    // k rows per A tile
 // LDS row stride (elements) of an A tile with CB column blocks: the 4 rows that
 // one 16-lane transposing read touches fall in distinct banks
 template <int CB> constexpr int kMLda = CB == 1 ? 16 : CB * 16 + 16;
+// A tiles per batch at most (register and LDS budget)
+template <int CB> constexpr int kMNtb = CB == 1 ? 4 : (CB == 2 ? 2 : 1);
 
 template <int R, int CB>
 __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p) {
   constexpr int SG = CB * 16 / R;   // slices per pass
   constexpr int QS = R / 16;        // octets of one slice per thread per tile
   constexpr int LDA = kMLda<CB>;
+  constexpr int NTB = kMNtb<CB>;
   static_assert(SG >= 1 && SG * QS == CB, "column blocks hold whole slices");
-  __shared__ uint16_t at[2][kMKT * LDA];
+  __shared__ uint16_t at[2][NTB * kMKT * LDA];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int mrow = lane % 16, kg = lane / 16;
-  // items (k-chunk, tile) over the metadata's tile list, padded to its
-  // host-known capacity: item = kc * tmax + tile, so the tiles of one segment
-  // that share an A chunk are neighbours; XCD x (blockIdx mod 8) takes a
-  // contiguous run of items, and those tiles meet in one L2
-  const int tmax = (int)max_tiles(p.meta.T, p.meta.S);
-  const int total = tmax * p.kch;
+  // live tiles: the tile list is in key order, so the tiles of tokens without
+  // an adapter come first and are skipped.  Items (k-chunk, live tile),
+  // chunk-major, so the tiles of one segment that share an A chunk are
+  // neighbours; XCD x (blockIdx mod 8) takes a contiguous run of items, and
+  // those tiles meet in one L2
+  const int ntl = uniform_value(p.meta.info[4]);
+  const int t0 = (uniform_value(p.meta.info[3]) + kTileRows - 1) / kTileRows;
+  const int live = ntl - t0;
+  if (live <= 0) return;
+  const int total = live * p.kch;
   const int run = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
-  const int lo = xcd * run, hi = min(total, lo + run);
+  const int hi = min(total, xcd * run + run);
+  int item = xcd * run + (int)blockIdx.x / 8;
+  if (item >= hi) return;
   const uint16_t *x = reinterpret_cast<const uint16_t *>(p.x);
   float *red = reinterpret_cast<float *>(&at[0][0]);  // [64 rows][CB * 16] after the k loop
 
-  for (int item = lo + (int)blockIdx.x / 8; item < hi; item += per) {
-    const int kc = item / tmax, tile = item % tmax;
-    // the tile's header and this lane's token come in one round trip, with
-    // the tile count
-    const int32_t *tl = p.meta.tiles + (int64_t)tile * kTileInts;
-    const int ntl = p.meta.info[4];
-    const int slot = tl[0], rows = tl[1];
-    const int64_t pos0 = tl[2];
-    const int r = 16 * wave + mrow;
-    const int64_t trow = tl[4 + r];
-    if (tile >= ntl || slot < 0) continue;  // past the list, or tokens without an adapter
+  // tile header, and this lane's token for each possible spread of waves over
+  // token blocks (which one applies depends on rows); the next item's header
+  // is loaded while the current item runs
+  struct Header {
+    int slot, rows, pos0, tk1, tk2, tk4, tfirst;
+  };
+  auto read_header = [&](int it) {
+    const int32_t *tl = p.meta.tiles + (int64_t)(t0 + it % live) * kTileInts;
+    return Header{tl[0], tl[1], tl[2], tl[4 + 16 * wave + mrow], tl[4 + 16 * (wave / 2) + mrow], tl[4 + mrow],
+                  tl[4]};
+  };
+  Header hnext = read_header(item);
+
+  for (; item < hi; item += per) {
+    const int kc = item / live;
+    const Header hd = hnext;
+    if (item + per < hi) hnext = read_header(item + per);
+    const int slot = uniform_value(hd.slot), rows = uniform_value(hd.rows);
+    const int64_t pos0 = uniform_value(hd.pos0);
+    if (slot < 0) continue;  // (never: live tiles hold adapter tokens)
     const int64_t kbeg = (int64_t)kc * p.kc;
     const int64_t kend = min(p.d_in, kbeg + p.kc);
     const int ntiles = (int)((kend - kbeg + kMKT - 1) / kMKT);
+    const int nb = (rows + 15) / 16;
+    const int wpt = nb == 1 ? 4 : (nb == 2 ? 2 : 1);  // waves per token block
+    const int tb = wave / wpt, kq = wave % wpt;       // token block, k-step share
+    const int fpt = 4 / wpt;                          // k-steps (x fragments) per tile and wave
+    const int ntb = min(NTB, wpt);                    // A tiles per batch
+    const int nbatch = (ntiles + ntb - 1) / ntb;
+    const int r = 16 * tb + mrow;                     // this lane's row of the tile
+    const bool rv = tb < nb && r < rows;
+    const int64_t trow = rv ? (int64_t)(wpt == 4 ? hd.tk4 : (wpt == 2 ? hd.tk2 : hd.tk1)) : (int64_t)hd.tfirst;
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
     const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
-    const uint16_t *xrow = x + x_row_of(p.meta, r < rows ? trow : (int64_t)tl[4]) * p.ldx;
+    const uint16_t *xrow = x + x_row_of(p.meta, trow) * p.ldx;
 
     for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
       const int ns = min(SG, p.n_slices - s0);
@@ -251,37 +283,53 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
                               (int64_t)slot * pick(p.a_stride, sidx, p.n_slices),
                           (uint32_t)(p.d_in * R * 2));
       }
-      // A tile octet q = sl * QS + qq of this thread: slice sl, flat element
-      // 8 (tid + 256 qq) of that slice's [128][R] block; rows past the k-chunk
-      // and slices past n_slices read zeros
-      u32x4 aq[CB];
-      auto load_a = [&](int it) {
-        const int64_t k0 = kbeg + (int64_t)it * kMKT;
+      // A octet q = t * CB + sl * QS + qq of this thread: tile t of the
+      // batch, slice sl, flat element 8 (tid + 256 qq) of that slice's
+      // [128][R] block; rows past the k-chunk and slices past n_slices read
+      // zeros, tiles past the chunk are not loaded
+      u32x4 aq[NTB * CB];
+      auto load_a = [&](int bi) {
 #pragma unroll
-        for (int q = 0; q < CB; ++q) {
-          const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
-          const int k = e / R, j0 = e % R;
-          const bool ok = sl < ns && k0 + k < kend && j0 < rk;
-          aq[q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * R + j0) * 2) : 0x7FFFFFF0u);
+        for (int t = 0; t < NTB; ++t) {
+          const int it = bi * ntb + t;
+          if (t < ntb && it < ntiles) {
+            const int64_t k0 = kbeg + (int64_t)it * kMKT;
+#pragma unroll
+            for (int q = 0; q < CB; ++q) {
+              const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
+              const int k = e / R, j0 = e % R;
+              const bool ok = sl < ns && k0 + k < kend && j0 < rk;
+              aq[t * CB + q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * R + j0) * 2) : 0x7FFFFFF0u);
+            }
+          }
         }
       };
-      auto store_a = [&](int buf) {
+      auto store_a = [&](int buf, int bi) {
 #pragma unroll
-        for (int q = 0; q < CB; ++q) {
-          const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
-          *reinterpret_cast<u32x4 *>(&at[buf][(e / R) * LDA + sl * R + e % R]) = aq[q];
+        for (int t = 0; t < NTB; ++t) {
+          if (t < ntb && bi * ntb + t < ntiles) {
+#pragma unroll
+            for (int q = 0; q < CB; ++q) {
+              const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
+              *reinterpret_cast<u32x4 *>(&at[buf][(t * kMKT + e / R) * LDA + sl * R + e % R]) = aq[t * CB + q];
+            }
+          }
         }
       };
-      // x fragments of tile it: k-step i, lane k offset 32 i + 8 kg.  Past the
-      // chunk a lane reads a valid element of its row instead: those products
-      // meet zero A rows.  Rows that are not ours are never stored.
+      // x fragment m of a batch: tile m / fpt, k-step wpt (m % fpt) + kq of
+      // that tile, lane k offset 32 (k-step) + 8 kg.  Past the chunk a lane
+      // reads a valid element of its row instead: those products meet zero A
+      // rows.  Rows that are not ours are never stored.
       u32x4 xf[4];
-      auto load_x = [&](int it) {
-        const int64_t k0 = kbeg + (int64_t)it * kMKT;
+      auto frag_ok = [&](int bi, int m) { return m < ntb * fpt && bi * ntb + m / fpt < ntiles; };
+      auto load_x = [&](int bi) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t k = k0 + 32 * i + 8 * kg;
-          xf[i] = gload16(xrow + (k < kend ? k : kbeg));
+        for (int m = 0; m < 4; ++m) {
+          if (frag_ok(bi, m)) {
+            const int it = bi * ntb + m / fpt, i = wpt * (m % fpt) + kq;
+            const int64_t k = kbeg + (int64_t)it * kMKT + 32 * i + 8 * kg;
+            xf[m] = gload16(xrow + (k < kend ? k : kbeg));
+          }
         }
       };
 
@@ -291,29 +339,37 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
       load_a(0);
       load_x(0);
       __syncthreads();  // earlier readers of both buffers are done
-      store_a(0);
+      store_a(0, 0);
       __syncthreads();
-      for (int it = 0; it < ntiles; ++it) {
+      for (int bi = 0; bi < nbatch; ++bi) {
         u32x4 xc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xc[i] = xf[i];
-        load_a(it + 1);  // one past the end reads zeros
-        load_x(it + 1);
-        const uint16_t *a_t = at[it & 1];
+        for (int m = 0; m < 4; ++m) xc[m] = xf[m];
+        const bool more = bi + 1 < nbatch;
+        if (more) {
+          load_a(bi + 1);
+          load_x(bi + 1);
+        }
+        const uint16_t *a_b = at[bi & 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x8 xa = __builtin_bit_cast(bf16x8, xc[i]);
+        for (int m = 0; m < 4; ++m) {
+          if (frag_ok(bi, m)) {
+            const int t = m / fpt, i = wpt * (m % fpt) + kq;
+            const bf16x8 xa = __builtin_bit_cast(bf16x8, xc[m]);
 #pragma unroll
-          for (int b = 0; b < CB; ++b) {
-            const bf16x8 bv = lds_col8(a_t, LDA, 32 * i + 8 * kg, 16 * b);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv, acc[b], 0, 0, 0);
+            for (int b = 0; b < CB; ++b) {
+              const bf16x8 bv = lds_col8(a_b + t * kMKT * LDA, LDA, 32 * i + 8 * kg, 16 * b);
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv, acc[b], 0, 0, 0);
+            }
           }
         }
-        if (it + 1 < ntiles) store_a((it + 1) & 1);
+        if (more) store_a((bi + 1) & 1, bi + 1);
         __syncthreads();
       }
-      // epilogue through LDS: acc[b][v] = C[16 wave + 4 kg + v][16 b + mrow];
-      // then whole row pieces of 4 ranks are written with 16-byte stores
+      // epilogue through LDS: acc[b][v] = this wave's share of
+      // C[16 tb + 4 kg + v][16 b + mrow], at red row 16 wave + 4 kg + v; the
+      // shares of a token block are added in wave order, then whole row pieces
+      // of 4 ranks are written with 16-byte stores
 #pragma unroll
       for (int b = 0; b < CB; ++b)
 #pragma unroll
@@ -322,7 +378,12 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
       const int C4 = ns * R / 4;
       for (int idx = tid; idx < rows * C4; idx += kMThreads) {
         const int r_ = idx / C4, n4 = 4 * (idx - r_ * C4);
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(&red[r_ * (CB * 16) + n4]);
+        const int row0 = 16 * ((r_ / 16) * wpt) + r_ % 16;  // red row of share 0
+        f32x4 v = *reinterpret_cast<const f32x4 *>(&red[row0 * (CB * 16) + n4]);
+        for (int q = 1; q < wpt; ++q) {
+          const f32x4 w = *reinterpret_cast<const f32x4 *>(&red[(row0 + 16 * q) * (CB * 16) + n4]);
+          v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+        }
         put4(p, R, s0 + n4 / R, pos0 + r_, n4 % R, kc, f32x4{v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc});
       }
     }
@@ -399,11 +460,8 @@ ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf1
   const int64_t want = std::max<int64_t>(1, std::min<int64_t>(std::min(tiles, cap), (target + chunks - 1) / chunks));
   c.kc = (int)(((tiles + want - 1) / want) * kMKT);
   c.kch = (int)((d_in + c.kc - 1) / c.kc);
-  const int64_t bound = chunks * c.kch;
-  if (c.use_mma_mode)
-    c.grid = (int)(8 * std::max<int64_t>(1, std::min<int64_t>((bound + 7) / 8, 256)));
-  else
-    c.grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, 2048));
+  c.bound = chunks * c.kch;
+  c.grid = (int)std::max<int64_t>(1, std::min<int64_t>(c.bound, 2048));  // vector kernel
   return c;
 }
 
@@ -420,7 +478,10 @@ static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) 
 }
 
 template <int R, int CB>
-static hipError_t launch_mma_t(const ShrinkParams &p, int grid, hipStream_t stream) {
+static hipError_t launch_mma_t(const ShrinkParams &p, int64_t bound, hipStream_t stream) {
+  static std::atomic<int> resident[kMaxDevices];
+  const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB>),
+                                                   kMThreads, 0));
   hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -461,15 +522,15 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   if (c.use_mma_mode) {
     const int cb = mma_col_blocks(n_slices, R);
     switch (R * 16 + cb) {
-      case 16 * 16 + 1: e = launch_mma_t<16, 1>(p, c.grid, stream); break;
-      case 16 * 16 + 2: e = launch_mma_t<16, 2>(p, c.grid, stream); break;
-      case 16 * 16 + 4: e = launch_mma_t<16, 4>(p, c.grid, stream); break;
-      case 16 * 16 + 8: e = launch_mma_t<16, 8>(p, c.grid, stream); break;
-      case 32 * 16 + 2: e = launch_mma_t<32, 2>(p, c.grid, stream); break;
-      case 32 * 16 + 4: e = launch_mma_t<32, 4>(p, c.grid, stream); break;
-      case 32 * 16 + 8: e = launch_mma_t<32, 8>(p, c.grid, stream); break;
-      case 64 * 16 + 4: e = launch_mma_t<64, 4>(p, c.grid, stream); break;
-      case 64 * 16 + 8: e = launch_mma_t<64, 8>(p, c.grid, stream); break;
+      case 16 * 16 + 1: e = launch_mma_t<16, 1>(p, c.bound, stream); break;
+      case 16 * 16 + 2: e = launch_mma_t<16, 2>(p, c.bound, stream); break;
+      case 16 * 16 + 4: e = launch_mma_t<16, 4>(p, c.bound, stream); break;
+      case 16 * 16 + 8: e = launch_mma_t<16, 8>(p, c.bound, stream); break;
+      case 32 * 16 + 2: e = launch_mma_t<32, 2>(p, c.bound, stream); break;
+      case 32 * 16 + 4: e = launch_mma_t<32, 4>(p, c.bound, stream); break;
+      case 32 * 16 + 8: e = launch_mma_t<32, 8>(p, c.bound, stream); break;
+      case 64 * 16 + 4: e = launch_mma_t<64, 4>(p, c.bound, stream); break;
+      case 64 * 16 + 8: e = launch_mma_t<64, 8>(p, c.bound, stream); break;
     }
   } else {
     switch (R) {
