@@ -189,24 +189,27 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
 // ------------------------------------------------------------- matrix-core path
 //
 // One item = (segment, tile of up to 64 sorted tokens, chunk of `cpi` columns of
-// one slice), walked in steps of 128 columns.  The product is taken transposed,
+// one slice), walked in steps of W columns.  The product is taken transposed,
 // D'[col][token] = B^T u^T with v_mfma_f32_16x16x16_bf16: the A operand (16
 // columns x 4 ranks per lane) comes from the step's B tile in LDS through the
 // gfx950 transposing read, the B operand (4 ranks of one token per lane) is u
-// split into bf16 hi + lo and held in registers for the whole item.  The B tile
-// is written to LDS with its columns permuted inside every 32-column group so
-// that, for each pair of 16-column blocks, a lane's 8 results are 8 consecutive
-// columns of one token: y is read and written 16 bytes per lane, with no LDS
-// round trip.  The next step's B tile and y octets are loaded while the current
-// step is multiplied (two LDS buffers, one barrier per step).
+// split into bf16 hi + lo and held in registers for the whole item.  The tile's
+// rank rows are read once per workgroup (split-K partial sums added in k-chunk
+// order) and handed to the lanes through LDS.  The B tile is written to LDS
+// with its columns permuted inside every 32-column group so that, for each
+// pair of 16-column blocks, a lane's 8 results are 8 consecutive columns of one
+// token: y is read and written 16 bytes per lane, with no LDS round trip.  The
+// next step's B tile and y octets are loaded while the current step is
+// multiplied (two LDS buffers, one barrier per step).
 //
 // Waves and tokens: a tile has nb = ceil(rows / 16) blocks of 16 tokens; the 4
 // waves are spread over them (4, 2 or 1 waves per block) and the waves that
-// share a block split the step's columns.
+// share a block split the step's columns.  A step is 128 columns, or up to
+// 512 for tiles of at most 32 tokens and ranks below 64, so that every step
+// moves the same RP x W block of B and a short tile needs few steps.
 
 constexpr int kXThreads = 256;
-constexpr int kXStep = 128;          // columns per step
-constexpr int kXLdb = kXStep + 16;   // LDS row stride (elements) of a B step tile
+constexpr int kXStep = 128;          // columns per step (the narrowest step)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -223,14 +226,17 @@ __device__ __forceinline__ s16x4 lds_col4(const uint16_t *tile, int ld, int row0
 template <int R>
 struct XLds {
   static constexpr int RP = R < 16 ? 16 : R;  // ranks padded to whole 16-wide steps
-  uint16_t bl[2][RP * kXLdb];
+  static constexpr int WMAX = kXStep * (64 / RP);  // widest step (short tiles)
+  uint16_t bl[2][RP * (WMAX + 16)];
+  uint16_t uh[kTileRows][RP], ul[kTileRows][RP];  // the tile's rank rows, bf16 hi and lo parts
+  int32_t tok[kTileRows];                         // the tile's tokens
 };
 
 template <int R>
-__global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(ExpandParams p) {
+__global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(ExpandParams p) {
   constexpr int RP = XLds<R>::RP;
   constexpr int KS = RP / 16;                     // MFMA k-steps
-  constexpr int BQ = RP * kXStep / 8 / kXThreads;  // B octets per thread per step
+  constexpr int BQ = 4;                           // B octets per thread per step, at most
   __shared__ XLds<R> lds;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n = lane % 16, kg = lane / 16;
@@ -238,14 +244,19 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
   // live tiles: the tile list is in key order, so the tiles of tokens without
   // an adapter come first, and adding into y they need no work
   const int ntl = uniform_value(p.meta.info[4]);
-  const int t0 = p.add ? (uniform_value(p.meta.info[3]) + kTileRows - 1) / kTileRows : 0;
+  const int nneg = p.add ? uniform_value(p.meta.info[3]) : 0;
+  const int t0 = (nneg + kTileRows - 1) / kTileRows;
   const int live = ntl - t0;
   if (live <= 0) return;
-  // steps per item: the live tiles' steps spread evenly over the grid, at most
-  // 16; an item is (column chunk of one slice, tile), chunk-major, so tiles
-  // that share a chunk of B are neighbours, and XCD x (blockIdx mod 8) takes a
-  // contiguous run of items
-  const int spi = min(16, max(1, (int)(((int64_t)live * p.steps_total + gridDim.x - 1) / gridDim.x)));
+  // steps (128 columns) per item: the live tiles' steps spread evenly over the
+  // grid, at most 16; when the live tiles average at most 32 tokens, at least
+  // the width of one wide step (see below).  An item is (column chunk of one
+  // slice, tile), chunk-major, so tiles that share a chunk of B are
+  // neighbours, and XCD x (blockIdx mod 8) takes a contiguous run of items
+  const int avg_rows = (int)((T - nneg) / live);
+  const int wide = avg_rows <= 16 ? 4 : (avg_rows <= 32 ? 2 : 1);
+  const int spi_min = min(wide, 64 / RP);
+  const int spi = min(16, max(spi_min, (int)(((int64_t)live * p.steps_total + gridDim.x - 1) / gridDim.x)));
   const int cpi = spi * kXStep;
   int nck = 0;
 #pragma unroll
@@ -293,22 +304,27 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
     const int64_t w = pick(p.width, s, p.n_slices);
     const int64_t col0 = (int64_t)(ck - cbase) * cpi;
     const int ncols = (int)min((int64_t)cpi, w - col0);
-    const int nsteps = (ncols + kXStep - 1) / kXStep;
     const int nb = (rows + 15) / 16;
     const int wpt = nb == 1 ? 4 : (nb == 2 ? 2 : 1);  // waves per token block
     const int tbw = wave / wpt, wq = wave % wpt;
-    const int cw = kXStep / wpt;                      // columns of this wave per step
+    // step width: 128 columns, or up to 64 / RP times that for short tiles,
+    // so that a step always moves RP x W = up to 8192 B elements
+    const int wx = min(wpt, 64 / RP);                 // 1, 2 or 4
+    const int W = kXStep * wx, ldb = W + 16;
+    const int osh = wx == 1 ? 4 : (wx == 2 ? 5 : 6);  // log2(W / 8): octets per B row
+    const int nq = RP * W / 8 / kXThreads;            // B octets per thread per step
+    const int nsteps = (ncols + W - 1) / W;
+    const int cw = W / wpt;                           // columns of this wave per step
     const int nbp = cw / 32;                          // 16-column block pairs per step
     const int r = 16 * tbw + n;
     const bool rv = tbw < nb && r < rows;
-    const int64_t pos = pos0 + (rv ? r : 0);
     const int64_t t = rv ? (int64_t)(wpt == 4 ? hd.tk4 : (wpt == 2 ? hd.tk2 : hd.tk1)) : (int64_t)hd.tfirst;
     const int64_t yo = pick(p.offset, s, p.n_slices) + col0;
     uint16_t *yrow = y + t * p.ldy + yo;
     // this lane's y octet of block pair pp in step i: columns
-    // i * 128 + wq * cw + 32 pp + 8 kg (clamped to the first one when not ours)
+    // i * W + wq * cw + 32 pp + 8 kg (clamped to the first one when not ours)
     auto ycol = [&](int i, int pp) -> int {
-      const int c = i * kXStep + wq * cw + 32 * pp + 8 * kg;
+      const int c = i * W + wq * cw + 32 * pp + 8 * kg;
       return (pp < nbp && c < ncols) ? c : 0;
     };
 
@@ -316,16 +332,16 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
       for (int i = 0; i < nsteps; ++i)
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          const int c = i * kXStep + wq * cw + 32 * pp + 8 * kg;
+          const int c = i * W + wq * cw + 32 * pp + 8 * kg;
           if (rv && pp < nbp && c < ncols) gstore16(yrow + c, u32x4{0, 0, 0, 0});
         }
       continue;
     }
 
-    // ---- B step tiles: rows j < RP, 128 columns; thread octet q covers row
-    // idx / 16, columns 8 (idx % 16) .. + 7 of the step (idx = tid + 256 q).
-    // Loads past the slot block read zeros (rows >= R); columns past the
-    // window may read anything: their results are never stored.
+    // ---- B step tiles: rows j < RP, W columns; thread octet q covers row
+    // idx / (W / 8), columns 8 (idx % (W / 8)) .. + 7 of the step
+    // (idx = tid + 256 q).  Loads past the slot block (rows >= R), past the
+    // slot's rank or past the chunk read zeros without touching memory.
     const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
     const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick(p.B, s, p.n_slices)) +
                                     (int64_t)slot * pick(p.b_stride, s, p.n_slices),
@@ -334,10 +350,12 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
     auto load_b = [&](int i) {
 #pragma unroll
       for (int q = 0; q < BQ; ++q) {
-        const int idx = tid + kXThreads * q;
-        const int j = idx / 16, h = idx % 16;
-        const int64_t c = col0 + (int64_t)i * kXStep + 8 * h;
-        bq[q] = buf_load16(br, j < rk ? (uint32_t)(((int64_t)j * w + c) * 2) : 0x7FFFFFF0u);
+        if (q < nq) {
+          const int idx = tid + kXThreads * q;
+          const int j = idx >> osh, h = idx & ((1 << osh) - 1);
+          const int c = i * W + 8 * h;
+          bq[q] = buf_load16(br, (j < rk && c < ncols) ? (uint32_t)(((int64_t)j * w + col0 + c) * 2) : 0x7FFFFFF0u);
+        }
       }
     };
     // permuted store: the 8 columns 32 g32 + 8 g4 .. + 7 go to block 2 g32
@@ -345,12 +363,14 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
     auto store_b = [&](int buf) {
 #pragma unroll
       for (int q = 0; q < BQ; ++q) {
-        const int idx = tid + kXThreads * q;
-        const int j = idx / 16, h = idx % 16;
-        const int col = 32 * (h / 4) + 4 * (h % 4);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2 *>(&lds.bl[buf][j * kXLdb + col]) = u32x2{bq[q][0], bq[q][1]};
-        *reinterpret_cast<u32x2 *>(&lds.bl[buf][j * kXLdb + col + 16]) = u32x2{bq[q][2], bq[q][3]};
+        if (q < nq) {
+          const int idx = tid + kXThreads * q;
+          const int j = idx >> osh, h = idx & ((1 << osh) - 1);
+          const int col = 32 * (h / 4) + 4 * (h % 4);
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u32x2 *>(&lds.bl[buf][j * ldb + col]) = u32x2{bq[q][0], bq[q][1]};
+          *reinterpret_cast<u32x2 *>(&lds.bl[buf][j * ldb + col + 16]) = u32x2{bq[q][2], bq[q][3]};
+        }
       }
     };
     u32x4 ycur[4], ynext[4];
@@ -361,30 +381,51 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
 
     load_b(0);
     load_y(0, ycur);
-    // ---- rank-r rows of this lane's token, split into bf16 hi + lo: k-step c
-    // holds ranks 16 c + 4 kg .. + 3
-    s16x4 uh[KS], ul[KS];
+    // ---- rank-r rows of the tile, read once per workgroup (rows x quads of
+    // 4 ranks, two per thread and batch), split-K sums added in k-chunk order,
+    // split into bf16 hi + lo parts in LDS; lane (token n, kg) then takes
+    // ranks 16 c + 4 kg .. + 3 of its token for k-step c.  Rows in token
+    // order need the tile's tokens, which the header already brought.
+    if (p.u_mode == 0 && kg == 0) lds.tok[16 * wave + n] = hd.tk1;
+    __syncthreads();  // the previous item's last step has read every buffer
     {
-      const int64_t urow = p.u_mode == 0 ? t : pos;
-      const float *ub = p.u + ((int64_t)s * T + urow) * R;
+      constexpr int QR = RP / 4;
+      const float *ubase = p.u + (int64_t)s * T * R;
       const int64_t plane = (int64_t)p.n_slices * T * R;
+      for (int pi = tid; pi < rows * QR; pi += 2 * kXThreads) {
+        f32x4 v[2];
 #pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        const int j = 16 * c + 4 * kg;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (rv && j < rk) v = sum_partials4(ub + j, plane, p.kch);  // split-K sums, in k-chunk order
-        uint32_t h[4], l[4];
+        for (int e = 0; e < 2; ++e) {
+          const int pe = pi + kXThreads * e;
+          const int row = pe / QR, j = 4 * (pe % QR);
+          const int64_t urow = p.u_mode == 0 ? (int64_t)lds.tok[row < kTileRows ? row : 0] : pos0 + row;
+          v[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (pe < rows * QR && j < rk) v[e] = sum_partials4(ubase + urow * R + j, plane, p.kch);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        uh[c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-        ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
+        for (int e = 0; e < 2; ++e) {
+          const int pe = pi + kXThreads * e;
+          if (pe < rows * QR) {
+            const int row = pe / QR, j = 4 * (pe % QR);
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) split_bf16(v[e][m], h[m], l[m]);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2 *>(&lds.uh[row][j]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            *reinterpret_cast<u32x2 *>(&lds.ul[row][j]) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+          }
+        }
       }
     }
-
-    __syncthreads();  // the previous item's last step has read both buffers
     store_b(0);
     __syncthreads();
+    // rows past the tile hold stale values: their results are never stored
+    s16x4 uh[KS], ul[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      uh[c] = *reinterpret_cast<const s16x4 *>(&lds.uh[r][16 * c + 4 * kg]);
+      ul[c] = *reinterpret_cast<const s16x4 *>(&lds.ul[r][16 * c + 4 * kg]);
+    }
     for (int i = 0; i < nsteps; ++i) {
       // next step's loads
       const bool more = i + 1 < nsteps;
@@ -393,43 +434,39 @@ __global__ __launch_bounds__(kXThreads, R <= 16 ? 4 : 3) void expand_mma_kernel(
         load_y(i + 1, ynext);
       }
       const uint16_t *bt = lds.bl[i & 1];
-      f32x4 acc[4][2];
+      // per 16-column block pair: products, then the lane's 8 columns of y
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) acc[pp][0] = acc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (tbw < nb) {
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          if (pp < nbp) {
+      for (int pp = 0; pp < 4; ++pp) {
+        if (pp < nbp) {
+          f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          if (tbw < nb) {
             const int blk0 = (wq * cw) / 16 + 2 * pp;
 #pragma unroll
             for (int c = 0; c < KS; ++c) {
 #pragma unroll
               for (int hh = 0; hh < 2; ++hh) {
-                const s16x4 a = lds_col4(bt, kXLdb, 16 * c + 4 * kg, 16 * (blk0 + hh));
-                acc[pp][hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ul[c], acc[pp][hh], 0, 0, 0);
-                acc[pp][hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, uh[c], acc[pp][hh], 0, 0, 0);
+                const s16x4 a = lds_col4(bt, ldb, 16 * c + 4 * kg, 16 * (blk0 + hh));
+                acc[hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ul[c], acc[hh], 0, 0, 0);
+                acc[hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, uh[c], acc[hh], 0, 0, 0);
               }
             }
           }
-        }
-      }
-      // epilogue: lane (token n, kg) holds columns 32 pp + 8 kg + 0..7 of the step
+          // lane (token n, kg) holds columns 32 pp + 8 kg + 0..7 of its share
+          const int c = i * W + wq * cw + 32 * pp + 8 * kg;
+          if (rv && c < ncols) {
+            float v[8];
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int c = i * kXStep + wq * cw + 32 * pp + 8 * kg;
-        if (rv && pp < nbp && c < ncols) {
-          float v[8];
+            for (int m = 0; m < 4; ++m) {
+              v[2 * m] = p.add ? bf16_lo(ycur[pp][m]) : 0.f;
+              v[2 * m + 1] = p.add ? bf16_hi(ycur[pp][m]) : 0.f;
+            }
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            v[2 * m] = p.add ? bf16_lo(ycur[pp][m]) : 0.f;
-            v[2 * m + 1] = p.add ? bf16_hi(ycur[pp][m]) : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              v[e] += acc[0][e];
+              v[4 + e] += acc[1][e];
+            }
+            store8(yrow + c, v);
           }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] += acc[pp][0][e];
-            v[4 + e] += acc[pp][1][e];
-          }
-          store8(yrow + c, v);
         }
       }
       if (more) {
