@@ -169,14 +169,8 @@ lora_status lora_meta_workspace_bytes(int64_t T, int32_t S, size_t *bytes) {
   return LORA_OK;
 }
 
-lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S, void *d_ws,
-                              size_t ws_bytes, lora_meta *out, void *stream) {
-  if (!out || T < 0 || T > INT32_MAX || S < 1 || !d_ws || !aligned16(d_ws))
-    return LORA_ERR_INVALID_ARG;
-  if (S > kMaxSlots) return LORA_ERR_UNSUPPORTED;
-  if (T > 0 && !d_token_slot) return LORA_ERR_INVALID_ARG;
-  const MetaLayout L = meta_layout(T, S);
-  if (ws_bytes < L.total) return LORA_ERR_WORKSPACE;
+// Points the metadata struct at its arrays inside the workspace.
+static void place_meta(lora_meta *out, void *d_ws, const MetaLayout &L, int64_t T, int32_t S) {
   char *base = static_cast<char *>(d_ws);
   out->num_tokens = T;
   out->num_slots = S;
@@ -188,6 +182,17 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
   out->seg_start = reinterpret_cast<int32_t *>(base + L.seg_start);
   out->info = reinterpret_cast<int32_t *>(base + L.info);
   out->tiles = reinterpret_cast<int32_t *>(base + L.tiles);
+}
+
+lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S, void *d_ws,
+                              size_t ws_bytes, lora_meta *out, void *stream) {
+  if (!out || T < 0 || T > INT32_MAX || S < 1 || !d_ws || !aligned16(d_ws))
+    return LORA_ERR_INVALID_ARG;
+  if (S > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+  if (T > 0 && !d_token_slot) return LORA_ERR_INVALID_ARG;
+  const MetaLayout L = meta_layout(T, S);
+  if (ws_bytes < L.total) return LORA_ERR_WORKSPACE;
+  place_meta(out, d_ws, L, T, S);
   const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->sorted_slot, out->seg_slot,
                                    out->seg_count, out->seg_start, out->info, out->tiles,
                                    static_cast<hipStream_t>(stream));
@@ -199,8 +204,7 @@ lora_status lora_moe_meta_workspace_bytes(int64_t T, int32_t topk, int32_t S, in
   if (!bytes || T < 0 || topk < 1 || S < 1 || E_local < 1) return LORA_ERR_INVALID_ARG;
   if (T * topk > INT32_MAX) return LORA_ERR_INVALID_ARG;
   if ((int64_t)S * E_local > kMaxSlots) return LORA_ERR_UNSUPPORTED;
-  const int64_t n = T * topk;
-  *bytes = align256(sizeof(int32_t) * (size_t)std::max<int64_t>(n, 1)) + meta_layout(n, S * E_local).total;
+  *bytes = meta_layout(T * topk, S * E_local).total;
   return LORA_OK;
 }
 
@@ -215,19 +219,15 @@ lora_status lora_prepare_moe_meta(const int32_t *d_topk_ids, int64_t T, int32_t 
   if (T > 0 && (!d_topk_ids || !d_token_slot)) return LORA_ERR_INVALID_ARG;
   if (!aligned4(d_topk_ids) || !aligned4(d_token_slot) || !aligned4(d_expert_map)) return LORA_ERR_INVALID_ARG;
   size_t need = 0;
-  lora_status st = lora_moe_meta_workspace_bytes(T, topk, S, E_local, &need);
+  const lora_status st = lora_moe_meta_workspace_bytes(T, topk, S, E_local, &need);
   if (st != LORA_OK) return st;
   if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   const int64_t n = T * topk;
-  int32_t *keys = static_cast<int32_t *>(d_ws);
-  char *rest = static_cast<char *>(d_ws) + align256(sizeof(int32_t) * (size_t)std::max<int64_t>(n, 1));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_moe_keys(d_topk_ids, T, topk, d_token_slot, S, E_global, E_local, d_expert_map, keys, s) !=
-      hipSuccess)
-    return LORA_ERR_HIP;
-  st = lora_prepare_meta(keys, n, S * E_local, rest, ws_bytes - (rest - static_cast<char *>(d_ws)), out,
-                         stream);
-  if (st != LORA_OK) return st;
+  place_meta(out, d_ws, meta_layout(n, S * E_local), n, S * E_local);
+  const hipError_t e = launch_meta_moe(d_topk_ids, T, topk, d_token_slot, S, E_global, E_local, d_expert_map,
+                                       out->sorted, out->sorted_slot, out->seg_slot, out->seg_count,
+                                       out->seg_start, out->info, out->tiles, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return LORA_ERR_HIP;
   out->x_row_div = topk;
   return LORA_OK;
 }

@@ -248,25 +248,47 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(ExpandParams p
   const int t0 = (nneg + kTileRows - 1) / kTileRows;
   const int live = ntl - t0;
   if (live <= 0) return;
-  // steps (128 columns) per item: the live tiles' steps spread evenly over the
-  // grid, at most 16; when the live tiles average at most 32 tokens, at least
-  // the width of one wide step (see below).  An item is (column chunk of one
-  // slice, tile), chunk-major, so tiles that share a chunk of B are
-  // neighbours, and XCD x (blockIdx mod 8) takes a contiguous run of items
+  // steps (128 columns) per item, spi: from spi0, the live tiles' steps spread
+  // evenly over the grid (when the live tiles average at most 32 tokens, at
+  // least the width of one wide step), up to 16, the choice with the fewest
+  // steps on the busiest workgroup (the smallest on ties).  An item is (column
+  // chunk of one slice, tile), chunk-major, so tiles that share a chunk of B
+  // are neighbours, and XCD x (blockIdx mod 8) takes a contiguous run of items
   const int avg_rows = (int)((T - nneg) / live);
   const int wide = avg_rows <= 16 ? 4 : (avg_rows <= 32 ? 2 : 1);
   const int spi_min = min(wide, 64 / RP);
-  const int spi = min(16, max(spi_min, (int)(((int64_t)live * p.steps_total + gridDim.x - 1) / gridDim.x)));
-  const int cpi = spi * kXStep;
-  int nck = 0;
+  const int per = gridDim.x / 8;
+  auto chunks = [&](int c) {
+    int nk = 0;
 #pragma unroll
-  for (int k = 0; k < kMaxSlices; ++k) {
-    if (k >= p.n_slices) break;
-    nck += (uniform_value(p.steps[k]) + spi - 1) / spi;
+    for (int k = 0; k < kMaxSlices; ++k) {
+      if (k >= p.n_slices) break;
+      nk += (uniform_value(p.steps[k]) + c - 1) / c;
+    }
+    return nk;
+  };
+  auto busiest = [&](int c, int nk) {  // steps on the busiest workgroup
+    const int64_t run_c = ((int64_t)live * nk + 7) / 8;
+    return ((run_c + per - 1) / per) * c;
+  };
+  const int spi0 = min(16, max(spi_min, (int)(((int64_t)live * p.steps_total + gridDim.x - 1) / gridDim.x)));
+  // lane l scores spi0 + l; the wave takes the lowest (cost, spi)
+  uint64_t score = ~0ull;
+  if (spi0 + lane <= 16) {
+    const int c = spi0 + lane;
+    score = ((uint64_t)busiest(c, chunks(c)) << 8) | (uint64_t)c;
   }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const uint64_t o = __shfl_xor(score, m, kWave);
+    score = o < score ? o : score;
+  }
+  const int spi = (int)uniform_value(score & 0xff);
+  const int nck = chunks(spi);
+  const int cpi = spi * kXStep;
   const int total = live * nck;
   const int run = (total + 7) / 8;
-  const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
+  const int xcd = blockIdx.x % 8;
   const int hi = min(total, xcd * run + run);
   int item = xcd * run + (int)blockIdx.x / 8;
   if (item >= hi) return;

@@ -53,13 +53,15 @@ struct ShrinkConfig {
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);
 size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32_t R);
 
-// keys of the (token, choice) pairs of a top-k routing step (MoE metadata)
-hipError_t launch_moe_keys(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
-                           int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
-                           int32_t *keys, hipStream_t stream);
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
                        int32_t *info, int32_t *tiles, hipStream_t stream);
+// the same over the T * topk (token, choice) pairs of a top-k routing step,
+// keyed by (slot, local expert): S * E_local keys
+hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
+                           int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
+                           int32_t *sorted, int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
+                           int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream);
 
 // for_apply: u is written in sorted-position order, and with a split d_in the
 // partial sums are left in ws for the expand to add (kch_out reports the split)

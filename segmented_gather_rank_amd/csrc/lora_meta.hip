@@ -5,20 +5,32 @@
 // distinct ids are listed in ascending order with their token counts, and the
 // start offsets are the running sum of the counts with a leading 0.
 //
-// Design (gfx950, wave64): keys are slot+1 in [0, S].
-//   1. histogram of keys with LDS integer atomics (order-free, exact);
-//   2. one wave scans the key counts (ballot + popcount for the segment index,
-//      a wave prefix sum for the offsets) and writes the segment arrays;
-//   3. a stable scatter over chunks of 1024 tokens in batch order: inside a
-//      wave, lanes holding the same key find each other with one ballot per
-//      key bit (a wave-wide match), and a lane's rank among equal keys is the
-//      popcount of the matching lanes below it; the per-(wave, key) counts are
-//      prefix-summed across the 16 waves in wave order (one 16-lane DPP row
-//      scan per key), so equal keys keep batch order across waves and across
-//      chunks;
-//   4. while scattering, every token also lands in its work tile (its
-//      segment's sorted range cut into runs of 64), and the token that opens a
-//      tile writes the tile's header.
+// Design (gfx950, wave64): keys are slot+1 in [0, S], K = S + 1 <= 1024.
+//   1. the keys of up to 1024 rows stay in registers (thread t holds row t);
+//      more rows are loaded in batches of 8 per thread, every load of a batch
+//      issued before any is used, and kept in LDS when they fit;
+//   2. every wave counts the keys of its own contiguous run of rows, 64 at a
+//      time: lanes holding the same key find each other through a per-wave
+//      table of lane masks in LDS (each lane ORs its bit into its key's entry
+//      and reads it back), or with one ballot per key bit when the tables do
+//      not fit; a lane's rank among equal keys is the popcount of the
+//      matching lanes below it, and one lane per key adds their number;
+//   3. per key, the 16 waves' counts are prefix-summed in wave order (one
+//      16-lane DPP row scan per key): each wave's first position per key;
+//   4. one thread per key prefix-sums counts, tile counts and presence over
+//      the keys (wave scans with DPP row shifts and row broadcasts): start
+//      offsets, first work tiles, segment indices;
+//   5. the segment arrays are written (no barrier follows global stores);
+//   6. a stable scatter: every wave walks its run again, a row going to its
+//      key's start + earlier waves' and earlier steps' counts + its rank, and
+//      into its work tile (the key's sorted range cut into runs of 64); the
+//      row that opens a tile writes the tile's header.  Equal keys keep batch
+//      order: within a step by lane, across steps and waves by run order.
+// MoE pairs (page "vLLM 源码完全拆解(十八)", section "融合计算:add_lora_w13 与
+// add_lora_w2": tokens regrouped by adapter and expert; section "EP
+// 下只装载本地专家的权重": a rank holds its local experts): row p = t * topk + j
+// is keyed here by slot(t) * E_local + local(topk_ids[p]), with the expert map
+// staged in LDS, so the pairs need no pass of their own.
 #include <algorithm>
 
 #include "lora_host.h"
@@ -27,6 +39,20 @@ namespace lora {
 
 constexpr int kMetaThreads = 1024;
 constexpr int kMetaWaves = kMetaThreads / kWave;
+constexpr int kMetaBatch = 8;                           // keys per thread per batch of loads
+constexpr int kMetaBatchRows = kMetaBatch * kMetaThreads;
+constexpr int kMetaMapLds = 4096;                       // expert maps up to this size go to LDS
+constexpr size_t kMetaLdsMax = 159 * 1024;              // dynamic LDS of the workgroup, at most
+
+// Where the keys come from: a slot id per row, or (MoE) the pair's slot and
+// expert, with key = slot * E_local + local expert (-1: no adapter or a remote
+// expert, -2: an id out of range, counted as bad).
+struct MetaSrc {
+  const int32_t *token_slot;  // per row (plain), or per token (MoE)
+  const int32_t *topk_ids;    // MoE: [T / topk][topk]
+  const int32_t *expert_map;  // MoE: [E_global] or null
+  int32_t topk, S_adapters, E_global, E_local;
+};
 
 // Inclusive prefix sum inside each row of 16 lanes (DPP row shifts; lanes
 // shifted in from outside the row contribute 0).
@@ -38,123 +64,251 @@ __device__ __forceinline__ int row16_inclusive_scan(int v) {
   return v;
 }
 
+template <bool MOE>
+__device__ __forceinline__ int moe_key(const MetaSrc &src, const int32_t *emap, int e, int slot) {
+  if (slot < -1 || slot >= src.S_adapters || e < 0 || e >= src.E_global) return -2;
+  const int le = !src.expert_map ? (e < src.E_local ? e : -2) : (emap ? emap[e] : src.expert_map[e]);
+  if (le < -1 || le >= src.E_local) return -2;
+  return (slot < 0 || le < 0) ? -1 : slot * src.E_local + le;
+}
+
+// Lanes of a wave holding the same key (valid lanes only): one ballot per key
+// bit.
+__device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {  // keys < 1024
+    if (b < nbits) {
+      const uint64_t ones = __ballot(valid && ((key >> b) & 1));
+      same &= ((key >> b) & 1) ? ones : ~ones;
+    }
+  }
+  return valid ? same : 0;
+}
+
+// SMALL: at most 1024 rows; thread tid holds row tid in registers throughout
+// (each wave's run below is then its own 64 rows), and the code for more rows
+// is left out.
+template <bool MOE, bool SMALL>
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
-    const int32_t *__restrict__ token_slot, int64_t T, int32_t S,
+    MetaSrc src, int64_t T, int32_t S, int32_t cached, int32_t match_lds,
     int32_t *__restrict__ sorted, int32_t *__restrict__ sorted_slot,
     int32_t *__restrict__ seg_slot,
     int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
     int32_t *__restrict__ info, int32_t *__restrict__ tiles) {
-  extern __shared__ int32_t lds[];
-  const int K = S + 1;                      // number of keys
-  int32_t *cnt = lds;                       // [K] tokens per key
-  int32_t *next = lds + K;                  // [K] next free position per key
-  int32_t *kstart = lds + 2 * K;            // [K] first sorted position per key
-  int32_t *tbase = lds + 3 * K;             // [K] first work tile per key
-  int32_t *wcnt = lds + 4 * K;              // [16][K] per-wave counts, then offsets
+  extern __shared__ __align__(16) int32_t lds[];  // 16-byte aligned: the lane-mask tables take 8-byte LDS atomics
+  const int K = S + 1;                      // number of keys (slot + 1; 0: none or bad)
+  int32_t *cnt = lds;                       // [K] rows per key
+  int32_t *kstart = lds + K;                // [K] first sorted position per key
+  int32_t *tbase = lds + 2 * K;             // [K] first work tile per key
+  int32_t *woff = lds + 3 * K;              // [16][K] per-wave counts, then offsets
+  // [T] the keys, when they fit in LDS (an LDS-typed pointer, so that its
+  // reads are LDS reads even next to the global path)
+  typedef __attribute__((address_space(3))) int32_t lds_i32;
+  lds_i32 *vcache = (lds_i32 *)(woff + kMetaWaves * K);
+  const bool map_lds = MOE && src.expert_map && src.E_global <= kMetaMapLds;
+  int32_t *emap = map_lds ? woff + kMetaWaves * K + (cached ? T : 0) : nullptr;  // [E_global]
+  // [16][K] per-wave lane masks of one group of rows, per key (8-byte aligned)
+  uint64_t *masks = reinterpret_cast<uint64_t *>(
+      lds + ((3 + kMetaWaves) * K + (cached ? T : 0) + (map_lds ? src.E_global : 0) + 1) / 2 * 2);
   __shared__ int32_t nbad;
+  __shared__ int32_t wsum[kMetaWaves][3];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
 
-  for (int i = tid; i < K; i += kMetaThreads) cnt[i] = 0;
-  for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) wcnt[i] = 0;
+  // raw inputs of one batch of rows, all loads issued before any is used
+  int raw[kMetaBatch], rsl[kMetaBatch];
+  auto load_raw = [&](int64_t b0) {
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i) {
+      const int64_t t = b0 + tid + (int64_t)kMetaThreads * i;
+      if (t < T) {
+        if constexpr (MOE) {
+          raw[i] = src.topk_ids[t];
+          rsl[i] = src.token_slot[t / src.topk];
+        } else {
+          raw[i] = src.token_slot[t];
+        }
+      }
+    }
+  };
+  // the key of row t in [-2, S): from LDS when cached, else from memory
+  auto value_at = [&](int64_t t) -> int {
+    if (cached) return vcache[(int)t];
+    if constexpr (MOE) return moe_key<MOE>(src, emap, src.topk_ids[t], src.token_slot[t / src.topk]);
+    return src.token_slot[t];
+  };
+
+  // 1. keys into LDS, in batches of up to 8 rows per thread (a batch's loads
+  //    are all issued before any is used)
+  if (SMALL || cached) load_raw(0);
+  for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) woff[i] = 0;
+  if (match_lds)
+    for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) masks[i] = 0;
+  if (map_lds)
+    for (int i = tid; i < src.E_global; i += kMetaThreads) emap[i] = src.expert_map[i];
   if (tid == 0) nbad = 0;
   __syncthreads();
+  if (!SMALL && cached) {
+    for (int64_t b0 = 0; b0 < T; b0 += kMetaBatchRows) {
+      if (b0 > 0) load_raw(b0);
+#pragma unroll
+      for (int i = 0; i < kMetaBatch; ++i) {
+        const int64_t t = b0 + tid + (int64_t)kMetaThreads * i;
+        if (t < T) vcache[(int)t] = MOE ? moe_key<MOE>(src, emap, raw[i], rsl[i]) : raw[i];
+      }
+    }
+    __syncthreads();
+  }
 
-  // 1. histogram (the first 1024 slot ids stay in registers for the scatter)
+  // 2. every wave counts the keys of its own contiguous run of rows, 64 rows
+  //    at a time: lanes with the same key find each other (through a per-wave
+  //    table of lane masks in LDS when it fits: every lane ORs its bit into
+  //    its key's entry and reads the entry back; else one ballot per key bit),
+  //    and one of them adds their number (no atomics on the counts: a wave
+  //    owns its row).  With the keys in LDS, each row's key, rank among equal
+  //    keys of its group and the group's count of that key replace it there
+  //    (10 + 6 + 7 bits), so the scatter needs no second match.
+  const int64_t per_w = (T + kMetaWaves * kWave - 1) / (kMetaWaves * kWave) * kWave;
+  const int64_t w_lo = wave * per_w, w_hi = min(T, w_lo + per_w);
+  uint64_t *wmask = masks + wave * K;
   int mybad = 0;
-  int first_v = -1;
-  for (int64_t t = tid; t < T; t += kMetaThreads) {
-    const int v = token_slot[t];
-    if (t < kMetaThreads) first_v = v;
-    const bool ok = v >= -1 && v < S;
-    mybad += ok ? 0 : 1;
-    atomicAdd(&cnt[ok ? v + 1 : 0], 1);
+  int pk_small = 0;  // SMALL: this thread's row, packed as in LDS
+  for (int64_t b = w_lo; b < w_hi; b += kWave) {
+    const int64_t t = b + lane;
+    const bool valid = t < w_hi;
+    int key = 0;
+    if (valid) {
+      int v;
+      if constexpr (SMALL) v = MOE ? moe_key<MOE>(src, emap, raw[0], rsl[0]) : raw[0];
+      else v = value_at(t);
+      const bool ok = v >= -1 && v < S;
+      mybad += ok ? 0 : 1;
+      key = ok ? v + 1 : 0;
+    }
+    uint64_t same;
+    if (match_lds) {
+      if (valid) atomicOr(reinterpret_cast<unsigned long long *>(&wmask[key]), 1ull << lane);
+      same = valid ? wmask[key] : 0;
+    } else {
+      same = match_key(key, valid, nbits);
+    }
+    const int rank = __popcll(same & lanemask_lt()), n = __popcll(same);
+    if (valid && rank == 0) {
+      woff[wave * K + key] += n;
+      if (match_lds) wmask[key] = 0;
+    }
+    const int pk = key | (rank << 10) | (n << 16);
+    if (SMALL) pk_small = pk;
+    else if (cached && valid) vcache[(int)t] = pk;
   }
   if (mybad) atomicAdd(&nbad, mybad);
   __syncthreads();
 
-  // 2. segments: one wave walks the keys in ascending order
-  if (wave == 0) {
-    int seg_base = 0, pos_base = 0, tile_base = 0;
-    for (int k0 = 0; k0 < K; k0 += kWave) {
-      const int k = k0 + lane;
-      const int c = k < K ? cnt[k] : 0;
-      const uint64_t present = __ballot(c > 0);
-      const int seg = seg_base + __popcll(present & lanemask_lt());
-      const int incl = wave_inclusive_scan(c);
-      const int start = pos_base + incl - c;
-      const int nt = (c + kTileRows - 1) / kTileRows;
-      const int tincl = wave_inclusive_scan(nt);
-      if (k < K) {
-        next[k] = start;
-        kstart[k] = start;
-        tbase[k] = tile_base + tincl - nt;
-      }
-      if (c > 0) {
-        seg_slot[seg] = k - 1;
-        seg_count[seg] = c;
-        seg_start[seg] = start;
-      }
-      seg_base += __popcll(present);
-      pos_base += __shfl(incl, kWave - 1, kWave);
-      tile_base += __shfl(tincl, kWave - 1, kWave);
+  // 3. per key, exclusive prefix of the 16 waves' counts in wave order: the
+  //    16 counts of one key sit in one 16-lane row (thread = 16 key + wave)
+  //    and are scanned with DPP row shifts; the row total is the key's count
+  for (int k0 = 0; k0 < K; k0 += kMetaThreads / kMetaWaves) {
+    const int k = k0 + tid / kMetaWaves, w = tid % kMetaWaves;
+    const int c = k < K ? woff[w * K + k] : 0;
+    const int incl = row16_inclusive_scan(c);
+    if (k < K) woff[w * K + k] = incl - c;
+    if (k < K && w == kMetaWaves - 1) cnt[k] = incl;
+  }
+  __syncthreads();
+
+  // 4. over the keys in ascending order (thread k, K <= 1024): start offsets,
+  //    first tiles and segment indices are prefix sums of the counts, tile
+  //    counts and presence.  The segment arrays are written after the barrier
+  //    below: a barrier after global stores would wait for them.
+  const int k = tid;
+  int c, start, nseg = 0, ntiles = 0, seg;
+  {
+    c = k < K ? cnt[k] : 0;
+    const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
+    const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
+    if (lane == kWave - 1) {
+      wsum[wave][0] = ic;
+      wsum[wave][1] = it;
+      wsum[wave][2] = ip;
     }
-    // padding past the last segment, and the closing offset
-    for (int i = seg_base + lane; i < K; i += kWave) {
-      seg_slot[i] = -1;
-      seg_count[i] = 0;
+    __syncthreads();
+    int bc = 0, bt = 0, bp = 0;
+    for (int w = 0; w < kMetaWaves; ++w) {
+      const int a = wsum[w][0], b2 = wsum[w][1], d = wsum[w][2];
+      if (w < wave) {
+        bc += a;
+        bt += b2;
+        bp += d;
+      }
+      nseg += d;
+      ntiles += b2;
     }
-    for (int i = seg_base + lane; i < K + 1; i += kWave) seg_start[i] = (int32_t)T;
-    if (lane == 0) {
-      info[0] = seg_base;
-      info[1] = (T - cnt[0] == 0) ? 1 : 0;
-      info[2] = nbad;
-      info[3] = cnt[0];
-      info[4] = tile_base;
-      info[5] = info[6] = info[7] = 0;
+    start = bc + ic - c;
+    seg = bp + ip - pr;
+    if (k < K) {
+      kstart[k] = start;
+      tbase[k] = bt + it - nt;
     }
   }
   __syncthreads();
 
-  // 3. stable scatter, 1024 tokens per pass in batch order
-  int nbits = 0;
-  while ((1 << nbits) < K) ++nbits;
-  for (int64_t base = 0; base < T; base += kMetaThreads) {
-    const int64_t t = base + tid;
-    const bool valid = t < T;
-    int key = 0;
+  // 5. the segment arrays (thread k), their padding past the last segment, the
+  //    closing offset and the counters; no barrier follows these stores
+  if (c > 0) {
+    seg_slot[seg] = k - 1;
+    seg_count[seg] = c;
+    seg_start[seg] = start;
+  }
+  if (k >= nseg && k < K) {
+    seg_slot[k] = -1;
+    seg_count[k] = 0;
+    seg_start[k] = (int32_t)T;
+  }
+  if (tid == 0) {
+    seg_start[K] = (int32_t)T;
+    info[0] = nseg;
+    info[1] = (T - c == 0) ? 1 : 0;  // thread 0 holds key 0: the rows without an adapter
+    info[2] = nbad;
+    info[3] = c;
+    info[4] = ntiles;
+    info[5] = info[6] = info[7] = 0;
+  }
+
+  // 6. stable scatter: every wave walks its run again, 64 rows at a time; a
+  //    row goes to its key's start + the counts of earlier waves and earlier
+  //    steps of this wave + its rank among equal keys of the step.  Rows also
+  //    land in their work tiles (the key's sorted range cut into runs of 64),
+  //    and the row that opens a tile writes the tile's header.
+  for (int64_t b = w_lo; b < w_hi; b += kWave) {
+    const int64_t t = b + lane;
+    const bool valid = t < w_hi;
+    int key = 0, rank = 0, n = 0;
+    if (SMALL || cached) {
+      if (valid) {
+        const int pk = SMALL ? pk_small : vcache[(int)t];
+        key = pk & 1023;
+        rank = (pk >> 10) & 63;
+        n = pk >> 16;
+      }
+    } else if constexpr (!SMALL) {
+      if (valid) {
+        const int v = value_at(t);
+        key = (v >= -1 && v < S) ? v + 1 : 0;
+      }
+      const uint64_t same = match_key(key, valid, nbits);
+      rank = __popcll(same & lanemask_lt());
+      n = __popcll(same);
+    }
     if (valid) {
-      const int v = base == 0 ? first_v : token_slot[t];
-      key = (v >= -1 && v < S) ? v + 1 : 0;
-    }
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const uint64_t ones = __ballot(valid && ((key >> b) & 1));
-      same &= ((key >> b) & 1) ? ones : ~ones;
-    }
-    const int rank = __popcll(same & lanemask_lt());
-    const bool leader = valid && rank == 0;
-    if (leader) wcnt[wave * K + key] = __popcll(same);
-    __syncthreads();
-    // per key, prefix of the 16 waves' counts in wave order: the 16 counts of
-    // one key sit in one 16-lane row (thread = 16 key + wave) and are scanned
-    // with DPP row shifts; the row's last lane advances the key's next position
-    for (int k0 = 0; k0 < K; k0 += kMetaThreads / kMetaWaves) {
-      const int k = k0 + tid / kMetaWaves, w = tid % kMetaWaves;
-      const int c = k < K ? wcnt[w * K + k] : 0;
-      const int incl = row16_inclusive_scan(c);
-      const int at = k < K ? next[k] : 0;
-      if (k < K) wcnt[w * K + k] = at + incl - c;
-      if (k < K && w == kMetaWaves - 1) next[k] = at + incl;
-    }
-    __syncthreads();
-    if (valid) {
-      const int dst = wcnt[wave * K + key] + rank;
+      const int off = woff[wave * K + key] + rank;  // position inside the key's range
+      const int dst = kstart[key] + off;
       sorted[dst] = (int32_t)t;
       sorted_slot[dst] = key - 1;
-      const int off = dst - kstart[key];
       int32_t *tl = tiles + (int64_t)(tbase[key] + off / kTileRows) * kTileInts;
       tl[4 + off % kTileRows] = (int32_t)t;
       if (off % kTileRows == 0) {
@@ -163,64 +317,73 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
         tl[2] = dst;
         tl[3] = 0;
       }
-    }
-    if (base + kMetaThreads < T) {  // the count table starts the next pass at zero
-      __syncthreads();
-      for (int k = tid; k < kMetaWaves * K; k += kMetaThreads) wcnt[k] = 0;
-      __syncthreads();
+      if (rank == 0) woff[wave * K + key] += n;
     }
   }
 }
 
-// Key of pair p = t * topk + j: slot * E_local + local expert, -1 for no
-// adapter or a remote expert, -2 (counted as bad by the metadata kernel) for
-// ids out of range.
-__global__ __launch_bounds__(256) void moe_keys_kernel(const int32_t *__restrict__ topk_ids, int64_t n,
-                                                       int32_t topk, const int32_t *__restrict__ token_slot,
-                                                       int32_t S, int32_t E_global, int32_t E_local,
-                                                       const int32_t *__restrict__ expert_map,
-                                                       int32_t *__restrict__ keys) {
-  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < n; p += (int64_t)gridDim.x * 256) {
-    const int slot = token_slot[p / topk];
-    const int e = topk_ids[p];
-    int key;
-    if (slot < -1 || slot >= S || e < 0 || e >= E_global) {
-      key = -2;
-    } else {
-      const int le = expert_map ? expert_map[e] : (e < E_local ? e : -2);
-      if (le < -1 || le >= E_local) key = -2;
-      else key = (slot < 0 || le < 0) ? -1 : slot * E_local + le;
-    }
-    keys[p] = key;
-  }
+// Dynamic LDS of the metadata kernel: the key tables, the expert map when it
+// fits, the keys themselves when they fit too, then the per-wave match tables
+// when those fit as well.
+static size_t meta_lds_bytes(int32_t S, int64_t T, int32_t E_map, bool &cached, bool &match_lds) {
+  size_t b = sizeof(int32_t) * (size_t)(S + 1) * (3 + kMetaWaves);
+  if (E_map > 0 && E_map <= kMetaMapLds) b += sizeof(int32_t) * (size_t)E_map;
+  // up to 1024 rows the keys stay in registers
+  cached = T > kMetaThreads && b + sizeof(int32_t) * (size_t)T <= kMetaLdsMax;
+  if (cached) b += sizeof(int32_t) * (size_t)T;
+  b = (b + 7) / 8 * 8;
+  const size_t tables = sizeof(uint64_t) * (size_t)(S + 1) * kMetaWaves;
+  match_lds = b + tables <= kMetaLdsMax;
+  if (match_lds) b += tables;
+  return b;
 }
 
-hipError_t launch_moe_keys(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
-                           int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
-                           int32_t *keys, hipStream_t stream) {
-  const int64_t n = T * topk;
-  if (n == 0) return hipSuccess;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1024));
-  hipLaunchKernelGGL(moe_keys_kernel, dim3(grid), dim3(256), 0, stream, topk_ids, n, topk, token_slot, S,
-                     E_global, E_local, expert_map, keys);
+template <bool MOE, bool SMALL>
+static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_t *sorted,
+                                int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
+                                int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream) {
+  bool cached = false, match_lds = false;
+  const size_t lds = meta_lds_bytes(S, T, MOE && src.expert_map ? src.E_global : 0, cached, match_lds);
+  if (lds > 65536) {
+    // more than the default 64 KB of dynamic LDS
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_kernel<MOE, SMALL>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((meta_kernel<MOE, SMALL>), dim3(1), dim3(kMetaThreads), lds, stream, src, T, S, (int32_t)cached,
+                     (int32_t)match_lds, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles);
   return hipGetLastError();
 }
-
-size_t meta_lds_bytes(int32_t S) { return sizeof(int32_t) * (size_t)(S + 1) * (4 + kMetaWaves); }
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
                        int32_t *info, int32_t *tiles, hipStream_t stream) {
-  const size_t lds = meta_lds_bytes(S);
-  if (lds > 65536) {
-    // large slot counts need more than the default 64 KB of dynamic LDS
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), lds, stream,
-                     token_slot, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles);
-  return hipGetLastError();
+  MetaSrc src{};
+  src.token_slot = token_slot;
+  if (T <= kMetaThreads)
+    return launch_meta_t<false, true>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles,
+                                      stream);
+  return launch_meta_t<false, false>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles,
+                                     stream);
+}
+
+hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
+                           int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
+                           int32_t *sorted, int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
+                           int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream) {
+  MetaSrc src{};
+  src.token_slot = token_slot;
+  src.topk_ids = topk_ids;
+  src.expert_map = expert_map;
+  src.topk = topk;
+  src.S_adapters = S;
+  src.E_global = E_global;
+  src.E_local = E_local;
+  if (T * topk <= kMetaThreads)
+    return launch_meta_t<true, true>(src, T * topk, S * E_local, sorted, sorted_slot, seg_slot, seg_count,
+                                     seg_start, info, tiles, stream);
+  return launch_meta_t<true, false>(src, T * topk, S * E_local, sorted, sorted_slot, seg_slot, seg_count,
+                                    seg_start, info, tiles, stream);
 }
 
 }  // namespace lora
