@@ -21,6 +21,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel arguments (the pointers each kernel reads first) arrive
+    # preloaded in scalar registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=6",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

@@ -99,9 +99,13 @@ template <> struct AOct<float> {
 };
 
 // RK: per-slot ranks are given (a separate instantiation, so that the common
-// case carries none of the extra registers)
+// case carries none of the extra registers).
+// The sorted order and T come first among the arguments, so that they are
+// preloaded into scalar registers and the first loads need no argument fetch.
 template <typename E, int R, bool RK>
-__global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
+__global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__restrict__ sorted,
+                                                               const int32_t *__restrict__ sorted_slot,
+                                                               int64_t T, BgmvParams p) {
   constexpr bool kBf16 = sizeof(E) == 2;
   constexpr int JO = R / 8;             // rank octets per A row
   constexpr int RB = kBThreads / JO;    // A rows covered by one load across the workgroup
@@ -113,15 +117,14 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(BgmvParams p) {
   __shared__ uint32_t uh[kMaxSlices][R / 2], ul[kMaxSlices][R / 2];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int64_t T = p.meta.T;
   const int64_t run = (T + 7) / 8;
   const int64_t local = blockIdx.x / 8;
   if (local >= run) return;
   const int64_t pos = (int64_t)(blockIdx.x % 8) * run + local;
   if (pos >= T) return;
   // both metadata loads go out before either is waited for
-  const int slot = __builtin_amdgcn_readfirstlane(p.meta.sorted_slot[pos]);
-  const int64_t t = __builtin_amdgcn_readfirstlane(p.meta.sorted[pos]);
+  const int slot = __builtin_amdgcn_readfirstlane(sorted_slot[pos]);
+  const int64_t t = __builtin_amdgcn_readfirstlane(sorted[pos]);
   // ranks this slot's adapter really has (rank 0: nothing to add)
   const int rk = slot < 0 ? 0 : (RK ? slot_rank_of(p.slot_rank, slot, R) : R);
   if ((rk == 0 && p.add) || t < 0) return;  // no adapter, add mode: nothing to do
@@ -399,9 +402,11 @@ bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64
 template <typename E, int R>
 static hipError_t launch_t(const BgmvParams &p, int grid, size_t lds, hipStream_t stream) {
   if (p.slot_rank)
-    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true>), dim3(grid), dim3(kBThreads), lds, stream, p);
+    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true>), dim3(grid), dim3(kBThreads), lds, stream, p.meta.sorted,
+                       p.meta.sorted_slot, p.meta.T, p);
   else
-    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false>), dim3(grid), dim3(kBThreads), lds, stream, p);
+    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false>), dim3(grid), dim3(kBThreads), lds, stream, p.meta.sorted,
+                       p.meta.sorted_slot, p.meta.T, p);
   return hipGetLastError();
 }
 

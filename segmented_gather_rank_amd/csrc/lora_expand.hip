@@ -233,7 +233,9 @@ struct XLds {
 };
 
 template <int R>
-__global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(ExpandParams p) {
+__global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t *__restrict__ info,
+                                                                  const int32_t *__restrict__ tiles,
+                                                                  ExpandParams p) {
   constexpr int RP = XLds<R>::RP;
   constexpr int KS = RP / 16;                     // MFMA k-steps
   constexpr int BQ = 4;                           // B octets per thread per step, at most
@@ -243,8 +245,8 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(ExpandParams p
   const int64_t T = p.meta.T;
   // live tiles: the tile list is in key order, so the tiles of tokens without
   // an adapter come first, and adding into y they need no work
-  const int ntl = uniform_value(p.meta.info[4]);
-  const int nneg = p.add ? uniform_value(p.meta.info[3]) : 0;
+  const int ntl = uniform_value(info[4]);
+  const int nneg = p.add ? uniform_value(info[3]) : 0;
   const int t0 = (nneg + kTileRows - 1) / kTileRows;
   const int live = ntl - t0;
   if (live <= 0) return;
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(ExpandParams p
     int slot, rows, pos0, tk1, tk2, tk4, tfirst;
   };
   auto read_header = [&](int it) {
-    const int32_t *tl = p.meta.tiles + (int64_t)(t0 + it % live) * kTileInts;
+    const int32_t *tl = tiles + (int64_t)(t0 + it % live) * kTileInts;
     return Header{tl[0], tl[1], tl[2], tl[4 + 16 * wave + n], tl[4 + 16 * (wave / 2) + n], tl[4 + n], tl[4]};
   };
   Header hnext = read_header(item);
@@ -541,7 +543,7 @@ static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, hipStream_t
   static std::atomic<int> resident[kMaxDevices];
   const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R>),
                                                    kXThreads, 0));
-  hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), 0, stream, p);
+  hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), 0, stream, p.meta.info, p.meta.tiles, p);
   return hipGetLastError();
 }
 

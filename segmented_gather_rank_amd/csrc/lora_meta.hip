@@ -91,7 +91,8 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
 // is left out.
 template <bool MOE, bool SMALL>
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
-    MetaSrc src, int64_t T, int32_t S, int32_t cached, int32_t match_lds,
+    const int32_t *__restrict__ token_slot, const int32_t *__restrict__ topk_ids, int64_t T, MetaSrc src,
+    int32_t S, int32_t cached, int32_t match_lds,
     int32_t *__restrict__ sorted, int32_t *__restrict__ sorted_slot,
     int32_t *__restrict__ seg_slot,
     int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
@@ -128,10 +129,10 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       const int64_t t = b0 + tid + (int64_t)kMetaThreads * i;
       if (t < T) {
         if constexpr (MOE) {
-          raw[i] = src.topk_ids[t];
-          rsl[i] = src.token_slot[t / src.topk];
+          raw[i] = topk_ids[t];
+          rsl[i] = token_slot[t / src.topk];
         } else {
-          raw[i] = src.token_slot[t];
+          raw[i] = token_slot[t];
         }
       }
     }
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   // the key of row t in [-2, S): from LDS when cached, else from memory
   auto value_at = [&](int64_t t) -> int {
     if (cached) return vcache[(int)t];
-    if constexpr (MOE) return moe_key<MOE>(src, emap, src.topk_ids[t], src.token_slot[t / src.topk]);
-    return src.token_slot[t];
+    if constexpr (MOE) return moe_key<MOE>(src, emap, topk_ids[t], token_slot[t / src.topk]);
+    return token_slot[t];
   };
 
   // 1. keys into LDS, in batches of up to 8 rows per thread (a batch's loads
@@ -350,7 +351,8 @@ static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((meta_kernel<MOE, SMALL>), dim3(1), dim3(kMetaThreads), lds, stream, src, T, S, (int32_t)cached,
+  hipLaunchKernelGGL((meta_kernel<MOE, SMALL>), dim3(1), dim3(kMetaThreads), lds, stream, src.token_slot,
+                     src.topk_ids, T, src, S, (int32_t)cached,
                      (int32_t)match_lds, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles);
   return hipGetLastError();
 }

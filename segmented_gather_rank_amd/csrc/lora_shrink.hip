@@ -210,7 +210,9 @@ template <int CB> constexpr int kMLda = CB == 1 ? 16 : CB * 16 + 16;
 template <int CB> constexpr int kMNtb = CB == 1 ? 4 : (CB == 2 ? 2 : 1);
 
 template <int R, int CB>
-__global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p) {
+__global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t *__restrict__ info,
+                                                                  const int32_t *__restrict__ tiles,
+                                                                  ShrinkParams p) {
   constexpr int SG = CB * 16 / R;   // slices per pass
   constexpr int QS = R / 16;        // octets of one slice per thread per tile
   constexpr int LDA = kMLda<CB>;
@@ -224,8 +226,8 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
   // chunk-major, so the tiles of one segment that share an A chunk are
   // neighbours; XCD x (blockIdx mod 8) takes a contiguous run of items, and
   // those tiles meet in one L2
-  const int ntl = uniform_value(p.meta.info[4]);
-  const int t0 = (uniform_value(p.meta.info[3]) + kTileRows - 1) / kTileRows;
+  const int ntl = uniform_value(info[4]);
+  const int t0 = (uniform_value(info[3]) + kTileRows - 1) / kTileRows;
   const int live = ntl - t0;
   if (live <= 0) return;
   const int total = live * p.kch;
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(ShrinkParams p
     int slot, rows, pos0, tk1, tk2, tk4, tfirst;
   };
   auto read_header = [&](int it) {
-    const int32_t *tl = p.meta.tiles + (int64_t)(t0 + it % live) * kTileInts;
+    const int32_t *tl = tiles + (int64_t)(t0 + it % live) * kTileInts;
     return Header{tl[0], tl[1], tl[2], tl[4 + 16 * wave + mrow], tl[4 + 16 * (wave / 2) + mrow], tl[4 + mrow],
                   tl[4]};
   };
@@ -482,7 +484,8 @@ static hipError_t launch_mma_t(const ShrinkParams &p, int64_t bound, hipStream_t
   static std::atomic<int> resident[kMaxDevices];
   const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB>),
                                                    kMThreads, 0));
-  hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), 0, stream, p);
+  hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), 0, stream, p.meta.info, p.meta.tiles,
+                     p);
   return hipGetLastError();
 }
 
