@@ -77,8 +77,9 @@ __device__ __forceinline__ float group_sum(float v, int jg) {
   return v;
 }
 
+template <int NS>
 __device__ __forceinline__ int slice_of_oct(const BgmvParams &p, int o) {
-  return last_le(p.oct_base, p.n_slices, o);
+  return last_le<NS>(p.oct_base, p.n_slices, o);
 }
 
 // One rank octet of A (8 consecutive ranks of one k row) as raw words.
@@ -102,7 +103,7 @@ template <> struct AOct<float> {
 // case carries none of the extra registers).
 // The sorted order and T come first among the arguments, so that they are
 // preloaded into scalar registers and the first loads need no argument fetch.
-template <typename E, int R, bool RK>
+template <typename E, int R, bool RK, int NS>
 __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__restrict__ sorted,
                                                                const int32_t *__restrict__ sorted_slot,
                                                                int64_t T, BgmvParams p) {
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
   // x row: bf16 -> (x[k], x[k + RB]) pair words, fp32 -> values; zero-padded
   extern __shared__ __align__(16) unsigned char bgmv_lds[];
   __shared__ float red[kBWaves][R];
-  __shared__ float us[kMaxSlices][R];
-  __shared__ uint32_t uh[kMaxSlices][R / 2], ul[kMaxSlices][R / 2];
+  __shared__ float us[NS][R];
+  __shared__ uint32_t uh[NS][R / 2], ul[NS][R / 2];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int64_t run = (T + 7) / 8;
@@ -128,14 +129,14 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
   // ranks this slot's adapter really has (rank 0: nothing to add)
   const int rk = slot < 0 ? 0 : (RK ? slot_rank_of(p.slot_rank, slot, R) : R);
   if ((rk == 0 && p.add) || t < 0) return;  // no adapter, add mode: nothing to do
-  const int n_oct = pick(p.oct_base, p.n_slices);
+  const int n_oct = pick<NS + 1>(p.oct_base, p.n_slices);
   E *y = reinterpret_cast<E *>(p.y) + t * p.ldy;
 
   if (rk == 0) {  // store mode, no adapter: the windows become 0
     const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int o = tid; o < n_oct; o += kBThreads) {
-      const int s = slice_of_oct(p, o);
-      store8(y + pick(p.offset, s) + 8 * (o - pick(p.oct_base, s)), z);
+      const int s = slice_of_oct<NS>(p, o);
+      store8(y + pick<NS>(p.offset, s) + 8 * (o - pick<NS + 1>(p.oct_base, s)), z);
     }
     return;
   }
@@ -151,12 +152,12 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
   const int o0 = tid / jg, ostep = kBThreads / jg;
   // threads without an octet read octet 0's rows and drop them
   const int oc = o0 < n_oct ? o0 : 0;
-  const int s0 = slice_of_oct(p, oc);
-  const int64_t n00 = 8 * (int64_t)(oc - pick(p.oct_base, s0, p.n_slices));
-  const E *Bb0 = reinterpret_cast<const E *>(pick(p.B, s0, p.n_slices)) +
-                 (int64_t)slot * pick(p.b_stride, s0, p.n_slices) + n00;  // rank row 0 of the octet
-  const int64_t w0 = pick(p.width, s0, p.n_slices);
-  const int64_t yoff0 = pick(p.offset, s0, p.n_slices) + n00;
+  const int s0 = slice_of_oct<NS>(p, oc);
+  const int64_t n00 = 8 * (int64_t)(oc - pick<NS + 1>(p.oct_base, s0, p.n_slices));
+  const E *Bb0 = reinterpret_cast<const E *>(pick<NS>(p.B, s0, p.n_slices)) +
+                 (int64_t)slot * pick<NS>(p.b_stride, s0, p.n_slices) + n00;  // rank row 0 of the octet
+  const int64_t w0 = pick<NS>(p.width, s0, p.n_slices);
+  const int64_t yoff0 = pick<NS>(p.offset, s0, p.n_slices) + n00;
   const rsrc_t xr = make_rsrc(reinterpret_cast<const E *>(p.x) + x_row_of(p.meta, t) * p.ldx,
                               (uint32_t)(p.d_in * sizeof(E)));
   const rsrc_t ar0 = make_rsrc(reinterpret_cast<const E *>(p.A[0]) + (int64_t)slot * p.a_stride[0], a_bytes);
@@ -248,8 +249,8 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
   // ---- shrink
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   for (int s = 0; s < p.n_slices; ++s) {
-    const rsrc_t ar = make_rsrc(reinterpret_cast<const E *>(pick(p.A, s, p.n_slices)) +
-                                    (int64_t)slot * pick(p.a_stride, s, p.n_slices),
+    const rsrc_t ar = make_rsrc(reinterpret_cast<const E *>(pick<NS>(p.A, s, p.n_slices)) +
+                                    (int64_t)slot * pick<NS>(p.a_stride, s, p.n_slices),
                                 a_bytes);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int bb = 0; bb < p.n_inst; bb += NA) {
@@ -316,12 +317,12 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
     int64_t n0 = n00, w = w0, yoff = yoff0;
     const E *Bb = Bb0;  // rank row 0 of this octet's columns
     if (it > 0) {
-      s = slice_of_oct(p, o);
-      n0 = 8 * (int64_t)(o - pick(p.oct_base, s, p.n_slices));
-      w = pick(p.width, s, p.n_slices);
-      Bb = reinterpret_cast<const E *>(pick(p.B, s, p.n_slices)) + (int64_t)slot * pick(p.b_stride, s, p.n_slices) +
+      s = slice_of_oct<NS>(p, o);
+      n0 = 8 * (int64_t)(o - pick<NS + 1>(p.oct_base, s, p.n_slices));
+      w = pick<NS>(p.width, s, p.n_slices);
+      Bb = reinterpret_cast<const E *>(pick<NS>(p.B, s, p.n_slices)) + (int64_t)slot * pick<NS>(p.b_stride, s, p.n_slices) +
            n0;
-      yoff = pick(p.offset, s, p.n_slices) + n0;
+      yoff = pick<NS>(p.offset, s, p.n_slices) + n0;
       if (g == 0 && p.add) load8(y + yoff, yv);
     }
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -401,13 +402,16 @@ bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64
 
 template <typename E, int R>
 static hipError_t launch_t(const BgmvParams &p, int grid, size_t lds, hipStream_t stream) {
-  if (p.slot_rank)
-    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true>), dim3(grid), dim3(kBThreads), lds, stream, p.meta.sorted,
-                       p.meta.sorted_slot, p.meta.T, p);
-  else
-    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false>), dim3(grid), dim3(kBThreads), lds, stream, p.meta.sorted,
-                       p.meta.sorted_slot, p.meta.T, p);
-  return hipGetLastError();
+  return with_slice_bound(p.n_slices, [&](auto ns) {
+    constexpr int NS = decltype(ns)::value;
+    if (p.slot_rank)
+      hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true, NS>), dim3(grid), dim3(kBThreads), lds, stream,
+                         p.meta.sorted, p.meta.sorted_slot, p.meta.T, p);
+    else
+      hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false, NS>), dim3(grid), dim3(kBThreads), lds, stream,
+                         p.meta.sorted, p.meta.sorted_slot, p.meta.T, p);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,

@@ -5,9 +5,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lora {
 
 constexpr int kMaxSlices = 8;
+
+// Kernels are instantiated for at most NS slices, NS = 1, 2, 4 or 8: f is
+// called with std::integral_constant<int, NS> for the smallest NS >= n.
+template <typename F>
+inline auto with_slice_bound(int n, F &&f) {
+  if (n <= 1) return f(std::integral_constant<int, 1>{});
+  if (n <= 2) return f(std::integral_constant<int, 2>{});
+  if (n <= 4) return f(std::integral_constant<int, 4>{});
+  return f(std::integral_constant<int, 8>{});
+}
 constexpr int kMaxSlots = 1023;
 constexpr int kWave = 64;
 
@@ -184,12 +196,15 @@ __device__ __forceinline__ T uniform_value(T v) {
 // may differ between lanes and only the first n entries are in use (n is
 // uniform).  Indexing the array with a runtime value would make the compiler
 // copy the whole block to scratch memory; an unrolled select over scalar
-// copies keeps it in registers.
-template <typename T, int N>
+// copies keeps it in registers.  M bounds the entries looked at at compile
+// time: kernels instantiated for at most M slices carry no code for more
+// (code that runs once per workgroup is fetched cold, so its size is time).
+template <int M = 1 << 20, typename T, int N>
 __device__ __forceinline__ T pick(const T (&a)[N], int i, int n = N) {
+  constexpr int L = M < N ? M : N;
   T v = uniform_value(a[0]);
 #pragma unroll
-  for (int k = 1; k < N; ++k) {
+  for (int k = 1; k < L; ++k) {
     if (k >= n) break;
     v = (i == k) ? uniform_value(a[k]) : v;
   }
@@ -198,11 +213,12 @@ __device__ __forceinline__ T pick(const T (&a)[N], int i, int n = N) {
 
 // Index of the last entry of prefix[0..n) (non-decreasing, prefix[0] = 0)
 // that is <= v.
-template <int N>
+template <int M = 1 << 20, int N>
 __device__ __forceinline__ int last_le(const int32_t (&prefix)[N], int n, int v) {
+  constexpr int L = M < N ? M : N;
   int s = 0;
 #pragma unroll
-  for (int k = 1; k < N; ++k) {
+  for (int k = 1; k < L; ++k) {
     if (k >= n) break;
     s = (uniform_value(prefix[k]) <= v) ? k : s;
   }

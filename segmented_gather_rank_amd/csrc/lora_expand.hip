@@ -232,7 +232,7 @@ struct XLds {
   int32_t tok[kTileRows];                         // the tile's tokens
 };
 
-template <int R>
+template <int R, int NS>
 __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t *__restrict__ info,
                                                                   const int32_t *__restrict__ tiles,
                                                                   ExpandParams p) {
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
   auto chunks = [&](int c) {
     int nk = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxSlices; ++k) {
+    for (int k = 0; k < NS; ++k) {
       if (k >= p.n_slices) break;
       nk += (uniform_value(p.steps[k]) + c - 1) / c;
     }
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     // chunk ck -> slice s and the chunk's first column in it
     int s = 0, cbase = 0, acc = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxSlices; ++k) {
+    for (int k = 0; k < NS; ++k) {
       if (k >= p.n_slices) break;
       if (ck >= acc) {
         s = k;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
       }
       acc += (uniform_value(p.steps[k]) + spi - 1) / spi;
     }
-    const int64_t w = pick(p.width, s, p.n_slices);
+    const int64_t w = pick<NS>(p.width, s, p.n_slices);
     const int64_t col0 = (int64_t)(ck - cbase) * cpi;
     const int ncols = (int)min((int64_t)cpi, w - col0);
     const int nb = (rows + 15) / 16;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     const int r = 16 * tbw + n;
     const bool rv = tbw < nb && r < rows;
     const int64_t t = rv ? (int64_t)(wpt == 4 ? hd.tk4 : (wpt == 2 ? hd.tk2 : hd.tk1)) : (int64_t)hd.tfirst;
-    const int64_t yo = pick(p.offset, s, p.n_slices) + col0;
+    const int64_t yo = pick<NS>(p.offset, s, p.n_slices) + col0;
     uint16_t *yrow = y + t * p.ldy + yo;
     // this lane's y octet of block pair pp in step i: columns
     // i * W + wq * cw + 32 pp + 8 kg (clamped to the first one when not ours)
@@ -367,8 +367,8 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     // (idx = tid + 256 q).  Loads past the slot block (rows >= R), past the
     // slot's rank or past the chunk read zeros without touching memory.
     const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
-    const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick(p.B, s, p.n_slices)) +
-                                    (int64_t)slot * pick(p.b_stride, s, p.n_slices),
+    const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick<NS>(p.B, s, p.n_slices)) +
+                                    (int64_t)slot * pick<NS>(p.b_stride, s, p.n_slices),
                                 (uint32_t)(R * w * 2));
     u32x4 bq[BQ];
     auto load_b = [&](int i) {
@@ -538,13 +538,19 @@ static hipError_t launch_t(const ExpandParams &p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int R, int NS>
+static hipError_t launch_mma_ns(const ExpandParams &p, int64_t bound, hipStream_t stream) {
+  static std::atomic<int> resident[kMaxDevices];
+  const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R, NS>),
+                                                   kXThreads, 0));
+  hipLaunchKernelGGL((expand_mma_kernel<R, NS>), dim3(grid), dim3(kXThreads), 0, stream, p.meta.info, p.meta.tiles,
+                     p);
+  return hipGetLastError();
+}
+
 template <int R>
 static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, hipStream_t stream) {
-  static std::atomic<int> resident[kMaxDevices];
-  const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R>),
-                                                   kXThreads, 0));
-  hipLaunchKernelGGL((expand_mma_kernel<R>), dim3(grid), dim3(kXThreads), 0, stream, p.meta.info, p.meta.tiles, p);
-  return hipGetLastError();
+  return with_slice_bound(p.n_slices, [&](auto ns) { return launch_mma_ns<R, decltype(ns)::value>(p, bound, stream); });
 }
 
 // Matrix-core expand: the bf16 path of SGMV and AUTO (tile heights follow the

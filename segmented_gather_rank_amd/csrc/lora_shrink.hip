@@ -209,7 +209,7 @@ template <int CB> constexpr int kMLda = CB == 1 ? 16 : CB * 16 + 16;
 // A tiles per batch at most (register and LDS budget)
 template <int CB> constexpr int kMNtb = CB == 1 ? 4 : (CB == 2 ? 2 : 1);
 
-template <int R, int CB>
+template <int R, int CB, int NS>
 __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t *__restrict__ info,
                                                                   const int32_t *__restrict__ tiles,
                                                                   ShrinkParams p) {
@@ -281,8 +281,8 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
 #pragma unroll
       for (int g = 0; g < SG; ++g) {
         const int sidx = s0 + (g < ns ? g : 0);
-        ar[g] = make_rsrc(reinterpret_cast<const uint16_t *>(pick(p.A, sidx, p.n_slices)) +
-                              (int64_t)slot * pick(p.a_stride, sidx, p.n_slices),
+        ar[g] = make_rsrc(reinterpret_cast<const uint16_t *>(pick<NS>(p.A, sidx, p.n_slices)) +
+                              (int64_t)slot * pick<NS>(p.a_stride, sidx, p.n_slices),
                           (uint32_t)(p.d_in * R * 2));
       }
       // A octet q = t * CB + sl * QS + qq of this thread: tile t of the
@@ -479,14 +479,20 @@ static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int R, int CB, int NS>
+static hipError_t launch_mma_ns(const ShrinkParams &p, int64_t bound, hipStream_t stream) {
+  static std::atomic<int> resident[kMaxDevices];
+  const int grid = xcd_grid(bound, resident_groups(resident,
+                                                   reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB, NS>),
+                                                   kMThreads, 0));
+  hipLaunchKernelGGL((shrink_mma_kernel<R, CB, NS>), dim3(grid), dim3(kMThreads), 0, stream, p.meta.info,
+                     p.meta.tiles, p);
+  return hipGetLastError();
+}
+
 template <int R, int CB>
 static hipError_t launch_mma_t(const ShrinkParams &p, int64_t bound, hipStream_t stream) {
-  static std::atomic<int> resident[kMaxDevices];
-  const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB>),
-                                                   kMThreads, 0));
-  hipLaunchKernelGGL((shrink_mma_kernel<R, CB>), dim3(grid), dim3(kMThreads), 0, stream, p.meta.info, p.meta.tiles,
-                     p);
-  return hipGetLastError();
+  return with_slice_bound(p.n_slices, [&](auto ns) { return launch_mma_ns<R, CB, decltype(ns)::value>(p, bound, stream); });
 }
 
 // column blocks per pass: the smallest power of two covering every slice's
