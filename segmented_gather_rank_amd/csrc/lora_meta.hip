@@ -86,13 +86,18 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
   return valid ? same : 0;
 }
 
-// SMALL: at most 1024 rows; thread tid holds row tid in registers throughout
-// (each wave's run below is then its own 64 rows), and the code for more rows
-// is left out.
-template <bool MOE, bool SMALL>
+// KIND 0 (kSmall): at most 1024 rows; thread tid holds row tid in registers
+// throughout (each wave's run below is then its own 64 rows).  KIND 1
+// (kCached): the keys of all rows are kept in LDS.  KIND 2 (kStreamed): rows
+// are read from memory again in each pass.  MLDS: the per-wave lane-mask tables fit in LDS (else keys are
+// matched with ballots).  Each instantiation carries only its own code: code
+// that runs once is fetched cold, so its size is time.
+constexpr int kSmall = 0, kCached = 1, kStreamed = 2;
+
+template <bool MOE, int KIND, bool MLDS>
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const int32_t *__restrict__ token_slot, const int32_t *__restrict__ topk_ids, int64_t T, MetaSrc src,
-    int32_t S, int32_t cached, int32_t match_lds,
+    int32_t S,
     int32_t *__restrict__ sorted, int32_t *__restrict__ sorted_slot,
     int32_t *__restrict__ seg_slot,
     int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
@@ -108,10 +113,10 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   typedef __attribute__((address_space(3))) int32_t lds_i32;
   lds_i32 *vcache = (lds_i32 *)(woff + kMetaWaves * K);
   const bool map_lds = MOE && src.expert_map && src.E_global <= kMetaMapLds;
-  int32_t *emap = map_lds ? woff + kMetaWaves * K + (cached ? T : 0) : nullptr;  // [E_global]
+  int32_t *emap = map_lds ? woff + kMetaWaves * K + (KIND == kCached ? T : 0) : nullptr;  // [E_global]
   // [16][K] per-wave lane masks of one group of rows, per key (8-byte aligned)
   uint64_t *masks = reinterpret_cast<uint64_t *>(
-      lds + ((3 + kMetaWaves) * K + (cached ? T : 0) + (map_lds ? src.E_global : 0) + 1) / 2 * 2);
+      lds + ((3 + kMetaWaves) * K + (KIND == kCached ? T : 0) + (map_lds ? src.E_global : 0) + 1) / 2 * 2);
   __shared__ int32_t nbad;
   __shared__ int32_t wsum[kMetaWaves][3];
 
@@ -124,39 +129,57 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   // raw inputs of one batch of rows, all loads issued before any is used
   int raw[kMetaBatch], rsl[kMetaBatch];
   auto load_raw = [&](int64_t b0) {
+    // MoE: the token of row t is t / topk, stepped along the batch's rows
+    // (rows < 2^31) instead of divided for each
+    uint32_t q = 0, r = 0, dq = 0, dr = 0;
+    if constexpr (MOE) {
+      const uint32_t t0 = (uint32_t)(b0 + tid), k = (uint32_t)src.topk;
+      q = t0 / k;
+      r = t0 - q * k;
+      dq = (uint32_t)kMetaThreads / k;
+      dr = (uint32_t)kMetaThreads - dq * k;
+    }
 #pragma unroll
-    for (int i = 0; i < kMetaBatch; ++i) {
+    for (int i = 0; i < (KIND == kSmall ? 1 : kMetaBatch); ++i) {
       const int64_t t = b0 + tid + (int64_t)kMetaThreads * i;
       if (t < T) {
         if constexpr (MOE) {
           raw[i] = topk_ids[t];
-          rsl[i] = token_slot[t / src.topk];
+          rsl[i] = token_slot[q];
         } else {
           raw[i] = token_slot[t];
+        }
+      }
+      if constexpr (MOE) {
+        q += dq;
+        r += dr;
+        if (r >= (uint32_t)src.topk) {
+          r -= (uint32_t)src.topk;
+          ++q;
         }
       }
     }
   };
   // the key of row t in [-2, S): from LDS when cached, else from memory
   auto value_at = [&](int64_t t) -> int {
-    if (cached) return vcache[(int)t];
-    if constexpr (MOE) return moe_key<MOE>(src, emap, topk_ids[t], token_slot[t / src.topk]);
+    if constexpr (KIND == kCached) return vcache[(int)t];
+    if constexpr (MOE) return moe_key<MOE>(src, emap, topk_ids[t], token_slot[(uint32_t)t / (uint32_t)src.topk]);
     return token_slot[t];
   };
 
   // 1. keys into LDS, in batches of up to 8 rows per thread (a batch's loads
   //    are all issued before any is used)
-  if (SMALL || cached) load_raw(0);
+  if (KIND == kSmall) load_raw(0);
   for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) woff[i] = 0;
-  if (match_lds)
+  if (MLDS)
     for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) masks[i] = 0;
   if (map_lds)
     for (int i = tid; i < src.E_global; i += kMetaThreads) emap[i] = src.expert_map[i];
   if (tid == 0) nbad = 0;
   __syncthreads();
-  if (!SMALL && cached) {
+  if constexpr (KIND == kCached) {
     for (int64_t b0 = 0; b0 < T; b0 += kMetaBatchRows) {
-      if (b0 > 0) load_raw(b0);
+      load_raw(b0);
 #pragma unroll
       for (int i = 0; i < kMetaBatch; ++i) {
         const int64_t t = b0 + tid + (int64_t)kMetaThreads * i;
@@ -178,21 +201,21 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   const int64_t w_lo = wave * per_w, w_hi = min(T, w_lo + per_w);
   uint64_t *wmask = masks + wave * K;
   int mybad = 0;
-  int pk_small = 0;  // SMALL: this thread's row, packed as in LDS
+  int pk_small = 0;  // kSmall: this thread's row, packed as in LDS
   for (int64_t b = w_lo; b < w_hi; b += kWave) {
     const int64_t t = b + lane;
     const bool valid = t < w_hi;
     int key = 0;
     if (valid) {
       int v;
-      if constexpr (SMALL) v = MOE ? moe_key<MOE>(src, emap, raw[0], rsl[0]) : raw[0];
+      if constexpr (KIND == kSmall) v = MOE ? moe_key<MOE>(src, emap, raw[0], rsl[0]) : raw[0];
       else v = value_at(t);
       const bool ok = v >= -1 && v < S;
       mybad += ok ? 0 : 1;
       key = ok ? v + 1 : 0;
     }
     uint64_t same;
-    if (match_lds) {
+    if constexpr (MLDS) {
       if (valid) atomicOr(reinterpret_cast<unsigned long long *>(&wmask[key]), 1ull << lane);
       same = valid ? wmask[key] : 0;
     } else {
@@ -201,11 +224,11 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const int rank = __popcll(same & lanemask_lt()), n = __popcll(same);
     if (valid && rank == 0) {
       woff[wave * K + key] += n;
-      if (match_lds) wmask[key] = 0;
+      if (MLDS) wmask[key] = 0;
     }
     const int pk = key | (rank << 10) | (n << 16);
-    if (SMALL) pk_small = pk;
-    else if (cached && valid) vcache[(int)t] = pk;
+    if (KIND == kSmall) pk_small = pk;
+    else if (KIND == kCached && valid) vcache[(int)t] = pk;
   }
   if (mybad) atomicAdd(&nbad, mybad);
   __syncthreads();
@@ -289,14 +312,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     const int64_t t = b + lane;
     const bool valid = t < w_hi;
     int key = 0, rank = 0, n = 0;
-    if (SMALL || cached) {
+    if constexpr (KIND != kStreamed) {
       if (valid) {
-        const int pk = SMALL ? pk_small : vcache[(int)t];
+        const int pk = KIND == kSmall ? pk_small : vcache[(int)t];
         key = pk & 1023;
         rank = (pk >> 10) & 63;
         n = pk >> 16;
       }
-    } else if constexpr (!SMALL) {
+    } else {
       if (valid) {
         const int v = value_at(t);
         key = (v >= -1 && v < S) ? v + 1 : 0;
@@ -339,22 +362,43 @@ static size_t meta_lds_bytes(int32_t S, int64_t T, int32_t E_map, bool &cached, 
   return b;
 }
 
-template <bool MOE, bool SMALL>
+template <bool MOE, int KIND, bool MLDS>
+static hipError_t launch_meta_k(const MetaSrc &src, int64_t T, int32_t S, size_t lds, int32_t *sorted,
+                                int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
+                                int32_t *info, int32_t *tiles, hipStream_t stream) {
+  if (lds > 65536) {
+    // more than the default 64 KB of dynamic LDS
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_kernel<MOE, KIND, MLDS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((meta_kernel<MOE, KIND, MLDS>), dim3(1), dim3(kMetaThreads), lds, stream, src.token_slot,
+                     src.topk_ids, T, src, S, sorted, sorted_slot, seg_slot, seg_count, seg_start,
+                     info, tiles);
+  return hipGetLastError();
+}
+
+template <bool MOE>
 static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_t *sorted,
                                 int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
                                 int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream) {
   bool cached = false, match_lds = false;
   const size_t lds = meta_lds_bytes(S, T, MOE && src.expert_map ? src.E_global : 0, cached, match_lds);
-  if (lds > 65536) {
-    // more than the default 64 KB of dynamic LDS
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_kernel<MOE, SMALL>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  const int kind = T <= kMetaThreads ? kSmall : (cached ? kCached : kStreamed);
+#define LORA_META_LAUNCH(K, M)                                                                                    \
+  return launch_meta_k<MOE, K, M>(src, T, S, lds, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, \
+                                  stream)
+  if (kind == kSmall) {
+    if (match_lds) LORA_META_LAUNCH(kSmall, true);
+    LORA_META_LAUNCH(kSmall, false);
   }
-  hipLaunchKernelGGL((meta_kernel<MOE, SMALL>), dim3(1), dim3(kMetaThreads), lds, stream, src.token_slot,
-                     src.topk_ids, T, src, S, (int32_t)cached,
-                     (int32_t)match_lds, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles);
-  return hipGetLastError();
+  if (kind == kCached) {
+    if (match_lds) LORA_META_LAUNCH(kCached, true);
+    LORA_META_LAUNCH(kCached, false);
+  }
+  if (match_lds) LORA_META_LAUNCH(kStreamed, true);
+  LORA_META_LAUNCH(kStreamed, false);
+#undef LORA_META_LAUNCH
 }
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
@@ -362,11 +406,7 @@ hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t 
                        int32_t *info, int32_t *tiles, hipStream_t stream) {
   MetaSrc src{};
   src.token_slot = token_slot;
-  if (T <= kMetaThreads)
-    return launch_meta_t<false, true>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles,
-                                      stream);
-  return launch_meta_t<false, false>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles,
-                                     stream);
+  return launch_meta_t<false>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, stream);
 }
 
 hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
@@ -381,11 +421,8 @@ hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, con
   src.S_adapters = S;
   src.E_global = E_global;
   src.E_local = E_local;
-  if (T * topk <= kMetaThreads)
-    return launch_meta_t<true, true>(src, T * topk, S * E_local, sorted, sorted_slot, seg_slot, seg_count,
-                                     seg_start, info, tiles, stream);
-  return launch_meta_t<true, false>(src, T * topk, S * E_local, sorted, sorted_slot, seg_slot, seg_count,
-                                    seg_start, info, tiles, stream);
+  return launch_meta_t<true>(src, T * topk, S * E_local, sorted, sorted_slot, seg_slot, seg_count, seg_start, info,
+                             tiles, stream);
 }
 
 }  // namespace lora
