@@ -47,6 +47,7 @@ struct ExpandParams {
   int32_t vec_cols;                   // columns per vector n-tile
   int32_t steps[kMaxSlices];          // matrix-core path: 128-column steps per slice
   int32_t steps_total;                // and over all slices
+  int32_t nck_tab[17];                // [c]: column chunks over all slices at c steps per item
   int32_t n_slices;
   void *y;
   int64_t ldy;
@@ -256,37 +257,37 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
   // steps on the busiest workgroup (the smallest on ties).  An item is (column
   // chunk of one slice, tile), chunk-major, so tiles that share a chunk of B
   // are neighbours, and XCD x (blockIdx mod 8) takes a contiguous run of items
-  const int avg_rows = (int)((T - nneg) / live);
+  const uint32_t live_u = (uint32_t)live;
+  const int avg_rows = (int)((uint32_t)(T - nneg) / live_u);  // rows < 2^31
   const int wide = avg_rows <= 16 ? 4 : (avg_rows <= 32 ? 2 : 1);
   const int spi_min = min(wide, 64 / RP);
-  const int per = gridDim.x / 8;
-  auto chunks = [&](int c) {
-    int nk = 0;
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      if (k >= p.n_slices) break;
-      nk += (uniform_value(p.steps[k]) + c - 1) / c;
-    }
-    return nk;
-  };
-  auto busiest = [&](int c, int nk) {  // steps on the busiest workgroup
-    const int64_t run_c = ((int64_t)live * nk + 7) / 8;
-    return ((run_c + per - 1) / per) * c;
-  };
-  const int spi0 = min(16, max(spi_min, (int)(((int64_t)live * p.steps_total + gridDim.x - 1) / gridDim.x)));
-  // lane l scores spi0 + l; the wave takes the lowest (cost, spi)
-  uint64_t score = ~0ull;
-  if (spi0 + lane <= 16) {
-    const int c = spi0 + lane;
-    score = ((uint64_t)busiest(c, chunks(c)) << 8) | (uint64_t)c;
+  const uint32_t per = gridDim.x / 8;
+  const int spi0 = min(16, max(spi_min, (int)((live_u * (uint32_t)p.steps_total + gridDim.x - 1) / gridDim.x)));
+  // lane l < 16 scores c = l + 1 steps per item (if c >= spi0): the steps on
+  // the busiest workgroup, ceil(ceil(live * chunks(c) / 8) / per) * c; the
+  // first row of lanes takes the lowest (cost, c) with DPP row rotations
+  uint32_t score = 0xffffffffu;
+  if (lane < 16 && lane + 1 >= spi0) {
+    const uint32_t c = (uint32_t)lane + 1;
+    const uint32_t run_c = (live_u * (uint32_t)pick<17>(p.nck_tab, (int)c) + 7) / 8;
+    const uint32_t cost = (run_c + per - 1) / per * c;
+    score = (cost < 0x7ffffffu ? cost : 0x7ffffffu) << 5 | c;
   }
+  auto row_min = [](uint32_t v, auto ctrl) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)v, decltype(ctrl)::value, 0xf, 0xf,
+                                                             false);
+    return o < v ? o : v;
+  };
+  score = row_min(score, std::integral_constant<int, 0x128>{});  // row_ror:8
+  score = row_min(score, std::integral_constant<int, 0x124>{});  // row_ror:4
+  score = row_min(score, std::integral_constant<int, 0x122>{});  // row_ror:2
+  score = row_min(score, std::integral_constant<int, 0x121>{});  // row_ror:1
+  const int spi = (int)(__builtin_amdgcn_readfirstlane(score) & 31);
+  const int nck = pick<17>(p.nck_tab, spi);
+  // column chunks per slice at spi steps per item, once per workgroup
+  int nk_s[NS];
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const uint64_t o = __shfl_xor(score, m, kWave);
-    score = o < score ? o : score;
-  }
-  const int spi = (int)uniform_value(score & 0xff);
-  const int nck = chunks(spi);
+  for (int k = 0; k < NS; ++k) nk_s[k] = k < p.n_slices ? (uniform_value(p.steps[k]) + spi - 1) / spi : 0;
   const int cpi = spi * kXStep;
   const int total = live * nck;
   const int run = (total + 7) / 8;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
         s = k;
         cbase = acc;
       }
-      acc += (uniform_value(p.steps[k]) + spi - 1) / spi;
+      acc += nk_s[k];
     }
     const int64_t w = pick<NS>(p.width, s, p.n_slices);
     const int64_t col0 = (int64_t)(ck - cbase) * cpi;
@@ -589,6 +590,11 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
     for (int s = 0; s < kMaxSlices; ++s) {
       p.steps[s] = s < n_slices ? (int32_t)((width[s] + kXStep - 1) / kXStep) : 0;
       p.steps_total += p.steps[s];
+    }
+    p.nck_tab[0] = 0;
+    for (int c = 1; c <= 16; ++c) {
+      p.nck_tab[c] = 0;
+      for (int s = 0; s < n_slices; ++s) p.nck_tab[c] += (p.steps[s] + c - 1) / c;
     }
     const int64_t bound = max_tiles(T, (int32_t)S) * p.steps_total;
     switch (R) {
