@@ -103,7 +103,10 @@ template <> struct AOct<float> {
 // case carries none of the extra registers).
 // The sorted order and T come first among the arguments, so that they are
 // preloaded into scalar registers and the first loads need no argument fetch.
-template <typename E, int R, bool RK, int NS>
+// ONE: one slice, one batch of A loads per thread, at most one output octet
+// per lane group and one batch of B rows (the common decode shape): the code
+// for the next batches is left out.
+template <typename E, int R, bool RK, int NS, bool ONE>
 __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__restrict__ sorted,
                                                                const int32_t *__restrict__ sorted_slot,
                                                                int64_t T, BgmvParams p) {
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
                                 a_bytes);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int bb = 0; bb < p.n_inst; bb += NA) {
-      if (s > 0 || bb > 0) {
+      if (!ONE && (s > 0 || bb > 0)) {
 #pragma unroll
         for (int q = 0; q < NA; ++q)
           a[q].load(ar, a_live ? (uint32_t)((((bb + q) * RB + rr) * R + 8 * jo) * sizeof(E)) : 0x7FFFFFF0u);
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
     int s = s0;
     int64_t n0 = n00, w = w0, yoff = yoff0;
     const E *Bb = Bb0;  // rank row 0 of this octet's columns
-    if (it > 0) {
+    if (!ONE && it > 0) {
       s = slice_of_oct<NS>(p, o);
       n0 = 8 * (int64_t)(o - pick<NS + 1>(p.oct_base, s, p.n_slices));
       w = pick<NS>(p.width, s, p.n_slices);
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kBThreads) void bgmv_fused_kernel(const int32_t *__
     }
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int jb = 0; jb < rj; jb += NB) {
-      if (it > 0 || jb > 0) {
+      if (!ONE && (it > 0 || jb > 0)) {
 #pragma unroll
         for (int jj = 0; jj < NB; ++jj) {
           const int jc = jb + (jj < span ? jj : span - 1);
@@ -400,18 +403,25 @@ bool bgmv_fits(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64
   return mode == 1 || T <= 16 * (int64_t)S;  // BGMV requested, or few tokens per slot
 }
 
+template <typename E, int R, int NS, bool ONE>
+static hipError_t launch_k(const BgmvParams &p, int grid, size_t lds, hipStream_t stream) {
+  if (p.slot_rank)
+    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true, NS, ONE>), dim3(grid), dim3(kBThreads), lds, stream,
+                       p.meta.sorted, p.meta.sorted_slot, p.meta.T, p);
+  else
+    hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false, NS, ONE>), dim3(grid), dim3(kBThreads), lds, stream,
+                       p.meta.sorted, p.meta.sorted_slot, p.meta.T, p);
+  return hipGetLastError();
+}
+
 template <typename E, int R>
 static hipError_t launch_t(const BgmvParams &p, int grid, size_t lds, hipStream_t stream) {
-  return with_slice_bound(p.n_slices, [&](auto ns) {
-    constexpr int NS = decltype(ns)::value;
-    if (p.slot_rank)
-      hipLaunchKernelGGL((bgmv_fused_kernel<E, R, true, NS>), dim3(grid), dim3(kBThreads), lds, stream,
-                         p.meta.sorted, p.meta.sorted_slot, p.meta.T, p);
-    else
-      hipLaunchKernelGGL((bgmv_fused_kernel<E, R, false, NS>), dim3(grid), dim3(kBThreads), lds, stream,
-                         p.meta.sorted, p.meta.sorted_slot, p.meta.T, p);
-    return hipGetLastError();
-  });
+  // one batch of everything: A rows (n_inst <= NA), the lane groups' octets
+  // (n_oct <= threads / jg) and their rank rows (R / jg <= NB)
+  const bool one = p.n_slices == 1 && p.n_inst <= kBNA<E> && p.oct_base[1] * p.jg <= kBThreads &&
+                   R / p.jg <= kBNB<E>;
+  if (one) return launch_k<E, R, 1, true>(p, grid, lds, stream);
+  return with_slice_bound(p.n_slices, [&](auto ns) { return launch_k<E, R, decltype(ns)::value, false>(p, grid, lds, stream); });
 }
 
 hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
