@@ -62,6 +62,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 KERNEL_SOURCES = {   # the sources each measured kernel is built from
+    "bgmv_split": ["lora_bgmv_split.hip"],
     "bgmv_fused_kernel": ["lora_bgmv.hip"],
     "shrink+expand": ["lora_shrink.hip", "lora_expand.hip"],
 }
@@ -114,8 +115,29 @@ def dominant_kernel(c, mode):
     fused = (os.environ.get("LORA_DISABLE_FUSED_BGMV", "0") in ("", "0") and mode != "sgmv" and sw // 8 <= 1024 and c.d_in * e <= 32768 and w_tok <= (1 << 20)
              and (mode == "bgmv" or c.T <= 16 * c.num_slots))
     if fused:
-        return "bgmv_fused_kernel"
+        return "bgmv_split" if split_takes(c) else "bgmv_fused_kernel"
     return "shrink+expand"
+
+
+def split_takes(c):
+    """Whether a decode-shaped call runs the split kernel (each work tile spread
+    over several workgroups): bf16, and some member count of at most 16 gives
+    every member an A chunk (<= 512 rows) and a B share that fit its LDS."""
+    if c.dtype != "bf16" or os.environ.get("LORA_DISABLE_SPLIT_BGMV", "0") not in ("", "0"):
+        return False
+    rp = max(16, c.r_max)
+    nsb = 1 << (c.n_slices - 1).bit_length()
+    if nsb * (rp // 16) > 8 or c.T * c.n_slices * rp > (1 << 17):
+        return False
+    nbt = sum((w + 15) // 16 for w in c.widths)
+    g = 1
+    while g <= 16:
+        kc = max(128, 1 << max(0, (-(-c.d_in // g) - 1).bit_length()))
+        bpm = -(-nbt // g)
+        if kc <= 512 and c.n_slices * kc * (rp // 8) <= 2048 and bpm <= 32 and bpm * 2 * rp <= 2048:
+            return True
+        g *= 2
+    return False
 
 
 def kernel_keys(kernel_key):

@@ -88,9 +88,17 @@ typedef struct lora_weight {
  *                   unspecified).  Tiles follow the order of `sorted`; there
  *                   are num_tiles <= ceil(T / 64) + S + 1 of them.  The compute
  *                   kernels take their work from this list.
+ *   sync            16 uint32 per possible tile, then 16 more: rendezvous
+ *                   flags of the decode-shaped lora_apply (below), set to 0
+ *                   here; the word after the tiles' flags counts waits that
+ *                   gave up (0 unless a workgroup waited for its peers past the
+ *                   spin limit)
  * The struct stays valid until its workspace is reused; rebuild it whenever
- * token_slot changes.  Pass it by pointer to the compute calls; they only read
- * it, so any number of them may use one lora_meta at the same time. */
+ * token_slot changes.  Pass it by pointer to the compute calls.  lora_shrink
+ * and lora_expand only read it, so any number of them may use one lora_meta at
+ * the same time; lora_apply counts its rendezvous in `sync`, so lora_apply
+ * calls that share one lora_meta must run one after another (one stream, or
+ * ordered by events). */
 typedef struct lora_meta {
     int64_t num_tokens;             /* rows of the batch */
     int32_t num_slots;              /* keys: slots, or (slot, local expert) pairs */
@@ -103,6 +111,7 @@ typedef struct lora_meta {
     int32_t *seg_start;
     int32_t *info;
     int32_t *tiles;
+    uint32_t *sync;
 } lora_meta;
 
 /* Bytes of device workspace lora_prepare_meta needs for T tokens and S slots. */

@@ -46,7 +46,8 @@ class lora_meta(C.Structure):
     _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("x_row_div", C.c_int32),
                 ("sorted", C.c_void_p), ("sorted_slot", C.c_void_p), ("seg_slot", C.c_void_p),
                 ("seg_count", C.c_void_p),
-                ("seg_start", C.c_void_p), ("info", C.c_void_p), ("tiles", C.c_void_p)]
+                ("seg_start", C.c_void_p), ("info", C.c_void_p), ("tiles", C.c_void_p),
+                ("sync", C.c_void_p)]
 
 
 _p, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
@@ -94,7 +95,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 4:
+if _lib.lora_abi_version() != 5:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -147,6 +148,7 @@ def _weights(ws, name: str, inner_shape_ok) -> tuple:
 
 
 TILE_ROWS = 64          # sorted positions per work tile of the metadata
+SPLIT_MEMBERS = 16  # rendezvous flag words per work tile
 TILE_INTS = 4 + TILE_ROWS
 
 
@@ -191,7 +193,14 @@ class LoraMeta:
                     seg_slot=self._view(self.c.seg_slot, S + 1),
                     seg_count=self._view(self.c.seg_count, S + 1),
                     seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 8),
-                    tiles=self._view(self.c.tiles, TILE_INTS * max_tiles(T, S)).view(-1, TILE_INTS))
+                    tiles=self._view(self.c.tiles, TILE_INTS * max_tiles(T, S)).view(-1, TILE_INTS),
+                    sync=self._view(self.c.sync, SPLIT_MEMBERS * (max_tiles(T, S) + 1)))
+
+    def split_wait_timeouts(self) -> int:
+        """Waits of the split decode kernel that gave up (0 in normal runs).
+        Synchronises with the device."""
+        T, S = self.num_tokens, self.num_slots
+        return int(self._view(self.c.sync, SPLIT_MEMBERS * (max_tiles(T, S) + 1))[SPLIT_MEMBERS * max_tiles(T, S)].item())
 
 
 def lora_meta_workspace_bytes(num_tokens: int, num_slots: int) -> int:

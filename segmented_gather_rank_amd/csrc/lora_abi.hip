@@ -21,6 +21,18 @@ bool fused_disabled() {
   static const bool v = env_int("LORA_DISABLE_FUSED_BGMV", 0) > 0;
   return v;
 }
+// LORA_DISABLE_SPLIT_BGMV=1 keeps decode-shaped bf16 calls on the one-workgroup-
+// per-token fused kernel.
+bool split_disabled() {
+  static const bool v = env_int("LORA_DISABLE_SPLIT_BGMV", 0) > 0;
+  return v;
+}
+// Polls a workgroup of the split kernel makes while waiting for its peers
+// before it gives up (LORA_SPLIT_SPIN_LIMIT): about a microsecond each.
+int split_spin_limit() {
+  static const int v = env_int("LORA_SPLIT_SPIN_LIMIT", 1 << 22);
+  return v;
+}
 
 }  // namespace lora
 
@@ -31,7 +43,7 @@ namespace {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -42,7 +54,7 @@ bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV ||
 size_t esize(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
 
 struct MetaLayout {
-  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, total;
+  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, sync, total;
 };
 MetaLayout meta_layout(int64_t T, int32_t S) {
   MetaLayout L{};
@@ -61,6 +73,8 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
   off += align256(sizeof(int32_t) * 8);
   L.tiles = off;
   off += align256(sizeof(int32_t) * kTileInts * (size_t)max_tiles(T, S));
+  L.sync = off;
+  off += align256(sizeof(uint32_t) * (size_t)sync_words(T, S));
   L.total = off;
   return L;
 }
@@ -69,7 +83,7 @@ lora_status check_meta(const lora_meta *m) {
   if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots || m->x_row_div < 1)
     return LORA_ERR_INVALID_ARG;
   if (!m->sorted || !m->sorted_slot || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info ||
-      !m->tiles)
+      !m->tiles || !m->sync)
     return LORA_ERR_INVALID_ARG;
   return LORA_OK;
 }
@@ -83,6 +97,7 @@ MetaView view_of(const lora_meta *m) {
   v.seg_start = m->seg_start;
   v.info = m->info;
   v.tiles = m->tiles;
+  v.sync = m->sync;
   v.T = m->num_tokens;
   v.S = m->num_slots;
   v.x_row_div = m->x_row_div;
@@ -182,6 +197,7 @@ static void place_meta(lora_meta *out, void *d_ws, const MetaLayout &L, int64_t 
   out->seg_start = reinterpret_cast<int32_t *>(base + L.seg_start);
   out->info = reinterpret_cast<int32_t *>(base + L.info);
   out->tiles = reinterpret_cast<int32_t *>(base + L.tiles);
+  out->sync = reinterpret_cast<uint32_t *>(base + L.sync);
 }
 
 lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S, void *d_ws,
@@ -194,7 +210,7 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
   if (ws_bytes < L.total) return LORA_ERR_WORKSPACE;
   place_meta(out, d_ws, L, T, S);
   const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->sorted_slot, out->seg_slot,
-                                   out->seg_count, out->seg_start, out->info, out->tiles,
+                                   out->seg_count, out->seg_start, out->info, out->tiles, out->sync,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -226,7 +242,8 @@ lora_status lora_prepare_moe_meta(const int32_t *d_topk_ids, int64_t T, int32_t 
   place_meta(out, d_ws, meta_layout(n, S * E_local), n, S * E_local);
   const hipError_t e = launch_meta_moe(d_topk_ids, T, topk, d_token_slot, S, E_global, E_local, d_expert_map,
                                        out->sorted, out->sorted_slot, out->seg_slot, out->seg_count,
-                                       out->seg_start, out->info, out->tiles, static_cast<hipStream_t>(stream));
+                                       out->seg_start, out->info, out->tiles, out->sync,
+                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return LORA_ERR_HIP;
   out->x_row_div = topk;
   return LORA_OK;
@@ -291,6 +308,8 @@ lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32
   size_t sh = 0;
   const lora_status st = lora_shrink_workspace_bytes(T, S, d_in, n_slices, r_max, dtype, mode, &sh);
   if (st != LORA_OK) return st;
+  // the split decode kernel's partial rank rows share the shrink's region
+  if (dtype == LORA_BF16 && mode != LORA_MODE_SGMV) sh = std::max(sh, split_ws_bytes(T, S, n_slices, r_max));
   *bytes = align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max) + sh;
   return LORA_OK;
 }
@@ -325,6 +344,14 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
                                      r_max, ldy, dtype == LORA_BF16, (int)mode)) {
+    if (dtype == LORA_BF16 && !split_disabled()) {
+      bool used = false;
+      const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
+                                             r_max, scale, d_slot_scale, d_slot_rank, d_y, ldy, add_into_y,
+                                             static_cast<float *>(sh_ws), ws_bytes - ubytes, s, &used);
+      if (e != hipSuccess) return LORA_ERR_HIP;
+      if (used) return LORA_OK;
+    }
     const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
                                      bptr, bstr, width, offset, r_max, scale, d_slot_scale,
                                      d_slot_rank, d_y, ldy, add_into_y, s);

@@ -244,6 +244,7 @@ struct MetaView {
   const int32_t *seg_start;
   const int32_t *info;   // num_segments, no_lora, num_bad, lora_begin, num_tiles
   const int32_t *tiles;  // kTileInts int32 per tile: slot, rows, pos0, 0, tokens[kTileRows]
+  uint32_t *sync;        // rendezvous flags of the split decode kernel
   int64_t T;
   int32_t S;
   int32_t x_row_div;     // batch row i reads x row i / x_row_div
@@ -355,6 +356,18 @@ __device__ __forceinline__ bf16x8 lds_col8(const uint16_t *tile, int ld, int row
       __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a + 4 * ld)));
   const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
   return __builtin_bit_cast(bf16x8, w);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A operand of v_mfma_f32_16x16x16_bf16 from a row-major bf16 tile in LDS:
+// lane i of each 16-lane group receives tile[row0 + e][col0 + i], e = 0..3,
+// where row0 is this lane's group's first row.
+__device__ __forceinline__ s16x4 lds_col4(const uint16_t *tile, int ld, int row0, int col0) {
+  const int l = threadIdx.x % 16;
+  const uint16_t *a = tile + (row0 + l / 4) * ld + col0 + 4 * (l % 4);
+  typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+  return __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a)));
 }
 
 // ---------------------------------------------------------------- DPP helpers

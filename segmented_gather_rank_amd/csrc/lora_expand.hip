@@ -212,18 +212,6 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
 constexpr int kXThreads = 256;
 constexpr int kXStep = 128;          // columns per step (the narrowest step)
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// A operand of v_mfma_f32_16x16x16_bf16 from a row-major bf16 tile in LDS:
-// lane i of each 16-lane group receives tile[row0 + e][col0 + i], e = 0..3,
-// where row0 is this lane's group's first row.
-__device__ __forceinline__ s16x4 lds_col4(const uint16_t *tile, int ld, int row0, int col0) {
-  const int l = threadIdx.x % 16;
-  const uint16_t *a = tile + (row0 + l / 4) * ld + col0 + 4 * (l % 4);
-  typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
-  return __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a)));
-}
-
 template <int R>
 struct XLds {
   static constexpr int RP = R < 16 ? 16 : R;  // ranks padded to whole 16-wide steps

@@ -53,15 +53,21 @@ struct ShrinkConfig {
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);
 size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32_t R);
 
+// Rendezvous flags of the split decode kernel: kSplitMembers words per work
+// tile, then one row whose first word counts waits that gave up.
+constexpr int kSplitMembers = 16;
+inline int64_t sync_words(int64_t T, int32_t S) { return kSplitMembers * (max_tiles(T, S) + 1); }
+
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
-                       int32_t *info, int32_t *tiles, hipStream_t stream);
+                       int32_t *info, int32_t *tiles, uint32_t *sync, hipStream_t stream);
 // the same over the T * topk (token, choice) pairs of a top-k routing step,
 // keyed by (slot, local expert): S * E_local keys
 hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
                            int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
                            int32_t *sorted, int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
-                           int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream);
+                           int32_t *seg_start, int32_t *info, int32_t *tiles, uint32_t *sync,
+                           hipStream_t stream);
 
 // for_apply: u is written in sorted-position order, and with a split d_in the
 // partial sums are left in ws for the expand to add (kch_out reports the split)
@@ -86,5 +92,17 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
                        const int64_t *offset, int32_t R, float scale, const float *slot_scale,
                        const int32_t *slot_rank, void *y, int64_t ldy, int add, hipStream_t stream);
 bool fused_disabled();
+
+// The fused kernel with each work tile split over several workgroups (bf16,
+// decode-shaped calls).  part: workspace of split_ws_bytes bytes for the
+// partial rank rows.  *used is false when the call is not one it takes.
+size_t split_ws_bytes(int64_t T, int32_t S, int32_t n_slices, int32_t R);
+hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, int32_t n_slices,
+                             const void *const *A, const int64_t *a_stride, const void *const *B,
+                             const int64_t *b_stride, const int64_t *width, const int64_t *offset, int32_t R,
+                             float scale, const float *slot_scale, const int32_t *slot_rank, void *y, int64_t ldy,
+                             int add, float *part, size_t part_bytes, hipStream_t stream, bool *used);
+bool split_disabled();
+int split_spin_limit();
 
 }  // namespace lora

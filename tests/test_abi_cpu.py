@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 4
+    assert L.lora_abi_version() == 5
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -72,7 +72,7 @@ def test_meta_rejections():
 def _meta(T=16, S=4):
     m = L.lora_meta()
     m.num_tokens, m.num_slots, m.x_row_div = T, S, 1
-    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info", "tiles"):
+    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info", "tiles", "sync"):
         setattr(m, f, _base)
     return m
 

@@ -1,0 +1,172 @@
+"""The split decode kernel: each work tile of a decode-shaped bf16 lora_apply
+spread over G workgroups that exchange partial rank rows through memory and
+meet at per-tile flag words (page "多 LoRA 服务：分段矩阵乘与适配器调度", section
+"不合并权重，批量计算": the fused gather-and-multiply form for decode).  Results
+against the oracle's fp64 rows; the flags show that the split path ran, that
+every call raised each word of each live tile once, and that no wait gave up."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import TOL, DevCase, check_rows, from_dev, oracle_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MEMBERS = 16
+
+
+@pytest.fixture(scope="module")
+def L():
+    import segmented_gather_rank_amd as lib
+    return lib
+
+
+def decode_case(seed, r, S=32, T=256, d_in=1024, widths=(512, 256, 136), none_frac=0.1, ranks=None):
+    """One token per request, slots drawn uniformly, some tokens without an
+    adapter; the last slice is 8.5 column blocks wide (a ragged block)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    req = rng.integers(0, S, T).astype(np.int32)
+    req[rng.random(T) < none_frac] = -1
+    widths = list(widths)
+    c = W.make_case(name=f"split_r{r}_s{seed}", seed=seed, rng=rng, dtype="bf16", lengths=np.ones(T, np.int64),
+                    req_slot=req, num_slots=S, d_in=d_in, r_max=r, widths=widths, scale=0.5, ranks=ranks,
+                    weight_sd=0.05)
+    c.slot_scale = rng.choice(np.array([0.5, 1.0, 2.0], np.float32), S)
+    return c
+
+
+def live_tiles(meta):
+    """Tile indices with an adapter, and all tile indices, from the metadata."""
+    t = {k: v.cpu().numpy() for k, v in meta.tensors().items()}
+    n = int(t["info"][4])
+    slots = t["tiles"][:n, 0]
+    return np.where(slots >= 0)[0], n
+
+
+def tile_flags(meta):
+    return meta.tensors()["sync"].cpu().numpy().view(np.uint32).reshape(-1, MEMBERS)
+
+
+def check_flags(meta, calls):
+    """Every word of a live tile equals the number of split calls; the others
+    were never touched; no wait gave up."""
+    f = tile_flags(meta)
+    live, n = live_tiles(meta)
+    assert (f[live] == calls).all(), f[live]
+    dead = np.setdiff1d(np.arange(f.shape[0] - 1), live)
+    assert (f[dead] == 0).all()
+    assert meta.split_wait_timeouts() == 0
+
+
+@pytest.mark.parametrize("r", [8, 16, 32, 64])
+@pytest.mark.parametrize("add", [True, False])
+def test_split_decode_parity(L, r, add):
+    # rank 64 takes at most two slices on this path (LDS of the rank rows)
+    c = decode_case(500 + r, r, widths=(512, 136) if r == 64 else (512, 256, 136))
+    print(f"[split] {c.name} T={c.T} S={c.num_slots} add={add}", flush=True)
+    d = DevCase(c)
+    y, meta = d.apply(L, mode="auto", add=add)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), c.name)
+    check_flags(meta, 1)
+
+
+def test_split_rank64_three_slices_falls_back(L):
+    """Three slices at rank 64 do not fit the split kernel's LDS: the call runs
+    on the one-workgroup-per-token kernel (flags untouched) and is still right."""
+    c = decode_case(505, 64)
+    d = DevCase(c)
+    y, meta = d.apply(L)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
+    assert (tile_flags(meta) == 0).all()
+
+
+def test_split_calls_share_one_meta(L):
+    """Calls of different shapes (so different member counts and chunks) on
+    one metadata struct, interleaved and repeated: each is right, and the
+    flags stay equal across a tile's words."""
+    S, T = 32, 256
+    shapes = [dict(d_in=1024, widths=(512, 256, 136), r=16), dict(d_in=4096, widths=(4096,), r=16),
+              dict(d_in=512, widths=(1024, 1024), r=32), dict(d_in=2048, widths=(8,), r=8)]
+    cases = []
+    base = decode_case(600, 16, S=S, T=T)
+    for i, sh in enumerate(shapes):
+        c = decode_case(600, sh["r"], S=S, T=T, d_in=sh["d_in"], widths=sh["widths"])
+        assert np.array_equal(c.token_slot, base.token_slot)
+        cases.append((c, DevCase(c)))
+    meta = L.lora_prepare_meta(cases[0][1].token_slot, S)
+    calls = 0
+    for rep in range(2):
+        for c, d in cases:
+            print(f"[split-share] rep {rep} {c.name} d_in={c.d_in} widths={c.widths}", flush=True)
+            y, _ = d.apply(L, mode="auto", meta=meta)
+            calls += 1
+            check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), f"{c.name} rep {rep}")
+    f = tile_flags(meta)
+    live, _ = live_tiles(meta)
+    assert (f[live] == f[live][:, :1]).all()
+    assert (f[live] >= 1).all()
+    assert meta.split_wait_timeouts() == 0
+
+
+def test_split_large_tiles(L):
+    """Segments of 17..64 tokens (2..4 token blocks per tile) and longer ones
+    cut into several tiles; BGMV mode keeps them on the fused path."""
+    rng = np.random.Generator(np.random.PCG64(610))
+    lengths = np.array([17, 33, 64, 65, 130, 1, 1, 48, 20], np.int64)
+    req = np.array([0, 1, 2, 3, 4, 5, -1, 6, 7], np.int32)
+    c = W.make_case(name="split_big_tiles", seed=610, rng=rng, dtype="bf16", lengths=lengths, req_slot=req,
+                    num_slots=8, d_in=768, r_max=16, widths=[384, 200], scale=1.0, weight_sd=0.05)
+    d = DevCase(c)
+    for add in (True, False):
+        y, meta = d.apply(L, mode="bgmv", add=add)
+        check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
+        check_flags(meta, 1)
+
+
+@pytest.mark.parametrize("add", [True, False])
+def test_split_slot_ranks(L, add):
+    """Per-slot ranks, one of them 0: that slot's rows are left as they are
+    (add) or cleared (store)."""
+    S = 16
+    rng = np.random.Generator(np.random.PCG64(620))
+    ranks = rng.choice(np.array([0, 8, 16, 24, 32], np.int32), S)
+    ranks[3] = 0
+    c = decode_case(620, 32, S=S, T=128, ranks=ranks)
+    d = DevCase(c)
+    y = d.y0.clone()
+    meta = L.lora_prepare_meta(d.token_slot, S)
+    L.lora_apply(meta, d.x, d.A, d.B, c.offsets, y, scale=c.scale, slot_scale=d.slot_scale, add=add,
+                 slot_rank=torch.from_numpy(ranks).cuda())
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), c.name)
+    assert meta.split_wait_timeouts() == 0
+
+
+def test_split_graph_replays(L):
+    """Metadata and apply captured in one HIP graph: every replay, with eager
+    work between them, gives the eager result bit for bit."""
+    c = decode_case(630, 16)
+    d = DevCase(c)
+    y_eager, _ = d.apply(L)
+    torch.cuda.synchronize()
+    y = d.y0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside the capture (workspace allocations)
+        meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+        ws = torch.empty(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, len(c.widths), c.r_max,
+                                                      torch.bfloat16), dtype=torch.uint8, device="cuda")
+    torch.cuda.current_stream().wait_stream(s)
+    meta_ws = meta.workspace
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m = L.lora_prepare_meta(d.token_slot, c.num_slots, workspace=meta_ws)
+        y.copy_(d.y0)
+        L.lora_apply(m, d.x, d.A, d.B, c.offsets, y, scale=c.scale, slot_scale=d.slot_scale, workspace=ws)
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i}"
+        d.apply(L)  # eager work between replays
+        torch.cuda.synchronize()
+    assert m.split_wait_timeouts() == 0
