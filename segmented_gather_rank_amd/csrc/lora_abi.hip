@@ -33,6 +33,15 @@ int split_spin_limit() {
   static const int v = env_int("LORA_SPLIT_SPIN_LIMIT", 1 << 22);
   return v;
 }
+// LORA_SPLIT_MEMBERS=n (1, 2, 4, 8 or 16): workgroups per tile of the split
+// kernel, instead of the count chosen from the batch (tuning).
+int split_members() {
+  static const int v = [] {
+    const int m = env_int("LORA_SPLIT_MEMBERS", 0);
+    return (m == 1 || m == 2 || m == 4 || m == 8 || m == 16) ? m : 0;
+  }();
+  return v;
+}
 
 }  // namespace lora
 

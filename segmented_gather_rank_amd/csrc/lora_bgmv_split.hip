@@ -530,21 +530,24 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 1024 + lane * 16);
   const uint32_t plane = (uint32_t)(p.n_frag * RB * 1024);  // between members
   if (xw) {
-    f32x4 acc[RB];
+    // two accumulator chains (even and odd k-steps), added at the end: the
+    // MFMAs of one chain wait for each other, the two chains do not
+    f32x4 acc[2][RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) acc[0][rb] = acc[1][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kleft = p.d_in - k0 - 8 * kg;  // x values of this lane past d_in are dropped
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       const u32x4 xv = p.x_full || 32 * i < kleft ? xa[i] : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_col8(As, LDA, 32 * i + 8 * kg, 16 * rb),
-                                                          __builtin_bit_cast(bf16x8, xv), acc[rb], 0, 0, 0);
+        acc[i & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_col8(As, LDA, 32 * i + 8 * kg, 16 * rb),
+                                                                 __builtin_bit_cast(bf16x8, xv), acc[i & 1][rb], 0, 0, 0);
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      __builtin_amdgcn_raw_buffer_store_b128(acc[rb], pr, fbase + g * plane + (wave * RB + rb) * 1024, 0, 16);
+      __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr, fbase + g * plane + (wave * RB + rb) * 1024,
+                                             0, 16);
   }
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
 #pragma unroll
@@ -567,6 +570,14 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   // ---- expand, token block by token block: u = scale * (members' partials
   // in member order) as bf16 hi + lo operands; every column block of this
   // wave (a block past the member's share reads block 0 and stores nothing)
+  // B^T operands first: their LDS reads overlap the gather's loads
+  s16x4 bw[QB][RB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int lb = wave + 4 * q < nbm ? wave + 4 * q : 0;
+#pragma unroll
+    for (int c = 0; c < RB; ++c) bw[q][c] = lds_col4(Bs, p.ldb, 16 * c + 4 * kg, 16 * lb);
+  }
   for (int t = 0; t < nb; ++t) {
     s16x4 uh[RB], ul[RB];
 #pragma unroll
@@ -587,13 +598,6 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
     }
     const bool rok = 16 * t + l16 < rows;
-    s16x4 bw[QB][RB];
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      const int lb = wave + 4 * q < nbm ? wave + 4 * q : 0;
-#pragma unroll
-      for (int c = 0; c < RB; ++c) bw[q][c] = lds_col4(Bs, p.ldb, 16 * c + 4 * kg, 16 * lb);
-    }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -644,6 +648,7 @@ size_t split_ws_bytes(int64_t T, int32_t S, int32_t n_slices, int32_t R) {
 }
 
 static std::atomic<int> g_split_resident[4][4][kMaxDevices];
+int split_members();
 
 int split_spin_limit();
 
@@ -685,6 +690,7 @@ static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices
   const int64_t est = std::min<int64_t>(mt, T);  // live tiles, at most
   int G = 1;
   while (G < kSplitMembers && G < g_cap && 2 * G * est <= 384) G *= 2;
+  if (split_members() > 0) G = std::min(split_members(), g_cap);  // tuning override
   for (;; G *= 2) {
     if (G > kSplitMembers || G > g_cap) return pl;
     const int64_t kc = std::max<int64_t>(128, (int64_t)1 << ilog2((d_in + G - 1) / G));
