@@ -91,8 +91,9 @@ typedef struct lora_weight {
  *   sync            16 uint32 per possible tile, then 16 more: rendezvous
  *                   flags of the decode-shaped lora_apply (below), set to 0
  *                   here; the word after the tiles' flags counts waits that
- *                   gave up (0 unless a workgroup waited for its peers past the
- *                   spin limit)
+ *                   gave up (a workgroup that waited for its peers past the
+ *                   spin limit computed their share itself: the result is the
+ *                   same, only slower)
  * The struct stays valid until its workspace is reused; rebuild it whenever
  * token_slot changes.  Pass it by pointer to the compute calls.  lora_shrink
  * and lora_expand only read it, so any number of them may use one lora_meta at

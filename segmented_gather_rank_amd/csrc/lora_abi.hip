@@ -28,9 +28,13 @@ bool split_disabled() {
   return v;
 }
 // Polls a workgroup of the split kernel makes while waiting for its peers
-// before it gives up (LORA_SPLIT_SPIN_LIMIT): about a microsecond each.
+// before it computes the missing members' partials itself
+// (LORA_SPLIT_SPIN_LIMIT, 0 allowed): about a microsecond each.
 int split_spin_limit() {
-  static const int v = env_int("LORA_SPLIT_SPIN_LIMIT", 1 << 22);
+  static const int v = [] {
+    const char *e = std::getenv("LORA_SPLIT_SPIN_LIMIT");
+    return e && *e ? std::max(0, std::atoi(e)) : 4096;
+  }();
   return v;
 }
 // LORA_SPLIT_MEMBERS=n (1, 2, 4, 8 or 16): workgroups per tile of the split

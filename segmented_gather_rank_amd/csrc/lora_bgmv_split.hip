@@ -29,10 +29,13 @@
 // 16 words exactly once (member 0 also raises the words of members >= G), so
 // they stay equal between calls and a member waits for "my value + 1".  The
 // loads of B and y are issued before the wait.  The wait is bounded: a
-// workgroup that gives up counts itself in the word after the flags.
+// workgroup that gives up counts itself in the word after the flags and
+// computes the missing members' partials itself, with the same code (so the
+// same bits), storing them into those members' slots.  The result never
+// depends on the members being resident together; the grid is kept within the
+// workgroups the device holds at once so that they normally are.
 //
-// Only bf16.  The grid never exceeds the workgroups the device holds at once,
-// so every member of a tile is resident while the others wait for it.
+// Only bf16.
 #include "lora_host.h"
 
 namespace lora {
@@ -90,18 +93,22 @@ __device__ __forceinline__ void split_zero(const SplitParams &p, const int32_t *
 
 // Raise this member's flag word of the tile (member 0 also those of members
 // >= G) to f + 1, then wait until the G members' words reach it: one wave,
-// at most spin_limit polls (a wait that gives up counts itself in *err).
-__device__ __forceinline__ void split_wait(uint32_t *fl, uint32_t f, int g, int G, int spin_limit, uint32_t *err) {
+// at most spin_limit polls.  Returns the members whose words were still low
+// when it gave up (bit g'), 0 when all arrived; a wait that gives up counts
+// itself in *err.
+__device__ __forceinline__ uint32_t split_wait(uint32_t *fl, uint32_t f, int g, int G, int spin_limit,
+                                               uint32_t *err) {
   const int lane = threadIdx.x % kWave;
   const uint32_t want = f + 1u;
   if (lane < kSplitMembers && (lane == g || (g == 0 && lane >= G)))
     __hip_atomic_store(fl + lane, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int polls = 0;; ++polls) {
     const uint32_t v = lane < G ? __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : want;
-    if (__all((int32_t)(v - want) >= 0)) break;
+    const uint64_t low = __ballot((int32_t)(v - want) < 0);
+    if (low == 0) return 0u;
     if (polls >= spin_limit) {
       if (lane == 0) atomicAdd(err, 1u);
-      break;
+      return (uint32_t)low;
     }
     __builtin_amdgcn_s_sleep(1);
   }
@@ -166,27 +173,31 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   // fragments of this wave's token block, B chunk, y of the first 16 rows),
   // then the slot's rank and scale
   const int kc = 1 << p.ksh, nsteps = kc >> 5;
-  const int64_t k0 = (int64_t)g << p.ksh;
   const int nb = (rows + 15) >> 4;  // 16-row token blocks: wave t takes block t in the shrink
   const int pa = p.n_slices << (p.ksh + LPR);  // A pieces: n_slices * kc * PR
   // pieces outside the chunk read the slot's first row and are stored as
   // zeros (aok); loaded values are never selected, so no load sits in a branch
   u32x4 av[kSBatch];
   uint32_t aok = 0;
+  auto load_a = [&](int gm) {  // member gm's A chunk of every slice
+    const int64_t k0 = (int64_t)gm << p.ksh;
+    aok = 0;
 #pragma unroll
-  for (int i = 0; i < kSBatch; ++i) {
-    const int q = tid + kSThreads * i;
-    const int s = q >> (p.ksh + LPR);
-    const int rem = q & ((kc * PR) - 1);
-    const int row = rem / PR, c8 = rem % PR;
-    const bool ok = q < pa && k0 + row < p.d_in && 8 * c8 < R;
-    aok |= (uint32_t)ok << i;
-    const int ss = ok ? s : 0;
-    const uint16_t *ptr = reinterpret_cast<const uint16_t *>(pick<NS>(p.A, ss, p.n_slices)) +
-                          (int64_t)slot * pick<NS>(p.a_stride, ss, p.n_slices) +
-                          (ok ? (k0 + row) * R + 8 * c8 : 0);
-    av[i] = gload16(ptr);
-  }
+    for (int i = 0; i < kSBatch; ++i) {
+      const int q = tid + kSThreads * i;
+      const int s = q >> (p.ksh + LPR);
+      const int rem = q & ((kc * PR) - 1);
+      const int row = rem / PR, c8 = rem % PR;
+      const bool ok = q < pa && k0 + row < p.d_in && 8 * c8 < R;
+      aok |= (uint32_t)ok << i;
+      const int ss = ok ? s : 0;
+      const uint16_t *ptr = reinterpret_cast<const uint16_t *>(pick<NS>(p.A, ss, p.n_slices)) +
+                            (int64_t)slot * pick<NS>(p.a_stride, ss, p.n_slices) +
+                            (ok ? (k0 + row) * R + 8 * c8 : 0);
+      av[i] = gload16(ptr);
+    }
+  };
+  load_a(g);
   const bool xw = wave < nb;  // this wave shrinks token block `wave`
   const bool xok = xw && 16 * wave + l16 < rows;
   const int xt = wave == 0 ? tok[0] : (wave == 1 ? tok[1] : (wave == 2 ? tok[2] : tok[3]));
@@ -194,15 +205,16 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
                           (xok ? (p.x_row_div == 1 ? (int64_t)xt : (int64_t)xt / p.x_row_div) * p.ldx : 0);
   // x fragments past d_in meet zero A rows, and rows past the tile feed
   // outputs that are never used: both read the row's first values instead
-  const int64_t kx = k0 + 8 * kg;  // this lane's k at step 0
   u32x4 xa[XB];
-  if (xw) {
+  auto load_x = [&](int gm) {  // member gm's x fragments of this wave's token block
+    const int64_t kx = ((int64_t)gm << p.ksh) + 8 * kg;  // this lane's k at step 0
 #pragma unroll
     for (int i = 0; i < XB; ++i) {
       const int64_t k = kx + 32 * (int64_t)i;
       xa[i] = gload16(xbase + (i < nsteps && k < p.d_in ? k : 0));
     }
-  }
+  };
+  if (xw) load_x(g);
   u32x4 bv[kSBatch];
   uint32_t bok = 0;
 #pragma unroll
@@ -245,17 +257,20 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   const int rk8 = (rk + 7) & ~7;  // ranks read, as the other kernels read them
 
   // ---- A chunk into LDS (ranks past the slot's rank as zeros)
+  auto stage_a = [&]() {
 #pragma unroll
-  for (int i = 0; i < kSBatch; ++i) {
-    const int q = tid + kSThreads * i;
-    if (q < pa) {
-      const int s = q >> (p.ksh + LPR);
-      const int rem = q & ((kc * PR) - 1);
-      const int row = rem / PR, c8 = rem % PR;
-      *reinterpret_cast<u32x4 *>(As + ((s << p.ksh) + row) * LDA + 8 * c8) =
-          ((aok >> i) & 1) && 8 * c8 < rk8 ? av[i] : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < kSBatch; ++i) {
+      const int q = tid + kSThreads * i;
+      if (q < pa) {
+        const int s = q >> (p.ksh + LPR);
+        const int rem = q & ((kc * PR) - 1);
+        const int row = rem / PR, c8 = rem % PR;
+        *reinterpret_cast<u32x4 *>(As + ((s << p.ksh) + row) * LDA + 8 * c8) =
+            ((aok >> i) & 1) && 8 * c8 < rk8 ? av[i] : u32x4{0, 0, 0, 0};
+      }
     }
-  }
+  };
+  stage_a();
   __syncthreads();
 
   // ---- shrink: wave t, all k-steps of token block t.  D' = A^T x^T, so that
@@ -266,7 +281,9 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   auto frag_off = [&](int gg, int t, int s, int c) {
     return (uint32_t)(((((gg * p.n_frag + fr0 + t) * p.n_slices + s) * RB + c) * kWave + lane) * 16);
   };
-  if (xw) {
+  // member gm's partial rows of token block `wave`, from the staged A chunk
+  // and xa, into member gm's slot
+  auto shrink_store = [&](int gm) {
     f32x4 acc[NS][RB];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -288,13 +305,13 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
         }
       }
     }
-    // this member's partial fragments, with agent-coherent stores
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        if (s < p.n_slices) __builtin_amdgcn_raw_buffer_store_b128(acc[s][rb], pr, frag_off(g, wave, s, rb), 0, 16);
-  }
+        if (s < p.n_slices) __builtin_amdgcn_raw_buffer_store_b128(acc[s][rb], pr, frag_off(gm, wave, s, rb), 0, 16);
+  };
+  if (xw) shrink_store(g);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
 #pragma unroll
   for (int i = 0; i < kSBatch; ++i) {
@@ -310,8 +327,28 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (G > 1) {
-    if (wave == 0) split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitMembers);
+    __shared__ uint32_t missing;
+    if (wave == 0) {
+      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitMembers);
+      if (lane == 0) missing = m;
+    }
     __syncthreads();
+    // members that did not arrive in time: their partials are computed here,
+    // by the same code, so they are the bits those members store themselves
+    for (uint32_t m = missing; m; m &= m - 1) {
+      const int gm = __builtin_ctz(m);
+      load_a(gm);
+      if (xw) load_x(gm);
+      __syncthreads();  // the A chunk's LDS is free
+      stage_a();
+      __syncthreads();
+      if (xw) shrink_store(gm);
+    }
+    if (missing) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   // ---- expand, token block by token block: u = scale * (the members'
@@ -466,24 +503,29 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
 
   // ---- second round trip: every load is issued, none behind a branch;
   // pieces that are not needed take an offset past their resource
-  const int k0 = g * KC;
   const int nb = (rows + 15) >> 4;
   const rsrc_t ar = make_rsrc(reinterpret_cast<const uint16_t *>(p.A) + (int64_t)slot * p.a_stride,
                               (uint32_t)(p.d_in * R * 2));
   u32x4 av[NA];
+  auto load_a = [&](int gm) {  // member gm's A chunk
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int q = tid + kSThreads * i;
-    av[i] = buf_load16(ar, q < NPA ? (uint32_t)(k0 * R * 2 + q * 16) : kOut);
-  }
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + kSThreads * i;
+      av[i] = buf_load16(ar, q < NPA ? (uint32_t)(gm * KC * R * 2 + q * 16) : kOut);
+    }
+  };
+  load_a(g);
   const bool xw = wave < nb;
   const int xt = wave == 0 ? tok[0] : (wave == 1 ? tok[1] : (wave == 2 ? tok[2] : tok[3]));
   const int xrow = 16 * wave + l16 < rows ? (p.x_row_div == 1 ? xt : xt / p.x_row_div) : 0;
   const rsrc_t xr = make_rsrc(p.x, p.x_bytes);
-  const uint32_t xo = xw ? (uint32_t)((xrow * p.ldx + k0 + 8 * kg) * 2) : kOut;
   u32x4 xa[KS];
+  auto load_x = [&](int gm) {  // member gm's x fragments of this wave's token block
+    const uint32_t xo = xw ? (uint32_t)((xrow * p.ldx + gm * KC + 8 * kg) * 2) : kOut;
 #pragma unroll
-  for (int i = 0; i < KS; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
+    for (int i = 0; i < KS; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
+  };
+  load_x(g);
   const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(p.B) + (int64_t)slot * p.b_stride,
                               (uint32_t)(R * p.width * 2));
   u32x4 bv[NBQ];
@@ -513,15 +555,18 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const int rk8 = (rk + 7) & ~7;
 
   // ---- A chunk into LDS: piece q = row q / (R / 8), ranks 8 (q % (R / 8)) ..
+  auto stage_a = [&]() {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int q = tid + kSThreads * i;
-    if (q < NPA) {
-      const int row = q / (R / 8), c8 = q % (R / 8);
-      *reinterpret_cast<u32x4 *>(As + row * LDA + 8 * c8) = 8 * c8 < rk8 ? av[i] : u32x4{0, 0, 0, 0};
-      if constexpr (R == 8) *reinterpret_cast<u32x4 *>(As + row * LDA + 8) = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + kSThreads * i;
+      if (q < NPA) {
+        const int row = q / (R / 8), c8 = q % (R / 8);
+        *reinterpret_cast<u32x4 *>(As + row * LDA + 8 * c8) = 8 * c8 < rk8 ? av[i] : u32x4{0, 0, 0, 0};
+        if constexpr (R == 8) *reinterpret_cast<u32x4 *>(As + row * LDA + 8) = u32x4{0, 0, 0, 0};
+      }
     }
-  }
+  };
+  stage_a();
   __syncthreads();
 
   // ---- shrink: wave t, all k-steps of token block t (D' = A^T x^T, so that
@@ -529,13 +574,15 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const rsrc_t pr = make_rsrc(p.part, p.part_bytes);
   const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 1024 + lane * 16);
   const uint32_t plane = (uint32_t)(p.n_frag * RB * 1024);  // between members
-  if (xw) {
-    // two accumulator chains (even and odd k-steps), added at the end: the
-    // MFMAs of one chain wait for each other, the two chains do not
+  // member gm's partial rows of token block `wave`, from the staged A chunk
+  // and xa, into member gm's slot.  Two accumulator chains (even and odd
+  // k-steps) added at the end: the MFMAs of one chain wait for each other,
+  // the two chains do not.
+  auto shrink_store = [&](int gm) {
     f32x4 acc[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[0][rb] = acc[1][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int kleft = p.d_in - k0 - 8 * kg;  // x values of this lane past d_in are dropped
+    const int kleft = p.d_in - gm * KC - 8 * kg;  // x values of this lane past d_in are dropped
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       const u32x4 xv = p.x_full || 32 * i < kleft ? xa[i] : u32x4{0, 0, 0, 0};
@@ -546,9 +593,10 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr, fbase + g * plane + (wave * RB + rb) * 1024,
+      __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr, fbase + gm * plane + (wave * RB + rb) * 1024,
                                              0, 16);
-  }
+  };
+  if (xw) shrink_store(g);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
 #pragma unroll
   for (int i = 0; i < NBQ; ++i) {
@@ -563,8 +611,29 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (G > 1) {
-    if (wave == 0) split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitMembers);
+    __shared__ uint32_t missing;
+    if (wave == 0) {
+      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitMembers);
+      if (lane == 0) missing = m;
+    }
     __syncthreads();
+    // members that did not arrive in time: their partials are computed here,
+    // by the same code, so they are the bits those members store themselves
+    // (a late member and this workgroup then write equal values)
+    for (uint32_t m = missing; m; m &= m - 1) {
+      const int gm = __builtin_ctz(m);
+      load_a(gm);
+      if (xw) load_x(gm);
+      __syncthreads();  // the A chunk's LDS is free
+      stage_a();
+      __syncthreads();
+      if (xw) shrink_store(gm);
+    }
+    if (missing) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   // ---- expand, token block by token block: u = scale * (members' partials

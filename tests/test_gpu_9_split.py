@@ -170,3 +170,58 @@ def test_split_graph_replays(L):
         d.apply(L)  # eager work between replays
         torch.cuda.synchronize()
     assert m.split_wait_timeouts() == 0
+
+
+_FALLBACK_CHILD = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, sys.argv[1] + "/tests")
+import segmented_gather_rank_amd as L
+from test_gpu_9_split import decode_case
+from gpu_util import DevCase, from_dev
+out = sys.argv[2]
+res = {}
+for name, args in (("one_slice", dict(seed=640, r=16, widths=(512,))),
+                   ("three_slices", dict(seed=641, r=16, widths=(512, 256, 136)))):
+    c = decode_case(args["seed"], args["r"], widths=args["widths"])
+    d = DevCase(c)
+    y, meta = d.apply(L)
+    torch.cuda.synchronize()
+    res[name] = from_dev(y)
+    res[name + "_gave_up"] = np.array([meta.split_wait_timeouts()])
+np.savez(out, **res)
+print("child done", flush=True)
+"""
+
+
+def test_split_fallback_when_peers_are_late(L, tmp_path):
+    """With no patience at all (spin limit 0, in a child process: the limit is
+    read once per process), members that do not see every peer at their first
+    look compute the missing partials themselves.  The results are the normal
+    run's, bit for bit."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = str(tmp_path / "fallback.npz")
+    env = dict(os.environ, LORA_SPLIT_SPIN_LIMIT="0")
+    print("[split-fallback] child process with LORA_SPLIT_SPIN_LIMIT=0", flush=True)
+    r = subprocess.run([sys.executable, "-c", _FALLBACK_CHILD, root, out], env=env, capture_output=True,
+                       text=True, timeout=100)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    got = np.load(out)
+    # the premise: with no patience some member missed a peer and took the
+    # fallback (two batches of 33 tiles x 8 members each looked once)
+    assert int(got["one_slice_gave_up"][0]) + int(got["three_slices_gave_up"][0]) > 0
+    for name, args in (("one_slice", dict(seed=640, r=16, widths=(512,))),
+                       ("three_slices", dict(seed=641, r=16, widths=(512, 256, 136)))):
+        c = decode_case(args["seed"], args["r"], widths=args["widths"])
+        d = DevCase(c)
+        y, meta = d.apply(L)
+        want = from_dev(y)
+        assert meta.split_wait_timeouts() == 0
+        print(f"[split-fallback] {name}: {int(got[name + '_gave_up'][0])} waits gave up", flush=True)
+        assert np.array_equal(got[name].view(np.uint16), want.view(np.uint16)), name
+        check_rows(c, got[name], oracle_rows(c, np.arange(c.T)), f"{name} after fallback")
