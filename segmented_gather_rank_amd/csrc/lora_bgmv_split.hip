@@ -537,15 +537,6 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     const bool ok = lb < nbm && j < R && col < p.width;
     bv[i] = buf_load16(br, ok ? (uint32_t)((j * p.width + col) * 2) : kOut);
   }
-  const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
-  const uint32_t yo0 = (uint32_t)((p.offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
-  uint32_t yrow = (uint32_t)(tok[0] * p.ldy * 2);
-  u32x2 yv[QB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const bool ok = p.add && wave + 4 * q < nbm;
-    yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
-  }
   const int rk = p.slot_rank ? min(max(p.slot_rank[slot], 0), R) : R;
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   if (rk == 0) {
@@ -610,6 +601,17 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // y is read once the fragments are acknowledged (an outstanding load would
+  // hold the acknowledgement wait): it streams while the members meet
+  const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
+  const uint32_t yo0 = (uint32_t)((p.offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
+  uint32_t yrow = (uint32_t)(tok[0] * p.ldy * 2);
+  u32x2 yv[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const bool ok = p.add && wave + 4 * q < nbm;
+    yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
+  }
   if (G > 1) {
     __shared__ uint32_t missing;
     if (wave == 0) {
