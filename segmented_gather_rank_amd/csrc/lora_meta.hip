@@ -252,8 +252,22 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   //    counts and presence.  The segment arrays are written after the barrier
   //    below: a barrier after global stores would wait for them.
   const int k = tid;
-  int c, start, nseg = 0, ntiles = 0, seg;
-  {
+  int c = 0, start = 0, nseg = 0, ntiles = 0, seg = 0;
+  if (K <= kWave) {  // every key in wave 0: no exchange between waves
+    if (wave == 0) {
+      c = k < K ? cnt[k] : 0;
+      const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
+      const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
+      nseg = __builtin_amdgcn_readlane(ip, kWave - 1);
+      ntiles = __builtin_amdgcn_readlane(it, kWave - 1);
+      start = ic - c;
+      seg = ip - pr;
+      if (k < K) {
+        kstart[k] = start;
+        tbase[k] = it - nt;
+      }
+    }
+  } else {
     c = k < K ? cnt[k] : 0;
     const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
     const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
