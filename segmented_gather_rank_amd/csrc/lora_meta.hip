@@ -277,22 +277,26 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
       wsum[wave][2] = ip;
     }
     __syncthreads();
-    int bc = 0, bt = 0, bp = 0;
-    for (int w = 0; w < kMetaWaves; ++w) {
-      const int a = wsum[w][0], b2 = wsum[w][1], d = wsum[w][2];
-      if (w < wave) {
-        bc += a;
-        bt += b2;
-        bp += d;
+    // only the waves that hold keys need the others' sums, and only theirs
+    const int nkw = (K + kWave - 1) / kWave;
+    if (wave < nkw) {
+      int bc = 0, bt = 0, bp = 0;
+      for (int w = 0; w < nkw; ++w) {
+        const int a = wsum[w][0], b2 = wsum[w][1], d = wsum[w][2];
+        if (w < wave) {
+          bc += a;
+          bt += b2;
+          bp += d;
+        }
+        nseg += d;
+        ntiles += b2;
       }
-      nseg += d;
-      ntiles += b2;
-    }
-    start = bc + ic - c;
-    seg = bp + ip - pr;
-    if (k < K) {
-      kstart[k] = start;
-      tbase[k] = bt + it - nt;
+      start = bc + ic - c;
+      seg = bp + ip - pr;
+      if (k < K) {
+        kstart[k] = start;
+        tbase[k] = bt + it - nt;
+      }
     }
   }
   __syncthreads();
