@@ -32,8 +32,9 @@
 // workgroup that gives up counts itself in the word after the flags and
 // computes the missing members' partials itself, with the same code (so the
 // same bits), storing them into those members' slots.  The result never
-// depends on the members being resident together; the grid is kept within the
-// workgroups the device holds at once so that they normally are.
+// depends on the members being resident together.  Workgroups are dispatched
+// in order on each XCD and a tile's members are neighbours there, so the tiles
+// within the resident part of a larger grid finish and make room for the rest.
 //
 // Only bf16.
 #include "lora_host.h"
@@ -783,8 +784,8 @@ static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices
   return pl;
 }
 
-// Plans the call for this instantiation and launches it, unless every member
-// of every tile cannot be resident at once (then *used stays false).
+// Plans the call for this instantiation and launches it, unless its grid
+// exceeds the workgroups the device holds at once (then *used stays false).
 template <int R, int NS>
 static hipError_t launch_split_k(const MetaView &meta, SplitParams &p, const int64_t *width, size_t part_bytes,
                                  hipStream_t stream, bool *used) {
@@ -803,7 +804,10 @@ static hipError_t launch_split_k(const MetaView &meta, SplitParams &p, const int
       if (e != hipSuccess) return e;
     }
     const int resident = resident_groups(g_split_resident[ri][ni], fn, kSThreads, lds_max);
-    if (pl.G > 1 && pl.grid > resident) {  // members of one tile could wait for one another forever
+    // this kernel runs only when its whole grid is resident: with more
+    // workgroups than that it measured slower than the one-workgroup-per-token
+    // kernel (packed q/k/v at G = 16, 21 us against 15 us)
+    if (pl.G > 1 && pl.grid > resident) {
       g_cap = pl.G / 2;
       continue;
     }
@@ -824,7 +828,7 @@ static hipError_t launch_split_k(const MetaView &meta, SplitParams &p, const int
 static std::atomic<int> g_split1_resident[12][kMaxDevices];
 
 // Launches the one-slice kernel for a plan whose chunk is 32 KS rows, unless
-// its grid exceeds the workgroups the device holds at once (*too_many).
+// one XCD cannot hold a whole tile's members (*too_many).
 template <int R, int KS>
 static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, const int64_t *width, SplitPlan pl,
                                   uint32_t x_bytes, uint32_t y_bytes, hipStream_t stream, bool *used, bool *too_many) {
@@ -842,7 +846,11 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
     if (e != hipSuccess) return e;
   }
   const int resident = resident_groups(g_split1_resident[ri], fn, kSThreads, lds_max);
-  if (pl.G > 1 && pl.grid > resident) {
+  // workgroups are dispatched in order on each XCD and a tile's members are
+  // neighbours there, so the tiles within the resident part of the grid
+  // finish and make room for the rest; only an XCD that cannot hold one whole
+  // tile would leave members waiting for the spin limit
+  if (pl.G > 1 && resident / 8 < pl.G) {
     *too_many = true;
     return hipSuccess;
   }
@@ -884,7 +892,8 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
 }
 
 // One slice: plan, then the instantiation for the plan's chunk (128, 256 or
-// 512 rows); when the grid would not be resident, plan again with G halved.
+// 512 rows); when an XCD cannot hold a tile's members, plan again with G
+// halved.
 template <int R>
 static hipError_t launch_split1(const MetaView &meta, const SplitParams &sp, const int64_t *width,
                                 size_t part_bytes, hipStream_t stream, bool *used) {
