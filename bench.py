@@ -122,7 +122,8 @@ def dominant_kernel(c, mode):
 def split_takes(c):
     """Whether a decode-shaped call runs the split kernel (each work tile spread
     over several workgroups): bf16, and some member count of at most 16 gives
-    every member an A chunk (<= 512 rows) and a B share that fit its LDS."""
+    every member an A chunk (<= 512 rows, <= 1024 for one slice at rank <= 16)
+    and a B share that fit its LDS."""
     if c.dtype != "bf16" or os.environ.get("LORA_DISABLE_SPLIT_BGMV", "0") not in ("", "0"):
         return False
     rp = max(16, c.r_max)
@@ -134,7 +135,8 @@ def split_takes(c):
     while g <= 16:
         kc = max(128, 1 << max(0, (-(-c.d_in // g) - 1).bit_length()))
         bpm = -(-nbt // g)
-        if kc <= 512 and c.n_slices * kc * (rp // 8) <= 2048 and bpm <= 32 and bpm * 2 * rp <= 2048:
+        kc_max = 1024 if c.n_slices == 1 and c.r_max <= 16 else 512
+        if kc <= kc_max and c.n_slices * kc * (rp // 8) <= 2048 and bpm <= 32 and bpm * 2 * rp <= 2048:
             return True
         g *= 2
     return False

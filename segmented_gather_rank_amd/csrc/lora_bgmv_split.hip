@@ -751,7 +751,7 @@ static size_t split_lds_max(int R, int NS) {
 // chunk are at most kSPieces 16-byte pieces.  Not ok when no G <= 16 fits or
 // the partial fragments exceed the workspace.
 static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64_t *width,
-                            int32_t R, size_t ws_bytes, int g_cap) {
+                            int32_t R, size_t ws_bytes, int g_cap, int kc_max = 512) {
   SplitPlan pl{};
   const int RP = R < 16 ? 16 : R, RB = RP / 16;
   const int NSb = n_slices <= 1 ? 1 : (n_slices <= 2 ? 2 : (n_slices <= 4 ? 4 : 8));
@@ -767,7 +767,7 @@ static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices
     if (G > kSplitMembers || G > g_cap) return pl;
     const int64_t kc = std::max<int64_t>(128, (int64_t)1 << ilog2((d_in + G - 1) / G));
     const int64_t bpm = (nbt + G - 1) / G;
-    if (kc <= 512 && (int64_t)n_slices * kc * (RP / 8) <= kSPieces && bpm <= kSMaxBpm && bpm * 2 * RP <= kSPieces) {
+    if (kc <= kc_max && (int64_t)n_slices * kc * (RP / 8) <= kSPieces && bpm <= kSMaxBpm && bpm * 2 * RP <= kSPieces) {
       pl.ksh = ilog2(kc);
       pl.bpm = (int)bpm;
       break;
@@ -825,7 +825,7 @@ static hipError_t launch_split_k(const MetaView &meta, SplitParams &p, const int
 
 // One-slice kernel: plan (as above, with the first LDS region holding only
 // the A chunk), residency, launch.
-static std::atomic<int> g_split1_resident[12][kMaxDevices];
+static std::atomic<int> g_split1_resident[16][kMaxDevices];
 
 // Launches the one-slice kernel for a plan whose chunk is 32 KS rows, unless
 // one XCD cannot hold a whole tile's members (*too_many).
@@ -834,7 +834,7 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
                                   uint32_t x_bytes, uint32_t y_bytes, hipStream_t stream, bool *used, bool *too_many) {
   constexpr int RP = R < 16 ? 16 : R, LDA = RP == 64 ? 80 : RP;
   const void *fn = reinterpret_cast<const void *>(&bgmv_split1_kernel<R, KS>);
-  constexpr int ri = (R == 8 ? 0 : (R == 16 ? 1 : (R == 32 ? 2 : 3))) * 3 + (KS == 4 ? 0 : (KS == 8 ? 1 : 2));
+  constexpr int ri = (R == 8 ? 0 : (R == 16 ? 1 : (R == 32 ? 2 : 3))) * 4 + (KS == 4 ? 0 : (KS == 8 ? 1 : (KS == 16 ? 2 : 3)));
   pl.bs_off = (32 * KS * LDA * 2 + 15) / 16 * 16;
   pl.lds = pl.bs_off + (size_t)RP * pl.ldb * 2;
   // the residency count is cached per device and taken at this
@@ -902,12 +902,18 @@ static hipError_t launch_split1(const MetaView &meta, const SplitParams &sp, con
   const int64_t x_bytes = ((x_rows - 1) * sp.ldx + sp.d_in) * 2;
   const int64_t y_bytes = ((meta.T - 1) * sp.ldy + sp.offset[0] + width[0]) * 2;
   if (x_bytes >= ((int64_t)1 << 32) || y_bytes >= ((int64_t)1 << 32)) return hipSuccess;
+  // ranks up to 16 also take 1024-row chunks (32 steps), so that d_in up to
+  // 16384 splits 16 ways
+  const int kc_max = R <= 16 ? 1024 : 512;
   for (int g_cap = kSplitMembers; g_cap >= 1; g_cap /= 2) {
-    const SplitPlan pl = plan_split(meta.T, meta.S, sp.d_in, 1, width, R, part_bytes, g_cap);
+    const SplitPlan pl = plan_split(meta.T, meta.S, sp.d_in, 1, width, R, part_bytes, g_cap, kc_max);
     if (!pl.ok) return hipSuccess;
     bool too_many = false;
     hipError_t e = hipSuccess;
-    if (pl.ksh == 7)
+    if (pl.ksh == 10) {
+      if constexpr (R <= 16)
+        e = launch_split1_k<R, 32>(meta, sp, width, pl, (uint32_t)x_bytes, (uint32_t)y_bytes, stream, used, &too_many);
+    } else if (pl.ksh == 7)
       e = launch_split1_k<R, 4>(meta, sp, width, pl, (uint32_t)x_bytes, (uint32_t)y_bytes, stream, used, &too_many);
     else if (pl.ksh == 8)
       e = launch_split1_k<R, 8>(meta, sp, width, pl, (uint32_t)x_bytes, (uint32_t)y_bytes, stream, used, &too_many);

@@ -71,6 +71,18 @@ def test_split_decode_parity(L, r, add):
     check_flags(meta, 1)
 
 
+@pytest.mark.parametrize("d_in,r", [(14336, 16), (3000, 8), (5000, 32)])
+def test_split_long_rows(L, d_in, r):
+    """d_in that splits into 1024-row chunks (rank <= 16) or into chunks that
+    do not tile it exactly (the tail of the last member's chunk reads zeros)."""
+    c = decode_case(560 + r, r, d_in=d_in, widths=(1024,))
+    print(f"[split-long] {c.name} d_in={d_in}", flush=True)
+    d = DevCase(c)
+    y, meta = d.apply(L)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
+    check_flags(meta, 1)
+
+
 def test_split_rank64_three_slices_falls_back(L):
     """Three slices at rank 64 do not fit the split kernel's LDS: the call runs
     on the one-workgroup-per-token kernel (flags untouched) and is still right."""
