@@ -28,7 +28,9 @@
 // counters that the metadata kernel zeroes: each call raises each of a tile's
 // 16 words exactly once (member 0 also raises the words of members >= G), so
 // they stay equal between calls and a member waits for "my value + 1".  The
-// loads of B and y are issued before the wait.  The wait is bounded: a
+// B chunk is loaded before the wait (y too in the packed-slice kernel; the
+// one-slice kernel reads y once its fragments are acknowledged, so that the
+// acknowledgement wait does not hold on y).  The wait is bounded: a
 // workgroup that gives up counts itself in the word after the flags and
 // computes the missing members' partials itself, with the same code (so the
 // same bits), storing them into those members' slots.  The result never
@@ -62,7 +64,7 @@ struct SplitParams {
   int32_t ksh;                       // log2 kc (kc >= 128)
   int32_t bpm;                       // 16-column blocks per member
   int32_t ldb;                       // row stride of the B chunk in LDS (elements)
-  int32_t bs_off;                    // LDS byte offset of the B chunk (after the A chunk / partials / rank rows)
+  int32_t bs_off;                    // LDS byte offset of the B chunk (after the A chunk)
   int32_t max_tiles;
   int32_t n_frag;                    // 16-row fragments per member plane
   int32_t spin_limit;
@@ -720,18 +722,11 @@ size_t split_ws_bytes(int64_t T, int32_t S, int32_t n_slices, int32_t R) {
 }
 
 static std::atomic<int> g_split_resident[4][4][kMaxDevices];
-int split_members();
 
-int split_spin_limit();
-
-// LDS of the first region (A chunk, then wave partials, then rank rows) and of
-// the B chunk.
+// LDS bytes of the A chunk (the B chunk follows it).
 static size_t split_region1(int n_slices, int64_t kc, int R) {
-  const int RP = R < 16 ? 16 : R, RB = RP / 16, LDA = RP == 64 ? 80 : RP;
-  const int NSb = n_slices <= 1 ? 1 : (n_slices <= 2 ? 2 : (n_slices <= 4 ? 4 : 8));
-  const size_t a = (size_t)n_slices * kc * LDA * 2, red = (size_t)4 * NSb * RB * 1024,
-               uhl = (size_t)kTileRows * n_slices * RP * 4;
-  return (std::max(a, std::max(red, uhl)) + 15) / 16 * 16;
+  const int RP = R < 16 ? 16 : R, LDA = RP == 64 ? 80 : RP;
+  return ((size_t)n_slices * kc * LDA * 2 + 15) / 16 * 16;
 }
 static int split_ldb(int bpm) { return 16 * bpm + ((16 - 16 * bpm) & 127); }  // = 16 (mod 128): conflict-free
 

@@ -104,5 +104,6 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
                              int add, float *part, size_t part_bytes, hipStream_t stream, bool *used);
 bool split_disabled();
 int split_spin_limit();
+int split_members();
 
 }  // namespace lora
