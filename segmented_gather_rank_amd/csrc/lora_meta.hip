@@ -407,6 +407,10 @@ static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_
   const int32_t n_sync = (int32_t)sync_words(T, S);
   const size_t lds = meta_lds_bytes(S, T, MOE && src.expert_map ? src.E_global : 0, cached, match_lds);
   const int kind = T <= kMetaThreads ? kSmall : (cached ? kCached : kStreamed);
+  // few keys (at most 4 key bits): one ballot per bit is cheaper than lanes
+  // contending for a handful of lane-mask words (measured: 9 keys over 17705
+  // rows, 10 us against 18 us of counting)
+  if (S + 1 <= 16) match_lds = false;
 #define LORA_META_LAUNCH(K, M)                                                                                    \
   return launch_meta_k<MOE, K, M>(src, T, S, lds, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, \
                                   sync, n_sync, stream)
