@@ -20,23 +20,32 @@
 //   * 16-column blocks [g bpm, (g + 1) bpm) of the concatenated slices: the
 //     expand D'[col][token] = B^T u^T (v_mfma_f32_16x16x16_bf16, u split into
 //     bf16 hi + lo parts) and the read-modify-write of those y columns.
-// The members exchange the partial rank rows through memory: each stores its
-// fragments with agent-coherent 16-byte stores, waits until they are
-// acknowledged, and raises its own flag word of the tile; then it waits until
-// every member's flag is raised, and adds the G partial fragments in member
-// order (every member gets the same u, bit for bit).  Flags are per-tile
-// counters that the metadata kernel zeroes: each call raises each of a tile's
-// 16 words exactly once (member 0 also raises the words of members >= G), so
-// they stay equal between calls and a member waits for "my value + 1".  The
-// B chunk is loaded before the wait (y too in the packed-slice kernel; the
-// one-slice kernel reads y once its fragments are acknowledged, so that the
-// acknowledgement wait does not hold on y).  The wait is bounded: a
-// workgroup that gives up counts itself in the word after the flags and
-// computes the missing members' partials itself, with the same code (so the
-// same bits), storing them into those members' slots.  The result never
-// depends on the members being resident together.  Workgroups are dispatched
-// in order on each XCD and a tile's members are neighbours there, so the tiles
-// within the resident part of a larger grid finish and make room for the rest.
+// The members exchange the partial rank rows through the L2 of their XCD.
+// Workgroups go to the XCDs in turn (blockIdx mod 8 names the XCD) and a
+// tile's members share that residue.  Each member stores its fragments with
+// plain 16-byte stores (the write-through L1 passes them to L2), waits until
+// L2 has acknowledged them, and raises its own flag word of the tile the same
+// way; the others read both with agent-coherent loads, which skip L1.
+// (Agent-coherent stores also go on to memory: twice the acknowledgement time,
+// and a flag took about 0.9 us instead of 0.2 us to reach a peer.)  Once every
+// member's flag is up, the G partial fragments are added in one fixed order
+// (each wave a quarter of the members, then the four sums in wave order
+// through LDS), so every member gets the same u, bit for bit.  Flags are
+// per-tile counters that the metadata kernel zeroes: each call raises each of
+// a tile's 16 words exactly once (member 0 also raises the words of members
+// >= G), so they stay equal between calls and a member waits for "my value +
+// 1".  The B chunk is loaded with the A chunk and x, and so is the y of the
+// first 16 rows except with the longest chunks, so that none of them is
+// outstanding at the acknowledgement wait or the polls (loads complete in
+// order).  The wait is bounded: a workgroup that
+// gives up counts itself in the word after the flags and computes the missing
+// members' partials itself, with the same code (so the same bits), storing
+// them into those members' slots.  The result therefore depends neither on
+// the members being resident together nor on their sharing an XCD (a member
+// elsewhere would not see the others' flags before the kernel ends; it only
+// costs the spin limit).  Workgroups are dispatched in order on each XCD and a
+// tile's members are neighbours there, so the tiles within the resident part
+// of a larger grid finish and make room for the rest.
 //
 // Only bf16.
 #include "lora_host.h"
@@ -98,13 +107,16 @@ __device__ __forceinline__ void split_zero(const SplitParams &p, const int32_t *
 // >= G) to f + 1, then wait until the G members' words reach it: one wave,
 // at most spin_limit polls.  Returns the members whose words were still low
 // when it gave up (bit g'), 0 when all arrived; a wait that gives up counts
-// itself in *err.
+// itself in *err.  The words are raised with plain stores, which stop in the
+// L2 of this XCD, where the other members (on the same XCD) poll them with
+// agent-coherent loads; a member on another XCD would not see them before
+// the kernel ends, give up at the spin limit and compute the partials itself.
 __device__ __forceinline__ uint32_t split_wait(uint32_t *fl, uint32_t f, int g, int G, int spin_limit,
                                                uint32_t *err) {
   const int lane = threadIdx.x % kWave;
   const uint32_t want = f + 1u;
   if (lane < kSplitMembers && (lane == g || (g == 0 && lane >= G)))
-    __hip_atomic_store(fl + lane, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_raw_buffer_store_b32(want, make_rsrc(fl, kSplitMembers * 4), lane * 4, 0, 0);
   for (int polls = 0;; ++polls) {
     const uint32_t v = lane < G ? __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : want;
     const uint64_t low = __ballot((int32_t)(v - want) < 0);
@@ -117,18 +129,56 @@ __device__ __forceinline__ uint32_t split_wait(uint32_t *fl, uint32_t f, int g, 
   }
 }
 
-// Sum of the MG members' partial fragments at off, off + plane, ... (member
-// order), with agent-coherent loads, all issued before the first is used.
-template <int MG>
-__device__ __forceinline__ f32x4 gather_partials(rsrc_t pr, uint32_t off, uint32_t plane) {
-  f32x4 v[MG];
+// The NF fragments u[i] = sum over the G members gm of the partial fragment
+// at off[i] + gm * plane, shared by the 4 waves: wave w loads members
+// w MG .. w MG + MG - 1 (agent-coherent loads, all issued before the first is
+// used; members past G read as zeros), adds them in member order and leaves
+// its sums in LDS; then every wave adds the 4 waves' sums in wave order.  The
+// additions run in one fixed order for every member of a tile, so all of them
+// get the same bits, and each fragment crosses from L2 once per workgroup, not
+// once per wave.  Only the first nf fragments are gathered (the others come
+// out as zeros).  stage: nf * 4 * 64 f32x4 of LDS that no wave uses on entry;
+// it is read until every wave has its u, so the caller passes a barrier before
+// writing it again.
+template <int MG, int NF>
+__device__ __forceinline__ void gather_waves(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int G, int nf,
+                                             f32x4 *stage, f32x4 (&u)[NF]) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  f32x4 v[NF][MG];
 #pragma unroll
-  for (int gg = 0; gg < MG; ++gg)
-    v[gg] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, off + gg * plane, 0, 16));
-  f32x4 u = v[0];
+  for (int i = 0; i < MG; ++i) {
+    const int gm = wave * MG + i;
 #pragma unroll
-  for (int gg = 1; gg < MG; ++gg) u += v[gg];
-  return u;
+    for (int f = 0; f < NF; ++f)
+      v[f][i] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, gm < G ? off[f] + gm * plane : 0x7FFFFFF0u, 0, 16));
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    f32x4 w = v[f][0];
+#pragma unroll
+    for (int i = 1; i < MG; ++i) w += v[f][i];
+    if (f < nf) stage[(f * 4 + wave) * kWave + lane] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const f32x4 *st = stage + f * 4 * kWave + lane;
+    u[f] = f < nf ? ((st[0] + st[kWave]) + st[2 * kWave]) + st[3 * kWave] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// gather_waves with the members per wave the member count G = 2^gsh needs
+template <int NF>
+__device__ __forceinline__ void gather_members(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int gsh, int nf,
+                                               f32x4 *stage, f32x4 (&u)[NF]) {
+  switch (gsh) {
+    case 0:
+    case 1:
+    case 2: gather_waves<1, NF>(pr, off, plane, 1 << gsh, nf, stage, u); break;
+    case 3: gather_waves<2, NF>(pr, off, plane, 8, nf, stage, u); break;
+    default: gather_waves<4, NF>(pr, off, plane, 16, nf, stage, u); break;
+  }
 }
 
 template <int R, int NS>
@@ -312,7 +362,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        if (s < p.n_slices) __builtin_amdgcn_raw_buffer_store_b128(acc[s][rb], pr, frag_off(gm, wave, s, rb), 0, 16);
+        if (s < p.n_slices) __builtin_amdgcn_raw_buffer_store_b128(acc[s][rb], pr, frag_off(gm, wave, s, rb), 0, 0);
   };
   if (xw) shrink_store(g);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
@@ -355,27 +405,28 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   }
 
   // ---- expand, token block by token block: u = scale * (the members'
-  // partials added in member order), split into bf16 hi + lo operands; then
+  // partials added in the gather's fixed order), split into bf16 hi + lo operands; then
   // every column block of this wave: B^T from LDS, two MFMAs, y.  The y of
   // the next token block is loaded at the end of each block.
   for (int t = 0; t < nb; ++t) {
     s16x4 uh[NS][RB], ul[NS][RB];
+    {
+      uint32_t off[NS * RB];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s < p.n_slices) {
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < RB; ++c) off[s * RB + c] = s < p.n_slices ? frag_off(0, t, s, c) : 0x7FFFFFF0u;
+      f32x4 u[NS * RB];
+      // the stage (n_slices RB 4 KB) fits the A chunk's region: kc >= 128
+      gather_members<NS * RB>(pr, off, p.n_frag * p.n_slices * RB * 1024, p.gsh, p.n_slices * RB,
+                              reinterpret_cast<f32x4 *>(split_lds), u);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int c = 0; c < RB; ++c) {
-          f32x4 u;
-          switch (p.gsh) {  // straight-line loads for each member count
-            case 0: u = gather_partials<1>(pr, frag_off(0, t, s, c), p.n_frag * p.n_slices * RB * 1024); break;
-            case 1: u = gather_partials<2>(pr, frag_off(0, t, s, c), p.n_frag * p.n_slices * RB * 1024); break;
-            case 2: u = gather_partials<4>(pr, frag_off(0, t, s, c), p.n_frag * p.n_slices * RB * 1024); break;
-            case 3: u = gather_partials<8>(pr, frag_off(0, t, s, c), p.n_frag * p.n_slices * RB * 1024); break;
-            default: u = gather_partials<16>(pr, frag_off(0, t, s, c), p.n_frag * p.n_slices * RB * 1024); break;
-          }
           uint32_t h[4], l[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) split_bf16(sc * u[e], h[e], l[e]);
+          for (int e = 0; e < 4; ++e) split_bf16(sc * u[s * RB + c][e], h[e], l[e]);
           uh[s][c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
           ul[s][c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
         }
@@ -416,13 +467,16 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
         }
       }
     }
-    if (t + 1 < nb && p.add) {  // y of the next token block
-      const int tn = t + 1 == 1 ? tok[1] : (t + 1 == 2 ? tok[2] : tok[3]);
+    if (t + 1 < nb) {
+      if (p.add) {  // y of the next token block
+        const int tn = t + 1 == 1 ? tok[1] : (t + 1 == 2 ? tok[2] : tok[3]);
 #pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        const bool ok = qok[q] && row + 16 < rows;  // else unused
-        yv[q] = *reinterpret_cast<const u32x2 *>(y + (ok ? (int64_t)tn * p.ldy + qcol[q] : 0));
+        for (int q = 0; q < QB; ++q) {
+          const bool ok = qok[q] && row + 16 < rows;  // else unused
+          yv[q] = *reinterpret_cast<const u32x2 *>(y + (ok ? (int64_t)tn * p.ldy + qcol[q] : 0));
+        }
       }
+      __syncthreads();  // every wave has read the gather's LDS
     }
   }
 }
@@ -474,6 +528,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   constexpr int NBQ = (RP == 64 ? 16 : kSMaxBpm) * 2 * RP / kSThreads;  // B pieces per thread, at most
   constexpr int QB = kSMaxBpm / 4;
   constexpr uint32_t kOut = 0x7FFFFFF0u;                    // past every resource: reads as zeros
+  static_assert(KC * LDA * 2 >= RB * 4 * kWave * 16, "the gather's stage fits the A chunk's region");
   extern __shared__ __align__(16) unsigned char split_lds[];
   uint16_t *const As = reinterpret_cast<uint16_t *>(split_lds);
   uint16_t *const Bs = reinterpret_cast<uint16_t *>(split_lds + p.bs_off);
@@ -540,6 +595,24 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     const bool ok = lb < nbm && j < R && col < p.width;
     bv[i] = buf_load16(br, ok ? (uint32_t)((j * p.width + col) * 2) : kOut);
   }
+  // y of the first token block.  Up to 512-row chunks it is loaded here and
+  // arrives with the rest of the batch, so it holds neither the
+  // acknowledgement wait nor the polls (loads complete in order).  With
+  // 1024-row chunks (32 x loads a lane) it is loaded once the fragments are
+  // acknowledged: each order measured faster for its own chunk length.
+  constexpr bool kYEarly = KS <= 16;
+  const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
+  const uint32_t yo0 = (uint32_t)((p.offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
+  uint32_t yrow = (uint32_t)(tok[0] * p.ldy * 2);
+  u32x2 yv[QB];
+  auto load_y0 = [&]() {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const bool ok = p.add && wave + 4 * q < nbm;
+      yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
+    }
+  };
+  if constexpr (kYEarly) load_y0();
   const int rk = p.slot_rank ? min(max(p.slot_rank[slot], 0), R) : R;
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   if (rk == 0) {
@@ -588,7 +661,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
       __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr, fbase + gm * plane + (wave * RB + rb) * 1024,
-                                             0, 16);
+                                             0, 0);
   };
   if (xw) shrink_store(g);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
@@ -604,17 +677,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // y is read once the fragments are acknowledged (an outstanding load would
-  // hold the acknowledgement wait): it streams while the members meet
-  const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
-  const uint32_t yo0 = (uint32_t)((p.offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
-  uint32_t yrow = (uint32_t)(tok[0] * p.ldy * 2);
-  u32x2 yv[QB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const bool ok = p.add && wave + 4 * q < nbm;
-    yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
-  }
+  if constexpr (!kYEarly) load_y0();
   if (G > 1) {
     __shared__ uint32_t missing;
     if (wave == 0) {
@@ -642,8 +705,11 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   }
 
   // ---- expand, token block by token block: u = scale * (members' partials
-  // in member order) as bf16 hi + lo operands; every column block of this
-  // wave (a block past the member's share reads block 0 and stores nothing)
+  // in the gather's fixed order) as bf16 hi + lo operands; every column block
+  // of this wave (a block past the member's share reads block 0 and stores
+  // nothing).  Each block's y is stored as soon as its two products are done:
+  // that measured faster than issuing every product first, and than one
+  // 16x16x32 product with hi and lo as the two halves of K.
   // B^T operands first: their LDS reads overlap the gather's loads
   s16x4 bw[QB][RB];
 #pragma unroll
@@ -654,22 +720,20 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   }
   for (int t = 0; t < nb; ++t) {
     s16x4 uh[RB], ul[RB];
+    {
+      uint32_t off[RB];
 #pragma unroll
-    for (int c = 0; c < RB; ++c) {
-      const uint32_t off = fbase + (t * RB + c) * 1024;
-      f32x4 u;
-      switch (p.gsh) {
-        case 0: u = gather_partials<1>(pr, off, plane); break;
-        case 1: u = gather_partials<2>(pr, off, plane); break;
-        case 2: u = gather_partials<4>(pr, off, plane); break;
-        case 3: u = gather_partials<8>(pr, off, plane); break;
-        default: u = gather_partials<16>(pr, off, plane); break;
+      for (int c = 0; c < RB; ++c) off[c] = fbase + (t * RB + c) * 1024;
+      f32x4 u[RB];
+      gather_members<RB>(pr, off, plane, p.gsh, RB, reinterpret_cast<f32x4 *>(split_lds), u);
+#pragma unroll
+      for (int c = 0; c < RB; ++c) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(sc * u[c][e], h[e], l[e]);
+        uh[c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
       }
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split_bf16(sc * u[e], h[e], l[e]);
-      uh[c] = __builtin_bit_cast(s16x4, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-      ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
     }
     const bool rok = 16 * t + l16 < rows;
 #pragma unroll
@@ -694,6 +758,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
         const bool ok = p.add && wave + 4 * q < nbm;
         yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
       }
+      __syncthreads();  // every wave has read the gather's LDS
     }
   }
 }
@@ -896,7 +961,9 @@ static hipError_t launch_split1(const MetaView &meta, const SplitParams &sp, con
   const int64_t x_rows = (meta.T + meta.x_row_div - 1) / meta.x_row_div;
   const int64_t x_bytes = ((x_rows - 1) * sp.ldx + sp.d_in) * 2;
   const int64_t y_bytes = ((meta.T - 1) * sp.ldy + sp.offset[0] + width[0]) * 2;
-  if (x_bytes >= ((int64_t)1 << 32) || y_bytes >= ((int64_t)1 << 32)) return hipSuccess;
+  // offsets from 0x7FFFFFF0 up must lie past both resources (pieces and
+  // stores that are not wanted are sent there)
+  if (x_bytes > 0x7FFFFFF0LL || y_bytes > 0x7FFFFFF0LL) return hipSuccess;
   // ranks up to 16 also take 1024-row chunks (32 steps), so that d_in up to
   // 16384 splits 16 ways
   const int kc_max = R <= 16 ? 1024 : 512;
