@@ -578,8 +578,10 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const int xrow = 16 * wave + l16 < rows ? (p.x_row_div == 1 ? xt : xt / p.x_row_div) : 0;
   const rsrc_t xr = make_rsrc(p.x, p.x_bytes);
   u32x4 xa[KS];
-  auto load_x = [&](int gm) {  // member gm's x fragments of this wave's token block
-    const uint32_t xo = xw ? (uint32_t)((xrow * p.ldx + gm * KC + 8 * kg) * 2) : kOut;
+  // member gm's x fragments of this wave's token block; rows past the tile
+  // read zeros (their partial rows are never stored)
+  auto load_x = [&](int gm) {
+    const uint32_t xo = xw && 16 * wave + l16 < rows ? (uint32_t)((xrow * p.ldx + gm * KC + 8 * kg) * 2) : kOut;
 #pragma unroll
     for (int i = 0; i < KS; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
   };
