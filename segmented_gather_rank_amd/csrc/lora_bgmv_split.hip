@@ -523,6 +523,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   constexpr int RB = RP / 16;
   constexpr int LDA = RP == 64 ? 80 : RP;
   constexpr int KC = 32 * KS;                               // k rows per member
+  constexpr int KQ = KS / 4;                                // k-steps per wave in a one-block tile
   constexpr int NPA = KC * R / 8;                           // A pieces of the chunk
   constexpr int NA = (NPA + kSThreads - 1) / kSThreads;     // ... per thread
   constexpr int NBQ = (RP == 64 ? 16 : kSMaxBpm) * 2 * RP / kSThreads;  // B pieces per thread, at most
@@ -573,17 +574,29 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     }
   };
   load_a(g);
-  const bool xw = wave < nb;
-  const int xt = wave == 0 ? tok[0] : (wave == 1 ? tok[1] : (wave == 2 ? tok[2] : tok[3]));
-  const int xrow = 16 * wave + l16 < rows ? (p.x_row_div == 1 ? xt : xt / p.x_row_div) : 0;
+  // the shrink: up to rank 32, a tile of one 16-row block (decode) spreads
+  // its k-steps over the four waves, wave w taking steps w KQ .. + KQ - 1; a
+  // taller tile, or rank 64, gives wave t every step of token block t
+  const bool one = RB <= 2 && nb == 1;
+  const int blk = one ? 0 : wave;
+  const bool xw = blk < nb;
+  const int xt = blk == 0 ? tok[0] : (blk == 1 ? tok[1] : (blk == 2 ? tok[2] : tok[3]));
+  const int xrow = 16 * blk + l16 < rows ? (p.x_row_div == 1 ? xt : xt / p.x_row_div) : 0;
   const rsrc_t xr = make_rsrc(p.x, p.x_bytes);
   u32x4 xa[KS];
-  // member gm's x fragments of this wave's token block; rows past the tile
-  // read zeros (their partial rows are never stored)
+  // member gm's x fragments of this wave's steps; rows past the tile read
+  // zeros (their partial rows are never stored)
   auto load_x = [&](int gm) {
-    const uint32_t xo = xw && 16 * wave + l16 < rows ? (uint32_t)((xrow * p.ldx + gm * KC + 8 * kg) * 2) : kOut;
+    const uint32_t xo = xw && 16 * blk + l16 < rows
+                            ? (uint32_t)((xrow * p.ldx + gm * KC + (one ? 32 * KQ * wave : 0) + 8 * kg) * 2)
+                            : kOut;
+    if (one) {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
+      for (int i = 0; i < KQ; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KS; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
+    }
   };
   load_x(g);
   const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(p.B) + (int64_t)slot * p.b_stride,
@@ -638,34 +651,62 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   stage_a();
   __syncthreads();
 
-  // ---- shrink: wave t, all k-steps of token block t (D' = A^T x^T, so that
-  // lane (token l16, kg) ends with ranks 4 kg .. + 3 of its token)
+  // ---- shrink (D' = A^T x^T, so that lane (token l16, kg) ends with ranks
+  // 4 kg .. + 3 of its token)
   const rsrc_t pr = make_rsrc(p.part, p.part_bytes);
   const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 1024 + lane * 16);
   const uint32_t plane = (uint32_t)(p.n_frag * RB * 1024);  // between members
-  // member gm's partial rows of token block `wave`, from the staged A chunk
-  // and xa, into member gm's slot.  Two accumulator chains (even and odd
-  // k-steps) added at the end: the MFMAs of one chain wait for each other,
-  // the two chains do not.
+  // member gm's partial rows, from the staged A chunk and xa, into member
+  // gm's slot.  Two accumulator chains (even and odd k-steps) added at the
+  // end: the MFMAs of one chain wait for each other, the two chains do not.
+  // A one-block tile's four waves add their sums in wave order through LDS
+  // (RB x 4 waves x 64 lanes, a region of its own after the B chunk), and
+  // wave 0 stores them.  Called by every wave.
+  f32x4 *const red = reinterpret_cast<f32x4 *>(split_lds + p.bs_off + RP * p.ldb * 2);
   auto shrink_store = [&](int gm) {
     f32x4 acc[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[0][rb] = acc[1][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int kleft = p.d_in - gm * KC - 8 * kg;  // x values of this lane past d_in are dropped
+    // x values of this lane past d_in are dropped
+    const int kleft = p.d_in - gm * KC - (one ? 32 * KQ * wave : 0) - 8 * kg;
+    if (one) {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      const u32x4 xv = p.x_full || 32 * i < kleft ? xa[i] : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < KQ; ++i) {
+        const u32x4 xv = p.x_full || 32 * i < kleft ? xa[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[i & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              lds_col8(As, LDA, 32 * (KQ * wave + i) + 8 * kg, 16 * rb), __builtin_bit_cast(bf16x8, xv), acc[i & 1][rb],
+              0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) red[(rb * 4 + wave) * kWave + lane] = acc[0][rb] + acc[1][rb];
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 *r4 = red + rb * 4 * kWave + lane;
+          __builtin_amdgcn_raw_buffer_store_b128(((r4[0] + r4[kWave]) + r4[2 * kWave]) + r4[3 * kWave], pr,
+                                                 fbase + gm * plane + rb * 1024, 0, 0);
+        }
+      }
+    } else if (xw) {
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        const u32x4 xv = p.x_full || 32 * i < kleft ? xa[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[i & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_col8(As, LDA, 32 * i + 8 * kg, 16 * rb),
+                                                                   __builtin_bit_cast(bf16x8, xv), acc[i & 1][rb], 0, 0,
+                                                                   0);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        acc[i & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_col8(As, LDA, 32 * i + 8 * kg, 16 * rb),
-                                                                 __builtin_bit_cast(bf16x8, xv), acc[i & 1][rb], 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr,
+                                               fbase + gm * plane + (wave * RB + rb) * 1024, 0, 0);
     }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr, fbase + gm * plane + (wave * RB + rb) * 1024,
-                                             0, 0);
   };
-  if (xw) shrink_store(g);
+  shrink_store(g);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
 #pragma unroll
   for (int i = 0; i < NBQ; ++i) {
@@ -693,11 +734,11 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     for (uint32_t m = missing; m; m &= m - 1) {
       const int gm = __builtin_ctz(m);
       load_a(gm);
-      if (xw) load_x(gm);
+      load_x(gm);
       __syncthreads();  // the A chunk's LDS is free
       stage_a();
       __syncthreads();
-      if (xw) shrink_store(gm);
+      shrink_store(gm);
     }
     if (missing) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -897,12 +938,14 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
   constexpr int RP = R < 16 ? 16 : R, LDA = RP == 64 ? 80 : RP;
   const void *fn = reinterpret_cast<const void *>(&bgmv_split1_kernel<R, KS>);
   constexpr int ri = (R == 8 ? 0 : (R == 16 ? 1 : (R == 32 ? 2 : 3))) * 4 + (KS == 4 ? 0 : (KS == 8 ? 1 : (KS == 16 ? 2 : 3)));
+  // the one-block shrink's sums (up to rank 32), after the B chunk
+  constexpr size_t kRed = RP <= 32 ? (size_t)(RP / 16) * 4 * kWave * 16 : 0;
   pl.bs_off = (32 * KS * LDA * 2 + 15) / 16 * 16;
-  pl.lds = pl.bs_off + (size_t)RP * pl.ldb * 2;
+  pl.lds = pl.bs_off + (size_t)RP * pl.ldb * 2 + kRed;
   // the residency count is cached per device and taken at this
   // instantiation's largest LDS, which the function is allowed first
   const size_t lds_max = (size_t)32 * KS * LDA * 2 +
-                         (size_t)RP * split_ldb(std::min(kSMaxBpm, kSPieces / (2 * RP))) * 2;
+                         (size_t)RP * split_ldb(std::min(kSMaxBpm, kSPieces / (2 * RP))) * 2 + kRed;
   if (lds_max > 65536) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
     if (e != hipSuccess) return e;

@@ -71,10 +71,11 @@ def test_split_decode_parity(L, r, add):
     check_flags(meta, 1)
 
 
-@pytest.mark.parametrize("d_in,r", [(14336, 16), (3000, 8), (5000, 32)])
+@pytest.mark.parametrize("d_in,r", [(14336, 16), (3000, 8), (5000, 32), (4096, 64), (1024, 64)])
 def test_split_long_rows(L, d_in, r):
     """d_in that splits into 1024-row chunks (rank <= 16) or into chunks that
-    do not tile it exactly (the tail of the last member's chunk reads zeros)."""
+    do not tile it exactly (the tail of the last member's chunk reads zeros);
+    one slice at rank 64."""
     c = decode_case(560 + r, r, d_in=d_in, widths=(1024,))
     print(f"[split-long] {c.name} d_in={d_in}", flush=True)
     d = DevCase(c)
