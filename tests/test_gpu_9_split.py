@@ -137,6 +137,24 @@ def test_split_large_tiles(L):
         check_flags(meta, 1)
 
 
+@pytest.mark.parametrize("r", [16, 32, 64])
+def test_split_large_tiles_one_slice(L, r):
+    """The one-slice kernel on tiles of 2..4 token blocks (each wave shrinks
+    its own block over the whole chunk) beside one-token tiles (the four
+    waves split the chunk), with d_in that the chunks do not tile exactly."""
+    rng = np.random.Generator(np.random.PCG64(615 + r))
+    lengths = np.array([17, 33, 64, 65, 130, 1, 1, 48, 20, 1, 1, 1], np.int64)
+    req = np.array([0, 1, 2, 3, 4, 5, -1, 6, 7, 8, 9, 10], np.int32)
+    c = W.make_case(name=f"split_big_tiles_1s_r{r}", seed=615 + r, rng=rng, dtype="bf16", lengths=lengths,
+                    req_slot=req, num_slots=12, d_in=1000, r_max=r, widths=[520], scale=1.0, weight_sd=0.05)
+    d = DevCase(c)
+    for add in (True, False):
+        print(f"[split-big-1s] r={r} add={add}", flush=True)
+        y, meta = d.apply(L, mode="bgmv", add=add)
+        check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
+        check_flags(meta, 1)
+
+
 @pytest.mark.parametrize("add", [True, False])
 def test_split_slot_ranks(L, add):
     """Per-slot ranks, one of them 0: that slot's rows are left as they are
