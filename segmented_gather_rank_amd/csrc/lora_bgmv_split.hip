@@ -137,28 +137,34 @@ __device__ __forceinline__ uint32_t split_wait(uint32_t *fl, uint32_t f, int g, 
 // additions run in one fixed order for every member of a tile, so all of them
 // get the same bits, and each fragment crosses from L2 once per workgroup, not
 // once per wave.  Only the first nf fragments are gathered (the others come
-// out as zeros).  stage: nf * 4 * 64 f32x4 of LDS that no wave uses on entry;
-// it is read until every wave has its u, so the caller passes a barrier before
-// writing it again.
+// out as zeros).  At most 16 loads a lane are in flight (64 registers): more
+// fragments go in chunks.  stage: nf * 4 * 64 f32x4 of LDS that no wave uses
+// on entry; it is read until every wave has its u, so the caller passes a
+// barrier before writing it again.
 template <int MG, int NF>
 __device__ __forceinline__ void gather_waves(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int G, int nf,
                                              f32x4 *stage, f32x4 (&u)[NF]) {
+  constexpr int FC = 16 / MG < NF ? 16 / MG : NF;  // fragments per chunk
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  f32x4 v[NF][MG];
 #pragma unroll
-  for (int i = 0; i < MG; ++i) {
-    const int gm = wave * MG + i;
+  for (int f0 = 0; f0 < NF; f0 += FC) {
+    f32x4 v[FC][MG];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      v[f][i] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, gm < G ? off[f] + gm * plane : 0x7FFFFFF0u, 0, 16));
-  }
+    for (int i = 0; i < MG; ++i) {
+      const int gm = wave * MG + i;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    f32x4 w = v[f][0];
+      for (int f = 0; f < FC; ++f)
+        v[f][i] = f0 + f < NF ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              pr, gm < G ? off[f0 + f] + gm * plane : 0x7FFFFFF0u, 0, 16))
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-    for (int i = 1; i < MG; ++i) w += v[f][i];
-    if (f < nf) stage[(f * 4 + wave) * kWave + lane] = w;
+    for (int f = 0; f < FC; ++f) {
+      f32x4 w = v[f][0];
+#pragma unroll
+      for (int i = 1; i < MG; ++i) w += v[f][i];
+      if (f0 + f < nf) stage[((f0 + f) * 4 + wave) * kWave + lane] = w;
+    }
   }
   __syncthreads();
 #pragma unroll
