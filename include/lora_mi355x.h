@@ -88,12 +88,13 @@ typedef struct lora_weight {
  *                   unspecified).  Tiles follow the order of `sorted`; there
  *                   are num_tiles <= ceil(T / 64) + S + 1 of them.  The compute
  *                   kernels take their work from this list.
- *   sync            16 uint32 per possible tile, then 16 more: rendezvous
- *                   flags of the decode-shaped lora_apply (below), set to 0
- *                   here; the word after the tiles' flags counts waits that
- *                   gave up (a workgroup that waited for its peers past the
- *                   spin limit computed their share itself: the result is the
- *                   same, only slower)
+ *   sync            64 uint32 per possible tile (four ranges of 16, one per
+ *                   output slice that runs side by side), then 64 more:
+ *                   rendezvous flags of the decode-shaped lora_apply (below),
+ *                   set to 0 here; the word after the tiles' flags counts
+ *                   waits that gave up (a workgroup that waited for its peers
+ *                   past the spin limit computed their share itself: the
+ *                   result is the same, only slower)
  * The struct stays valid until its workspace is reused; rebuild it whenever
  * token_slot changes.  Pass it by pointer to the compute calls.  lora_shrink
  * and lora_expand only read it, so any number of them may use one lora_meta at

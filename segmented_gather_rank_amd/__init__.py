@@ -95,7 +95,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 5:
+if _lib.lora_abi_version() != 6:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -148,7 +148,8 @@ def _weights(ws, name: str, inner_shape_ok) -> tuple:
 
 
 TILE_ROWS = 64          # sorted positions per work tile of the metadata
-SPLIT_MEMBERS = 16  # rendezvous flag words per work tile
+SPLIT_MEMBERS = 16  # rendezvous flag words per work tile and slice range
+SPLIT_FLAG_WORDS = 64  # per work tile: four ranges
 TILE_INTS = 4 + TILE_ROWS
 
 
@@ -194,13 +195,13 @@ class LoraMeta:
                     seg_count=self._view(self.c.seg_count, S + 1),
                     seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 8),
                     tiles=self._view(self.c.tiles, TILE_INTS * max_tiles(T, S)).view(-1, TILE_INTS),
-                    sync=self._view(self.c.sync, SPLIT_MEMBERS * (max_tiles(T, S) + 1)))
+                    sync=self._view(self.c.sync, SPLIT_FLAG_WORDS * (max_tiles(T, S) + 1)))
 
     def split_wait_timeouts(self) -> int:
         """Waits of the split decode kernel that gave up (0 in normal runs).
         Synchronises with the device."""
         T, S = self.num_tokens, self.num_slots
-        return int(self._view(self.c.sync, SPLIT_MEMBERS * (max_tiles(T, S) + 1))[SPLIT_MEMBERS * max_tiles(T, S)].item())
+        return int(self._view(self.c.sync, SPLIT_FLAG_WORDS * (max_tiles(T, S) + 1))[SPLIT_FLAG_WORDS * max_tiles(T, S)].item())
 
 
 def lora_meta_workspace_bytes(num_tokens: int, num_slots: int) -> int:

@@ -56,7 +56,7 @@ namespace {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

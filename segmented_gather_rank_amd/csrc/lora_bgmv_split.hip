@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   int tok[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) tok[q] = tl[4 + 16 * q + l16];
-  uint32_t *fl = flags + (int64_t)ti * kSplitMembers;
+  uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords;  // the first range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
   const int gb0 = g * p.bpm;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   if (G > 1) {
     __shared__ uint32_t missing;
     if (wave == 0) {
-      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitMembers);
+      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitFlagWords);
       if (lane == 0) missing = m;
     }
     __syncthreads();
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   int tok[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) tok[q] = tl[4 + 16 * q + l16];
-  uint32_t *fl = flags + (int64_t)ti * kSplitMembers;
+  uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords;  // the first range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
   const int gb0 = g * p.bpm;
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   if (G > 1) {
     __shared__ uint32_t missing;
     if (wave == 0) {
-      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitMembers);
+      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitFlagWords);
       if (lane == 0) missing = m;
     }
     __syncthreads();

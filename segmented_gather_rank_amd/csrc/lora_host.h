@@ -53,10 +53,13 @@ struct ShrinkConfig {
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);
 size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32_t R);
 
-// Rendezvous flags of the split decode kernel: kSplitMembers words per work
-// tile, then one row whose first word counts waits that gave up.
+// Rendezvous flags of the split decode kernel: per work tile one range of
+// kSplitMembers words for each of up to kSplitRanges slices that run side by
+// side, then one row whose first word counts waits that gave up.
 constexpr int kSplitMembers = 16;
-inline int64_t sync_words(int64_t T, int32_t S) { return kSplitMembers * (max_tiles(T, S) + 1); }
+constexpr int kSplitRanges = 4;
+constexpr int kSplitFlagWords = kSplitMembers * kSplitRanges;  // per tile
+inline int64_t sync_words(int64_t T, int32_t S) { return kSplitFlagWords * (max_tiles(T, S) + 1); }
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,

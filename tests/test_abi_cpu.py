@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 5
+    assert L.lora_abi_version() == 6
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"

@@ -13,7 +13,8 @@ from gpu_util import TOL, DevCase, check_rows, from_dev, oracle_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MEMBERS = 16
+MEMBERS = 16           # flag words per slice range
+RANGES = 4             # slice ranges per work tile
 
 
 @pytest.fixture(scope="module")
@@ -45,15 +46,18 @@ def live_tiles(meta):
 
 
 def tile_flags(meta):
-    return meta.tensors()["sync"].cpu().numpy().view(np.uint32).reshape(-1, MEMBERS)
+    """[tiles + 1][range][word]"""
+    return meta.tensors()["sync"].cpu().numpy().view(np.uint32).reshape(-1, RANGES, MEMBERS)
 
 
-def check_flags(meta, calls):
-    """Every word of a live tile equals the number of split calls; the others
-    were never touched; no wait gave up."""
+def check_flags(meta, calls, ranges=1):
+    """Every word of the first `ranges` slice ranges of a live tile equals the
+    number of split calls; the other words were never touched; no wait gave
+    up."""
     f = tile_flags(meta)
     live, n = live_tiles(meta)
-    assert (f[live] == calls).all(), f[live]
+    assert (f[live, :ranges] == calls).all(), f[live]
+    assert (f[live, ranges:] == 0).all()
     dead = np.setdiff1d(np.arange(f.shape[0] - 1), live)
     assert (f[dead] == 0).all()
     assert meta.split_wait_timeouts() == 0
@@ -117,8 +121,8 @@ def test_split_calls_share_one_meta(L):
             check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), f"{c.name} rep {rep}")
     f = tile_flags(meta)
     live, _ = live_tiles(meta)
-    assert (f[live] == f[live][:, :1]).all()
-    assert (f[live] >= 1).all()
+    assert (f[live] == f[live][:, :, :1]).all()  # each range's words stay equal
+    assert (f[live, 0] >= 1).all()
     assert meta.split_wait_timeouts() == 0
 
 
