@@ -112,31 +112,39 @@ def dominant_kernel(c, mode):
     sw = sum(c.widths)
     e = 4 if c.dtype == "f32" else 2
     w_tok = (c.n_slices * c.d_in + sw) * c.r_max * e
-    fused = (os.environ.get("LORA_DISABLE_FUSED_BGMV", "0") in ("", "0") and mode != "sgmv" and sw // 8 <= 1024 and c.d_in * e <= 32768 and w_tok <= (1 << 20)
-             and (mode == "bgmv" or c.T <= 16 * c.num_slots))
-    if fused:
-        return "bgmv_split" if split_takes(c) else "bgmv_fused_kernel"
+    enabled = os.environ.get("LORA_DISABLE_FUSED_BGMV", "0") in ("", "0")
+    decode = mode != "sgmv" and (mode == "bgmv" or c.T <= 16 * c.num_slots)
+    if enabled and decode and split_takes(c):
+        return "bgmv_split"
+    if enabled and decode and sw // 8 <= 1024 and c.d_in * e <= 32768 and w_tok <= (1 << 20):
+        return "bgmv_fused_kernel"
     return "shrink+expand"
 
 
 def split_takes(c):
     """Whether a decode-shaped call runs the split kernel (each work tile spread
     over several workgroups): bf16, and some member count of at most 16 gives
-    every member an A chunk (<= 512 rows, <= 1024 for one slice at rank <= 16)
-    and a B share that fit its LDS."""
+    every member an A chunk and a B share that fit its LDS.  Up to four slices
+    run side by side (one slice per workgroup: A chunk <= 512 rows, 1024 at
+    rank <= 16; the widest slice sets the B share); more slices share each
+    workgroup (every slice's A chunk, <= 512 rows)."""
     if c.dtype != "bf16" or os.environ.get("LORA_DISABLE_SPLIT_BGMV", "0") not in ("", "0"):
         return False
     rp = max(16, c.r_max)
-    nsb = 1 << (c.n_slices - 1).bit_length()
-    if nsb * (rp // 16) > 8 or c.T * c.n_slices * rp > (1 << 17):
+    if c.T * c.n_slices * rp > (1 << 17):
         return False
-    nbt = sum((w + 15) // 16 for w in c.widths)
+    side = c.n_slices <= 4
+    if not side and (1 << (c.n_slices - 1).bit_length()) * (rp // 16) > 8:
+        return False
+    blocks = [(w + 15) // 16 for w in c.widths]
+    nbt = max(blocks) if side else sum(blocks)
+    a_slices = 1 if side else c.n_slices
+    kc_max = 1024 if side and c.r_max <= 16 else 512
     g = 1
     while g <= 16:
         kc = max(128, 1 << max(0, (-(-c.d_in // g) - 1).bit_length()))
         bpm = -(-nbt // g)
-        kc_max = 1024 if c.n_slices == 1 and c.r_max <= 16 else 512
-        if kc <= kc_max and c.n_slices * kc * (rp // 8) <= 2048 and bpm <= 32 and bpm * 2 * rp <= 2048:
+        if kc <= kc_max and a_slices * kc * (rp // 8) <= 2048 and bpm <= 32 and bpm * 2 * rp <= 2048:
             return True
         g *= 2
     return False

@@ -355,16 +355,20 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   unpack(B, n_slices, bptr, bstr);
   const MetaView mv = view_of(meta);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  // decode-shaped (BGMV requested, or few tokens per slot): the split kernel
+  // first (bf16; it checks its own limits), then the per-token kernel when
+  // its limits hold
+  const bool decode = (int)mode != 2 && ((int)mode == 1 || meta->num_tokens <= 16 * (int64_t)meta->num_slots);
+  if (!fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
+    bool used = false;
+    const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
+                                           r_max, scale, d_slot_scale, d_slot_rank, d_y, ldy, add_into_y,
+                                           static_cast<float *>(sh_ws), ws_bytes - ubytes, s, &used);
+    if (e != hipSuccess) return LORA_ERR_HIP;
+    if (used) return LORA_OK;
+  }
   if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
                                      r_max, ldy, dtype == LORA_BF16, (int)mode)) {
-    if (dtype == LORA_BF16 && !split_disabled()) {
-      bool used = false;
-      const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
-                                             r_max, scale, d_slot_scale, d_slot_rank, d_y, ldy, add_into_y,
-                                             static_cast<float *>(sh_ws), ws_bytes - ubytes, s, &used);
-      if (e != hipSuccess) return LORA_ERR_HIP;
-      if (used) return LORA_OK;
-    }
     const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
                                      bptr, bstr, width, offset, r_max, scale, d_slot_scale,
                                      d_slot_rank, d_y, ldy, add_into_y, s);

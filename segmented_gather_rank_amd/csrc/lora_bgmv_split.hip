@@ -497,26 +497,44 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
 // workgroup runs this code once, so its length is its latency.
 
 struct Split1Params {
-  const void *x, *A, *B;
+  const void *x;
   void *y;
   float *part;
   const float *slot_scale;
   const int32_t *slot_rank;
-  int64_t a_stride, b_stride;
-  uint32_t x_bytes, y_bytes, part_bytes;
-  int32_t ldx, d_in, x_row_div, ldy, width, offset, nbt;
-  int32_t gsh, ksh, bpm, ldb, bs_off, max_tiles, n_frag, spin_limit, add, x_full;
+  uint32_t x_bytes, y_bytes, part_bytes, part_slice;  // part_slice: bytes between slices' partials
+  int32_t ldx, d_in, x_row_div, ldy;
+  int32_t gsh, ksh, ldb, bs_off, max_tiles, n_frag, spin_limit, add, x_full;
   float scale;
 };
 
-// Zero the member's columns of the tile's rows (store mode, no adapter).
-__device__ __forceinline__ void split1_zero(const Split1Params &p, const int32_t *tl, int rows, int gb0, int nbm) {
+// The slices' own values, a kernel argument of their own: it is indexed by
+// the slice at run time, which would otherwise make the compiler load every
+// field of Split1Params at its use instead of once at the start.
+struct Split1Slices {
+  const void *A[kSplitRanges], *B[kSplitRanges];
+  int64_t a_stride[kSplitRanges], b_stride[kSplitRanges];
+  int32_t width[kSplitRanges], offset[kSplitRanges], nbt[kSplitRanges], bpm[kSplitRanges];
+};
+
+// p[s] for a workgroup-uniform s < kSplitRanges: one scalar load from the
+// argument block at an offset known at launch (selecting among all four
+// entries kept every slice's values in scalar registers, which spilled)
+template <typename V>
+__device__ __forceinline__ V sel_slice(const V (&p)[kSplitRanges], int s) {
+  return p[s];
+}
+
+// Zero the member's columns of the tile's rows in the window [offset,
+// offset + width) (store mode, no adapter).
+__device__ __forceinline__ void split1_zero(const Split1Params &p, const int32_t *tl, int rows, int gb0, int nbm,
+                                            int offset, int width) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int row = wave; row < rows; row += kSThreads / kWave) {
-    uint16_t *yr = reinterpret_cast<uint16_t *>(p.y) + (int64_t)tl[4 + row] * p.ldy + p.offset;
+    uint16_t *yr = reinterpret_cast<uint16_t *>(p.y) + (int64_t)tl[4 + row] * p.ldy + offset;
     for (int h = lane; h < 2 * nbm; h += kWave) {
       const int col = 16 * (gb0 + h / 2) + 8 * (h & 1);
-      if (col < p.width) gstore16(yr + col, u32x4{0, 0, 0, 0});
+      if (col < width) gstore16(yr + col, u32x4{0, 0, 0, 0});
     }
   }
 }
@@ -524,7 +542,8 @@ __device__ __forceinline__ void split1_zero(const Split1Params &p, const int32_t
 template <int R, int KS>
 __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t *__restrict__ info,
                                                                 const int32_t *__restrict__ tiles,
-                                                                uint32_t *__restrict__ flags, Split1Params p) {
+                                                                uint32_t *__restrict__ flags, Split1Params p,
+                                                                Split1Slices q) {
   constexpr int RP = R < 16 ? 16 : R;
   constexpr int RB = RP / 16;
   constexpr int LDA = RP == 64 ? 80 : RP;
@@ -543,10 +562,19 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l16 = lane % 16, kg = lane / 16;
   const int G = 1 << p.gsh;
-  const int lb8 = blockIdx.x >> 3;
+  // slices run side by side: slice blockIdx.y is a row of the grid whose
+  // width is a multiple of 8, so blockIdx.x mod 8 still names the XCD (the
+  // grid is dispatched row after row)
+  const int sl = blockIdx.y, lbx = blockIdx.x;
+  const int lb8 = lbx >> 3;
   const int g = lb8 & (G - 1);
-  const int ti = ((lb8 >> p.gsh) << 3) | (blockIdx.x & 7);
+  const int ti = ((lb8 >> p.gsh) << 3) | (lbx & 7);
   if (ti >= p.max_tiles) return;
+  // this slice's values
+  const int width = sel_slice(q.width, sl), offset = sel_slice(q.offset, sl);
+  const int nbt = sel_slice(q.nbt, sl), bpm = sel_slice(q.bpm, sl);
+  const void *a_base = sel_slice(q.A, sl), *b_base = sel_slice(q.B, sl);
+  const int64_t a_stride = sel_slice(q.a_stride, sl), b_stride = sel_slice(q.b_stride, sl);
 
   // ---- first round trip: tile count and header, the tokens of the four
   // 16-row blocks this lane may serve, this member's flag
@@ -556,20 +584,20 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   int tok[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) tok[q] = tl[4 + 16 * q + l16];
-  uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords;  // the first range
+  uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords + kSplitMembers * sl;  // this slice's range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
-  const int gb0 = g * p.bpm;
-  const int nbm = min(p.bpm, p.nbt - gb0);
+  const int gb0 = g * bpm;
+  const int nbm = min(bpm, nbt - gb0);
   if (slot < 0) {
-    if (!p.add) split1_zero(p, tl, rows, gb0, nbm);
+    if (!p.add) split1_zero(p, tl, rows, gb0, nbm, offset, width);
     return;
   }
 
   // ---- second round trip: every load is issued, none behind a branch;
   // pieces that are not needed take an offset past their resource
   const int nb = (rows + 15) >> 4;
-  const rsrc_t ar = make_rsrc(reinterpret_cast<const uint16_t *>(p.A) + (int64_t)slot * p.a_stride,
+  const rsrc_t ar = make_rsrc(reinterpret_cast<const uint16_t *>(a_base) + (int64_t)slot * a_stride,
                               (uint32_t)(p.d_in * R * 2));
   u32x4 av[NA];
   auto load_a = [&](int gm) {  // member gm's A chunk
@@ -605,16 +633,16 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     }
   };
   load_x(g);
-  const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(p.B) + (int64_t)slot * p.b_stride,
-                              (uint32_t)(R * p.width * 2));
+  const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(b_base) + (int64_t)slot * b_stride,
+                              (uint32_t)(R * width * 2));
   u32x4 bv[NBQ];
 #pragma unroll
   for (int i = 0; i < NBQ; ++i) {
     const int q = tid + kSThreads * i;
     const int lb = q / (2 * RP), j = (q >> 1) % RP, half = q & 1;
     const int col = 16 * (gb0 + lb) + 8 * half;
-    const bool ok = lb < nbm && j < R && col < p.width;
-    bv[i] = buf_load16(br, ok ? (uint32_t)((j * p.width + col) * 2) : kOut);
+    const bool ok = lb < nbm && j < R && col < width;
+    bv[i] = buf_load16(br, ok ? (uint32_t)((j * width + col) * 2) : kOut);
   }
   // y of the first token block.  Up to 512-row chunks it is loaded here and
   // arrives with the rest of the batch, so it holds neither the
@@ -623,7 +651,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   // acknowledged: each order measured faster for its own chunk length.
   constexpr bool kYEarly = KS <= 16;
   const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
-  const uint32_t yo0 = (uint32_t)((p.offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
+  const uint32_t yo0 = (uint32_t)((offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
   uint32_t yrow = (uint32_t)(tok[0] * p.ldy * 2);
   u32x2 yv[QB];
   auto load_y0 = [&]() {
@@ -637,7 +665,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const int rk = p.slot_rank ? min(max(p.slot_rank[slot], 0), R) : R;
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   if (rk == 0) {
-    if (!p.add) split1_zero(p, tl, rows, gb0, nbm);
+    if (!p.add) split1_zero(p, tl, rows, gb0, nbm, offset, width);
     return;
   }
   const int rk8 = (rk + 7) & ~7;
@@ -660,7 +688,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   // ---- shrink (D' = A^T x^T, so that lane (token l16, kg) ends with ranks
   // 4 kg .. + 3 of its token)
   const rsrc_t pr = make_rsrc(p.part, p.part_bytes);
-  const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 1024 + lane * 16);
+  const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 1024 + lane * 16) + sl * p.part_slice;
   const uint32_t plane = (uint32_t)(p.n_frag * RB * 1024);  // between members
   // member gm's partial rows, from the staged A chunk and xa, into member
   // gm's slot.  Two accumulator chains (even and odd k-steps) added at the
@@ -717,7 +745,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
 #pragma unroll
   for (int i = 0; i < NBQ; ++i) {
     const int q = tid + kSThreads * i;
-    if (q < 2 * RP * p.bpm) {
+    if (q < 2 * RP * bpm) {
       const int lb = q / (2 * RP), j = (q >> 1) % RP, half = q & 1;
       *reinterpret_cast<u32x4 *>(Bs + j * p.ldb + 16 * lb + 8 * half) = j < rk8 ? bv[i] : u32x4{0, 0, 0, 0};
     }
@@ -796,7 +824,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       const u32x2 old = p.add ? yv[q] : u32x2{0, 0};
       const u32x2 v = {pack_bf16x2(bf16_lo(old[0]) + d[0], bf16_hi(old[0]) + d[1]),
                        pack_bf16x2(bf16_lo(old[1]) + d[2], bf16_hi(old[1]) + d[3])};
-      if (rok && wave + 4 * q < nbm && 16 * (gb0 + wave + 4 * q) + 4 * kg < p.width)
+      if (rok && wave + 4 * q < nbm && 16 * (gb0 + wave + 4 * q) + 4 * kg < width)
         __builtin_amdgcn_raw_buffer_store_b64(v, yr, yrow + yo0 + 128 * q, 0, 0);
     }
     if (t + 1 < nb) {  // y of the next token block
@@ -859,14 +887,20 @@ static size_t split_lds_max(int R, int NS) {
 // (about one workgroup per CU), raised until each member's A chunk and B
 // chunk are at most kSPieces 16-byte pieces.  Not ok when no G <= 16 fits or
 // the partial fragments exceed the workspace.
+// side: the slices run side by side (one slice per workgroup, the one-slice
+// kernel): the A budget is one slice's chunk and the column share is the
+// widest slice's; otherwise one workgroup holds every slice's A chunk and a
+// share of all their column blocks.
 static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices, const int64_t *width,
-                            int32_t R, size_t ws_bytes, int g_cap, int kc_max = 512) {
+                            int32_t R, size_t ws_bytes, int g_cap, int kc_max = 512, bool side = false) {
   SplitPlan pl{};
   const int RP = R < 16 ? 16 : R, RB = RP / 16;
   const int NSb = n_slices <= 1 ? 1 : (n_slices <= 2 ? 2 : (n_slices <= 4 ? 4 : 8));
-  if (NSb * RB > 8 || split_ws_bytes(T, S, n_slices, R) == 0) return pl;
+  if ((side ? n_slices > kSplitRanges : NSb * RB > 8) || split_ws_bytes(T, S, n_slices, R) == 0) return pl;
   int64_t nbt = 0;
-  for (int s = 0; s < n_slices; ++s) nbt += (width[s] + 15) / 16;
+  for (int s = 0; s < n_slices; ++s)
+    nbt = side ? std::max<int64_t>(nbt, (width[s] + 15) / 16) : nbt + (width[s] + 15) / 16;
+  const int a_slices = side ? 1 : n_slices;
   const int64_t mt = max_tiles(T, S);
   const int64_t est = std::min<int64_t>(mt, T);  // live tiles, at most
   int G = 1;
@@ -876,7 +910,7 @@ static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices
     if (G > kSplitMembers || G > g_cap) return pl;
     const int64_t kc = std::max<int64_t>(128, (int64_t)1 << ilog2((d_in + G - 1) / G));
     const int64_t bpm = (nbt + G - 1) / G;
-    if (kc <= kc_max && (int64_t)n_slices * kc * (RP / 8) <= kSPieces && bpm <= kSMaxBpm && bpm * 2 * RP <= kSPieces) {
+    if (kc <= kc_max && (int64_t)a_slices * kc * (RP / 8) <= kSPieces && bpm <= kSMaxBpm && bpm * 2 * RP <= kSPieces) {
       pl.ksh = ilog2(kc);
       pl.bpm = (int)bpm;
       break;
@@ -884,9 +918,9 @@ static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices
   }
   pl.G = G;
   pl.ldb = split_ldb(pl.bpm);
-  pl.bs_off = (int)split_region1(n_slices, (int64_t)1 << pl.ksh, R);
+  pl.bs_off = (int)split_region1(a_slices, (int64_t)1 << pl.ksh, R);
   pl.lds = pl.bs_off + (size_t)RP * pl.ldb * 2;
-  pl.grid = (int)(8 * G * ((mt + 7) / 8));
+  pl.grid = (int)(8 * G * ((mt + 7) / 8)) * (side ? n_slices : 1);
   const size_t need = (size_t)G * ((T + 15) / 16 + mt) * n_slices * RB * 1024;
   if (need > ws_bytes) return pl;
   pl.ok = true;
@@ -967,15 +1001,24 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
   }
   *used = true;
   Split1Params p{};
+  Split1Slices q{};
   p.x = sp.x;
-  p.A = sp.A[0];
-  p.B = sp.B[0];
+  const int RB = RP / 16;
+  for (int s = 0; s < sp.n_slices; ++s) {
+    q.A[s] = sp.A[s];
+    q.B[s] = sp.B[s];
+    q.a_stride[s] = sp.a_stride[s];
+    q.b_stride[s] = sp.b_stride[s];
+    q.width[s] = (int32_t)width[s];
+    q.offset[s] = (int32_t)sp.offset[s];
+    q.nbt[s] = sp.blk_base[s + 1] - sp.blk_base[s];
+    q.bpm[s] = (q.nbt[s] + pl.G - 1) / pl.G;
+  }
+  p.part_slice = (uint32_t)((size_t)pl.G * sp.n_frag * RB * 1024);
   p.y = sp.y;
   p.part = sp.part;
   p.slot_scale = sp.slot_scale;
   p.slot_rank = sp.slot_rank;
-  p.a_stride = sp.a_stride[0];
-  p.b_stride = sp.b_stride[0];
   p.x_bytes = x_bytes;
   p.y_bytes = y_bytes;
   p.part_bytes = sp.part_bytes;
@@ -983,12 +1026,8 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
   p.d_in = (int32_t)sp.d_in;
   p.x_row_div = sp.x_row_div;
   p.ldy = (int32_t)sp.ldy;
-  p.width = (int32_t)width[0];
-  p.offset = (int32_t)sp.offset[0];
-  p.nbt = sp.blk_base[1];
   p.gsh = ilog2(pl.G);
   p.ksh = pl.ksh;
-  p.bpm = pl.bpm;
   p.ldb = pl.ldb;
   p.bs_off = pl.bs_off;
   p.max_tiles = sp.max_tiles;
@@ -997,21 +1036,23 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
   p.add = sp.add;
   p.x_full = ((int64_t)pl.G << pl.ksh) == sp.d_in ? 1 : 0;
   p.scale = sp.scale;
-  hipLaunchKernelGGL((bgmv_split1_kernel<R, KS>), dim3(pl.grid), dim3(kSThreads), pl.lds, stream, meta.info,
-                     meta.tiles, meta.sync, p);
+  hipLaunchKernelGGL((bgmv_split1_kernel<R, KS>), dim3(pl.grid / sp.n_slices, sp.n_slices), dim3(kSThreads), pl.lds,
+                     stream, meta.info, meta.tiles, meta.sync, p, q);
   return hipGetLastError();
 }
 
-// One slice: plan, then the instantiation for the plan's chunk (128, 256 or
-// 512 rows); when an XCD cannot hold a tile's members, plan again with G
-// halved.
+// One slice, or up to four side by side: plan, then the instantiation for
+// the plan's chunk (128, 256, 512 or 1024 rows); when an XCD cannot hold a
+// tile's members, plan again with G halved.
 template <int R>
 static hipError_t launch_split1(const MetaView &meta, const SplitParams &sp, const int64_t *width,
                                 size_t part_bytes, hipStream_t stream, bool *used) {
   // 32-bit offsets into x and y
   const int64_t x_rows = (meta.T + meta.x_row_div - 1) / meta.x_row_div;
   const int64_t x_bytes = ((x_rows - 1) * sp.ldx + sp.d_in) * 2;
-  const int64_t y_bytes = ((meta.T - 1) * sp.ldy + sp.offset[0] + width[0]) * 2;
+  int64_t y_end = 0;
+  for (int s = 0; s < sp.n_slices; ++s) y_end = std::max(y_end, sp.offset[s] + width[s]);
+  const int64_t y_bytes = ((meta.T - 1) * sp.ldy + y_end) * 2;
   // offsets from 0x7FFFFFF0 up must lie past both resources (pieces and
   // stores that are not wanted are sent there)
   if (x_bytes > 0x7FFFFFF0LL || y_bytes > 0x7FFFFFF0LL) return hipSuccess;
@@ -1019,7 +1060,7 @@ static hipError_t launch_split1(const MetaView &meta, const SplitParams &sp, con
   // 16384 splits 16 ways
   const int kc_max = R <= 16 ? 1024 : 512;
   for (int g_cap = kSplitMembers; g_cap >= 1; g_cap /= 2) {
-    const SplitPlan pl = plan_split(meta.T, meta.S, sp.d_in, 1, width, R, part_bytes, g_cap, kc_max);
+    const SplitPlan pl = plan_split(meta.T, meta.S, sp.d_in, sp.n_slices, width, R, part_bytes, g_cap, kc_max, true);
     if (!pl.ok) return hipSuccess;
     bool too_many = false;
     hipError_t e = hipSuccess;
@@ -1089,14 +1130,17 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
   p.ldy = ldy;
   p.add = add ? 1 : 0;
   p.part = part;
-  // ldx and ldy also enter 32-bit offsets on the one-slice path
-  if (n_slices == 1 && ldx < ((int64_t)1 << 31) && ldy < ((int64_t)1 << 31)) {
+  // one slice, or up to four side by side, on the one-slice kernel (ldx and
+  // ldy also enter its 32-bit offsets); else every slice in one workgroup
+  if (n_slices <= kSplitRanges && ldx < ((int64_t)1 << 31) && ldy < ((int64_t)1 << 31)) {
+    hipError_t e = hipSuccess;
     switch (R) {
-      case 8: return launch_split1<8>(meta, p, width, part_bytes, stream, used);
-      case 16: return launch_split1<16>(meta, p, width, part_bytes, stream, used);
-      case 32: return launch_split1<32>(meta, p, width, part_bytes, stream, used);
-      case 64: return launch_split1<64>(meta, p, width, part_bytes, stream, used);
+      case 8: e = launch_split1<8>(meta, p, width, part_bytes, stream, used); break;
+      case 16: e = launch_split1<16>(meta, p, width, part_bytes, stream, used); break;
+      case 32: e = launch_split1<32>(meta, p, width, part_bytes, stream, used); break;
+      case 64: e = launch_split1<64>(meta, p, width, part_bytes, stream, used); break;
     }
+    if (e != hipSuccess || *used || n_slices == 1) return e;
   }
   switch (R) {
     case 8: return launch_split_t<8>(meta, p, width, part_bytes, stream, used);

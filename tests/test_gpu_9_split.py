@@ -66,13 +66,12 @@ def check_flags(meta, calls, ranges=1):
 @pytest.mark.parametrize("r", [8, 16, 32, 64])
 @pytest.mark.parametrize("add", [True, False])
 def test_split_decode_parity(L, r, add):
-    # rank 64 takes at most two slices on this path (LDS of the rank rows)
     c = decode_case(500 + r, r, widths=(512, 136) if r == 64 else (512, 256, 136))
     print(f"[split] {c.name} T={c.T} S={c.num_slots} add={add}", flush=True)
     d = DevCase(c)
     y, meta = d.apply(L, mode="auto", add=add)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), c.name)
-    check_flags(meta, 1)
+    check_flags(meta, 1, ranges=len(c.widths))  # the slices run side by side
 
 
 @pytest.mark.parametrize("d_in,r", [(14336, 16), (3000, 8), (5000, 32), (4096, 64), (1024, 64)])
@@ -88,10 +87,21 @@ def test_split_long_rows(L, d_in, r):
     check_flags(meta, 1)
 
 
-def test_split_rank64_three_slices_falls_back(L):
-    """Three slices at rank 64 do not fit the split kernel's LDS: the call runs
-    on the one-workgroup-per-token kernel (flags untouched) and is still right."""
+def test_split_rank64_three_slices_side_by_side(L):
+    """Three slices at rank 64: each workgroup takes one slice, so the LDS of
+    one slice's rank rows is all a workgroup needs."""
     c = decode_case(505, 64)
+    d = DevCase(c)
+    y, meta = d.apply(L)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
+    check_flags(meta, 1, ranges=3)
+
+
+def test_split_five_slices_rank64_falls_back(L):
+    """Five slices at rank 64 fit neither split kernel (at most four slices
+    side by side; the packed-slice kernel's LDS): the call runs on the
+    one-workgroup-per-token kernel (flags untouched) and is still right."""
+    c = decode_case(506, 64, widths=(256, 128, 136, 64, 200))
     d = DevCase(c)
     y, meta = d.apply(L)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
@@ -138,7 +148,7 @@ def test_split_large_tiles(L):
     for add in (True, False):
         y, meta = d.apply(L, mode="bgmv", add=add)
         check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
-        check_flags(meta, 1)
+        check_flags(meta, 1, ranges=2)
 
 
 @pytest.mark.parametrize("r", [16, 32, 64])
