@@ -69,17 +69,20 @@ KERNEL_SOURCES = {   # the sources each measured kernel is built from
 
 
 def source_digest(kernel_key):
-    """Hash of the sources of one kernel (its file, the shared device headers,
-    the C header): a traffic figure is only reported while the kernel it was
-    measured on is unchanged."""
+    """Hash of the code of one kernel (its file, the shared device headers,
+    the C header), comments and blank lines left out: a traffic figure is only
+    reported while the code it was measured on is unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "segmented_gather_rank_amd", "csrc")
     files = [os.path.join(csrc, f) for f in KERNEL_SOURCES[kernel_key] + ["lora_common.h", "lora_host.h"]]
     files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
     for f in files:
+        text = re.sub(r"/\*.*?\*/", "", open(f, encoding="utf-8").read(), flags=re.S)
+        code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update("\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 

@@ -489,8 +489,9 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
 
 // ------------------------------------------------------------------ one slice
 //
-// The same algorithm for a single output slice (separate projections, the
-// common decode case), written for the fewest executed instructions: every
+// The same algorithm for one output slice per workgroup (separate
+// projections, the common decode case; packed slices, up to four, run side by
+// side as rows of the grid), written for the fewest executed instructions: every
 // operand is read through a buffer resource with a uniform base (the slot's A
 // and B matrices, x, y), 32-bit offsets and immediate steps; pieces outside a
 // matrix read as zeros by the resource bound instead of by selects.  A
