@@ -87,6 +87,19 @@ def test_split_long_rows(L, d_in, r):
     check_flags(meta, 1)
 
 
+@pytest.mark.parametrize("r", [16, 32])
+def test_split_packed_qkv_decode_shape(L, r):
+    """Packed q/k/v of a 4096-wide model at decode (256 tokens, 32 slots):
+    three slices side by side, the widest (q, 256 column blocks) setting the
+    member count; every slice checked against the oracle."""
+    c = decode_case(520 + r, r, d_in=4096, widths=(4096, 1024, 1024))
+    print(f"[split-qkv] r={r}", flush=True)
+    d = DevCase(c)
+    y, meta = d.apply(L)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
+    check_flags(meta, 1, ranges=3)
+
+
 def test_split_rank64_three_slices_side_by_side(L):
     """Three slices at rank 64: each workgroup takes one slice, so the LDS of
     one slice's rank rows is all a workgroup needs."""
