@@ -1,23 +1,28 @@
 """Benchmark of the multi-LoRA shrink/expand hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: slot metadata
-(lora_prepare_meta), then shrink and expand (lora_apply; on this decode
-workload a single fused kernel).  The K steps are captured once into a HIP
-graph and the timed region is one replay of it, bracketed by HIP events on the
-launch stream: a serving loop launches these calls the same way, and an eager
-Python loop would time the host's issue rate instead (reported separately).
-Per-call averages come from graphs holding only that call.  Inputs are
-resident in HBM before the timed region starts.  Enough
-copies of the inputs are rotated that consecutive steps never find their data
-in the 256 MB last-level cache (MALL).
+(lora_prepare_meta), then shrink and expand (lora_apply).  The K steps are
+captured once into a HIP graph and the timed region is one replay of it,
+bracketed by HIP events on the launch stream: a serving loop launches these
+calls the same way, and an eager Python loop would time the host's issue rate
+instead (reported separately).  Per-call averages come from graphs holding only
+that call.  Inputs are resident in HBM before the timed region starts, and a
+1 GiB copy runs right before every timed replay, so no timed step finds its
+data in the 256 MB last-level cache (MALL) or the L2s, whatever K is; enough
+copies of the inputs are rotated that consecutive steps of one replay do not
+either.
 
-Default workload: decode (BGMV form) on a q_proj shape, 4096 -> 4096, rank 16,
-32 slots, 256 one-token requests with 10% of them without an adapter, bf16.
+Default workload: prefill (SGMV form) on a fused gate/up shape, 4096 -> 2 x
+14336, rank 64, 8 slots, 16 requests of 128..2048 tokens (17 705 tokens), bf16.
+The decode workloads (q_proj 4096 -> 4096 at rank 16, 256 tokens; down_proj
+14336 -> 4096 at rank 64, 4096 tokens over 128 slots) are measured in the same
+run and reported under "extra", each with its own roofline.
 
 One JSON line on stdout:  value = tokens per second of the whole step (all T
 tokens of the batch, including those without an adapter), plus the roofline
-of the dominant kernel (algorithmic bytes / measured average duration against
-the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample.
+of the dominant call (algorithmic bytes / measured average duration against
+the 8 TB/s HBM peak, with the bf16 matrix-core rate from counters beside it),
+a measured device copy rate, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -38,22 +43,33 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..8 (2 = the headline decode case; 7, 8 = MoE experts' LoRA)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1..8 (3 = prefill gate/up, the headline; 2, 5 = decode; 7, 8 = MoE experts' LoRA)")
+    ap.add_argument("--extra", default="2,5",
+                    help="comma-separated workloads also measured and reported under 'extra' ('' for none)")
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--slot-ranks", action="store_true",
                     help="pass each slot's own rank (the kernels then skip the zero-padded ranks)")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the rotated input copies (beats the 256 MB MALL)")
+    ap.add_argument("--flush-mb", type=float, default=1024.0,
+                    help="size of the copy run before every timed replay (evicts the MALL and the L2s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: every host core)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run under rocprofv3 --pmc: a plain copy of known size, then --steps eager steps")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --pmc-pass (FETCH_SIZE, WRITE_SIZE) into the "
                          "traffic summary under profiles/")
+    ap.add_argument("--summarize-mfma", metavar="MFMA_DIR",
+                    help="turn a rocprofv3 --pmc run of --pmc-pass (SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil) "
+                         "into the matrix-core summary under profiles/")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of this bench (and its JSON line) into "
+                         "the trace summary under profiles/")
     return ap.parse_args()
 
 
@@ -270,70 +286,239 @@ def algorithmic(c, ranked=False):
                 shrink_flops=shrink_flops, expand_flops=expand_flops)
 
 
-def cpu_baseline(c, seconds):
-    """The oracle as it stands (plain C, fp64, one thread) on a bounded sample
-    of the same workload: whole batches, metadata plus every token's delta,
-    repeated until `seconds` have passed (at least one token).  An MoE step is
-    counted in tokens: a token is done when all its top-k pairs are."""
+def _counter_means(d, counter):
+    """Per-kernel lists of one counter's per-dispatch values from a rocprofv3
+    --pmc run (csv output) under directory d."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert f, f"no counter_collection.csv under {d}"
+    vals = {}
+    for r in csv.DictReader(open(f[0])):
+        if r["Counter_Name"] == counter:
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def mfma_file(c):
+    return os.path.join(PROFILES, f"mfma_{c.name}.md")
+
+
+def summarize_mfma(c, k, d, kernel_key):
+    """bf16 matrix-core operations per launch of the dominant call (the sum over
+    its kernels of SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per dispatch) and the
+    derived MfmaUtil (matrix-core busy cycles over all SIMDs and the busy time)."""
+    mops = _counter_means(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    util = _counter_means(d, "MfmaUtil")
+    keys = kernel_keys(kernel_key)
+    rows, flops = [], 0.0
+    for name, v in sorted(mops.items()):
+        if not any(key in name for key in keys):
+            continue
+        f = 512.0 * sum(v) / len(v)
+        u = util.get(name, [float("nan")])
+        flops += f
+        rows.append(f"| `{name[:90]}` | {len(v)} | {f / 1e9:.3f} | {sum(u) / len(u):.2f} |")
+    assert rows, list(mops)
+    alg = algorithmic(c)
+    alg_f = alg["shrink_flops"] + alg["expand_flops"]
+    lines = [
+        f"# bf16 matrix-core work of `{kernel_key}` on workload {c.name}",
+        "",
+        "One rocprofv3 counter run of `bench.py --pmc-pass` (the workload's steps, eager):",
+        "",
+        "```",
+        "export TMPDIR=/tmp",
+        f"rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil -d gpurun_out/pmc_mfma -o p --output-format csv -- "
+        f"python bench.py --config {k} --pmc-pass --steps 20",
+        f"python bench.py --config {k} --summarize-mfma gpurun_out/pmc_mfma",
+        "```",
+        "",
+        "| Kernel | dispatches | bf16 MFMA GFLOP per dispatch (MOPS x 512) | MfmaUtil % |",
+        "|---|---|---|---|",
+        *rows,
+        "",
+        f"Per launch {flops / 1e9:.3f} GFLOP issued on the matrix cores against {alg_f / 1e9:.3f} GFLOP algorithmic "
+        f"({flops / alg_f:.2f}x: the expand multiplies the rank-r rows as bf16 high and low parts, two products).",
+        "The bench divides the issued figure by its own measured duration of the call.",
+        "",
+        f"- kernel sources: {source_digest(kernel_key)}",
+        f"- mfma flops per launch: {int(round(flops))}",
+        "",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    open(mfma_file(c), "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def read_mfma(c, kernel_key):
+    """Matrix-core flops per launch from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    try:
+        text = open(mfma_file(c)).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith("- ") and ": " in line)
+    if fields.get("- kernel sources") != source_digest(kernel_key):
+        return None
+    return int(fields["- mfma flops per launch"])
+
+
+def summarize_trace(c, k, d, bench_json, kernel_key):
+    """rocprofv3 --kernel-trace --stats summary of a bench run (the stats csv)
+    next to the bench's own figures for the dominant call."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    assert f, f"no kernel_stats.csv under {d}"
+    rows = list(csv.DictReader(open(f[0])))
+    b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    lines = [f"# Kernel trace: {c.name}", "", "Command (repository root, one MI355X):", "", "```",
+             "export TMPDIR=/tmp",
+             f"rocprofv3 --kernel-trace --stats -d gpurun_out/trace{k} -o t --output-format csv -- "
+             f"python bench.py --config {k} --extra '' --no-cpu-baseline > gpurun_out/trace{k}.json",
+             f"python bench.py --config {k} --summarize-trace gpurun_out/trace{k} gpurun_out/trace{k}.json",
+             "```", "",
+             "Kernel statistics (durations in ns; the graphs replay the timed steps twice each, plus eager warm-up "
+             "steps and the flush copies):", "",
+             "| Kernel | Calls | Average ns | Min ns | Max ns | Share |", "|---|---|---|---|---|---|"]
+    apply_ns = 0.0
+    for r in rows:
+        name = r["Name"]
+        avg = float(r["AverageNs"])
+        lines.append(f"| `{name[:100]}` | {r['Calls']} | {avg:.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r['Percentage']):.2f} % |")
+        if any(key in name for key in kernel_keys(kernel_key)):
+            apply_ns += avg
+    alg = algorithmic(c)
+    ab = alg["shrink_bytes"] + alg["expand_bytes"]
+    bus = b["roofline"]["kernel_avg_us"]
+    lines += ["",
+              f"Trace average of the dominant call `{kernel_key}` (sum of its kernels' averages): "
+              f"{apply_ns / 1e3:.3f} us, {ab / (apply_ns * 1e-9) / 1e9:.1f} GB/s = "
+              f"{ab / (apply_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.4f} of 8 TB/s "
+              f"({ab} algorithmic bytes per launch).",
+              f"The same run's bench line (HIP events around a flushed graph of the calls): {bus:.3f} us, "
+              f"frac {b['roofline']['frac']:.4f} ({100 * (bus * 1e3 - apply_ns) / apply_ns:+.1f} % from the trace; "
+              "the tracer adds its own time between graph nodes, which the events count and the per-kernel "
+              "durations do not).", ""]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"trace_{c.name}.md")
+    open(out, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(c, seconds, threads):
+    """The oracle as it stands (plain C, fp64) on a bounded sample of the same
+    workload: whole batches, metadata plus every token's delta, until `seconds`
+    have passed.  The oracle's calls run on `threads` host threads at once,
+    each on its own chunk of rows (the C calls release the interpreter lock);
+    the oracle itself is unchanged.  An MoE step is counted in tokens: a token
+    is done when all its top-k pairs are."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
     moe = getattr(c, "moe", None)
     T = c.T if moe is None else moe.T
-    rows_per_call = max(1, min(T, 64 if moe is None else 8))
+    rows_per_call = max(1, min(T, 16 if moe is None else 4))
+    deadline = [None]
+
+    def rows_of(r0):
+        return np.arange(r0, min(T, r0 + rows_per_call))
+
+    def work(r0):
+        if time.perf_counter() > deadline[0]:
+            return 0
+        rows = rows_of(r0)
+        if moe is None:
+            oracle.lora_rows(c.x, c.token_slot, c.num_slots, c.A, c.B, c.offsets, c.scale, c.y0, rows=rows)
+        else:
+            pairs = (rows[:, None] * moe.topk + np.arange(moe.topk)).reshape(-1)
+            oracle.moe_rows(moe.x, moe.topk_ids, moe.token_slot, moe.num_slots, moe.num_experts,
+                            moe.num_local_experts, moe.A, moe.B, moe.offsets, moe.scale, moe.y0,
+                            expert_map=moe.expert_map, x_per_pair=moe.x_per_pair, rows=pairs)
+        return rows.shape[0]
+
+    oracle.load()
     done = 0
     t0 = time.perf_counter()
-    while True:
-        if moe is None:
-            oracle.prepare_meta(c.token_slot, c.num_slots)
-        else:
-            oracle.prepare_meta(oracle.moe_keys(moe.topk_ids, moe.token_slot, moe.num_slots, moe.num_experts,
-                                                moe.num_local_experts, moe.expert_map), c.num_slots)
-        for r0 in range(0, T, rows_per_call):
-            rows = np.arange(r0, min(T, r0 + rows_per_call))
+    deadline[0] = t0 + seconds
+    with ThreadPoolExecutor(threads) as pool:
+        while time.perf_counter() < deadline[0]:
             if moe is None:
-                oracle.lora_rows(c.x, c.token_slot, c.num_slots, c.A, c.B, c.offsets, c.scale, c.y0,
-                                 rows=rows)
+                oracle.prepare_meta(c.token_slot, c.num_slots)
             else:
-                pairs = (rows[:, None] * moe.topk + np.arange(moe.topk)).reshape(-1)
-                oracle.moe_rows(moe.x, moe.topk_ids, moe.token_slot, moe.num_slots, moe.num_experts,
-                                moe.num_local_experts, moe.A, moe.B, moe.offsets, moe.scale, moe.y0,
-                                expert_map=moe.expert_map, x_per_pair=moe.x_per_pair, rows=pairs)
-            done += rows.shape[0]
-            if time.perf_counter() - t0 > seconds:
-                break
-        if time.perf_counter() - t0 > seconds:
-            break
+                oracle.prepare_meta(oracle.moe_keys(moe.topk_ids, moe.token_slot, moe.num_slots, moe.num_experts,
+                                                    moe.num_local_experts, moe.expert_map), c.num_slots)
+            done += sum(pool.map(work, range(0, T, rows_per_call)))
     dt = time.perf_counter() - t0
-    return dict(value=done / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} tokens of workload '{c.name}' (metadata + fp64 delta of every "
-                       f"token, whole batches of {T}) in {dt:.1f} s on one host thread")
+    return dict(value=round(done / dt, 2), unit="tokens/s", cores=threads, kind="oracle", cpu_model=cpu_model(),
+                sample=f"{done} tokens of workload '{c.name}' (metadata + fp64 delta of every token, batches of "
+                       f"{T}, {rows_per_call} rows per oracle call) in {dt:.1f} s on {threads} host threads")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (the path has no multi-GPU stage); "
-              "run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def load_case(k):
     import workloads as W
-
-    c = W.config(args.config)
+    c = W.config(k)
     moe = None
     if isinstance(c, W.MoeCase):
         moe, c = c, MoeFlat(c)
-    alg = algorithmic(c, args.slot_ranks)
-    if args.summarize_pmc:
-        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode))
-        return
+    return c, moe
 
-    import torch
 
-    import segmented_gather_rank_amd as L
+class Flush:
+    """A copy of flush_mb MiB (half read, half written) run before a timed
+    region, so that no input of the timed steps is left in the MALL or an L2."""
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    def __init__(self, torch, dev, mb):
+        n = max(1, int(mb * 2 ** 20 / 2))
+        self.src = torch.ones(n // 2, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.dst.copy_(self.src)
+
+
+def copy_rate_gbs(torch, dev):
+    """Device copy rate: a 1 GiB copy, best of 5, timed with HIP events
+    (2 GiB moved per copy)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * n / (best * 1e-3) / 1e9
+
+
+def measure(c, moe, args, L, torch, dev, flush, K, warmup):
+    """Graph-timed step, metadata and apply of one workload; returns the
+    figures of its JSON line (roofline of lora_apply included)."""
+    import numpy as np
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -341,6 +526,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    alg = algorithmic(c, args.slot_ranks)
     if moe is None:
         base = dict(ts=torch.from_numpy(c.token_slot).to(dev), x=to_dev(c.x),
                     A=[to_dev(a) for a in c.A], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
@@ -363,7 +549,7 @@ def main():
                  L.lora_moe_meta_workspace_bytes(moe.T, moe.topk, moe.num_slots, moe.num_local_experts))
     for s in sets:
         s["mws"] = torch.empty(mws_bytes, dtype=torch.uint8, device=dev)
-        s["aws"] = torch.empty(max(ap_need, 16), dtype=torch.uint8, device=dev)
+        s["aws"] = L.apply_workspace(ap_need, dev)
 
     metas = [None] * nrot
     ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).to(dev) if args.slot_ranks else None
@@ -386,21 +572,8 @@ def main():
         meta_call(i)
         apply_call(i)
 
-    K = args.steps
-    if args.pmc_pass:
-        # the calibration copy (reads and writes PMC_COPY_ELEMS bf16 values),
-        # then K eager steps; rocprofv3 --pmc collects the counters per dispatch
-        src = torch.ones(PMC_COPY_ELEMS, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        for i in range(max(K, nrot)):
-            step(i)
-        torch.cuda.synchronize()
-        print(f"pmc pass done: {K} steps of {c.name}", flush=True)
-        return
     # eager warm-up (also builds every set's metadata once)
-    for i in range(max(args.warmup, nrot)):
+    for i in range(max(warmup, nrot)):
         step(i)
     torch.cuda.synchronize()
 
@@ -418,7 +591,8 @@ def main():
         return g
 
     def time_graph(g):
-        g.replay()                       # warm replay
+        g.replay()                       # first replay (uploads the graph)
+        flush()                          # nothing the timed replay reads stays cached
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -438,6 +612,7 @@ def main():
     del g_step, g_meta, g_apply
 
     # the same steps issued eagerly from Python, for reference (host-issue bound)
+    flush()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(K):
@@ -445,47 +620,145 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     eager_ms_per_step = e0.elapsed_time(e1) / K
+    del sets, metas
+    torch.cuda.empty_cache()
 
     ms_per_step = total_ms / K
     tokens = c.T if moe is None else moe.T       # an MoE step's tokens (each with top-k pairs)
-    value = tokens * K / (total_ms / 1e3)
-
-    d_us = apply_us
+    key = dominant_kernel(c, args.mode)
     d_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
-    achieved = d_bytes / (d_us * 1e-6) / 1e9
+    d_flops = alg["shrink_flops"] + alg["expand_flops"]
+    achieved = d_bytes / (apply_us * 1e-6) / 1e9
+    mf = None if args.slot_ranks else read_mfma(c, key)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if args.slot_ranks else read_traffic(c, dominant_kernel(c, args.mode)),
-                "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + dominant_kernel(c, args.mode) + ")",
-                "kernel_avg_us": round(d_us, 3), "algorithmic_bytes_per_launch": int(d_bytes)}
-    step_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
-    step_flops = alg["shrink_flops"] + alg["expand_flops"]
+                "traffic": None if args.slot_ranks else read_traffic(c, key),
+                "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + key + ")",
+                "kernel_avg_us": round(apply_us, 3), "algorithmic_bytes_per_launch": int(d_bytes),
+                "mfma_bf16": {"algorithmic_tflops": round(d_flops / (apply_us * 1e-6) / 1e12, 2),
+                              "algorithmic_frac": round(d_flops / (apply_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                              "issued_tflops": None if mf is None else round(mf / (apply_us * 1e-6) / 1e12, 2),
+                              "issued_frac": None if mf is None else round(
+                                  mf / (apply_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                              "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                              "issued_from": "rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per launch (profiles/)"}}
+    config = {"workload": c.name, "tokens": tokens,
+              **({} if moe is None else {"topk": moe.topk, "pairs": c.T, "experts": moe.num_experts,
+                                         "local_experts": moe.num_local_experts,
+                                         "adapter_slots": moe.num_slots}),
+              "tokens_with_adapter" if moe is None else "keyed_pairs": alg["T_lora"],
+              "distinct_slots" if moe is None else "distinct_keys": alg["U"],
+              "slots": c.num_slots, "d_in": c.d_in,
+              "slice_widths": c.widths, "r_max": r, "mode": args.mode,
+              "slot_ranks": bool(args.slot_ranks),
+              "rotated_input_sets": nrot, "flush_mb_before_timed_replay": args.flush_mb,
+              "parallelism": "single GPU"}
+    return {
+        "value": round(tokens * K / (total_ms / 1e3), 1), "ms_per_step": round(ms_per_step, 5),
+        "dtype": "bf16" if c.dtype == "bf16" else "f32", "config": config, "roofline": roofline,
+        "calls_us": {"lora_prepare_meta": round(meta_us, 3), "lora_apply": round(apply_us, 3),
+                     "lora_prepare_meta_per_layer_of_32": round(meta_us / 32, 3)},
+        "step": {"algorithmic_bytes": int(d_bytes),
+                 "hbm_frac": round(d_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_bf16_frac": round(d_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                 "timed_as": "one HIP graph of the K steps, replayed once after a flushing copy",
+                 "host_wall_s": round(t_host, 4), "eager_ms_per_step": round(eager_ms_per_step, 5)},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the path has no multi-GPU stage); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    c, moe = load_case(args.config)
+    if args.summarize_pmc:
+        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode))
+        return
+    if args.summarize_mfma:
+        summarize_mfma(c, args.config, args.summarize_mfma, dominant_kernel(c, args.mode))
+        return
+    if args.summarize_trace:
+        summarize_trace(c, args.config, *args.summarize_trace, dominant_kernel(c, args.mode))
+        return
+
+    import torch
+
+    import segmented_gather_rank_amd as L
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K = args.steps
+
+    if args.pmc_pass:
+        import numpy as np
+
+        def to_dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+        # the calibration copy (reads and writes PMC_COPY_ELEMS bf16 values),
+        # then K eager steps; rocprofv3 --pmc collects the counters per dispatch
+        src = torch.ones(PMC_COPY_ELEMS, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        src = moe if moe is not None else c
+        ts = torch.from_numpy(src.token_slot).to(dev)
+        x, y = to_dev(src.x), to_dev(src.y0)
+        SE = c.num_slots
+        A = [to_dev(a).view(SE, *a.shape[2:]) if moe is not None else to_dev(a) for a in src.A]
+        B = [to_dev(b).view(SE, *b.shape[2:]) if moe is not None else to_dev(b) for b in src.B]
+        ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).to(dev) if args.slot_ranks else None
+        ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, c.r_max,
+                                                            x.dtype, args.mode), dev)
+        for i in range(K):
+            if moe is None:
+                m = L.lora_prepare_meta(ts, c.num_slots)
+            else:
+                m = L.lora_prepare_moe_meta(torch.from_numpy(moe.topk_ids).to(dev), ts, moe.num_slots,
+                                            moe.num_experts, moe.num_local_experts,
+                                            None if moe.expert_map is None else
+                                            torch.from_numpy(moe.expert_map).to(dev))
+                m = m.with_x_row_div(1) if moe.x_per_pair else m
+            L.lora_apply(m, x, A, B, c.offsets, y, scale=c.scale, add=True, mode=args.mode, workspace=ws,
+                         slot_rank=ranks)
+        torch.cuda.synchronize()
+        print(f"pmc pass done: {K} steps of {c.name}", flush=True)
+        return
+
+    flush = Flush(torch, dev, args.flush_mb)
+    print(f"bench: workload {c.name}, {K} steps", file=sys.stderr, flush=True)
+    head = measure(c, moe, args, L, torch, dev, flush, K, args.warmup)
+    extra = {}
+    for k in [int(v) for v in args.extra.split(",") if v.strip()]:
+        if k == args.config:
+            continue
+        ck, mk = load_case(k)
+        print(f"bench: extra workload {ck.name}", file=sys.stderr, flush=True)
+        e = measure(ck, mk, args, L, torch, dev, flush, K, args.warmup)
+        extra[ck.name] = {kk: e[kk] for kk in ("value", "ms_per_step", "roofline", "calls_us")}
+        extra[ck.name]["unit"] = "tokens/s"
+        del ck, mk
+    del flush
+    torch.cuda.empty_cache()
+    copy_gbs = copy_rate_gbs(torch, dev)
+
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if c.dtype == "bf16" else "f32",
-        "data": "synthetic",
-        "config": {"workload": c.name, "tokens": tokens,
-                   **({} if moe is None else {"topk": moe.topk, "pairs": c.T, "experts": moe.num_experts,
-                                              "local_experts": moe.num_local_experts,
-                                              "adapter_slots": moe.num_slots}),
-                   "tokens_with_adapter" if moe is None else "keyed_pairs": alg["T_lora"],
-                   "distinct_slots" if moe is None else "distinct_keys": alg["U"],
-                   "slots": c.num_slots, "d_in": c.d_in,
-                   "slice_widths": c.widths, "r_max": r, "mode": args.mode,
-                   "slot_ranks": bool(args.slot_ranks),
-                   "rotated_input_sets": nrot, "parallelism": "single GPU"},
-        "roofline": roofline,
-        "calls_us": {"lora_prepare_meta": round(meta_us, 3), "lora_apply": round(apply_us, 3)},
-        "step": {"algorithmic_bytes": int(step_bytes), "hbm_frac": round(
-            step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_bf16_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
-            "timed_as": "one HIP graph of the K steps, replayed once", "host_wall_s": round(t_host, 4),
-            "eager_ms_per_step": round(eager_ms_per_step, 5)},
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+        "config": head["config"], "roofline": head["roofline"], "calls_us": head["calls_us"], "step": head["step"],
+        "hbm_copy_gbs": {"measured": round(copy_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                         "how": "torch copy_ of 1 GiB (2 GiB moved), best of 6, HIP events"},
+        "extra": extra,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
-        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
+        out["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds, args.cpu_threads or host_threads())
     print(json.dumps(out), flush=True)
 
 

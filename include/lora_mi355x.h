@@ -66,6 +66,17 @@ typedef struct lora_weight {
     int64_t slot_stride;            /* elements between consecutive slots */
 } lora_weight;
 
+/* Bytes at the start of every lora_apply workspace that hold the rendezvous
+ * words of the decode-shaped apply (below, lora_apply_workspace_init). */
+#define LORA_APPLY_SYNC_BYTES 295168
+/* Word indices, in that region, of two counters the decode-shaped apply keeps
+ * (read them as uint32): waits for peer workgroups that gave up, and waits
+ * that met a peer on another accelerator die (XCD).  Each case is handled
+ * (the waiting workgroup computes the peer's share itself, with the same
+ * result); the counters only report that it happened. */
+#define LORA_APPLY_WAITS_GAVE_UP_WORD 73728
+#define LORA_APPLY_OTHER_XCD_WORD 73729
+
 /* Slot metadata of one batch (page "vLLM 源码完全拆解(十八):多 LoRA 服务",
  * section "LoRAKernelMeta:先按槽位排序").  lora_prepare_meta fills the struct on
  * the host with device pointers into the caller's workspace and enqueues the
@@ -88,19 +99,10 @@ typedef struct lora_weight {
  *                   unspecified).  Tiles follow the order of `sorted`; there
  *                   are num_tiles <= ceil(T / 64) + S + 1 of them.  The compute
  *                   kernels take their work from this list.
- *   sync            64 uint32 per possible tile (four ranges of 16, one per
- *                   output slice that runs side by side), then 64 more:
- *                   rendezvous flags of the decode-shaped lora_apply (below),
- *                   set to 0 here; the word after the tiles' flags counts
- *                   waits that gave up (a workgroup that waited for its peers
- *                   past the spin limit computed their share itself: the
- *                   result is the same, only slower)
  * The struct stays valid until its workspace is reused; rebuild it whenever
- * token_slot changes.  Pass it by pointer to the compute calls.  lora_shrink
- * and lora_expand only read it, so any number of them may use one lora_meta at
- * the same time; lora_apply counts its rendezvous in `sync`, so lora_apply
- * calls that share one lora_meta must run one after another (one stream, or
- * ordered by events). */
+ * token_slot changes.  Pass it by pointer to the compute calls.  They only
+ * read it, so any number of calls, on any streams, may use one lora_meta at
+ * the same time. */
 typedef struct lora_meta {
     int64_t num_tokens;             /* rows of the batch */
     int32_t num_slots;              /* keys: slots, or (slot, local expert) pairs */
@@ -113,7 +115,6 @@ typedef struct lora_meta {
     int32_t *seg_start;
     int32_t *info;
     int32_t *tiles;
-    uint32_t *sync;
 } lora_meta;
 
 /* Bytes of device workspace lora_prepare_meta needs for T tokens and S slots. */
@@ -233,12 +234,27 @@ lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slice
                         lora_dtype dtype, int add_into_y, lora_mode mode,
                         void *stream);
 
-/* Bytes of device workspace lora_apply needs: the fp32 rank-r buffer plus the
- * shrink workspace.  No initialisation is required. */
+/* Bytes of device workspace lora_apply needs for these sizes (a workspace
+ * sized for the largest call can serve every smaller one).  Layout: the
+ * rendezvous words (LORA_APPLY_SYNC_BYTES), the fp32 rank-r buffer, then the
+ * partial sums of a shrink that splits d_in or of the decode-shaped kernel.
+ * Only the rendezvous words need initialising: see lora_apply_workspace_init. */
 lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
                                        int64_t d_in, int32_t n_slices,
                                        int32_t r_max, lora_dtype dtype,
                                        lora_mode mode, size_t *bytes);
+
+/* Zero the rendezvous words of an apply workspace (its first
+ * LORA_APPLY_SYNC_BYTES bytes; enqueued on `stream`).  Call it once, before
+ * the first lora_apply on a workspace; zero-filled memory needs no call.  The
+ * decode-shaped apply (page "多 LoRA 服务：分段矩阵乘与适配器调度", section
+ * "不合并权重，批量计算": the fused form for decode batches) spreads each work
+ * tile over several workgroups that meet at per-tile flag words kept here.
+ * Every call leaves them consistent for the next call on the same workspace,
+ * whatever its shapes.  The words must not be written between calls.
+ *   d_ws      device workspace, 16-byte aligned
+ *   ws_bytes  its size, at least LORA_APPLY_SYNC_BYTES (else LORA_ERR_WORKSPACE) */
+lora_status lora_apply_workspace_init(void *d_ws, size_t ws_bytes, void *stream);
 
 /* Shrink then expand on one stream: the whole delta of one layer, added into
  * (or stored to) the slices of y.  Arguments as in lora_shrink and lora_expand;
@@ -247,7 +263,12 @@ lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
  * each token's rank-r vector on chip; the others run the shrink and expand
  * kernels.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
  * 服务", section "调用链" (add_lora_linear = shrink into an fp32 buffer, then
- * expand into the output slices). */
+ * expand into the output slices).
+ *   d_ws      workspace of at least lora_apply_workspace_bytes bytes, 16-byte
+ *             aligned, whose rendezvous words were initialised once
+ *             (lora_apply_workspace_init) and not written since except by
+ *             lora_apply.  Calls that run at the same time need workspaces of
+ *             their own; calls in stream order may share one. */
 lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx,
                        int64_t d_in, lora_dtype dtype, int32_t n_slices,
                        const lora_weight *A, const lora_weight *B,

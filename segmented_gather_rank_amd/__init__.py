@@ -46,8 +46,7 @@ class lora_meta(C.Structure):
     _fields_ = [("num_tokens", C.c_int64), ("num_slots", C.c_int32), ("x_row_div", C.c_int32),
                 ("sorted", C.c_void_p), ("sorted_slot", C.c_void_p), ("seg_slot", C.c_void_p),
                 ("seg_count", C.c_void_p),
-                ("seg_start", C.c_void_p), ("info", C.c_void_p), ("tiles", C.c_void_p),
-                ("sync", C.c_void_p)]
+                ("seg_start", C.c_void_p), ("info", C.c_void_p), ("tiles", C.c_void_p)]
 
 
 _p, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
@@ -65,6 +64,7 @@ _decl = {
     "lora_expand": ([C.POINTER(lora_meta), _p, _i32, C.POINTER(lora_weight), C.POINTER(_i64),
                      C.POINTER(_i64), _i32, _p, _p, _i64, _i32, C.c_int, _i32, _p], _i32),
     "lora_apply_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
+    "lora_apply_workspace_init": ([_p, _sz, _p], _i32),
     "lora_apply": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight),
                     C.POINTER(lora_weight), C.POINTER(_i64), C.POINTER(_i64), _i32, C.c_float, _p,
                     _p, _p, _i64, C.c_int, _i32, _p, _sz, _p], _i32),
@@ -95,7 +95,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 6:
+if _lib.lora_abi_version() != 7:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -148,9 +148,14 @@ def _weights(ws, name: str, inner_shape_ok) -> tuple:
 
 
 TILE_ROWS = 64          # sorted positions per work tile of the metadata
-SPLIT_MEMBERS = 16  # rendezvous flag words per work tile and slice range
-SPLIT_FLAG_WORDS = 64  # per work tile: four ranges
 TILE_INTS = 4 + TILE_ROWS
+# the apply workspace's rendezvous words (LORA_APPLY_SYNC_BYTES and the two
+# counter indices of the C header)
+APPLY_SYNC_BYTES = 295168
+WAITS_GAVE_UP_WORD = 73728
+OTHER_XCD_WORD = 73729
+SPLIT_MEMBERS = 16      # rendezvous words per work tile and slice range
+SPLIT_RANGES = 4        # slice ranges per work tile
 
 
 def max_tiles(num_tokens: int, num_slots: int) -> int:
@@ -194,14 +199,7 @@ class LoraMeta:
                     seg_slot=self._view(self.c.seg_slot, S + 1),
                     seg_count=self._view(self.c.seg_count, S + 1),
                     seg_start=self._view(self.c.seg_start, S + 2), info=self._view(self.c.info, 8),
-                    tiles=self._view(self.c.tiles, TILE_INTS * max_tiles(T, S)).view(-1, TILE_INTS),
-                    sync=self._view(self.c.sync, SPLIT_FLAG_WORDS * (max_tiles(T, S) + 1)))
-
-    def split_wait_timeouts(self) -> int:
-        """Waits of the split decode kernel that gave up (0 in normal runs).
-        Synchronises with the device."""
-        T, S = self.num_tokens, self.num_slots
-        return int(self._view(self.c.sync, SPLIT_FLAG_WORDS * (max_tiles(T, S) + 1))[SPLIT_FLAG_WORDS * max_tiles(T, S)].item())
+                    tiles=self._view(self.c.tiles, TILE_INTS * max_tiles(T, S)).view(-1, TILE_INTS))
 
 
 def lora_meta_workspace_bytes(num_tokens: int, num_slots: int) -> int:
@@ -279,6 +277,36 @@ def lora_apply_workspace_bytes(num_tokens, num_slots, d_in, n_slices, r_max, dty
     return int(b.value)
 
 
+def lora_apply_workspace_init(workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Zero the rendezvous words at the start of an apply workspace (once,
+    before its first lora_apply)."""
+    _check("lora_apply_workspace_init",
+           _lib.lora_apply_workspace_init(_dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def apply_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled apply workspace of at least nbytes (and at least the
+    rendezvous words), ready for lora_apply."""
+    return torch.zeros(max(int(nbytes), APPLY_SYNC_BYTES), dtype=torch.uint8, device=device)
+
+
+def apply_workspace_counters(workspace: torch.Tensor) -> dict:
+    """The decode-shaped apply's counters in a workspace: waits that gave up
+    and waits that met a peer on another XCD (0 and 0 in normal runs; either
+    case is still computed right).  Synchronises with the device."""
+    w = workspace[:APPLY_SYNC_BYTES].view(torch.int32)
+    v = w[WAITS_GAVE_UP_WORD:OTHER_XCD_WORD + 1].cpu().tolist()
+    return {"gave_up": int(v[0]) & 0xFFFFFFFF, "other_xcd": int(v[1]) & 0xFFFFFFFF}
+
+
+def apply_workspace_flags(workspace: torch.Tensor, tiles: int) -> torch.Tensor:
+    """The rendezvous words of the first `tiles` work tiles, [tile][range][member]
+    (int32 view of uint32 words: the call count in bits 31:4, an XCD in 3:0)."""
+    w = workspace[:APPLY_SYNC_BYTES].view(torch.int32)
+    return w[:tiles * SPLIT_RANGES * SPLIT_MEMBERS].view(tiles, SPLIT_RANGES, SPLIT_MEMBERS)
+
+
 def _x_args(x: torch.Tensor):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be [T][ldx] with unit column stride")
@@ -350,7 +378,7 @@ def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, 
         raise ValueError("A and B need one entry per slice")
     need = lora_apply_workspace_bytes(meta.num_tokens, meta.num_slots, d_in, n, r, x.dtype, mode)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = apply_workspace(need, x.device)
     if y.dim() != 2 or y.stride(1) != 1:
         raise ValueError("y must be [T][ldy] with unit column stride")
     ss = None if slot_scale is None else _dev(slot_scale, "slot_scale")
@@ -366,4 +394,5 @@ def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, 
 __all__ = ["lora_abi_version", "lora_status_string", "lora_meta_workspace_bytes", "lora_prepare_meta",
            "lora_moe_meta_workspace_bytes", "lora_prepare_moe_meta",
            "lora_shrink_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_workspace_bytes",
+           "lora_apply_workspace_init", "apply_workspace", "apply_workspace_counters", "apply_workspace_flags",
            "lora_apply", "LoraMeta", "LoraError", "lora_weight", "lora_meta", "LIB_PATH"]

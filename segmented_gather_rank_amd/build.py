@@ -16,8 +16,8 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -26,6 +26,7 @@ FLAGS = [
     "-mllvm", "-amdgpu-kernarg-preload-count=6",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+LINK_FLAGS = [f"--offload-arch={ARCH}", "-shared", "-fPIC"]
 
 
 def sources():
@@ -33,8 +34,22 @@ def sources():
 
 
 def build(out: str = LIB, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-o", out + ".tmp", *sources()]
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object (in parallel, one hipcc per file),
+    then link the shared library; the objects go to a temporary directory."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory(prefix="lora_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in sources()]
+
+        def compile_one(src_obj):
+            src, obj = src_obj
+            subprocess.run([HIPCC, *COMPILE_FLAGS, *extra, "-c", src, "-o", obj], check=True)
+
+        jobs = min(len(objs), max(1, min(8, os.cpu_count() or 1)))
+        with ThreadPoolExecutor(jobs) as pool:
+            list(pool.map(compile_one, zip(sources(), objs)))
+        subprocess.run([HIPCC, *LINK_FLAGS, "-o", out + ".tmp", *objs], check=True)
     os.replace(out + ".tmp", out)
     return out
 

@@ -53,10 +53,22 @@ using namespace lora;
 
 namespace {
 
+// Clears n words with vector stores (a fill kernel rather than hipMemsetAsync,
+// so that a captured graph holds a kernel node).
+__global__ void zero_words_kernel(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t stream) {
+  const int grid = (int)std::min<int64_t>(256, (n + 255) / 256);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 6;
+constexpr int32_t kAbiVersion = 7;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -67,7 +79,7 @@ bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV ||
 size_t esize(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
 
 struct MetaLayout {
-  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, sync, total;
+  size_t sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, total;
 };
 MetaLayout meta_layout(int64_t T, int32_t S) {
   MetaLayout L{};
@@ -86,8 +98,6 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
   off += align256(sizeof(int32_t) * 8);
   L.tiles = off;
   off += align256(sizeof(int32_t) * kTileInts * (size_t)max_tiles(T, S));
-  L.sync = off;
-  off += align256(sizeof(uint32_t) * (size_t)sync_words(T, S));
   L.total = off;
   return L;
 }
@@ -96,7 +106,7 @@ lora_status check_meta(const lora_meta *m) {
   if (!m || m->num_tokens < 0 || m->num_slots < 1 || m->num_slots > kMaxSlots || m->x_row_div < 1)
     return LORA_ERR_INVALID_ARG;
   if (!m->sorted || !m->sorted_slot || !m->seg_slot || !m->seg_count || !m->seg_start || !m->info ||
-      !m->tiles || !m->sync)
+      !m->tiles)
     return LORA_ERR_INVALID_ARG;
   return LORA_OK;
 }
@@ -110,7 +120,6 @@ MetaView view_of(const lora_meta *m) {
   v.seg_start = m->seg_start;
   v.info = m->info;
   v.tiles = m->tiles;
-  v.sync = m->sync;
   v.T = m->num_tokens;
   v.S = m->num_slots;
   v.x_row_div = m->x_row_div;
@@ -173,6 +182,62 @@ void unpack(const lora_weight *W, int32_t n, const void **ptrs, int64_t *strides
   }
 }
 
+
+// lora_apply on a workspace that holds the rendezvous words, then the rank-r
+// buffer, then the partial sums (ws_bytes in all, already checked to be
+// enough).
+lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in, lora_dtype dtype,
+                     int32_t n_slices, const lora_weight *A, const lora_weight *B, const int64_t *width,
+                     const int64_t *offset, int32_t r_max, float scale, const float *d_slot_scale,
+                     const int32_t *d_slot_rank, void *d_y, int64_t ldy, int add_into_y, lora_mode mode,
+                     char *ws, size_t ws_bytes, hipStream_t s) {
+  uint32_t *sync = reinterpret_cast<uint32_t *>(ws);
+  float *u = reinterpret_cast<float *>(ws + kSyncBytes);
+  lora_status st = check_shrink_args(meta, d_x, ldx, d_in, dtype, n_slices, A, r_max, d_slot_scale, u, mode);
+  if (st != LORA_OK) return st;
+  st = check_expand_args(meta, u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
+  if (st != LORA_OK) return st;
+  if (!aligned4(d_slot_rank)) return LORA_ERR_INVALID_ARG;
+  const size_t ubytes = align256(sizeof(float) * (size_t)n_slices * (size_t)meta->num_tokens *
+                                 (size_t)r_max);
+  void *sh_ws = ws + kSyncBytes + ubytes;
+  const size_t sh_bytes = ws_bytes - kSyncBytes - ubytes;
+  const void *aptr[kMaxSlices], *bptr[kMaxSlices];
+  int64_t astr[kMaxSlices], bstr[kMaxSlices];
+  unpack(A, n_slices, aptr, astr);
+  unpack(B, n_slices, bptr, bstr);
+  const MetaView mv = view_of(meta);
+  // decode-shaped (BGMV requested, or few tokens per slot): the split kernel
+  // first (bf16; it checks its own limits), then the per-token kernel when
+  // its limits hold
+  const bool decode = (int)mode != 2 && ((int)mode == 1 || meta->num_tokens <= 16 * (int64_t)meta->num_slots);
+  if (!fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
+    bool used = false;
+    const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
+                                           r_max, scale, d_slot_scale, d_slot_rank, d_y, ldy, add_into_y, sync,
+                                           static_cast<float *>(sh_ws), sh_bytes, s, &used);
+    if (e != hipSuccess) return LORA_ERR_HIP;
+    if (used) return LORA_OK;
+  }
+  if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
+                                     r_max, ldy, dtype == LORA_BF16, (int)mode)) {
+    const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
+                                     bptr, bstr, width, offset, r_max, scale, d_slot_scale,
+                                     d_slot_rank, d_y, ldy, add_into_y, s);
+    return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
+  int kch = 1;
+  hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
+                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  // the rank-r rows are in sorted order; with a split d_in they are still the
+  // partial sums, which the expand adds
+  const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
+  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, r_max,
+                    d_slot_rank, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,7 +275,6 @@ static void place_meta(lora_meta *out, void *d_ws, const MetaLayout &L, int64_t 
   out->seg_start = reinterpret_cast<int32_t *>(base + L.seg_start);
   out->info = reinterpret_cast<int32_t *>(base + L.info);
   out->tiles = reinterpret_cast<int32_t *>(base + L.tiles);
-  out->sync = reinterpret_cast<uint32_t *>(base + L.sync);
 }
 
 lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S, void *d_ws,
@@ -223,7 +287,7 @@ lora_status lora_prepare_meta(const int32_t *d_token_slot, int64_t T, int32_t S,
   if (ws_bytes < L.total) return LORA_ERR_WORKSPACE;
   place_meta(out, d_ws, L, T, S);
   const hipError_t e = launch_meta(d_token_slot, T, S, out->sorted, out->sorted_slot, out->seg_slot,
-                                   out->seg_count, out->seg_start, out->info, out->tiles, out->sync,
+                                   out->seg_count, out->seg_start, out->info, out->tiles,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -255,8 +319,7 @@ lora_status lora_prepare_moe_meta(const int32_t *d_topk_ids, int64_t T, int32_t 
   place_meta(out, d_ws, meta_layout(n, S * E_local), n, S * E_local);
   const hipError_t e = launch_meta_moe(d_topk_ids, T, topk, d_token_slot, S, E_global, E_local, d_expert_map,
                                        out->sorted, out->sorted_slot, out->seg_slot, out->seg_count,
-                                       out->seg_start, out->info, out->tiles, out->sync,
-                                       static_cast<hipStream_t>(stream));
+                                       out->seg_start, out->info, out->tiles, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return LORA_ERR_HIP;
   out->x_row_div = topk;
   return LORA_OK;
@@ -323,8 +386,18 @@ lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32
   if (st != LORA_OK) return st;
   // the split decode kernel's partial rank rows share the shrink's region
   if (dtype == LORA_BF16 && mode != LORA_MODE_SGMV) sh = std::max(sh, split_ws_bytes(T, S, n_slices, r_max));
-  *bytes = align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max) + sh;
+  // rendezvous words, then the rank-r buffer, then the shrink's or the split
+  // kernel's partial sums
+  *bytes = kSyncBytes + align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max) + sh;
   return LORA_OK;
+}
+
+lora_status lora_apply_workspace_init(void *d_ws, size_t ws_bytes, void *stream) {
+  if (!d_ws || !aligned16(d_ws)) return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < kSyncBytes) return LORA_ERR_WORKSPACE;
+  const hipError_t e = launch_zero_words(static_cast<uint32_t *>(d_ws), kSyncBytes / sizeof(uint32_t),
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in,
@@ -338,52 +411,10 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   lora_status st = lora_apply_workspace_bytes(meta->num_tokens, meta->num_slots, d_in, n_slices,
                                               r_max, dtype, mode, &need);
   if (st != LORA_OK) return st;
-  if (ws_bytes < need || (need > 0 && (!d_ws || !aligned16(d_ws)))) return LORA_ERR_WORKSPACE;
-  // the rank-r buffer sits at the start of the workspace
-  float *u = static_cast<float *>(d_ws);
-  st = check_shrink_args(meta, d_x, ldx, d_in, dtype, n_slices, A, r_max, d_slot_scale, u, mode);
-  if (st != LORA_OK) return st;
-  st = check_expand_args(meta, u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
-  if (st != LORA_OK) return st;
-  if (!aligned4(d_slot_rank)) return LORA_ERR_INVALID_ARG;
-  const size_t ubytes = align256(sizeof(float) * (size_t)n_slices * (size_t)meta->num_tokens *
-                                 (size_t)r_max);
-  void *sh_ws = static_cast<char *>(d_ws) + ubytes;
-  const void *aptr[kMaxSlices], *bptr[kMaxSlices];
-  int64_t astr[kMaxSlices], bstr[kMaxSlices];
-  unpack(A, n_slices, aptr, astr);
-  unpack(B, n_slices, bptr, bstr);
-  const MetaView mv = view_of(meta);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  // decode-shaped (BGMV requested, or few tokens per slot): the split kernel
-  // first (bf16; it checks its own limits), then the per-token kernel when
-  // its limits hold
-  const bool decode = (int)mode != 2 && ((int)mode == 1 || meta->num_tokens <= 16 * (int64_t)meta->num_slots);
-  if (!fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
-    bool used = false;
-    const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
-                                           r_max, scale, d_slot_scale, d_slot_rank, d_y, ldy, add_into_y,
-                                           static_cast<float *>(sh_ws), ws_bytes - ubytes, s, &used);
-    if (e != hipSuccess) return LORA_ERR_HIP;
-    if (used) return LORA_OK;
-  }
-  if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
-                                     r_max, ldy, dtype == LORA_BF16, (int)mode)) {
-    const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
-                                     bptr, bstr, width, offset, r_max, scale, d_slot_scale,
-                                     d_slot_rank, d_y, ldy, add_into_y, s);
-    return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
-  }
-  int kch = 1;
-  hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
-                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s);
-  if (e != hipSuccess) return LORA_ERR_HIP;
-  // the rank-r rows are in sorted order; with a split d_in they are still the
-  // partial sums, which the expand adds
-  const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
-  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, r_max,
-                    d_slot_rank, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
-  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  if (ws_bytes < need || !d_ws || !aligned16(d_ws)) return LORA_ERR_WORKSPACE;
+  return apply_in(meta, d_x, ldx, d_in, dtype, n_slices, A, B, width, offset, r_max, scale, d_slot_scale,
+                  d_slot_rank, d_y, ldy, add_into_y, mode, static_cast<char *>(d_ws), ws_bytes,
+                  static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -30,22 +30,31 @@
 // and a flag took about 0.9 us instead of 0.2 us to reach a peer.)  Once every
 // member's flag is up, the G partial fragments are added in one fixed order
 // (each wave a quarter of the members, then the four sums in wave order
-// through LDS), so every member gets the same u, bit for bit.  Flags are
-// per-tile counters that the metadata kernel zeroes: each call raises each of
-// a tile's 16 words exactly once (member 0 also raises the words of members
-// >= G), so they stay equal between calls and a member waits for "my value +
-// 1".  The B chunk is loaded with the A chunk and x, and so is the y of the
-// first 16 rows except with the longest chunks, so that none of them is
-// outstanding at the acknowledgement wait or the polls (loads complete in
-// order).  The wait is bounded: a workgroup that
-// gives up counts itself in the word after the flags and computes the missing
-// members' partials itself, with the same code (so the same bits), storing
-// them into those members' slots.  The result therefore depends neither on
-// the members being resident together nor on their sharing an XCD (a member
-// elsewhere would not see the others' flags before the kernel ends; it only
-// costs the spin limit).  Workgroups are dispatched in order on each XCD and a
-// tile's members are neighbours there, so the tiles within the resident part
-// of a larger grid finish and make room for the rest.
+// through LDS), so every member gets the same u, bit for bit.
+//
+// The flag words live at the start of the caller's apply workspace, so calls
+// with workspaces of their own share nothing.  A word counts the calls that
+// raised it and names the XCD (hardware register XCC_ID) of the member that
+// raised it last.  Each call raises each of a tile's 16 words exactly once
+// (member 0 also raises the words of members >= G), so the words of a range
+// stay equal between calls, and a member waits for "my count + 1".  A member
+// trusts a peer's word only when it names its own XCD: plain stores stay in
+// the L2 of the XCD that made them until that L2 writes them back, in any
+// order, so a flag seen from another XCD (evicted early, say) does not prove
+// that the fragments it guards are visible here.  The B chunk is loaded with
+// the A chunk and x, and so is the y of the first 16 rows except with the
+// longest chunks, so that none of them is outstanding at the acknowledgement
+// wait or the polls (loads complete in order).  The wait is bounded.  A
+// member computes itself, with the same code (so the same bits), the partials
+// of every peer it does not trust: still low at the spin limit, or raised from
+// another XCD.  It stores them into those peers' slots, where the peer writes
+// equal values, and reads them back through its own L2.  The result therefore
+// depends neither on the members being resident together nor on their sharing
+// an XCD: a member placed elsewhere costs the spin limit and is counted (a
+// status word beside the flags), never a wrong value.  Workgroups are
+// dispatched in order on each XCD and a tile's members are neighbours there,
+// so the tiles within the resident part of a larger grid finish and make room
+// for the rest.
 //
 // Only bf16.
 #include "lora_host.h"
@@ -85,6 +94,7 @@ struct SplitParams {
   int64_t ldy;
   int32_t add;
   float *part;  // partial fragments [G][n_frag][n_slices][R16 blocks][64 lanes][4]
+  uint32_t *sync;  // rendezvous words (host side only: the kernels take them as an argument)
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -103,27 +113,38 @@ __device__ __forceinline__ void split_zero(const SplitParams &p, const int32_t *
   }
 }
 
+// XCD this workgroup runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15u; }
+
 // Raise this member's flag word of the tile (member 0 also those of members
-// >= G) to f + 1, then wait until the G members' words reach it: one wave,
-// at most spin_limit polls.  Returns the members whose words were still low
-// when it gave up (bit g'), 0 when all arrived; a wait that gives up counts
-// itself in *err.  The words are raised with plain stores, which stop in the
-// L2 of this XCD, where the other members (on the same XCD) poll them with
-// agent-coherent loads; a member on another XCD would not see them before
-// the kernel ends, give up at the spin limit and compute the partials itself.
+// >= G) to the next call count, tagged with this workgroup's XCD, then wait
+// until the G members' words carry that count: one wave, at most spin_limit
+// polls.  A peer's word is trusted only when its tag names this XCD: flags and
+// the partial fragments they guard are stored with plain stores, which stay in
+// the L2 of the XCD that made them until that L2 writes them back, so only a
+// peer on this XCD is known to have its fragments where this workgroup reads
+// them.  Returns the members (bit g') whose partials this workgroup computes
+// itself: those still low when it gave up, and those raised from another XCD.
+// status[0] counts waits that gave up, status[1] waits that met a word raised
+// on another XCD.
 __device__ __forceinline__ uint32_t split_wait(uint32_t *fl, uint32_t f, int g, int G, int spin_limit,
-                                               uint32_t *err) {
+                                               uint32_t xcc, uint32_t *status) {
   const int lane = threadIdx.x % kWave;
-  const uint32_t want = f + 1u;
+  const uint32_t want = (f & ~15u) + 16u;  // this call's count, in bits 31:4
   if (lane < kSplitMembers && (lane == g || (g == 0 && lane >= G)))
-    __builtin_amdgcn_raw_buffer_store_b32(want, make_rsrc(fl, kSplitMembers * 4), lane * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(want | xcc, make_rsrc(fl, kSplitMembers * 4), lane * 4, 0, 0);
   for (int polls = 0;; ++polls) {
-    const uint32_t v = lane < G ? __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : want;
-    const uint64_t low = __ballot((int32_t)(v - want) < 0);
-    if (low == 0) return 0u;
-    if (polls >= spin_limit) {
-      if (lane == 0) atomicAdd(err, 1u);
-      return (uint32_t)low;
+    const uint32_t v =
+        lane < G ? __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : (want | xcc);
+    const bool up = (int32_t)((v & ~15u) - want) >= 0;
+    const uint64_t low = __ballot(!up);
+    if (low == 0 || polls >= spin_limit) {
+      const uint64_t foreign = __ballot(up && (v & 15u) != xcc);
+      if (lane == 0) {
+        if (low) atomicAdd(status, 1u);
+        if (foreign) atomicAdd(status + 1, 1u);
+      }
+      return (uint32_t)(low | foreign);
     }
     __builtin_amdgcn_s_sleep(1);
   }
@@ -388,7 +409,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   if (G > 1) {
     __shared__ uint32_t missing;
     if (wave == 0) {
-      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitFlagWords);
+      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, xcc_id(), flags + (int64_t)kSyncTiles * kSplitFlagWords);
       if (lane == 0) missing = m;
     }
     __syncthreads();
@@ -759,7 +780,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   if (G > 1) {
     __shared__ uint32_t missing;
     if (wave == 0) {
-      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, flags + (int64_t)p.max_tiles * kSplitFlagWords);
+      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, xcc_id(), flags + (int64_t)kSyncTiles * kSplitFlagWords);
       if (lane == 0) missing = m;
     }
     __syncthreads();
@@ -962,7 +983,7 @@ static hipError_t launch_split_k(const MetaView &meta, SplitParams &p, const int
     p.ldb = pl.ldb;
     p.bs_off = pl.bs_off;
     hipLaunchKernelGGL((bgmv_split_kernel<R, NS>), dim3(pl.grid), dim3(kSThreads), pl.lds, stream, meta.info,
-                       meta.tiles, meta.sync, p);
+                       meta.tiles, p.sync, p);
     return hipGetLastError();
   }
 }
@@ -1038,7 +1059,7 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
   p.x_full = ((int64_t)pl.G << pl.ksh) == sp.d_in ? 1 : 0;
   p.scale = sp.scale;
   hipLaunchKernelGGL((bgmv_split1_kernel<R, KS>), dim3(pl.grid / sp.n_slices, sp.n_slices), dim3(kSThreads), pl.lds,
-                     stream, meta.info, meta.tiles, meta.sync, p, q);
+                     stream, meta.info, meta.tiles, sp.sync, p, q);
   return hipGetLastError();
 }
 
@@ -1100,9 +1121,11 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
                              const void *const *A, const int64_t *a_stride, const void *const *B,
                              const int64_t *b_stride, const int64_t *width, const int64_t *offset, int32_t R,
                              float scale, const float *slot_scale, const int32_t *slot_rank, void *y, int64_t ldy,
-                             int add, float *part, size_t part_bytes, hipStream_t stream, bool *used) {
+                             int add, uint32_t *sync, float *part, size_t part_bytes, hipStream_t stream,
+                             bool *used) {
   *used = false;
   if (meta.T == 0 || part_bytes >= ((size_t)1 << 32) || ldy >= ((int64_t)1 << 30)) return hipSuccess;
+  if (max_tiles(meta.T, meta.S) > kSyncTiles) return hipSuccess;  // tiles past the rendezvous region
   SplitParams p{};
   p.x = x;
   p.ldx = ldx;
@@ -1131,6 +1154,7 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
   p.ldy = ldy;
   p.add = add ? 1 : 0;
   p.part = part;
+  p.sync = sync;
   // one slice, or up to four side by side, on the one-slice kernel (ldx and
   // ldy also enter its 32-bit offsets); else every slice in one workgroup
   if (n_slices <= kSplitRanges && ldx < ((int64_t)1 << 31) && ldy < ((int64_t)1 << 31)) {

@@ -244,7 +244,6 @@ struct MetaView {
   const int32_t *seg_start;
   const int32_t *info;   // num_segments, no_lora, num_bad, lora_begin, num_tiles
   const int32_t *tiles;  // kTileInts int32 per tile: slot, rows, pos0, 0, tokens[kTileRows]
-  uint32_t *sync;        // rendezvous flags of the split decode kernel
   int64_t T;
   int32_t S;
   int32_t x_row_div;     // batch row i reads x row i / x_row_div

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 
+#include "../../include/lora_mi355x.h"
 #include "lora_common.h"
 
 namespace lora {
@@ -53,24 +54,34 @@ struct ShrinkConfig {
 ShrinkConfig plan_shrink(int64_t T, int32_t S, int64_t d_in, int32_t R, bool bf16, int mode);
 size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32_t R);
 
-// Rendezvous flags of the split decode kernel: per work tile one range of
-// kSplitMembers words for each of up to kSplitRanges slices that run side by
-// side, then one row whose first word counts waits that gave up.
+// Rendezvous words of the split decode kernel, at the start of every apply
+// workspace: per work tile one range of kSplitMembers words for each of up to
+// kSplitRanges slices that run side by side, for tile indices below
+// kSyncTiles, then one row of counters (word 0: waits that gave up; word 1:
+// flags found raised from another XCD).  A word holds the number of split
+// calls that raised it (bits 31:4) and the XCD of the member that raised it
+// last (bits 3:0).  The region must be zero before the first call on a
+// workspace; every call raises each word of each range it uses exactly once,
+// so the words of a range stay equal between calls.  The split kernel runs
+// only for T * n_slices * max(r, 16) <= 2^17 tokens x ranks, so T <= 8192 and
+// a batch has at most 8192 / 64 + 1023 + 1 = 1152 tiles.
 constexpr int kSplitMembers = 16;
 constexpr int kSplitRanges = 4;
 constexpr int kSplitFlagWords = kSplitMembers * kSplitRanges;  // per tile
-inline int64_t sync_words(int64_t T, int32_t S) { return kSplitFlagWords * (max_tiles(T, S) + 1); }
+constexpr int kSyncTiles = 1152;
+constexpr size_t kSyncBytes = sizeof(uint32_t) * kSplitFlagWords * (kSyncTiles + 1);
+static_assert(kSyncBytes % 256 == 0, "the rank buffer after the rendezvous words stays 256-byte aligned");
+static_assert(kSyncBytes == LORA_APPLY_SYNC_BYTES, "the C header states the region's size");
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
-                       int32_t *info, int32_t *tiles, uint32_t *sync, hipStream_t stream);
+                       int32_t *info, int32_t *tiles, hipStream_t stream);
 // the same over the T * topk (token, choice) pairs of a top-k routing step,
 // keyed by (slot, local expert): S * E_local keys
 hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
                            int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
                            int32_t *sorted, int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
-                           int32_t *seg_start, int32_t *info, int32_t *tiles, uint32_t *sync,
-                           hipStream_t stream);
+                           int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream);
 
 // for_apply: u is written in sorted-position order, and with a split d_in the
 // partial sums are left in ws for the expand to add (kch_out reports the split)
@@ -97,14 +108,16 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
 bool fused_disabled();
 
 // The fused kernel with each work tile split over several workgroups (bf16,
-// decode-shaped calls).  part: workspace of split_ws_bytes bytes for the
-// partial rank rows.  *used is false when the call is not one it takes.
+// decode-shaped calls).  sync: the rendezvous words (kSyncBytes, above);
+// part: workspace of split_ws_bytes bytes for the partial rank rows.  *used is
+// false when the call is not one it takes.
 size_t split_ws_bytes(int64_t T, int32_t S, int32_t n_slices, int32_t R);
 hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, int32_t n_slices,
                              const void *const *A, const int64_t *a_stride, const void *const *B,
                              const int64_t *b_stride, const int64_t *width, const int64_t *offset, int32_t R,
                              float scale, const float *slot_scale, const int32_t *slot_rank, void *y, int64_t ldy,
-                             int add, float *part, size_t part_bytes, hipStream_t stream, bool *used);
+                             int add, uint32_t *sync, float *part, size_t part_bytes, hipStream_t stream,
+                             bool *used);
 bool split_disabled();
 int split_spin_limit();
 int split_members();

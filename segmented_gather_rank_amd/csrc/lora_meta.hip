@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
     int32_t *__restrict__ sorted, int32_t *__restrict__ sorted_slot,
     int32_t *__restrict__ seg_slot,
     int32_t *__restrict__ seg_count, int32_t *__restrict__ seg_start,
-    int32_t *__restrict__ info, int32_t *__restrict__ tiles, uint32_t *__restrict__ sync, int32_t n_sync) {
+    int32_t *__restrict__ info, int32_t *__restrict__ tiles) {
   extern __shared__ __align__(16) int32_t lds[];  // 16-byte aligned: the lane-mask tables take 8-byte LDS atomics
   const int K = S + 1;                      // number of keys (slot + 1; 0: none or bad)
   int32_t *cnt = lds;                       // [K] rows per key
@@ -121,8 +121,6 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   __shared__ int32_t wsum[kMetaWaves][3];
 
   const int tid = threadIdx.x;
-  // the split decode kernel's rendezvous flags start equal (zero) for every tile
-  for (int i = tid; i < n_sync; i += kMetaThreads) sync[i] = 0u;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   int nbits = 0;
@@ -385,7 +383,7 @@ static size_t meta_lds_bytes(int32_t S, int64_t T, int32_t E_map, bool &cached, 
 template <bool MOE, int KIND, bool MLDS>
 static hipError_t launch_meta_k(const MetaSrc &src, int64_t T, int32_t S, size_t lds, int32_t *sorted,
                                 int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
-                                int32_t *info, int32_t *tiles, uint32_t *sync, int32_t n_sync, hipStream_t stream) {
+                                int32_t *info, int32_t *tiles, hipStream_t stream) {
   if (lds > 65536) {
     // more than the default 64 KB of dynamic LDS
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_kernel<MOE, KIND, MLDS>),
@@ -394,17 +392,15 @@ static hipError_t launch_meta_k(const MetaSrc &src, int64_t T, int32_t S, size_t
   }
   hipLaunchKernelGGL((meta_kernel<MOE, KIND, MLDS>), dim3(1), dim3(kMetaThreads), lds, stream, src.token_slot,
                      src.topk_ids, T, src, S, sorted, sorted_slot, seg_slot, seg_count, seg_start,
-                     info, tiles, sync, n_sync);
+                     info, tiles);
   return hipGetLastError();
 }
 
 template <bool MOE>
 static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_t *sorted,
                                 int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
-                                int32_t *seg_start, int32_t *info, int32_t *tiles, uint32_t *sync,
-                                hipStream_t stream) {
+                                int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream) {
   bool cached = false, match_lds = false;
-  const int32_t n_sync = (int32_t)sync_words(T, S);
   const size_t lds = meta_lds_bytes(S, T, MOE && src.expert_map ? src.E_global : 0, cached, match_lds);
   const int kind = T <= kMetaThreads ? kSmall : (cached ? kCached : kStreamed);
   // few keys (at most 4 key bits): one ballot per bit is cheaper than lanes
@@ -413,7 +409,7 @@ static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_
   if (S + 1 <= 16) match_lds = false;
 #define LORA_META_LAUNCH(K, M)                                                                                    \
   return launch_meta_k<MOE, K, M>(src, T, S, lds, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, \
-                                  sync, n_sync, stream)
+                                  stream)
   if (kind == kSmall) {
     if (match_lds) LORA_META_LAUNCH(kSmall, true);
     LORA_META_LAUNCH(kSmall, false);
@@ -429,18 +425,16 @@ static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
-                       int32_t *info, int32_t *tiles, uint32_t *sync, hipStream_t stream) {
+                       int32_t *info, int32_t *tiles, hipStream_t stream) {
   MetaSrc src{};
   src.token_slot = token_slot;
-  return launch_meta_t<false>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, sync,
-                              stream);
+  return launch_meta_t<false>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles, stream);
 }
 
 hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, const int32_t *token_slot,
                            int32_t S, int32_t E_global, int32_t E_local, const int32_t *expert_map,
                            int32_t *sorted, int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
-                           int32_t *seg_start, int32_t *info, int32_t *tiles, uint32_t *sync,
-                           hipStream_t stream) {
+                           int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream) {
   MetaSrc src{};
   src.token_slot = token_slot;
   src.topk_ids = topk_ids;
@@ -450,7 +444,7 @@ hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, con
   src.E_global = E_global;
   src.E_local = E_local;
   return launch_meta_t<true>(src, T * topk, S * E_local, sorted, sorted_slot, seg_slot, seg_count, seg_start, info,
-                             tiles, sync, stream);
+                             tiles, stream);
 }
 
 }  // namespace lora

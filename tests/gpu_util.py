@@ -43,11 +43,17 @@ class DevCase:
         self.slot_scale = (None if c.slot_scale is None
                            else torch.from_numpy(np.asarray(c.slot_scale, np.float32)).to(device))
 
-    def apply(self, L, mode="auto", add=True, y=None, meta=None, workspace=None):
-        meta = meta or L.lora_prepare_meta(self.token_slot, self.c.num_slots)
+    def apply(self, L, mode="auto", add=True, y=None, meta=None, workspace=None, stream=None):
+        """lora_apply on this case; the apply workspace used (a fresh,
+        zero-filled one unless given) is kept in self.ws."""
+        meta = meta or L.lora_prepare_meta(self.token_slot, self.c.num_slots, stream=stream)
         y = self.y0.clone() if y is None else y
+        if workspace is None:
+            workspace = L.apply_workspace(L.lora_apply_workspace_bytes(
+                meta.num_tokens, meta.num_slots, self.c.d_in, len(self.A), self.c.r_max, self.x.dtype, mode))
+        self.ws = workspace
         L.lora_apply(meta, self.x, self.A, self.B, self.c.offsets, y, scale=self.c.scale,
-                     slot_scale=self.slot_scale, add=add, mode=mode, workspace=workspace)
+                     slot_scale=self.slot_scale, add=add, mode=mode, workspace=workspace, stream=stream)
         return y, meta
 
 

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 6
+    assert L.lora_abi_version() == 7
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -39,12 +39,28 @@ def test_workspace_sizes():
     assert L.lora_meta_workspace_bytes(0, 1) > 0
     import torch
     b_apply = L.lora_apply_workspace_bytes(4096, 128, 14336, 1, 64, torch.bfloat16)
-    assert b_apply >= 4 * 4096 * 64
+    assert b_apply >= L.APPLY_SYNC_BYTES + 4 * 4096 * 64
+    # every apply workspace starts with the rendezvous words, whatever the call
+    assert L.lora_apply_workspace_bytes(1, 1, 8, 1, 8, torch.float32) >= L.APPLY_SYNC_BYTES
     b2 = L.lora_shrink_workspace_bytes(256, 32, 4096, 1, 16, torch.bfloat16)
     assert b2 > 0 and b2 % 256 == 0
 
 
-_buf = (C.c_uint8 * (1 << 16))()
+def test_header_constants_match_binding():
+    """The binding's copies of the header's #define values, and the layout
+    they imply: a row of 64 words per possible work tile (1152 of them), then
+    the counters."""
+    text = open(HEADER).read()
+    d = {k: int(v) for k, v in re.findall(r"#define\s+(LORA_\w+)\s+(\d+)", text)}
+    assert d["LORA_APPLY_SYNC_BYTES"] == L.APPLY_SYNC_BYTES
+    assert d["LORA_APPLY_WAITS_GAVE_UP_WORD"] == L.WAITS_GAVE_UP_WORD
+    assert d["LORA_APPLY_OTHER_XCD_WORD"] == L.OTHER_XCD_WORD
+    tiles = (8192 + 63) // 64 + 1023 + 1
+    assert L.WAITS_GAVE_UP_WORD == tiles * L.SPLIT_RANGES * L.SPLIT_MEMBERS
+    assert L.APPLY_SYNC_BYTES == 4 * (tiles + 1) * L.SPLIT_RANGES * L.SPLIT_MEMBERS
+
+
+_buf = (C.c_uint8 * (1 << 20))()
 _base = (C.addressof(_buf) + 255) // 256 * 256
 
 
@@ -72,7 +88,7 @@ def test_meta_rejections():
 def _meta(T=16, S=4):
     m = L.lora_meta()
     m.num_tokens, m.num_slots, m.x_row_div = T, S, 1
-    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info", "tiles", "sync"):
+    for f in ("sorted", "sorted_slot", "seg_slot", "seg_count", "seg_start", "info", "tiles"):
         setattr(m, f, _base)
     return m
 
@@ -144,10 +160,22 @@ def test_apply_rejections():
     wd, of = (C.c_int64 * 1)(64), (C.c_int64 * 1)(0)
     args = lambda ws, ws_bytes: (C.byref(_meta()), _ptr(), 64, 64, 1, n, A, B, wd, of, 16,
                                  C.c_float(1.0), None, None, _ptr(), 64, 1, 0, ws, ws_bytes, None)
+    big = 1 << 19   # enough for this call: rendezvous words + rank buffer
     assert _call("lora_apply", *args(_ptr(), 16)) == L.LORA_ERR_WORKSPACE
-    assert _call("lora_apply", None, *args(_ptr(), 1 << 15)[1:]) == L.LORA_ERR_INVALID_ARG
-    assert _call("lora_apply", *args(None, 1 << 15)) == L.LORA_ERR_WORKSPACE
-    assert _call("lora_apply", *args(_ptr(8), 1 << 15)) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_apply", *args(_ptr(), L.APPLY_SYNC_BYTES)) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_apply", None, *args(_ptr(), big)[1:]) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_apply", *args(None, big)) == L.LORA_ERR_WORKSPACE
+    assert _call("lora_apply", *args(_ptr(8), big)) == L.LORA_ERR_WORKSPACE
+    bad = _meta()
+    bad.tiles = None
+    assert _call("lora_apply", C.byref(bad), *args(_ptr(), big)[1:]) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_apply", *args(_ptr(), big)[:15], 63, *args(_ptr(), big)[16:]) == L.LORA_ERR_INVALID_ARG  # ldy
+
+
+def test_workspace_init_rejections():
+    assert _call("lora_apply_workspace_init", None, 1 << 19, None) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_apply_workspace_init", _ptr(8), 1 << 19, None) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_apply_workspace_init", _ptr(), L.APPLY_SYNC_BYTES - 16, None) == L.LORA_ERR_WORKSPACE
 
 
 def test_moe_meta_rejections():

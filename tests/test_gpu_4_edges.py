@@ -104,8 +104,9 @@ def test_integer_inputs_bit_exact(L, mode, shape):
 
 
 def test_workspace_reuse_two_shapes(L):
-    """One apply workspace (left uninitialised) serves calls of different
-    sizes in a row."""
+    """One apply workspace serves calls of different sizes in a row: garbage
+    everywhere except the rendezvous words, which lora_apply_workspace_init
+    clears once."""
     from test_gpu_2_apply import small_case
     big = W.config(5)
     dbig = DevCase(big)
@@ -114,6 +115,7 @@ def test_workspace_reuse_two_shapes(L):
     need = max(L.lora_apply_workspace_bytes(big.T, big.num_slots, big.d_in, 1, 64, torch.bfloat16),
                L.lora_apply_workspace_bytes(small.T, small.num_slots, small.d_in, 3, 64, torch.bfloat16))
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    L.lora_apply_workspace_init(ws)
     rows = np.arange(0, big.T, 97)
     for _ in range(2):
         yb, _ = dbig.apply(L, workspace=ws)

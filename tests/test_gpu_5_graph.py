@@ -21,9 +21,8 @@ def test_graph_replays_match_eager(L, k, mode):
     c = W.config(k)
     print(f"[graph] {c.name} mode={mode}", flush=True)
     d = DevCase(c)
-    ws = torch.empty(max(16, L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices,
-                                                           c.r_max, d.x.dtype, mode)),
-                     dtype=torch.uint8, device="cuda")
+    ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, c.r_max,
+                                                        d.x.dtype, mode))
     mws = torch.empty(L.lora_meta_workspace_bytes(c.T, c.num_slots), dtype=torch.uint8, device="cuda")
     y = d.y0.clone()
 

@@ -13,10 +13,6 @@ from gpu_util import TOL, DevCase, check_rows, from_dev, oracle_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MEMBERS = 16           # flag words per slice range
-RANGES = 4             # slice ranges per work tile
-
-
 @pytest.fixture(scope="module")
 def L():
     import segmented_gather_rank_amd as lib
@@ -45,22 +41,32 @@ def live_tiles(meta):
     return np.where(slots >= 0)[0], n
 
 
-def tile_flags(meta):
-    """[tiles + 1][range][word]"""
-    return meta.tensors()["sync"].cpu().numpy().view(np.uint32).reshape(-1, RANGES, MEMBERS)
+def tile_flags(L, d, meta):
+    """The rendezvous words of the apply workspace d.ws, [tile][range][member],
+    as uint32: the call count in bits 31:4, the XCD that raised the word last
+    in bits 3:0."""
+    n = L.max_tiles(meta.num_tokens, meta.num_slots)
+    return L.apply_workspace_flags(d.ws, n).cpu().numpy().view(np.uint32)
 
 
-def check_flags(meta, calls, ranges=1):
-    """Every word of the first `ranges` slice ranges of a live tile equals the
-    number of split calls; the other words were never touched; no wait gave
-    up."""
-    f = tile_flags(meta)
+def check_counters(L, ws):
+    """No wait gave up and no member met a peer on another XCD."""
+    assert L.apply_workspace_counters(ws) == {"gave_up": 0, "other_xcd": 0}
+
+
+def check_flags(L, d, meta, calls, ranges=1):
+    """Every word of the first `ranges` slice ranges of a live tile counts
+    `calls` calls and names one XCD (all members of a tile ran on one); the
+    other words were never touched; no wait gave up."""
+    f = tile_flags(L, d, meta)
     live, n = live_tiles(meta)
-    assert (f[live, :ranges] == calls).all(), f[live]
+    cnt, tag = f >> 4, f & 15
+    assert (cnt[live, :ranges] == calls).all(), cnt[live]
+    assert (tag[live, :ranges] == tag[live, :ranges, :1]).all(), tag[live]
     assert (f[live, ranges:] == 0).all()
-    dead = np.setdiff1d(np.arange(f.shape[0] - 1), live)
+    dead = np.setdiff1d(np.arange(f.shape[0]), live)
     assert (f[dead] == 0).all()
-    assert meta.split_wait_timeouts() == 0
+    check_counters(L, d.ws)
 
 
 @pytest.mark.parametrize("r", [8, 16, 32, 64])
@@ -71,7 +77,7 @@ def test_split_decode_parity(L, r, add):
     d = DevCase(c)
     y, meta = d.apply(L, mode="auto", add=add)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), c.name)
-    check_flags(meta, 1, ranges=len(c.widths))  # the slices run side by side
+    check_flags(L, d, meta, 1, ranges=len(c.widths))  # the slices run side by side
 
 
 @pytest.mark.parametrize("d_in,r", [(14336, 16), (3000, 8), (5000, 32), (4096, 64), (1024, 64)])
@@ -84,7 +90,7 @@ def test_split_long_rows(L, d_in, r):
     d = DevCase(c)
     y, meta = d.apply(L)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
-    check_flags(meta, 1)
+    check_flags(L, d, meta, 1)
 
 
 @pytest.mark.parametrize("r", [16, 32])
@@ -97,7 +103,7 @@ def test_split_packed_qkv_decode_shape(L, r):
     d = DevCase(c)
     y, meta = d.apply(L)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
-    check_flags(meta, 1, ranges=3)
+    check_flags(L, d, meta, 1, ranges=3)
 
 
 def test_split_rank64_three_slices_side_by_side(L):
@@ -107,7 +113,7 @@ def test_split_rank64_three_slices_side_by_side(L):
     d = DevCase(c)
     y, meta = d.apply(L)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
-    check_flags(meta, 1, ranges=3)
+    check_flags(L, d, meta, 1, ranges=3)
 
 
 def test_split_five_slices_rank64_falls_back(L):
@@ -118,7 +124,7 @@ def test_split_five_slices_rank64_falls_back(L):
     d = DevCase(c)
     y, meta = d.apply(L)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), c.name)
-    assert (tile_flags(meta) == 0).all()
+    assert (tile_flags(L, d, meta) == 0).all()
 
 
 def test_split_calls_share_one_meta(L):
@@ -135,18 +141,52 @@ def test_split_calls_share_one_meta(L):
         assert np.array_equal(c.token_slot, base.token_slot)
         cases.append((c, DevCase(c)))
     meta = L.lora_prepare_meta(cases[0][1].token_slot, S)
-    calls = 0
+    ws = L.apply_workspace(max(L.lora_apply_workspace_bytes(T, S, c.d_in, len(c.widths), c.r_max, torch.bfloat16)
+                               for c, _ in cases))
     for rep in range(2):
         for c, d in cases:
             print(f"[split-share] rep {rep} {c.name} d_in={c.d_in} widths={c.widths}", flush=True)
-            y, _ = d.apply(L, mode="auto", meta=meta)
-            calls += 1
+            y, _ = d.apply(L, mode="auto", meta=meta, workspace=ws)
             check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), f"{c.name} rep {rep}")
-    f = tile_flags(meta)
+    f = tile_flags(L, cases[0][1], meta)
     live, _ = live_tiles(meta)
-    assert (f[live] == f[live][:, :, :1]).all()  # each range's words stay equal
-    assert (f[live, 0] >= 1).all()
-    assert meta.split_wait_timeouts() == 0
+    assert ((f[live] >> 4) == (f[live][:, :, :1] >> 4)).all()  # each range's words stay equal
+    assert ((f[live, 0] >> 4) >= 2).all()
+    check_counters(L, ws)
+
+
+def test_split_two_streams_one_meta(L):
+    """Two decode-shaped applies of different shapes on one lora_meta, at the
+    same time on two streams, each call with its own workspace: the metadata is
+    only read and the rendezvous words live in each call's workspace, so both
+    give the oracle's rows, and each stream's repeats are equal bit for bit.
+    (With two kernels sharing the CUs, a wait may give up: that case computes
+    the same bits, so it is not asserted away.)"""
+    S, T = 32, 256
+    c1 = decode_case(650, 16, S=S, T=T, d_in=4096, widths=(4096,))
+    c2 = decode_case(650, 32, S=S, T=T, d_in=1024, widths=(512, 256, 136))
+    assert np.array_equal(c1.token_slot, c2.token_slot)
+    d1, d2 = DevCase(c1), DevCase(c2)
+    meta = L.lora_prepare_meta(d1.token_slot, S)
+    ws = [L.apply_workspace(L.lora_apply_workspace_bytes(T, S, c.d_in, len(c.widths), c.r_max, torch.bfloat16))
+          for c in (c1, c2)]
+    reps = 6
+    ys = [[d.y0.clone() for _ in range(reps)] for d in (d1, d2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print("[split-2streams] launching", flush=True)
+    for i in range(reps):
+        for k, d in enumerate((d1, d2)):
+            with torch.cuda.stream(streams[k]):
+                d.apply(L, meta=meta, y=ys[k][i], workspace=ws[k], stream=streams[k])
+    torch.cuda.synchronize()
+    for k, c in enumerate((c1, c2)):
+        got = [from_dev(y) for y in ys[k]]
+        for i in range(1, reps):
+            assert np.array_equal(got[i].view(np.uint16), got[0].view(np.uint16)), f"stream {k} rep {i}"
+        check_rows(c, got[0], oracle_rows(c, np.arange(c.T)), f"stream {k}")
+        print(f"[split-2streams] stream {k}: {L.apply_workspace_counters(ws[k])}", flush=True)
+        assert L.apply_workspace_counters(ws[k])["other_xcd"] == 0
 
 
 def test_split_large_tiles(L):
@@ -161,7 +201,7 @@ def test_split_large_tiles(L):
     for add in (True, False):
         y, meta = d.apply(L, mode="bgmv", add=add)
         check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
-        check_flags(meta, 1, ranges=2)
+        check_flags(L, d, meta, 1, ranges=2)
 
 
 @pytest.mark.parametrize("r", [16, 32, 64])
@@ -179,7 +219,7 @@ def test_split_large_tiles_one_slice(L, r):
         print(f"[split-big-1s] r={r} add={add}", flush=True)
         y, meta = d.apply(L, mode="bgmv", add=add)
         check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} add={add}")
-        check_flags(meta, 1)
+        check_flags(L, d, meta, 1)
 
 
 @pytest.mark.parametrize("add", [True, False])
@@ -194,10 +234,11 @@ def test_split_slot_ranks(L, add):
     d = DevCase(c)
     y = d.y0.clone()
     meta = L.lora_prepare_meta(d.token_slot, S)
+    ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, S, c.d_in, len(c.widths), c.r_max, torch.bfloat16))
     L.lora_apply(meta, d.x, d.A, d.B, c.offsets, y, scale=c.scale, slot_scale=d.slot_scale, add=add,
-                 slot_rank=torch.from_numpy(ranks).cuda())
+                 slot_rank=torch.from_numpy(ranks).cuda(), workspace=ws)
     check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), c.name)
-    assert meta.split_wait_timeouts() == 0
+    check_counters(L, ws)
 
 
 def test_split_graph_replays(L):
@@ -212,8 +253,8 @@ def test_split_graph_replays(L):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):  # warm-up outside the capture (workspace allocations)
         meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
-        ws = torch.empty(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, len(c.widths), c.r_max,
-                                                      torch.bfloat16), dtype=torch.uint8, device="cuda")
+        ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, len(c.widths), c.r_max,
+                                                            torch.bfloat16))
     torch.cuda.current_stream().wait_stream(s)
     meta_ws = meta.workspace
     g = torch.cuda.CUDAGraph()
@@ -227,7 +268,7 @@ def test_split_graph_replays(L):
         assert torch.equal(y, y_eager), f"replay {i}"
         d.apply(L)  # eager work between replays
         torch.cuda.synchronize()
-    assert m.split_wait_timeouts() == 0
+    check_counters(L, ws)
 
 
 _FALLBACK_CHILD = r"""
@@ -248,7 +289,7 @@ for name, args in (("one_slice", dict(seed=640, r=16, widths=(512,))),
     y, meta = d.apply(L)
     torch.cuda.synchronize()
     res[name] = from_dev(y)
-    res[name + "_gave_up"] = np.array([meta.split_wait_timeouts()])
+    res[name + "_gave_up"] = np.array([L.apply_workspace_counters(d.ws)["gave_up"]])
 np.savez(out, **res)
 print("child done", flush=True)
 """
@@ -279,7 +320,7 @@ def test_split_fallback_when_peers_are_late(L, tmp_path):
         d = DevCase(c)
         y, meta = d.apply(L)
         want = from_dev(y)
-        assert meta.split_wait_timeouts() == 0
+        check_counters(L, d.ws)
         print(f"[split-fallback] {name}: {int(got[name + '_gave_up'][0])} waits gave up", flush=True)
         assert np.array_equal(got[name].view(np.uint16), want.view(np.uint16)), name
         check_rows(c, got[name], oracle_rows(c, np.arange(c.T)), f"{name} after fallback")
