@@ -278,6 +278,31 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx,
                        int add_into_y, lora_mode mode, void *d_ws,
                        size_t ws_bytes, void *stream);
 
+/* Size of the device array that lora_apply_noalloc uses as its workspace. */
+#define LORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* lora_apply for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, checks and results as lora_apply,
+ * without d_ws and ws_bytes: the workspace is a static device array of the
+ * library, LORA_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which each device
+ * holds from the library's first use there until the process ends (zero at
+ * load, so no lora_apply_workspace_init is needed).  Calls whose
+ * lora_apply_workspace_bytes exceed that size return LORA_ERR_WORKSPACE and
+ * enqueue nothing.  Allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine; the first call on a device looks up that device's copy of
+ * the array once (hipGetSymbolAddress; LORA_ERR_HIP if that fails).  Every call
+ * on a device shares its array: calls in stream order are fine, but calls
+ * that overlap on one device (other streams, graphs replayed at the same time)
+ * race and give wrong results. */
+lora_status lora_apply_noalloc(const lora_meta *meta, const void *d_x, int64_t ldx,
+                               int64_t d_in, lora_dtype dtype, int32_t n_slices,
+                               const lora_weight *A, const lora_weight *B,
+                               const int64_t *width, const int64_t *offset,
+                               int32_t r_max, float scale, const float *d_slot_scale,
+                               const int32_t *d_slot_rank, void *d_y, int64_t ldy,
+                               int add_into_y, lora_mode mode, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *lora_status_string(lora_status status);
 

@@ -65,6 +65,9 @@ _decl = {
                      C.POINTER(_i64), _i32, _p, _p, _i64, _i32, C.c_int, _i32, _p], _i32),
     "lora_apply_workspace_bytes": ([_i64, _i32, _i64, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "lora_apply_workspace_init": ([_p, _sz, _p], _i32),
+    "lora_apply_noalloc": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight),
+                            C.POINTER(lora_weight), C.POINTER(_i64), C.POINTER(_i64), _i32, C.c_float, _p,
+                            _p, _p, _i64, C.c_int, _i32, _p], _i32),
     "lora_apply": ([C.POINTER(lora_meta), _p, _i64, _i64, _i32, _i32, C.POINTER(lora_weight),
                     C.POINTER(lora_weight), C.POINTER(_i64), C.POINTER(_i64), _i32, C.c_float, _p,
                     _p, _p, _i64, C.c_int, _i32, _p, _sz, _p], _i32),
@@ -391,7 +394,34 @@ def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, 
     return y
 
 
-__all__ = ["lora_abi_version", "lora_status_string", "lora_meta_workspace_bytes", "lora_prepare_meta",
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LORA_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def lora_apply_noalloc(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
+                       slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto", stream=None,
+                       slot_rank: torch.Tensor | None = None) -> torch.Tensor:
+    """lora_apply with the library's own device scratch as its workspace (no
+    workspace argument, nothing allocated).  Calls that overlap on one device
+    share that scratch and race."""
+    xp, ldx, d_in = _x_args(x)
+    A_arr, A_list = _weights(A, "A", lambda i, w: None)
+    B_arr, B_list = _weights(B, "B", lambda i, w: None)
+    width, offs = _slices(B_list, offsets)
+    if len(B_list) != len(A_list):
+        raise ValueError("A and B need one entry per slice")
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be [T][ldy] with unit column stride")
+    if y.dtype != x.dtype:
+        raise TypeError("x and y must share one dtype")
+    ss = None if slot_scale is None else _dev(slot_scale, "slot_scale")
+    st = _lib.lora_apply_noalloc(C.byref(meta.c), xp, ldx, d_in, _dtype(x), len(A_list), A_arr, B_arr, width,
+                                 offs, A_list[0].shape[2], float(scale), ss, _ranks(slot_rank), _dev(y, "y"),
+                                 y.stride(0), int(bool(add)), MODES[mode], _stream(stream))
+    _check("lora_apply_noalloc", st)
+    return y
+
+
+__all__ = ["lora_apply_noalloc", "NOALLOC_SCRATCH_BYTES", "lora_abi_version", "lora_status_string", "lora_meta_workspace_bytes", "lora_prepare_meta",
            "lora_moe_meta_workspace_bytes", "lora_prepare_moe_meta",
            "lora_shrink_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_workspace_bytes",
            "lora_apply_workspace_init", "apply_workspace", "apply_workspace_counters", "apply_workspace_flags",

@@ -3,9 +3,19 @@
 // can fail runs before the first HIP call, so a rejected call enqueues nothing.
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/lora_mi355x.h"
 #include "lora_host.h"
+
+// Workspace of lora_apply_noalloc: a static device array of the library, one
+// copy per device, zero at load (so its rendezvous words start initialised).
+// In host code its name stands for a host-side shadow, not a device address:
+// a device's copy is reached only through the address hipGetSymbolAddress
+// gives on that device (scratch_of_current_device, below).
+static constexpr size_t kScratchBytes = (size_t)LORA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes >= lora::kSyncBytes, "scratch holds the rendezvous words");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace lora {
 
@@ -238,6 +248,27 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+std::mutex g_scratch_mu;
+char *g_scratch_dev[kMaxDevices];
+
+// This device's copy of the scratch array, looked up once per device.
+hipError_t scratch_of_current_device(char **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = static_cast<char *>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -415,6 +446,27 @@ lora_status lora_apply(const lora_meta *meta, const void *d_x, int64_t ldx, int6
   return apply_in(meta, d_x, ldx, d_in, dtype, n_slices, A, B, width, offset, r_max, scale, d_slot_scale,
                   d_slot_rank, d_y, ldy, add_into_y, mode, static_cast<char *>(d_ws), ws_bytes,
                   static_cast<hipStream_t>(stream));
+}
+
+lora_status lora_apply_noalloc(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in,
+                               lora_dtype dtype, int32_t n_slices, const lora_weight *A,
+                               const lora_weight *B, const int64_t *width, const int64_t *offset,
+                               int32_t r_max, float scale, const float *d_slot_scale,
+                               const int32_t *d_slot_rank, void *d_y, int64_t ldy, int add_into_y,
+                               lora_mode mode, void *stream) {
+  if (!meta) return LORA_ERR_INVALID_ARG;
+  size_t need = 0;
+  const lora_status st = lora_apply_workspace_bytes(meta->num_tokens, meta->num_slots, d_in, n_slices, r_max,
+                                                    dtype, mode, &need);
+  if (st != LORA_OK) return st;
+  if (need > kScratchBytes) return LORA_ERR_WORKSPACE;
+  char *ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) {
+    (void)hipGetLastError();  // the failed lookup must not be reported by the next launch
+    return LORA_ERR_HIP;
+  }
+  return apply_in(meta, d_x, ldx, d_in, dtype, n_slices, A, B, width, offset, r_max, scale, d_slot_scale,
+                  d_slot_rank, d_y, ldy, add_into_y, mode, ws, kScratchBytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -193,3 +193,17 @@ def test_moe_meta_rejections():
     bad = _meta()
     bad.x_row_div = 0
     assert _shrink(meta=bad) == L.LORA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejections():
+    """lora_apply_noalloc checks its arguments, and that the call fits the
+    library's scratch, before touching a device."""
+    A, B = _w(1, 64 * 16), _w(1, 16 * 64)
+    wd, of = (C.c_int64 * 1)(64), (C.c_int64 * 1)(0)
+    args = lambda meta, r: (C.byref(meta), _ptr(), 64, 64, 1, 1, A, B, wd, of, r, C.c_float(1.0), None, None,
+                            _ptr(), 64, 1, 0, None)
+    assert _call("lora_apply_noalloc", None, *args(_meta(), 16)[1:]) == L.LORA_ERR_INVALID_ARG
+    assert _call("lora_apply_noalloc", *args(_meta(), 12)) == L.LORA_ERR_UNSUPPORTED
+    huge = _meta(T=1 << 22, S=4)   # 4 M tokens x 16 ranks of fp32: past the 64 MiB scratch
+    assert _call("lora_apply_noalloc", *args(huge, 16)) == L.LORA_ERR_WORKSPACE
+
