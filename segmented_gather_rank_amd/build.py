@@ -44,7 +44,13 @@ def build(out: str = LIB, extra=()) -> str:
 
         def compile_one(src_obj):
             src, obj = src_obj
-            subprocess.run([HIPCC, *COMPILE_FLAGS, *extra, "-c", src, "-o", obj], check=True)
+            r = subprocess.run([HIPCC, *COMPILE_FLAGS, *extra, "-c", src, "-o", obj], capture_output=True, text=True)
+            # the host pass does not know the packed-fp32 feature it is asked to
+            # switch off (harmless); everything else is shown
+            noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+            sys.stderr.write("".join(ln for ln in r.stderr.splitlines(True) if noise not in ln))
+            if r.returncode != 0:
+                raise subprocess.CalledProcessError(r.returncode, r.args)
 
         jobs = min(len(objs), max(1, min(8, os.cpu_count() or 1)))
         with ThreadPoolExecutor(jobs) as pool:

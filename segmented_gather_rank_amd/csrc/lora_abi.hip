@@ -47,6 +47,15 @@ int split_spin_limit() {
   }();
   return v;
 }
+// LORA_EXPAND_ROWS=0 or 1: keep long batches off, or put every bf16 AUTO/SGMV
+// batch on, the long-segment expand (tuning); unset: chosen by size.
+int expand_rows_knob() {
+  static const int v = [] {
+    const char *e = std::getenv("LORA_EXPAND_ROWS");
+    return e && *e ? (std::atoi(e) > 0 ? 1 : 0) : -1;
+  }();
+  return v;
+}
 // LORA_SPLIT_MEMBERS=n (1, 2, 4, 8 or 16): workgroups per tile of the split
 // kernel, instead of the count chosen from the batch (tuning).
 int split_members() {
@@ -237,9 +246,16 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   int kch = 1;
+  const bool rows = expand_rows_fits(meta->num_tokens, meta->num_slots, dtype == LORA_BF16, (int)mode) &&
+                    expand_rows_addressable(meta->num_tokens, n_slices, width, offset, ldy, r_max);
   hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
-                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s);
+                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s, rows);
   if (e != hipSuccess) return LORA_ERR_HIP;
+  if (rows) {  // long segments: the sums become bf16 planes in the rank buffer, then the row-stream expand
+    e = launch_expand_rows(mv, static_cast<const float *>(sh_ws), kch, reinterpret_cast<uint16_t *>(u), n_slices,
+                           bptr, bstr, width, offset, r_max, d_slot_rank, d_y, ldy, add_into_y, s);
+    return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
   // the rank-r rows are in sorted order; with a split d_in they are still the
   // partial sums, which the expand adds
   const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
@@ -417,6 +433,10 @@ lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32
   if (st != LORA_OK) return st;
   // the split decode kernel's partial rank rows share the shrink's region
   if (dtype == LORA_BF16 && mode != LORA_MODE_SGMV) sh = std::max(sh, split_ws_bytes(T, S, n_slices, r_max));
+  // the long-segment expand takes the shrink's sums from that region even
+  // without a split of d_in
+  if (expand_rows_fits(T, S, dtype == LORA_BF16, (int)mode))
+    sh = std::max(sh, align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max));
   // rendezvous words, then the rank-r buffer, then the shrink's or the split
   // kernel's partial sums
   *bytes = kSyncBytes + align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max) + sh;

@@ -53,6 +53,13 @@ struct ExpandParams {
   int64_t ldy;
   int32_t add;
   const int32_t *slot_rank;  // per-slot ranks, or null (every slot uses R)
+  // long-segment path: the rank-r rows as bf16 high and low planes
+  // [n_slices][T][R] each, in sorted-position order, and 512-column chunks
+  const uint16_t *uh, *ul;
+  int32_t rows_nck[kMaxSlices];       // 512-column chunks per slice
+  int32_t rows_nck_total;
+  uint32_t y_bytes;                   // bytes of y the windows reach (< 2^31)
+  uint32_t plane_bytes;               // bytes of one u plane (< 2^30)
 };
 
 template <typename E, int R>
@@ -518,6 +525,259 @@ __global__ __launch_bounds__(kExpThreads) void expand_kernel(ExpandParams p) {
   }
 }
 
+// ------------------------------------------------------------- long-segment path
+//
+// Prefill batches: segments of hundreds of tokens, so every work tile is full
+// (64 tokens) and the expand is a stream over y.  How that stream is cut
+// decides its speed: measured on a 1 GB bf16 y, an in-place add in steps of
+// 64 rows x 128 columns (the tile kernel's step) runs at about 4.2 TB/s, and
+// in steps of 16 rows x 512 columns, neighbouring workgroups on neighbouring
+// columns of the same rows, at about 4.8 TB/s (a plain contiguous stream:
+// 5.3 TB/s).  So here a workgroup owns one 512-column chunk of one slice and
+// walks a range of consecutive tiles 16 tokens at a time: wave w owns columns
+// 128 w .. + 127 of the chunk, the four waves on the same 16 rows, and the
+// workgroups of one range (one per chunk) sweep the same rows together.  The
+// B^T operands of a wave's columns stay in registers while the slot does not
+// change (the chunk goes to LDS straight from memory, then into registers
+// through the transposing read), so the token loop has no LDS traffic and no
+// barrier.  The rank-r rows come as
+// bf16 high and low planes that a small kernel folds from the shrink's
+// partial sums once per call; the loop prefetches the next token block's
+// planes and y.
+
+constexpr int kRowsCols = 512;             // columns per item, 128 per wave
+constexpr int kRowsLdb = kRowsCols + 16;   // LDS row stride of the B chunk
+
+// u planes: uh[i] + ul[i] = sum over k-chunks, in order, of the partial sums
+// at i (the split of fp32 into bf16 high and low parts, as the MFMA operands
+// take them).  Rows of tokens without an adapter are skipped.
+__global__ __launch_bounds__(256) void u_planes_kernel(const int32_t *__restrict__ info, const float *part,
+                                                       int64_t T, int32_t n_slices, int32_t R, int32_t kch,
+                                                       uint16_t *uh, uint16_t *ul) {
+  const int64_t plane = (int64_t)n_slices * T * R;
+  const int64_t lo_pos = info[3];  // first sorted position with an adapter
+  const int64_t quads = plane / 4;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = 4 * q;
+    const int64_t pos = (i / R) % T;
+    if (pos < lo_pos) continue;
+    const f32x4 v = sum_partials4(part + i, plane, kch);
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) split_bf16(v[m], h[m], l[m]);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2 *>(uh + i) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *reinterpret_cast<u32x2 *>(ul + i) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  }
+}
+
+template <int R, int NS>
+__global__ __launch_bounds__(kXThreads, 2) void expand_rows_kernel(const int32_t *__restrict__ info,
+                                                                   const int32_t *__restrict__ tiles,
+                                                                   ExpandParams p) {
+  constexpr int RK = R < 32 ? 32 : R;          // ranks padded to whole 32-rank MFMA steps
+  constexpr int KS = RK / 32;                  // MFMA k-steps
+  constexpr uint32_t kOut = 0x7FFFFFF0u;       // past every resource: reads as zeros
+  extern __shared__ __align__(16) uint16_t rows_lds[];  // B chunk [RK][kRowsLdb]
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = lane % 16, kg = lane / 16;
+  const int64_t T = p.meta.T;
+  const int ntl = uniform_value(info[4]);
+  const int nneg = p.add ? uniform_value(info[3]) : 0;
+  const int t0 = (nneg + kTileRows - 1) / kTileRows;  // the no-adapter tiles lead; adding, they need no work
+  const int live = ntl - t0;
+  if (live <= 0) return;
+  // work: nr ranges of consecutive live tiles x nck column chunks; a
+  // workgroup takes one (range, chunk) and walks the range's tiles, so its B
+  // chunk changes only where the slot does, and the workgroups of one range
+  // (one per chunk) sweep the same rows together
+  const int nck = p.rows_nck_total;
+  const int G = (int)gridDim.x;
+  const int nr = max(1, G / nck);
+  const int tpr = (live + nr - 1) / nr;
+  uint16_t *y = reinterpret_cast<uint16_t *>(p.y);
+
+  // tile header; tk[q] is this lane's token of block q (unspecified past the
+  // tile's rows, so never used there), tfirst the tile's first token, which
+  // lanes past the rows read instead
+  struct Header {
+    int slot, rows, pos0, tfirst, tk[4];
+  };
+  auto read_header = [&](int i) {
+    const int32_t *tl = tiles + (int64_t)(t0 + i) * kTileInts;
+    return Header{tl[0], tl[1], tl[2], tl[4], {tl[4 + n], tl[4 + 16 + n], tl[4 + 32 + n], tl[4 + 48 + n]}};
+  };
+  auto tok_of = [](const Header h, int tb) __attribute__((always_inline)) {
+    return tb == 0 ? h.tk[0] : (tb == 1 ? h.tk[1] : (tb == 2 ? h.tk[2] : h.tk[3]));
+  };
+
+  for (int unit = (int)blockIdx.x; unit < nr * nck; unit += G) {
+    const int ck = unit % nck, rng = unit / nck;
+    const int ta = rng * tpr, tz = min(live, ta + tpr);
+    if (ta >= tz) continue;
+    // chunk -> slice s and its first column in the slice
+    int s = 0, cbase = 0, acc = 0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      if (k >= p.n_slices) break;
+      if (ck >= acc) {
+        s = k;
+        cbase = acc;
+      }
+      acc += uniform_value(p.rows_nck[k]);
+    }
+    const int w = (int)pick<NS>(p.width, s, p.n_slices);
+    const int col0 = (ck - cbase) * kRowsCols;
+    const int64_t yo = pick<NS>(p.offset, s, p.n_slices) + col0 + 128 * wave;  // this wave's first column
+    const int wcol = col0 + 128 * wave;                                      // ... in the slice
+    const uint16_t *bslice = reinterpret_cast<const uint16_t *>(pick<NS>(p.B, s, p.n_slices));
+    const int64_t bstride = pick<NS>(p.b_stride, s, p.n_slices);
+
+    // the rank rows and y of token block tb of a tile into register set b.
+    // Both go through buffer resources with 32-bit offsets: the four y
+    // pieces of a lane share one row offset (the 64-byte steps are immediate
+    // offsets), the low plane follows the high one; pieces past the slice
+    // are read anyway (they are never stored) and reads past y return zeros
+    const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
+    const rsrc_t ur = make_rsrc(p.uh, 2 * p.plane_bytes);
+    const uint32_t uplane = p.plane_bytes;
+    u32x4 uhv[2][KS], ulv[2][KS];
+    u32x4 yv[2][4];
+    auto row_off = [&](int64_t row) { return (uint32_t)((row * p.ldy + yo + 8 * kg) * 2); };
+    // issued for every block slot, even past the tile's last block (then
+    // every piece reads zeros): no load sits behind a branch, so the wait
+    // before a block's products counts only the loads issued after it
+    // (the register set is a compile-time constant: a runtime index would put
+    // the sets in scratch memory)
+    auto load_block = [&](const Header h, int tb, auto bc) __attribute__((always_inline)) {
+      constexpr int b = decltype(bc)::value;
+      const int rows = uniform_value(h.rows);
+      const bool bv = 16 * tb < rows;                // the block exists
+      const bool rv = 16 * tb + n < rows;
+      const int64_t pos = uniform_value(h.pos0) + 16 * tb + (rv ? n : 0);
+      // ranks 32 c + 8 kg .. + 7 of k-step c; ranks past R read zeros
+      const uint32_t uo = bv ? (uint32_t)((((int64_t)s * T + pos) * R + 8 * kg) * 2) : kOut;
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const uint32_t o = 32 * c + 8 * kg < R ? uo + 64 * c : kOut;
+        uhv[b][c] = buf_load16(ur, o);
+        ulv[b][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ur, o, uplane, 0));
+      }
+      const uint32_t yo32 =
+          p.add && bv ? row_off(rv ? (int64_t)tok_of(h, tb < 4 ? tb : 0) : (int64_t)h.tfirst) : kOut;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) yv[b][pp] = buf_load16(yr, yo32 + 64 * pp);
+    };
+
+    bf16x8 bt[KS][8];
+    int cur = -2;      // slot whose chunk is in bt
+    Header hd = read_header(ta);
+    Header hn = hd;
+    if (ta + 1 < tz) hn = read_header(ta + 1);
+    for (int ti = ta; ti < tz; ++ti) {
+      const int slot = uniform_value(hd.slot), rows = uniform_value(hd.rows);
+      const int nb = (rows + 15) / 16;
+      if (slot < 0) {  // store mode, no adapter: the windows become 0
+        for (int tb = 0; tb < nb; ++tb) {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const int c = 32 * pp + 8 * kg;
+            if (16 * tb + n < rows && wcol + c < w)
+              gstore16(y + (int64_t)tok_of(hd, tb) * p.ldy + yo + c, u32x4{0, 0, 0, 0});
+          }
+        }
+      } else {
+        load_block(hd, 0, std::integral_constant<int, 0>{});
+        if (slot != cur) {
+          // ---- the slot's chunk of B (rows j < RP, 512 columns) into LDS
+          // straight from memory, one row per wave instruction (lane l's 16
+          // bytes at 16 l; ranks past the slot's rank and columns past the
+          // slice read as zeros), then this wave's B^T operands into
+          // registers.  Block pair pp of the wave: columns 128 w + 32 pp +
+          // 8 h + i (h, i < 4) go to block 2 pp (i < 4) and 2 pp + 1 (i + 4):
+          // lane 4 e + h of a 16-lane group names 4 columns of rank row e, and
+          // the transposing read hands lane m the column 8 (m / 4) + m % 4
+          // (+ 4), so a lane's 8 outputs of the pair are 8 consecutive
+          // columns of one token.
+          const int rk = slot_rank_of(p.slot_rank, slot, R);
+          const rsrc_t br = make_rsrc(bslice + (int64_t)slot * bstride, (uint32_t)(R * w * 2));
+          const int c8 = col0 + 8 * lane;
+          __syncthreads();  // every wave has read the previous chunk
+#pragma unroll
+          for (int jj = 0; jj < RK / 4; ++jj) {
+            const int j = wave + 4 * jj;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                br, (__attribute__((address_space(3))) void *)(rows_lds + j * kRowsLdb), 16,
+                (j < rk && c8 < w) ? (uint32_t)((j * w + c8) * 2) : kOut, 0, 0, 0);
+          }
+          __builtin_amdgcn_s_waitcnt(0);  // loads return in order: the chunk (and the block loads) are in
+          __syncthreads();
+          // (8 ranks a lane: two transposing reads, rank rows 32 c + 8 kg .. + 3
+          // and + 4 .. + 7)
+          const int l = lane % 16;
+#pragma unroll
+          for (int c = 0; c < KS; ++c)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+              const uint16_t *a = rows_lds + (32 * c + 8 * kg + l / 4) * kRowsLdb + 128 * wave + 32 * (b / 2) +
+                                  8 * (l % 4) + 4 * (b % 2);
+              const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a)));
+              const u32x2 hi =
+                  __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a + 4 * kRowsLdb)));
+              bt[c][b] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+            }
+          cur = slot;
+        }
+        // ---- token blocks, two per trip (register sets 0 and 1 named at
+        // compile time; a runtime trip count keeps the compiler from hoisting
+        // later blocks' loads): products, then y, 16 bytes per lane; the next
+        // block's rank rows and y are in flight meanwhile
+        auto compute = [&](int tb, auto bc) __attribute__((always_inline)) {
+          constexpr int b = decltype(bc)::value;
+          const bool rv = 16 * tb + n < rows;
+          const uint32_t yst = row_off(rv ? (int64_t)tok_of(hd, tb) : (int64_t)hd.tfirst);
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KS; ++c) {
+              const bf16x8 uh8 = __builtin_bit_cast(bf16x8, uhv[b][c]), ul8 = __builtin_bit_cast(bf16x8, ulv[b][c]);
+              a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp], ul8, a0, 0, 0, 0);
+              a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp], uh8, a0, 0, 0, 0);
+              a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp + 1], ul8, a1, 0, 0, 0);
+              a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp + 1], uh8, a1, 0, 0, 0);
+            }
+            // stores of lanes past the rows or the slice go past the resource
+            // and are dropped (no store behind a branch either)
+            const int c = 32 * pp + 8 * kg;
+            const u32x4 old = yv[b][pp];
+            u32x4 o;
+            o[0] = pack_bf16x2(bf16_lo(old[0]) + a0[0], bf16_hi(old[0]) + a0[1]);
+            o[1] = pack_bf16x2(bf16_lo(old[1]) + a0[2], bf16_hi(old[1]) + a0[3]);
+            o[2] = pack_bf16x2(bf16_lo(old[2]) + a1[0], bf16_hi(old[2]) + a1[1]);
+            o[3] = pack_bf16x2(bf16_lo(old[3]) + a1[2], bf16_hi(old[3]) + a1[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), yr,
+                                                   rv && wcol + c < w ? yst + 64 * pp : kOut, 0, 0);
+          }
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        for (int tb = 0; tb < nb; tb += 2) {
+          load_block(hd, tb + 1, S1{});
+          compute(tb, S0{});
+          if (tb + 1 >= nb) break;
+          load_block(hd, tb + 2, S0{});
+          compute(tb + 1, S1{});
+        }
+      }
+      hd = hn;
+      if (ti + 2 < tz) hn = read_header(ti + 2);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 template <typename E, int R>
@@ -540,6 +800,96 @@ static hipError_t launch_mma_ns(const ExpandParams &p, int64_t bound, hipStream_
 template <int R>
 static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, hipStream_t stream) {
   return with_slice_bound(p.n_slices, [&](auto ns) { return launch_mma_ns<R, decltype(ns)::value>(p, bound, stream); });
+}
+
+// Long-segment expand, one instantiation (dynamic LDS: the B chunk).
+template <int R, int NS>
+static hipError_t launch_rows_ns(const ExpandParams &p, int64_t bound, hipStream_t stream) {
+  static std::atomic<int> resident[kMaxDevices];
+  constexpr int RK = R < 32 ? 32 : R;
+  constexpr size_t lds = (size_t)RK * kRowsLdb * 2;
+  const void *fn = reinterpret_cast<const void *>(&expand_rows_kernel<R, NS>);
+  if (lds > 65536) {  // more than the default dynamic LDS
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int grid = xcd_grid(bound, resident_groups(resident, fn, kXThreads, lds));
+  hipLaunchKernelGGL((expand_rows_kernel<R, NS>), dim3(grid), dim3(kXThreads), lds, stream, p.meta.info,
+                     p.meta.tiles, p);
+  return hipGetLastError();
+}
+
+// The long-segment expand serves this call?  Whole tiles are likely when the
+// batch has at least 64 tokens per possible segment.  LORA_EXPAND_ROWS=0 or 1
+// forces the choice (tuning).
+bool expand_rows_fits(int64_t T, int32_t S, bool bf16, int mode) {
+  if (!bf16 || mode == 1) return false;
+  const int v = expand_rows_knob();
+  if (v >= 0) return v == 1;
+  return T >= 64 * ((int64_t)S + 1);
+}
+
+// y bytes a call's windows reach, and whether y and the u planes fit the
+// long-segment expand's 32-bit buffer offsets (with room past their ends for
+// the pieces it reads and never stores).
+static int64_t rows_y_bytes(int64_t T, int32_t n_slices, const int64_t *width, const int64_t *offset, int64_t ldy) {
+  int64_t y_end = 0;
+  for (int s = 0; s < n_slices; ++s) y_end = std::max(y_end, offset[s] + width[s]);
+  return ((T - 1) * ldy + y_end) * 2;
+}
+bool expand_rows_addressable(int64_t T, int32_t n_slices, const int64_t *width, const int64_t *offset, int64_t ldy,
+                             int32_t R) {
+  if (T == 0) return true;
+  return rows_y_bytes(T, n_slices, width, offset, ldy) + 4096 < 0x7FFFFFF0LL &&
+         (int64_t)n_slices * T * R * 2 < ((int64_t)1 << 30);
+}
+
+hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, uint16_t *planes, int32_t n_slices,
+                              const void *const *B, const int64_t *b_stride, const int64_t *width,
+                              const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y, int64_t ldy,
+                              int add, hipStream_t stream) {
+  const int64_t T = meta.T;
+  if (T == 0) return hipSuccess;
+  const int64_t plane = (int64_t)n_slices * T * R;
+  {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((plane / 4 + 255) / 256, 2048));
+    hipLaunchKernelGGL(u_planes_kernel, dim3(grid), dim3(256), 0, stream, meta.info, part, T, n_slices, R, kch,
+                       planes, planes + plane);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ExpandParams p{};
+  p.meta = meta;
+  p.n_slices = n_slices;
+  p.uh = planes;
+  p.ul = planes + plane;
+  p.rows_nck_total = 0;
+  for (int s = 0; s < n_slices; ++s) {
+    p.B[s] = B[s];
+    p.b_stride[s] = b_stride[s];
+    p.width[s] = width[s];
+    p.offset[s] = offset[s];
+    p.rows_nck[s] = (int32_t)((width[s] + kRowsCols - 1) / kRowsCols);
+    p.rows_nck_total += p.rows_nck[s];
+  }
+  p.y = y;
+  p.ldy = ldy;
+  p.add = add ? 1 : 0;
+  p.slot_rank = slot_rank;
+  p.y_bytes = (uint32_t)rows_y_bytes(T, n_slices, width, offset, ldy);
+  p.plane_bytes = (uint32_t)(plane * 2);
+  // one workgroup per (tile range, chunk): as many as stay resident
+  const int64_t bound = max_tiles(T, meta.S) * p.rows_nck_total;
+  return with_slice_bound(n_slices, [&](auto ns) -> hipError_t {
+    constexpr int NS = decltype(ns)::value;
+    switch (R) {
+      case 8: return launch_rows_ns<8, NS>(p, bound, stream);
+      case 16: return launch_rows_ns<16, NS>(p, bound, stream);
+      case 32: return launch_rows_ns<32, NS>(p, bound, stream);
+      case 64: return launch_rows_ns<64, NS>(p, bound, stream);
+    }
+    return hipErrorInvalidValue;
+  });
 }
 
 // Matrix-core expand: the bf16 path of SGMV and AUTO (tile heights follow the

@@ -506,7 +506,8 @@ static int mma_col_blocks(int32_t n_slices, int32_t R) {
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
                          int32_t R, float scale, const float *slot_scale, const int32_t *slot_rank,
-                         float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream) {
+                         float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream,
+                         bool to_partials) {
   const ShrinkConfig c = plan_shrink(meta.T, meta.S, d_in, R, bf16, mode);
   if (kch_out) *kch_out = c.kch;
   ShrinkParams p{};
@@ -522,7 +523,7 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   p.scale = scale;
   p.slot_scale = slot_scale;
   p.slot_rank = slot_rank;
-  p.out = c.kch == 1 ? u : reinterpret_cast<float *>(ws);
+  p.out = c.kch == 1 && !to_partials ? u : reinterpret_cast<float *>(ws);
   p.u_sorted = for_apply ? 1 : 0;
   p.kc = c.kc;
   p.kch = c.kch;
