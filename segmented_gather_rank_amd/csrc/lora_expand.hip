@@ -53,9 +53,9 @@ struct ExpandParams {
   int64_t ldy;
   int32_t add;
   const int32_t *slot_rank;  // per-slot ranks, or null (every slot uses R)
-  // long-segment path: the rank-r rows as bf16 high and low planes
-  // [n_slices][T][R] each, in sorted-position order, and 512-column chunks
-  const uint16_t *uh, *ul;
+  // long-segment path: the rank-r rows rounded to bf16 [n_slices][T][R], in
+  // sorted-position order, and 512-column chunks
+  const uint16_t *uh;
   int32_t rows_nck[kMaxSlices];       // 512-column chunks per slice
   int32_t rows_nck_total;
   uint32_t y_bytes;                   // bytes of y the windows reach (< 2^31)
@@ -540,20 +540,21 @@ __global__ __launch_bounds__(kExpThreads) void expand_kernel(ExpandParams p) {
 // B^T operands of a wave's columns stay in registers while the slot does not
 // change (the chunk goes to LDS straight from memory, then into registers
 // through the transposing read), so the token loop has no LDS traffic and no
-// barrier.  The rank-r rows come as
-// bf16 high and low planes that a small kernel folds from the shrink's
-// partial sums once per call; the loop prefetches the next token block's
-// planes and y.
+// barrier.  The rank-r rows come as one bf16 plane that a small kernel folds
+// from the shrink's partial sums once per call: u is rounded to bf16 once, as
+// the matrix cores take it, so a 32-rank step is one product (a high and a low
+// part, two products, cost 9 % of the call here).  The loop prefetches the
+// next token block's plane rows and y.
 
 constexpr int kRowsCols = 512;             // columns per item, 128 per wave
 constexpr int kRowsLdb = kRowsCols + 16;   // LDS row stride of the B chunk
 
-// u planes: uh[i] + ul[i] = sum over k-chunks, in order, of the partial sums
-// at i (the split of fp32 into bf16 high and low parts, as the MFMA operands
-// take them).  Rows of tokens without an adapter are skipped.
+// u plane: ub[i] = the sum over k-chunks, in order, of the partial sums at i,
+// rounded once to bf16 (nearest even), as the MFMA operand takes it.  Rows of
+// tokens without an adapter are skipped.
 __global__ __launch_bounds__(256) void u_planes_kernel(const int32_t *__restrict__ info, const float *part,
                                                        int64_t T, int32_t n_slices, int32_t R, int32_t kch,
-                                                       uint16_t *uh, uint16_t *ul) {
+                                                       uint16_t *ub) {
   const int64_t plane = (int64_t)n_slices * T * R;
   const int64_t lo_pos = info[3];  // first sorted position with an adapter
   const int64_t quads = plane / 4;
@@ -562,23 +563,19 @@ __global__ __launch_bounds__(256) void u_planes_kernel(const int32_t *__restrict
     const int64_t pos = (i / R) % T;
     if (pos < lo_pos) continue;
     const f32x4 v = sum_partials4(part + i, plane, kch);
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) split_bf16(v[m], h[m], l[m]);
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2 *>(uh + i) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    *reinterpret_cast<u32x2 *>(ul + i) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    *reinterpret_cast<u32x2 *>(ub + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
 
 template <int R, int NS>
-__global__ __launch_bounds__(kXThreads, 2) void expand_rows_kernel(const int32_t *__restrict__ info,
+__global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel(const int32_t *__restrict__ info,
                                                                    const int32_t *__restrict__ tiles,
                                                                    ExpandParams p) {
   constexpr int RK = R < 32 ? 32 : R;          // ranks padded to whole 32-rank MFMA steps
   constexpr int KS = RK / 32;                  // MFMA k-steps
   constexpr uint32_t kOut = 0x7FFFFFF0u;       // past every resource: reads as zeros
-  extern __shared__ __align__(16) uint16_t rows_lds[];  // B chunk [RK][kRowsLdb]
+  extern __shared__ __align__(16) uint16_t rows_lds[];  // one 32-rank step of the B chunk [32][kRowsLdb]
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -641,9 +638,8 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_rows_kernel(const int32_t
     // offsets), the low plane follows the high one; pieces past the slice
     // are read anyway (they are never stored) and reads past y return zeros
     const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
-    const rsrc_t ur = make_rsrc(p.uh, 2 * p.plane_bytes);
-    const uint32_t uplane = p.plane_bytes;
-    u32x4 uhv[2][KS], ulv[2][KS];
+    const rsrc_t ur = make_rsrc(p.uh, p.plane_bytes);
+    u32x4 uhv[2][KS];
     u32x4 yv[2][4];
     auto row_off = [&](int64_t row) { return (uint32_t)((row * p.ldy + yo + 8 * kg) * 2); };
     // issued for every block slot, even past the tile's last block (then
@@ -663,7 +659,6 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_rows_kernel(const int32_t
       for (int c = 0; c < KS; ++c) {
         const uint32_t o = 32 * c + 8 * kg < R ? uo + 64 * c : kOut;
         uhv[b][c] = buf_load16(ur, o);
-        ulv[b][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ur, o, uplane, 0));
       }
       const uint32_t yo32 =
           p.add && bv ? row_off(rv ? (int64_t)tok_of(h, tb < 4 ? tb : 0) : (int64_t)h.tfirst) : kOut;
@@ -704,30 +699,31 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_rows_kernel(const int32_t
           const int rk = slot_rank_of(p.slot_rank, slot, R);
           const rsrc_t br = make_rsrc(bslice + (int64_t)slot * bstride, (uint32_t)(R * w * 2));
           const int c8 = col0 + 8 * lane;
-          __syncthreads();  // every wave has read the previous chunk
-#pragma unroll
-          for (int jj = 0; jj < RK / 4; ++jj) {
-            const int j = wave + 4 * jj;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                br, (__attribute__((address_space(3))) void *)(rows_lds + j * kRowsLdb), 16,
-                (j < rk && c8 < w) ? (uint32_t)((j * w + c8) * 2) : kOut, 0, 0, 0);
-          }
-          __builtin_amdgcn_s_waitcnt(0);  // loads return in order: the chunk (and the block loads) are in
-          __syncthreads();
-          // (8 ranks a lane: two transposing reads, rank rows 32 c + 8 kg .. + 3
-          // and + 4 .. + 7)
           const int l = lane % 16;
+          // one 32-rank step at a time through a 32-row LDS buffer
 #pragma unroll
-          for (int c = 0; c < KS; ++c)
+          for (int c = 0; c < KS; ++c) {
+            __syncthreads();  // every wave has read the buffer's previous contents
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int jl = wave + 4 * jj, j = 32 * c + jl;
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  br, (__attribute__((address_space(3))) void *)(rows_lds + jl * kRowsLdb), 16,
+                  (j < rk && c8 < w) ? (uint32_t)((j * w + c8) * 2) : kOut, 0, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // loads return in order: these rows (and the block loads) are in
+            __syncthreads();
+            // 8 ranks a lane: two transposing reads, rank rows 8 kg .. + 3 and + 4 .. + 7
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
-              const uint16_t *a = rows_lds + (32 * c + 8 * kg + l / 4) * kRowsLdb + 128 * wave + 32 * (b / 2) +
-                                  8 * (l % 4) + 4 * (b % 2);
+              const uint16_t *a = rows_lds + (8 * kg + l / 4) * kRowsLdb + 128 * wave + 32 * (b / 2) + 8 * (l % 4) +
+                                  4 * (b % 2);
               const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a)));
               const u32x2 hi =
                   __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(a + 4 * kRowsLdb)));
               bt[c][b] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
             }
+          }
           cur = slot;
         }
         // ---- token blocks, two per trip (register sets 0 and 1 named at
@@ -743,11 +739,9 @@ __global__ __launch_bounds__(kXThreads, 2) void expand_rows_kernel(const int32_t
             f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < KS; ++c) {
-              const bf16x8 uh8 = __builtin_bit_cast(bf16x8, uhv[b][c]), ul8 = __builtin_bit_cast(bf16x8, ulv[b][c]);
-              a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp], ul8, a0, 0, 0, 0);
-              a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp], uh8, a0, 0, 0, 0);
-              a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp + 1], ul8, a1, 0, 0, 0);
-              a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp + 1], uh8, a1, 0, 0, 0);
+              const bf16x8 u8 = __builtin_bit_cast(bf16x8, uhv[b][c]);
+              a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp], u8, a0, 0, 0, 0);
+              a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp + 1], u8, a1, 0, 0, 0);
             }
             // stores of lanes past the rows or the slice go past the resource
             // and are dropped (no store behind a branch either)
@@ -806,8 +800,7 @@ static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, hipStream_t
 template <int R, int NS>
 static hipError_t launch_rows_ns(const ExpandParams &p, int64_t bound, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];
-  constexpr int RK = R < 32 ? 32 : R;
-  constexpr size_t lds = (size_t)RK * kRowsLdb * 2;
+  constexpr size_t lds = (size_t)32 * kRowsLdb * 2;
   const void *fn = reinterpret_cast<const void *>(&expand_rows_kernel<R, NS>);
   if (lds > 65536) {  // more than the default dynamic LDS
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -854,7 +847,7 @@ hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, 
   {
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((plane / 4 + 255) / 256, 2048));
     hipLaunchKernelGGL(u_planes_kernel, dim3(grid), dim3(256), 0, stream, meta.info, part, T, n_slices, R, kch,
-                       planes, planes + plane);
+                       planes);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -862,7 +855,6 @@ hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, 
   p.meta = meta;
   p.n_slices = n_slices;
   p.uh = planes;
-  p.ul = planes + plane;
   p.rows_nck_total = 0;
   for (int s = 0; s < n_slices; ++s) {
     p.B[s] = B[s];

@@ -105,7 +105,7 @@ bool expand_rows_addressable(int64_t T, int32_t n_slices, const int64_t *width, 
                              int32_t R);
 int expand_rows_knob();
 // It runs on the shrink's partial sums [kch][n_slices][T][R] (sorted order),
-// folded into bf16 high and low planes at `planes` (n_slices * T * R * 4 bytes).
+// folded into one bf16 plane at `planes` (n_slices * T * R * 2 bytes).
 hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, uint16_t *planes, int32_t n_slices,
                               const void *const *B, const int64_t *b_stride, const int64_t *width,
                               const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y, int64_t ldy,
