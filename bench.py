@@ -81,6 +81,7 @@ KERNEL_SOURCES = {   # the sources each measured kernel is built from
     "bgmv_split": ["lora_bgmv_split.hip"],
     "bgmv_fused_kernel": ["lora_bgmv.hip"],
     "shrink+expand": ["lora_shrink.hip", "lora_expand.hip"],
+    "shrink+u_planes+expand_rows": ["lora_shrink.hip", "lora_expand.hip"],
 }
 
 
@@ -137,7 +138,26 @@ def dominant_kernel(c, mode):
         return "bgmv_split"
     if enabled and decode and sw // 8 <= 1024 and c.d_in * e <= 32768 and w_tok <= (1 << 20):
         return "bgmv_fused_kernel"
+    if rows_takes(c, mode):
+        return "shrink+u_planes+expand_rows"
     return "shrink+expand"
+
+
+def rows_takes(c, mode):
+    """Whether the call's expand runs on the long-segment kernel: bf16, AUTO or
+    SGMV, at least 64 tokens per possible segment, and y and the rank rows
+    within its 32-bit buffer offsets (LORA_EXPAND_ROWS=0/1 forces it)."""
+    force = os.environ.get("LORA_EXPAND_ROWS", "")
+    if c.dtype != "bf16" or mode == "bgmv":
+        return False
+    if force:
+        ok = int(force) > 0
+    else:
+        ok = c.T >= 64 * (c.num_slots + 1)
+    ldy = getattr(c, "ldy", None) or max(o + w for o, w in zip(c.offsets, c.widths))
+    y_end = max(o + w for o, w in zip(c.offsets, c.widths))
+    y_bytes = ((c.T - 1) * ldy + y_end) * 2
+    return ok and y_bytes + 4096 < 0x7FFFFFF0 and c.n_slices * c.T * c.r_max * 2 < (1 << 30)
 
 
 def split_takes(c):
@@ -339,7 +359,8 @@ def summarize_mfma(c, k, d, kernel_key):
         *rows,
         "",
         f"Per launch {flops / 1e9:.3f} GFLOP issued on the matrix cores against {alg_f / 1e9:.3f} GFLOP algorithmic "
-        f"({flops / alg_f:.2f}x: the expand multiplies the rank-r rows as bf16 high and low parts, two products).",
+        f"({flops / alg_f:.2f}x; above 1 where a kernel multiplies the rank-r rows as bf16 high and low parts, or "
+        "pads a short tile to a whole 16-token block).",
         "The bench divides the issued figure by its own measured duration of the call.",
         "",
         f"- kernel sources: {source_digest(kernel_key)}",
