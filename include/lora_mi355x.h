@@ -27,7 +27,9 @@
  *   - Element types: x, A, B and y share one dtype, fp32 or bf16; the rank-r
  *     buffer u is always fp32; scales are fp32.  Accumulation is fp32.  bf16
  *     outputs are rounded once, to nearest even, when y is stored.
- *   - Supported shapes: 1 <= S <= 1023, r_max in {8, 16, 32, 64}, d_in and every
+ *   - Supported shapes: 1 <= S <= 1023, r_max a multiple of 8 in [8, 128]
+ *     (the kernels run at the next of 8, 16, 32, 64, 128 and read ranks past
+ *     r_max as zeros; A, B and u keep r_max as their rank extent), d_in and every
  *     slice width a multiple of 8, 1 <= n_slices <= 8, every device pointer
  *     16-byte aligned, ldx and ldy multiples of 8, (r_max + 1) * d_in and
  *     (r_max + 1) * width below 2^28 (one slot's factor matrix is addressed with
@@ -259,9 +261,9 @@ lora_status lora_apply_workspace_init(void *d_ws, size_t ws_bytes, void *stream)
 /* Shrink then expand on one stream: the whole delta of one layer, added into
  * (or stored to) the slices of y.  Arguments as in lora_shrink and lora_expand;
  * the rank-r buffer lives in d_ws.  Decode-shaped calls (few tokens per slot,
- * small per-token factors, mode AUTO or BGMV) run as one fused kernel that keeps
- * each token's rank-r vector on chip; the others run the shrink and expand
- * kernels.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
+ * small per-token factors, mode AUTO or BGMV, r_max one of 8, 16, 32, 64) run
+ * as one fused kernel that keeps each token's rank-r vector on chip; the others
+ * run the shrink and expand kernels.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
  * 服务", section "调用链" (add_lora_linear = shrink into an fp32 buffer, then
  * expand into the output slices).
  *   d_ws      workspace of at least lora_apply_workspace_bytes bytes, 16-byte

@@ -98,7 +98,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 7:
+if _lib.lora_abi_version() != 8:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 

@@ -87,11 +87,11 @@ hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t stream) {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 7;
+constexpr int32_t kAbiVersion = 8;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool rank_ok(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
+bool rank_ok(int32_t r) { return tile_rank(r) != 0; }
 bool dtype_ok(lora_dtype d) { return d == LORA_F32 || d == LORA_BF16; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool mode_ok(lora_mode m) { return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV || m == LORA_MODE_SGMV; }
@@ -217,8 +217,8 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   st = check_expand_args(meta, u, n_slices, B, width, offset, r_max, d_y, ldy, dtype, mode);
   if (st != LORA_OK) return st;
   if (!aligned4(d_slot_rank)) return LORA_ERR_INVALID_ARG;
-  const size_t ubytes = align256(sizeof(float) * (size_t)n_slices * (size_t)meta->num_tokens *
-                                 (size_t)r_max);
+  const int32_t R = tile_rank(r_max);  // the kernels' rank; A, B and the caller's u keep r_max
+  const size_t ubytes = align256(sizeof(float) * (size_t)n_slices * (size_t)meta->num_tokens * (size_t)R);
   void *sh_ws = ws + kSyncBytes + ubytes;
   const size_t sh_bytes = ws_bytes - kSyncBytes - ubytes;
   const void *aptr[kMaxSlices], *bptr[kMaxSlices];
@@ -228,9 +228,10 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   const MetaView mv = view_of(meta);
   // decode-shaped (BGMV requested, or few tokens per slot): the split kernel
   // first (bf16; it checks its own limits), then the per-token kernel when
-  // its limits hold
+  // its limits hold; both take r_max of 8, 16, 32 or 64 only
   const bool decode = (int)mode != 2 && ((int)mode == 1 || meta->num_tokens <= 16 * (int64_t)meta->num_slots);
-  if (!fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
+  const bool fused_rank = r_max == R && R <= 64;
+  if (fused_rank && !fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
     bool used = false;
     const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
                                            r_max, scale, d_slot_scale, d_slot_rank, d_y, ldy, add_into_y, sync,
@@ -238,28 +239,29 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
     if (e != hipSuccess) return LORA_ERR_HIP;
     if (used) return LORA_OK;
   }
-  if (!fused_disabled() && bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width,
-                                     r_max, ldy, dtype == LORA_BF16, (int)mode)) {
+  if (fused_rank && !fused_disabled() &&
+      bgmv_fits(meta->num_tokens, meta->num_slots, d_in, n_slices, width, r_max, ldy, dtype == LORA_BF16,
+                (int)mode)) {
     const hipError_t e = launch_bgmv(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr,
                                      bptr, bstr, width, offset, r_max, scale, d_slot_scale,
                                      d_slot_rank, d_y, ldy, add_into_y, s);
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   int kch = 1;
-  const bool rows = expand_rows_fits(meta->num_tokens, meta->num_slots, dtype == LORA_BF16, (int)mode) &&
-                    expand_rows_addressable(meta->num_tokens, n_slices, width, offset, ldy, r_max);
-  hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, r_max,
+  const bool rows = expand_rows_fits(meta->num_tokens, meta->num_slots, dtype == LORA_BF16, (int)mode, R) &&
+                    expand_rows_addressable(meta->num_tokens, n_slices, width, offset, ldy, R);
+  hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, R, r_max,
                                scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s, rows);
   if (e != hipSuccess) return LORA_ERR_HIP;
   if (rows) {  // long segments: the sums become bf16 planes in the rank buffer, then the row-stream expand
     e = launch_expand_rows(mv, static_cast<const float *>(sh_ws), kch, reinterpret_cast<uint16_t *>(u), n_slices,
-                           bptr, bstr, width, offset, r_max, d_slot_rank, d_y, ldy, add_into_y, s);
+                           bptr, bstr, width, offset, R, r_max, d_slot_rank, d_y, ldy, add_into_y, s);
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   // the rank-r rows are in sorted order; with a split d_in they are still the
   // partial sums, which the expand adds
   const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
-  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, r_max,
+  e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, R, r_max,
                     d_slot_rank, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -380,8 +382,9 @@ lora_status lora_shrink_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int3
   if (S > kMaxSlots || n_slices < 1 || n_slices > kMaxSlices || !rank_ok(r_max) ||
       !dtype_ok(dtype) || !mode_ok(mode))
     return LORA_ERR_UNSUPPORTED;
-  const ShrinkConfig c = plan_shrink(T, S, d_in, r_max, dtype == LORA_BF16, (int)mode);
-  *bytes = shrink_ws_bytes(c, T, n_slices, r_max);
+  const int32_t R = tile_rank(r_max);
+  const ShrinkConfig c = plan_shrink(T, S, d_in, R, dtype == LORA_BF16, (int)mode);
+  *bytes = shrink_ws_bytes(c, T, n_slices, R);
   return LORA_OK;
 }
 
@@ -403,7 +406,7 @@ lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx, int
   unpack(A, n_slices, ptrs, strides);
   const hipError_t e =
       launch_shrink(view_of(meta), d_x, ldx, d_in, dtype == LORA_BF16, n_slices, ptrs, strides,
-                    r_max, scale, d_slot_scale, d_slot_rank, d_u, (int)mode, d_ws, false, nullptr,
+                    tile_rank(r_max), r_max, scale, d_slot_scale, d_slot_rank, d_u, (int)mode, d_ws, false, nullptr,
                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -420,7 +423,7 @@ lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slice
   int64_t strides[kMaxSlices];
   unpack(B, n_slices, ptrs, strides);
   const hipError_t e = launch_expand(view_of(meta), d_u, 0, 1, n_slices, ptrs, strides, width,
-                                     offset, r_max, d_slot_rank, d_y, ldy, dtype == LORA_BF16,
+                                     offset, tile_rank(r_max), r_max, d_slot_rank, d_y, ldy, dtype == LORA_BF16,
                                      add_into_y, (int)mode, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -431,15 +434,17 @@ lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32
   size_t sh = 0;
   const lora_status st = lora_shrink_workspace_bytes(T, S, d_in, n_slices, r_max, dtype, mode, &sh);
   if (st != LORA_OK) return st;
+  const int32_t R = tile_rank(r_max);  // the kernels' rank
   // the split decode kernel's partial rank rows share the shrink's region
-  if (dtype == LORA_BF16 && mode != LORA_MODE_SGMV) sh = std::max(sh, split_ws_bytes(T, S, n_slices, r_max));
+  if (dtype == LORA_BF16 && mode != LORA_MODE_SGMV && r_max == R && R <= 64)
+    sh = std::max(sh, split_ws_bytes(T, S, n_slices, R));
   // the long-segment expand takes the shrink's sums from that region even
   // without a split of d_in
-  if (expand_rows_fits(T, S, dtype == LORA_BF16, (int)mode))
-    sh = std::max(sh, align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max));
-  // rendezvous words, then the rank-r buffer, then the shrink's or the split
+  if (expand_rows_fits(T, S, dtype == LORA_BF16, (int)mode, R))
+    sh = std::max(sh, align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)R));
+  // rendezvous words, then the rank-R buffer, then the shrink's or the split
   // kernel's partial sums
-  *bytes = kSyncBytes + align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)r_max) + sh;
+  *bytes = kSyncBytes + align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)R) + sh;
   return LORA_OK;
 }
 

@@ -234,6 +234,18 @@ __device__ __forceinline__ int slot_rank_of(const int32_t *slot_rank, int slot, 
   return r <= 0 ? 0 : (r >= R ? R : (r + 7) & ~7);
 }
 
+// ---------------------------------------------------------------- factor rows
+
+// The kernels are built for a rank R in {8, 16, 32, 64, 128} and walk a
+// slot's A as a packed [k][R] block; the caller's matrix is [d_in][ra] with
+// ra = r_max, a multiple of 8 and at most R.  Element e of the packed block
+// (row e / R, rank e % R) lives at e / R * ra + e % R, and ranks past ra read
+// as zeros (rank_limit caps the ranks a kernel reads at ra).
+template <int R>
+__device__ __forceinline__ int64_t packed_to_factor(int64_t e, int ra) {
+  return R == 0 ? e : (e / R) * ra + (e % R);
+}
+
 // ---------------------------------------------------------------- metadata view
 
 struct MetaView {
@@ -376,15 +388,16 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over the lanes of a wave that share (lane mod JO), JO in {1,2,4,8}: DPP
+// Sum over the lanes of a wave that share (lane mod JO), JO in {1,2,4,8,16}: DPP
 // row rotations inside each 16-lane row, then the gfx950 permlane16 and
 // permlane32 swaps across rows.
 template <int JO>
 __device__ __forceinline__ float wave_sum_mod(float v) {
-  if constexpr (JO < 2) v += dpp_f32<0x121>(v);  // row_ror:1
-  if constexpr (JO < 4) v += dpp_f32<0x122>(v);  // row_ror:2
-  if constexpr (JO < 8) v += dpp_f32<0x124>(v);  // row_ror:4
-  v += dpp_f32<0x128>(v);                        // row_ror:8
+  static_assert(JO == 1 || JO == 2 || JO == 4 || JO == 8 || JO == 16, "lanes share a residue mod 1..16");
+  if constexpr (JO < 2) v += dpp_f32<0x121>(v);   // row_ror:1
+  if constexpr (JO < 4) v += dpp_f32<0x122>(v);   // row_ror:2
+  if constexpr (JO < 8) v += dpp_f32<0x124>(v);   // row_ror:4
+  if constexpr (JO < 16) v += dpp_f32<0x128>(v);  // row_ror:8
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

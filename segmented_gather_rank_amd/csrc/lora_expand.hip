@@ -60,6 +60,8 @@ struct ExpandParams {
   int32_t rows_nck_total;
   uint32_t y_bytes;                   // bytes of y the windows reach (< 2^31)
   uint32_t plane_bytes;               // bytes of one u plane (< 2^30)
+  int32_t ra;                         // the caller's r_max: B rows and ranks read (ra <= R)
+  int32_t u_ld;                       // row stride of u in token order (the caller's u: ra)
 };
 
 template <typename E, int R>
@@ -95,7 +97,8 @@ __device__ __forceinline__ void load_u8(const ExpandParams &p, int R, int s, int
                                         int64_t t, int j, float v[8]) {
   const int64_t T = p.meta.T;
   const int64_t row = p.u_mode == 0 ? t : pos;
-  const float *src = p.u + ((int64_t)s * T + row) * R + j;
+  const int ld = p.u_mode == 0 ? p.u_ld : R;  // the caller's u is [n_slices][T][ra]
+  const float *src = p.u + ((int64_t)s * T + row) * ld + j;
   const int64_t plane = (int64_t)p.n_slices * T * R;
   const int kch = p.u_mode == 2 ? p.kch : 1;
   const f32x4 a = sum_partials4(src, plane, kch), b = sum_partials4(src + 4, plane, kch);
@@ -111,7 +114,7 @@ __device__ __forceinline__ void load_u8(const ExpandParams &p, int R, int s, int
 template <typename E, int R>
 __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E, R> &lds, int slot, int64_t pos0,
                              int rows, int s, int nt) {
-  const int rk = slot >= 0 ? slot_rank_of(p.slot_rank, slot, R) : 0;  // ranks past rk are not read
+  const int rk = slot >= 0 ? slot_rank_of(p.slot_rank, slot, p.ra) : 0;  // ranks past rk are not read
   const int tid = threadIdx.x;
   const int NC = p.vec_cols;           // columns of this tile (a multiple of 8)
   const int OCT = NC / 8;
@@ -362,10 +365,10 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     // idx / (W / 8), columns 8 (idx % (W / 8)) .. + 7 of the step
     // (idx = tid + 256 q).  Loads past the slot block (rows >= R), past the
     // slot's rank or past the chunk read zeros without touching memory.
-    const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
+    const int rk = slot_rank_of(p.slot_rank, slot, p.ra);  // ranks past rk are not read
     const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick<NS>(p.B, s, p.n_slices)) +
                                     (int64_t)slot * pick<NS>(p.b_stride, s, p.n_slices),
-                                (uint32_t)(R * w * 2));
+                                (uint32_t)(p.ra * w * 2));
     u32x4 bq[BQ];
     auto load_b = [&](int i) {
 #pragma unroll
@@ -410,7 +413,8 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     __syncthreads();  // the previous item's last step has read every buffer
     {
       constexpr int QR = RP / 4;
-      const float *ubase = p.u + (int64_t)s * T * R;
+      const int uld = p.u_mode == 0 ? p.u_ld : R;  // the caller's u is [n_slices][T][ra]
+      const float *ubase = p.u + (int64_t)s * T * uld;
       const int64_t plane = (int64_t)p.n_slices * T * R;
       for (int pi = tid; pi < rows * QR; pi += 2 * kXThreads) {
         f32x4 v[2];
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
           const int row = pe / QR, j = 4 * (pe % QR);
           const int64_t urow = p.u_mode == 0 ? (int64_t)lds.tok[row < kTileRows ? row : 0] : pos0 + row;
           v[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (pe < rows * QR && j < rk) v[e] = sum_partials4(ubase + urow * R + j, plane, p.kch);
+          if (pe < rows * QR && j < rk) v[e] = sum_partials4(ubase + urow * uld + j, plane, p.kch);
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -696,8 +700,8 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
           // the transposing read hands lane m the column 8 (m / 4) + m % 4
           // (+ 4), so a lane's 8 outputs of the pair are 8 consecutive
           // columns of one token.
-          const int rk = slot_rank_of(p.slot_rank, slot, R);
-          const rsrc_t br = make_rsrc(bslice + (int64_t)slot * bstride, (uint32_t)(R * w * 2));
+          const int rk = slot_rank_of(p.slot_rank, slot, p.ra);
+          const rsrc_t br = make_rsrc(bslice + (int64_t)slot * bstride, (uint32_t)(p.ra * w * 2));
           const int c8 = col0 + 8 * lane;
           const int l = lane % 16;
           // one 32-rank step at a time through a 32-row LDS buffer
@@ -815,8 +819,8 @@ static hipError_t launch_rows_ns(const ExpandParams &p, int64_t bound, hipStream
 // The long-segment expand serves this call?  Whole tiles are likely when the
 // batch has at least 64 tokens per possible segment.  LORA_EXPAND_ROWS=0 or 1
 // forces the choice (tuning).
-bool expand_rows_fits(int64_t T, int32_t S, bool bf16, int mode) {
-  if (!bf16 || mode == 1) return false;
+bool expand_rows_fits(int64_t T, int32_t S, bool bf16, int mode, int32_t R) {
+  if (!bf16 || mode == 1 || R > 64) return false;  // rank 128 would not keep its B chunk in registers
   const int v = expand_rows_knob();
   if (v >= 0) return v == 1;
   return T >= 64 * ((int64_t)S + 1);
@@ -839,7 +843,8 @@ bool expand_rows_addressable(int64_t T, int32_t n_slices, const int64_t *width, 
 
 hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, uint16_t *planes, int32_t n_slices,
                               const void *const *B, const int64_t *b_stride, const int64_t *width,
-                              const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y, int64_t ldy,
+                              const int64_t *offset, int32_t R, int32_t ra, const int32_t *slot_rank, void *y,
+                              int64_t ldy,
                               int add, hipStream_t stream) {
   const int64_t T = meta.T;
   if (T == 0) return hipSuccess;
@@ -855,6 +860,8 @@ hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, 
   p.meta = meta;
   p.n_slices = n_slices;
   p.uh = planes;
+  p.ra = ra;
+  p.u_ld = R;
   p.rows_nck_total = 0;
   for (int s = 0; s < n_slices; ++s) {
     p.B[s] = B[s];
@@ -890,7 +897,7 @@ bool expand_uses_mma(bool bf16, int mode) { return bf16 && mode != 1; }
 
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
-                         const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y,
+                         const int64_t *offset, int32_t R, int32_t ra, const int32_t *slot_rank, void *y,
                          int64_t ldy, bool bf16, int add, int mode, hipStream_t stream) {
   ExpandParams p{};
   p.meta = meta;
@@ -898,8 +905,10 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   p.u_mode = u_mode;
   p.kch = kch;
   p.n_slices = n_slices;
+  p.ra = ra;
+  p.u_ld = ra;
   const int64_t e = bf16 ? 2 : 4;
-  const bool mma = expand_uses_mma(bf16, mode);
+  const bool mma = expand_uses_mma(bf16, mode) && R <= 64;  // rank 128: the vector kernel
   const int64_t T = meta.T, S = meta.S;
   for (int s = 0; s < n_slices; ++s) {
     p.B[s] = B[s];
@@ -946,6 +955,7 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
     case 16: return bf16 ? launch_t<uint16_t, 16>(p, grid, stream) : launch_t<float, 16>(p, grid, stream);
     case 32: return bf16 ? launch_t<uint16_t, 32>(p, grid, stream) : launch_t<float, 32>(p, grid, stream);
     case 64: return bf16 ? launch_t<uint16_t, 64>(p, grid, stream) : launch_t<float, 64>(p, grid, stream);
+    case 128: return bf16 ? launch_t<uint16_t, 128>(p, grid, stream) : launch_t<float, 128>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }

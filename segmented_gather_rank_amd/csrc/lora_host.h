@@ -83,24 +83,38 @@ hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, con
                            int32_t *sorted, int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
                            int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream);
 
-// for_apply: u is written in sorted-position order, and with a split d_in the
+// R: the rank the kernels are built for (8, 16, 32, 64 or 128); ra: the
+// caller's r_max (a multiple of 8, at most R), the row stride of A and of the
+// caller's u.  for_apply: u is written in sorted-position order with row
+// stride R, and with a split d_in the
 // partial sums are left in ws for the expand to add (kch_out reports the
 // split); to_partials: the sums go to ws even without a split (kch = 1)
+// The rank the kernels are built for: the smallest of 8, 16, 32, 64, 128 that
+// holds r_max (0 when r_max is not a multiple of 8 in [8, 128]).
+inline int32_t tile_rank(int32_t r_max) {
+  if (r_max < 8 || r_max > 128 || r_max % 8) return 0;
+  int32_t R = 8;
+  while (R < r_max) R *= 2;
+  return R;
+}
+
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
-                         int32_t R, float scale, const float *slot_scale, const int32_t *slot_rank,
+                         int32_t R, int32_t ra, float scale, const float *slot_scale, const int32_t *slot_rank,
                          float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream,
                          bool to_partials = false);
-// u_mode 0: u [n_slices][T][R] in token order; 1: the same in sorted-position
-// order; 2: kch partial sums [kch][n_slices][T][R] in sorted-position order
+// R, ra: as for the shrink (B holds ra rank rows per slot).  u_mode 0: u
+// [n_slices][T][ra] in token order (the caller's); 1: [n_slices][T][R] in
+// sorted-position order; 2: kch partial sums [kch][n_slices][T][R] in
+// sorted-position order
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
-                         const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y,
+                         const int64_t *offset, int32_t R, int32_t ra, const int32_t *slot_rank, void *y,
                          int64_t ldy, bool bf16, int add, int mode, hipStream_t stream);
 
 // The long-segment expand (whole 64-token tiles, 512-column chunks) serves
 // this call?  Decided from host-known sizes only.
-bool expand_rows_fits(int64_t T, int32_t S, bool bf16, int mode);
+bool expand_rows_fits(int64_t T, int32_t S, bool bf16, int mode, int32_t R);
 bool expand_rows_addressable(int64_t T, int32_t n_slices, const int64_t *width, const int64_t *offset, int64_t ldy,
                              int32_t R);
 int expand_rows_knob();
@@ -108,8 +122,8 @@ int expand_rows_knob();
 // folded into one bf16 plane at `planes` (n_slices * T * R * 2 bytes).
 hipError_t launch_expand_rows(const MetaView &meta, const float *part, int kch, uint16_t *planes, int32_t n_slices,
                               const void *const *B, const int64_t *b_stride, const int64_t *width,
-                              const int64_t *offset, int32_t R, const int32_t *slot_rank, void *y, int64_t ldy,
-                              int add, hipStream_t stream);
+                              const int64_t *offset, int32_t R, int32_t ra, const int32_t *slot_rank, void *y,
+                              int64_t ldy, int add, hipStream_t stream);
 
 // The fused BGMV kernel (one workgroup per token) serves this call?  Decided
 // from host-known sizes only.

@@ -57,11 +57,13 @@ struct ShrinkParams {
   float *out;
   int32_t u_sorted;
   int32_t kc, kch;       // k-chunk length (a multiple of 128) and count
+  int32_t ra;            // the caller's r_max: A row stride, ranks read (ra <= R)
+  int32_t u_ld;          // row stride of u written in token order (the caller's u: ra)
 };
 
 struct ShrinkLds {
   float xs[kVecRows][kVecSub];
-  float red[4][kVecRows][64];
+  float red[4][kVecRows][128];
 };
 
 // Store one result: into u (token or sorted order) when d_in is not split,
@@ -70,8 +72,11 @@ __device__ __forceinline__ void put(const ShrinkParams &p, int R, int s, int64_t
                                    int kc, float v) {
   const int64_t T = p.meta.T;
   if (p.kch == 1) {
-    const int64_t row = p.u_sorted ? pos : (int64_t)p.meta.sorted[pos];
-    p.out[((int64_t)s * T + row) * R + j] = v;
+    if (p.u_sorted) {
+      p.out[((int64_t)s * T + pos) * R + j] = v;
+    } else if (j < p.ra) {  // the caller's u: [n_slices][T][ra]
+      p.out[((int64_t)s * T + p.meta.sorted[pos]) * p.u_ld + j] = v;
+    }
   } else {
     p.out[(((int64_t)kc * p.n_slices + s) * T + pos) * R + j] = v;
   }
@@ -83,8 +88,12 @@ __device__ __forceinline__ void put4(const ShrinkParams &p, int R, int s, int64_
   const int64_t T = p.meta.T;
   float *dst;
   if (p.kch == 1) {
-    const int64_t row = p.u_sorted ? pos : (int64_t)p.meta.sorted[pos];
-    dst = p.out + ((int64_t)s * T + row) * R + j;
+    if (p.u_sorted) {
+      dst = p.out + ((int64_t)s * T + pos) * R + j;
+    } else {
+      if (j >= p.ra) return;  // the caller's u: [n_slices][T][ra] (ra and j multiples of 4)
+      dst = p.out + ((int64_t)s * T + p.meta.sorted[pos]) * p.u_ld + j;
+    }
   } else {
     dst = p.out + (((int64_t)kc * p.n_slices + s) * T + pos) * R + j;
   }
@@ -116,13 +125,13 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
       const int slen = min(kVecSub, klen - sub);
       const int nel = slen * R;
       const E *Ab = reinterpret_cast<const E *>(pick(p.A, s)) + (int64_t)slot * pick(p.a_stride, s) +
-                    (k0 + sub) * R;
+                    (k0 + sub) * p.ra;
       // the first A batch goes out before the x rows are staged
       Raw8<E> a[VA];
 #pragma unroll
       for (int q = 0; q < VA; ++q) {
         const int e = 8 * (tid + kShrinkThreads * q);
-        if (e < nel && e % R < rk) a[q].load(Ab + e); else a[q].zero();
+        if (e < nel && e % R < rk) a[q].load(Ab + packed_to_factor<R>(e, p.ra)); else a[q].zero();
       }
       if (staged != sub) {
         __syncthreads();  // earlier readers of xs are done
@@ -143,7 +152,7 @@ __device__ __forceinline__ void vec_item(const ShrinkParams &p, ShrinkLds &lds, 
 #pragma unroll
           for (int q = 0; q < VA; ++q) {
             const int e = base + 8 * (tid + kShrinkThreads * q);
-            if (e < nel && e % R < rk) a[q].load(Ab + e); else a[q].zero();
+            if (e < nel && e % R < rk) a[q].load(Ab + packed_to_factor<R>(e, p.ra)); else a[q].zero();
           }
         }
 #pragma unroll
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
     const bool rv = tb < nb && r < rows;
     const int64_t trow = rv ? (int64_t)(wpt == 4 ? hd.tk4 : (wpt == 2 ? hd.tk2 : hd.tk1)) : (int64_t)hd.tfirst;
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
-    const int rk = slot_rank_of(p.slot_rank, slot, R);  // ranks past rk are not read
+    const int rk = slot_rank_of(p.slot_rank, slot, p.ra);  // ranks past rk are not read
     const uint16_t *xrow = x + x_row_of(p.meta, trow) * p.ldx;
 
     for (int s0 = 0; s0 < p.n_slices; s0 += SG) {
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
         const int sidx = s0 + (g < ns ? g : 0);
         ar[g] = make_rsrc(reinterpret_cast<const uint16_t *>(pick<NS>(p.A, sidx, p.n_slices)) +
                               (int64_t)slot * pick<NS>(p.a_stride, sidx, p.n_slices),
-                          (uint32_t)(p.d_in * R * 2));
+                          (uint32_t)(p.d_in * p.ra * 2));
       }
       // A octet q = t * CB + sl * QS + qq of this thread: tile t of the
       // batch, slice sl, flat element 8 (tid + 256 qq) of that slice's
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
               const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
               const int k = e / R, j0 = e % R;
               const bool ok = sl < ns && k0 + k < kend && j0 < rk;
-              aq[t * CB + q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * R + j0) * 2) : 0x7FFFFFF0u);
+              aq[t * CB + q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * p.ra + j0) * 2) : 0x7FFFFFF0u);
             }
           }
         }
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
     const int64_t pos0 = (int64_t)tb.start[seg] + (int64_t)chunk * kVecRows;
     vec_item<E, R>(p, lds, slot, pos0, min(kVecRows, count - chunk * kVecRows), kc, sc,
-                   slot_rank_of(p.slot_rank, slot, R));
+                   slot_rank_of(p.slot_rank, slot, p.ra));
   }
 }
 
@@ -420,10 +429,10 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 // for every sorted position of a token with an adapter.
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(MetaView meta, const float *partial,
                                                             float *u, int32_t n_slices, int32_t R,
-                                                            int32_t kch) {
+                                                            int32_t kch, int32_t ra) {
   const int64_t T = meta.T;
   const int64_t begin = meta.info[3];
-  const int64_t q_per_row = R / 4;
+  const int64_t q_per_row = ra / 4;  // the caller's u holds ranks < ra, row stride ra
   const int64_t total = (T - begin) * n_slices * q_per_row;
   const int64_t plane = (int64_t)n_slices * T * R;
   for (int64_t idx = blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(MetaView meta, const
     const float *src = partial + (s * T + pos) * R + 4 * q;
     const f32x4 v = sum_partials4(src, plane, kch);
     const int64_t t = meta.sorted[pos];
-    *reinterpret_cast<f32x4 *>(u + (s * T + t) * R + 4 * q) = v;
+    *reinterpret_cast<f32x4 *>(u + (s * T + t) * ra + 4 * q) = v;
   }
 }
 
@@ -505,7 +514,7 @@ static int mma_col_blocks(int32_t n_slices, int32_t R) {
 
 hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64_t d_in, bool bf16,
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
-                         int32_t R, float scale, const float *slot_scale, const int32_t *slot_rank,
+                         int32_t R, int32_t ra, float scale, const float *slot_scale, const int32_t *slot_rank,
                          float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream,
                          bool to_partials) {
   const ShrinkConfig c = plan_shrink(meta.T, meta.S, d_in, R, bf16, mode);
@@ -527,6 +536,8 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   p.u_sorted = for_apply ? 1 : 0;
   p.kc = c.kc;
   p.kch = c.kch;
+  p.ra = ra;
+  p.u_ld = ra;
   if (meta.T == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
   if (c.use_mma_mode) {
@@ -541,6 +552,7 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
       case 32 * 16 + 8: e = launch_mma_t<32, 8>(p, c.bound, stream); break;
       case 64 * 16 + 4: e = launch_mma_t<64, 4>(p, c.bound, stream); break;
       case 64 * 16 + 8: e = launch_mma_t<64, 8>(p, c.bound, stream); break;
+      case 128 * 16 + 8: e = launch_mma_t<128, 8>(p, c.bound, stream); break;
     }
   } else {
     switch (R) {
@@ -548,15 +560,16 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
       case 16: e = bf16 ? launch_t<uint16_t, 16>(p, c.grid, stream) : launch_t<float, 16>(p, c.grid, stream); break;
       case 32: e = bf16 ? launch_t<uint16_t, 32>(p, c.grid, stream) : launch_t<float, 32>(p, c.grid, stream); break;
       case 64: e = bf16 ? launch_t<uint16_t, 64>(p, c.grid, stream) : launch_t<float, 64>(p, c.grid, stream); break;
+      case 128: e = bf16 ? launch_t<uint16_t, 128>(p, c.grid, stream) : launch_t<float, 128>(p, c.grid, stream); break;
     }
   }
   // lora_apply's expand reads the partial sums itself; lora_shrink must hand
   // back a finished u
   if (e != hipSuccess || c.kch == 1 || for_apply) return e;
-  const int64_t work = meta.T * n_slices * (R / 4);
+  const int64_t work = meta.T * n_slices * (ra / 4);
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, 1024));
   hipLaunchKernelGGL(shrink_reduce_kernel, dim3(grid), dim3(256), 0, stream, meta,
-                     reinterpret_cast<const float *>(ws), u, n_slices, R, c.kch);
+                     reinterpret_cast<const float *>(ws), u, n_slices, R, c.kch, ra);
   return hipGetLastError();
 }
 

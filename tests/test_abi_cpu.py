@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 7
+    assert L.lora_abi_version() == 8
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -44,6 +44,25 @@ def test_workspace_sizes():
     assert L.lora_apply_workspace_bytes(1, 1, 8, 1, 8, torch.float32) >= L.APPLY_SYNC_BYTES
     b2 = L.lora_shrink_workspace_bytes(256, 32, 4096, 1, 16, torch.bfloat16)
     assert b2 > 0 and b2 % 256 == 0
+
+
+def test_workspace_sizes_follow_the_tile_rank():
+    """r_max that is not a power of two runs at the next of 8, 16, 32, 64, 128:
+    the shrink's partial sums and lora_apply's rank buffer are sized at that
+    rank, so r_max = 24 needs the shrink workspace of r_max = 32 and 48 that of
+    64.  lora_apply's may be smaller than at the power of two (the fused decode
+    kernels, which take only 8, 16, 32 and 64, add their partials there)."""
+    import torch
+    for T, S, d_in, n in ((4096, 32, 4096, 1), (17705, 4, 4096, 2), (64, 64, 14336, 3)):
+        for dt in (torch.bfloat16, torch.float32):
+            for lo, hi in ((24, 32), (40, 64), (48, 64), (72, 128), (120, 128)):
+                assert L.lora_shrink_workspace_bytes(T, S, d_in, n, lo, dt) == \
+                    L.lora_shrink_workspace_bytes(T, S, d_in, n, hi, dt), (T, lo, dt)
+                a = L.lora_apply_workspace_bytes(T, S, d_in, n, lo, dt)
+                assert L.APPLY_SYNC_BYTES + 4 * n * T * hi <= a <= \
+                    L.lora_apply_workspace_bytes(T, S, d_in, n, hi, dt), (T, lo, dt)
+    assert L.lora_apply_workspace_bytes(4096, 32, 4096, 1, 128, torch.bfloat16) >= \
+        L.APPLY_SYNC_BYTES + 4 * 4096 * 128
 
 
 def test_header_constants_match_binding():
@@ -110,8 +129,10 @@ def _shrink(meta=None, ldx=64, d_in=64, dtype=1, n=1, A=None, r=16, ss=None, u=N
 
 
 def test_shrink_rejections():
-    assert _shrink(r=12) == L.LORA_ERR_UNSUPPORTED
-    assert _shrink(r=128) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(r=12) == L.LORA_ERR_UNSUPPORTED      # not a multiple of 8
+    assert _shrink(r=136) == L.LORA_ERR_UNSUPPORTED     # past 128
+    assert _shrink(r=0) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(r=24, A=_w(1, 64 * 24 - 8)) == L.LORA_ERR_INVALID_ARG   # A slots sized for r_max = 24
     assert _shrink(n=0, A=_w(1, 64 * 16)) == L.LORA_ERR_UNSUPPORTED
     assert _shrink(n=9, A=_w(9, 64 * 16)) == L.LORA_ERR_UNSUPPORTED
     assert _shrink(dtype=7) == L.LORA_ERR_UNSUPPORTED
@@ -148,7 +169,8 @@ def test_expand_rejections():
     assert _expand(ldy=88) == L.LORA_ERR_INVALID_ARG                 # window past ldy
     assert _expand(widths=(64, 30)) == L.LORA_ERR_INVALID_ARG        # width not a multiple of 8
     assert _expand(offsets=(0, 68)) == L.LORA_ERR_INVALID_ARG        # offset not a multiple of 8
-    assert _expand(r=24) == L.LORA_ERR_UNSUPPORTED
+    assert _expand(r=20) == L.LORA_ERR_UNSUPPORTED
+    assert _expand(r=256) == L.LORA_ERR_UNSUPPORTED
     assert _expand(y=_ptr(2)) == L.LORA_ERR_INVALID_ARG
     thin = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64), L.lora_weight(_base, 16 * 32 - 8))
     assert _expand(B=thin) == L.LORA_ERR_INVALID_ARG

@@ -121,3 +121,63 @@ def test_ranked_integer_bit_exact(L, mode):
     d = RankedDev(c)
     y, _ = d.apply_ranked(L, mode=mode)
     assert np.array_equal(as_f64(from_dev(y)), ref)
+
+
+# r_max that is not a power of two, and 128: A is [d_in][r_max] and B
+# [r_max][width] per slot, packed at that rank; the kernels run at the next of
+# 8, 16, 32, 64, 128 and must neither read past r_max into the next row nor
+# let ranks past it add anything.
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("r", [24, 48, 128])
+@pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
+def test_apply_any_r_max(L, dtype, r, mode):
+    c = small_case(700 + r, dtype, r)
+    print(f"[r_max] {c.name} ranks={sorted(set(c.ranks.tolist()))} mode={mode}", flush=True)
+    d = RankedDev(c)
+    for add in (True, False):
+        y, _ = d.apply_ranked(L, mode=mode, add=add)
+        check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} ranked add={add}")
+    plain = DevCase(c)                  # no d_slot_rank: every slot read at r_max
+    y, _ = plain.apply(L, mode=mode, add=True)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), f"{c.name} r_max")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("r", [24, 40, 120])
+def test_shrink_and_expand_alone_any_r_max(L, dtype, r):
+    """lora_shrink writes the caller's u as [n_slices][T][r_max] and
+    lora_expand reads it so, at a rank between the kernels' tile ranks."""
+    c = small_case(800 + r, dtype, r)
+    d = DevCase(c)
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    u = torch.full((c.n_slices, c.T, c.r_max), float("nan"), dtype=torch.float32, device="cuda")
+    L.lora_shrink(meta, d.x, d.A, u, scale=c.scale, slot_scale=d.slot_scale, mode="auto")
+    torch.cuda.synchronize()
+    _, uref = oracle_rows(c, np.arange(c.T), return_u=True)
+    got = u.cpu().numpy()
+    has = c.token_slot >= 0
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for s in range(c.n_slices):
+        g, ref = got[s][has].astype(np.float64), uref[has, s, :]
+        assert np.all(np.abs(g - ref) <= tol * (1 + np.abs(ref))), s
+    y = d.y0.clone()
+    uu = torch.from_numpy(np.ascontiguousarray(np.transpose(uref, (1, 0, 2))).astype(np.float32)).cuda()
+    uu[:, ~torch.from_numpy(has).cuda(), :] = 0
+    L.lora_expand(meta, uu, d.B, c.offsets, y, add=True, mode="auto")
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), f"{c.name} expand alone")
+
+
+@pytest.mark.parametrize("r", [24, 48, 128])
+@pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
+def test_any_r_max_integer_bit_exact(L, r, mode):
+    """Integer inputs at r_max 24, 48 and 128 over long segments (the shrink's
+    split of d_in and the long-segment expand) and one-token requests: every
+    element bit-identical to the oracle."""
+    c = integer_case(30 + r, [1] * 96 + [700, 300, 129, 64], 6, 2048, [1024, 512], r, 2.0)
+    ref = oracle_rows(c, np.arange(c.T))
+    assert np.all(ref == np.round(ref)) and np.max(np.abs(ref)) <= 256
+    print(f"[r_max] integer r={r} T={c.T} mode={mode}", flush=True)
+    d = DevCase(c)
+    y, _ = d.apply(L, mode=mode, add=True)
+    assert np.array_equal(as_f64(from_dev(y)), ref)
