@@ -50,15 +50,30 @@ typedef enum lora_status {
     LORA_ERR_INVALID_ARG = 1,       /* null pointer, bad size, misalignment, overlap */
     LORA_ERR_UNSUPPORTED = 2,       /* dtype, r_max, slot count or slice count not built */
     LORA_ERR_WORKSPACE = 3,         /* workspace smaller than the *_workspace_bytes value */
-    LORA_ERR_HIP = 4                /* a HIP launch failed (hipGetLastError) */
+    LORA_ERR_HIP = 4,               /* a HIP launch failed (hipGetLastError) */
+    /* Range markers, not statuses: with them every int is a value of the type,
+     * so a C caller may pass any int and a C++ definition may read it. */
+    LORA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    LORA_STATUS_RANGE_MAX_ = 2147483647
 } lora_status;
 
-typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+typedef enum lora_dtype {
+    LORA_F32 = 0,
+    LORA_BF16 = 1,
+    LORA_DTYPE_RANGE_MIN_ = -2147483647 - 1,  /* range markers, as above */
+    LORA_DTYPE_RANGE_MAX_ = 2147483647
+} lora_dtype;
 
 /* How segments are computed.  BGMV: every segment on the vector (matrix-vector)
  * path; SGMV: every segment on the matrix-core tile path (bf16 only; fp32 falls
  * back to the vector path); AUTO: per segment, by its token count. */
-typedef enum lora_mode { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode;
+typedef enum lora_mode {
+    LORA_MODE_AUTO = 0,
+    LORA_MODE_BGMV = 1,
+    LORA_MODE_SGMV = 2,
+    LORA_MODE_RANGE_MIN_ = -2147483647 - 1,  /* range markers, as above */
+    LORA_MODE_RANGE_MAX_ = 2147483647
+} lora_mode;
 
 /* One packed slice of a stacked factor: slot a's matrix starts at
  * ptr + a * slot_stride elements.  A_s matrices are [d_in][r_max] (row-major,

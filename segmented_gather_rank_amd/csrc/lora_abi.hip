@@ -300,6 +300,7 @@ const char *lora_status_string(lora_status s) {
     case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED";
     case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE";
     case LORA_ERR_HIP: return "LORA_ERR_HIP";
+    default: break;
   }
   return "LORA_ERR_UNKNOWN";
 }
