@@ -70,6 +70,10 @@ def parse():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="turn a rocprofv3 --kernel-trace --stats run of this bench (and its JSON line) into "
                          "the trace summary under profiles/")
+    ap.add_argument("--phase-budget", metavar="OUT_MD",
+                    help="build the library with the split kernel's phase clock (-DLORA_PHASE_CLOCK) into a "
+                         "temporary directory, run --steps cold steps of the workload on it and write the "
+                         "per-phase latency budget of the one-slice split kernel to OUT_MD")
     return ap.parse_args()
 
 
@@ -641,6 +645,15 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     e1.record()
     torch.cuda.synchronize()
     eager_ms_per_step = e0.elapsed_time(e1) / K
+    # the split decode kernel's rendezvous counters, summed over the sets'
+    # workspaces: waits that gave up, and flags met from another XCD (both
+    # mean a member computed a peer's partials itself)
+    n_apply = max(warmup, nrot) + 2 + 4 * K + K
+    rdv = {"apply_calls": n_apply, "waits_gave_up": 0, "flags_from_other_xcd": 0}
+    for s in sets:
+        cnt = L.apply_workspace_counters(s["aws"])
+        rdv["waits_gave_up"] += cnt["gave_up"]
+        rdv["flags_from_other_xcd"] += cnt["other_xcd"]
     del sets, metas
     torch.cuda.empty_cache()
 
@@ -684,7 +697,106 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
                  "mfma_bf16_frac": round(d_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
                  "timed_as": "one HIP graph of the K steps, replayed once after a flushing copy",
                  "host_wall_s": round(t_host, 4), "eager_ms_per_step": round(eager_ms_per_step, 5)},
+        **({"split_rendezvous": rdv} if key.startswith("bgmv_split") else {}),
     }
+
+
+PHASES = ["launch spread (start - first start)", "tile header (1 - 0)", "A chunk in LDS (2 - 1)",
+          "rest of batch, shrink, partials acknowledged (3 - 2)", "rendezvous (4 - 3)",
+          "gather of the first block's u (5 - 4)", "expand, y stores acknowledged (6 - 5)",
+          "workgroup total (6 - 0)", "end (6 - first start)"]
+
+
+def phase_budget(c, args, out_md):
+    """Per-phase latency of the one-slice split kernel, from its own clock.
+
+    The measurement build records, per workgroup, the 100 MHz real-time counter
+    at the kernel's phase boundaries (csrc/lora_bgmv_split.hip, LORA_PHASE_CLOCK).
+    Each of --steps steps is one flushing copy, the metadata and lora_apply,
+    as in the timed graph; the records of the workgroups that had work are
+    read back after each step."""
+    import importlib.util
+    import tempfile
+
+    import numpy as np
+
+    spec = importlib.util.spec_from_file_location(
+        "_lora_hip_build", os.path.join(ROOT, "segmented_gather_rank_amd", "build.py"))
+    hb = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(hb)
+    tmp = tempfile.mkdtemp(prefix="lora_phase_")
+    lib = hb.build(out=os.path.join(tmp, "liblora_mi355x_phase.so"), extra=["-DLORA_PHASE_CLOCK"])
+    os.environ["LORA_MI355X_LIB"] = lib
+    import ctypes
+
+    import torch
+
+    import segmented_gather_rank_amd as L
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    words = 10
+    clk = torch.zeros(words * 8192, dtype=torch.int64, device=dev)
+    L._cdll.lora_debug_phase_clock.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L._cdll.lora_debug_phase_clock(ctypes.c_void_p(clk.data_ptr()), clk.numel())
+    ts, x, y = torch.from_numpy(c.token_slot).to(dev), to_dev(c.x), to_dev(c.y0)
+    A, B = [to_dev(a) for a in c.A], [to_dev(b) for b in c.B]
+    ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, c.r_max,
+                                                        x.dtype, args.mode), dev)
+    mws = torch.empty(L.lora_meta_workspace_bytes(c.T, c.num_slots), dtype=torch.uint8, device=dev)
+    flush = Flush(torch, dev, args.flush_mb)
+    rows, spans_ev = [], []
+    for it in range(args.warmup + args.steps):
+        flush()
+        clk.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m = L.lora_prepare_meta(ts, c.num_slots, workspace=mws)
+        e0.record()
+        L.lora_apply(m, x, A, B, c.offsets, y, scale=c.scale, add=True, mode=args.mode, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if it < args.warmup:
+            continue
+        r = clk.cpu().numpy().reshape(-1, words)
+        r = r[r[:, 0] != 0]
+        if r.shape[0] == 0:
+            raise SystemExit("the split kernel did not run (no phase records): not a split-kernel workload")
+        t = r[:, :7].astype(np.float64) * 10.0 / 1000.0   # 100 MHz ticks -> us
+        first = t[:, 0].min()
+        rows.append(np.stack([t[:, 0] - first, t[:, 1] - t[:, 0], t[:, 2] - t[:, 1], t[:, 3] - t[:, 2],
+                              t[:, 4] - t[:, 3], t[:, 5] - t[:, 4], t[:, 6] - t[:, 5], t[:, 6] - t[:, 0],
+                              t[:, 6] - first], axis=1))
+        spans_ev.append(e0.elapsed_time(e1) * 1e3)
+    allr = np.concatenate(rows)
+    ends = np.array([rr[:, 8].max() for rr in rows])
+    crit = np.stack([rr[int(np.argmax(rr[:, 8]))] for rr in rows])   # the last workgroup of each step
+    lines = [f"# Phase budget of the one-slice split kernel: {c.name}", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
+             f"--phase-budget {out_md}", "```", "",
+             "The library is rebuilt with `-DLORA_PHASE_CLOCK`: each workgroup of the kernel writes the 100 MHz "
+             "real-time counter at its phase boundaries (10 ns resolution). Each step is a 1 GiB flushing copy, "
+             "`lora_prepare_meta`, then `lora_apply`, as in the timed graph. "
+             f"{args.steps} steps, {allr.shape[0] // len(rows)} workgroups with work per step.", "",
+             "| Phase (us) | median | p90 | max | last workgroup (median) |", "|---|---|---|---|---|"]
+    for i, name in enumerate(PHASES):
+        col = allr[:, i]
+        lines.append(f"| {name} | {np.median(col):.2f} | {np.percentile(col, 90):.2f} | {col.max():.2f} | "
+                     f"{np.median(crit[:, i]):.2f} |")
+    lines += ["", f"First start to last end, median over steps: {np.median(ends):.2f} us "
+              f"(p90 {np.percentile(ends, 90):.2f}). HIP events around the lora_apply launch of the same steps: "
+              f"median {np.median(spans_ev):.2f} us (these add the launch and the gap before the first "
+              f"workgroup starts)."]
+    os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
 
 
 def main():
@@ -703,6 +815,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(c, args.config, *args.summarize_trace, dominant_kernel(c, args.mode))
+        return
+    if args.phase_budget:
+        phase_budget(c, args, args.phase_budget)
         return
 
     import torch
@@ -761,7 +876,8 @@ def main():
         ck, mk = load_case(k)
         print(f"bench: extra workload {ck.name}", file=sys.stderr, flush=True)
         e = measure(ck, mk, args, L, torch, dev, flush, K, args.warmup)
-        extra[ck.name] = {kk: e[kk] for kk in ("value", "ms_per_step", "roofline", "calls_us")}
+        extra[ck.name] = {kk: e[kk] for kk in ("value", "ms_per_step", "roofline", "calls_us", "split_rendezvous")
+                          if kk in e}
         extra[ck.name]["unit"] = "tokens/s"
         del ck, mk
     del flush
@@ -773,6 +889,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
         "config": head["config"], "roofline": head["roofline"], "calls_us": head["calls_us"], "step": head["step"],
+        **({"split_rendezvous": head["split_rendezvous"]} if "split_rendezvous" in head else {}),
         "hbm_copy_gbs": {"measured": round(copy_gbs, 1), "peak": HBM_PEAK_GBS,
                          "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "how": "torch copy_ of 1 GiB (2 GiB moved), best of 6, HIP events"},

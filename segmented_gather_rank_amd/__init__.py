@@ -18,7 +18,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
+# LORA_MI355X_LIB names another build of the same library (a measurement
+# build, say); by default the in-tree one is loaded
+LIB_PATH = os.environ.get("LORA_MI355X_LIB") or os.path.join(_HERE, "liblora_mi355x.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

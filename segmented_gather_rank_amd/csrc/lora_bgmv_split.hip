@@ -528,7 +528,31 @@ struct Split1Params {
   int32_t ldx, d_in, x_row_div, ldy;
   int32_t gsh, ksh, ldb, bs_off, max_tiles, n_frag, spin_limit, add, x_full;
   float scale;
+#ifdef LORA_PHASE_CLOCK
+  unsigned long long *clk;  // kPhaseWords per workgroup (a measurement build only)
+#endif
 };
+
+#ifdef LORA_PHASE_CLOCK
+// A measurement build: each workgroup of the one-slice kernel records the
+// 100 MHz real-time counter when it starts (0), has its tile header (1), its
+// A chunk in LDS (2), every load of the batch landed and its partial rows
+// acknowledged (3), the rendezvous done (4), the first token block's u
+// gathered (5) and its y stores acknowledged (6); then (7) ti | g << 16 |
+// slice << 24, (8) the HW_ID register, (9) XCC_ID.  Workgroups that leave
+// early record nothing.
+constexpr int kPhaseWords = 10;
+static unsigned long long *g_phase_clock = nullptr;
+static size_t g_phase_words = 0;
+#define LORA_PHASE(i)                                                                      \
+  do {                                                                                     \
+    if (threadIdx.x == 0) clk_rec[i] = (unsigned long long)__builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define LORA_PHASE(i) \
+  do {                \
+  } while (0)
+#endif
 
 // The slices' own values, a kernel argument of their own: it is indexed by
 // the slice at run time, which would otherwise make the compiler load every
@@ -581,6 +605,10 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   uint16_t *const As = reinterpret_cast<uint16_t *>(split_lds);
   uint16_t *const Bs = reinterpret_cast<uint16_t *>(split_lds + p.bs_off);
 
+#ifdef LORA_PHASE_CLOCK
+  const unsigned long long t_start = (unsigned long long)__builtin_amdgcn_s_memrealtime();
+  unsigned long long *const clk_rec = p.clk + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kPhaseWords;
+#endif
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l16 = lane % 16, kg = lane / 16;
   const int G = 1 << p.gsh;
@@ -615,6 +643,15 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     if (!p.add) split1_zero(p, tl, rows, gb0, nbm, offset, width);
     return;
   }
+#ifdef LORA_PHASE_CLOCK
+  if (tid == 0) {
+    clk_rec[0] = t_start;
+    clk_rec[7] = (unsigned long long)(ti | g << 16 | sl << 24);
+    clk_rec[8] = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));
+    clk_rec[9] = xcc_id();
+  }
+#endif
+  LORA_PHASE(1);
 
   // ---- second round trip: every load is issued, none behind a branch;
   // pieces that are not needed take an offset past their resource
@@ -706,6 +743,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   };
   stage_a();
   __syncthreads();
+  LORA_PHASE(2);
 
   // ---- shrink (D' = A^T x^T, so that lane (token l16, kg) ends with ranks
   // 4 kg .. + 3 of its token)
@@ -776,6 +814,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  LORA_PHASE(3);
   if constexpr (!kYEarly) load_y0();
   if (G > 1) {
     __shared__ uint32_t missing;
@@ -802,6 +841,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       __syncthreads();
     }
   }
+  LORA_PHASE(4);
 
   // ---- expand, token block by token block: u = scale * (members' partials
   // in the gather's fixed order) as bf16 hi + lo operands; every column block
@@ -834,6 +874,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
         ul[c] = __builtin_bit_cast(s16x4, u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)});
       }
     }
+    if (t == 0) LORA_PHASE(5);
     const bool rok = 16 * t + l16 < rows;
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
@@ -860,6 +901,11 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       __syncthreads();  // every wave has read the gather's LDS
     }
   }
+#ifdef LORA_PHASE_CLOCK
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  LORA_PHASE(6);
+#endif
 }
 
 // ------------------------------------------------------------------ host side
@@ -1058,6 +1104,11 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
   p.add = sp.add;
   p.x_full = ((int64_t)pl.G << pl.ksh) == sp.d_in ? 1 : 0;
   p.scale = sp.scale;
+#ifdef LORA_PHASE_CLOCK
+  p.clk = g_phase_clock;
+  // lora_debug_phase_clock not called, or its buffer too small for the grid
+  if (!p.clk || (size_t)pl.grid * kPhaseWords > g_phase_words) return hipErrorInvalidValue;
+#endif
   hipLaunchKernelGGL((bgmv_split1_kernel<R, KS>), dim3(pl.grid / sp.n_slices, sp.n_slices), dim3(kSThreads), pl.lds,
                      stream, meta.info, meta.tiles, sp.sync, p, q);
   return hipGetLastError();
@@ -1177,3 +1228,13 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
 }
 
 }  // namespace lora
+
+#ifdef LORA_PHASE_CLOCK
+// The buffer the one-slice split kernel writes its phase timestamps to
+// (kPhaseWords 64-bit words per workgroup of its grid), a measurement build
+// only.
+extern "C" void lora_debug_phase_clock(void *d_buf, size_t words) {
+  lora::g_phase_clock = static_cast<unsigned long long *>(d_buf);
+  lora::g_phase_words = words;
+}
+#endif
