@@ -23,38 +23,38 @@
 // The members exchange the partial rank rows through the L2 of their XCD.
 // Workgroups go to the XCDs in turn (blockIdx mod 8 names the XCD) and a
 // tile's members share that residue.  Each member stores its fragments with
-// plain 16-byte stores (the write-through L1 passes them to L2), waits until
-// L2 has acknowledged them, and raises its own flag word of the tile the same
-// way; the others read both with agent-coherent loads, which skip L1.
-// (Agent-coherent stores also go on to memory: twice the acknowledgement time,
-// and a flag took about 0.9 us instead of 0.2 us to reach a peer.)  Once every
-// member's flag is up, the G partial fragments are added in one fixed order
-// (each wave a quarter of the members, then the four sums in wave order
-// through LDS), so every member gets the same u, bit for bit.
+// plain 16-byte stores (the write-through L1 passes them to L2), every fp32
+// value beside a tag word that names the call, in one 8-byte word with it;
+// the others poll the fragments themselves with agent-coherent loads, which
+// skip L1, until every tag they read names this call.  A value read beside
+// this call's tag is the value stored with that tag (one store wrote both,
+// one load read both), so no flag has to order anything and no member waits
+// for its own stores to be acknowledged: the exchange costs the polls alone.
+// The G partial fragments are then added in one fixed order (each wave a
+// quarter of the members, then the four sums in wave order through LDS), so
+// every member gets the same u, bit for bit.
 //
-// The flag words live at the start of the caller's apply workspace, so calls
-// with workspaces of their own share nothing.  A word counts the calls that
-// raised it and names the XCD (hardware register XCC_ID) of the member that
-// raised it last.  Each call raises each of a tile's 16 words exactly once
-// (member 0 also raises the words of members >= G), so the words of a range
-// stay equal between calls, and a member waits for "my count + 1".  A member
-// trusts a peer's word only when it names its own XCD: plain stores stay in
-// the L2 of the XCD that made them until that L2 writes them back, in any
-// order, so a flag seen from another XCD (evicted early, say) does not prove
-// that the fragments it guards are visible here.  The B chunk is loaded with
-// the A chunk and x, and so is the y of the first 16 rows except with the
-// longest chunks, so that none of them is outstanding at the acknowledgement
-// wait or the polls (loads complete in order).  The wait is bounded.  A
-// member computes itself, with the same code (so the same bits), the partials
-// of every peer it does not trust: still low at the spin limit, or raised from
-// another XCD.  It stores them into those peers' slots, where the peer writes
-// equal values, and reads them back through its own L2.  The result therefore
-// depends neither on the members being resident together nor on their sharing
-// an XCD: a member placed elsewhere costs the spin limit and is counted (a
-// status word beside the flags), never a wrong value.  Workgroups are
-// dispatched in order on each XCD and a tile's members are neighbours there,
-// so the tiles within the resident part of a larger grid finish and make room
-// for the rest.
+// The tag is the call count of the tile in bits 31:4 and the XCD (hardware
+// register XCC_ID) of the storing member in bits 3:0.  The counts live in
+// count words at the start of the caller's apply workspace, so calls with
+// workspaces of their own share nothing: a member reads its word at the start
+// and tags with "count + 1", and raises the word to that tag for the next
+// call (member 0 also raises the words of members >= G), so the words of a
+// tile stay equal between calls.  The B chunk is loaded with the A chunk and
+// x, and so is the y of the first 16 rows except with the longest chunks, so
+// that none of them is outstanding at the polls (loads complete in order).
+// The polls are bounded: a member computes itself, with the same code (so the
+// same bits), the partials of every peer whose tags have not all arrived at
+// the spin limit, stores them into those peers' slots (where the peer writes
+// equal values) and reads them back through its own L2.  A member on another
+// XCD is no hazard either: whatever its tagged words are seen to hold, a word
+// with this call's tag carries its value.  The result therefore depends
+// neither on the members being resident together nor on their sharing an
+// XCD: a late member costs the spin limit and is counted (a status word
+// beside the count words), never a wrong value.  Workgroups are dispatched in
+// order on each XCD and a tile's members are neighbours there, so the tiles
+// within the resident part of a larger grid finish and make room for the
+// rest.
 //
 // Only bf16.
 #include "lora_host.h"
@@ -116,95 +116,139 @@ __device__ __forceinline__ void split_zero(const SplitParams &p, const int32_t *
 // XCD this workgroup runs on (hardware register XCC_ID, bits 3:0).
 __device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15u; }
 
-// Raise this member's flag word of the tile (member 0 also those of members
-// >= G) to the next call count, tagged with this workgroup's XCD, then wait
-// until the G members' words carry that count: one wave, at most spin_limit
-// polls.  A peer's word is trusted only when its tag names this XCD: flags and
-// the partial fragments they guard are stored with plain stores, which stay in
-// the L2 of the XCD that made them until that L2 writes them back, so only a
-// peer on this XCD is known to have its fragments where this workgroup reads
-// them.  Returns the members (bit g') whose partials this workgroup computes
-// itself: those still low when it gave up, and those raised from another XCD.
-// status[0] counts waits that gave up, status[1] waits that met a word raised
-// on another XCD.
-__device__ __forceinline__ uint32_t split_wait(uint32_t *fl, uint32_t f, int g, int G, int spin_limit,
-                                               uint32_t xcc, uint32_t *status) {
+// Raise this member's count word of the tile (member 0 also those of members
+// >= G) to this call's tag: the next call's members read their count there.
+// No peer waits for these words; a plain store that reaches L2 whenever it does.
+__device__ __forceinline__ void raise_count(uint32_t *fl, int g, int G, uint32_t tag) {
   const int lane = threadIdx.x % kWave;
-  const uint32_t want = (f & ~15u) + 16u;  // this call's count, in bits 31:4
   if (lane < kSplitMembers && (lane == g || (g == 0 && lane >= G)))
-    __builtin_amdgcn_raw_buffer_store_b32(want | xcc, make_rsrc(fl, kSplitMembers * 4), lane * 4, 0, 0);
-  for (int polls = 0;; ++polls) {
-    const uint32_t v =
-        lane < G ? __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : (want | xcc);
-    const bool up = (int32_t)((v & ~15u) - want) >= 0;
-    const uint64_t low = __ballot(!up);
-    if (low == 0 || polls >= spin_limit) {
-      const uint64_t foreign = __ballot(up && (v & 15u) != xcc);
-      if (lane == 0) {
-        if (low) atomicAdd(status, 1u);
-        if (foreign) atomicAdd(status + 1, 1u);
-      }
-      return (uint32_t)(low | foreign);
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
+    __builtin_amdgcn_raw_buffer_store_b32(tag, make_rsrc(fl, kSplitMembers * 4), lane * 4, 0, 0);
 }
 
-// The NF fragments u[i] = sum over the G members gm of the partial fragment
-// at off[i] + gm * plane, shared by the 4 waves: wave w loads members
-// w MG .. w MG + MG - 1 (agent-coherent loads, all issued before the first is
-// used; members past G read as zeros), adds them in member order and leaves
-// its sums in LDS; then every wave adds the 4 waves' sums in wave order.  The
-// additions run in one fixed order for every member of a tile, so all of them
-// get the same bits, and each fragment crosses from L2 once per workgroup, not
-// once per wave.  Only the first nf fragments are gathered (the others come
-// out as zeros).  At most 16 loads a lane are in flight (64 registers): more
-// fragments go in chunks.  stage: nf * 4 * 64 f32x4 of LDS that no wave uses
-// on entry; it is read until every wave has its u, so the caller passes a
-// barrier before writing it again.
+// A lane's four fp32 partials of a fragment, each beside the call's tag:
+// (v0, tag, v1, tag) at off and (v2, tag, v3, tag) at off + 1024, so that a
+// fragment of 64 lanes takes 2048 bytes.  A value and its tag share one
+// naturally aligned 8-byte word, written by one store and read by one load:
+// a reader that finds this call's tag has the value stored with it, whichever
+// XCD stored it and however the line travelled.
+// The bits of a value as another type of the same size.  The value comes in
+// by value: applied to an element of a vector directly (v[1]), the bit cast
+// has been seen to read the vector's first element instead.
+template <typename T, typename S>
+__device__ __forceinline__ T bits_as(S s) {
+  return __builtin_bit_cast(T, s);
+}
+
+__device__ __forceinline__ void store_tagged(rsrc_t pr, uint32_t off, f32x4 v, uint32_t tag) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{bits_as<uint32_t>(v[0]), tag, bits_as<uint32_t>(v[1]), tag}, pr, off,
+                                         0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{bits_as<uint32_t>(v[2]), tag, bits_as<uint32_t>(v[3]), tag}, pr,
+                                         off + 1024, 0, 0);
+}
+
+// Wave w's part of gathering the nf fragments (of NF) at off[f] + gm plane
+// over the G members gm: it polls members w MG .. w MG + MG - 1 (those below
+// G) with agent-coherent loads, every load of a look issued before the first
+// is used, until each tag of a member carries this call's count `want`, at
+// most spin_limit + 1 looks.  Then it adds each fragment's values in member
+// order into stage[f][wave] (fragments past nf: nothing), so that the caller
+// adds the four waves' sums in wave order after a barrier, and every member
+// of a tile gets the same bits.  Returns the members (bit gm) whose tags were
+// still not all there at the last look, and with `guard` also those whose
+// tags name another XCD (*foreign gets those): their values in the sums are
+// not used, the caller computes their partials itself and gathers again.
+// At most 16 loads a lane are in flight: more fragments go in chunks.
 template <int MG, int NF>
-__device__ __forceinline__ void gather_waves(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int G, int nf,
-                                             f32x4 *stage, f32x4 (&u)[NF]) {
-  constexpr int FC = 16 / MG < NF ? 16 / MG : NF;  // fragments per chunk
+__device__ __forceinline__ uint32_t poll_wave(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int G, int nf,
+                                              uint32_t want, uint32_t xcc, int spin_limit, bool guard, f32x4 *stage,
+                                              uint32_t *foreign) {
+  constexpr int FC = 8 / MG < NF ? 8 / MG : NF;  // fragments per chunk
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t missing = 0, other = 0;
 #pragma unroll
   for (int f0 = 0; f0 < NF; f0 += FC) {
-    f32x4 v[FC][MG];
+    u32x4 lo[FC][MG], hi[FC][MG];
+    uint32_t late = 0;  // bit i: member w MG + i
+    for (int polls = 0;; ++polls) {
+#pragma unroll
+      for (int i = 0; i < MG; ++i) {
+        const int gm = wave * MG + i;
+#pragma unroll
+        for (int f = 0; f < FC; ++f) {
+          const uint32_t o = f0 + f < nf && gm < G ? off[f0 + f] + gm * plane : 0x7FFFFFF0u;
+          lo[f][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 16));
+          hi[f][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o + 1024, 0, 16));
+        }
+      }
+      late = 0;
+#pragma unroll
+      for (int i = 0; i < MG; ++i) {
+        bool ok = true;
+#pragma unroll
+        for (int f = 0; f < FC; ++f) {
+          if (f0 + f < nf) {
+            const uint32_t t0 = lo[f][i][1], t1 = lo[f][i][3], t2 = hi[f][i][1], t3 = hi[f][i][3];
+            ok = ok && (t0 & ~15u) == want && (t1 & ~15u) == want && (t2 & ~15u) == want && (t3 & ~15u) == want;
+          }
+        }
+        if (wave * MG + i < G && __ballot(!ok) != 0) late |= 1u << i;
+      }
+      if (late == 0 || polls >= spin_limit) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
 #pragma unroll
     for (int i = 0; i < MG; ++i) {
-      const int gm = wave * MG + i;
-#pragma unroll
-      for (int f = 0; f < FC; ++f)
-        v[f][i] = f0 + f < NF ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                              pr, gm < G ? off[f0 + f] + gm * plane : 0x7FFFFFF0u, 0, 16))
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint32_t bit = 1u << (wave * MG + i);
+      if ((late >> i) & 1)
+        missing |= bit;
+      else if (guard && wave * MG + i < G && f0 < nf && __ballot((lo[0][i][1] & 15u) != xcc) != 0)
+        other |= bit;
     }
 #pragma unroll
     for (int f = 0; f < FC; ++f) {
-      f32x4 w = v[f][0];
+      f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 1; i < MG; ++i) w += v[f][i];
+      for (int i = 0; i < MG; ++i) {
+        const f32x4 v = {bits_as<float>(lo[f][i][0]), bits_as<float>(lo[f][i][2]), bits_as<float>(hi[f][i][0]),
+                         bits_as<float>(hi[f][i][2])};
+        w = i == 0 ? v : w + v;
+      }
       if (f0 + f < nf) stage[((f0 + f) * 4 + wave) * kWave + lane] = w;
     }
   }
-  __syncthreads();
+  *foreign = other;
+  return missing | other;
+}
+
+// poll_wave with the members per wave the member count G = 2^gsh needs
+template <int NF>
+__device__ __forceinline__ uint32_t poll_members(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int gsh,
+                                                 int nf, uint32_t want, uint32_t xcc, int spin_limit, bool guard,
+                                                 f32x4 *stage, uint32_t *foreign) {
+  switch (gsh) {
+    case 0:
+    case 1:
+    case 2: return poll_wave<1, NF>(pr, off, plane, 1 << gsh, nf, want, xcc, spin_limit, guard, stage, foreign);
+    case 3: return poll_wave<2, NF>(pr, off, plane, 8, nf, want, xcc, spin_limit, guard, stage, foreign);
+    default: return poll_wave<4, NF>(pr, off, plane, 16, nf, want, xcc, spin_limit, guard, stage, foreign);
+  }
+}
+
+// Polls that the later token blocks of a tile may take: by then every member
+// is known to run on this XCD or was computed here, so its fragments are on
+// their way to this L2 and the bound is never reached (if it were, status[0]
+// counts it).
+constexpr int kLaterPolls = 1 << 20;
+
+// The four waves' sums of each fragment, added in wave order (after the
+// barrier that follows poll_members).
+template <int NF>
+__device__ __forceinline__ void stage_sums(const f32x4 *stage, int nf, f32x4 (&u)[NF]) {
+  const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const f32x4 *st = stage + f * 4 * kWave + lane;
     u[f] = f < nf ? ((st[0] + st[kWave]) + st[2 * kWave]) + st[3 * kWave] : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// gather_waves with the members per wave the member count G = 2^gsh needs
-template <int NF>
-__device__ __forceinline__ void gather_members(rsrc_t pr, const uint32_t (&off)[NF], uint32_t plane, int gsh, int nf,
-                                               f32x4 *stage, f32x4 (&u)[NF]) {
-  switch (gsh) {
-    case 0:
-    case 1:
-    case 2: gather_waves<1, NF>(pr, off, plane, 1 << gsh, nf, stage, u); break;
-    case 3: gather_waves<2, NF>(pr, off, plane, 8, nf, stage, u); break;
-    default: gather_waves<4, NF>(pr, off, plane, 16, nf, stage, u); break;
   }
 }
 
@@ -242,6 +286,9 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords;  // the first range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
+  const uint32_t want = (f & ~15u) + 16u;  // this call's count (bits 31:4)
+  const uint32_t xcc = xcc_id(), tag = want | xcc;
+  uint32_t *const status = flags + (int64_t)kSyncTiles * kSplitFlagWords;
   const int gb0 = g * p.bpm;
   const int nbm = min(p.bpm, p.blk_base[p.n_slices] - gb0);  // this member's blocks (may be <= 0)
   if (slot < 0) {  // no adapter: nothing to add, or windows to clear
@@ -257,9 +304,11 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   const int pa = p.n_slices << (p.ksh + LPR);  // A pieces: n_slices * kc * PR
   // pieces outside the chunk read the slot's first row and are stored as
   // zeros (aok); loaded values are never selected, so no load sits in a branch
+  // (the operand arrays are parameters, so that the fallback below holds
+  // arrays of its own and these die after the first shrink)
   u32x4 av[kSBatch];
   uint32_t aok = 0;
-  auto load_a = [&](int gm) {  // member gm's A chunk of every slice
+  auto load_a = [&](int gm, u32x4 (&av)[kSBatch], uint32_t &aok) {  // member gm's A chunk of every slice
     const int64_t k0 = (int64_t)gm << p.ksh;
     aok = 0;
 #pragma unroll
@@ -277,7 +326,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
       av[i] = gload16(ptr);
     }
   };
-  load_a(g);
+  load_a(g, av, aok);
   const bool xw = wave < nb;  // this wave shrinks token block `wave`
   const bool xok = xw && 16 * wave + l16 < rows;
   const int xt = wave == 0 ? tok[0] : (wave == 1 ? tok[1] : (wave == 2 ? tok[2] : tok[3]));
@@ -286,7 +335,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   // x fragments past d_in meet zero A rows, and rows past the tile feed
   // outputs that are never used: both read the row's first values instead
   u32x4 xa[XB];
-  auto load_x = [&](int gm) {  // member gm's x fragments of this wave's token block
+  auto load_x = [&](int gm, u32x4 (&xa)[XB]) {  // member gm's x fragments of this wave's token block
     const int64_t kx = ((int64_t)gm << p.ksh) + 8 * kg;  // this lane's k at step 0
 #pragma unroll
     for (int i = 0; i < XB; ++i) {
@@ -294,7 +343,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
       xa[i] = gload16(xbase + (i < nsteps && k < p.d_in ? k : 0));
     }
   };
-  if (xw) load_x(g);
+  if (xw) load_x(g, xa);
   u32x4 bv[kSBatch];
   uint32_t bok = 0;
 #pragma unroll
@@ -325,9 +374,16 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
     const int64_t col = 16 * (int64_t)(gb - pick<NS + 1>(p.blk_base, qs[q], p.n_slices + 1)) + 4 * kg;
     qok[q] = lb < nbm && col < pick<NS>(p.width, qs[q], p.n_slices);
     qcol[q] = pick<NS>(p.offset, qs[q], p.n_slices) + col;
-    const bool ok = p.add && qok[q] && l16 < rows;  // else unused
-    yv[q] = *reinterpret_cast<const u32x2 *>(y + (ok ? (int64_t)tok[0] * p.ldy + qcol[q] : 0));
   }
+  auto load_yv = [&](int t) {  // y of token block t (rows past the tile: unused)
+    const int tk = t == 0 ? tok[0] : (t == 1 ? tok[1] : (t == 2 ? tok[2] : tok[3]));
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const bool ok = p.add && qok[q] && 16 * t + l16 < rows;
+      yv[q] = *reinterpret_cast<const u32x2 *>(y + (ok ? (int64_t)tk * p.ldy + qcol[q] : 0));
+    }
+  };
+  load_yv(0);
   const int rk = p.slot_rank ? min(max(p.slot_rank[slot], 0), R) : R;
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   if (rk == 0) {  // the adapter adds nothing
@@ -337,7 +393,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   const int rk8 = (rk + 7) & ~7;  // ranks read, as the other kernels read them
 
   // ---- A chunk into LDS (ranks past the slot's rank as zeros)
-  auto stage_a = [&]() {
+  auto stage_a = [&](const u32x4 (&av)[kSBatch], uint32_t aok) {
 #pragma unroll
     for (int i = 0; i < kSBatch; ++i) {
       const int q = tid + kSThreads * i;
@@ -350,7 +406,9 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
       }
     }
   };
-  stage_a();
+  __shared__ uint32_t missing_s;  // members whose partials this workgroup computes itself
+  if (tid == 0) missing_s = 0;
+  stage_a(av, aok);
   __syncthreads();
 
   // ---- shrink: wave t, all k-steps of token block t.  D' = A^T x^T, so that
@@ -359,11 +417,11 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   const rsrc_t pr = make_rsrc(p.part, p.part_bytes);
   const int fr0 = ((pos0 + 15) >> 4) + ti;  // the tile's first fragment
   auto frag_off = [&](int gg, int t, int s, int c) {
-    return (uint32_t)(((((gg * p.n_frag + fr0 + t) * p.n_slices + s) * RB + c) * kWave + lane) * 16);
+    return (uint32_t)((((gg * p.n_frag + fr0 + t) * p.n_slices + s) * RB + c) * 2048 + lane * 16);
   };
   // member gm's partial rows of token block `wave`, from the staged A chunk
   // and xa, into member gm's slot
-  auto shrink_store = [&](int gm) {
+  auto shrink_store = [&](int gm, const u32x4 (&xa)[XB]) {
     f32x4 acc[NS][RB];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -389,9 +447,9 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        if (s < p.n_slices) __builtin_amdgcn_raw_buffer_store_b128(acc[s][rb], pr, frag_off(gm, wave, s, rb), 0, 0);
+        if (s < p.n_slices) store_tagged(pr, frag_off(gm, wave, s, rb), acc[s][rb], tag);
   };
-  if (xw) shrink_store(g);
+  if (xw) shrink_store(g, xa);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
 #pragma unroll
   for (int i = 0; i < kSBatch; ++i) {
@@ -402,32 +460,52 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
           ((bok >> i) & 1) && j < rk8 ? bv[i] : u32x4{0, 0, 0, 0};
     }
   }
-  // ---- rendezvous: the fragments are acknowledged before the flag goes up
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (G > 1) {
-    __shared__ uint32_t missing;
-    if (wave == 0) {
-      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, xcc_id(), flags + (int64_t)kSyncTiles * kSplitFlagWords);
-      if (lane == 0) missing = m;
+  // ---- the count word for the next call (the peers read the partials' own tags)
+  if (wave == 0) raise_count(fl, g, G, tag);
+
+  // ---- rendezvous: the members' fragments of token block 0 are polled.
+  // Members whose partials do not arrive in time, or arrive tagged by
+  // another XCD (whose later blocks could stay in that XCD's L2 until the
+  // kernel ends), are computed here, by the same code, so they are the bits
+  // those members store themselves; block 0 is then gathered again, from
+  // this workgroup's own stores for those members.  The stage (n_slices RB
+  // 4 KB) fits the A chunk's region: kc >= 128.
+  f32x4 *const stage = reinterpret_cast<f32x4 *>(split_lds);
+  const uint32_t plane = (uint32_t)(p.n_frag * p.n_slices * RB * 2048);
+  bool regather = false;
+  {
+    uint32_t off[NS * RB];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < RB; ++c) off[s * RB + c] = s < p.n_slices ? frag_off(0, 0, s, c) : 0x7FFFFFF0u;
+    uint32_t foreign = 0;
+    const uint32_t miss = poll_members<NS * RB>(pr, off, plane, p.gsh, p.n_slices * RB, want, xcc, p.spin_limit,
+                                                true, stage, &foreign);
+    if (miss && lane == 0) atomicOr(&missing_s, miss);
+    if (lane == 0) {
+      if (miss & ~foreign) atomicAdd(status, 1u);
+      if (foreign) atomicAdd(status + 1, 1u);
     }
     __syncthreads();
-    // members that did not arrive in time: their partials are computed here,
-    // by the same code, so they are the bits those members store themselves
-    for (uint32_t m = missing; m; m &= m - 1) {
-      const int gm = __builtin_ctz(m);
-      load_a(gm);
-      if (xw) load_x(gm);
-      __syncthreads();  // the A chunk's LDS is free
-      stage_a();
-      __syncthreads();
-      if (xw) shrink_store(gm);
-    }
-    if (missing) {
+    const uint32_t m_all = missing_s;
+    if (m_all) {
+      for (uint32_t m = m_all; m; m &= m - 1) {
+        const int gm = __builtin_ctz(m);
+        u32x4 av2[kSBatch], xa2[XB];
+        uint32_t aok2 = 0;
+        load_a(gm, av2, aok2);
+        if (xw) load_x(gm, xa2);
+        __syncthreads();  // the A chunk's LDS (the stage too) is free
+        stage_a(av2, aok2);
+        __syncthreads();
+        if (xw) shrink_store(gm, xa2);
+      }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      load_yv(0);  // again: the block's y is not kept over this path
+      regather = true;
     }
   }
 
@@ -444,9 +522,14 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
 #pragma unroll
         for (int c = 0; c < RB; ++c) off[s * RB + c] = s < p.n_slices ? frag_off(0, t, s, c) : 0x7FFFFFF0u;
       f32x4 u[NS * RB];
-      // the stage (n_slices RB 4 KB) fits the A chunk's region: kc >= 128
-      gather_members<NS * RB>(pr, off, p.n_frag * p.n_slices * RB * 1024, p.gsh, p.n_slices * RB,
-                              reinterpret_cast<f32x4 *>(split_lds), u);
+      if (t > 0 || regather) {  // the fragments of block t (of every member: see above)
+        uint32_t foreign = 0;
+        const uint32_t miss = poll_members<NS * RB>(pr, off, plane, p.gsh, p.n_slices * RB, want, xcc, kLaterPolls,
+                                                    false, stage, &foreign);
+        if (miss && lane == 0) atomicAdd(status, 1u);
+        __syncthreads();
+      }
+      stage_sums<NS * RB>(stage, p.n_slices * RB, u);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
 #pragma unroll
@@ -637,6 +720,9 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords + kSplitMembers * sl;  // this slice's range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
+  const uint32_t want = (f & ~15u) + 16u;  // this call's count (bits 31:4)
+  const uint32_t xcc = xcc_id(), tag = want | xcc;
+  uint32_t *const status = flags + (int64_t)kSyncTiles * kSplitFlagWords;
   const int gb0 = g * bpm;
   const int nbm = min(bpm, nbt - gb0);
   if (slot < 0) {
@@ -658,15 +744,17 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const int nb = (rows + 15) >> 4;
   const rsrc_t ar = make_rsrc(reinterpret_cast<const uint16_t *>(a_base) + (int64_t)slot * a_stride,
                               (uint32_t)(p.d_in * R * 2));
+  // (the operand arrays are parameters, so that the fallback below holds
+  // arrays of its own and these die after the first shrink)
   u32x4 av[NA];
-  auto load_a = [&](int gm) {  // member gm's A chunk
+  auto load_a = [&](int gm, u32x4 (&av)[NA]) {  // member gm's A chunk
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int q = tid + kSThreads * i;
       av[i] = buf_load16(ar, q < NPA ? (uint32_t)(gm * KC * R * 2 + q * 16) : kOut);
     }
   };
-  load_a(g);
+  load_a(g, av);
   // the shrink: up to rank 32, a tile of one 16-row block (decode) spreads
   // its k-steps over the four waves, wave w taking steps w KQ .. + KQ - 1; a
   // taller tile, or rank 64, gives wave t every step of token block t
@@ -679,7 +767,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   u32x4 xa[KS];
   // member gm's x fragments of this wave's steps; rows past the tile read
   // zeros (their partial rows are never stored)
-  auto load_x = [&](int gm) {
+  auto load_x = [&](int gm, u32x4 (&xa)[KS]) {
     const uint32_t xo = xw && 16 * blk + l16 < rows
                             ? (uint32_t)((xrow * p.ldx + gm * KC + (one ? 32 * KQ * wave : 0) + 8 * kg) * 2)
                             : kOut;
@@ -691,7 +779,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       for (int i = 0; i < KS; ++i) xa[i] = buf_load16(xr, xo + 64 * i);
     }
   };
-  load_x(g);
+  load_x(g, xa);
   const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(b_base) + (int64_t)slot * b_stride,
                               (uint32_t)(R * width * 2));
   u32x4 bv[NBQ];
@@ -704,23 +792,24 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
     bv[i] = buf_load16(br, ok ? (uint32_t)((j * width + col) * 2) : kOut);
   }
   // y of the first token block.  Up to 512-row chunks it is loaded here and
-  // arrives with the rest of the batch, so it holds neither the
-  // acknowledgement wait nor the polls (loads complete in order).  With
-  // 1024-row chunks (32 x loads a lane) it is loaded once the fragments are
-  // acknowledged: each order measured faster for its own chunk length.
+  // arrives with the rest of the batch, so it does not hold the polls (loads
+  // complete in order).  With 1024-row chunks (32 x loads a lane) it is
+  // loaded once the partials are stored.
   constexpr bool kYEarly = KS <= 16;
   const rsrc_t yr = make_rsrc(p.y, p.y_bytes);
   const uint32_t yo0 = (uint32_t)((offset + 16 * (gb0 + wave) + 4 * kg) * 2);  // + 128 q: block wave + 4 q
-  uint32_t yrow = (uint32_t)(tok[0] * p.ldy * 2);
+  uint32_t yrow = 0;
   u32x2 yv[QB];
-  auto load_y0 = [&]() {
+  auto load_y = [&](int t) {  // y of token block t
+    const int tk = t == 0 ? tok[0] : (t == 1 ? tok[1] : (t == 2 ? tok[2] : tok[3]));
+    yrow = (uint32_t)(tk * p.ldy * 2);
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const bool ok = p.add && wave + 4 * q < nbm;
       yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
     }
   };
-  if constexpr (kYEarly) load_y0();
+  if constexpr (kYEarly) load_y(0);
   const int rk = p.slot_rank ? min(max(p.slot_rank[slot], 0), R) : R;
   const float sc = p.scale * (p.slot_scale ? p.slot_scale[slot] : 1.f);
   if (rk == 0) {
@@ -730,7 +819,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   const int rk8 = (rk + 7) & ~7;
 
   // ---- A chunk into LDS: piece q = row q / (R / 8), ranks 8 (q % (R / 8)) ..
-  auto stage_a = [&]() {
+  auto stage_a = [&](const u32x4 (&av)[NA]) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int q = tid + kSThreads * i;
@@ -741,15 +830,17 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       }
     }
   };
-  stage_a();
+  __shared__ uint32_t missing_s;  // members whose partials this workgroup computes itself
+  if (tid == 0) missing_s = 0;
+  stage_a(av);
   __syncthreads();
   LORA_PHASE(2);
 
   // ---- shrink (D' = A^T x^T, so that lane (token l16, kg) ends with ranks
   // 4 kg .. + 3 of its token)
   const rsrc_t pr = make_rsrc(p.part, p.part_bytes);
-  const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 1024 + lane * 16) + sl * p.part_slice;
-  const uint32_t plane = (uint32_t)(p.n_frag * RB * 1024);  // between members
+  const uint32_t fbase = (uint32_t)((((pos0 + 15) >> 4) + ti) * RB * 2048 + lane * 16) + sl * p.part_slice;
+  const uint32_t plane = (uint32_t)(p.n_frag * RB * 2048);  // between members
   // member gm's partial rows, from the staged A chunk and xa, into member
   // gm's slot.  Two accumulator chains (even and odd k-steps) added at the
   // end: the MFMAs of one chain wait for each other, the two chains do not.
@@ -757,7 +848,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   // (RB x 4 waves x 64 lanes, a region of its own after the B chunk), and
   // wave 0 stores them.  Called by every wave.
   f32x4 *const red = reinterpret_cast<f32x4 *>(split_lds + p.bs_off + RP * p.ldb * 2);
-  auto shrink_store = [&](int gm) {
+  auto shrink_store = [&](int gm, const u32x4 (&xa)[KS]) {
     f32x4 acc[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[0][rb] = acc[1][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -780,8 +871,8 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const f32x4 *r4 = red + rb * 4 * kWave + lane;
-          __builtin_amdgcn_raw_buffer_store_b128(((r4[0] + r4[kWave]) + r4[2 * kWave]) + r4[3 * kWave], pr,
-                                                 fbase + gm * plane + rb * 1024, 0, 0);
+          store_tagged(pr, fbase + gm * plane + rb * 2048, ((r4[0] + r4[kWave]) + r4[2 * kWave]) + r4[3 * kWave],
+                       tag);
         }
       }
     } else if (xw) {
@@ -796,11 +887,10 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        __builtin_amdgcn_raw_buffer_store_b128(acc[0][rb] + acc[1][rb], pr,
-                                               fbase + gm * plane + (wave * RB + rb) * 1024, 0, 0);
+        store_tagged(pr, fbase + gm * plane + (wave * RB + rb) * 2048, acc[0][rb] + acc[1][rb], tag);
     }
   };
-  shrink_store(g);
+  shrink_store(g, xa);
   // ---- B chunk into LDS (rank rows past the slot's rank as zeros)
 #pragma unroll
   for (int i = 0; i < NBQ; ++i) {
@@ -810,35 +900,51 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       *reinterpret_cast<u32x4 *>(Bs + j * p.ldb + 16 * lb + 8 * half) = j < rk8 ? bv[i] : u32x4{0, 0, 0, 0};
     }
   }
-  // ---- rendezvous: the fragments are acknowledged before the flag goes up
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
+  // ---- the count word for the next call (the peers read the partials' own
+  // tags); the B chunk is staged before any wave reads it
+  if (wave == 0) raise_count(fl, g, G, tag);
   __syncthreads();
   LORA_PHASE(3);
-  if constexpr (!kYEarly) load_y0();
-  if (G > 1) {
-    __shared__ uint32_t missing;
-    if (wave == 0) {
-      const uint32_t m = split_wait(fl, f, g, G, p.spin_limit, xcc_id(), flags + (int64_t)kSyncTiles * kSplitFlagWords);
-      if (lane == 0) missing = m;
+  if constexpr (!kYEarly) load_y(0);
+
+  // ---- rendezvous: the members' fragments of token block 0 are polled.
+  // Members whose partials do not arrive in time, or arrive tagged by
+  // another XCD (whose later blocks could stay in that XCD's L2 until the
+  // kernel ends), are computed here, by the same code, so they are the bits
+  // those members store themselves (a late member and this workgroup then
+  // write equal values); block 0 is then gathered again, from this
+  // workgroup's own stores for those members.
+  f32x4 *const stage = reinterpret_cast<f32x4 *>(split_lds);
+  bool regather = false;
+  {
+    uint32_t off[RB];
+#pragma unroll
+    for (int c = 0; c < RB; ++c) off[c] = fbase + c * 2048;
+    uint32_t foreign = 0;
+    const uint32_t miss = poll_members<RB>(pr, off, plane, p.gsh, RB, want, xcc, p.spin_limit, true, stage, &foreign);
+    if (miss && lane == 0) atomicOr(&missing_s, miss);
+    if (lane == 0) {
+      if (miss & ~foreign) atomicAdd(status, 1u);
+      if (foreign) atomicAdd(status + 1, 1u);
     }
     __syncthreads();
-    // members that did not arrive in time: their partials are computed here,
-    // by the same code, so they are the bits those members store themselves
-    // (a late member and this workgroup then write equal values)
-    for (uint32_t m = missing; m; m &= m - 1) {
-      const int gm = __builtin_ctz(m);
-      load_a(gm);
-      load_x(gm);
-      __syncthreads();  // the A chunk's LDS is free
-      stage_a();
-      __syncthreads();
-      shrink_store(gm);
-    }
-    if (missing) {
+    const uint32_t m_all = missing_s;
+    if (m_all) {
+      for (uint32_t m = m_all; m; m &= m - 1) {
+        const int gm = __builtin_ctz(m);
+        u32x4 av2[NA], xa2[KS];
+        load_a(gm, av2);
+        load_x(gm, xa2);
+        __syncthreads();  // the A chunk's LDS (the stage too) is free
+        stage_a(av2);
+        __syncthreads();
+        shrink_store(gm, xa2);
+      }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if constexpr (kYEarly) load_y(0);  // again: the block's y is not kept over this path
+      regather = true;
     }
   }
   LORA_PHASE(4);
@@ -849,22 +955,20 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   // nothing).  Each block's y is stored as soon as its two products are done:
   // that measured faster than issuing every product first, and than one
   // 16x16x32 product with hi and lo as the two halves of K.
-  // B^T operands first: their LDS reads overlap the gather's loads
-  s16x4 bw[QB][RB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const int lb = wave + 4 * q < nbm ? wave + 4 * q : 0;
-#pragma unroll
-    for (int c = 0; c < RB; ++c) bw[q][c] = lds_col4(Bs, p.ldb, 16 * c + 4 * kg, 16 * lb);
-  }
   for (int t = 0; t < nb; ++t) {
     s16x4 uh[RB], ul[RB];
     {
-      uint32_t off[RB];
-#pragma unroll
-      for (int c = 0; c < RB; ++c) off[c] = fbase + (t * RB + c) * 1024;
       f32x4 u[RB];
-      gather_members<RB>(pr, off, plane, p.gsh, RB, reinterpret_cast<f32x4 *>(split_lds), u);
+      if (t > 0 || regather) {  // the fragments of block t (of every member: see above)
+        uint32_t off[RB];
+#pragma unroll
+        for (int c = 0; c < RB; ++c) off[c] = fbase + (t * RB + c) * 2048;
+        uint32_t foreign = 0;
+        const uint32_t miss = poll_members<RB>(pr, off, plane, p.gsh, RB, want, xcc, kLaterPolls, false, stage, &foreign);
+        if (miss && lane == 0) atomicAdd(status, 1u);
+        __syncthreads();
+      }
+      stage_sums<RB>(stage, RB, u);
 #pragma unroll
       for (int c = 0; c < RB; ++c) {
         uint32_t h[4], l[4];
@@ -875,6 +979,14 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       }
     }
     if (t == 0) LORA_PHASE(5);
+    // B^T operands of this wave's column blocks (the B chunk stays in LDS)
+    s16x4 bw[QB][RB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int lb = wave + 4 * q < nbm ? wave + 4 * q : 0;
+#pragma unroll
+      for (int c = 0; c < RB; ++c) bw[q][c] = lds_col4(Bs, p.ldb, 16 * c + 4 * kg, 16 * lb);
+    }
     const bool rok = 16 * t + l16 < rows;
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
@@ -890,14 +1002,8 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
       if (rok && wave + 4 * q < nbm && 16 * (gb0 + wave + 4 * q) + 4 * kg < width)
         __builtin_amdgcn_raw_buffer_store_b64(v, yr, yrow + yo0 + 128 * q, 0, 0);
     }
-    if (t + 1 < nb) {  // y of the next token block
-      const int tn = t + 1 == 1 ? tok[1] : (t + 1 == 2 ? tok[2] : tok[3]);
-      yrow = (uint32_t)(tn * p.ldy * 2);
-#pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        const bool ok = p.add && wave + 4 * q < nbm;
-        yv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yr, ok ? yrow + yo0 + 128 * q : kOut, 0, 0));
-      }
+    if (t + 1 < nb) {
+      load_y(t + 1);
       __syncthreads();  // every wave has read the gather's LDS
     }
   }
@@ -928,7 +1034,7 @@ size_t split_ws_bytes(int64_t T, int32_t S, int32_t n_slices, int32_t R) {
   const int64_t RP = R < 16 ? 16 : R;
   if (T * n_slices * RP > ((int64_t)1 << 17)) return 0;
   const int64_t n_frag = (T + 15) / 16 + max_tiles(T, S);
-  return (size_t)kSplitMembers * n_frag * n_slices * (RP / 16) * 1024;
+  return (size_t)kSplitMembers * n_frag * n_slices * (RP / 16) * 2048;  // tagged fragments of 2048 bytes
 }
 
 static std::atomic<int> g_split_resident[4][4][kMaxDevices];
@@ -989,7 +1095,7 @@ static SplitPlan plan_split(int64_t T, int32_t S, int64_t d_in, int32_t n_slices
   pl.bs_off = (int)split_region1(a_slices, (int64_t)1 << pl.ksh, R);
   pl.lds = pl.bs_off + (size_t)RP * pl.ldb * 2;
   pl.grid = (int)(8 * G * ((mt + 7) / 8)) * (side ? n_slices : 1);
-  const size_t need = (size_t)G * ((T + 15) / 16 + mt) * n_slices * RB * 1024;
+  const size_t need = (size_t)G * ((T + 15) / 16 + mt) * n_slices * RB * 2048;
   if (need > ws_bytes) return pl;
   pl.ok = true;
   return pl;
@@ -1082,7 +1188,7 @@ static hipError_t launch_split1_k(const MetaView &meta, const SplitParams &sp, c
     q.nbt[s] = sp.blk_base[s + 1] - sp.blk_base[s];
     q.bpm[s] = (q.nbt[s] + pl.G - 1) / pl.G;
   }
-  p.part_slice = (uint32_t)((size_t)pl.G * sp.n_frag * RB * 1024);
+  p.part_slice = (uint32_t)((size_t)pl.G * sp.n_frag * RB * 2048);
   p.y = sp.y;
   p.part = sp.part;
   p.slot_scale = sp.slot_scale;

@@ -182,7 +182,7 @@ def test_apply_rejections():
     wd, of = (C.c_int64 * 1)(64), (C.c_int64 * 1)(0)
     args = lambda ws, ws_bytes: (C.byref(_meta()), _ptr(), 64, 64, 1, n, A, B, wd, of, 16,
                                  C.c_float(1.0), None, None, _ptr(), 64, 1, 0, ws, ws_bytes, None)
-    big = 1 << 19   # enough for this call: rendezvous words + rank buffer
+    big = 1 << 22   # enough for this call: count words, rank buffer, tagged partials
     assert _call("lora_apply", *args(_ptr(), 16)) == L.LORA_ERR_WORKSPACE
     assert _call("lora_apply", *args(_ptr(), L.APPLY_SYNC_BYTES)) == L.LORA_ERR_WORKSPACE
     assert _call("lora_apply", None, *args(_ptr(), big)[1:]) == L.LORA_ERR_INVALID_ARG
