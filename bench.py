@@ -702,8 +702,9 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
 
 
 PHASES = ["launch spread (start - first start)", "tile header (1 - 0)", "A chunk in LDS (2 - 1)",
-          "rest of batch, shrink, partials acknowledged (3 - 2)", "rendezvous (4 - 3)",
-          "gather of the first block's u (5 - 4)", "expand, y stores acknowledged (6 - 5)",
+          "rest of batch, shrink, partials stored, B staged (3 - 2)",
+          "rendezvous: the members' first-block partials polled in (4 - 3)",
+          "sum of the first block's u (5 - 4)", "expand, y stores acknowledged (6 - 5)",
           "workgroup total (6 - 0)", "end (6 - first start)"]
 
 

@@ -83,12 +83,12 @@ typedef struct lora_weight {
     int64_t slot_stride;            /* elements between consecutive slots */
 } lora_weight;
 
-/* Bytes at the start of every lora_apply workspace that hold the rendezvous
- * words of the decode-shaped apply (below, lora_apply_workspace_init). */
+/* Bytes at the start of every lora_apply workspace that hold the per-tile call
+ * count words of the decode-shaped apply (below, lora_apply_workspace_init). */
 #define LORA_APPLY_SYNC_BYTES 295168
 /* Word indices, in that region, of two counters the decode-shaped apply keeps
- * (read them as uint32): waits for peer workgroups that gave up, and waits
- * that met a peer on another accelerator die (XCD).  Each case is handled
+ * (read them as uint32): waits for peer workgroups' partial results that gave
+ * up, and peers met on another accelerator die (XCD).  Each case is handled
  * (the waiting workgroup computes the peer's share itself, with the same
  * result); the counters only report that it happened. */
 #define LORA_APPLY_WAITS_GAVE_UP_WORD 73728
@@ -253,22 +253,23 @@ lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slice
 
 /* Bytes of device workspace lora_apply needs for these sizes (a workspace
  * sized for the largest call can serve every smaller one).  Layout: the
- * rendezvous words (LORA_APPLY_SYNC_BYTES), the fp32 rank-r buffer, then the
+ * count words (LORA_APPLY_SYNC_BYTES), the fp32 rank-r buffer, then the
  * partial sums of a shrink that splits d_in or of the decode-shaped kernel.
- * Only the rendezvous words need initialising: see lora_apply_workspace_init. */
+ * Only the count words need initialising: see lora_apply_workspace_init. */
 lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
                                        int64_t d_in, int32_t n_slices,
                                        int32_t r_max, lora_dtype dtype,
                                        lora_mode mode, size_t *bytes);
 
-/* Zero the rendezvous words of an apply workspace (its first
+/* Zero the count words of an apply workspace (its first
  * LORA_APPLY_SYNC_BYTES bytes; enqueued on `stream`).  Call it once, before
  * the first lora_apply on a workspace; zero-filled memory needs no call.  The
  * decode-shaped apply (page "多 LoRA 服务：分段矩阵乘与适配器调度", section
  * "不合并权重，批量计算": the fused form for decode batches) spreads each work
- * tile over several workgroups that meet at per-tile flag words kept here.
- * Every call leaves them consistent for the next call on the same workspace,
- * whatever its shapes.  The words must not be written between calls.
+ * tile over several workgroups that exchange partial results tagged with the
+ * tile's call count, which these words keep.  Every call leaves them
+ * consistent for the next call on the same workspace, whatever its shapes.
+ * The words must not be written between calls.
  *   d_ws      device workspace, 16-byte aligned
  *   ws_bytes  its size, at least LORA_APPLY_SYNC_BYTES (else LORA_ERR_WORKSPACE) */
 lora_status lora_apply_workspace_init(void *d_ws, size_t ws_bytes, void *stream);
@@ -282,7 +283,7 @@ lora_status lora_apply_workspace_init(void *d_ws, size_t ws_bytes, void *stream)
  * 服务", section "调用链" (add_lora_linear = shrink into an fp32 buffer, then
  * expand into the output slices).
  *   d_ws      workspace of at least lora_apply_workspace_bytes bytes, 16-byte
- *             aligned, whose rendezvous words were initialised once
+ *             aligned, whose count words were initialised once
  *             (lora_apply_workspace_init) and not written since except by
  *             lora_apply.  Calls that run at the same time need workspaces of
  *             their own; calls in stream order may share one. */

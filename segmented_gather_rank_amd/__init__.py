@@ -154,12 +154,12 @@ def _weights(ws, name: str, inner_shape_ok) -> tuple:
 
 TILE_ROWS = 64          # sorted positions per work tile of the metadata
 TILE_INTS = 4 + TILE_ROWS
-# the apply workspace's rendezvous words (LORA_APPLY_SYNC_BYTES and the two
+# the apply workspace's count words (LORA_APPLY_SYNC_BYTES and the two
 # counter indices of the C header)
 APPLY_SYNC_BYTES = 295168
 WAITS_GAVE_UP_WORD = 73728
 OTHER_XCD_WORD = 73729
-SPLIT_MEMBERS = 16      # rendezvous words per work tile and slice range
+SPLIT_MEMBERS = 16      # count words per work tile and slice range
 SPLIT_RANGES = 4        # slice ranges per work tile
 
 
@@ -283,7 +283,7 @@ def lora_apply_workspace_bytes(num_tokens, num_slots, d_in, n_slices, r_max, dty
 
 
 def lora_apply_workspace_init(workspace: torch.Tensor, stream=None) -> torch.Tensor:
-    """Zero the rendezvous words at the start of an apply workspace (once,
+    """Zero the count words at the start of an apply workspace (once,
     before its first lora_apply)."""
     _check("lora_apply_workspace_init",
            _lib.lora_apply_workspace_init(_dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
@@ -292,7 +292,7 @@ def lora_apply_workspace_init(workspace: torch.Tensor, stream=None) -> torch.Ten
 
 def apply_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A zero-filled apply workspace of at least nbytes (and at least the
-    rendezvous words), ready for lora_apply."""
+    count words), ready for lora_apply."""
     return torch.zeros(max(int(nbytes), APPLY_SYNC_BYTES), dtype=torch.uint8, device=device)
 
 
@@ -306,7 +306,7 @@ def apply_workspace_counters(workspace: torch.Tensor) -> dict:
 
 
 def apply_workspace_flags(workspace: torch.Tensor, tiles: int) -> torch.Tensor:
-    """The rendezvous words of the first `tiles` work tiles, [tile][range][member]
+    """The count words of the first `tiles` work tiles, [tile][range][member]
     (int32 view of uint32 words: the call count in bits 31:4, an XCD in 3:0)."""
     w = workspace[:APPLY_SYNC_BYTES].view(torch.int32)
     return w[:tiles * SPLIT_RANGES * SPLIT_MEMBERS].view(tiles, SPLIT_RANGES, SPLIT_MEMBERS)

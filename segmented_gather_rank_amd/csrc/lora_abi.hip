@@ -9,12 +9,12 @@
 #include "lora_host.h"
 
 // Workspace of lora_apply_noalloc: a static device array of the library, one
-// copy per device, zero at load (so its rendezvous words start initialised).
+// copy per device, zero at load (so its count words start initialised).
 // In host code its name stands for a host-side shadow, not a device address:
 // a device's copy is reached only through the address hipGetSymbolAddress
 // gives on that device (scratch_of_current_device, below).
 static constexpr size_t kScratchBytes = (size_t)LORA_NOALLOC_SCRATCH_BYTES;
-static_assert(kScratchBytes % 256 == 0 && kScratchBytes >= lora::kSyncBytes, "scratch holds the rendezvous words");
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes >= lora::kSyncBytes, "scratch holds the count words");
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace lora {
@@ -37,9 +37,10 @@ bool split_disabled() {
   static const bool v = env_int("LORA_DISABLE_SPLIT_BGMV", 0) > 0;
   return v;
 }
-// Polls a workgroup of the split kernel makes while waiting for its peers
-// before it computes the missing members' partials itself
-// (LORA_SPLIT_SPIN_LIMIT, 0 allowed): about a microsecond each.
+// Looks a workgroup of the split kernel takes at its peers' partials before it
+// computes the missing members' partials itself (LORA_SPLIT_SPIN_LIMIT, 0
+// allowed): each look is one L2 round trip and a short sleep, under a
+// microsecond.
 int split_spin_limit() {
   static const int v = [] {
     const char *e = std::getenv("LORA_SPLIT_SPIN_LIMIT");
@@ -202,7 +203,7 @@ void unpack(const lora_weight *W, int32_t n, const void **ptrs, int64_t *strides
 }
 
 
-// lora_apply on a workspace that holds the rendezvous words, then the rank-r
+// lora_apply on a workspace that holds the count words, then the rank-r
 // buffer, then the partial sums (ws_bytes in all, already checked to be
 // enough).
 lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_t d_in, lora_dtype dtype,
@@ -443,7 +444,7 @@ lora_status lora_apply_workspace_bytes(int64_t T, int32_t S, int64_t d_in, int32
   // without a split of d_in
   if (expand_rows_fits(T, S, dtype == LORA_BF16, (int)mode, R))
     sh = std::max(sh, align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)R));
-  // rendezvous words, then the rank-R buffer, then the shrink's or the split
+  // count words, then the rank-R buffer, then the shrink's or the split
   // kernel's partial sums
   *bytes = kSyncBytes + align256(sizeof(float) * (size_t)n_slices * (size_t)T * (size_t)R) + sh;
   return LORA_OK;

@@ -94,7 +94,7 @@ struct SplitParams {
   int64_t ldy;
   int32_t add;
   float *part;  // partial fragments [G][n_frag][n_slices][R16 blocks][64 lanes][4]
-  uint32_t *sync;  // rendezvous words (host side only: the kernels take them as an argument)
+  uint32_t *sync;  // count words (host side only: the kernels take them as an argument)
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -619,11 +619,11 @@ struct Split1Params {
 #ifdef LORA_PHASE_CLOCK
 // A measurement build: each workgroup of the one-slice kernel records the
 // 100 MHz real-time counter when it starts (0), has its tile header (1), its
-// A chunk in LDS (2), every load of the batch landed and its partial rows
-// acknowledged (3), the rendezvous done (4), the first token block's u
-// gathered (5) and its y stores acknowledged (6); then (7) ti | g << 16 |
-// slice << 24, (8) the HW_ID register, (9) XCC_ID.  Workgroups that leave
-// early record nothing.
+// A chunk in LDS (2), its partial rows stored and the B chunk staged (3), the
+// members' first-block partials polled in (4, the rendezvous), the first
+// token block's u summed (5) and its y stores acknowledged (6); then (7) ti |
+// g << 16 | slice << 24, (8) the HW_ID register, (9) XCC_ID.  Workgroups that
+// leave early record nothing.
 constexpr int kPhaseWords = 10;
 static unsigned long long *g_phase_clock = nullptr;
 static size_t g_phase_words = 0;
@@ -1282,7 +1282,7 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
                              bool *used) {
   *used = false;
   if (meta.T == 0 || part_bytes >= ((size_t)1 << 32) || ldy >= ((int64_t)1 << 30)) return hipSuccess;
-  if (max_tiles(meta.T, meta.S) > kSyncTiles) return hipSuccess;  // tiles past the rendezvous region
+  if (max_tiles(meta.T, meta.S) > kSyncTiles) return hipSuccess;  // tiles past the count words
   SplitParams p{};
   p.x = x;
   p.ldx = ldx;

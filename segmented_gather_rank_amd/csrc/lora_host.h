@@ -70,7 +70,7 @@ constexpr int kSplitRanges = 4;
 constexpr int kSplitFlagWords = kSplitMembers * kSplitRanges;  // per tile
 constexpr int kSyncTiles = 1152;
 constexpr size_t kSyncBytes = sizeof(uint32_t) * kSplitFlagWords * (kSyncTiles + 1);
-static_assert(kSyncBytes % 256 == 0, "the rank buffer after the rendezvous words stays 256-byte aligned");
+static_assert(kSyncBytes % 256 == 0, "the rank buffer after the count words stays 256-byte aligned");
 static_assert(kSyncBytes == LORA_APPLY_SYNC_BYTES, "the C header states the region's size");
 
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
@@ -137,7 +137,7 @@ hipError_t launch_bgmv(const MetaView &meta, const void *x, int64_t ldx, int64_t
 bool fused_disabled();
 
 // The fused kernel with each work tile split over several workgroups (bf16,
-// decode-shaped calls).  sync: the rendezvous words (kSyncBytes, above);
+// decode-shaped calls).  sync: the count words (kSyncBytes, above);
 // part: workspace of split_ws_bytes bytes for the partial rank rows.  *used is
 // false when the call is not one it takes.
 size_t split_ws_bytes(int64_t T, int32_t S, int32_t n_slices, int32_t R);

@@ -40,7 +40,7 @@ def test_workspace_sizes():
     import torch
     b_apply = L.lora_apply_workspace_bytes(4096, 128, 14336, 1, 64, torch.bfloat16)
     assert b_apply >= L.APPLY_SYNC_BYTES + 4 * 4096 * 64
-    # every apply workspace starts with the rendezvous words, whatever the call
+    # every apply workspace starts with the count words, whatever the call
     assert L.lora_apply_workspace_bytes(1, 1, 8, 1, 8, torch.float32) >= L.APPLY_SYNC_BYTES
     b2 = L.lora_shrink_workspace_bytes(256, 32, 4096, 1, 16, torch.bfloat16)
     assert b2 > 0 and b2 % 256 == 0

@@ -105,7 +105,7 @@ def test_integer_inputs_bit_exact(L, mode, shape):
 
 def test_workspace_reuse_two_shapes(L):
     """One apply workspace serves calls of different sizes in a row: garbage
-    everywhere except the rendezvous words, which lora_apply_workspace_init
+    everywhere except the count words, which lora_apply_workspace_init
     clears once."""
     from test_gpu_2_apply import small_case
     big = W.config(5)

@@ -42,7 +42,7 @@ def live_tiles(meta):
 
 
 def tile_flags(L, d, meta):
-    """The rendezvous words of the apply workspace d.ws, [tile][range][member],
+    """The count words of the apply workspace d.ws, [tile][range][member],
     as uint32: the call count in bits 31:4, the XCD that raised the word last
     in bits 3:0."""
     n = L.max_tiles(meta.num_tokens, meta.num_slots)
@@ -158,7 +158,7 @@ def test_split_calls_share_one_meta(L):
 def test_split_two_streams_one_meta(L):
     """Two decode-shaped applies of different shapes on one lora_meta, at the
     same time on two streams, each call with its own workspace: the metadata is
-    only read and the rendezvous words live in each call's workspace, so both
+    only read and the count words live in each call's workspace, so both
     give the oracle's rows, and each stream's repeats are equal bit for bit.
     (With two kernels sharing the CUs, a wait may give up: that case computes
     the same bits, so it is not asserted away.)"""
