@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--slot-ranks", action="store_true",
                     help="pass each slot's own rank (the kernels then skip the zero-padded ranks)")
+    ap.add_argument("--a-rank-rows", action="store_true",
+                    help="hand A over rank-major ([S][r][d_in], the pages' A layout), so that with --slot-ranks "
+                         "the ranks past a slot's own are whole rows that are never fetched")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the rotated input copies (beats the 256 MB MALL)")
     ap.add_argument("--flush-mb", type=float, default=1024.0,
@@ -553,8 +556,9 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
 
     alg = algorithmic(c, args.slot_ranks)
     if moe is None:
+        A_host = [np.transpose(a, (0, 2, 1)) for a in c.A] if args.a_rank_rows else c.A
         base = dict(ts=torch.from_numpy(c.token_slot).to(dev), x=to_dev(c.x),
-                    A=[to_dev(a) for a in c.A], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
+                    A=[to_dev(a) for a in A_host], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
     else:
         SE = c.num_slots
         base = dict(ts=torch.from_numpy(moe.token_slot).to(dev), x=to_dev(moe.x),
@@ -591,7 +595,7 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     def apply_call(i):
         s = sets[i % nrot]
         L.lora_apply(metas[i % nrot], s["x"], s["A"], s["B"], c.offsets, s["y"], scale=c.scale,
-                     add=True, mode=args.mode, workspace=s["aws"], slot_rank=ranks)
+                     add=True, mode=args.mode, workspace=s["aws"], slot_rank=ranks, a_rank_rows=args.a_rank_rows)
 
     def step(i):
         meta_call(i)
@@ -663,10 +667,10 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     d_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
     d_flops = alg["shrink_flops"] + alg["expand_flops"]
     achieved = d_bytes / (apply_us * 1e-6) / 1e9
-    mf = None if args.slot_ranks else read_mfma(c, key)
+    mf = None if args.slot_ranks or args.a_rank_rows else read_mfma(c, key)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if args.slot_ranks else read_traffic(c, key),
+                "traffic": None if args.slot_ranks or args.a_rank_rows else read_traffic(c, key),
                 "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + key + ")",
                 "kernel_avg_us": round(apply_us, 3), "algorithmic_bytes_per_launch": int(d_bytes),
                 "mfma_bf16": {"algorithmic_tflops": round(d_flops / (apply_us * 1e-6) / 1e12, 2),
@@ -684,7 +688,7 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
               "distinct_slots" if moe is None else "distinct_keys": alg["U"],
               "slots": c.num_slots, "d_in": c.d_in,
               "slice_widths": c.widths, "r_max": r, "mode": args.mode,
-              "slot_ranks": bool(args.slot_ranks),
+              "slot_ranks": bool(args.slot_ranks), "a_rank_rows": bool(args.a_rank_rows),
               "rotated_input_sets": nrot, "flush_mb_before_timed_replay": args.flush_mb,
               "parallelism": "single GPU"}
     return {
@@ -847,7 +851,8 @@ def main():
         ts = torch.from_numpy(src.token_slot).to(dev)
         x, y = to_dev(src.x), to_dev(src.y0)
         SE = c.num_slots
-        A = [to_dev(a).view(SE, *a.shape[2:]) if moe is not None else to_dev(a) for a in src.A]
+        A = [to_dev(a).view(SE, *a.shape[2:]) if moe is not None else
+             to_dev(np.transpose(a, (0, 2, 1)) if args.a_rank_rows else a) for a in src.A]
         B = [to_dev(b).view(SE, *b.shape[2:]) if moe is not None else to_dev(b) for b in src.B]
         ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).to(dev) if args.slot_ranks else None
         ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, c.r_max,
@@ -862,7 +867,7 @@ def main():
                                             torch.from_numpy(moe.expert_map).to(dev))
                 m = m.with_x_row_div(1) if moe.x_per_pair else m
             L.lora_apply(m, x, A, B, c.offsets, y, scale=c.scale, add=True, mode=args.mode, workspace=ws,
-                         slot_rank=ranks)
+                         slot_rank=ranks, a_rank_rows=args.a_rank_rows)
         torch.cuda.synchronize()
         print(f"pmc pass done: {K} steps of {c.name}", flush=True)
         return

@@ -75,12 +75,29 @@ typedef enum lora_mode {
     LORA_MODE_RANGE_MAX_ = 2147483647
 } lora_mode;
 
+/* Layout of a slice's per-slot factor matrices (lora_weight.layout). */
+typedef enum lora_layout {
+    /* A_s [d_in][r_max] (row stride r_max), B_s [r_max][width_s] (row stride
+     * width_s): the layout of page "多 LoRA 服务：分段矩阵乘与适配器调度",
+     * section "不合并权重，批量计算". */
+    LORA_LAYOUT_DEFAULT = 0,
+    /* A only: A_s [r_max][d_in] (row stride d_in), the rank-major layout of
+     * page "vLLM 源码完全拆解(十八):多 LoRA 服务", section "包装层的形态".  A
+     * slot's ranks are then whole rows, so with per-slot ranks (d_slot_rank)
+     * the ranks past a slot's own are never fetched.  bf16 only, r_max >= 16,
+     * mode AUTO or SGMV; every slice of A must use it (else
+     * LORA_ERR_UNSUPPORTED / LORA_ERR_INVALID_ARG).  B keeps the default
+     * layout, whose ranks are already whole rows. */
+    LORA_LAYOUT_RANK_ROWS = 1
+} lora_layout;
+
 /* One packed slice of a stacked factor: slot a's matrix starts at
- * ptr + a * slot_stride elements.  A_s matrices are [d_in][r_max] (row-major,
- * row stride r_max); B_s matrices are [r_max][width_s] (row stride width_s). */
+ * ptr + a * slot_stride elements, laid out as `layout` says. */
 typedef struct lora_weight {
     const void *ptr;
     int64_t slot_stride;            /* elements between consecutive slots */
+    int32_t layout;                 /* a lora_layout value */
+    int32_t reserved;               /* must be 0 */
 } lora_weight;
 
 /* Bytes at the start of every lora_apply workspace that hold the per-tile call

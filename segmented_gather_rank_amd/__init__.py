@@ -41,7 +41,10 @@ class LoraError(RuntimeError):
 
 
 class lora_weight(C.Structure):
-    _fields_ = [("ptr", C.c_void_p), ("slot_stride", C.c_int64)]
+    _fields_ = [("ptr", C.c_void_p), ("slot_stride", C.c_int64), ("layout", C.c_int32), ("reserved", C.c_int32)]
+
+
+LORA_LAYOUT_DEFAULT, LORA_LAYOUT_RANK_ROWS = 0, 1
 
 
 class lora_meta(C.Structure):
@@ -100,7 +103,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 8:
+if _lib.lora_abi_version() != 9:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -137,7 +140,7 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
-def _weights(ws, name: str, inner_shape_ok) -> tuple:
+def _weights(ws, name: str, inner_shape_ok, layout: int = 0) -> tuple:
     """Per-slice stacked factors [S][rows][cols] -> lora_weight array.  The
     matrices must be contiguous; the slot stride is taken from the tensor."""
     if isinstance(ws, torch.Tensor):
@@ -149,7 +152,15 @@ def _weights(ws, name: str, inner_shape_ok) -> tuple:
         inner_shape_ok(i, w)
         arr[i].ptr = _dev(w, f"{name}[{i}]")
         arr[i].slot_stride = w.stride(0)
+        arr[i].layout = layout
     return arr, list(ws)
+
+
+def _a_weights(A, a_rank_rows: bool):
+    """A as [S][d_in][r] (default) or, with a_rank_rows, [S][r][d_in] (the
+    rank-major layout); returns the descriptors, the tensors and r."""
+    A_arr, A_list = _weights(A, "A", lambda i, w: None, LORA_LAYOUT_RANK_ROWS if a_rank_rows else LORA_LAYOUT_DEFAULT)
+    return A_arr, A_list, A_list[0].shape[1] if a_rank_rows else A_list[0].shape[2]
 
 
 TILE_ROWS = 64          # sorted positions per work tile of the metadata
@@ -329,12 +340,12 @@ def _ranks(slot_rank):
 def lora_shrink(meta: LoraMeta, x: torch.Tensor, A, u: torch.Tensor, scale: float = 1.0,
                 slot_scale: torch.Tensor | None = None, mode: str = "auto",
                 workspace: torch.Tensor | None = None, stream=None,
-                slot_rank: torch.Tensor | None = None) -> torch.Tensor:
-    """u[s][t][:] = scale * slot_scale[slot] * x[t] @ A[s][slot]; A: list of [S][d_in][r].
-    slot_rank: optional int32 [S], ranks each slot's adapter really has."""
+                slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False) -> torch.Tensor:
+    """u[s][t][:] = scale * slot_scale[slot] * x[t] @ A[s][slot]; A: list of [S][d_in][r]
+    (or [S][r][d_in] with a_rank_rows).  slot_rank: optional int32 [S], ranks
+    each slot's adapter really has."""
     xp, ldx, d_in = _x_args(x)
-    A_arr, A_list = _weights(A, "A", lambda i, w: None)
-    r = A_list[0].shape[2]
+    A_arr, A_list, r = _a_weights(A, a_rank_rows)
     n = len(A_list)
     need = lora_shrink_workspace_bytes(meta.num_tokens, meta.num_slots, d_in, n, r, x.dtype, mode)
     if workspace is None:
@@ -371,13 +382,13 @@ def lora_expand(meta: LoraMeta, u: torch.Tensor, B, offsets, y: torch.Tensor, ad
 def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
                slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto",
                workspace: torch.Tensor | None = None, stream=None,
-               slot_rank: torch.Tensor | None = None) -> torch.Tensor:
-    """Shrink then expand into the slices of y (the whole delta of one layer)."""
+               slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False) -> torch.Tensor:
+    """Shrink then expand into the slices of y (the whole delta of one layer).
+    A: list of [S][d_in][r], or [S][r][d_in] with a_rank_rows; B: list of [S][r][w_s]."""
     xp, ldx, d_in = _x_args(x)
-    A_arr, A_list = _weights(A, "A", lambda i, w: None)
+    A_arr, A_list, r = _a_weights(A, a_rank_rows)
     B_arr, B_list = _weights(B, "B", lambda i, w: None)
     width, offs = _slices(B_list, offsets)
-    r = A_list[0].shape[2]
     n = len(A_list)
     if len(B_list) != n:
         raise ValueError("A and B need one entry per slice")
@@ -401,12 +412,12 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # LORA_NOALLOC_SCRATCH_BYTES of the C header
 
 def lora_apply_noalloc(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
                        slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto", stream=None,
-                       slot_rank: torch.Tensor | None = None) -> torch.Tensor:
+                       slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False) -> torch.Tensor:
     """lora_apply with the library's own device scratch as its workspace (no
     workspace argument, nothing allocated).  Calls that overlap on one device
     share that scratch and race."""
     xp, ldx, d_in = _x_args(x)
-    A_arr, A_list = _weights(A, "A", lambda i, w: None)
+    A_arr, A_list, r = _a_weights(A, a_rank_rows)
     B_arr, B_list = _weights(B, "B", lambda i, w: None)
     width, offs = _slices(B_list, offsets)
     if len(B_list) != len(A_list):
@@ -417,7 +428,7 @@ def lora_apply_noalloc(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.
         raise TypeError("x and y must share one dtype")
     ss = None if slot_scale is None else _dev(slot_scale, "slot_scale")
     st = _lib.lora_apply_noalloc(C.byref(meta.c), xp, ldx, d_in, _dtype(x), len(A_list), A_arr, B_arr, width,
-                                 offs, A_list[0].shape[2], float(scale), ss, _ranks(slot_rank), _dev(y, "y"),
+                                 offs, r, float(scale), ss, _ranks(slot_rank), _dev(y, "y"),
                                  y.stride(0), int(bool(add)), MODES[mode], _stream(stream))
     _check("lora_apply_noalloc", st)
     return y
@@ -427,4 +438,5 @@ __all__ = ["lora_apply_noalloc", "NOALLOC_SCRATCH_BYTES", "lora_abi_version", "l
            "lora_moe_meta_workspace_bytes", "lora_prepare_moe_meta",
            "lora_shrink_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_workspace_bytes",
            "lora_apply_workspace_init", "apply_workspace", "apply_workspace_counters", "apply_workspace_flags",
-           "lora_apply", "LoraMeta", "LoraError", "lora_weight", "lora_meta", "LIB_PATH"]
+           "lora_apply", "LoraMeta", "LoraError", "lora_weight", "lora_meta", "LIB_PATH", "LORA_LAYOUT_DEFAULT",
+           "LORA_LAYOUT_RANK_ROWS"]

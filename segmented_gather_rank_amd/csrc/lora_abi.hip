@@ -88,7 +88,7 @@ hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t stream) {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 8;
+constexpr int32_t kAbiVersion = 9;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -163,9 +163,13 @@ lora_status check_shrink_args(const lora_meta *meta, const void *x, int64_t ldx,
   if (slot_scale && (reinterpret_cast<uintptr_t>(slot_scale) & 3u)) return LORA_ERR_INVALID_ARG;
   for (int s = 0; s < n_slices; ++s) {
     if (!A[s].ptr || !aligned16(A[s].ptr) || A[s].slot_stride % 8 ||
-        A[s].slot_stride < d_in * r_max)
+        A[s].slot_stride < d_in * r_max || A[s].reserved != 0 || A[s].layout != A[0].layout)
       return LORA_ERR_INVALID_ARG;
   }
+  if (A[0].layout != LORA_LAYOUT_DEFAULT && A[0].layout != LORA_LAYOUT_RANK_ROWS) return LORA_ERR_UNSUPPORTED;
+  // rank-major A is read by the matrix-core shrink only
+  if (A[0].layout == LORA_LAYOUT_RANK_ROWS && (dtype != LORA_BF16 || tile_rank(r_max) < 16 || mode == LORA_MODE_BGMV))
+    return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
@@ -186,8 +190,10 @@ lora_status check_expand_args(const lora_meta *meta, const float *u, int32_t n_s
     const int64_t w = width[s], o = offset[s];
     if (w < 8 || w % 8 || o < 0 || o % 8 || o + w > ldy) return LORA_ERR_INVALID_ARG;
     if ((int64_t)(r_max + 1) * w >= kMaxFactorElems) return LORA_ERR_UNSUPPORTED;  // 32-bit offsets
-    if (!B[s].ptr || !aligned16(B[s].ptr) || B[s].slot_stride % 8 || B[s].slot_stride < r_max * w)
+    if (!B[s].ptr || !aligned16(B[s].ptr) || B[s].slot_stride % 8 || B[s].slot_stride < r_max * w ||
+        B[s].reserved != 0)
       return LORA_ERR_INVALID_ARG;
+    if (B[s].layout != LORA_LAYOUT_DEFAULT) return LORA_ERR_UNSUPPORTED;
     for (int q = 0; q < s; ++q) {
       if (o < offset[q] + width[q] && offset[q] < o + w) return LORA_ERR_INVALID_ARG;
     }
@@ -231,7 +237,8 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   // first (bf16; it checks its own limits), then the per-token kernel when
   // its limits hold; both take r_max of 8, 16, 32 or 64 only
   const bool decode = (int)mode != 2 && ((int)mode == 1 || meta->num_tokens <= 16 * (int64_t)meta->num_slots);
-  const bool fused_rank = r_max == R && R <= 64;
+  const bool a_rows = A[0].layout == LORA_LAYOUT_RANK_ROWS;  // rank-major A: the tile shrink reads it
+  const bool fused_rank = r_max == R && R <= 64 && !a_rows;
   if (fused_rank && !fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
     bool used = false;
     const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
@@ -252,7 +259,7 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   const bool rows = expand_rows_fits(meta->num_tokens, meta->num_slots, dtype == LORA_BF16, (int)mode, R) &&
                     expand_rows_addressable(meta->num_tokens, n_slices, width, offset, ldy, R);
   hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, R, r_max,
-                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s, rows);
+                               scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s, rows, a_rows);
   if (e != hipSuccess) return LORA_ERR_HIP;
   if (rows) {  // long segments: the sums become bf16 planes in the rank buffer, then the row-stream expand
     e = launch_expand_rows(mv, static_cast<const float *>(sh_ws), kch, reinterpret_cast<uint16_t *>(u), n_slices,
@@ -409,7 +416,7 @@ lora_status lora_shrink(const lora_meta *meta, const void *d_x, int64_t ldx, int
   const hipError_t e =
       launch_shrink(view_of(meta), d_x, ldx, d_in, dtype == LORA_BF16, n_slices, ptrs, strides,
                     tile_rank(r_max), r_max, scale, d_slot_scale, d_slot_rank, d_u, (int)mode, d_ws, false, nullptr,
-                    static_cast<hipStream_t>(stream));
+                    static_cast<hipStream_t>(stream), false, A[0].layout == LORA_LAYOUT_RANK_ROWS);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

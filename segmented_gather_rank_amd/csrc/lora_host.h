@@ -88,7 +88,9 @@ hipError_t launch_meta_moe(const int32_t *topk_ids, int64_t T, int32_t topk, con
 // caller's u.  for_apply: u is written in sorted-position order with row
 // stride R, and with a split d_in the
 // partial sums are left in ws for the expand to add (kch_out reports the
-// split); to_partials: the sums go to ws even without a split (kch = 1)
+// split); to_partials: the sums go to ws even without a split (kch = 1);
+// a_rank_rows: A_s[slot] is [ra][d_in] (the matrix-core path only: bf16,
+// R >= 16, mode AUTO or SGMV)
 // The rank the kernels are built for: the smallest of 8, 16, 32, 64, 128 that
 // holds r_max (0 when r_max is not a multiple of 8 in [8, 128]).
 inline int32_t tile_rank(int32_t r_max) {
@@ -102,7 +104,7 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
                          int32_t R, int32_t ra, float scale, const float *slot_scale, const int32_t *slot_rank,
                          float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream,
-                         bool to_partials = false);
+                         bool to_partials = false, bool a_rank_rows = false);
 // R, ra: as for the shrink (B holds ra rank rows per slot).  u_mode 0: u
 // [n_slices][T][ra] in token order (the caller's); 1: [n_slices][T][R] in
 // sorted-position order; 2: kch partial sums [kch][n_slices][T][R] in

@@ -59,6 +59,7 @@ struct ShrinkParams {
   int32_t kc, kch;       // k-chunk length (a multiple of 128) and count
   int32_t ra;            // the caller's r_max: A row stride, ranks read (ra <= R)
   int32_t u_ld;          // row stride of u written in token order (the caller's u: ra)
+  int32_t a_rank_rows;   // A_s[slot] is [ra][d_in] (rank-major), not [d_in][ra]
 };
 
 struct ShrinkLds {
@@ -217,8 +218,17 @@ constexpr int kMKT = 128;    // k rows per A tile
 template <int CB> constexpr int kMLda = CB == 1 ? 16 : CB * 16 + 16;
 // A tiles per batch at most (register and LDS budget)
 template <int CB> constexpr int kMNtb = CB == 1 ? 4 : (CB == 2 ? 2 : 1);
+// A rank-major A tile sits in LDS as CB * 16 rank rows of 128 k values, row
+// stride kMLdk: 16 lanes reading 16 bytes of 16 consecutive rank rows fall in
+// distinct banks (272 bytes apart)
+constexpr int kMLdk = kMKT + 8;
+template <int CB, bool RM> constexpr int kMTile = RM ? CB * 16 * kMLdk : kMKT * kMLda<CB>;
 
-template <int R, int CB, int NS>
+// RM: A is rank-major, [ra][d_in] per slot (the pages' A layout): a slot's
+// ranks past its own are whole rows, never fetched.  The tile then goes to LDS
+// as rank rows, and the MFMA reads 8 consecutive k of one rank with a plain
+// 16-byte read instead of the transposing one.
+template <int R, int CB, int NS, bool RM>
 __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t *__restrict__ info,
                                                                   const int32_t *__restrict__ tiles,
                                                                   ShrinkParams p) {
@@ -226,8 +236,9 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
   constexpr int QS = R / 16;        // octets of one slice per thread per tile
   constexpr int LDA = kMLda<CB>;
   constexpr int NTB = kMNtb<CB>;
+  constexpr int TILE = kMTile<CB, RM>;
   static_assert(SG >= 1 && SG * QS == CB, "column blocks hold whole slices");
-  __shared__ uint16_t at[2][NTB * kMKT * LDA];
+  __shared__ uint16_t at[2][NTB * TILE];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int mrow = lane % 16, kg = lane / 16;
   // live tiles: the tile list is in key order, so the tiles of tokens without
@@ -296,7 +307,8 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
       }
       // A octet q = t * CB + sl * QS + qq of this thread: tile t of the
       // batch, slice sl, flat element 8 (tid + 256 qq) of that slice's
-      // [128][R] block; rows past the k-chunk and slices past n_slices read
+      // [128][R] block (rank-major: of its [R][128] block); rows past the
+      // k-chunk, ranks past the slot's rank and slices past n_slices read
       // zeros, tiles past the chunk are not loaded
       u32x4 aq[NTB * CB];
       auto load_a = [&](int bi) {
@@ -308,9 +320,15 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
 #pragma unroll
             for (int q = 0; q < CB; ++q) {
               const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
-              const int k = e / R, j0 = e % R;
-              const bool ok = sl < ns && k0 + k < kend && j0 < rk;
-              aq[t * CB + q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * p.ra + j0) * 2) : 0x7FFFFFF0u);
+              if constexpr (RM) {
+                const int j = e / kMKT, k = e % kMKT;
+                const bool ok = sl < ns && k0 + k < kend && j < rk;
+                aq[t * CB + q] = buf_load16(ar[sl], ok ? (uint32_t)(((int64_t)j * p.d_in + k0 + k) * 2) : 0x7FFFFFF0u);
+              } else {
+                const int k = e / R, j0 = e % R;
+                const bool ok = sl < ns && k0 + k < kend && j0 < rk;
+                aq[t * CB + q] = buf_load16(ar[sl], ok ? (uint32_t)(((k0 + k) * p.ra + j0) * 2) : 0x7FFFFFF0u);
+              }
             }
           }
         }
@@ -322,7 +340,11 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
 #pragma unroll
             for (int q = 0; q < CB; ++q) {
               const int sl = q / QS, e = 8 * (tid + kMThreads * (q % QS));
-              *reinterpret_cast<u32x4 *>(&at[buf][(t * kMKT + e / R) * LDA + sl * R + e % R]) = aq[t * CB + q];
+              if constexpr (RM)
+                *reinterpret_cast<u32x4 *>(&at[buf][t * TILE + (sl * R + e / kMKT) * kMLdk + e % kMKT]) =
+                    aq[t * CB + q];
+              else
+                *reinterpret_cast<u32x4 *>(&at[buf][(t * kMKT + e / R) * LDA + sl * R + e % R]) = aq[t * CB + q];
             }
           }
         }
@@ -369,7 +391,12 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
             const bf16x8 xa = __builtin_bit_cast(bf16x8, xc[m]);
 #pragma unroll
             for (int b = 0; b < CB; ++b) {
-              const bf16x8 bv = lds_col8(a_b + t * kMKT * LDA, LDA, 32 * i + 8 * kg, 16 * b);
+              bf16x8 bv;
+              if constexpr (RM)
+                bv = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(a_b + t * TILE + (16 * b + mrow) * kMLdk + 32 * i + 8 * kg));
+              else
+                bv = lds_col8(a_b + t * TILE, LDA, 32 * i + 8 * kg, 16 * b);
               acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv, acc[b], 0, 0, 0);
             }
           }
@@ -488,20 +515,24 @@ static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <int R, int CB, int NS>
+template <int R, int CB, int NS, bool RM>
 static hipError_t launch_mma_ns(const ShrinkParams &p, int64_t bound, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];
   const int grid = xcd_grid(bound, resident_groups(resident,
-                                                   reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB, NS>),
+                                                   reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB, NS, RM>),
                                                    kMThreads, 0));
-  hipLaunchKernelGGL((shrink_mma_kernel<R, CB, NS>), dim3(grid), dim3(kMThreads), 0, stream, p.meta.info,
+  hipLaunchKernelGGL((shrink_mma_kernel<R, CB, NS, RM>), dim3(grid), dim3(kMThreads), 0, stream, p.meta.info,
                      p.meta.tiles, p);
   return hipGetLastError();
 }
 
 template <int R, int CB>
 static hipError_t launch_mma_t(const ShrinkParams &p, int64_t bound, hipStream_t stream) {
-  return with_slice_bound(p.n_slices, [&](auto ns) { return launch_mma_ns<R, CB, decltype(ns)::value>(p, bound, stream); });
+  return with_slice_bound(p.n_slices, [&](auto ns) {
+    constexpr int NS = decltype(ns)::value;
+    return p.a_rank_rows ? launch_mma_ns<R, CB, NS, true>(p, bound, stream)
+                         : launch_mma_ns<R, CB, NS, false>(p, bound, stream);
+  });
 }
 
 // column blocks per pass: the smallest power of two covering every slice's
@@ -516,8 +547,9 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
                          int32_t n_slices, const void *const *A, const int64_t *a_stride,
                          int32_t R, int32_t ra, float scale, const float *slot_scale, const int32_t *slot_rank,
                          float *u, int mode, void *ws, bool for_apply, int *kch_out, hipStream_t stream,
-                         bool to_partials) {
+                         bool to_partials, bool a_rank_rows) {
   const ShrinkConfig c = plan_shrink(meta.T, meta.S, d_in, R, bf16, mode);
+  if (a_rank_rows && !c.use_mma_mode) return hipErrorInvalidValue;  // the caller checks the layout's limits
   if (kch_out) *kch_out = c.kch;
   ShrinkParams p{};
   p.meta = meta;
@@ -538,6 +570,7 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
   p.kch = c.kch;
   p.ra = ra;
   p.u_ld = ra;
+  p.a_rank_rows = a_rank_rows ? 1 : 0;
   if (meta.T == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
   if (c.use_mma_mode) {

@@ -108,6 +108,8 @@ static void library_checks(void) {
   /* argument checks of the compute calls (all return before a launch) */
   lora_meta m = fake_meta(64, 4);
   lora_weight A[9], B[9];
+  memset(A, 0, sizeof A);
+  memset(B, 0, sizeof B);
   for (int s = 0; s < 9; ++s) {
     A[s].ptr = fake(0);
     A[s].slot_stride = 64 * 16;
@@ -131,6 +133,28 @@ static void library_checks(void) {
                     LORA_MODE_AUTO, NULL) == LORA_ERR_UNSUPPORTED);
   CHECK(lora_apply(&m, fake(0), 64, 64, LORA_BF16, 1, A, B, width, offset, 16, 1.f, NULL, NULL, fake(0), 96, 1,
                    (lora_mode)9, fake(0), 1 << 22, NULL) == LORA_ERR_UNSUPPORTED);
+  /* rank-major A: bf16, r_max >= 16, AUTO or SGMV, every slice alike; B default only */
+  A[0].layout = LORA_LAYOUT_RANK_ROWS;
+  CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_F32, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
+                    fake(0), 1 << 15, NULL) == LORA_ERR_UNSUPPORTED);
+  CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_BF16, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_BGMV,
+                    fake(0), 1 << 15, NULL) == LORA_ERR_UNSUPPORTED);
+  CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_BF16, 1, A, 8, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
+                    fake(0), 1 << 15, NULL) == LORA_ERR_UNSUPPORTED);
+  CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_BF16, 2, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
+                    fake(0), 1 << 15, NULL) == LORA_ERR_INVALID_ARG);  /* slices differ */
+  A[0].layout = 7;
+  CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_BF16, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
+                    fake(0), 1 << 15, NULL) == LORA_ERR_UNSUPPORTED);
+  A[0].layout = LORA_LAYOUT_DEFAULT;
+  A[0].reserved = 1;
+  CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_BF16, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
+                    fake(0), 1 << 15, NULL) == LORA_ERR_INVALID_ARG);
+  A[0].reserved = 0;
+  B[1].layout = LORA_LAYOUT_RANK_ROWS;
+  CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 96, LORA_BF16, 1,
+                    LORA_MODE_AUTO, NULL) == LORA_ERR_UNSUPPORTED);
+  B[1].layout = LORA_LAYOUT_DEFAULT;
   CHECK(lora_shrink(&m, fake(2), 64, 64, LORA_BF16, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
                     fake(0), 1 << 15, NULL) == LORA_ERR_INVALID_ARG);
   CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 90, LORA_BF16, 1,

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 8
+    assert L.lora_abi_version() == 9
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -161,6 +161,25 @@ def _expand(n=2, widths=(64, 32), offsets=(0, 64), r=16, ldy=96, B=None, y=None,
     B = B if B is not None else (L.lora_weight * n)(*[L.lora_weight(_base, r * w) for w in widths[:n]])
     return _call("lora_expand", C.byref(_meta()), _ptr(), n, B, wd, of, r, None,
                  y if y is not None else _ptr(), ldy, 1, 1, mode, None)
+
+
+def test_layout_rejections():
+    """Rank-major A ([r][d_in]) is read by the matrix-core shrink only: bf16,
+    r_max >= 16, mode AUTO or SGMV, every slice alike; B has one layout."""
+    def A_rows(n=1, layouts=(1,), stride=64 * 16):
+        arr = (L.lora_weight * n)()
+        for i in range(n):
+            arr[i].ptr, arr[i].slot_stride, arr[i].layout = _base, stride, layouts[min(i, len(layouts) - 1)]
+        return arr
+    assert _shrink(A=A_rows(), dtype=0) == L.LORA_ERR_UNSUPPORTED          # fp32
+    assert _shrink(A=A_rows(), mode=1) == L.LORA_ERR_UNSUPPORTED           # BGMV
+    assert _shrink(A=A_rows(stride=64 * 8), r=8) == L.LORA_ERR_UNSUPPORTED  # r_max 8
+    assert _shrink(A=A_rows(2, (1, 0)), n=2) == L.LORA_ERR_INVALID_ARG     # slices differ
+    assert _shrink(A=A_rows(layouts=(7,))) == L.LORA_ERR_UNSUPPORTED
+    Bl = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64), L.lora_weight(_base, 16 * 32, 1))
+    assert _expand(B=Bl) == L.LORA_ERR_UNSUPPORTED
+    Bz = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64, 0, 5), L.lora_weight(_base, 16 * 32))
+    assert _expand(B=Bz) == L.LORA_ERR_INVALID_ARG                          # reserved != 0
 
 
 def test_expand_rejections():

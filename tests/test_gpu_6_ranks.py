@@ -181,3 +181,88 @@ def test_any_r_max_integer_bit_exact(L, r, mode):
     d = DevCase(c)
     y, _ = d.apply(L, mode=mode, add=True)
     assert np.array_equal(as_f64(from_dev(y)), ref)
+
+
+# A in the rank-major layout ([S][r_max][d_in], the pages' A layout): a slot's
+# ranks are whole rows, so with per-slot ranks the rows past a slot's rank
+# (rounded up to 8) are never fetched; the tests put NaN there.
+
+def rank_rows(A, dtype):
+    """Device copies of A [S][d_in][r] as [S][r][d_in]."""
+    return [to_dev(np.ascontiguousarray(np.transpose(a, (0, 2, 1))), dtype) for a in A]
+
+
+@pytest.mark.parametrize("r", [16, 24, 64, 128])
+@pytest.mark.parametrize("mode", ["auto", "sgmv"])
+def test_rank_rows_apply(L, r, mode):
+    c = small_case(900 + r, "bf16", r)
+    print(f"[rank-rows] {c.name} mode={mode}", flush=True)
+    d = RankedDev(c)
+    A_nan, _ = nan_padded(c)
+    Arm = rank_rows(A_nan, c.dtype)
+    for add in (True, False):
+        meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+        y = d.y0.clone()
+        L.lora_apply(meta, d.x, Arm, d.B, c.offsets, y, scale=c.scale, slot_scale=d.slot_scale, add=add, mode=mode,
+                     slot_rank=d.ranks, a_rank_rows=True)
+        check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T), add=add), f"{c.name} rank rows add={add}")
+    # without per-slot ranks every rank row is read: the zero padding, no NaN
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    y = d.y0.clone()
+    L.lora_apply(meta, d.x, rank_rows(c.A, c.dtype), d.B, c.offsets, y, scale=c.scale, slot_scale=d.slot_scale,
+                 mode=mode, a_rank_rows=True)
+    check_rows(c, from_dev(y), oracle_rows(c, np.arange(c.T)), f"{c.name} rank rows, r_max read")
+
+
+def test_rank_rows_shrink_alone_and_bgmv_refused(L):
+    c = small_case(960, "bf16", 32)
+    d = RankedDev(c)
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    u = torch.full((c.n_slices, c.T, c.r_max), float("nan"), dtype=torch.float32, device="cuda")
+    A_nan, _ = nan_padded(c)
+    L.lora_shrink(meta, d.x, rank_rows(A_nan, c.dtype), u, scale=c.scale, slot_scale=d.slot_scale, mode="auto",
+                  slot_rank=d.ranks, a_rank_rows=True)
+    torch.cuda.synchronize()
+    _, uref = oracle_rows(c, np.arange(c.T), return_u=True)
+    got = u.cpu().numpy()
+    has = c.token_slot >= 0
+    for s in range(c.n_slices):
+        g, ref = got[s][has].astype(np.float64), uref[has, s, :]
+        assert np.all(np.abs(g - ref) <= 2e-2 * (1 + np.abs(ref))), s
+    with pytest.raises(L.LoraError):
+        L.lora_apply(meta, d.x, rank_rows(c.A, c.dtype), d.B, c.offsets, d.y0.clone(), scale=c.scale, mode="bgmv",
+                     a_rank_rows=True)
+
+
+@pytest.mark.parametrize("r", [32, 64])
+def test_rank_rows_integer_bit_exact(L, r):
+    c = integer_case(70 + r, [1] * 96 + [700, 300, 129, 64], 6, 2048, [1024, 512], r, 2.0)
+    ref = oracle_rows(c, np.arange(c.T))
+    assert np.all(ref == np.round(ref)) and np.max(np.abs(ref)) <= 256
+    d = DevCase(c)
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    for mode in ("auto", "sgmv"):
+        y = d.y0.clone()
+        L.lora_apply(meta, d.x, rank_rows(c.A, c.dtype), d.B, c.offsets, y, scale=c.scale, mode=mode,
+                     a_rank_rows=True)
+        assert np.array_equal(as_f64(from_dev(y)), ref), mode
+
+
+@pytest.mark.parametrize("k", [4, 5])
+def test_rank_rows_workloads(L, k):
+    """The mixed-rank workloads at full size with rank-major A and per-slot
+    ranks (NaN past every slot's rank rows), sampled rows."""
+    c = W.config(k)
+    print(f"[rank-rows] workload {c.name}", flush=True)
+    d = RankedDev(c)
+    A_nan, _ = nan_padded(c)
+    Arm = rank_rows(A_nan, c.dtype)
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    y = d.y0.clone()
+    L.lora_apply(meta, d.x, Arm, d.B, c.offsets, y, scale=c.scale, slot_scale=d.slot_scale, slot_rank=d.ranks,
+                 a_rank_rows=True)
+    rng = np.random.Generator(np.random.PCG64(k))
+    rows = np.sort(rng.choice(c.T, 96, replace=False))
+    check_rows(c, from_dev(y)[rows], oracle_rows(c, rows), c.name)
+    del Arm, y, d
+    torch.cuda.empty_cache()
