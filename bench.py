@@ -201,15 +201,21 @@ def kernel_keys(kernel_key):
     return kernel_key.split("+")
 
 
-def traffic_file(c):
-    return os.path.join(PROFILES, f"traffic_{c.name}.md")
+def variant(args):
+    """(file-name suffix, command-line flags) of the weight options of a run."""
+    flags = [f for f, on in (("--slot-ranks", args.slot_ranks), ("--a-rank-rows", args.a_rank_rows)) if on]
+    return "".join("_" + f[2:].replace("-", "_") for f in flags), "".join(" " + f for f in flags)
 
 
-def read_traffic(c, kernel_key):
+def traffic_file(c, args):
+    return os.path.join(PROFILES, f"traffic_{c.name}{variant(args)[0]}.md")
+
+
+def read_traffic(c, kernel_key, args):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel sources."""
     try:
-        text = open(traffic_file(c)).read()
+        text = open(traffic_file(c, args)).read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith("- ") and ": " in line)
@@ -218,7 +224,7 @@ def read_traffic(c, kernel_key):
     return int(fields["- traffic bytes per launch"])
 
 
-def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
+def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key, args):
     """FETCH_SIZE / WRITE_SIZE per dispatch (KiB) of the dominant kernel, scaled
     by what the same counters read for the calibration copy."""
     import csv
@@ -248,19 +254,20 @@ def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
     f_r = nbytes / (out["FETCH_SIZE"][1] * 1024)
     f_w = nbytes / (out["WRITE_SIZE"][1] * 1024)
     traffic = out["FETCH_SIZE"][0] * 1024 * f_r + out["WRITE_SIZE"][0] * 1024 * f_w
-    alg = algorithmic(c)
+    alg = algorithmic(c, args.slot_ranks)
     alg_b = alg["shrink_bytes"] + alg["expand_bytes"]
+    sfx, fl = variant(args)
     lines = [
-        f"# HBM traffic of `{kernel_key}` on workload {c.name}",
+        f"# HBM traffic of `{kernel_key}` on workload {c.name}{fl}",
         "",
         "Two rocprofv3 counter runs of `bench.py --pmc-pass` (a bf16 negation of "
         f"{PMC_COPY_ELEMS} elements as the plain copy of known size, then the workload's steps):",
         "",
         "```",
         "export TMPDIR=/tmp",
-        f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200",
-        f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200",
-        f"python bench.py --config {k} --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200{fl}",
+        f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200{fl}",
+        f"python bench.py --config {k} --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write{fl}",
         "```",
         "",
         f"| Counter | `{kernel_key}` KiB/dispatch | copy KiB/dispatch | copy bytes | scale |",
@@ -269,14 +276,17 @@ def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key):
         f"| WRITE_SIZE | {out['WRITE_SIZE'][0]:.1f} (n={out['WRITE_SIZE'][2]}) | {out['WRITE_SIZE'][1]:.1f} | {nbytes} | {f_w:.4f} |",
         "",
         f"Scaled traffic {traffic / 1e6:.3f} MB per launch against {alg_b / 1e6:.3f} MB algorithmic "
-        f"({traffic / alg_b:.3f}x).",
+        f"({traffic / alg_b:.3f}x)" + ("" if not args.slot_ranks else
+                                       f"; the same workload without per-slot ranks moves "
+                                       f"{sum(algorithmic(c)[q] for q in ('shrink_bytes', 'expand_bytes')) / 1e6:.3f} MB "
+                                       f"algorithmic") + ".",
         "",
         f"- kernel sources: {source_digest(kernel_key)}",
         f"- traffic bytes per launch: {int(round(traffic))}",
         "",
     ]
     os.makedirs(PROFILES, exist_ok=True)
-    open(traffic_file(c), "w").write("\n".join(lines))
+    open(traffic_file(c, args), "w").write("\n".join(lines))
     print("\n".join(lines))
 
 
@@ -392,7 +402,7 @@ def read_mfma(c, kernel_key):
     return int(fields["- mfma flops per launch"])
 
 
-def summarize_trace(c, k, d, bench_json, kernel_key):
+def summarize_trace(c, k, d, bench_json, kernel_key, args):
     """rocprofv3 --kernel-trace --stats summary of a bench run (the stats csv)
     next to the bench's own figures for the dominant call."""
     import csv
@@ -401,11 +411,12 @@ def summarize_trace(c, k, d, bench_json, kernel_key):
     assert f, f"no kernel_stats.csv under {d}"
     rows = list(csv.DictReader(open(f[0])))
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
-    lines = [f"# Kernel trace: {c.name}", "", "Command (repository root, one MI355X):", "", "```",
+    sfx, fl = variant(args)
+    lines = [f"# Kernel trace: {c.name}{fl}", "", "Command (repository root, one MI355X):", "", "```",
              "export TMPDIR=/tmp",
              f"rocprofv3 --kernel-trace --stats -d gpurun_out/trace{k} -o t --output-format csv -- "
-             f"python bench.py --config {k} --extra '' --no-cpu-baseline > gpurun_out/trace{k}.json",
-             f"python bench.py --config {k} --summarize-trace gpurun_out/trace{k} gpurun_out/trace{k}.json",
+             f"python bench.py --config {k} --extra '' --no-cpu-baseline{fl} > gpurun_out/trace{k}.json",
+             f"python bench.py --config {k} --summarize-trace gpurun_out/trace{k} gpurun_out/trace{k}.json{fl}",
              "```", "",
              "Kernel statistics (durations in ns; the graphs replay the timed steps twice each, plus eager warm-up "
              "steps and the flush copies):", "",
@@ -418,7 +429,7 @@ def summarize_trace(c, k, d, bench_json, kernel_key):
                      f"{float(r['Percentage']):.2f} % |")
         if any(key in name for key in kernel_keys(kernel_key)):
             apply_ns += avg
-    alg = algorithmic(c)
+    alg = algorithmic(c, args.slot_ranks)
     ab = alg["shrink_bytes"] + alg["expand_bytes"]
     bus = b["roofline"]["kernel_avg_us"]
     lines += ["",
@@ -431,7 +442,7 @@ def summarize_trace(c, k, d, bench_json, kernel_key):
               "the tracer adds its own time between graph nodes, which the events count and the per-kernel "
               "durations do not).", ""]
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, f"trace_{c.name}.md")
+    out = os.path.join(PROFILES, f"trace_{c.name}{sfx}.md")
     open(out, "w").write("\n".join(lines))
     print("\n".join(lines))
 
@@ -670,7 +681,7 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     mf = None if args.slot_ranks or args.a_rank_rows else read_mfma(c, key)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if args.slot_ranks or args.a_rank_rows else read_traffic(c, key),
+                "traffic": read_traffic(c, key, args),
                 "traffic_unit": "bytes per launch", "kernel": "lora_apply (" + key + ")",
                 "kernel_avg_us": round(apply_us, 3), "algorithmic_bytes_per_launch": int(d_bytes),
                 "mfma_bf16": {"algorithmic_tflops": round(d_flops / (apply_us * 1e-6) / 1e12, 2),
@@ -813,13 +824,13 @@ def main():
 
     c, moe = load_case(args.config)
     if args.summarize_pmc:
-        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode))
+        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode), args=args)
         return
     if args.summarize_mfma:
         summarize_mfma(c, args.config, args.summarize_mfma, dominant_kernel(c, args.mode))
         return
     if args.summarize_trace:
-        summarize_trace(c, args.config, *args.summarize_trace, dominant_kernel(c, args.mode))
+        summarize_trace(c, args.config, *args.summarize_trace, dominant_kernel(c, args.mode), args)
         return
     if args.phase_budget:
         phase_budget(c, args, args.phase_budget)
