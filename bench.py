@@ -768,6 +768,7 @@ def phase_budget(c, args, out_md):
     mws = torch.empty(L.lora_meta_workspace_bytes(c.T, c.num_slots), dtype=torch.uint8, device=dev)
     flush = Flush(torch, dev, args.flush_mb)
     rows, spans_ev = [], []
+    xcc_total = xcc_match = 0
     for it in range(args.warmup + args.steps):
         flush()
         clk.zero_()
@@ -780,6 +781,11 @@ def phase_budget(c, args, out_md):
         if it < args.warmup:
             continue
         r = clk.cpu().numpy().reshape(-1, words)
+        # the record's index is the workgroup's flat index (blockIdx.y * gridDim.x + blockIdx.x);
+        # every slice's row of the grid is a multiple of 8 wide, so blockIdx.x mod 8 = index mod 8
+        live_idx = np.nonzero(r[:, 0] != 0)[0]
+        xcc_total += live_idx.shape[0]
+        xcc_match += int(np.sum(r[live_idx, 9] == live_idx % 8))
         r = r[r[:, 0] != 0]
         if r.shape[0] == 0:
             raise SystemExit("the split kernel did not run (no phase records): not a split-kernel workload")
@@ -808,7 +814,10 @@ def phase_budget(c, args, out_md):
     lines += ["", f"First start to last end, median over steps: {np.median(ends):.2f} us "
               f"(p90 {np.percentile(ends, 90):.2f}). HIP events around the lora_apply launch of the same steps: "
               f"median {np.median(spans_ev):.2f} us (these add the launch and the gap before the first "
-              f"workgroup starts)."]
+              f"workgroup starts).", "",
+              f"XCD placement: the hardware register XCC_ID equals blockIdx mod 8 in {xcc_match} of {xcc_total} "
+              f"workgroup records (the split kernel assumes it for a tile's members, and computes a peer's "
+              f"partials itself when a peer's tags name another XCD)."]
     os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
