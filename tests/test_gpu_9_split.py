@@ -50,23 +50,32 @@ def tile_flags(L, d, meta):
 
 
 def check_counters(L, ws):
-    """No wait gave up and no member met a peer on another XCD."""
-    assert L.apply_workspace_counters(ws) == {"gave_up": 0, "other_xcd": 0}
+    """No wait gave up.  A member that met a peer on another XCD is counted
+    and printed, not failed: which XCD runs a workgroup is the dispatcher's
+    choice (round robin over blockIdx as a rule, with rare exceptions seen),
+    and such a member computes the peer's partials itself, so the results
+    checked before this stay exact."""
+    cnt = L.apply_workspace_counters(ws)
+    if cnt["other_xcd"]:
+        print(f"[counters] {cnt}", flush=True)
+    assert cnt["gave_up"] == 0, cnt
+    return cnt
 
 
 def check_flags(L, d, meta, calls, ranges=1):
     """Every word of the first `ranges` slice ranges of a live tile counts
-    `calls` calls and names one XCD (all members of a tile ran on one); the
-    other words were never touched; no wait gave up."""
+    `calls` calls and, unless a member met a peer on another XCD, names one
+    XCD (all members of a tile ran on one); the other words were never
+    touched; no wait gave up."""
     f = tile_flags(L, d, meta)
     live, n = live_tiles(meta)
     cnt, tag = f >> 4, f & 15
     assert (cnt[live, :ranges] == calls).all(), cnt[live]
-    assert (tag[live, :ranges] == tag[live, :ranges, :1]).all(), tag[live]
     assert (f[live, ranges:] == 0).all()
     dead = np.setdiff1d(np.arange(f.shape[0]), live)
     assert (f[dead] == 0).all()
-    check_counters(L, d.ws)
+    if check_counters(L, d.ws)["other_xcd"] == 0:
+        assert (tag[live, :ranges] == tag[live, :ranges, :1]).all(), tag[live]
 
 
 @pytest.mark.parametrize("r", [8, 16, 32, 64])
@@ -186,7 +195,7 @@ def test_split_two_streams_one_meta(L):
             assert np.array_equal(got[i].view(np.uint16), got[0].view(np.uint16)), f"stream {k} rep {i}"
         check_rows(c, got[0], oracle_rows(c, np.arange(c.T)), f"stream {k}")
         print(f"[split-2streams] stream {k}: {L.apply_workspace_counters(ws[k])}", flush=True)
-        assert L.apply_workspace_counters(ws[k])["other_xcd"] == 0
+        check_counters(L, ws[k])
 
 
 def test_split_large_tiles(L):
