@@ -552,6 +552,9 @@ __global__ __launch_bounds__(kExpThreads) void expand_kernel(ExpandParams p) {
 
 constexpr int kRowsCols = 512;             // columns per item, 128 per wave
 constexpr int kRowsLdb = kRowsCols + 16;   // LDS row stride of the B chunk
+constexpr int kXchLdb = kRowsCols + 8;     // ... of a token block's results: 16 B lanes of 16 rows hit
+                                           // distinct banks
+static_assert(2 * 16 * kXchLdb <= 32 * kRowsLdb, "two result blocks fit the B chunk's buffer");
 
 // u plane: ub[i] = the sum over k-chunks, in order, of the partial sums at i,
 // rounded once to bf16 (nearest even), as the MFMA operand takes it.  Rows of
@@ -633,6 +636,7 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
     const int col0 = (ck - cbase) * kRowsCols;
     const int64_t yo = pick<NS>(p.offset, s, p.n_slices) + col0 + 128 * wave;  // this wave's first column
     const int wcol = col0 + 128 * wave;                                      // ... in the slice
+    const int64_t yrow = pick<NS>(p.offset, s, p.n_slices) + col0;          // the workgroup's first column
     const uint16_t *bslice = reinterpret_cast<const uint16_t *>(pick<NS>(p.B, s, p.n_slices));
     const int64_t bstride = pick<NS>(p.b_stride, s, p.n_slices);
 
@@ -670,14 +674,28 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
       for (int pp = 0; pp < 4; ++pp) yv[b][pp] = buf_load16(yr, yo32 + 64 * pp);
     };
 
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
     bf16x8 bt[KS][8];
     int cur = -2;      // slot whose chunk is in bt
     Header hd = read_header(ta);
     Header hn = hd;
     if (ta + 1 < tz) hn = read_header(ta + 1);
+    // block 0 of every tile with an adapter is in flight in set 0 when the
+    // tile starts: the previous tile (or this line, for the range's first)
+    // issued it, so a workgroup's stream of blocks has no gap at tile
+    // boundaries.  A header with rows = 0 issues only reads past the
+    // resources.
+    {
+      Header h0 = hd;
+      if (uniform_value(hd.slot) < 0) h0.rows = 0;
+      load_block(h0, 0, S0{});
+    }
     for (int ti = ta; ti < tz; ++ti) {
       const int slot = uniform_value(hd.slot), rows = uniform_value(hd.rows);
       const int nb = (rows + 15) / 16;
+      Header hx = hn;  // the next tile's header, for its block 0
+      if (ti + 1 >= tz || uniform_value(hn.slot) < 0) hx.rows = 0;
       if (slot < 0) {  // store mode, no adapter: the windows become 0
         for (int tb = 0; tb < nb; ++tb) {
 #pragma unroll
@@ -687,8 +705,8 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
               gstore16(y + (int64_t)tok_of(hd, tb) * p.ldy + yo + c, u32x4{0, 0, 0, 0});
           }
         }
+        load_block(hx, 0, S0{});
       } else {
-        load_block(hd, 0, std::integral_constant<int, 0>{});
         if (slot != cur) {
           // ---- the slot's chunk of B (rows j < RP, 512 columns) into LDS
           // straight from memory, one row per wave instruction (lane l's 16
@@ -729,6 +747,7 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
             }
           }
           cur = slot;
+          __syncthreads();  // every wave holds its operands before results reuse the buffer
         }
         // ---- token blocks, two per trip (register sets 0 and 1 named at
         // compile time; a runtime trip count keeps the compiler from hoisting
@@ -736,8 +755,7 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
         // block's rank rows and y are in flight meanwhile
         auto compute = [&](int tb, auto bc) __attribute__((always_inline)) {
           constexpr int b = decltype(bc)::value;
-          const bool rv = 16 * tb + n < rows;
-          const uint32_t yst = row_off(rv ? (int64_t)tok_of(hd, tb) : (int64_t)hd.tfirst);
+          uint16_t *xb = rows_lds + (tb & 1) * 16 * kXchLdb;  // results of blocks of this parity
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
             f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -747,26 +765,38 @@ __global__ __launch_bounds__(kXThreads, R >= 64 ? 2 : 3) void expand_rows_kernel
               a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp], u8, a0, 0, 0, 0);
               a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[c][2 * pp + 1], u8, a1, 0, 0, 0);
             }
-            // stores of lanes past the rows or the slice go past the resource
-            // and are dropped (no store behind a branch either)
-            const int c = 32 * pp + 8 * kg;
             const u32x4 old = yv[b][pp];
             u32x4 o;
             o[0] = pack_bf16x2(bf16_lo(old[0]) + a0[0], bf16_hi(old[0]) + a0[1]);
             o[1] = pack_bf16x2(bf16_lo(old[1]) + a0[2], bf16_hi(old[1]) + a0[3]);
             o[2] = pack_bf16x2(bf16_lo(old[2]) + a1[0], bf16_hi(old[2]) + a1[1]);
             o[3] = pack_bf16x2(bf16_lo(old[3]) + a1[2], bf16_hi(old[3]) + a1[3]);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), yr,
-                                                   rv && wcol + c < w ? yst + 64 * pp : kOut, 0, 0);
+            *reinterpret_cast<u32x4 *>(xb + n * kXchLdb + 128 * wave + 32 * pp + 8 * kg) = o;
+          }
+          // the block's 16 x 512 results meet in LDS, and each wave stores 4
+          // whole rows of 1 KB, one row per instruction: y goes out in long
+          // contiguous runs.  Rows past the tile and columns past the slice go
+          // past the resource and are dropped (no store behind a branch).
+          __syncthreads();
+          const int tkb = tok_of(hd, tb);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r = 4 * wave + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(xb + r * kXchLdb + 8 * lane);
+            const int64_t tok = __builtin_amdgcn_readlane(tkb, r);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, yr, 16 * tb + r < rows && col0 + 8 * lane < w ? (uint32_t)((tok * p.ldy + yrow + 8 * lane) * 2) : kOut,
+                0, 0);
           }
         };
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
+        // an odd block count runs one more block of zeros (reads and stores
+        // past the resources), so every tile ends in set 1 and the next
+        // tile's block 0 goes to set 0
         for (int tb = 0; tb < nb; tb += 2) {
           load_block(hd, tb + 1, S1{});
           compute(tb, S0{});
-          if (tb + 1 >= nb) break;
-          load_block(hd, tb + 2, S0{});
+          const bool last = tb + 2 >= nb;
+          load_block(last ? hx : hd, last ? 0 : tb + 2, S0{});
           compute(tb + 1, S1{});
         }
       }
