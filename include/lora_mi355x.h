@@ -133,6 +133,9 @@ typedef struct lora_weight {
  *                   unspecified).  Tiles follow the order of `sorted`; there
  *                   are num_tiles <= ceil(T / 64) + S + 1 of them.  The compute
  *                   kernels take their work from this list.
+ * Past the tiles the workspace holds per-key counts that lora_prepare_meta
+ * uses while it builds the arrays (large batches are counted in parts, by
+ * several workgroups); they are not part of the result.
  * The struct stays valid until its workspace is reused; rebuild it whenever
  * token_slot changes.  Pass it by pointer to the compute calls.  They only
  * read it, so any number of calls, on any streams, may use one lora_meta at

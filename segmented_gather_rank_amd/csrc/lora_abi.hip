@@ -57,6 +57,15 @@ int expand_rows_knob() {
   }();
   return v;
 }
+// LORA_META_MULTI=0 or 1: build the metadata on one workgroup, or on several,
+// whatever the batch size (tuning); unset: chosen by size.
+int meta_multi_knob() {
+  static const int v = [] {
+    const char *e = std::getenv("LORA_META_MULTI");
+    return e && *e ? (std::atoi(e) > 0 ? 1 : 0) : -1;
+  }();
+  return v;
+}
 // LORA_SPLIT_MEMBERS=n (1, 2, 4, 8 or 16): workgroups per tile of the split
 // kernel, instead of the count chosen from the batch (tuning).
 int split_members() {
@@ -117,7 +126,8 @@ MetaLayout meta_layout(int64_t T, int32_t S) {
   L.info = off;
   off += align256(sizeof(int32_t) * 8);
   L.tiles = off;
-  off += align256(sizeof(int32_t) * kTileInts * (size_t)max_tiles(T, S));
+  off += meta_tiles_bytes(T, S);
+  off += meta_counts_bytes(T, S);  // the several-workgroup path's counts
   L.total = off;
   return L;
 }

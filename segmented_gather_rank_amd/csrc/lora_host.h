@@ -73,6 +73,24 @@ constexpr size_t kSyncBytes = sizeof(uint32_t) * kSplitFlagWords * (kSyncTiles +
 static_assert(kSyncBytes % 256 == 0, "the rank buffer after the count words stays 256-byte aligned");
 static_assert(kSyncBytes == LORA_APPLY_SYNC_BYTES, "the C header states the region's size");
 
+// The metadata workspace past the tile list holds the counts of the
+// several-workgroup metadata path: per part of the rows, its count of each key
+// and its bad ids.
+constexpr int kMetaPartRows = 1024;  // rows per part, up to kMetaMaxParts parts
+constexpr int kMetaMaxParts = 64;
+inline int meta_parts(int64_t T) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kMetaMaxParts, (T + kMetaPartRows - 1) / kMetaPartRows));
+}
+inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+inline size_t meta_tiles_bytes(int64_t T, int32_t S) {
+  return round256(sizeof(int32_t) * kTileInts * (size_t)max_tiles(T, S));
+}
+inline size_t meta_counts_bytes(int64_t T, int32_t S) {
+  const size_t K = (size_t)S + 1;
+  return round256(sizeof(int32_t) * (size_t)meta_parts(T) * (K + 1));
+}
+int meta_multi_knob();
+
 hipError_t launch_meta(const int32_t *token_slot, int64_t T, int32_t S, int32_t *sorted,
                        int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start,
                        int32_t *info, int32_t *tiles, hipStream_t stream);

@@ -43,6 +43,7 @@ constexpr int kMetaBatch = 8;                           // keys per thread per b
 constexpr int kMetaBatchRows = kMetaBatch * kMetaThreads;
 constexpr int kMetaMapLds = 4096;                       // expert maps up to this size go to LDS
 constexpr size_t kMetaLdsMax = 159 * 1024;              // dynamic LDS of the workgroup, at most
+constexpr int64_t kMetaMultiMin = 8192;                 // rows from which several workgroups build the metadata
 
 // Where the keys come from: a slot id per row, or (MoE) the pair's slot and
 // expert, with key = slot * E_local + local expert (-1: no adapter or a remote
@@ -84,6 +85,91 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
     }
   }
   return valid ? same : 0;
+}
+
+// Steps 4 and 5 of the metadata, for all 1024 threads of a workgroup (it holds
+// barriers): over the keys in ascending order (thread k, K <= 1024), start
+// offsets, first tiles and segment indices are prefix sums of the counts
+// cnt[k] (LDS), tile counts and presence; kstart and tbase (LDS) get the first
+// two.  Then, with `store`, the segment arrays, their padding past the last
+// segment, the closing offset and the counters are stored (no barrier follows
+// these stores: a barrier after global stores would wait for them).
+__device__ __forceinline__ void key_tables(int K, int64_t T, const int32_t *cnt, int32_t *kstart, int32_t *tbase,
+                                           int32_t (*wsum)[3], int nbad, int32_t *seg_slot, int32_t *seg_count,
+                                           int32_t *seg_start, int32_t *info, bool store = true) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int k = tid;
+  int c = 0, start = 0, nseg = 0, ntiles = 0, seg = 0;
+  if (K <= kWave) {  // every key in wave 0: no exchange between waves
+    if (wave == 0) {
+      c = k < K ? cnt[k] : 0;
+      const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
+      const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
+      nseg = __builtin_amdgcn_readlane(ip, kWave - 1);
+      ntiles = __builtin_amdgcn_readlane(it, kWave - 1);
+      start = ic - c;
+      seg = ip - pr;
+      if (k < K) {
+        kstart[k] = start;
+        tbase[k] = it - nt;
+      }
+    }
+  } else {
+    c = k < K ? cnt[k] : 0;
+    const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
+    const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
+    if (lane == kWave - 1) {
+      wsum[wave][0] = ic;
+      wsum[wave][1] = it;
+      wsum[wave][2] = ip;
+    }
+    __syncthreads();
+    // only the waves that hold keys need the others' sums, and only theirs
+    const int nkw = (K + kWave - 1) / kWave;
+    if (wave < nkw) {
+      int bc = 0, bt = 0, bp = 0;
+      for (int w = 0; w < nkw; ++w) {
+        const int a = wsum[w][0], b2 = wsum[w][1], d = wsum[w][2];
+        if (w < wave) {
+          bc += a;
+          bt += b2;
+          bp += d;
+        }
+        nseg += d;
+        ntiles += b2;
+      }
+      start = bc + ic - c;
+      seg = bp + ip - pr;
+      if (k < K) {
+        kstart[k] = start;
+        tbase[k] = bt + it - nt;
+      }
+    }
+  }
+  __syncthreads();
+  if (!store) return;
+
+  if (c > 0) {
+    seg_slot[seg] = k - 1;
+    seg_count[seg] = c;
+    seg_start[seg] = start;
+  }
+  if (k >= nseg && k < K) {
+    seg_slot[k] = -1;
+    seg_count[k] = 0;
+    seg_start[k] = (int32_t)T;
+  }
+  if (tid == 0) {
+    seg_start[K] = (int32_t)T;
+    info[0] = nseg;
+    info[1] = (T - c == 0) ? 1 : 0;  // thread 0 holds key 0: the rows without an adapter
+    info[2] = nbad;
+    info[3] = c;
+    info[4] = ntiles;
+    info[5] = info[6] = info[7] = 0;
+  }
 }
 
 // KIND 0 (kSmall): at most 1024 rows; thread tid holds row tid in registers
@@ -245,81 +331,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   }
   __syncthreads();
 
-  // 4. over the keys in ascending order (thread k, K <= 1024): start offsets,
-  //    first tiles and segment indices are prefix sums of the counts, tile
-  //    counts and presence.  The segment arrays are written after the barrier
-  //    below: a barrier after global stores would wait for them.
-  const int k = tid;
-  int c = 0, start = 0, nseg = 0, ntiles = 0, seg = 0;
-  if (K <= kWave) {  // every key in wave 0: no exchange between waves
-    if (wave == 0) {
-      c = k < K ? cnt[k] : 0;
-      const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
-      const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
-      nseg = __builtin_amdgcn_readlane(ip, kWave - 1);
-      ntiles = __builtin_amdgcn_readlane(it, kWave - 1);
-      start = ic - c;
-      seg = ip - pr;
-      if (k < K) {
-        kstart[k] = start;
-        tbase[k] = it - nt;
-      }
-    }
-  } else {
-    c = k < K ? cnt[k] : 0;
-    const int nt = (c + kTileRows - 1) / kTileRows, pr = c > 0 ? 1 : 0;
-    const int ic = wave_inclusive_scan(c), it = wave_inclusive_scan(nt), ip = wave_inclusive_scan(pr);
-    if (lane == kWave - 1) {
-      wsum[wave][0] = ic;
-      wsum[wave][1] = it;
-      wsum[wave][2] = ip;
-    }
-    __syncthreads();
-    // only the waves that hold keys need the others' sums, and only theirs
-    const int nkw = (K + kWave - 1) / kWave;
-    if (wave < nkw) {
-      int bc = 0, bt = 0, bp = 0;
-      for (int w = 0; w < nkw; ++w) {
-        const int a = wsum[w][0], b2 = wsum[w][1], d = wsum[w][2];
-        if (w < wave) {
-          bc += a;
-          bt += b2;
-          bp += d;
-        }
-        nseg += d;
-        ntiles += b2;
-      }
-      start = bc + ic - c;
-      seg = bp + ip - pr;
-      if (k < K) {
-        kstart[k] = start;
-        tbase[k] = bt + it - nt;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 5. the segment arrays (thread k), their padding past the last segment, the
-  //    closing offset and the counters; no barrier follows these stores
-  if (c > 0) {
-    seg_slot[seg] = k - 1;
-    seg_count[seg] = c;
-    seg_start[seg] = start;
-  }
-  if (k >= nseg && k < K) {
-    seg_slot[k] = -1;
-    seg_count[k] = 0;
-    seg_start[k] = (int32_t)T;
-  }
-  if (tid == 0) {
-    seg_start[K] = (int32_t)T;
-    info[0] = nseg;
-    info[1] = (T - c == 0) ? 1 : 0;  // thread 0 holds key 0: the rows without an adapter
-    info[2] = nbad;
-    info[3] = c;
-    info[4] = ntiles;
-    info[5] = info[6] = info[7] = 0;
-  }
+  // 4-5. the key tables, segment arrays and counters
+  key_tables(K, T, cnt, kstart, tbase, wsum, nbad, seg_slot, seg_count, seg_start, info);
 
   // 6. stable scatter: every wave walks its run again, 64 rows at a time; a
   //    row goes to its key's start + the counts of earlier waves and earlier
@@ -364,6 +377,181 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(
   }
 }
 
+// ---------------------------------------------------------------- several workgroups
+//
+// Past several thousand rows one workgroup is bound by its own CU.  Then the
+// rows are cut into P contiguous parts and two short kernels share the work:
+// every part's workgroup counts its keys; then every part's workgroup reads
+// all parts' counts, takes its own first position inside every key and the
+// key tables from them (part 0 stores the segment arrays and counters), and
+// scatters its rows.
+// A part's rows of a key follow those of the parts before it, and inside a
+// part the rows keep batch order (by wave and lane, as in the one-workgroup
+// kernel): the sort stays stable, and its result is the same.
+
+template <bool MOE>
+__device__ __forceinline__ int meta_row_key(const MetaSrc &src, int64_t t, int32_t S, int &bad) {
+  const int v = MOE ? moe_key<MOE>(src, nullptr, src.topk_ids[t], src.token_slot[(uint32_t)t / (uint32_t)src.topk])
+                    : src.token_slot[t];
+  const bool ok = v >= -1 && v < S;
+  bad += ok ? 0 : 1;
+  return ok ? v + 1 : 0;
+}
+
+// Part p's rows [p q, min(T, (p + 1) q)), q = ceil(T / P).
+__device__ __forceinline__ void meta_part(int64_t T, int64_t &lo, int64_t &hi) {
+  const int64_t q = (T + gridDim.x - 1) / gridDim.x;
+  lo = (int64_t)blockIdx.x * q;
+  hi = min(T, lo + q);
+}
+
+// 1. counts of part p: counts[p][k] (k < K), counts[p][K] = its bad ids
+template <bool MOE>
+__global__ __launch_bounds__(kMetaThreads) void meta_count_kernel(MetaSrc src, int64_t T, int32_t S,
+                                                                  int32_t *__restrict__ counts) {
+  extern __shared__ __align__(16) int32_t lds[];  // [K] this part's count per key
+  __shared__ int32_t nbad;
+  const int K = S + 1, tid = threadIdx.x;
+  for (int i = tid; i < K; i += kMetaThreads) lds[i] = 0;
+  if (tid == 0) nbad = 0;
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  __syncthreads();
+  int64_t lo, hi;
+  meta_part(T, lo, hi);
+  int mybad = 0;
+  for (int64_t b = lo; b < hi; b += kMetaThreads) {
+    const int64_t t = b + tid;
+    const bool valid = t < hi;
+    const int key = valid ? meta_row_key<MOE>(src, t, S, mybad) : 0;
+    const uint64_t same = match_key(key, valid, nbits);
+    if (valid && __popcll(same & lanemask_lt()) == 0) atomicAdd(&lds[key], __popcll(same));
+  }
+  if (mybad) atomicAdd(&nbad, mybad);
+  __syncthreads();
+  int32_t *out = counts + (int64_t)blockIdx.x * (K + 1);
+  for (int i = tid; i < K; i += kMetaThreads) out[i] = lds[i];
+  if (tid == 0) out[K] = nbad;
+}
+
+// 2. part p: per key (and for the bad ids), the count of the parts before p
+// (its first position inside the key) and of all parts; the key tables from
+// those (part 0 also stores the segment arrays and counters).  Then the
+// scatter, 1024 rows at a time: per step, every wave counts its rows of each
+// key (lanes with the same key find each other by ballots), the 16 waves'
+// counts per key are prefix-summed in wave order on top of the part's running
+// position in the key, and every row goes to its key's start + that position
+// + its rank among the wave's equal keys; rows also land in their work tiles,
+// the row that opens a tile writing the tile's header
+template <bool MOE>
+__global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(MetaSrc src, int64_t T, int32_t S,
+                                                                    const int32_t *__restrict__ counts,
+                                                                    int32_t *__restrict__ sorted,
+                                                                    int32_t *__restrict__ sorted_slot,
+                                                                    int32_t *__restrict__ seg_slot,
+                                                                    int32_t *__restrict__ seg_count,
+                                                                    int32_t *__restrict__ seg_start,
+                                                                    int32_t *__restrict__ info,
+                                                                    int32_t *__restrict__ tiles) {
+  // [K] counts, [K] first positions, [K] first tiles, [K] this part's next
+  // position inside each key, [16][K] per-wave counts of a step, then offsets
+  extern __shared__ __align__(16) int32_t lds[];
+  __shared__ int32_t nbad;
+  __shared__ int32_t wsum[kMetaWaves][3];
+  const int K = S + 1, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int part = (int)blockIdx.x, nparts = (int)gridDim.x;
+  int32_t *cnt = lds, *kstart = lds + K, *tbase = lds + 2 * K, *run = lds + 3 * K, *woff = lds + 4 * K;
+  for (int k = tid; k <= K; k += kMetaThreads) {
+    int before = 0, all = 0;
+    for (int p0 = 0; p0 < nparts; p0 += 8) {  // 8 loads in flight
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = p0 + j < nparts ? counts[(int64_t)(p0 + j) * (K + 1) + k] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        before += p0 + j < part ? c[j] : 0;
+        all += c[j];
+      }
+    }
+    if (k < K) {
+      cnt[k] = all;
+      run[k] = before;
+    } else {
+      nbad = all;
+    }
+  }
+  for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) woff[i] = 0;
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  __syncthreads();
+  key_tables(K, T, cnt, kstart, tbase, wsum, nbad, seg_slot, seg_count, seg_start, info, part == 0);
+  int64_t lo, hi;
+  meta_part(T, lo, hi);
+  for (int64_t b = lo; b < hi; b += kMetaThreads) {
+    const int64_t t = b + tid;
+    const bool valid = t < hi;
+    int unused = 0;
+    const int key = valid ? meta_row_key<MOE>(src, t, S, unused) : 0;
+    const uint64_t same = match_key(key, valid, nbits);
+    const int rank = __popcll(same & lanemask_lt());
+    if (valid && rank == 0) woff[wave * K + key] = __popcll(same);
+    __syncthreads();
+    // per key, the 16 waves' counts sit in one 16-lane row (thread = 16 key +
+    // wave): exclusive offsets on top of the running position, which the
+    // row's last lane then advances (a wave reads before it writes)
+    for (int k0 = 0; k0 < K; k0 += kMetaThreads / kMetaWaves) {
+      const int k = k0 + tid / kMetaWaves, w = tid % kMetaWaves;
+      const int c = k < K ? woff[w * K + k] : 0;
+      const int base = k < K ? run[k] : 0;
+      const int incl = row16_inclusive_scan(c);
+      if (k < K) woff[w * K + k] = base + incl - c;
+      if (k < K && w == kMetaWaves - 1) run[k] = base + incl;
+    }
+    __syncthreads();
+    if (valid) {
+      const int off = woff[wave * K + key] + rank;  // position inside the key's range
+      const int dst = kstart[key] + off;
+      sorted[dst] = (int32_t)t;
+      sorted_slot[dst] = key - 1;
+      int32_t *tl = tiles + (int64_t)(tbase[key] + off / kTileRows) * kTileInts;
+      tl[4 + off % kTileRows] = (int32_t)t;
+      if (off % kTileRows == 0) {
+        tl[0] = key - 1;
+        tl[1] = min(kTileRows, cnt[key] - off);
+        tl[2] = dst;
+        tl[3] = 0;
+      }
+    }
+    __syncthreads();  // every row has its offset before the next step's counts
+    for (int i = tid; i < kMetaWaves * K; i += kMetaThreads) woff[i] = 0;
+    __syncthreads();
+  }
+}
+
+template <bool MOE>
+static hipError_t launch_meta_multi(const MetaSrc &src, int64_t T, int32_t S, int32_t *sorted, int32_t *sorted_slot,
+                                    int32_t *seg_slot, int32_t *seg_count, int32_t *seg_start, int32_t *info,
+                                    int32_t *tiles, hipStream_t stream) {
+  const int K = S + 1;
+  const int parts = meta_parts(T);
+  // the counts sit past the tile list (the workspace layout reserves them)
+  int32_t *counts = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(tiles) + meta_tiles_bytes(T, S));
+  const size_t scatter_lds = sizeof(int32_t) * (size_t)K * (4 + kMetaWaves);
+  if (scatter_lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&meta_scatter_kernel<MOE>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)scatter_lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((meta_count_kernel<MOE>), dim3(parts), dim3(kMetaThreads), sizeof(int32_t) * K, stream, src, T,
+                     S, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((meta_scatter_kernel<MOE>), dim3(parts), dim3(kMetaThreads), scatter_lds, stream, src, T, S,
+                     counts, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles);
+  return hipGetLastError();
+}
+
 // Dynamic LDS of the metadata kernel: the key tables, the expert map when it
 // fits, the keys themselves when they fit too, then the per-wave match tables
 // when those fit as well.
@@ -400,6 +588,12 @@ template <bool MOE>
 static hipError_t launch_meta_t(const MetaSrc &src, int64_t T, int32_t S, int32_t *sorted,
                                 int32_t *sorted_slot, int32_t *seg_slot, int32_t *seg_count,
                                 int32_t *seg_start, int32_t *info, int32_t *tiles, hipStream_t stream) {
+  // several workgroups from a few thousand rows on (LORA_META_MULTI forces
+  // either way)
+  const int knob = meta_multi_knob();
+  if (T > 0 && (knob == 1 || (knob < 0 && T >= kMetaMultiMin)))
+    return launch_meta_multi<MOE>(src, T, S, sorted, sorted_slot, seg_slot, seg_count, seg_start, info, tiles,
+                                  stream);
   bool cached = false, match_lds = false;
   const size_t lds = meta_lds_bytes(S, T, MOE && src.expert_map ? src.E_global : 0, cached, match_lds);
   const int kind = T <= kMetaThreads ? kSmall : (cached ? kCached : kStreamed);

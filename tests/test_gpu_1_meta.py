@@ -1,4 +1,7 @@
-"""GPU slot metadata against the oracle: bit-exact on every array."""
+"""GPU slot metadata against the oracle: bit-exact on every array.  Batches of
+8192 rows and more are counted in parts by several workgroups (up to 64 parts
+of at least 1024 rows, a part taking 1024 rows per step); smaller ones run on
+one workgroup."""
 import numpy as np
 import pytest
 import torch
@@ -59,7 +62,7 @@ def _rng(seed):
 PATTERNS = ["uniform", "all_none", "one_slot", "sorted", "reversed", "zipf", "bad_ids"]
 
 
-@pytest.mark.parametrize("T", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025, 5000, 20000])
+@pytest.mark.parametrize("T", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025, 5000, 8192, 20000])
 @pytest.mark.parametrize("S", [1, 2, 33, 1023])
 @pytest.mark.parametrize("pattern", PATTERNS)
 def test_meta_random(L, T, S, pattern):
@@ -100,3 +103,40 @@ def test_meta_repeatable_and_workspace_reuse(L):
     for i in range(int(a["info"][4])):
         rows = int(ta[i, 1])
         assert np.array_equal(ta[i, :4 + rows], tb[i, :4 + rows]), i
+
+
+@pytest.mark.parametrize("S", [8, 1023])
+@pytest.mark.parametrize("pattern", ["uniform", "zipf", "bad_ids"])
+def test_meta_many_parts(L, S, pattern):
+    """100 000 rows: 64 parts of 1563 rows, each two steps of up to 1024."""
+    T = 100_000
+    rng = _rng(S * 17 + PATTERNS.index(pattern))
+    if pattern == "uniform":
+        ts = rng.integers(-1, S, T)
+    elif pattern == "zipf":
+        ts = W.zipf_slots(rng, T, S, 1.1)
+    else:
+        ts = rng.integers(-3, S + 3, T)
+    _meta_check(L, ts.astype(np.int32), S, f"many parts {pattern}")
+
+
+def test_meta_parts_repeatable_and_workspace_reuse(L):
+    """The several-workgroup path twice into one workspace, another batch in
+    between: identical arrays (its counts are rebuilt on every call)."""
+    rng = _rng(6)
+    ts_np = rng.integers(-1, 64, 9000).astype(np.int32)
+    ts = torch.from_numpy(ts_np).cuda()
+    ws = torch.full((L.lora_meta_workspace_bytes(9000, 64),), 0x5A, dtype=torch.uint8, device="cuda")
+    a = {k: v.clone() for k, v in L.lora_prepare_meta(ts, 64, workspace=ws).tensors().items()}
+    other = torch.from_numpy(rng.integers(-1, 64, 9000).astype(np.int32)).cuda()
+    L.lora_prepare_meta(other, 64, workspace=ws)
+    b = L.lora_prepare_meta(ts, 64, workspace=ws).tensors()
+    torch.cuda.synchronize()
+    for k in a:
+        if k != "tiles":
+            assert torch.equal(a[k], b[k]), k
+    ta, tb = a["tiles"].cpu().numpy(), b["tiles"].cpu().numpy()
+    for i in range(int(a["info"][4])):
+        rows = int(ta[i, 1])
+        assert np.array_equal(ta[i, :4 + rows], tb[i, :4 + rows]), i
+    _meta_check(L, ts_np, 64, "parts, checked against the oracle")

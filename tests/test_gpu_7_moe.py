@@ -117,6 +117,20 @@ def test_moe_meta_bit_exact(L, seed, with_map, bad):
     assert (ref.num_bad > 0) == bad
 
 
+@pytest.mark.parametrize("with_map,bad", [(True, False), (False, True)])
+def test_moe_meta_many_rows(L, with_map, bad):
+    """1100 tokens x top-8: 8800 (token, expert) rows, counted in parts by
+    several workgroups; the apply on them too."""
+    c = small_moe(740 + int(bad), T=1100, K=8, E=64, EL=16 if with_map else 64, with_map=with_map, bad=bad)
+    print(f"[moe-meta] {c.name} rows={c.rows} map={with_map} bad={bad}", flush=True)
+    d = MoeDev(c)
+    ref = check_meta(L, d)
+    assert (ref.num_bad > 0) == bad
+    y, _ = d.apply(L)
+    rows = np.arange(0, c.rows, 7)
+    check(c, from_dev(y)[rows], moe_ref(c, rows=rows), c.name)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("per_pair", [False, True])
 @pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
