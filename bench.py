@@ -84,6 +84,13 @@ PMC_COPY_ELEMS = 64 << 20   # bf16 elements of the calibration copy (128 MiB rea
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def rel(path):
+    """A path as given on the command line, relative to the repository root
+    when it lies inside it (for the commands recorded in profiles/)."""
+    a = os.path.abspath(path)
+    return os.path.relpath(a, ROOT) if a.startswith(ROOT + os.sep) else path
+
+
 KERNEL_SOURCES = {   # the sources each measured kernel is built from
     "bgmv_split": ["lora_bgmv_split.hip"],
     "bgmv_fused_kernel": ["lora_bgmv.hip"],
@@ -265,9 +272,9 @@ def summarize_pmc(c, k, fetch_dir, write_dir, kernel_key, args):
         "",
         "```",
         "export TMPDIR=/tmp",
-        f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200{fl}",
-        f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200{fl}",
-        f"python bench.py --config {k} --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write{fl}",
+        f"rocprofv3 --pmc FETCH_SIZE -d {rel(fetch_dir)} -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200{fl}",
+        f"rocprofv3 --pmc WRITE_SIZE -d {rel(write_dir)} -o p --output-format csv -- python bench.py --config {k} --pmc-pass --steps 200{fl}",
+        f"python bench.py --config {k} --summarize-pmc {rel(fetch_dir)} {rel(write_dir)}{fl}",
         "```",
         "",
         f"| Counter | `{kernel_key}` KiB/dispatch | copy KiB/dispatch | copy bytes | scale |",
@@ -366,9 +373,9 @@ def summarize_mfma(c, k, d, kernel_key):
         "",
         "```",
         "export TMPDIR=/tmp",
-        f"rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil -d gpurun_out/pmc_mfma -o p --output-format csv -- "
+        f"rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil -d {rel(d)} -o p --output-format csv -- "
         f"python bench.py --config {k} --pmc-pass --steps 20",
-        f"python bench.py --config {k} --summarize-mfma gpurun_out/pmc_mfma",
+        f"python bench.py --config {k} --summarize-mfma {rel(d)}",
         "```",
         "",
         "| Kernel | dispatches | bf16 MFMA GFLOP per dispatch (MOPS x 512) | MfmaUtil % |",
@@ -414,9 +421,9 @@ def summarize_trace(c, k, d, bench_json, kernel_key, args):
     sfx, fl = variant(args)
     lines = [f"# Kernel trace: {c.name}{fl}", "", "Command (repository root, one MI355X):", "", "```",
              "export TMPDIR=/tmp",
-             f"rocprofv3 --kernel-trace --stats -d gpurun_out/trace{k} -o t --output-format csv -- "
-             f"python bench.py --config {k} --extra '' --no-cpu-baseline{fl} > gpurun_out/trace{k}.json",
-             f"python bench.py --config {k} --summarize-trace gpurun_out/trace{k} gpurun_out/trace{k}.json{fl}",
+             f"rocprofv3 --kernel-trace --stats -d {rel(d)} -o t --output-format csv -- "
+             f"python bench.py --config {k} --extra '' --no-cpu-baseline{fl} > {rel(bench_json)}",
+             f"python bench.py --config {k} --summarize-trace {rel(d)} {rel(bench_json)}{fl}",
              "```", "",
              "Kernel statistics (durations in ns; the graphs replay the timed steps twice each, plus eager warm-up "
              "steps and the flush copies):", "",

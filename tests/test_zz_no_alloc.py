@@ -1,7 +1,7 @@
 """lora_apply_noalloc, the entry point for callers that cannot allocate: the
 library's own device scratch replaces the workspace.  Through the C ABI, its
 output equals lora_apply's (the same kernels on the same inputs, so bit for
-bit) and the oracle's within the survey's bf16 tolerance, on calls in a row
+bit) and the oracle's within the bf16 tolerance, 2e-2·(1+|ref|), on calls in a row
 whose second input is smaller than the first; a call too large for the
 scratch is refused."""
 import numpy as np
