@@ -287,7 +287,7 @@ lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
  * decode-shaped apply (page "多 LoRA 服务：分段矩阵乘与适配器调度", section
  * "不合并权重，批量计算": the fused form for decode batches) spreads each work
  * tile over several workgroups that exchange partial results tagged with the
- * tile's call count, which these words keep.  Every call leaves them
+ * tile, the slice range and the call count, which these words keep.  Every call leaves them
  * consistent for the next call on the same workspace, whatever its shapes.
  * The words must not be written between calls.
  *   d_ws      device workspace, 16-byte aligned

@@ -318,7 +318,8 @@ def apply_workspace_counters(workspace: torch.Tensor) -> dict:
 
 def apply_workspace_flags(workspace: torch.Tensor, tiles: int) -> torch.Tensor:
     """The count words of the first `tiles` work tiles, [tile][range][member]
-    (int32 view of uint32 words: the call count in bits 31:4, an XCD in 3:0)."""
+    (int32 view of uint32 words: the call count in bits 31:17, the tile in
+    16:6, the range in 5:4, an XCD in 3:0)."""
     w = workspace[:APPLY_SYNC_BYTES].view(torch.int32)
     return w[:tiles * SPLIT_RANGES * SPLIT_MEMBERS].view(tiles, SPLIT_RANGES, SPLIT_MEMBERS)
 

@@ -34,15 +34,21 @@
 // quarter of the members, then the four sums in wave order through LDS), so
 // every member gets the same u, bit for bit.
 //
-// The tag is the call count of the tile in bits 31:4 and the XCD (hardware
-// register XCC_ID) of the storing member in bits 3:0.  The counts live in
-// count words at the start of the caller's apply workspace, so calls with
-// workspaces of their own share nothing: a member reads its word at the start
-// and tags with "count + 1", and raises the word to that tag for the next
-// call (member 0 also raises the words of members >= G), so the words of a
-// tile stay equal between calls.  The B chunk is loaded with the A chunk and
-// x, and so is the y of the first 16 rows except with the longest chunks, so
-// that none of them is outstanding at the polls (loads complete in order).
+// The tag is the call count of the tile's range (bits 31:17, modulo 2^15),
+// the tile (bits 16:6), the range (bits 5:4) and the XCD (hardware register
+// XCC_ID) of the storing member (bits 3:0).  The counts live in count words at
+// the start of the caller's apply workspace, so calls with workspaces of
+// their own share nothing: a member reads its word at the start and tags with
+// "count + 1", and raises the word to that tag for the next call (member 0
+// also raises the words of members >= G), so the words of a range stay equal
+// between calls.  A fragment slot written by an earlier call of another shape
+// belongs to another tile or range there, or carries an earlier count of this
+// one: either way its tags differ from this call's (until the range's count
+// comes round again after 32768 calls and the slot was never rewritten since).
+//
+// The B chunk is loaded with the A chunk and x, and so is the y of the first
+// 16 rows except with the longest chunks, so that none of them is outstanding
+// at the polls (loads complete in order).
 // The polls are bounded: a member computes itself, with the same code (so the
 // same bits), the partials of every peer whose tags have not all arrived at
 // the spin limit, stores them into those peers' slots (where the peer writes
@@ -113,6 +119,18 @@ __device__ __forceinline__ void split_zero(const SplitParams &p, const int32_t *
   }
 }
 
+// This call's tag of (tile ti, range sl) without the XCD bits, from the
+// member's count word f: the count, one more than the word's (bits 31:17,
+// modulo 2^15), the tile (bits 16:6) and the range (bits 5:4).  Calls of
+// other shapes on the same workspace lay their fragments out differently, so
+// a fragment slot may hold another tile's or range's partials from an earlier
+// call, whose own count can equal this one; naming the tile and the range in
+// the tag keeps those from passing for this call's.
+static_assert(kSyncTiles <= 2048 && kSplitRanges <= 4, "tile and range fit their tag fields");
+__device__ __forceinline__ uint32_t split_want(uint32_t f, int ti, int sl) {
+  return ((((f >> 17) + 1u) & 0x7FFFu) << 17) | ((uint32_t)ti << 6) | ((uint32_t)sl << 4);
+}
+
 // XCD this workgroup runs on (hardware register XCC_ID, bits 3:0).
 __device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15u; }
 
@@ -149,7 +167,7 @@ __device__ __forceinline__ void store_tagged(rsrc_t pr, uint32_t off, f32x4 v, u
 // Wave w's part of gathering the nf fragments (of NF) at off[f] + gm plane
 // over the G members gm: it polls members w MG .. w MG + MG - 1 (those below
 // G) with agent-coherent loads, every load of a look issued before the first
-// is used, until each tag of a member carries this call's count `want`, at
+// is used, until each tag of a member, XCD bits aside, equals `want`, at
 // most spin_limit + 1 looks.  Then it adds each fragment's values in member
 // order into stage[f][wave] (fragments past nf: nothing), so that the caller
 // adds the four waves' sums in wave order after a barrier, and every member
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split_kernel(const int32_t 
   uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords;  // the first range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
-  const uint32_t want = (f & ~15u) + 16u;  // this call's count (bits 31:4)
+  const uint32_t want = split_want(f, ti, 0);  // this call's tag, XCD bits aside
   const uint32_t xcc = xcc_id(), tag = want | xcc;
   uint32_t *const status = flags + (int64_t)kSyncTiles * kSplitFlagWords;
   const int gb0 = g * p.bpm;
@@ -720,7 +738,7 @@ __global__ __launch_bounds__(kSThreads, 2) void bgmv_split1_kernel(const int32_t
   uint32_t *fl = flags + (int64_t)ti * kSplitFlagWords + kSplitMembers * sl;  // this slice's range
   const uint32_t f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(fl + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (ti >= ntiles) return;
-  const uint32_t want = (f & ~15u) + 16u;  // this call's count (bits 31:4)
+  const uint32_t want = split_want(f, ti, sl);  // this call's tag, XCD bits aside
   const uint32_t xcc = xcc_id(), tag = want | xcc;
   uint32_t *const status = flags + (int64_t)kSyncTiles * kSplitFlagWords;
   const int gb0 = g * bpm;

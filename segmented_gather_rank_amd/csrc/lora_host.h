@@ -59,9 +59,9 @@ size_t shrink_ws_bytes(const ShrinkConfig &c, int64_t T, int32_t n_slices, int32
 // kSplitRanges slices that run side by side, for tile indices below
 // kSyncTiles, then one row of counters (word 0: waits that gave up; word 1:
 // flags found raised from another XCD).  A word holds the number of split
-// calls that raised it (bits 31:4) and the XCD of the member that raised it
-// last (bits 3:0).  The region must be zero before the first call on a
-// workspace; every call raises each word of each range it uses exactly once,
+// calls that raised it (bits 31:17, modulo 2^15), its tile (bits 16:6), its
+// range (bits 5:4) and the XCD of the member that raised it last (bits 3:0).
+// The region must be zero before the first call on a workspace; every call raises each word of each range it uses exactly once,
 // so the words of a range stay equal between calls.  The split kernel runs
 // only for T * n_slices * max(r, 16) <= 2^17 tokens x ranks, so T <= 8192 and
 // a batch has at most 8192 / 64 + 1023 + 1 = 1152 tiles.

@@ -43,8 +43,8 @@ def live_tiles(meta):
 
 def tile_flags(L, d, meta):
     """The count words of the apply workspace d.ws, [tile][range][member],
-    as uint32: the call count in bits 31:4, the XCD that raised the word last
-    in bits 3:0."""
+    as uint32: the call count in bits 31:17 (modulo 2^15), the tile in 16:6,
+    the range in 5:4, the XCD that raised the word last in 3:0."""
     n = L.max_tiles(meta.num_tokens, meta.num_slots)
     return L.apply_workspace_flags(d.ws, n).cpu().numpy().view(np.uint32)
 
@@ -52,9 +52,9 @@ def tile_flags(L, d, meta):
 def check_counters(L, ws):
     """No wait gave up.  A member that met a peer on another XCD is counted
     and printed, not failed: which XCD runs a workgroup is the dispatcher's
-    choice (round robin over blockIdx as a rule, with rare exceptions seen),
-    and such a member computes the peer's partials itself, so the results
-    checked before this stay exact."""
+    choice (round robin over blockIdx in every record taken), and such a
+    member computes the peer's partials itself, so the results checked before
+    this stay exact."""
     cnt = L.apply_workspace_counters(ws)
     if cnt["other_xcd"]:
         print(f"[counters] {cnt}", flush=True)
@@ -69,8 +69,11 @@ def check_flags(L, d, meta, calls, ranges=1):
     touched; no wait gave up."""
     f = tile_flags(L, d, meta)
     live, n = live_tiles(meta)
-    cnt, tag = f >> 4, f & 15
+    cnt, tag = f >> 17, f & 15
     assert (cnt[live, :ranges] == calls).all(), cnt[live]
+    # every raised word names its own tile and range
+    assert (((f[live, :ranges] >> 6) & 2047) == live[:, None, None]).all()
+    assert (((f[live, :ranges] >> 4) & 3) == np.arange(ranges)[None, :, None]).all()
     assert (f[live, ranges:] == 0).all()
     dead = np.setdiff1d(np.arange(f.shape[0]), live)
     assert (f[dead] == 0).all()
@@ -160,7 +163,34 @@ def test_split_calls_share_one_meta(L):
     f = tile_flags(L, cases[0][1], meta)
     live, _ = live_tiles(meta)
     assert ((f[live] >> 4) == (f[live][:, :, :1] >> 4)).all()  # each range's words stay equal
-    assert ((f[live, 0] >> 4) >= 2).all()
+    assert ((f[live, 0] >> 17) >= 2).all()
+    check_counters(L, ws)
+
+
+def test_split_shapes_alternate_on_one_workspace(L):
+    """One workspace, calls of four shapes in turn, six rounds: one, two and
+    three slices side by side advance their ranges' counts at different
+    rates, and the shapes lay the partial fragments out differently, so a
+    fragment slot often holds another tile's or range's partials from an
+    earlier call with the same count.  The tags name tile and range as well,
+    so every call is still right."""
+    S, T = 32, 256
+    shapes = [dict(d_in=1024, widths=(512, 256, 136), r=16), dict(d_in=2048, widths=(1024, 512), r=16),
+              dict(d_in=512, widths=(1024,), r=32), dict(d_in=1024, widths=(256, 256, 256), r=8)]
+    base = decode_case(630, 16, S=S, T=T)
+    cases = []
+    for sh in shapes:
+        c = decode_case(630, sh["r"], S=S, T=T, d_in=sh["d_in"], widths=sh["widths"])
+        assert np.array_equal(c.token_slot, base.token_slot)
+        cases.append((c, DevCase(c), oracle_rows(c, np.arange(c.T))))
+    meta = L.lora_prepare_meta(cases[0][1].token_slot, S)
+    ws = L.apply_workspace(max(L.lora_apply_workspace_bytes(T, S, c.d_in, len(c.widths), c.r_max, torch.bfloat16)
+                               for c, _, _ in cases))
+    for rep in range(6):
+        for c, d, ref in cases:
+            print(f"[split-alt] rep {rep} d_in={c.d_in} widths={c.widths} r={c.r_max}", flush=True)
+            y, _ = d.apply(L, mode="auto", meta=meta, workspace=ws)
+            check_rows(c, from_dev(y), ref, f"{c.name} rep {rep}")
     check_counters(L, ws)
 
 
