@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--a-rank-rows", action="store_true",
                     help="hand A over rank-major ([S][r][d_in], the pages' A layout), so that with --slot-ranks "
                          "the ranks past a slot's own are whole rows that are never fetched")
+    ap.add_argument("--b-out-rows", action="store_true",
+                    help="hand B over output-major ([S][w][r], the pages' stacked B layout); lora_apply then runs "
+                         "the tile shrink and the matrix-core expand")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the rotated input copies (beats the 256 MB MALL)")
     ap.add_argument("--flush-mb", type=float, default=1024.0,
@@ -141,8 +144,10 @@ class MoeFlat:
         self.x_rows = int(keyed.sum()) if c.x_per_pair else int(np.unique(tok[keyed]).shape[0])
 
 
-def dominant_kernel(c, mode):
+def dominant_kernel(c, mode, b_out_rows=False):
     """Name (substring) of the kernel that lora_apply runs on this workload."""
+    if b_out_rows:   # output-major B: the tile kernels only
+        return "shrink+expand"
     sw = sum(c.widths)
     e = 4 if c.dtype == "f32" else 2
     w_tok = (c.n_slices * c.d_in + sw) * c.r_max * e
@@ -210,7 +215,8 @@ def kernel_keys(kernel_key):
 
 def variant(args):
     """(file-name suffix, command-line flags) of the weight options of a run."""
-    flags = [f for f, on in (("--slot-ranks", args.slot_ranks), ("--a-rank-rows", args.a_rank_rows)) if on]
+    flags = [f for f, on in (("--slot-ranks", args.slot_ranks), ("--a-rank-rows", args.a_rank_rows),
+                             ("--b-out-rows", args.b_out_rows)) if on]
     return "".join("_" + f[2:].replace("-", "_") for f in flags), "".join(" " + f for f in flags)
 
 
@@ -575,13 +581,16 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     alg = algorithmic(c, args.slot_ranks)
     if moe is None:
         A_host = [np.transpose(a, (0, 2, 1)) for a in c.A] if args.a_rank_rows else c.A
+        B_host = [np.transpose(b, (0, 2, 1)) for b in c.B] if args.b_out_rows else c.B
         base = dict(ts=torch.from_numpy(c.token_slot).to(dev), x=to_dev(c.x),
-                    A=[to_dev(a) for a in A_host], B=[to_dev(b) for b in c.B], y=to_dev(c.y0))
+                    A=[to_dev(a) for a in A_host], B=[to_dev(b) for b in B_host], y=to_dev(c.y0))
     else:
         SE = c.num_slots
         base = dict(ts=torch.from_numpy(moe.token_slot).to(dev), x=to_dev(moe.x),
                     A=[to_dev(a).view(SE, *a.shape[2:]) for a in moe.A],
-                    B=[to_dev(b).view(SE, *b.shape[2:]) for b in moe.B], y=to_dev(moe.y0),
+                    B=[to_dev(np.transpose(b, (0, 1, 3, 2)) if args.b_out_rows else b).view(
+                        SE, *(b.shape[:1:-1] if args.b_out_rows else b.shape[2:])) for b in moe.B],
+                    y=to_dev(moe.y0),
                     topk=torch.from_numpy(moe.topk_ids).to(dev),
                     emap=None if moe.expert_map is None else torch.from_numpy(moe.expert_map).to(dev))
     set_bytes = sum(t.numel() * t.element_size()
@@ -613,7 +622,8 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     def apply_call(i):
         s = sets[i % nrot]
         L.lora_apply(metas[i % nrot], s["x"], s["A"], s["B"], c.offsets, s["y"], scale=c.scale,
-                     add=True, mode=args.mode, workspace=s["aws"], slot_rank=ranks, a_rank_rows=args.a_rank_rows)
+                     add=True, mode=args.mode, workspace=s["aws"], slot_rank=ranks, a_rank_rows=args.a_rank_rows,
+                     b_out_rows=args.b_out_rows)
 
     def step(i):
         meta_call(i)
@@ -681,11 +691,11 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
 
     ms_per_step = total_ms / K
     tokens = c.T if moe is None else moe.T       # an MoE step's tokens (each with top-k pairs)
-    key = dominant_kernel(c, args.mode)
+    key = dominant_kernel(c, args.mode, args.b_out_rows)
     d_bytes = alg["shrink_bytes"] + alg["expand_bytes"]
     d_flops = alg["shrink_flops"] + alg["expand_flops"]
     achieved = d_bytes / (apply_us * 1e-6) / 1e9
-    mf = None if args.slot_ranks or args.a_rank_rows else read_mfma(c, key)
+    mf = None if args.slot_ranks or args.a_rank_rows or args.b_out_rows else read_mfma(c, key)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(c, key, args),
@@ -707,6 +717,7 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
               "slots": c.num_slots, "d_in": c.d_in,
               "slice_widths": c.widths, "r_max": r, "mode": args.mode,
               "slot_ranks": bool(args.slot_ranks), "a_rank_rows": bool(args.a_rank_rows),
+              "b_out_rows": bool(args.b_out_rows),
               "rotated_input_sets": nrot, "flush_mb_before_timed_replay": args.flush_mb,
               "parallelism": "single GPU"}
     return {
@@ -840,13 +851,14 @@ def main():
 
     c, moe = load_case(args.config)
     if args.summarize_pmc:
-        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode), args=args)
+        summarize_pmc(c, args.config, *args.summarize_pmc, kernel_key=dominant_kernel(c, args.mode, args.b_out_rows),
+                      args=args)
         return
     if args.summarize_mfma:
-        summarize_mfma(c, args.config, args.summarize_mfma, dominant_kernel(c, args.mode))
+        summarize_mfma(c, args.config, args.summarize_mfma, dominant_kernel(c, args.mode, args.b_out_rows))
         return
     if args.summarize_trace:
-        summarize_trace(c, args.config, *args.summarize_trace, dominant_kernel(c, args.mode), args)
+        summarize_trace(c, args.config, *args.summarize_trace, dominant_kernel(c, args.mode, args.b_out_rows), args)
         return
     if args.phase_budget:
         phase_budget(c, args, args.phase_budget)
@@ -880,7 +892,9 @@ def main():
         SE = c.num_slots
         A = [to_dev(a).view(SE, *a.shape[2:]) if moe is not None else
              to_dev(np.transpose(a, (0, 2, 1)) if args.a_rank_rows else a) for a in src.A]
-        B = [to_dev(b).view(SE, *b.shape[2:]) if moe is not None else to_dev(b) for b in src.B]
+        B = [to_dev(np.transpose(b, (0, 1, 3, 2)) if args.b_out_rows else b).view(
+                 SE, *(b.shape[:1:-1] if args.b_out_rows else b.shape[2:])) if moe is not None else
+             to_dev(np.transpose(b, (0, 2, 1)) if args.b_out_rows else b) for b in src.B]
         ranks = torch.from_numpy(np.asarray(c.ranks, np.int32)).to(dev) if args.slot_ranks else None
         ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, c.r_max,
                                                             x.dtype, args.mode), dev)
@@ -894,7 +908,7 @@ def main():
                                             torch.from_numpy(moe.expert_map).to(dev))
                 m = m.with_x_row_div(1) if moe.x_per_pair else m
             L.lora_apply(m, x, A, B, c.offsets, y, scale=c.scale, add=True, mode=args.mode, workspace=ws,
-                         slot_rank=ranks, a_rank_rows=args.a_rank_rows)
+                         slot_rank=ranks, a_rank_rows=args.a_rank_rows, b_out_rows=args.b_out_rows)
         torch.cuda.synchronize()
         print(f"pmc pass done: {K} steps of {c.name}", flush=True)
         return

@@ -86,9 +86,16 @@ typedef enum lora_layout {
      * slot's ranks are then whole rows, so with per-slot ranks (d_slot_rank)
      * the ranks past a slot's own are never fetched.  bf16 only, r_max >= 16,
      * mode AUTO or SGMV; every slice of A must use it (else
-     * LORA_ERR_UNSUPPORTED / LORA_ERR_INVALID_ARG).  B keeps the default
-     * layout, whose ranks are already whole rows. */
-    LORA_LAYOUT_RANK_ROWS = 1
+     * LORA_ERR_UNSUPPORTED / LORA_ERR_INVALID_ARG). */
+    LORA_LAYOUT_RANK_ROWS = 1,
+    /* B only: B_s [width_s][r_max] (row stride r_max), one row of ranks per
+     * output column: the output-major B of the same page and section (B
+     * stored d_out x r).  A step of the expand then reads one contiguous
+     * block of B.  bf16 only, r_max <= 64, mode AUTO or SGMV; every slice of B
+     * must use it (else LORA_ERR_UNSUPPORTED / LORA_ERR_INVALID_ARG).
+     * lora_apply runs such calls on the tile kernels (matrix-core expand),
+     * never on the decode kernels or the long-segment expand. */
+    LORA_LAYOUT_OUT_ROWS = 2
 } lora_layout;
 
 /* One packed slice of a stacked factor: slot a's matrix starts at
@@ -287,8 +294,9 @@ lora_status lora_apply_workspace_bytes(int64_t num_tokens, int32_t num_slots,
  * decode-shaped apply (page "多 LoRA 服务：分段矩阵乘与适配器调度", section
  * "不合并权重，批量计算": the fused form for decode batches) spreads each work
  * tile over several workgroups that exchange partial results tagged with the
- * tile, the slice range and the call count, which these words keep.  Every call leaves them
- * consistent for the next call on the same workspace, whatever its shapes.
+ * tile, the slice range and the call count, which these words keep.  Every
+ * call leaves them consistent for the next call on the same workspace,
+ * whatever its shapes.
  * The words must not be written between calls.
  *   d_ws      device workspace, 16-byte aligned
  *   ws_bytes  its size, at least LORA_APPLY_SYNC_BYTES (else LORA_ERR_WORKSPACE) */

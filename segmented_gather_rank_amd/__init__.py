@@ -44,7 +44,7 @@ class lora_weight(C.Structure):
     _fields_ = [("ptr", C.c_void_p), ("slot_stride", C.c_int64), ("layout", C.c_int32), ("reserved", C.c_int32)]
 
 
-LORA_LAYOUT_DEFAULT, LORA_LAYOUT_RANK_ROWS = 0, 1
+LORA_LAYOUT_DEFAULT, LORA_LAYOUT_RANK_ROWS, LORA_LAYOUT_OUT_ROWS = 0, 1, 2
 
 
 class lora_meta(C.Structure):
@@ -103,7 +103,7 @@ class _Lib:
 
 _lib = _Lib(_cdll, _decl)
 
-if _lib.lora_abi_version() != 9:
+if _lib.lora_abi_version() != 10:
     raise ImportError("liblora_mi355x.so has an unexpected ABI version; rebuild it")
 
 
@@ -359,22 +359,31 @@ def lora_shrink(meta: LoraMeta, x: torch.Tensor, A, u: torch.Tensor, scale: floa
     return u
 
 
-def _slices(B_list, offsets):
+def _b_weights(B, b_out_rows: bool):
+    """B as [S][r][w] (default) or, with b_out_rows, [S][w][r] (one row of
+    ranks per output column); returns the descriptors, the tensors and r."""
+    B_arr, B_list = _weights(B, "B", lambda i, w: None, LORA_LAYOUT_OUT_ROWS if b_out_rows else LORA_LAYOUT_DEFAULT)
+    return B_arr, B_list, B_list[0].shape[2] if b_out_rows else B_list[0].shape[1]
+
+
+def _slices(B_list, offsets, b_out_rows: bool = False):
     n = len(B_list)
-    width = (C.c_int64 * n)(*[b.shape[2] for b in B_list])
+    width = (C.c_int64 * n)(*[b.shape[1] if b_out_rows else b.shape[2] for b in B_list])
     offs = (C.c_int64 * n)(*[int(o) for o in offsets])
     return width, offs
 
 
 def lora_expand(meta: LoraMeta, u: torch.Tensor, B, offsets, y: torch.Tensor, add: bool = True,
-                mode: str = "auto", stream=None, slot_rank: torch.Tensor | None = None) -> torch.Tensor:
-    """y[t][off_s:off_s+w_s] (+)= u[s][t] @ B[s][slot]; B: list of [S][r][w_s]."""
-    B_arr, B_list = _weights(B, "B", lambda i, w: None)
-    width, offs = _slices(B_list, offsets)
+                mode: str = "auto", stream=None, slot_rank: torch.Tensor | None = None,
+                b_out_rows: bool = False) -> torch.Tensor:
+    """y[t][off_s:off_s+w_s] (+)= u[s][t] @ B[s][slot]; B: list of [S][r][w_s]
+    (or [S][w_s][r] with b_out_rows)."""
+    B_arr, B_list, rb = _b_weights(B, b_out_rows)
+    width, offs = _slices(B_list, offsets, b_out_rows)
     if y.dim() != 2 or y.stride(1) != 1:
         raise ValueError("y must be [T][ldy] with unit column stride")
     st = _lib.lora_expand(C.byref(meta.c), _dev(u, "u"), len(B_list), B_arr, width, offs,
-                          B_list[0].shape[1], _ranks(slot_rank), _dev(y, "y"), y.stride(0), _dtype(y),
+                          rb, _ranks(slot_rank), _dev(y, "y"), y.stride(0), _dtype(y),
                           int(bool(add)), MODES[mode], _stream(stream))
     _check("lora_expand", st)
     return y
@@ -383,13 +392,15 @@ def lora_expand(meta: LoraMeta, u: torch.Tensor, B, offsets, y: torch.Tensor, ad
 def lora_apply(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
                slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto",
                workspace: torch.Tensor | None = None, stream=None,
-               slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False) -> torch.Tensor:
+               slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False,
+               b_out_rows: bool = False) -> torch.Tensor:
     """Shrink then expand into the slices of y (the whole delta of one layer).
-    A: list of [S][d_in][r], or [S][r][d_in] with a_rank_rows; B: list of [S][r][w_s]."""
+    A: list of [S][d_in][r], or [S][r][d_in] with a_rank_rows; B: list of
+    [S][r][w_s], or [S][w_s][r] with b_out_rows."""
     xp, ldx, d_in = _x_args(x)
     A_arr, A_list, r = _a_weights(A, a_rank_rows)
-    B_arr, B_list = _weights(B, "B", lambda i, w: None)
-    width, offs = _slices(B_list, offsets)
+    B_arr, B_list, _ = _b_weights(B, b_out_rows)
+    width, offs = _slices(B_list, offsets, b_out_rows)
     n = len(A_list)
     if len(B_list) != n:
         raise ValueError("A and B need one entry per slice")
@@ -413,14 +424,15 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # LORA_NOALLOC_SCRATCH_BYTES of the C header
 
 def lora_apply_noalloc(meta: LoraMeta, x: torch.Tensor, A, B, offsets, y: torch.Tensor, scale: float = 1.0,
                        slot_scale: torch.Tensor | None = None, add: bool = True, mode: str = "auto", stream=None,
-                       slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False) -> torch.Tensor:
+                       slot_rank: torch.Tensor | None = None, a_rank_rows: bool = False,
+                       b_out_rows: bool = False) -> torch.Tensor:
     """lora_apply with the library's own device scratch as its workspace (no
     workspace argument, nothing allocated).  Calls that overlap on one device
     share that scratch and race."""
     xp, ldx, d_in = _x_args(x)
     A_arr, A_list, r = _a_weights(A, a_rank_rows)
-    B_arr, B_list = _weights(B, "B", lambda i, w: None)
-    width, offs = _slices(B_list, offsets)
+    B_arr, B_list, _ = _b_weights(B, b_out_rows)
+    width, offs = _slices(B_list, offsets, b_out_rows)
     if len(B_list) != len(A_list):
         raise ValueError("A and B need one entry per slice")
     if y.dim() != 2 or y.stride(1) != 1:
@@ -440,4 +452,4 @@ __all__ = ["lora_apply_noalloc", "NOALLOC_SCRATCH_BYTES", "lora_abi_version", "l
            "lora_shrink_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_workspace_bytes",
            "lora_apply_workspace_init", "apply_workspace", "apply_workspace_counters", "apply_workspace_flags",
            "lora_apply", "LoraMeta", "LoraError", "lora_weight", "lora_meta", "LIB_PATH", "LORA_LAYOUT_DEFAULT",
-           "LORA_LAYOUT_RANK_ROWS"]
+           "LORA_LAYOUT_RANK_ROWS", "LORA_LAYOUT_OUT_ROWS"]

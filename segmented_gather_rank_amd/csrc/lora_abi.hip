@@ -97,7 +97,7 @@ hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t stream) {
 // Kernels address one slot's factor matrix with 32-bit byte offsets.
 constexpr int64_t kMaxFactorElems = (int64_t)1 << 28;
 
-constexpr int32_t kAbiVersion = 9;
+constexpr int32_t kAbiVersion = 10;
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -201,13 +201,16 @@ lora_status check_expand_args(const lora_meta *meta, const float *u, int32_t n_s
     if (w < 8 || w % 8 || o < 0 || o % 8 || o + w > ldy) return LORA_ERR_INVALID_ARG;
     if ((int64_t)(r_max + 1) * w >= kMaxFactorElems) return LORA_ERR_UNSUPPORTED;  // 32-bit offsets
     if (!B[s].ptr || !aligned16(B[s].ptr) || B[s].slot_stride % 8 || B[s].slot_stride < r_max * w ||
-        B[s].reserved != 0)
+        B[s].reserved != 0 || B[s].layout != B[0].layout)
       return LORA_ERR_INVALID_ARG;
-    if (B[s].layout != LORA_LAYOUT_DEFAULT) return LORA_ERR_UNSUPPORTED;
     for (int q = 0; q < s; ++q) {
       if (o < offset[q] + width[q] && offset[q] < o + w) return LORA_ERR_INVALID_ARG;
     }
   }
+  if (B[0].layout != LORA_LAYOUT_DEFAULT && B[0].layout != LORA_LAYOUT_OUT_ROWS) return LORA_ERR_UNSUPPORTED;
+  // B in the output-rows layout is read by the matrix-core expand only
+  if (B[0].layout == LORA_LAYOUT_OUT_ROWS && (dtype != LORA_BF16 || tile_rank(r_max) > 64 || mode == LORA_MODE_BGMV))
+    return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
@@ -248,7 +251,8 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   // its limits hold; both take r_max of 8, 16, 32 or 64 only
   const bool decode = (int)mode != 2 && ((int)mode == 1 || meta->num_tokens <= 16 * (int64_t)meta->num_slots);
   const bool a_rows = A[0].layout == LORA_LAYOUT_RANK_ROWS;  // rank-major A: the tile shrink reads it
-  const bool fused_rank = r_max == R && R <= 64 && !a_rows;
+  const bool b_out = B[0].layout == LORA_LAYOUT_OUT_ROWS;    // output-rows B: the tile expand reads it
+  const bool fused_rank = r_max == R && R <= 64 && !a_rows && !b_out;
   if (fused_rank && !fused_disabled() && decode && dtype == LORA_BF16 && !split_disabled()) {
     bool used = false;
     const hipError_t e = launch_bgmv_split(mv, d_x, ldx, d_in, n_slices, aptr, astr, bptr, bstr, width, offset,
@@ -266,7 +270,7 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   int kch = 1;
-  const bool rows = expand_rows_fits(meta->num_tokens, meta->num_slots, dtype == LORA_BF16, (int)mode, R) &&
+  const bool rows = !b_out && expand_rows_fits(meta->num_tokens, meta->num_slots, dtype == LORA_BF16, (int)mode, R) &&
                     expand_rows_addressable(meta->num_tokens, n_slices, width, offset, ldy, R);
   hipError_t e = launch_shrink(mv, d_x, ldx, d_in, dtype == LORA_BF16, n_slices, aptr, astr, R, r_max,
                                scale, d_slot_scale, d_slot_rank, u, (int)mode, sh_ws, true, &kch, s, rows, a_rows);
@@ -280,7 +284,7 @@ lora_status apply_in(const lora_meta *meta, const void *d_x, int64_t ldx, int64_
   // partial sums, which the expand adds
   const float *ue = kch > 1 ? static_cast<const float *>(sh_ws) : u;
   e = launch_expand(mv, ue, kch > 1 ? 2 : 1, kch, n_slices, bptr, bstr, width, offset, R, r_max,
-                    d_slot_rank, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode, s);
+                    d_slot_rank, d_y, ldy, dtype == LORA_BF16, add_into_y, (int)mode, s, b_out);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -443,7 +447,8 @@ lora_status lora_expand(const lora_meta *meta, const float *d_u, int32_t n_slice
   unpack(B, n_slices, ptrs, strides);
   const hipError_t e = launch_expand(view_of(meta), d_u, 0, 1, n_slices, ptrs, strides, width,
                                      offset, tile_rank(r_max), r_max, d_slot_rank, d_y, ldy, dtype == LORA_BF16,
-                                     add_into_y, (int)mode, static_cast<hipStream_t>(stream));
+                                     add_into_y, (int)mode, static_cast<hipStream_t>(stream),
+                                     B[0].layout == LORA_LAYOUT_OUT_ROWS);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

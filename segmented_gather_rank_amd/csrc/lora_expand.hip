@@ -222,23 +222,29 @@ __device__ __forceinline__ void exp_vec_item(const ExpandParams &p, ExpandLds<E,
 constexpr int kXThreads = 256;
 constexpr int kXStep = 128;          // columns per step (the narrowest step)
 
-template <int R>
+// BO: B in the output-rows layout; a step's B tile then sits in LDS as one
+// row of RP ranks per column (row stride LDO: the 16 columns that one MFMA
+// operand read touches fall in distinct banks), else as RP rank rows of W
+// columns
+template <int R, bool BO>
 struct XLds {
   static constexpr int RP = R < 16 ? 16 : R;  // ranks padded to whole 16-wide steps
   static constexpr int WMAX = kXStep * (64 / RP);  // widest step (short tiles)
-  uint16_t bl[2][RP * (WMAX + 16)];
+  static constexpr int LDO = RP + 8;
+  uint16_t bl[2][BO ? WMAX * LDO : RP * (WMAX + 16)];
   uint16_t uh[kTileRows][RP], ul[kTileRows][RP];  // the tile's rank rows, bf16 hi and lo parts
   int32_t tok[kTileRows];                         // the tile's tokens
 };
 
-template <int R, int NS>
+template <int R, int NS, bool BO>
 __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t *__restrict__ info,
                                                                   const int32_t *__restrict__ tiles,
                                                                   ExpandParams p) {
-  constexpr int RP = XLds<R>::RP;
+  constexpr int RP = XLds<R, BO>::RP;
+  constexpr int LDO = XLds<R, BO>::LDO;
   constexpr int KS = RP / 16;                     // MFMA k-steps
   constexpr int BQ = 4;                           // B octets per thread per step, at most
-  __shared__ XLds<R> lds;
+  __shared__ XLds<R, BO> lds;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n = lane % 16, kg = lane / 16;
   const int64_t T = p.meta.T;
@@ -363,8 +369,10 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
 
     // ---- B step tiles: rows j < RP, W columns; thread octet q covers row
     // idx / (W / 8), columns 8 (idx % (W / 8)) .. + 7 of the step
-    // (idx = tid + 256 q).  Loads past the slot block (rows >= R), past the
-    // slot's rank or past the chunk read zeros without touching memory.
+    // (idx = tid + 256 q); with BO (B_s[slot] is [w][ra]) it covers ranks
+    // 8 (idx % (RP / 8)) .. + 7 of column idx / (RP / 8).  Loads past the slot
+    // block (ranks >= R), past the slot's rank or past the chunk read zeros
+    // without touching memory.
     const int rk = slot_rank_of(p.slot_rank, slot, p.ra);  // ranks past rk are not read
     const rsrc_t br = make_rsrc(reinterpret_cast<const uint16_t *>(pick<NS>(p.B, s, p.n_slices)) +
                                     (int64_t)slot * pick<NS>(p.b_stride, s, p.n_slices),
@@ -375,18 +383,29 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
       for (int q = 0; q < BQ; ++q) {
         if (q < nq) {
           const int idx = tid + kXThreads * q;
-          const int j = idx >> osh, h = idx & ((1 << osh) - 1);
-          const int c = i * W + 8 * h;
-          bq[q] = buf_load16(br, (j < rk && c < ncols) ? (uint32_t)(((int64_t)j * w + col0 + c) * 2) : 0x7FFFFFF0u);
+          if constexpr (BO) {
+            const int c = i * W + idx / (RP / 8), j = 8 * (idx % (RP / 8));
+            bq[q] = buf_load16(br, (j < rk && c < ncols) ? (uint32_t)(((col0 + c) * p.ra + j) * 2) : 0x7FFFFFF0u);
+          } else {
+            const int j = idx >> osh, h = idx & ((1 << osh) - 1);
+            const int c = i * W + 8 * h;
+            bq[q] = buf_load16(br, (j < rk && c < ncols) ? (uint32_t)(((int64_t)j * w + col0 + c) * 2) : 0x7FFFFFF0u);
+          }
         }
       }
     };
     // permuted store: the 8 columns 32 g32 + 8 g4 .. + 7 go to block 2 g32
-    // (rows 4 g4 .. + 3) and block 2 g32 + 1 (same rows)
+    // (rows 4 g4 .. + 3) and block 2 g32 + 1 (same rows); with BO each
+    // column's rank octet goes to the row of its permuted column
     auto store_b = [&](int buf) {
 #pragma unroll
       for (int q = 0; q < BQ; ++q) {
-        if (q < nq) {
+        if (q < nq && BO) {
+          const int idx = tid + kXThreads * q;
+          const int c = idx / (RP / 8), j = 8 * (idx % (RP / 8)), h = c / 8, e = c % 8;
+          const int col = 32 * (h / 4) + 4 * (h % 4) + (e < 4 ? e : 12 + e);
+          *reinterpret_cast<u32x4 *>(&lds.bl[buf][col * LDO + j]) = bq[q];
+        } else if (q < nq) {
           const int idx = tid + kXThreads * q;
           const int j = idx >> osh, h = idx & ((1 << osh) - 1);
           const int col = 32 * (h / 4) + 4 * (h % 4);
@@ -469,7 +488,9 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
             for (int c = 0; c < KS; ++c) {
 #pragma unroll
               for (int hh = 0; hh < 2; ++hh) {
-                const s16x4 a = lds_col4(bt, ldb, 16 * c + 4 * kg, 16 * (blk0 + hh));
+                const s16x4 a =
+                    BO ? *reinterpret_cast<const s16x4 *>(bt + (16 * (blk0 + hh) + n) * LDO + 16 * c + 4 * kg)
+                       : lds_col4(bt, ldb, 16 * c + 4 * kg, 16 * (blk0 + hh));
                 acc[hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ul[c], acc[hh], 0, 0, 0);
                 acc[hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, uh[c], acc[hh], 0, 0, 0);
               }
@@ -819,19 +840,22 @@ static hipError_t launch_t(const ExpandParams &p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <int R, int NS>
+template <int R, int NS, bool BO>
 static hipError_t launch_mma_ns(const ExpandParams &p, int64_t bound, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];
-  const int grid = xcd_grid(bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R, NS>),
-                                                   kXThreads, 0));
-  hipLaunchKernelGGL((expand_mma_kernel<R, NS>), dim3(grid), dim3(kXThreads), 0, stream, p.meta.info, p.meta.tiles,
-                     p);
+  const int grid = xcd_grid(
+      bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R, NS, BO>), kXThreads, 0));
+  hipLaunchKernelGGL((expand_mma_kernel<R, NS, BO>), dim3(grid), dim3(kXThreads), 0, stream, p.meta.info,
+                     p.meta.tiles, p);
   return hipGetLastError();
 }
 
 template <int R>
-static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, hipStream_t stream) {
-  return with_slice_bound(p.n_slices, [&](auto ns) { return launch_mma_ns<R, decltype(ns)::value>(p, bound, stream); });
+static hipError_t launch_mma_t(const ExpandParams &p, int64_t bound, bool b_out_rows, hipStream_t stream) {
+  return with_slice_bound(p.n_slices, [&](auto ns) {
+    constexpr int NS = decltype(ns)::value;
+    return b_out_rows ? launch_mma_ns<R, NS, true>(p, bound, stream) : launch_mma_ns<R, NS, false>(p, bound, stream);
+  });
 }
 
 // Long-segment expand, one instantiation (dynamic LDS: the B chunk).
@@ -932,7 +956,7 @@ bool expand_uses_mma(bool bf16, int mode) { return bf16 && mode != 1; }
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
                          const int64_t *offset, int32_t R, int32_t ra, const int32_t *slot_rank, void *y,
-                         int64_t ldy, bool bf16, int add, int mode, hipStream_t stream) {
+                         int64_t ldy, bool bf16, int add, int mode, hipStream_t stream, bool b_out_rows) {
   ExpandParams p{};
   p.meta = meta;
   p.u = u;
@@ -942,7 +966,11 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
   p.ra = ra;
   p.u_ld = ra;
   const int64_t e = bf16 ? 2 : 4;
-  const bool mma = expand_uses_mma(bf16, mode) && R <= 64;  // rank 128: the vector kernel
+  // rank 128: the vector kernel; B in the output-rows layout: the matrix-core
+  // kernel only (the argument checks keep such calls to bf16, R <= 64 and
+  // mode AUTO or SGMV)
+  const bool mma = (expand_uses_mma(bf16, mode) && R <= 64) || b_out_rows;
+  if (b_out_rows && !(bf16 && R <= 64)) return hipErrorInvalidValue;
   const int64_t T = meta.T, S = meta.S;
   for (int s = 0; s < n_slices; ++s) {
     p.B[s] = B[s];
@@ -971,10 +999,10 @@ hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int k
     }
     const int64_t bound = max_tiles(T, (int32_t)S) * p.steps_total;
     switch (R) {
-      case 8: return launch_mma_t<8>(p, bound, stream);
-      case 16: return launch_mma_t<16>(p, bound, stream);
-      case 32: return launch_mma_t<32>(p, bound, stream);
-      case 64: return launch_mma_t<64>(p, bound, stream);
+      case 8: return launch_mma_t<8>(p, bound, b_out_rows, stream);
+      case 16: return launch_mma_t<16>(p, bound, b_out_rows, stream);
+      case 32: return launch_mma_t<32>(p, bound, b_out_rows, stream);
+      case 64: return launch_mma_t<64>(p, bound, b_out_rows, stream);
     }
     return hipErrorInvalidValue;
   }

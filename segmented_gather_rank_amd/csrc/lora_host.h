@@ -126,11 +126,12 @@ hipError_t launch_shrink(const MetaView &meta, const void *x, int64_t ldx, int64
 // R, ra: as for the shrink (B holds ra rank rows per slot).  u_mode 0: u
 // [n_slices][T][ra] in token order (the caller's); 1: [n_slices][T][R] in
 // sorted-position order; 2: kch partial sums [kch][n_slices][T][R] in
-// sorted-position order
+// sorted-position order.  b_out_rows: B_s[slot] is [w][ra] (the matrix-core
+// kernel only: bf16, R <= 64)
 hipError_t launch_expand(const MetaView &meta, const float *u, int u_mode, int kch, int32_t n_slices,
                          const void *const *B, const int64_t *b_stride, const int64_t *width,
                          const int64_t *offset, int32_t R, int32_t ra, const int32_t *slot_rank, void *y,
-                         int64_t ldy, bool bf16, int add, int mode, hipStream_t stream);
+                         int64_t ldy, bool bf16, int add, int mode, hipStream_t stream, bool b_out_rows = false);
 
 // The long-segment expand (whole 64-token tiles, 512-column chunks) serves
 // this call?  Decided from host-known sizes only.

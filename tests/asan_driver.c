@@ -151,10 +151,18 @@ static void library_checks(void) {
   CHECK(lora_shrink(&m, fake(0), 64, 64, LORA_BF16, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
                     fake(0), 1 << 15, NULL) == LORA_ERR_INVALID_ARG);
   A[0].reserved = 0;
-  B[1].layout = LORA_LAYOUT_RANK_ROWS;
+  B[1].layout = LORA_LAYOUT_OUT_ROWS;  /* slices differ */
+  CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 96, LORA_BF16, 1,
+                    LORA_MODE_AUTO, NULL) == LORA_ERR_INVALID_ARG);
+  B[0].layout = B[1].layout = LORA_LAYOUT_RANK_ROWS;
   CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 96, LORA_BF16, 1,
                     LORA_MODE_AUTO, NULL) == LORA_ERR_UNSUPPORTED);
-  B[1].layout = LORA_LAYOUT_DEFAULT;
+  B[0].layout = B[1].layout = LORA_LAYOUT_OUT_ROWS;
+  CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 96, LORA_F32, 1,
+                    LORA_MODE_AUTO, NULL) == LORA_ERR_UNSUPPORTED);
+  CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 96, LORA_BF16, 1,
+                    LORA_MODE_BGMV, NULL) == LORA_ERR_UNSUPPORTED);
+  B[0].layout = B[1].layout = LORA_LAYOUT_DEFAULT;
   CHECK(lora_shrink(&m, fake(2), 64, 64, LORA_BF16, 1, A, 16, 1.f, NULL, NULL, (float *)fake(0), LORA_MODE_AUTO,
                     fake(0), 1 << 15, NULL) == LORA_ERR_INVALID_ARG);
   CHECK(lora_expand(&m, (const float *)fake(0), 2, B, width, offset, 16, NULL, fake(0), 90, LORA_BF16, 1,

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert L.lora_abi_version() == 9
+    assert L.lora_abi_version() == 10
     assert L.lora_status_string(0) == "LORA_OK"
     assert L.lora_status_string(3) == "LORA_ERR_WORKSPACE"
     assert L.lora_status_string(99) == "LORA_ERR_UNKNOWN"
@@ -155,17 +155,19 @@ def test_shrink_rejections():
                    ws_bytes=need - 1) == L.LORA_ERR_WORKSPACE
 
 
-def _expand(n=2, widths=(64, 32), offsets=(0, 64), r=16, ldy=96, B=None, y=None, mode=0):
+def _expand(n=2, widths=(64, 32), offsets=(0, 64), r=16, ldy=96, B=None, y=None, mode=0, dtype=1):
     wd = (C.c_int64 * n)(*widths[:n])
     of = (C.c_int64 * n)(*offsets[:n])
     B = B if B is not None else (L.lora_weight * n)(*[L.lora_weight(_base, r * w) for w in widths[:n]])
     return _call("lora_expand", C.byref(_meta()), _ptr(), n, B, wd, of, r, None,
-                 y if y is not None else _ptr(), ldy, 1, 1, mode, None)
+                 y if y is not None else _ptr(), ldy, dtype, 1, mode, None)
 
 
 def test_layout_rejections():
     """Rank-major A ([r][d_in]) is read by the matrix-core shrink only: bf16,
-    r_max >= 16, mode AUTO or SGMV, every slice alike; B has one layout."""
+    r_max >= 16, mode AUTO or SGMV, every slice alike.  Output-rows B
+    ([w][r]) by the matrix-core expand only: bf16, r_max <= 64, mode AUTO or
+    SGMV, every slice alike.  Neither layout is taken by the other factor."""
     def A_rows(n=1, layouts=(1,), stride=64 * 16):
         arr = (L.lora_weight * n)()
         for i in range(n):
@@ -176,8 +178,19 @@ def test_layout_rejections():
     assert _shrink(A=A_rows(stride=64 * 8), r=8) == L.LORA_ERR_UNSUPPORTED  # r_max 8
     assert _shrink(A=A_rows(2, (1, 0)), n=2) == L.LORA_ERR_INVALID_ARG     # slices differ
     assert _shrink(A=A_rows(layouts=(7,))) == L.LORA_ERR_UNSUPPORTED
-    Bl = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64), L.lora_weight(_base, 16 * 32, 1))
-    assert _expand(B=Bl) == L.LORA_ERR_UNSUPPORTED
+    assert _shrink(A=A_rows(layouts=(L.LORA_LAYOUT_OUT_ROWS,))) == L.LORA_ERR_UNSUPPORTED
+    def B_rows(layouts, r=16, widths=(64, 32)):
+        return (L.lora_weight * 2)(*[L.lora_weight(_base, r * w, layouts[min(i, len(layouts) - 1)])
+                                     for i, w in enumerate(widths)])
+    out = L.LORA_LAYOUT_OUT_ROWS
+    assert _expand(B=B_rows((0, out))) == L.LORA_ERR_INVALID_ARG             # slices differ
+    assert _expand(B=B_rows((L.LORA_LAYOUT_RANK_ROWS,))) == L.LORA_ERR_UNSUPPORTED
+    assert _expand(B=B_rows((7,))) == L.LORA_ERR_UNSUPPORTED
+    assert _expand(B=B_rows((out,)), dtype=0) == L.LORA_ERR_UNSUPPORTED     # fp32
+    assert _expand(B=B_rows((out,)), mode=1) == L.LORA_ERR_UNSUPPORTED      # BGMV
+    assert _expand(B=B_rows((out,), r=128), r=128) == L.LORA_ERR_UNSUPPORTED  # past the tile expand's 64
+    thin = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64 - 8, out), L.lora_weight(_base, 16 * 32, out))
+    assert _expand(B=thin) == L.LORA_ERR_INVALID_ARG                          # slots overlap
     Bz = (L.lora_weight * 2)(L.lora_weight(_base, 16 * 64, 0, 5), L.lora_weight(_base, 16 * 32))
     assert _expand(B=Bz) == L.LORA_ERR_INVALID_ARG                          # reserved != 0
 
