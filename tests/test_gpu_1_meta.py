@@ -1,7 +1,9 @@
 """GPU slot metadata against the oracle: bit-exact on every array.  Batches of
 8192 rows and more are counted in parts by several workgroups (up to 64 parts
 of at least 1024 rows, a part taking 1024 rows per step); smaller ones run on
-one workgroup."""
+one workgroup, which from 3072 rows scatters batches of mixed keys through LDS
+(the random, Zipf and bad-id patterns) and the others straight to memory
+(sorted, reversed, one slot, all without an adapter)."""
 import numpy as np
 import pytest
 import torch
@@ -62,8 +64,8 @@ def _rng(seed):
 PATTERNS = ["uniform", "all_none", "one_slot", "sorted", "reversed", "zipf", "bad_ids"]
 
 
-@pytest.mark.parametrize("T", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025, 5000, 8192, 20000])
-@pytest.mark.parametrize("S", [1, 2, 33, 1023])
+@pytest.mark.parametrize("T", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025, 3071, 3072, 5000, 8191, 8192, 20000])
+@pytest.mark.parametrize("S", [1, 2, 33, 128, 1023])
 @pytest.mark.parametrize("pattern", PATTERNS)
 def test_meta_random(L, T, S, pattern):
     rng = _rng(T * 7919 + S * 31 + PATTERNS.index(pattern))

@@ -131,6 +131,17 @@ def test_moe_meta_many_rows(L, with_map, bad):
     check(c, from_dev(y)[rows], moe_ref(c, rows=rows), c.name)
 
 
+@pytest.mark.parametrize("with_map,bad", [(True, False), (False, True)])
+def test_moe_meta_one_workgroup_scattered(L, with_map, bad):
+    """600 tokens x top-8: 4800 (token, expert) rows of many keys in batch
+    order, on one workgroup, whose scatter then goes through LDS."""
+    c = small_moe(760 + int(bad), T=600, K=8, E=64, EL=16 if with_map else 64, with_map=with_map, bad=bad)
+    print(f"[moe-meta] {c.name} rows={c.rows} map={with_map} bad={bad}", flush=True)
+    d = MoeDev(c)
+    ref = check_meta(L, d)
+    assert (ref.num_bad > 0) == bad
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("per_pair", [False, True])
 @pytest.mark.parametrize("mode", ["auto", "bgmv", "sgmv"])
