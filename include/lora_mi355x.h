@@ -305,9 +305,10 @@ lora_status lora_apply_workspace_init(void *d_ws, size_t ws_bytes, void *stream)
 /* Shrink then expand on one stream: the whole delta of one layer, added into
  * (or stored to) the slices of y.  Arguments as in lora_shrink and lora_expand;
  * the rank-r buffer lives in d_ws.  Decode-shaped calls (few tokens per slot,
- * small per-token factors, mode AUTO or BGMV, r_max one of 8, 16, 32, 64) run
- * as one fused kernel that keeps each token's rank-r vector on chip; the others
- * run the shrink and expand kernels.  Cites page "vLLM 源码完全拆解(十八):多 LoRA
+ * small per-token factors, mode AUTO or BGMV, r_max one of 8, 16, 32, 64,
+ * default factor layouts) run as one fused kernel that keeps each token's
+ * rank-r vector on chip; the others run the shrink and expand kernels.  Cites
+ * page "vLLM 源码完全拆解(十八):多 LoRA
  * 服务", section "调用链" (add_lora_linear = shrink into an fp32 buffer, then
  * expand into the output slices).
  *   d_ws      workspace of at least lora_apply_workspace_bytes bytes, 16-byte
