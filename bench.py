@@ -926,6 +926,9 @@ def main():
         extra[ck.name] = {kk: e[kk] for kk in ("value", "ms_per_step", "roofline", "calls_us", "split_rendezvous")
                           if kk in e}
         extra[ck.name]["unit"] = "tokens/s"
+        if not args.no_cpu_baseline and k in (1, 2):
+            # the small workloads' oracle also on one thread (a few seconds)
+            extra[ck.name]["cpu_baseline_one_thread"] = cpu_baseline(ck, 3.0, 1)
         del ck, mk
     del flush
     torch.cuda.empty_cache()
@@ -944,6 +947,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds, args.cpu_threads or host_threads())
+        if args.config in (1, 2):
+            out["cpu_baseline_one_thread"] = cpu_baseline(c, 3.0, 1)
     print(json.dumps(out), flush=True)
 
 
