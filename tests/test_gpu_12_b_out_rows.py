@@ -6,14 +6,16 @@ see the same factors.  Cases: the small mixed batch at every rank the tile
 expand takes (r_max on and off the tile ranks), both A layouts, per-slot ranks
 with NaN past them, add and store, the expand alone from a seeded rank-r
 buffer, long segments and decode batches (which lora_apply then runs on the
-tile kernels), and integer inputs that every summation order gets exactly."""
+tile kernels), integer inputs that every summation order gets exactly, and the
+prefill and many-adapter decode workloads at full size."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from gpu_util import DELTA_L2, DevCase, as_f64, check_rows, from_dev, oracle_rows, to_dev
+from gpu_util import DELTA_L2, DevCase, as_f64, check_rows, from_dev, oracle_rows, sample_rows, to_dev
+from test_gpu_10_fullsize import delta_gates
 from test_gpu_2_apply import small_case
 from test_gpu_4_edges import integer_case
 from test_gpu_6_ranks import nan_padded, rank_rows
@@ -132,7 +134,8 @@ def test_b_out_rows_matches_default_layout_on_decode(L):
 
 
 def test_b_out_rows_rejected_calls(L):
-    """fp32, mode BGMV and r_max 128 are not served in this layout."""
+    """fp32 and mode BGMV are not served in this layout (r_max 128 neither:
+    the argument checks run on the CPU too)."""
     c = small_case(2100, "f32", 16)
     d = DevCase(c)
     meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
@@ -145,3 +148,22 @@ def test_b_out_rows_rejected_calls(L):
     with pytest.raises(L.LoraError) as e:
         L.lora_apply(meta, d.x, d.A, out_rows(c.B, c.dtype), c.offsets, d.y0.clone(), mode="bgmv", b_out_rows=True)
     assert e.value.status == L.LORA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("k", [3, 5])
+def test_b_out_rows_full_size_store_mode(L, k):
+    """The prefill gate/up and many-adapter decode workloads at full size with
+    output-major B, in store mode (the gates then apply to the delta itself),
+    on the sampled rows."""
+    c = W.config(k)
+    print(f"[b-out-full] {c.name} T={c.T}", flush=True)
+    d = DevCase(c)
+    B = out_rows(c.B, c.dtype)
+    meta = L.lora_prepare_meta(d.token_slot, c.num_slots)
+    y = d.y0.clone()
+    L.lora_apply(meta, d.x, d.A, B, c.offsets, y, scale=c.scale, add=False, b_out_rows=True)
+    rows = sample_rows(c)
+    got = from_dev(y.index_select(0, torch.from_numpy(rows).cuda()))
+    delta_gates(c, got, oracle_rows(c, rows, add=False), f"{c.name} b_out_rows")
+    del y, d, B
+    torch.cuda.empty_cache()
