@@ -80,6 +80,9 @@ def parse():
                     help="build the library with the split kernel's phase clock (-DLORA_PHASE_CLOCK) into a "
                          "temporary directory, run --steps cold steps of the workload on it and write the "
                          "per-phase latency budget of the one-slice split kernel to OUT_MD")
+    ap.add_argument("--tile-phase-budget", metavar="OUT_MD",
+                    help="the same measurement build, for the tile shrink and the tile expand of the workload: "
+                         "their items' timing per workgroup, written to OUT_MD")
     return ap.parse_args()
 
 
@@ -842,6 +845,143 @@ def phase_budget(c, args, out_md):
     print("\n".join(lines), flush=True)
 
 
+def tile_phase_budget(c, moe, args, out_md):
+    """Timing of the tile shrink's items and of the tile expand's phases, from
+    their own clocks in the measurement build (LORA_PHASE_CLOCK; the kernel
+    that records is chosen with LORA_PHASE_KERNEL).  Each of --steps steps is
+    one flushing copy, the metadata and lora_apply, as in the timed graph,
+    once with the shrink recording and once with the expand recording."""
+    import ctypes
+    import importlib.util
+    import tempfile
+
+    import numpy as np
+
+    if moe is not None:
+        raise SystemExit("--tile-phase-budget takes a plain (non-MoE) workload")
+    spec = importlib.util.spec_from_file_location(
+        "_lora_hip_build", os.path.join(ROOT, "segmented_gather_rank_amd", "build.py"))
+    hb = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(hb)
+    tmp = tempfile.mkdtemp(prefix="lora_phase_")
+    os.environ["LORA_MI355X_LIB"] = hb.build(out=os.path.join(tmp, "liblora_mi355x_phase.so"),
+                                             extra=["-DLORA_PHASE_CLOCK"])
+    import torch
+
+    import segmented_gather_rank_amd as L
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    words = 16   # 64-bit words per workgroup record (kTilePhaseWords)
+    clk = torch.zeros(words * 8192, dtype=torch.int64, device=dev)
+    L._cdll.lora_debug_phase_clock.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L._cdll.lora_debug_phase_clock(ctypes.c_void_p(clk.data_ptr()), clk.numel())
+    ts, x, y = torch.from_numpy(c.token_slot).to(dev), to_dev(c.x), to_dev(c.y0)
+    A, B = [to_dev(a) for a in c.A], [to_dev(b) for b in c.B]
+    ws = L.apply_workspace(L.lora_apply_workspace_bytes(c.T, c.num_slots, c.d_in, c.n_slices, c.r_max,
+                                                        x.dtype, args.mode), dev)
+    mws = torch.empty(L.lora_meta_workspace_bytes(c.T, c.num_slots), dtype=torch.uint8, device=dev)
+    flush = Flush(torch, dev, args.flush_mb)
+
+    def records(kernel):
+        os.environ["LORA_PHASE_KERNEL"] = kernel
+        out = []
+        for it in range(args.warmup + args.steps):
+            flush()
+            clk.zero_()
+            m = L.lora_prepare_meta(ts, c.num_slots, workspace=mws)
+            L.lora_apply(m, x, A, B, c.offsets, y, scale=c.scale, add=True, mode=args.mode, workspace=ws)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                r = clk.cpu().numpy().reshape(-1, words).astype(np.float64)
+                r = r[(r[:, 0] != 0) & (r[:, 15] != 0)]
+                if r.shape[0]:
+                    out.append(r)
+        os.environ.pop("LORA_PHASE_KERNEL")
+        return out
+
+    q = lambda a: f"{np.median(a):.1f} | {np.percentile(a, 90):.1f} | {a.max():.1f}"
+    lines = [f"# Tile shrink and tile expand timing: {c.name}", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
+             f"--tile-phase-budget {out_md}", "```", "",
+             "The library is rebuilt with `-DLORA_PHASE_CLOCK`: the chosen kernel's workgroups write the 100 MHz "
+             "real-time counter at their phase boundaries (10 ns resolution). Each step is a 1 GiB flushing copy, "
+             "`lora_prepare_meta`, then `lora_apply`; the shrink records in one set of steps, the expand in "
+             f"another ({args.steps} each). Times in us from the kernel's first workgroup start; "
+             "median | p90 | max over workgroups and steps.", ""]
+    # the shrink: items per workgroup and each item's duration
+    sh = records("shrink")
+    if not sh:
+        raise SystemExit("the tile shrink did not run: not a tile-path workload")
+    durs, ends, nits, first_d, later_d = [], [], [], [], []
+    for r in sh:
+        t0 = r[:, 0].min()
+        for w in r:
+            n = int(w[13])
+            nits.append(n)
+            ends.append((w[15] - t0) / 100.0)
+            for j in range(min(n, 6)):
+                d = (w[2 + 2 * j] - w[1 + 2 * j]) / 100.0
+                durs.append(d)
+                (first_d if j == 0 else later_d).append(d)
+    nits, ends = np.array(nits), np.array(ends)
+    lines += ["## Tile shrink (`shrink_mma_kernel`)", "",
+              f"{sh[0].shape[0]} workgroups; items per workgroup: " +
+              ", ".join(f"{int(k)}: {int(v // len(sh))}" for k, v in zip(*np.unique(nits, return_counts=True))) +
+              ".", "", "| | median | p90 | max |", "|---|---|---|---|",
+              f"| item duration | {q(np.array(durs))} |",
+              f"| first item of a workgroup | {q(np.array(first_d))} |"]
+    if later_d:
+        lines.append(f"| later items | {q(np.array(later_d))} |")
+    for n in sorted(set(nits.tolist())):
+        lines.append(f"| end, workgroups of {n} item(s) | {q(ends[nits == n])} |")
+    spans = [(r[:, 15].max() - r[:, 0].min()) / 100.0 for r in sh]
+    busy = [np.sum(r[:, 15] - r[:, 0]) / (r.shape[0] * (r[:, 15].max() - r[:, 0].min())) for r in sh]
+    lines += ["", f"Kernel span (first start to last end), median over steps: {np.median(spans):.1f} us; "
+              f"workgroups busy {np.median(busy):.2f} of it.", ""]
+    # the expand: phases of each workgroup's first item, by the tile's rows
+    ex = records("expand")
+    if not ex:
+        lines += ["The expand of this workload is the long-segment kernel, which does not record."]
+    rows_all, hdr, pro, step, end = [], [], [], [], []
+    for r in ex:
+        t0 = r[:, 0].min()
+        for w in r:
+            ns, rw = int(w[13]) & 255, (int(w[13]) >> 8) & 255
+            k = min(ns, 10)
+            rows_all.append(rw)
+            hdr.append((w[1] - w[0]) / 100.0)
+            pro.append((w[2] - w[1]) / 100.0)
+            step.append(np.mean(np.diff(w[2:3 + k])) / 100.0 if k else 0.0)
+            end.append((w[15] - t0) / 100.0)
+    rows_all, hdr, pro, step, end = map(np.array, (rows_all, hdr, pro, step, end))
+    lines += [] if not ex else ["## Tile expand (`expand_mma_kernel`), each workgroup's first item", "",
+              f"{ex[0].shape[0]} workgroups per step.", "",
+              "| Tile rows | workgroups | header in | prologue | one step | end |", "|---|---|---|---|---|---|"]
+    for lo, hi in ((1, 16), (17, 32), (33, 48), (49, 64)):
+        mask = (rows_all >= lo) & (rows_all <= hi)
+        if mask.any():
+            lines.append(f"| {lo}-{hi} | {int(mask.sum() // len(ex))} | {np.median(hdr[mask]):.2f} | "
+                         f"{np.median(pro[mask]):.2f} | {np.median(step[mask]):.2f} | {np.median(end[mask]):.1f} |")
+    if ex:
+        spans = [(r[:, 15].max() - r[:, 0].min()) / 100.0 for r in ex]
+        lines += ["", "Medians in us: header in = the tile header's arrival after the workgroup's start; prologue = "
+                  "B's first step staged and the tile's rank rows gathered; one step = a step of 128 or more "
+                  "columns; end = from the kernel's first start.", "",
+                  f"Kernel span (first start to last end), median over steps: {np.median(spans):.1f} us."]
+    os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -862,6 +1002,9 @@ def main():
         return
     if args.phase_budget:
         phase_budget(c, args, args.phase_budget)
+        return
+    if args.tile_phase_budget:
+        tile_phase_budget(c, moe, args, args.tile_phase_budget)
         return
 
     import torch

@@ -63,6 +63,9 @@
 // rest.
 //
 // Only bf16.
+#include <cstdlib>
+#include <cstring>
+
 #include "lora_host.h"
 
 namespace lora {
@@ -1350,6 +1353,24 @@ hipError_t launch_bgmv_split(const MetaView &meta, const void *x, int64_t ldx, i
   }
   return hipSuccess;
 }
+
+#ifdef LORA_PHASE_CLOCK
+unsigned long long *phase_clock_buffer(size_t *words) {
+  *words = g_phase_words;
+  return g_phase_clock;
+}
+int phase_clock_kernel() {
+  const char *k = getenv("LORA_PHASE_KERNEL");
+  if (!k) return 0;
+  return strcmp(k, "shrink") == 0 ? 1 : (strcmp(k, "expand") == 0 ? 2 : 0);
+}
+#else
+unsigned long long *phase_clock_buffer(size_t *words) {
+  *words = 0;
+  return nullptr;
+}
+int phase_clock_kernel() { return 0; }
+#endif
 
 }  // namespace lora
 

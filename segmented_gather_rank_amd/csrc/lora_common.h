@@ -246,6 +246,31 @@ __device__ __forceinline__ int64_t packed_to_factor(int64_t e, int ra) {
   return R == 0 ? e : (e / R) * ra + (e % R);
 }
 
+// ---------------------------------------------------------------- measurement build
+// With -DLORA_PHASE_CLOCK (a measurement build) the tile shrink and the tile
+// expand can record, per workgroup, the 100 MHz real-time counter at their
+// phase boundaries into kTilePhaseWords 64-bit words; `rec` is null unless the
+// host asked the kernel to record.  Other builds compile the stamps out.
+constexpr int kTilePhaseWords = 16;
+#ifdef LORA_PHASE_CLOCK
+constexpr bool kPhaseClock = true;
+#else
+constexpr bool kPhaseClock = false;
+#endif
+__device__ __forceinline__ void phase_stamp(unsigned long long *rec, int k) {
+  if constexpr (kPhaseClock) {
+    if (rec && threadIdx.x == 0) rec[k] = (unsigned long long)__builtin_amdgcn_s_memrealtime();
+  }
+}
+__device__ __forceinline__ void phase_put(unsigned long long *rec, int k, unsigned long long v) {
+  if constexpr (kPhaseClock) {
+    if (rec && threadIdx.x == 0) rec[k] = v;
+  }
+}
+__device__ __forceinline__ unsigned long long *phase_record(unsigned long long *clk) {
+  return kPhaseClock && clk ? clk + (int64_t)blockIdx.x * kTilePhaseWords : nullptr;
+}
+
 // ---------------------------------------------------------------- metadata view
 
 struct MetaView {

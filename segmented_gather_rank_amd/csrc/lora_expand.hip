@@ -62,6 +62,7 @@ struct ExpandParams {
   uint32_t plane_bytes;               // bytes of one u plane (< 2^30)
   int32_t ra;                         // the caller's r_max: B rows and ranks read (ra <= R)
   int32_t u_ld;                       // row stride of u in token order (the caller's u: ra)
+  unsigned long long *clk;            // a measurement build's phase records, or null
 };
 
 template <typename E, int R>
@@ -246,6 +247,13 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
   constexpr int BQ = 4;                           // B octets per thread per step, at most
   __shared__ XLds<R, BO> lds;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // measurement build, the first item with an adapter: 0 start, 1 header
+  // in, 2 prologue done (B's first step staged, the rank rows in LDS), 3 + i
+  // after step i < 10, 13 steps | rows << 8, 14 XCC_ID, 15 end (stores
+  // acknowledged)
+  unsigned long long *rec = phase_record(p.clk);
+  unsigned long long *const rec0 = rec;
+  phase_stamp(rec, 0);
   const int n = lane % 16, kg = lane / 16;
   const int64_t T = p.meta.T;
   // live tiles: the tile list is in key order, so the tiles of tokens without
@@ -319,6 +327,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     if (item + per < hi) hnext = read_header(item + per);
     const int slot = uniform_value(hd.slot), rows = uniform_value(hd.rows);
     const int64_t pos0 = uniform_value(hd.pos0);
+    phase_stamp(rec, 1);
     // chunk ck -> slice s and the chunk's first column in it
     int s = 0, cbase = 0, acc = 0;
 #pragma unroll
@@ -462,6 +471,7 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
     }
     store_b(0);
     __syncthreads();
+    phase_stamp(rec, 2);
     // rows past the tile hold stale values: their results are never stored
     s16x4 uh[KS], ul[KS];
 #pragma unroll
@@ -520,6 +530,17 @@ __global__ __launch_bounds__(kXThreads, 3) void expand_mma_kernel(const int32_t 
         for (int pp = 0; pp < 4; ++pp) ycur[pp] = ynext[pp];
       }
       __syncthreads();
+      if (i < 10) phase_stamp(rec, 3 + i);
+    }
+    phase_put(rec, 13, (unsigned long long)(nsteps | rows << 8));
+    if constexpr (kPhaseClock) phase_put(rec, 14, __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15u);
+    rec = nullptr;
+  }
+  if constexpr (kPhaseClock) {
+    if (rec0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      phase_stamp(rec0, 15);
     }
   }
 }
@@ -841,10 +862,14 @@ static hipError_t launch_t(const ExpandParams &p, int grid, hipStream_t stream) 
 }
 
 template <int R, int NS, bool BO>
-static hipError_t launch_mma_ns(const ExpandParams &p, int64_t bound, hipStream_t stream) {
+static hipError_t launch_mma_ns(const ExpandParams &p0, int64_t bound, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];
   const int grid = xcd_grid(
       bound, resident_groups(resident, reinterpret_cast<const void *>(&expand_mma_kernel<R, NS, BO>), kXThreads, 0));
+  ExpandParams p = p0;
+  size_t words = 0;
+  unsigned long long *clk = phase_clock_buffer(&words);
+  p.clk = phase_clock_kernel() == 2 && (size_t)grid * kTilePhaseWords <= words ? clk : nullptr;
   hipLaunchKernelGGL((expand_mma_kernel<R, NS, BO>), dim3(grid), dim3(kXThreads), 0, stream, p.meta.info,
                      p.meta.tiles, p);
   return hipGetLastError();

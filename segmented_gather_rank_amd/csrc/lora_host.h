@@ -172,4 +172,11 @@ bool split_disabled();
 int split_spin_limit();
 int split_members();
 
+// A measurement build (-DLORA_PHASE_CLOCK): the buffer lora_debug_phase_clock
+// set and its size in 64-bit words, and the tile kernel asked to record into
+// it (environment LORA_PHASE_KERNEL: "shrink" 1, "expand" 2, else 0; the split
+// decode kernel always records).  Other builds: null, 0.
+unsigned long long *phase_clock_buffer(size_t *words);
+int phase_clock_kernel();
+
 }  // namespace lora

@@ -60,6 +60,7 @@ struct ShrinkParams {
   int32_t ra;            // the caller's r_max: A row stride, ranks read (ra <= R)
   int32_t u_ld;          // row stride of u written in token order (the caller's u: ra)
   int32_t a_rank_rows;   // A_s[slot] is [ra][d_in] (rank-major), not [d_in][ra]
+  unsigned long long *clk;  // a measurement build's phase records, or null
 };
 
 struct ShrinkLds {
@@ -255,6 +256,11 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
   const int xcd = blockIdx.x % 8, per = gridDim.x / 8;
   const int hi = min(total, xcd * run + run);
   int item = xcd * run + (int)blockIdx.x / 8;
+  // measurement build: 0 start, 1 + 2n / 2 + 2n start and end of item n < 6,
+  // 13 items, 14 the last item's rows, 15 end (stores acknowledged)
+  unsigned long long *const rec = phase_record(p.clk);
+  phase_stamp(rec, 0);
+  int nit = 0;
   if (item >= hi) return;
   const uint16_t *x = reinterpret_cast<const uint16_t *>(p.x);
   float *red = reinterpret_cast<float *>(&at[0][0]);  // [64 rows][CB * 16] after the k loop
@@ -273,6 +279,7 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
   Header hnext = read_header(item);
 
   for (; item < hi; item += per) {
+    if (nit < 6) phase_stamp(rec, 1 + 2 * nit);
     const int kc = item / live;
     const Header hd = hnext;
     if (item + per < hi) hnext = read_header(item + per);
@@ -425,6 +432,17 @@ __global__ __launch_bounds__(kMThreads, 2) void shrink_mma_kernel(const int32_t 
         put4(p, R, s0 + n4 / R, pos0 + r_, n4 % R, kc, f32x4{v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc});
       }
     }
+    if (nit < 6) phase_stamp(rec, 2 + 2 * nit);
+    phase_put(rec, 14, (unsigned long long)rows);
+    ++nit;
+  }
+  if constexpr (kPhaseClock) {
+    phase_put(rec, 13, (unsigned long long)nit);
+    if (rec) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      phase_stamp(rec, 15);
+    }
   }
 }
 
@@ -516,11 +534,15 @@ static hipError_t launch_t(const ShrinkParams &p, int grid, hipStream_t stream) 
 }
 
 template <int R, int CB, int NS, bool RM>
-static hipError_t launch_mma_ns(const ShrinkParams &p, int64_t bound, hipStream_t stream) {
+static hipError_t launch_mma_ns(const ShrinkParams &p0, int64_t bound, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];
   const int grid = xcd_grid(bound, resident_groups(resident,
                                                    reinterpret_cast<const void *>(&shrink_mma_kernel<R, CB, NS, RM>),
                                                    kMThreads, 0));
+  ShrinkParams p = p0;
+  size_t words = 0;
+  unsigned long long *clk = phase_clock_buffer(&words);
+  p.clk = phase_clock_kernel() == 1 && (size_t)grid * kTilePhaseWords <= words ? clk : nullptr;
   hipLaunchKernelGGL((shrink_mma_kernel<R, CB, NS, RM>), dim3(grid), dim3(kMThreads), 0, stream, p.meta.info,
                      p.meta.tiles, p);
   return hipGetLastError();
