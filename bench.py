@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3,
                     help="workload 1..8 (3 = prefill gate/up, the headline; 2, 5 = decode; 7, 8 = MoE experts' LoRA)")
-    ap.add_argument("--extra", default="2,5",
+    ap.add_argument("--extra", default="2,4,5,6,7,8",
                     help="comma-separated workloads also measured and reported under 'extra' ('' for none)")
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--slot-ranks", action="store_true",
