@@ -434,8 +434,8 @@ def summarize_trace(c, k, d, bench_json, kernel_key, args):
              f"python bench.py --config {k} --extra '' --no-cpu-baseline{fl} > {rel(bench_json)}",
              f"python bench.py --config {k} --summarize-trace {rel(d)} {rel(bench_json)}{fl}",
              "```", "",
-             "Kernel statistics (durations in ns; the graphs replay the timed steps twice each, plus eager warm-up "
-             "steps and the flush copies):", "",
+             "Kernel statistics (durations in ns; the step graph is replayed twice and each per-call graph "
+             f"{CALL_REPLAYS + 1} times, plus eager warm-up and reference steps and the flush copies):", "",
              "| Kernel | Calls | Average ns | Min ns | Max ns | Share |", "|---|---|---|---|---|---|"]
     apply_ns = 0.0
     for r in rows:
@@ -570,6 +570,9 @@ def copy_rate_gbs(torch, dev):
     return 2 * n / (best * 1e-3) / 1e9
 
 
+CALL_REPLAYS = 5   # timed replays of each per-call graph (their median is reported)
+
+
 def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     """Graph-timed step, metadata and apply of one workload; returns the
     figures of its JSON line (roofline of lora_apply included)."""
@@ -667,8 +670,9 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
     t_host0 = time.perf_counter()
     total_ms = time_graph(g_step)           # the timed region: exactly K steps
     t_host = time.perf_counter() - t_host0
-    meta_us = 1e3 * time_graph(g_meta) / K
-    apply_us = 1e3 * time_graph(g_apply) / K
+    # per-call figures: the median of CALL_REPLAYS replays, each after a flush
+    meta_us = 1e3 * float(np.median([time_graph(g_meta) for _ in range(CALL_REPLAYS)])) / K
+    apply_us = 1e3 * float(np.median([time_graph(g_apply) for _ in range(CALL_REPLAYS)])) / K
     del g_step, g_meta, g_apply
 
     # the same steps issued eagerly from Python, for reference (host-issue bound)
@@ -727,7 +731,9 @@ def measure(c, moe, args, L, torch, dev, flush, K, warmup):
         "value": round(tokens * K / (total_ms / 1e3), 1), "ms_per_step": round(ms_per_step, 5),
         "dtype": "bf16" if c.dtype == "bf16" else "f32", "config": config, "roofline": roofline,
         "calls_us": {"lora_prepare_meta": round(meta_us, 3), "lora_apply": round(apply_us, 3),
-                     "lora_prepare_meta_per_layer_of_32": round(meta_us / 32, 3)},
+                     "lora_prepare_meta_per_layer_of_32": round(meta_us / 32, 3),
+                     "timed_as": f"a HIP graph of K calls of one kind, the median of {CALL_REPLAYS} replays, "
+                                 "each after a flushing copy"},
         "step": {"algorithmic_bytes": int(d_bytes),
                  "hbm_frac": round(d_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_bf16_frac": round(d_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
